@@ -1,0 +1,383 @@
+/*
+ * nsa_oracle.c -- plain, slow CPU reference of Native Sparse Attention (NSA).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  The HIP library
+ * shares no code, header, table or constant with it.
+ *
+ * Arithmetic is IEEE double throughout.  Loops are scalar and follow the
+ * order in which the pages describe the method; the only parallelism is an
+ * OpenMP loop over independent (batch, query position, KV group) rows.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [deepdaiv]  deepdaiv newsletter on DeepSeek's Native Sparse Attention
+ *              (deepdaiv.stibee.com/p/82): the paragraphs on token compression,
+ *              token selection and the sliding window (the three branches that
+ *              see the same input).
+ *  [valuable12] "AI 모델의 '긴 문장 처리' 한계 돌파, 딥시크의 새 어텐션 기술 화제"
+ *              (valuable12.com), section II (NSA structure: l=32, d=16, l'=64,
+ *              n=16 including 1 initial and 2 local blocks, w=512) and section
+ *              III.3 (decode reads 5,632 tokens instead of 65,536 at 64k).
+ *  [allinfo]   DSA explainer (allinfo.ai.kr), section "쉽게 이해하기": the
+ *              softmax denominator runs over the selected set only.
+ *  [ctol]      ctol-kr.com news article on NSA, "주요 내용" and "하드웨어 인식
+ *              설계": group-centric loading of GQA heads with a shared KV fetch.
+ *
+ * Readings where the pages are silent (each is listed with its reason in the
+ * repository's design notes):
+ *  - compression: one linear map of the flattened, position-embedded block,
+ *    W[c][tau*dim + e] applied to (x[i*d + tau][e] + PE[tau][e]); no bias,
+ *    no activation; one (W, PE) pair for K and one for V shared by all KV
+ *    heads; only complete blocks: N_cmp = floor((T - l)/d) + 1 for T >= l.
+ *  - compressed causality: block i is visible to position t iff i*d + l - 1 <= t.
+ *  - softmax scale 1/sqrt(d_k) in all three branches.
+ *  - importance: the compressed branch's softmax probabilities summed over the
+ *    G query heads of a KV group, mapped to selection blocks by token overlap:
+ *    w(i, j) = |[i*d, i*d+l) intersect [j*l', (j+1)*l')| / d.
+ *  - selection: forced blocks {0, j_cur-1, j_cur} (j_cur = floor(t/l')), then
+ *    the highest-scoring remaining blocks (ties: lower j) up to n in total;
+ *    if no more than n candidates exist, all are taken.  Ascending, -1 padded.
+ *  - selected branch: one softmax over the union of the selected blocks'
+ *    tokens with tau <= t; window branch: tokens [max(0, t-w+1), t].
+ *  - gates: g_c = sigmoid(W_g[h][c] . q_h + b_g[h][c]) for c in (cmp, slc, win);
+ *    o = g_cmp*o_cmp + g_slc*o_slc + g_win*o_win.
+ *  - an empty visible set (t < l - 1) gives o_cmp = 0 and zero scores.
+ *  - decode: the query is the last cached token, t = seq_len - 1.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#include <fenv.h>
+
+typedef struct {
+    int B, T, Hkv, G, dk, dv; /* H_q = Hkv*G; query head h belongs to KV group h/G */
+    int l, d, lsel, n, w;     /* block length, stride, selection block, count, window */
+    double scale;             /* softmax scale */
+} orc_cfg;
+
+/* Number of complete compression blocks of a length-T sequence. */
+int orc_n_cmp(int T, int l, int d)
+{
+    if (T < l) return 0;
+    return (T - l) / d + 1;
+}
+
+/* Round a double to the nearest bfloat16 value (8 significant bits), ties to
+ * even.  The compressed K/V of the bf16 configurations are stored in bf16, so
+ * the oracle rounds them at that point too. */
+double orc_round_bf16(double x)
+{
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    double m = frexp(x, &e);               /* x = m * 2^e, 0.5 <= |m| < 1 */
+    double r = nearbyint(ldexp(m, 8));     /* default mode: nearest, ties even */
+    return ldexp(r, e - 8);
+}
+
+/* Token compression ([deepdaiv], token compression paragraph; [valuable12] II:
+ * blocks of l tokens at stride d).
+ *   x   [B][H][T][dim]     keys or values
+ *   W   [dim][l*dim]       linear map, input index tau*dim + e
+ *   PE  [l][dim]           intra-block position embedding
+ *   out [B][H][n_out][dim] with n_out >= N_cmp; entries past N_cmp are zeroed */
+void orc_compress(int B, int H, int T, int dim, int l, int d, int n_out, int round_bf16,
+                  const double *x, const double *W, const double *PE, double *out)
+{
+    int ncmp = orc_n_cmp(T, l, d);
+    for (int b = 0; b < B; b++)
+        for (int h = 0; h < H; h++) {
+            const double *xs = x + ((size_t)b * H + h) * (size_t)T * dim;
+            double *os = out + ((size_t)b * H + h) * (size_t)n_out * dim;
+            for (int i = 0; i < n_out; i++)
+                for (int c = 0; c < dim; c++) {
+                    double acc = 0.0;
+                    if (i < ncmp) {
+                        for (int tau = 0; tau < l; tau++)
+                            for (int e = 0; e < dim; e++)
+                                acc += W[(size_t)c * l * dim + (size_t)tau * dim + e] *
+                                       (xs[(size_t)(i * d + tau) * dim + e] + PE[(size_t)tau * dim + e]);
+                        if (round_bf16) acc = orc_round_bf16(acc);
+                    }
+                    os[(size_t)i * dim + c] = acc;
+                }
+        }
+}
+
+static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+/* Softmax attention of one query vector over an explicit list of key rows.
+ *   keys[r] = row index into K/V (row stride dk / dv); out[dv] = sum p_r V[r]
+ *   returns the log-sum-exp of the scaled logits (or -INFINITY if empty). */
+static double attend_list(const double *qh, const double *K, const double *V, int dk, int dv,
+                          double scale, const int *rows, int nrows, double *out, double *p_out)
+{
+    for (int c = 0; c < dv; c++) out[c] = 0.0;
+    if (nrows == 0) return -INFINITY;
+    double *s = (double *)malloc(sizeof(double) * (size_t)nrows);
+    double mx = -INFINITY;
+    for (int r = 0; r < nrows; r++) {
+        const double *kr = K + (size_t)rows[r] * dk;
+        double dot = 0.0;
+        for (int e = 0; e < dk; e++) dot += qh[e] * kr[e];
+        s[r] = scale * dot;
+        if (s[r] > mx) mx = s[r];
+    }
+    double sum = 0.0;
+    for (int r = 0; r < nrows; r++) {
+        s[r] = exp(s[r] - mx);
+        sum += s[r];
+    }
+    for (int r = 0; r < nrows; r++) {
+        double p = s[r] / sum;
+        if (p_out) p_out[r] = p;
+        const double *vr = V + (size_t)rows[r] * dv;
+        for (int c = 0; c < dv; c++) out[c] += p * vr[c];
+    }
+    free(s);
+    return mx + log(sum);
+}
+
+/* Overlap weight between compression block i and selection block j:
+ * number of shared tokens divided by the stride d. */
+static double overlap_weight(const orc_cfg *c, int i, int j)
+{
+    long a0 = (long)i * c->d, a1 = a0 + c->l;
+    long b0 = (long)j * c->lsel, b1 = b0 + c->lsel;
+    long lo = a0 > b0 ? a0 : b0, hi = a1 < b1 ? a1 : b1;
+    return hi > lo ? (double)(hi - lo) / c->d : 0.0;
+}
+
+typedef struct { double s; int j; } cand_t;
+
+/* Higher score first; on exact equality, lower block index first. */
+static int cand_cmp(const void *pa, const void *pb)
+{
+    const cand_t *a = (const cand_t *)pa, *b = (const cand_t *)pb;
+    if (a->s > b->s) return -1;
+    if (a->s < b->s) return 1;
+    return (a->j > b->j) - (a->j < b->j);
+}
+
+static int int_cmp(const void *pa, const void *pb)
+{
+    int a = *(const int *)pa, b = *(const int *)pb;
+    return (a > b) - (a < b);
+}
+
+/* Block selection for one (position, KV group) row ([deepdaiv], token
+ * selection paragraph; [valuable12] II: n blocks including the initial block
+ * and 2 local blocks).  S[0..j_cur] are the importance scores.  Writes n
+ * ascending indices, -1 padded; returns the number selected. */
+static int select_blocks(const orc_cfg *c, int t, const double *S, int *idx)
+{
+    int jcur = t / c->lsel;
+    int *sel = (int *)malloc(sizeof(int) * (size_t)(jcur + 1));
+    char *forced = (char *)calloc((size_t)jcur + 1, 1);
+    int nsel = 0;
+    int fcand[3] = {0, jcur - 1, jcur};
+    for (int f = 0; f < 3; f++) {
+        int j = fcand[f];
+        if (j >= 0 && j <= jcur && !forced[j]) {
+            forced[j] = 1;
+            sel[nsel++] = j;
+        }
+    }
+    int nrest = jcur + 1 - nsel;
+    int k = c->n - nsel;
+    cand_t *rest = (cand_t *)malloc(sizeof(cand_t) * (size_t)(nrest > 0 ? nrest : 1));
+    int r = 0;
+    for (int j = 0; j <= jcur; j++)
+        if (!forced[j]) { rest[r].s = S[j]; rest[r].j = j; r++; }
+    if (nrest <= k) {
+        for (int q = 0; q < nrest; q++) sel[nsel++] = rest[q].j;
+    } else {
+        qsort(rest, (size_t)nrest, sizeof(cand_t), cand_cmp);
+        for (int q = 0; q < k; q++) sel[nsel++] = rest[q].j;
+    }
+    qsort(sel, (size_t)nsel, sizeof(int), int_cmp);
+    for (int q = 0; q < c->n; q++) idx[q] = q < nsel ? sel[q] : -1;
+    free(rest);
+    free(forced);
+    free(sel);
+    return nsel;
+}
+
+/* One (position t, KV group) row of the NSA forward pass.
+ *   q      [G][dk]      the G query heads of the group at position t
+ *   kc, vc [>=N_cmp(t)][dk|dv]  compressed keys / values of the group
+ *   k, v   [>=t+1][dk|dv]       raw keys / values of the group
+ *   wg     [G][3][dk], bg [G][3]  gate weights of these heads
+ *   idx_in [n] or NULL: if given, these blocks are used instead of selecting
+ *   o      [G][dv]
+ *   idx_out[n], scores[nb] (nb >= j_cur+1; entries past j_cur = -inf) or NULL,
+ *   branches [3][G][dv] (o_cmp, o_slc, o_win) or NULL, gates [G][3] or NULL,
+ *   lse [G] (compressed-branch log-sum-exp, -inf if empty) or NULL */
+void orc_row(const orc_cfg *c, int t, const double *q, const double *kc, const double *vc,
+             const double *k, const double *v, const double *wg, const double *bg,
+             const int *idx_in, double *o, int *idx_out, double *scores, int nb,
+             double *branches, double *gates, double *lse)
+{
+    const int G = c->G, dk = c->dk, dv = c->dv;
+    const int jcur = t / c->lsel;
+    /* compressed blocks visible at t: i*d + l - 1 <= t */
+    int nvis = (t - (c->l - 1) >= 0) ? (t - (c->l - 1)) / c->d + 1 : 0;
+    double *S = (double *)calloc((size_t)jcur + 1, sizeof(double));
+    double *ocmp = (double *)calloc((size_t)G * dv, sizeof(double));
+    double *oslc = (double *)calloc((size_t)G * dv, sizeof(double));
+    double *owin = (double *)calloc((size_t)G * dv, sizeof(double));
+    double *p = (double *)malloc(sizeof(double) * (size_t)(nvis > 0 ? nvis : 1));
+    double *P = (double *)calloc((size_t)(nvis > 0 ? nvis : 1), sizeof(double));
+    int *rows = (int *)malloc(sizeof(int) * (size_t)(t + 1 > nvis ? t + 1 : nvis + 1));
+
+    /* Compressed branch and its per-group importance. */
+    for (int i = 0; i < nvis; i++) rows[i] = i;
+    for (int h = 0; h < G; h++) {
+        double L = attend_list(q + (size_t)h * dk, kc, vc, dk, dv, c->scale, rows, nvis,
+                               ocmp + (size_t)h * dv, p);
+        if (lse) lse[h] = L;
+        for (int i = 0; i < nvis; i++) P[i] += p[i];
+    }
+    for (int i = 0; i < nvis; i++) {
+        /* block i spans tokens [i*d, i*d+l); it can touch at most the blocks
+         * holding its first and last token */
+        int j0 = (i * c->d) / c->lsel, j1 = (i * c->d + c->l - 1) / c->lsel;
+        for (int j = j0; j <= j1; j++) S[j] += overlap_weight(c, i, j) * P[i];
+    }
+    if (scores)
+        for (int j = 0; j < nb; j++) scores[j] = j <= jcur ? S[j] : -INFINITY;
+
+    /* Selection. */
+    int idx[64];
+    int nsel;
+    if (idx_in) {
+        nsel = 0;
+        for (int q2 = 0; q2 < c->n; q2++) {
+            idx[q2] = idx_in[q2];
+            if (idx_in[q2] >= 0) nsel++;
+        }
+    } else {
+        nsel = select_blocks(c, t, S, idx);
+    }
+    if (idx_out)
+        for (int q2 = 0; q2 < c->n; q2++) idx_out[q2] = idx[q2];
+
+    /* Selected branch: one softmax over the union of the selected blocks'
+     * tokens that are causal ([allinfo]: denominator over the selected set). */
+    int nr = 0;
+    {
+        int *sorted = (int *)malloc(sizeof(int) * (size_t)(c->n));
+        int m = 0;
+        for (int q2 = 0; q2 < c->n; q2++)
+            if (idx[q2] >= 0) sorted[m++] = idx[q2];
+        qsort(sorted, (size_t)m, sizeof(int), int_cmp);
+        for (int q2 = 0; q2 < m; q2++) {
+            if (q2 > 0 && sorted[q2] == sorted[q2 - 1]) continue; /* a set, not a list */
+            for (int tau = sorted[q2] * c->lsel; tau < (sorted[q2] + 1) * c->lsel; tau++)
+                if (tau <= t) rows[nr++] = tau;
+        }
+        free(sorted);
+    }
+    for (int h = 0; h < G; h++)
+        attend_list(q + (size_t)h * dk, k, v, dk, dv, c->scale, rows, nr, oslc + (size_t)h * dv, NULL);
+
+    /* Sliding window: [max(0, t-w+1), t]. */
+    int lo = t - c->w + 1 > 0 ? t - c->w + 1 : 0;
+    nr = 0;
+    for (int tau = lo; tau <= t; tau++) rows[nr++] = tau;
+    for (int h = 0; h < G; h++)
+        attend_list(q + (size_t)h * dk, k, v, dk, dv, c->scale, rows, nr, owin + (size_t)h * dv, NULL);
+
+    /* Gated combination. */
+    for (int h = 0; h < G; h++) {
+        double g3[3];
+        for (int cc = 0; cc < 3; cc++) {
+            double z = bg[h * 3 + cc];
+            const double *wr = wg + ((size_t)h * 3 + cc) * dk;
+            for (int e = 0; e < dk; e++) z += wr[e] * q[(size_t)h * dk + e];
+            g3[cc] = sigmoid(z);
+            if (gates) gates[h * 3 + cc] = g3[cc];
+        }
+        for (int cc = 0; cc < dv; cc++)
+            o[(size_t)h * dv + cc] = g3[0] * ocmp[(size_t)h * dv + cc] +
+                                     g3[1] * oslc[(size_t)h * dv + cc] +
+                                     g3[2] * owin[(size_t)h * dv + cc];
+    }
+    if (branches) {
+        memcpy(branches, ocmp, sizeof(double) * (size_t)G * dv);
+        memcpy(branches + (size_t)G * dv, oslc, sizeof(double) * (size_t)G * dv);
+        memcpy(branches + (size_t)2 * G * dv, owin, sizeof(double) * (size_t)G * dv);
+    }
+    (void)nsel;
+    free(rows); free(P); free(p); free(owin); free(oslc); free(ocmp); free(S);
+}
+
+/* Prefill forward over a list of rows.
+ *   q        [R][Hq][dk]   query rows (row r is position t_list[r] of batch b_list[r])
+ *   kc, vc   [B][Hkv][npad][dk|dv]
+ *   k, v     [B][Hkv][T][dk|dv]
+ *   wg [Hq][3][dk], bg [Hq][3]
+ *   idx_in   [R][Hkv][n] or NULL
+ *   o        [R][Hq][dv];  idx_out [R][Hkv][n];  scores [R][Hkv][nb] or NULL;
+ *   branches [R][3][Hq][dv] or NULL; lse [R][Hq] or NULL */
+void orc_forward_rows(const orc_cfg *c, int R, const int *b_list, const int *t_list,
+                      const double *q, const double *kc, const double *vc, int npad,
+                      const double *k, const double *v, const double *wg, const double *bg,
+                      const int *idx_in, double *o, int *idx_out, double *scores, int nb,
+                      double *branches, double *lse)
+{
+    const int Hkv = c->Hkv, G = c->G, Hq = Hkv * G, dk = c->dk, dv = c->dv, n = c->n, T = c->T;
+    long total = (long)R * Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long job = 0; job < total; job++) {
+        int r = (int)(job / Hkv), g = (int)(job % Hkv);
+        int b = b_list[r], t = t_list[r];
+        const double *qr = q + ((size_t)r * Hq + (size_t)g * G) * dk;
+        const double *kcg = kc + ((size_t)b * Hkv + g) * (size_t)npad * dk;
+        const double *vcg = vc + ((size_t)b * Hkv + g) * (size_t)npad * dv;
+        const double *kg = k + ((size_t)b * Hkv + g) * (size_t)T * dk;
+        const double *vg = v + ((size_t)b * Hkv + g) * (size_t)T * dv;
+        double *br = NULL;
+        double *tmp = NULL;
+        if (branches) tmp = (double *)malloc(sizeof(double) * 3 * (size_t)G * dv);
+        orc_row(c, t, qr, kcg, vcg, kg, vg, wg + (size_t)g * G * 3 * dk, bg + (size_t)g * G * 3,
+                idx_in ? idx_in + ((size_t)r * Hkv + g) * n : NULL,
+                o + ((size_t)r * Hq + (size_t)g * G) * dv,
+                idx_out + ((size_t)r * Hkv + g) * n,
+                scores ? scores + ((size_t)r * Hkv + g) * nb : NULL, nb, tmp, NULL,
+                lse ? lse + (size_t)r * Hq + (size_t)g * G : NULL);
+        if (branches) {
+            for (int br_i = 0; br_i < 3; br_i++) {
+                br = branches + (((size_t)r * 3 + br_i) * Hq + (size_t)g * G) * dv;
+                memcpy(br, tmp + (size_t)br_i * G * dv, sizeof(double) * (size_t)G * dv);
+            }
+            free(tmp);
+        }
+    }
+}
+
+/* Decode step ([valuable12] III.3: the decode step reads a bounded token set).
+ * The query of sequence b is its last cached token, t = seq_lens[b] - 1; the
+ * caches hold T (capacity) raw tokens and npad compressed slots per group.
+ *   q [B][Hq][dk], o [B][Hq][dv], idx_in / idx_out [B][Hkv][n] */
+void orc_decode(const orc_cfg *c, const int *seq_lens, const double *q, const double *kc,
+                const double *vc, int npad, const double *k, const double *v,
+                const double *wg, const double *bg, const int *idx_in, double *o, int *idx_out)
+{
+    const int B = c->B;
+    int *b_list = (int *)malloc(sizeof(int) * (size_t)B);
+    int *t_list = (int *)malloc(sizeof(int) * (size_t)B);
+    for (int b = 0; b < B; b++) {
+        b_list[b] = b;
+        t_list[b] = seq_lens[b] - 1;
+    }
+    orc_forward_rows(c, B, b_list, t_list, q, kc, vc, npad, k, v, wg, bg, idx_in, o, idx_out,
+                     NULL, 0, NULL, NULL);
+    free(t_list);
+    free(b_list);
+}
+
+/* Selection only, for tests that supply their own scores S[0..t/l']. */
+int orc_select(const orc_cfg *c, int t, const double *S, int *idx)
+{
+    return select_blocks(c, t, S, idx);
+}

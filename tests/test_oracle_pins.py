@@ -1,0 +1,411 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+library routines (scaled-dot-product attention, logsumexp, matmul, bf16
+casts), closed forms, invariants, brute force on tiny inputs, and the numbers
+the pages print (fixtures in tests/golden/).  CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rnd(rng, *shape, std=1.0):
+    return rng.standard_normal(shape) * std
+
+
+def make_case(T, Hkv=1, G=4, dk=16, dv=8, n=16, w=512, B=1, seed=0, act_std=1.0):
+    rng = np.random.default_rng(seed)
+    cfg = orc.Cfg(B, T, Hkv, G, dk, dv, n=n, w=w)
+    x = dict(
+        q=_rnd(rng, B, T, Hkv * G, dk, std=act_std),
+        k=_rnd(rng, B, Hkv, T, dk, std=act_std),
+        v=_rnd(rng, B, Hkv, T, dv),
+        wck=_rnd(rng, dk, 32 * dk, std=1 / math.sqrt(32 * dk)),
+        pek=_rnd(rng, 32, dk, std=1 / math.sqrt(dk)),
+        wcv=_rnd(rng, dv, 32 * dv, std=1 / math.sqrt(32 * dv)),
+        pev=_rnd(rng, 32, dv, std=1 / math.sqrt(dv)),
+        wg=_rnd(rng, Hkv * G, 3, dk, std=1 / math.sqrt(dk)),
+        bg=_rnd(rng, Hkv * G, 3, std=1 / math.sqrt(dk)),
+    )
+    npad = max(64, -(-orc.n_cmp(T) // 64) * 64)
+    x["kc"] = orc.compress(x["k"], x["wck"], x["pek"], n_out=npad)
+    x["vc"] = orc.compress(x["v"], x["wcv"], x["pev"], n_out=npad)
+    return cfg, x
+
+
+def run(cfg, x, **kw):
+    return orc.forward(cfg, x["q"], x["kc"], x["vc"], x["k"], x["v"], x["wg"], x["bg"], **kw)
+
+
+def sdpa(q, k, v, mask, scale):
+    """Library attention in float64: q [H,L,E], k [S,E], v [S,Ev], mask [L,S] bool."""
+    qt = torch.from_numpy(q)
+    kt = torch.from_numpy(k)[None].expand(q.shape[0], -1, -1)
+    vt = torch.from_numpy(v)[None].expand(q.shape[0], -1, -1)
+    return F.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(mask), scale=scale).numpy()
+
+
+# ---------------------------------------------------------------- compression
+
+def test_n_cmp_closed_form():
+    assert orc.n_cmp(31) == 0
+    assert orc.n_cmp(32) == 1
+    assert orc.n_cmp(47) == 1
+    assert orc.n_cmp(48) == 2
+    # the 64k decode workload's compressed cache holds 4,095 entries
+    assert orc.n_cmp(65536) == 4095
+
+
+@pytest.mark.parametrize("tau", [0, 7, 31])
+def test_compress_onehot_is_strided_gather(tau):
+    """W selecting token tau of each block turns compression into a gather of
+    token i*16 + tau (plus that slot's position embedding)."""
+    rng = np.random.default_rng(1)
+    dim, T = 6, 130
+    x = _rnd(rng, 1, 2, T, dim)
+    W = np.zeros((dim, 32 * dim))
+    for c in range(dim):
+        W[c, tau * dim + c] = 1.0
+    PE = _rnd(rng, 32, dim)
+    out = orc.compress(x, W, PE)
+    N = orc.n_cmp(T)
+    assert out.shape == (1, 2, N, dim)
+    want = x[:, :, tau + 16 * np.arange(N), :] + PE[tau]
+    np.testing.assert_array_equal(out, want)
+
+
+def test_compress_mean_pooling():
+    rng = np.random.default_rng(2)
+    dim, T = 5, 100
+    x = _rnd(rng, 2, 1, T, dim)
+    W = np.tile(np.eye(dim), (1, 32)) / 32.0
+    PE = np.zeros((32, dim))
+    out = orc.compress(x, W, PE)
+    N = orc.n_cmp(T)
+    want = np.stack([x[:, :, 16 * i:16 * i + 32].mean(axis=2) for i in range(N)], axis=2)
+    np.testing.assert_allclose(out, want, rtol=1e-13, atol=1e-14)
+
+
+def test_compress_equals_window_matmul():
+    """General W: the flattened (block + PE) rows times W^T, via numpy's strided
+    window view and matmul."""
+    rng = np.random.default_rng(3)
+    dim, T = 12, 211
+    x = _rnd(rng, 1, 3, T, dim)
+    W = _rnd(rng, dim, 32 * dim)
+    PE = _rnd(rng, 32, dim)
+    out = orc.compress(x, W, PE, n_out=20)
+    N = orc.n_cmp(T)
+    win = np.lib.stride_tricks.sliding_window_view(x, 32, axis=2)[:, :, ::16]  # [1,3,N,dim,32]
+    win = win[:, :, :N].transpose(0, 1, 2, 4, 3) + PE                            # [1,3,N,32,dim]
+    want = win.reshape(1, 3, N, 32 * dim) @ W.T
+    np.testing.assert_allclose(out[:, :, :N], want, rtol=1e-12, atol=1e-11)
+    assert np.all(out[:, :, N:] == 0)
+
+
+def test_round_bf16_matches_torch_cast():
+    rng = np.random.default_rng(4)
+    vals = np.concatenate([_rnd(rng, 2000).astype(np.float32).astype(np.float64),
+                           np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -1 - 2 ** -8, 3.0e-3, -7.5e4])])
+    want = torch.from_numpy(vals.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([orc.round_bf16(v) for v in vals])
+    np.testing.assert_array_equal(got, want)
+
+
+def test_compress_bf16_rounding_applied():
+    rng = np.random.default_rng(5)
+    x = _rnd(rng, 1, 1, 64, 4)
+    W = _rnd(rng, 4, 128)
+    PE = _rnd(rng, 32, 4)
+    exact = orc.compress(x, W, PE)
+    rounded = orc.compress(x, W, PE, round_bf16=True)
+    want = torch.from_numpy(exact).to(torch.bfloat16).to(torch.float64).numpy()
+    # the double -> bf16 rounding and torch's double -> bf16 cast agree except
+    # on exact ties, which random doubles do not hit
+    np.testing.assert_array_equal(rounded, want)
+
+
+# ------------------------------------------------------- compressed attention
+
+def cmp_mask(T, N):
+    t = np.arange(T)[:, None]
+    i = np.arange(N)[None, :]
+    return i * 16 + 31 <= t
+
+
+@pytest.mark.parametrize("T", [31, 32, 33, 64, 65, 127, 200])
+def test_compressed_branch_is_masked_attention(T):
+    cfg, x = make_case(T, Hkv=2, G=3, dk=16, dv=8, seed=T)
+    out = run(cfg, x, want_branches=True, want_lse=True)
+    ocmp = out["branches"][0, :, 0]  # [T, Hq, dv]
+    N = orc.n_cmp(T)
+    m = cmp_mask(T, N)
+    for g in range(2):
+        heads = slice(3 * g, 3 * g + 3)
+        if N > 0:
+            rows = m.any(axis=1)
+            want = sdpa(x["q"][0, :, heads].transpose(1, 0, 2)[:, rows], x["kc"][0, g, :N], x["vc"][0, g, :N],
+                        m[rows], 1 / math.sqrt(16))
+            np.testing.assert_allclose(ocmp[rows, heads].transpose(1, 0, 2), want, rtol=1e-11, atol=1e-12)
+            # log-sum-exp of the masked logits
+            s = np.einsum("the,ne->htn", x["q"][0, :, heads], x["kc"][0, g, :N]) / 4.0
+            lse = torch.logsumexp(torch.from_numpy(np.where(m[None], s, -np.inf)), dim=-1).numpy()
+            np.testing.assert_allclose(out["lse"][0, rows, heads].T, lse[:, rows], rtol=1e-12)
+        empty = ~m.any(axis=1) if N > 0 else np.ones(T, bool)
+        assert np.all(ocmp[empty, heads] == 0)
+        assert np.all(np.isneginf(out["lse"][0, empty, heads]))
+
+
+def test_importance_sums_to_2G():
+    """Each compressed block overlaps selection blocks in l/d = 2 strides, and
+    each head's probabilities sum to one, so a row's scores sum to 2G."""
+    cfg, x = make_case(300, Hkv=2, G=5, seed=11)
+    sc = run(cfg, x, want_scores=True)["scores"][0]  # [Hkv,T,nb]
+    for t in range(300):
+        jc = t // 64
+        if t >= 31:
+            np.testing.assert_allclose(sc[:, t, :jc + 1].sum(-1), 10.0, rtol=1e-12)
+        else:
+            assert np.all(sc[:, t, :jc + 1] == 0)
+        assert np.all(np.isneginf(sc[:, t, jc + 1:]))
+
+
+@pytest.mark.parametrize("istar", [4, 5, 6, 7, 12, 19])
+def test_importance_planted_block(istar):
+    """One compressed key dominating every head gives S[j] = G * overlap(i*, j)/d:
+    2G on its block for i* = 4a, 4a+1, 4a+2; G on blocks a and a+1 for i* = 4a+3."""
+    T, G, dk = 512, 4, 8
+    cfg, x = make_case(T, Hkv=1, G=G, dk=dk, dv=4, seed=istar)
+    alpha = 40.0
+    x["kc"][0, 0, :, 0] = 0.0
+    x["kc"][0, 0, istar, :] = 0.0
+    x["kc"][0, 0, istar, 0] = alpha
+    x["q"][0, :, :, 0] = alpha
+    sc = run(cfg, x, want_scores=True)["scores"][0, 0]
+    a, r = divmod(istar, 4)
+    want = np.zeros(sc.shape[1])
+    if r < 3:
+        want[a] = 2 * G
+    else:
+        want[a] = want[a + 1] = G
+    for t in range(istar * 16 + 31, T):
+        jc = t // 64
+        np.testing.assert_allclose(sc[t, :jc + 1], want[:jc + 1], atol=1e-9)
+
+
+# ------------------------------------------------------------------ selection
+
+def check_topn_properties(t, S, idx, n):
+    jc = t // 64
+    sel = [j for j in idx if j >= 0]
+    assert sel == sorted(set(sel)), "ascending and distinct"
+    assert all(0 <= j <= jc for j in sel)
+    assert all(j == -1 for j in idx[len(sel):])
+    forced = {0, jc - 1, jc} & set(range(jc + 1))
+    assert forced <= set(sel)
+    assert len(sel) == min(n, jc + 1)
+    free_sel = [j for j in sel if j not in forced]
+    free_out = [j for j in range(jc + 1) if j not in sel]
+    if free_sel and free_out:
+        worst = min(free_sel, key=lambda j: (S[j], -j))
+        for j in free_out:   # every left-out block ranks below every kept one
+            assert (S[j], -j) < (S[worst], -worst)
+
+
+def test_selection_properties_reduced_n():
+    """T=512 with n=4 (1 initial + 2 local + 1 free): real ranking on every row
+    with more than 4 candidate blocks."""
+    cfg, x = make_case(512, Hkv=2, G=4, n=4, w=128, seed=21, act_std=3.0)
+    out = run(cfg, x, want_scores=True)
+    for g in range(2):
+        for t in range(512):
+            check_topn_properties(t, out["scores"][0, g, t], list(out["idx"][0, g, t]), 4)
+
+
+def test_selection_ties_take_lower_block():
+    cfg = orc.Cfg(1, 4096, 1, 1, 4, 4, n=6)
+    t = 64 * 40 + 5
+    S = np.ones(41)
+    idx = orc.select(cfg, t, S)
+    # forced {0, 39, 40}; three free picks at equal score: 1, 2, 3
+    assert list(idx) == [0, 1, 2, 3, 39, 40]
+    S[17] = 2.0
+    S[30] = 1.5
+    idx = orc.select(cfg, t, S)
+    assert list(idx) == [0, 1, 17, 30, 39, 40]
+
+
+@pytest.mark.parametrize("t", [0, 63, 64, 127, 128, 1023, 1024, 5000])
+def test_selection_small_rows(t):
+    cfg = orc.Cfg(1, 8192, 1, 1, 4, 4)
+    rng = np.random.default_rng(t)
+    S = rng.random(t // 64 + 1)
+    idx = list(orc.select(cfg, t, S))
+    check_topn_properties(t, S, idx, 16)
+
+
+# ------------------------------------------------ selected and window branches
+
+@pytest.mark.parametrize("T", [1, 33, 64, 65, 128, 200, 256])
+def test_dense_reduction(T):
+    """With n*l' and w covering the whole causal prefix (T <= 256), both the
+    selected and the window branch are dense causal attention."""
+    cfg, x = make_case(T, Hkv=2, G=2, dk=16, dv=8, seed=100 + T)
+    out = run(cfg, x, want_branches=True)
+    causal = np.tril(np.ones((T, T), bool))
+    for g in range(2):
+        heads = slice(2 * g, 2 * g + 2)
+        want = sdpa(x["q"][0, :, heads].transpose(1, 0, 2), x["k"][0, g], x["v"][0, g], causal, 0.25)
+        want = want.transpose(1, 0, 2)
+        np.testing.assert_allclose(out["branches"][0, :, 1, heads], want, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(out["branches"][0, :, 2, heads], want, rtol=1e-11, atol=1e-12)
+
+
+def test_window_is_banded_attention():
+    T, w = 300, 64
+    cfg, x = make_case(T, Hkv=1, G=3, dk=16, dv=8, w=w, seed=7)
+    out = run(cfg, x, want_branches=True)
+    t = np.arange(T)[:, None]
+    s = np.arange(T)[None, :]
+    band = (s <= t) & (s >= t - w + 1)
+    want = sdpa(x["q"][0].transpose(1, 0, 2), x["k"][0, 0], x["v"][0, 0], band, 0.25).transpose(1, 0, 2)
+    np.testing.assert_allclose(out["branches"][0, :, 2], want, rtol=1e-11, atol=1e-12)
+    # selection is total for T <= n*l', so the selected branch is dense causal
+    want = sdpa(x["q"][0].transpose(1, 0, 2), x["k"][0, 0], x["v"][0, 0], s <= t, 0.25).transpose(1, 0, 2)
+    np.testing.assert_allclose(out["branches"][0, :, 1], want, rtol=1e-11, atol=1e-12)
+
+
+def test_selected_branch_is_attention_over_selected_blocks():
+    T, n = 640, 4
+    cfg, x = make_case(T, Hkv=1, G=2, dk=16, dv=8, n=n, w=128, seed=8, act_std=2.0)
+    out = run(cfg, x, want_branches=True)
+    idx = out["idx"][0, 0]  # [T, n]
+    t = np.arange(T)[:, None]
+    s = np.arange(T)[None, :]
+    blk = np.zeros((T, T // 64), bool)
+    for tt in range(T):
+        blk[tt, [j for j in idx[tt] if j >= 0]] = True
+    mask = blk[:, s[0] // 64] & (s <= t)
+    want = sdpa(x["q"][0].transpose(1, 0, 2), x["k"][0, 0], x["v"][0, 0], mask, 0.25).transpose(1, 0, 2)
+    np.testing.assert_allclose(out["branches"][0, :, 1], want, rtol=1e-11, atol=1e-12)
+    assert (mask.sum(1) < (t[:, 0] + 1)).any(), "some rows must really be sparse"
+
+
+def test_idx_injection_is_used():
+    T = 400
+    cfg, x = make_case(T, Hkv=1, G=2, n=4, seed=9)
+    inj = np.full((1, 1, T, 4), -1, np.int32)
+    inj[..., 0] = 0      # only block 0
+    out = run(cfg, x, idx_in=inj, want_branches=True)
+    assert np.array_equal(out["idx"], inj)
+    mask = np.zeros((T, T), bool)
+    mask[:, :64] = True
+    mask &= np.tril(np.ones((T, T), bool))
+    want = sdpa(x["q"][0].transpose(1, 0, 2), x["k"][0, 0], x["v"][0, 0], mask, 0.25).transpose(1, 0, 2)
+    np.testing.assert_allclose(out["branches"][0, :, 1], want, rtol=1e-11, atol=1e-12)
+
+
+# -------------------------------------------------------------------- gating
+
+def test_gates_and_combination():
+    T = 150
+    cfg, x = make_case(T, Hkv=2, G=2, seed=12)
+    out = run(cfg, x, want_branches=True)
+    qt = torch.from_numpy(x["q"][0])                                  # [T,Hq,dk]
+    z = torch.einsum("thd,hcd->thc", qt, torch.from_numpy(x["wg"])) + torch.from_numpy(x["bg"])
+    g = torch.sigmoid(z).numpy()                                      # [T,Hq,3]
+    br = out["branches"][0]                                           # [T,3,Hq,dv]
+    want = np.einsum("thc,tchv->thv", g, br)
+    np.testing.assert_allclose(out["o"][0], want, rtol=1e-12, atol=1e-13)
+
+
+def test_zero_gate_weights_give_sigmoid_bias():
+    T = 90
+    cfg, x = make_case(T, Hkv=1, G=2, seed=13)
+    x["wg"][:] = 0.0
+    out = run(cfg, x, want_branches=True)
+    g = 1 / (1 + np.exp(-x["bg"]))  # [Hq,3]
+    want = np.einsum("hc,tchv->thv", g, out["branches"][0])
+    np.testing.assert_allclose(out["o"][0], want, rtol=1e-13, atol=1e-14)
+
+
+# --------------------------------------------------------------------- decode
+
+def test_decode_equals_prefill_of_truncated_sequence():
+    """Decode at seq_len L over a longer cache equals the last row of a
+    prefill over the first L tokens (compressed entries recomputed there)."""
+    cap = 700
+    cfg, x = make_case(cap, Hkv=2, G=2, B=4, n=6, w=128, seed=14, act_std=2.0)
+    seq = [700, 333, 64, 31]
+    qd = np.stack([x["q"][b, seq[b] - 1] for b in range(4)])
+    d = orc.decode(cfg, seq, qd, x["kc"], x["vc"], x["k"], x["v"], x["wg"], x["bg"])
+    for b, L in enumerate(seq):
+        c2 = orc.Cfg(1, L, 2, 2, 16, 8, n=6, w=128)
+        k, v = x["k"][b:b + 1, :, :L], x["v"][b:b + 1, :, :L]
+        npad = max(64, -(-orc.n_cmp(L) // 64) * 64)
+        kc = orc.compress(k, x["wck"], x["pek"], n_out=npad)
+        vc = orc.compress(v, x["wcv"], x["pev"], n_out=npad)
+        p = orc.forward(c2, x["q"][b:b + 1, :L], kc, vc, k, v, x["wg"], x["bg"])
+        np.testing.assert_allclose(d["o"][b], p["o"][0, L - 1], rtol=1e-12, atol=1e-13)
+        assert np.array_equal(d["idx"][b], p["idx"][0, :, L - 1])
+
+
+# ------------------------------------------------------------ pages' numbers
+
+def test_golden_hyperparameters_are_the_defaults():
+    from sparse_attention_long_07_amd.config import NSAShape
+    gold = json.load(open(os.path.join(GOLDEN, "nsa_hyperparams.json")))
+    s = NSAShape(1, 1, 1, 1, 1, 1)
+    c = orc.Cfg(1, 1, 1, 1, 1, 1)
+    for obj in (s, c):
+        assert obj.l == gold["compression_block_l"]
+        assert obj.d == gold["compression_stride_d"]
+        assert obj.lsel == gold["selection_block_l_prime"]
+        assert obj.n == gold["selected_blocks_n"]
+        assert obj.w == gold["window_w"]
+    # "n includes 1 initial and 2 local blocks": 3 forced blocks on a long row
+    idx = orc.select(c.__class__(1, 65536, 1, 1, 1, 1), 65535, np.zeros(1024))
+    forced = {0, 1022, 1023}
+    assert len(forced) == gold["forced_initial_blocks"] + gold["forced_local_blocks"]
+    assert forced <= set(idx.tolist())
+
+
+def test_golden_decode_token_count():
+    """5,632 tokens per 64k decode step = 4,096 compressed slots + 16 x 64
+    selected + 512 window; 4,095 of the compressed slots hold complete blocks;
+    65,536 / 5,632 is the pages' 11.6x."""
+    from sparse_attention_long_07_amd.config import NSAShape, decode_slots
+    gold = json.load(open(os.path.join(GOLDEN, "decode_64k.json")))
+    T = gold["context_tokens"]
+    s = NSAShape(1, T, 1, 1, 8, 8)
+    slots = decode_slots(s)
+    assert slots["total_slots"] == gold["nsa_tokens_per_decode_step"]
+    assert slots["cmp_valid"] == orc.n_cmp(T) == 4095
+    assert round(gold["full_attention_tokens_per_decode_step"] / slots["total_slots"], 1) == \
+        gold["decode_speedup_up_to"]
+    # the oracle's own row at t = T-1 touches 4,095 compressed blocks, 16
+    # selected blocks of 64 tokens and 512 window tokens
+    cfg, x = make_case(T, Hkv=1, G=1, dk=2, dv=2, seed=15)
+    r = orc.forward_rows(cfg, [0], [T - 1], x["q"][:, T - 1], x["kc"], x["vc"], x["k"], x["v"],
+                         x["wg"], x["bg"])
+    sel = [j for j in r["idx"][0, 0] if j >= 0]
+    assert len(sel) * 64 + 512 + orc.n_cmp(T) == gold["nsa_tokens_per_decode_step"] - 1
+
+
+def test_flop_accounting_context():
+    """Dense causal / NSA algorithmic flops at 64k is close to the pages'
+    measured 9.0x forward speedup (a check of the accounting, not a target)."""
+    from sparse_attention_long_07_amd.config import WORKLOADS, dense_causal_flops, prefill_flops
+    gold = json.load(open(os.path.join(GOLDEN, "decode_64k.json")))
+    s = WORKLOADS["bf16_T65536"].shape
+    f = prefill_flops(s)
+    ratio = dense_causal_flops(s) / f["total"]
+    assert abs(ratio - gold["forward_speedup"]) < 0.5
+    assert abs(f["total"] / 1e12 - 9.568) < 0.01
