@@ -1,0 +1,219 @@
+"""NSA benchmark on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input:
+  * the 64k prefill forward (B=1, T=65536, 4 KV heads x 16 query heads,
+    d_k=192, d_v=128, bf16): compression (S1), compressed attention with
+    block importance (S2), top-n selection (S3), selected + window attention
+    with the gated sum (S4);
+  * one decode step on 32 sequences with 65,536-token caches (same heads).
+Inputs are resident in HBM before timing starts.  Each stage is bracketed by
+HIP events on the stream the kernels run on; the printed JSON line carries
+the prefill throughput (the headline metric), the decode step time, the
+roofline of the dominant kernel and the CPU oracle on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from sparse_attention_long_07_amd import nsa  # noqa: E402
+from sparse_attention_long_07_amd.config import (WORKLOADS, decode_bytes, decode_flops,  # noqa: E402
+                                                 decode_slots, prefill_flops)
+from sparse_attention_long_07_amd.inputs import make_decode, make_prefill  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_FP32_VALU_TFLOPS = 157.3
+PEAK_HBM_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(s, x, flops_total, rows_sample=192, seed=5):
+    """The oracle on a bounded sample of the prefill workload: the full
+    compression of all tokens plus `rows_sample` query positions drawn
+    uniformly (every KV group); extrapolated to the whole workload."""
+    from oracle import oracle as orc
+
+    def np64(t):
+        return t.detach().to(torch.float64).cpu().numpy()
+
+    k64, v64 = np64(x["k"]), np64(x["v"])
+    t0 = time.perf_counter()
+    kc = orc.compress(k64, np64(x["w_ck"]), np64(x["pe_k"]), n_out=s.n_pad, round_bf16=True)
+    vc = orc.compress(v64, np64(x["w_cv"]), np64(x["pe_v"]), n_out=s.n_pad, round_bf16=True)
+    t_cmp = time.perf_counter() - t0
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.integers(0, s.T, rows_sample)).astype(np.int32)
+    qr = np64(x["q"][0, torch.from_numpy(rows).long().to(x["q"].device)])
+    oc = orc.Cfg(s.B, s.T, s.Hkv, s.G, s.dk, s.dv)
+    t0 = time.perf_counter()
+    orc.forward_rows(oc, np.zeros_like(rows), rows, qr, kc, vc, k64, v64, np64(x["w_g"]), np64(x["b_g"]))
+    t_rows = time.perf_counter() - t0
+    est = t_cmp + t_rows * s.T / rows_sample
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": flops_total / est / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "compression of all %d tokens (%.1f s) + %d uniformly drawn query positions x %d KV groups "
+                      "(%.1f s), extrapolated to all %d positions: %.0f s for the step"
+                      % (s.T, t_cmp, rows_sample, s.Hkv, t_rows, s.T, est),
+            "seconds_measured": round(t_cmp + t_rows, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=192)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this NSA build has no multi-GPU path (--gpus %d requested)"
+              % args.gpus, flush=True)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs as a single process on one GPU", flush=True)
+        sys.exit(2)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nsa.lib()
+    wp = WORKLOADS["bf16_T65536"]
+    wd = WORKLOADS["bf16_decode_B32_T65536"]
+    sp, sd = wp.shape, wd.shape
+
+    log("setup: prefill inputs", sp)
+    x = make_prefill(sp, 1002, dev, unit_scaled=wp.unit_scaled)
+    ck = torch.empty((sp.B, sp.Hkv, sp.n_pad, sp.dk), dtype=torch.bfloat16, device=dev)
+    cv = torch.empty((sp.B, sp.Hkv, sp.n_pad, sp.dv), dtype=torch.bfloat16, device=dev)
+    ocmp = torch.empty((sp.B, sp.T, sp.Hq, sp.dv), dtype=torch.bfloat16, device=dev)
+    scores = torch.empty((sp.B, sp.Hkv, sp.T, sp.nb), dtype=torch.float32, device=dev)
+    idx = torch.empty((sp.B, sp.Hkv, sp.T, sp.n), dtype=torch.int32, device=dev)
+    o = torch.empty((sp.B, sp.T, sp.Hq, sp.dv), dtype=torch.bfloat16, device=dev)
+
+    log("setup: decode caches (2 copies)", sd)
+    dec = []
+    for c in range(2):
+        y = make_decode(sd, 1003 + c, dev, unit_scaled=wd.unit_scaled)
+        y["ck"], y["cv"] = nsa.compress_kv(sd, y["k"], y["v"], y["w_ck"], y["pe_k"], y["w_cv"], y["pe_v"])
+        dec.append(y)
+    od = torch.empty((sd.B, sd.Hq, sd.dv), dtype=torch.bfloat16, device=dev)
+    idd = torch.empty((sd.B, sd.Hkv, sd.n), dtype=torch.int32, device=dev)
+    wsd = nsa.workspace(sd, nsa.OP_DECODE, dev)
+    torch.cuda.synchronize()
+
+    stages = ["S1_compress", "S2_compressed_attention", "S3_select", "S4_sparse_window_gate", "decode_step"]
+
+    def step(i, ev=None):
+        def mark(j):
+            if ev is not None:
+                ev[j].record()
+        mark(0)
+        nsa.compress_kv(sp, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"], ck, cv)
+        mark(1)
+        nsa.compressed_attention(sp, x["q"], ck, cv, ocmp, scores)
+        mark(2)
+        nsa.select_topn(sp, scores, idx)
+        mark(3)
+        nsa.sparse_attention(sp, x["q"], x["k"], x["v"], ocmp, idx, x["w_g"], x["b_g"], o)
+        mark(4)
+        y = dec[i % 2]
+        nsa.decode_step(sd, y["seq_lens"], y["q"], y["k"], y["v"], y["ck"], y["cv"], y["w_g"], y["b_g"], None,
+                        od, None, wsd)
+        mark(5)
+
+    log("warmup", args.warmup)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    log("timed steps", args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(5)] for e in evs])  # ms
+    st_ms = per.mean(axis=0)
+    step_ms = float(np.array([e[0].elapsed_time(e[5]) for e in evs]).mean())
+
+    fl = prefill_flops(sp)
+    prefill_ms = float(st_ms[:4].sum())
+    tflops = fl["total"] / (prefill_ms * 1e-3) / 1e12
+    dec_bytes = decode_bytes(sd)
+    dec_us = float(st_ms[4] * 1e3)
+    dec_gbps = dec_bytes / (dec_us * 1e-6) / 1e9
+
+    # roofline of the dominant stage (each stage is one kernel launch, S1 two)
+    work = {
+        "S1_compress": ("alu", fl["compress"], PEAK_FP32_VALU_TFLOPS, "TFLOP/s"),
+        "S2_compressed_attention": ("mfma", fl["compressed"], PEAK_BF16_TFLOPS, "TFLOP/s"),
+        "S3_select": ("hbm", 4 * sp.B * sp.Hkv * sum(t // 64 + 1 for t in range(0, sp.T, 1)) +
+                      4 * sp.B * sp.Hkv * sp.T * sp.n, PEAK_HBM_GBPS, "GB/s"),
+        "S4_sparse_window_gate": ("mfma", fl["selected"] + fl["window"] + fl["gates"], PEAK_BF16_TFLOPS,
+                                  "TFLOP/s"),
+        "decode_step": ("hbm", dec_bytes, PEAK_HBM_GBPS, "GB/s"),
+    }
+    dom = stages[int(np.argmax(st_ms))]
+    bound, units, peak, unit = work[dom]
+    dur_s = st_ms[stages.index(dom)] * 1e-3
+    achieved = units / dur_s / (1e12 if unit == "TFLOP/s" else 1e9)
+    roof = {"bound": bound, "kernel": dom, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": None,
+            "avg_launch_ms": round(float(dur_s * 1e3), 4)}
+
+    res = {
+        "metric": "NSA fwd TFLOP/s @64k prefill",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "NSA prefill forward bf16 T=65536 (B=1, 4 KV x 16 q heads, d_k=192, d_v=128, "
+                               "l=32 d=16 l'=64 n=16 w=512) + NSA decode step bf16 B=32 @65536-token caches",
+                   "global_batch": sp.B, "seq_len": sp.T, "parallelism": "single GPU"},
+        "prefill_ms": round(prefill_ms, 3),
+        "prefill_tokens_per_s": round(sp.T * sp.B / (prefill_ms * 1e-3), 1),
+        "prefill_mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "prefill_algorithmic_tflop": round(fl["total"] / 1e12, 4),
+        "stage_ms": {k: round(float(v), 4) for k, v in zip(stages, st_ms)},
+        "decode_us_per_step": round(dec_us, 2),
+        "decode_tokens_per_s": round(sd.B / (dec_us * 1e-6), 1),
+        "decode_GBps": round(dec_gbps, 1),
+        "decode_hbm_frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
+        "decode_algorithmic_MB": round(dec_bytes / 1e6, 2),
+        "decode_slots_per_group": decode_slots(sd)["total_slots"],
+        "decode_gflop": round(decode_flops(sd) / 1e9, 3),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(sp, x, fl["total"], rows_sample=args.cpu_rows)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,179 @@
+/*
+ * nsa.h -- C ABI of libnsa: Native Sparse Attention (NSA) forward pass and
+ * decode step on AMD MI355X (gfx950).
+ *
+ * NSA passes the same queries through three attention branches and sums
+ * them with per-head gates (deepdaiv newsletter on DeepSeek's NSA,
+ * deepdaiv.stibee.com/p/82, paragraphs on token compression, token selection
+ * and the sliding window; valuable12.com, "AI 모델의 '긴 문장 처리' 한계 돌파,
+ * 딥시크의 새 어텐션 기술 화제", section II for the sizes l=32, d=16, l'=64,
+ * n=16 including 1 initial and 2 local blocks, w=512):
+ *   1. compressed branch: attention over one summary vector per block of l
+ *      tokens taken every d tokens;
+ *   2. selected branch: attention over the n selection blocks of l' tokens
+ *      that rank highest by importance derived from the compressed branch's
+ *      attention probabilities (the first block and the 2 most recent blocks
+ *      are always kept);
+ *   3. sliding window: attention over the w most recent tokens.
+ *
+ * Conventions for every entry point
+ *  - All tensor arguments are DEVICE pointers, row-major, densely packed, in
+ *    the element type given by nsa_config.dtype (fp32 or bf16), except the
+ *    int32 index tensors, the fp32 score tensor and the int32 seq_lens.
+ *    Every tensor pointer must be 16-byte aligned; the workspace 256-byte
+ *    aligned.
+ *  - The caller owns all memory, including the workspace; the library never
+ *    allocates device memory and never synchronizes.  Work is enqueued on
+ *    `stream` (a hipStream_t; NULL = the default stream) in argument order,
+ *    and the call returns once it is enqueued.
+ *  - Arguments are checked on the host before anything is enqueued; on a
+ *    failed check the call returns an error status and enqueues nothing.
+ *    A failed launch returns NSA_ERR_HIP.  Faults inside kernels surface at
+ *    the caller's next synchronization.  No C++ exception crosses the ABI.
+ *  - The library holds no state between calls; calls on different streams
+ *    may run concurrently if their outputs and workspaces do not overlap.
+ *
+ * Layouts (B batch, T tokens, Hkv KV heads, G query heads per KV head,
+ * Hq = Hkv*G, dk/dv head dims, N_cmp = floor((T-32)/16)+1 compressed blocks
+ * (0 if T < 32), N_pad = max(64, N_cmp rounded up to a multiple of 64),
+ * NB = ceil(T/64) selection blocks):
+ *   q      [B][T][Hq][dk]       query head h belongs to KV head h / G
+ *   k      [B][Hkv][T][dk]      v [B][Hkv][T][dv]
+ *   cmp_k  [B][Hkv][N_pad][dk]  cmp_v [B][Hkv][N_pad][dv]  (rows >= N_cmp are 0)
+ *   w_ck   [dk][32*dk]  pe_k [32][dk]   w_cv [dv][32*dv]  pe_v [32][dv]
+ *   w_g    [Hq][3][dk]  b_g  [Hq][3]    gate order: compressed, selected, window
+ *   o      [B][T][Hq][dv]
+ *   idx    [B][Hkv][T][n] int32, ascending, padded with -1
+ *   scores [B][Hkv][T][NB] fp32; entries j > floor(t/64) are -inf
+ */
+#ifndef NSA_H
+#define NSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NSA_OK = 0,
+    NSA_ERR_NULL = -1,      /* a required pointer is NULL */
+    NSA_ERR_SHAPE = -2,     /* a size is out of the supported range */
+    NSA_ERR_DTYPE = -3,     /* dtype is not NSA_FP32 or NSA_BF16 */
+    NSA_ERR_PARAM = -4,     /* l, d, l_sel, n, w or scale unsupported */
+    NSA_ERR_WORKSPACE = -5, /* workspace NULL or smaller than nsa_workspace_bytes */
+    NSA_ERR_HIP = -6,       /* a HIP launch failed */
+    NSA_ERR_ALIGN = -7      /* a pointer is not aligned as required */
+} nsa_status;
+
+typedef enum { NSA_FP32 = 0, NSA_BF16 = 1 } nsa_dtype;
+
+typedef enum {
+    NSA_OP_FORWARD = 0, /* nsa_forward */
+    NSA_OP_SELECT = 1,  /* nsa_select_blocks */
+    NSA_OP_DECODE = 2   /* nsa_decode_step */
+} nsa_op;
+
+/* Problem description.  Supported ranges (checked on every call):
+ *   B >= 1; 1 <= T <= 524288; Hkv >= 1; 1 <= group <= 16;
+ *   d_k, d_v multiples of 8 in [8, 256];
+ *   l = 32, d = 16, l_sel = 64 (the sizes the kernels are built around);
+ *   3 <= n <= 16 (n counts the 3 always-kept blocks); 1 <= w <= 8192;
+ *   scale > 0, or 0 for 1/sqrt(d_k). */
+typedef struct {
+    int32_t B, T, H_kv, group, d_k, d_v;
+    int32_t l, d, l_sel, n, w;
+    float scale;
+    int32_t dtype; /* nsa_dtype */
+} nsa_config;
+
+/* Bytes of workspace `op` needs for `cfg` (0 if cfg is invalid). */
+size_t nsa_workspace_bytes(const nsa_config *cfg, int op);
+
+/* Token compression (deepdaiv newsletter, token compression paragraph: each
+ * block of consecutive tokens is summarised into one vector by a small
+ * learned map with a position encoding of each token in the block).
+ * For every (b, h) and block i < N_cmp:
+ *   cmp_k[b][h][i][c] = sum_{tau<32, e<dk} w_ck[c][tau*dk+e] * (k[b][h][16i+tau][e] + pe_k[tau][e])
+ * and likewise cmp_v from v, w_cv, pe_v.  Rows N_cmp..N_pad-1 are written as 0.
+ * fp32 accumulation; bf16 outputs are rounded to nearest even. */
+nsa_status nsa_compress_kv(const nsa_config *cfg, const void *k, const void *v, const void *w_ck,
+                           const void *pe_k, const void *w_cv, const void *pe_v, void *cmp_k, void *cmp_v,
+                           void *stream);
+
+/* Stage S2 -- compressed attention and block importance (deepdaiv
+ * newsletter, token compression and token selection paragraphs: the block
+ * scores are computed from the compressed tokens).  For each (b, g, t) and
+ * each of the G query heads h of KV head g:
+ *   p_h[i] = softmax over visible blocks i (16i+31 <= t) of scale*q_h.cmp_k[i]
+ *   o_cmp[b][t][h] = sum_i p_h[i] cmp_v[i]          (0 if no block is visible)
+ *   scores[b][g][t][j] = sum_h sum_i overlap(i, j)/16 * p_h[i]
+ * where overlap(i, j) counts the tokens compression block i shares with
+ * selection block j (weights 1,2,2,2,1 over i = 4j-1 .. 4j+3); entries
+ * j > floor(t/64) are -inf, visible-less rows score 0.
+ *   cmp_v / o_cmp: may both be NULL (scores only); o_cmp [B][T][Hq][dv] in
+ *   the config dtype.  scores: required, fp32. */
+nsa_status nsa_compressed_attention(const nsa_config *cfg, const void *q, const void *cmp_k, const void *cmp_v,
+                                    void *o_cmp, float *scores, void *stream);
+
+/* Stage S3 -- top-n block selection (valuable12.com section II: n blocks
+ * including the initial block and 2 local blocks).  For each (b, g, t) with
+ * jc = floor(t/64): blocks {0, jc-1, jc} are always kept; the other
+ * n - #kept are the highest-scoring remaining blocks (ties: lower j), or all
+ * of them when there are no more than that.  idx [B][Hkv][T][n], ascending,
+ * -1 padded.  scores as written by nsa_compressed_attention. */
+nsa_status nsa_select_topn(const nsa_config *cfg, const float *scores, int32_t *idx, void *stream);
+
+/* Stage S4 -- selected-block attention, window attention and the gated sum.
+ * For each (b, t) and head h:
+ *   o_slc = one softmax attention over the tokens tau <= t of the blocks in
+ *           idx[b][h/G][t] (as a set; entries outside 0..floor(t/64) add
+ *           nothing; allinfo.ai.kr DSA explainer, "쉽게 이해하기": the softmax
+ *           normalises over the selected set only);
+ *   o_win = softmax attention over tokens [max(0, t-w+1), t] (deepdaiv
+ *           newsletter, sliding window paragraph);
+ *   o = sigmoid(w_g[h][0].q_h + b_g[h][0]) * o_cmp + sigmoid(w_g[h][1].q_h
+ *       + b_g[h][1]) * o_slc + sigmoid(w_g[h][2].q_h + b_g[h][2]) * o_win.
+ * o_cmp as written by nsa_compressed_attention. */
+nsa_status nsa_sparse_attention(const nsa_config *cfg, const void *q, const void *k, const void *v,
+                                const void *o_cmp, const int32_t *idx, const void *w_g, const void *b_g, void *o,
+                                void *stream);
+
+/* S2 (scores only) followed by S3.  scores_out may be NULL (the workspace
+ * holds them then); idx_out is required. */
+nsa_status nsa_select_blocks(const nsa_config *cfg, const void *q, const void *cmp_k, float *scores_out,
+                             int32_t *idx_out, void *ws, size_t ws_bytes, void *stream);
+
+/* Full NSA forward for every position of every sequence: S2, S3 (unless
+ * idx_in is given), S4.  idx_in: if non-NULL, these block lists
+ * ([B][Hkv][T][n]) replace the selection.  idx_out / scores_out: optional
+ * copies of the indices used / the scores (scores exist only when
+ * selecting).  cmp_k/cmp_v as written by nsa_compress_kv.  The workspace
+ * holds o_cmp and, when not supplied by the caller, scores and indices. */
+nsa_status nsa_forward(const nsa_config *cfg, const void *q, const void *k, const void *v, const void *cmp_k,
+                       const void *cmp_v, const void *w_g, const void *b_g, const int32_t *idx_in, void *o,
+                       int32_t *idx_out, float *scores_out, void *ws, size_t ws_bytes, void *stream);
+
+/* One decode step for B sequences (valuable12.com section III.3: at 64k
+ * context a step reads 5,632 tokens' keys and values instead of 65,536).
+ * cfg->T is the cache capacity.  Sequence b holds seq_lens[b] tokens
+ * (device int32 [B], each in 1..T; values outside are clamped into that
+ * range); its new query q[b] ([B][Hq][dk]) is the last cached token, so the
+ * row computed is the forward row t = seq_lens[b]-1 over the caches
+ * k_cache/v_cache ([B][Hkv][T][dk|dv]) and the compressed caches
+ * cmp_k/cmp_v ([B][Hkv][N_pad][dk|dv], complete for every block with
+ * 16i+31 < seq_lens[b]).  o: [B][Hq][dv]; idx_in/idx_out: [B][Hkv][n]. */
+nsa_status nsa_decode_step(const nsa_config *cfg, const int32_t *seq_lens, const void *q, const void *k_cache,
+                           const void *v_cache, const void *cmp_k, const void *cmp_v, const void *w_g,
+                           const void *b_g, const int32_t *idx_in, void *o, int32_t *idx_out, void *ws,
+                           size_t ws_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *nsa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NSA_H */

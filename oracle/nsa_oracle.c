@@ -7,7 +7,8 @@
  *
  * Arithmetic is IEEE double throughout.  Loops are scalar and follow the
  * order in which the pages describe the method; the only parallelism is an
- * OpenMP loop over independent (batch, query position, KV group) rows.
+ * OpenMP loop over independent items (compressed blocks; (batch, query
+ * position, KV group) rows), which leaves every sum in source order.
  *
  * Sources (web pages, cited by title and section):
  *  [deepdaiv]  deepdaiv newsletter on DeepSeek's Native Sparse Attention
@@ -84,11 +85,13 @@ void orc_compress(int B, int H, int T, int dim, int l, int d, int n_out, int rou
                   const double *x, const double *W, const double *PE, double *out)
 {
     int ncmp = orc_n_cmp(T, l, d);
+    /* every (b, h, i) summary is independent of the others */
+#pragma omp parallel for collapse(3) schedule(static)
     for (int b = 0; b < B; b++)
-        for (int h = 0; h < H; h++) {
-            const double *xs = x + ((size_t)b * H + h) * (size_t)T * dim;
-            double *os = out + ((size_t)b * H + h) * (size_t)n_out * dim;
-            for (int i = 0; i < n_out; i++)
+        for (int h = 0; h < H; h++)
+            for (int i = 0; i < n_out; i++) {
+                const double *xs = x + ((size_t)b * H + h) * (size_t)T * dim;
+                double *os = out + ((size_t)b * H + h) * (size_t)n_out * dim;
                 for (int c = 0; c < dim; c++) {
                     double acc = 0.0;
                     if (i < ncmp) {

@@ -1,0 +1,308 @@
+// C ABI of libnsa: argument checks, workspace layout and launch order.
+// Every check runs on the host before anything is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include <initializer_list>
+
+#include "nsa_internal.h"
+
+using namespace nsa;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+nsa_status check_config(const nsa_config *c, Dims *out)
+{
+    if (!c) return NSA_ERR_NULL;
+    if (c->dtype != NSA_FP32 && c->dtype != NSA_BF16) return NSA_ERR_DTYPE;
+    if (c->B < 1 || c->T < 1 || c->T > 524288 || c->H_kv < 1 || c->group < 1 || c->group > 16)
+        return NSA_ERR_SHAPE;
+    if (c->d_k < 8 || c->d_k > 256 || c->d_k % 8 || c->d_v < 8 || c->d_v > 256 || c->d_v % 8)
+        return NSA_ERR_SHAPE;
+    if ((long)c->B * c->H_kv * c->group > (1L << 20)) return NSA_ERR_SHAPE;
+    if (c->l != 32 || c->d != 16 || c->l_sel != 64) return NSA_ERR_PARAM;
+    if (c->n < 3 || c->n > 16 || c->w < 1 || c->w > 8192) return NSA_ERR_PARAM;
+    if (!(c->scale >= 0.f) || isinf(c->scale)) return NSA_ERR_PARAM;
+    if (out) {
+        Dims &d = *out;
+        d.B = c->B;
+        d.T = c->T;
+        d.Hkv = c->H_kv;
+        d.G = c->group;
+        d.Hq = c->H_kv * c->group;
+        d.dk = c->d_k;
+        d.dv = c->d_v;
+        d.n = c->n;
+        d.w = c->w;
+        d.ncmp = c->T < 32 ? 0 : (c->T - 32) / 16 + 1;
+        d.npad = d.ncmp <= 64 ? 64 : (d.ncmp + 63) / 64 * 64;
+        d.nb = (c->T + 63) / 64;
+        d.scale = c->scale > 0.f ? c->scale : 1.f / sqrtf((float)c->d_k);
+        d.dtype = c->dtype;
+    }
+    return NSA_OK;
+}
+
+// Workspace regions (each 256-byte aligned), for R rows per sequence:
+//   ocmp   [B][R][Hq][dv]  storage dtype  compressed-branch output
+//   scores [B][Hkv][R][nb] fp32  importance scores (when the caller passes none)
+//   idx    [B][Hkv][R][n]  int32 selected blocks (when the caller passes none)
+struct Layout {
+    size_t ocmp, scores, idx, total;
+};
+
+Layout layout(const Dims &d, long R)
+{
+    Layout L;
+    size_t off = 0;
+    L.ocmp = off;
+    off = align_up(off + (d.dtype == NSA_FP32 ? 4 : 2) * (size_t)d.B * R * d.Hq * d.dv);
+    L.scores = off;
+    off = align_up(off + sizeof(float) * (size_t)d.B * d.Hkv * R * d.nb);
+    L.idx = off;
+    off = align_up(off + sizeof(int32_t) * (size_t)d.B * d.Hkv * R * d.n);
+    L.total = off;
+    return L;
+}
+
+nsa_status check_ws(const Dims &d, long R, void *ws, size_t ws_bytes, Layout *L)
+{
+    *L = layout(d, R);
+    if (!ws || ws_bytes < L->total) return NSA_ERR_WORKSPACE;
+    if ((uintptr_t)ws % kAlign) return NSA_ERR_ALIGN;
+    return NSA_OK;
+}
+
+nsa_status hip_status(hipError_t e) { return e == hipSuccess ? NSA_OK : NSA_ERR_HIP; }
+
+#define NSA_TRY(expr)                              \
+    do {                                           \
+        nsa_status st_ = hip_status(expr);         \
+        if (st_ != NSA_OK) return st_;             \
+    } while (0)
+
+RowArgs row_args(const Dims &d, long R)
+{
+    RowArgs a;
+    memset(&a, 0, sizeof a);
+    a.d = d;
+    a.R = (int)R;
+    return a;
+}
+
+// Row arguments of a prefill call: every position of every sequence.
+RowArgs prefill_args(const Dims &d, const void *q)
+{
+    RowArgs a = row_args(d, d.T);
+    a.q = q;
+    a.q_sb = (long)d.T * d.Hq * d.dk;
+    a.q_sr = (long)d.Hq * d.dk;
+    a.o_sb = (long)d.T * d.Hq * d.dv;
+    a.o_sr = (long)d.Hq * d.dv;
+    return a;
+}
+
+bool all_aligned(std::initializer_list<const void *> ps)
+{
+    for (const void *p : ps)
+        if (!aligned16(p)) return false;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nsa_workspace_bytes(const nsa_config *cfg, int op)
+{
+    Dims d;
+    if (check_config(cfg, &d) != NSA_OK) return 0;
+    switch (op) {
+    case NSA_OP_FORWARD:
+    case NSA_OP_SELECT:
+        return layout(d, d.T).total;
+    case NSA_OP_DECODE:
+        return layout(d, 1).total;
+    default:
+        return 0;
+    }
+}
+
+nsa_status nsa_compress_kv(const nsa_config *cfg, const void *k, const void *v, const void *w_ck, const void *pe_k,
+                           const void *w_cv, const void *pe_v, void *cmp_k, void *cmp_v, void *stream)
+{
+    Dims d;
+    nsa_status st = check_config(cfg, &d);
+    if (st != NSA_OK) return st;
+    if (!k || !v || !w_ck || !pe_k || !w_cv || !pe_v || !cmp_k || !cmp_v) return NSA_ERR_NULL;
+    const void *ptrs[] = {k, v, w_ck, pe_k, w_cv, pe_v, cmp_k, cmp_v};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return NSA_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    NSA_TRY(launch_compress_generic(d, k, w_ck, pe_k, cmp_k, d.dk, s));
+    NSA_TRY(launch_compress_generic(d, v, w_cv, pe_v, cmp_v, d.dv, s));
+    return NSA_OK;
+}
+
+nsa_status nsa_compressed_attention(const nsa_config *cfg, const void *q, const void *cmp_k, const void *cmp_v,
+                                    void *o_cmp, float *scores, void *stream)
+{
+    Dims d;
+    nsa_status st = check_config(cfg, &d);
+    if (st != NSA_OK) return st;
+    if (!q || !cmp_k || !scores || (!cmp_v) != (!o_cmp)) return NSA_ERR_NULL;
+    if (!all_aligned({q, cmp_k, cmp_v, o_cmp, scores})) return NSA_ERR_ALIGN;
+    RowArgs a = prefill_args(d, q);
+    a.kc = cmp_k;
+    a.vc = cmp_v;
+    a.ocmp = o_cmp;
+    a.scores = scores;
+    return hip_status(launch_cmp_attn_generic(a, o_cmp != nullptr, (hipStream_t)stream));
+}
+
+nsa_status nsa_select_topn(const nsa_config *cfg, const float *scores, int32_t *idx, void *stream)
+{
+    Dims d;
+    nsa_status st = check_config(cfg, &d);
+    if (st != NSA_OK) return st;
+    if (!scores || !idx) return NSA_ERR_NULL;
+    if (!all_aligned({scores, idx})) return NSA_ERR_ALIGN;
+    RowArgs a = prefill_args(d, nullptr);
+    a.scores = (float *)scores;
+    a.idx_sel = idx;
+    return hip_status(launch_select_generic(a, (hipStream_t)stream));
+}
+
+nsa_status nsa_sparse_attention(const nsa_config *cfg, const void *q, const void *k, const void *v,
+                                const void *o_cmp, const int32_t *idx, const void *w_g, const void *b_g, void *o,
+                                void *stream)
+{
+    Dims d;
+    nsa_status st = check_config(cfg, &d);
+    if (st != NSA_OK) return st;
+    if (!q || !k || !v || !o_cmp || !idx || !w_g || !b_g || !o) return NSA_ERR_NULL;
+    if (!all_aligned({q, k, v, o_cmp, idx, w_g, b_g, o})) return NSA_ERR_ALIGN;
+    RowArgs a = prefill_args(d, q);
+    a.k = k;
+    a.v = v;
+    a.ocmp = (void *)o_cmp;
+    a.idx = idx;
+    a.wg = w_g;
+    a.bg = b_g;
+    a.o = o;
+    return hip_status(launch_sparse_generic(a, (hipStream_t)stream));
+}
+
+nsa_status nsa_select_blocks(const nsa_config *cfg, const void *q, const void *cmp_k, float *scores_out,
+                             int32_t *idx_out, void *ws, size_t ws_bytes, void *stream)
+{
+    Dims d;
+    nsa_status st = check_config(cfg, &d);
+    if (st != NSA_OK) return st;
+    if (!q || !cmp_k || !idx_out) return NSA_ERR_NULL;
+    if (!all_aligned({q, cmp_k, scores_out, idx_out})) return NSA_ERR_ALIGN;
+    Layout L;
+    if ((st = check_ws(d, d.T, ws, ws_bytes, &L)) != NSA_OK) return st;
+    float *scores = scores_out ? scores_out : (float *)((char *)ws + L.scores);
+    if ((st = nsa_compressed_attention(cfg, q, cmp_k, nullptr, nullptr, scores, stream)) != NSA_OK) return st;
+    return nsa_select_topn(cfg, scores, idx_out, stream);
+}
+
+nsa_status nsa_forward(const nsa_config *cfg, const void *q, const void *k, const void *v, const void *cmp_k,
+                       const void *cmp_v, const void *w_g, const void *b_g, const int32_t *idx_in, void *o,
+                       int32_t *idx_out, float *scores_out, void *ws, size_t ws_bytes, void *stream)
+{
+    Dims d;
+    nsa_status st = check_config(cfg, &d);
+    if (st != NSA_OK) return st;
+    if (!q || !k || !v || !cmp_k || !cmp_v || !w_g || !b_g || !o) return NSA_ERR_NULL;
+    if (!all_aligned({q, k, v, cmp_k, cmp_v, w_g, b_g, idx_in, o, idx_out, scores_out})) return NSA_ERR_ALIGN;
+    Layout L;
+    if ((st = check_ws(d, d.T, ws, ws_bytes, &L)) != NSA_OK) return st;
+    char *w = (char *)ws;
+    hipStream_t s = (hipStream_t)stream;
+    void *ocmp = w + L.ocmp;
+    float *scores = scores_out ? scores_out : (float *)(w + L.scores);
+    if ((st = nsa_compressed_attention(cfg, q, cmp_k, cmp_v, ocmp, scores, stream)) != NSA_OK) return st;
+    const int32_t *idx = idx_in;
+    if (idx_in) {
+        if (idx_out)
+            NSA_TRY(hipMemcpyAsync(idx_out, idx_in, sizeof(int32_t) * (size_t)d.B * d.Hkv * d.T * d.n,
+                                   hipMemcpyDeviceToDevice, s));
+    } else {
+        int32_t *sel = idx_out ? idx_out : (int32_t *)(w + L.idx);
+        if ((st = nsa_select_topn(cfg, scores, sel, stream)) != NSA_OK) return st;
+        idx = sel;
+    }
+    return nsa_sparse_attention(cfg, q, k, v, ocmp, idx, w_g, b_g, o, stream);
+}
+
+nsa_status nsa_decode_step(const nsa_config *cfg, const int32_t *seq_lens, const void *q, const void *k_cache,
+                           const void *v_cache, const void *cmp_k, const void *cmp_v, const void *w_g,
+                           const void *b_g, const int32_t *idx_in, void *o, int32_t *idx_out, void *ws,
+                           size_t ws_bytes, void *stream)
+{
+    Dims d;
+    nsa_status st = check_config(cfg, &d);
+    if (st != NSA_OK) return st;
+    if (!seq_lens || !q || !k_cache || !v_cache || !cmp_k || !cmp_v || !w_g || !b_g || !o) return NSA_ERR_NULL;
+    const void *ptrs[] = {seq_lens, q, k_cache, v_cache, cmp_k, cmp_v, w_g, b_g, idx_in, o, idx_out};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return NSA_ERR_ALIGN;
+    Layout L;
+    if ((st = check_ws(d, 1, ws, ws_bytes, &L)) != NSA_OK) return st;
+    char *w = (char *)ws;
+    hipStream_t s = (hipStream_t)stream;
+    RowArgs a = row_args(d, 1);
+    a.seq_lens = seq_lens;
+    a.q = q;
+    a.q_sb = (long)d.Hq * d.dk;
+    a.q_sr = 0;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.kc = cmp_k;
+    a.vc = cmp_v;
+    a.wg = w_g;
+    a.bg = b_g;
+    a.ocmp = w + L.ocmp;
+    a.scores = (float *)(w + L.scores);
+    a.idx_sel = idx_out ? idx_out : (int32_t *)(w + L.idx);
+    a.o = o;
+    a.o_sb = (long)d.Hq * d.dv;
+    a.o_sr = 0;
+    NSA_TRY(launch_cmp_attn_generic(a, true, s));
+    if (idx_in) {
+        a.idx = idx_in;
+        if (idx_out)
+            NSA_TRY(hipMemcpyAsync(idx_out, idx_in, sizeof(int32_t) * (size_t)d.B * d.Hkv * d.n,
+                                   hipMemcpyDeviceToDevice, s));
+    } else {
+        NSA_TRY(launch_select_generic(a, s));
+        a.idx = a.idx_sel;
+    }
+    NSA_TRY(launch_sparse_generic(a, s));
+    return NSA_OK;
+}
+
+const char *nsa_status_string(int status)
+{
+    switch (status) {
+    case NSA_OK: return "ok";
+    case NSA_ERR_NULL: return "a required pointer is NULL";
+    case NSA_ERR_SHAPE: return "a size is out of the supported range";
+    case NSA_ERR_DTYPE: return "unsupported dtype";
+    case NSA_ERR_PARAM: return "unsupported method parameter (l, d, l_sel, n, w or scale)";
+    case NSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case NSA_ERR_HIP: return "HIP launch failed";
+    case NSA_ERR_ALIGN: return "pointer not aligned as required";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

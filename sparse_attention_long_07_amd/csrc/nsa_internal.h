@@ -1,0 +1,66 @@
+// Internal declarations shared by the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nsa.h"
+
+namespace nsa {
+
+typedef uint16_t bf16_t;
+
+// bf16 <-> fp32.  bf16 is the upper half of an IEEE single; conversion to
+// bf16 rounds to nearest, ties to even (NaN maps to a quiet NaN).
+__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ __forceinline__ bf16_t f2bf(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16_t x) { return bf2f(x); }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float x) { return f2bf(x); }
+
+// Resolved problem sizes (from nsa_config after validation).
+struct Dims {
+    int B, T, Hkv, G, Hq, dk, dv, n, w;
+    int ncmp;   // complete compression blocks of a length-T sequence
+    int npad;   // compressed slots per (b, h)
+    int nb;     // selection blocks, ceil(T/64)
+    float scale;
+    int dtype;
+};
+
+// Arguments of the per-row kernels.  A "row" is one query position of one
+// sequence: prefill rows are r = 0..T-1 with t = r; a decode step has one row
+// per sequence with t = clamp(seq_lens[b], 1, T) - 1.
+struct RowArgs {
+    Dims d;
+    int R;                      // rows per sequence
+    const int32_t *seq_lens;    // decode: device [B]; prefill: nullptr
+    const void *q;              // row (b, r) head h at q + b*q_sb + r*q_sr + h*dk
+    long q_sb, q_sr;
+    const void *k, *v;          // [B][Hkv][T][dk|dv]
+    const void *kc, *vc;        // [B][Hkv][npad][dk|dv]
+    const void *wg, *bg;        // [Hq][3][dk], [Hq][3]
+    void *ocmp;                 // [B][R][Hq][dv] compressed-branch output, storage dtype
+    float *scores;              // [B][Hkv][R][nb]
+    const int32_t *idx;         // [B][Hkv][R][n] blocks used by the sparse kernel
+    int32_t *idx_sel;           // [B][Hkv][R][n] written by the selector
+    void *o;                    // row (b, r) head h at o + b*o_sb + r*o_sr + h*dv
+    long o_sb, o_sr;
+};
+
+// Generic kernels: plain VALU code, any supported shape, fp32 or bf16 storage.
+hipError_t launch_compress_generic(const Dims &d, const void *x, const void *W, const void *PE, void *out,
+                                   int dim, hipStream_t s);
+hipError_t launch_cmp_attn_generic(const RowArgs &a, bool with_v, hipStream_t s);
+hipError_t launch_select_generic(const RowArgs &a, hipStream_t s);
+hipError_t launch_sparse_generic(const RowArgs &a, hipStream_t s);
+
+}  // namespace nsa

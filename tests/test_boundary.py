@@ -1,0 +1,151 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/nsa.h declares, sizes workspaces, and rejects bad arguments on the
+host before anything reaches HIP.  Fake device pointers are never
+dereferenced because every call here fails its host-side checks."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_long_07_amd import nsa
+from sparse_attention_long_07_amd.config import WORKLOADS, NSAShape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "nsa.h")
+
+NULL, SHAPE, DTYPE, PARAM, WS, HIP, ALIGN = -1, -2, -3, -4, -5, -6, -7
+FAKE = ctypes.c_void_p(0x10000)        # 16-byte aligned, never dereferenced
+MIS = ctypes.c_void_p(0x10004)         # misaligned
+
+
+def declared_functions():
+    text = open(HDR).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(nsa_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    L = nsa.lib()
+    decl = declared_functions()
+    assert set(decl) == set(nsa.EXPORTS)
+    for name in decl:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = nsa.lib()
+    for code in [0, NULL, SHAPE, DTYPE, PARAM, WS, HIP, ALIGN]:
+        assert L.nsa_status_string(code).decode() != "unknown status"
+    assert L.nsa_status_string(12345).decode() == "unknown status"
+
+
+def cfg(**kw):
+    s = NSAShape(1, 256, 2, 4, 64, 32, "bf16")
+    c = nsa.config(s)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_workspace_bytes():
+    for w in WORKLOADS.values():
+        s = w.shape
+        f = nsa.workspace_bytes(s, nsa.OP_FORWARD)
+        d = nsa.workspace_bytes(s, nsa.OP_DECODE)
+        assert f >= s.esize * s.B * s.T * s.Hq * s.dv    # compressed-branch output
+        assert d >= s.esize * s.B * s.Hq * s.dv
+        assert f % 256 == 0 and d % 256 == 0
+    L = nsa.lib()
+    assert L.nsa_workspace_bytes(ctypes.byref(cfg(T=0)), 0) == 0
+    assert L.nsa_workspace_bytes(ctypes.byref(cfg()), 99) == 0
+    assert L.nsa_workspace_bytes(None, 0) == 0
+
+
+BAD_CONFIGS = [
+    (dict(dtype=2), DTYPE),
+    (dict(B=0), SHAPE), (dict(T=0), SHAPE), (dict(T=524289), SHAPE), (dict(H_kv=0), SHAPE),
+    (dict(group=0), SHAPE), (dict(group=17), SHAPE), (dict(d_k=12), SHAPE), (dict(d_k=264), SHAPE),
+    (dict(d_v=0), SHAPE),
+    (dict(l=16), PARAM), (dict(d=8), PARAM), (dict(l_sel=32), PARAM), (dict(n=2), PARAM), (dict(n=17), PARAM),
+    (dict(w=0), PARAM), (dict(w=8193), PARAM), (dict(scale=-1.0), PARAM), (dict(scale=float("nan")), PARAM),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_CONFIGS)
+def test_bad_config_rejected_everywhere(kw, code):
+    L = nsa.lib()
+    c = ctypes.byref(cfg(**kw))
+    f = [FAKE] * 16
+    assert L.nsa_compress_kv(c, *f[:8], None) == code
+    assert L.nsa_select_blocks(c, f[0], f[1], None, f[2], f[3], 1 << 40, None) == code
+    assert L.nsa_forward(c, *f[:7], None, f[0], None, None, f[1], 1 << 40, None) == code
+    assert L.nsa_decode_step(c, *f[:8], None, f[0], None, f[1], 1 << 40, None) == code
+
+
+def test_null_config():
+    L = nsa.lib()
+    assert L.nsa_compress_kv(None, *[FAKE] * 8, None) == NULL
+    assert L.nsa_forward(None, *[FAKE] * 12, 1 << 40, None) == NULL
+
+
+@pytest.mark.parametrize("pos", range(8))
+def test_compress_null_and_misaligned(pos):
+    L = nsa.lib()
+    c = ctypes.byref(cfg())
+    args = [FAKE] * 8
+    args[pos] = None
+    assert L.nsa_compress_kv(c, *args, None) == NULL
+    args[pos] = MIS
+    assert L.nsa_compress_kv(c, *args, None) == ALIGN
+
+
+@pytest.mark.parametrize("pos", range(8))
+def test_forward_required_pointers(pos):
+    L = nsa.lib()
+    c = ctypes.byref(cfg())
+    args = [FAKE] * 8           # q k v cmp_k cmp_v w_g b_g | o
+    args[pos] = None
+    q, k, v, ck, cv, wg, bg, o = args
+    assert L.nsa_forward(c, q, k, v, ck, cv, wg, bg, None, o, None, None, FAKE, 1 << 40, None) == NULL
+
+
+def test_forward_workspace_checks():
+    L = nsa.lib()
+    c = cfg()
+    need = L.nsa_workspace_bytes(ctypes.byref(c), 0)
+    f = [FAKE] * 7
+    assert L.nsa_forward(ctypes.byref(c), *f, None, FAKE, None, None, None, need, None) == WS
+    assert L.nsa_forward(ctypes.byref(c), *f, None, FAKE, None, None, FAKE, need - 1, None) == WS
+    assert L.nsa_forward(ctypes.byref(c), *f, None, FAKE, None, None, ctypes.c_void_p(0x10010), need,
+                         None) == ALIGN
+    # optional outputs are checked for alignment too
+    assert L.nsa_forward(ctypes.byref(c), *f, MIS, FAKE, None, None, FAKE, 0, None) == ALIGN
+
+
+def test_select_and_decode_checks():
+    L = nsa.lib()
+    c = cfg()
+    assert L.nsa_select_blocks(ctypes.byref(c), FAKE, FAKE, None, None, FAKE, 1 << 40, None) == NULL
+    assert L.nsa_select_blocks(ctypes.byref(c), FAKE, FAKE, None, FAKE, FAKE, 0, None) == WS
+    need = L.nsa_workspace_bytes(ctypes.byref(c), 2)
+    f = [FAKE] * 7
+    assert L.nsa_decode_step(ctypes.byref(c), None, *f, None, FAKE, None, FAKE, need, None) == NULL
+    assert L.nsa_decode_step(ctypes.byref(c), FAKE, *f, None, FAKE, None, FAKE, need - 256, None) == WS
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    s = NSAShape(1, 64, 1, 2, 16, 16, "fp32")
+    t = torch.zeros(1)
+    with pytest.raises(ValueError):
+        nsa.compress_kv(s, t, t, t, t, t, t)
+
+
+def test_binding_arity_matches_header():
+    """Each ctypes prototype has as many parameters as the header declares."""
+    text = open(HDR).read()
+    L = nsa.lib()
+    for name in declared_functions():
+        m = re.search(r"\b%s\s*\(([^)]*)\)" % name, text, re.S)
+        nparams = len([p for p in m.group(1).split(",") if p.strip()])
+        assert len(getattr(L, name).argtypes) == nparams, name

@@ -1,0 +1,247 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on the same
+seeded inputs.  Small cases are compared element by element; the full-size
+workloads on sampled rows that the oracle computes one by one."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from sparse_attention_long_07_amd import nsa
+from sparse_attention_long_07_amd.config import BF16, FP32, WORKLOADS, NSAShape
+from sparse_attention_long_07_amd.inputs import make_decode, make_prefill, torch_dtype
+from tests.parity_util import check_idx, compressed_close, np64, ocfg, oracle_compress, out_tol
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    nsa.lib()
+
+
+SMALL = [
+    ("fp32_T1024_scaled", NSAShape(1, 1024, 1, 4, 64, 64, FP32), True),
+    ("fp32_T1024_unscaled", NSAShape(1, 1024, 1, 4, 64, 64, FP32), False),
+    ("bf16_T777_g16", NSAShape(1, 777, 2, 16, 192, 128), False),
+    ("bf16_T1024_n6_w128", NSAShape(1, 1024, 2, 16, 192, 128, n=6, w=128), False),
+    ("bf16_T2000_n16", NSAShape(1, 2000, 1, 16, 192, 128), False),
+    ("bf16_odd_dims_B2", NSAShape(2, 333, 3, 3, 24, 40, n=5, w=100), False),
+    ("fp32_T1", NSAShape(1, 1, 1, 1, 8, 8, FP32), True),
+    ("bf16_T31", NSAShape(1, 31, 1, 2, 16, 16), False),
+    ("bf16_T64_g16", NSAShape(1, 64, 1, 16, 64, 64), False),
+    ("fp32_T300_g5_w64", NSAShape(1, 300, 2, 5, 32, 16, FP32, n=3, w=64), False),
+]
+
+
+def _inputs(s, seed, scaled):
+    return make_prefill(s, seed, "cuda", unit_scaled=scaled)
+
+
+@pytest.mark.parametrize("name,s,scaled", SMALL, ids=[c[0] for c in SMALL])
+def test_compress_parity(name, s, scaled):
+    say("compress", name, s)
+    x = _inputs(s, 1, scaled)
+    ck, cv = nsa.compress_kv(s, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"])
+    torch.cuda.synchronize()
+    for got, src, W, PE in ((ck, "k", "w_ck", "pe_k"), (cv, "v", "w_cv", "pe_v")):
+        ref = oracle_compress(s, x[src], x[W], x[PE])
+        g = np64(got)
+        assert g.shape == ref.shape
+        assert np.all(g[:, :, s.n_cmp:] == 0)
+        assert compressed_close(s, g, ref), float(np.abs(g - ref).max())
+
+
+@pytest.mark.parametrize("name,s,scaled", SMALL, ids=[c[0] for c in SMALL])
+def test_select_and_forward_parity(name, s, scaled):
+    say("forward", name, s)
+    x = _inputs(s, 2, scaled)
+    dt = torch_dtype(s)
+    kc = oracle_compress(s, x["k"], x["w_ck"], x["pe_k"])
+    vc = oracle_compress(s, x["v"], x["w_cv"], x["pe_v"])
+    ref = orc.forward(ocfg(s), np64(x["q"]), kc, vc, np64(x["k"]), np64(x["v"]), np64(x["w_g"]), np64(x["b_g"]),
+                      want_scores=True)
+    kc_d = torch.from_numpy(kc).to(dt).cuda()
+    vc_d = torch.from_numpy(vc).to(dt).cuda()
+
+    # selection with the oracle's compressed keys injected
+    idx, scores = nsa.select_blocks(s, x["q"], kc_d, want_scores=True)
+    torch.cuda.synchronize()
+    sc = np64(scores)
+    fin = np.isfinite(ref["scores"])
+    assert np.array_equal(fin, np.isfinite(sc))
+    np.testing.assert_allclose(sc[fin], ref["scores"][fin], rtol=1e-4, atol=2e-6)
+    tt = np.tile(np.arange(s.T), s.B * s.Hkv)
+    n_exact, n_rows = check_idx(s, ref["scores"].reshape(-1, s.nb), tt, ref["idx"].reshape(-1, s.n),
+                                idx.cpu().numpy().reshape(-1, s.n))
+    say("  idx rows checked exactly: %d / %d" % (n_exact, n_rows))
+
+    # output with the oracle's indices injected
+    idx_ref = torch.from_numpy(ref["idx"]).cuda()
+    o = nsa.forward(s, x["q"], x["k"], x["v"], kc_d, vc_d, x["w_g"], x["b_g"], idx_in=idx_ref)
+    torch.cuda.synchronize()
+    err = np.abs(np64(o) - ref["o"]).max()
+    tol = out_tol(s, ref["o"])
+    say("  max|o-o_ref| = %.3g (tol %.3g)" % (err, tol))
+    assert err <= tol
+
+    # the whole path on the GPU's own compression and selection
+    ck, cv = nsa.compress_kv(s, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"])
+    o2, idx2 = nsa.forward(s, x["q"], x["k"], x["v"], ck, cv, x["w_g"], x["b_g"], want_idx=True)
+    torch.cuda.synchronize()
+    check_idx(s, ref["scores"].reshape(-1, s.nb), tt, ref["idx"].reshape(-1, s.n),
+              idx2.cpu().numpy().reshape(-1, s.n))
+    ref2 = orc.forward(ocfg(s), np64(x["q"]), kc, vc, np64(x["k"]), np64(x["v"]), np64(x["w_g"]), np64(x["b_g"]),
+                       idx_in=idx2.cpu().numpy())
+    assert np.abs(np64(o2) - ref2["o"]).max() <= out_tol(s, ref2["o"])
+
+
+def test_forward_is_deterministic():
+    s = NSAShape(1, 1500, 2, 16, 192, 128)
+    say("determinism", s)
+    x = _inputs(s, 3, False)
+    ck, cv = nsa.compress_kv(s, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"])
+    outs = [nsa.forward(s, x["q"], x["k"], x["v"], ck, cv, x["w_g"], x["b_g"], want_idx=True, want_scores=True)
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, i, sc in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(i, outs[0][1]) and torch.equal(sc, outs[0][2])
+
+
+def test_select_matches_forward_selection():
+    s = NSAShape(1, 2500, 2, 16, 192, 128)
+    say("select vs forward", s)
+    x = _inputs(s, 4, False)
+    ck, cv = nsa.compress_kv(s, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"])
+    i1 = nsa.select_blocks(s, x["q"], ck)
+    _, i2 = nsa.forward(s, x["q"], x["k"], x["v"], ck, cv, x["w_g"], x["b_g"], want_idx=True)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2)
+
+
+DECODE_SMALL = [
+    ("bf16_cap1500", NSAShape(4, 1500, 2, 16, 192, 128), [1500, 777, 64, 1]),
+    ("fp32_cap1024", NSAShape(3, 1024, 1, 4, 64, 64, FP32), [1024, 33, 300]),
+    ("bf16_odd", NSAShape(2, 400, 3, 3, 24, 40, n=5, w=100), [400, 129]),
+]
+
+
+@pytest.mark.parametrize("name,s,seq", DECODE_SMALL, ids=[c[0] for c in DECODE_SMALL])
+def test_decode_parity(name, s, seq):
+    say("decode", name, s, seq)
+    x = make_decode(s, 5, "cuda", unit_scaled=False, seq_lens=seq)
+    dt = torch_dtype(s)
+    kc = oracle_compress(s, x["k"], x["w_ck"], x["pe_k"])
+    vc = oracle_compress(s, x["v"], x["w_cv"], x["pe_v"])
+    oc = ocfg(s)
+    tl = np.array(seq) - 1
+    ref = orc.forward_rows(oc, np.arange(s.B), tl, np64(x["q"]), kc, vc, np64(x["k"]), np64(x["v"]),
+                           np64(x["w_g"]), np64(x["b_g"]), want_scores=True)
+    kc_d = torch.from_numpy(kc).to(dt).cuda()
+    vc_d = torch.from_numpy(vc).to(dt).cuda()
+    o, idx = nsa.decode_step(s, x["seq_lens"], x["q"], x["k"], x["v"], kc_d, vc_d, x["w_g"], x["b_g"],
+                             want_idx=True)
+    torch.cuda.synchronize()
+    check_idx(s, ref["scores"].reshape(-1, s.nb), np.repeat(tl, s.Hkv), ref["idx"].reshape(-1, s.n),
+              idx.cpu().numpy().reshape(-1, s.n))
+    ref2 = orc.forward_rows(oc, np.arange(s.B), tl, np64(x["q"]), kc, vc, np64(x["k"]), np64(x["v"]),
+                            np64(x["w_g"]), np64(x["b_g"]), idx_in=idx.cpu().numpy())
+    err = np.abs(np64(o) - ref2["o"]).max()
+    say("  max|o-o_ref| = %.3g" % err)
+    assert err <= out_tol(s, ref2["o"])
+    # decode row == prefill row of the same tokens (GPU against GPU)
+    b = 1
+    L = seq[b]
+    sp = s.with_(B=1, T=L)
+    qp = torch.zeros((1, L, s.Hq, s.dk), dtype=dt, device="cuda")
+    qp[0, L - 1] = x["q"][b]
+    kp = x["k"][b:b + 1, :, :L].contiguous()
+    vp = x["v"][b:b + 1, :, :L].contiguous()
+    ckp, cvp = nsa.compress_kv(sp, kp, vp, x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"])
+    op, ip = nsa.forward(sp, qp, kp, vp, ckp, cvp, x["w_g"], x["b_g"], want_idx=True)
+    ck_full, cv_full = nsa.compress_kv(s, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"])
+    od, idd = nsa.decode_step(s, x["seq_lens"], x["q"], x["k"], x["v"], ck_full, cv_full, x["w_g"], x["b_g"],
+                              want_idx=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ip[0, :, L - 1], idd[b])
+    assert np.abs(np64(op[0, L - 1]) - np64(od[b])).max() <= out_tol(s, np64(od[b])) * 0.25
+
+
+# ------------------------------------------------------------------ full size
+
+def _sample_rows(T, rng, extra=12):
+    base = [0, 1, 31, 32, 63, 64, 127, 128, 1023, 1024, 1087, T // 2, T - 65, T - 64, T - 2, T - 1]
+    base += list(rng.integers(0, T, extra))
+    return np.array(sorted(set(t for t in base if 0 <= t < T)), dtype=np.int32)
+
+
+@pytest.mark.parametrize("wname", ["bf16_T8192", "bf16_T65536"])
+def test_prefill_full_size_sampled(wname):
+    wl = WORKLOADS[wname]
+    s = wl.shape
+    say("full-size prefill", wname, s)
+    x = make_prefill(s, 1000, "cuda", unit_scaled=wl.unit_scaled)
+    ck, cv = nsa.compress_kv(s, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"])
+    o, idx = nsa.forward(s, x["q"], x["k"], x["v"], ck, cv, x["w_g"], x["b_g"], want_idx=True)
+    torch.cuda.synchronize()
+    say("  gpu done; oracle compression")
+    kc = oracle_compress(s, x["k"], x["w_ck"], x["pe_k"])
+    vc = oracle_compress(s, x["v"], x["w_cv"], x["pe_v"])
+    for got, ref in ((ck, kc), (cv, vc)):
+        assert compressed_close(s, np64(got), ref)
+    rows = _sample_rows(s.T, np.random.default_rng(7))
+    say("  oracle rows", len(rows))
+    qr = np64(x["q"][0, torch.from_numpy(rows).long().cuda()])
+    k64, v64 = np64(x["k"]), np64(x["v"])
+    wg, bg = np64(x["w_g"]), np64(x["b_g"])
+    oc = ocfg(s)
+    zeros = np.zeros(len(rows), np.int32)
+    ref = orc.forward_rows(oc, zeros, rows, qr, kc, vc, k64, v64, wg, bg, want_scores=True)
+    ig = idx.cpu().numpy()[0][:, rows].transpose(1, 0, 2)          # [R,Hkv,n]
+    n_exact, n_all = check_idx(s, ref["scores"].reshape(-1, s.nb), np.repeat(rows, s.Hkv),
+                               ref["idx"].reshape(-1, s.n), ig.reshape(-1, s.n))
+    say("  idx rows checked exactly: %d / %d" % (n_exact, n_all))
+    ref2 = orc.forward_rows(oc, zeros, rows, qr, kc, vc, k64, v64, wg, bg, idx_in=ig)
+    og = np64(o[0, torch.from_numpy(rows).long().cuda()])
+    err = np.abs(og - ref2["o"]).max()
+    say("  max|o-o_ref| = %.3g (tol %.3g)" % (err, out_tol(s, ref2["o"])))
+    assert err <= out_tol(s, ref2["o"])
+
+
+def test_decode_full_size_sampled():
+    wl = WORKLOADS["bf16_decode_B32_T65536"]
+    s = wl.shape
+    say("full-size decode", s)
+    x = make_decode(s, 1003, "cuda", unit_scaled=wl.unit_scaled)
+    ck, cv = nsa.compress_kv(s, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"])
+    o, idx = nsa.decode_step(s, x["seq_lens"], x["q"], x["k"], x["v"], ck, cv, x["w_g"], x["b_g"], want_idx=True)
+    torch.cuda.synchronize()
+    for b in (0, 21):
+        say("  oracle sequence", b)
+        s1 = s.with_(B=1)
+        kb, vb = x["k"][b:b + 1], x["v"][b:b + 1]
+        kc = oracle_compress(s1, kb, x["w_ck"], x["pe_k"])
+        vc = oracle_compress(s1, vb, x["w_cv"], x["pe_v"])
+        assert compressed_close(s, np64(ck[b:b + 1]), kc)
+        oc = ocfg(s1)
+        t = np.array([s.T - 1], np.int32)
+        qb = np64(x["q"][b:b + 1])
+        k64, v64 = np64(kb), np64(vb)
+        ref = orc.forward_rows(oc, [0], t, qb, kc, vc, k64, v64, np64(x["w_g"]), np64(x["b_g"]), want_scores=True)
+        check_idx(s1, ref["scores"].reshape(-1, s.nb), np.repeat(t, s.Hkv), ref["idx"].reshape(-1, s.n),
+                  idx[b:b + 1].cpu().numpy().reshape(-1, s.n))
+        ref2 = orc.forward_rows(oc, [0], t, qb, kc, vc, k64, v64, np64(x["w_g"]), np64(x["b_g"]),
+                                idx_in=idx[b:b + 1].cpu().numpy())
+        err = np.abs(np64(o[b:b + 1]) - ref2["o"]).max()
+        say("  max|o-o_ref| = %.3g" % err)
+        assert err <= out_tol(s, ref2["o"])
