@@ -44,7 +44,7 @@
  *   w_g    [Hq][3][dk]  b_g  [Hq][3]    gate order: compressed, selected, window
  *   o      [B][T][Hq][dv]
  *   idx    [B][Hkv][T][n] int32, ascending, padded with -1
- *   scores [B][Hkv][T][NB] fp32; entries j > floor(t/64) are -inf
+ *   scores [B][Hkv][T][NB] fp32; entries j > floor(t/64) are unspecified
  */
 #ifndef NSA_H
 #define NSA_H
@@ -110,8 +110,9 @@ nsa_status nsa_compress_kv(const nsa_config *cfg, const void *k, const void *v, 
  *   o_cmp[b][t][h] = sum_i p_h[i] cmp_v[i]          (0 if no block is visible)
  *   scores[b][g][t][j] = sum_h sum_i overlap(i, j)/16 * p_h[i]
  * where overlap(i, j) counts the tokens compression block i shares with
- * selection block j (weights 1,2,2,2,1 over i = 4j-1 .. 4j+3); entries
- * j > floor(t/64) are -inf, visible-less rows score 0.
+ * selection block j (weights 1,2,2,2,1 over i = 4j-1 .. 4j+3).  Only the
+ * entries j <= floor(t/64) are written (rows with no visible block score 0);
+ * the others are left as they were.
  *   cmp_v / o_cmp: may both be NULL (scores only); o_cmp [B][T][Hq][dv] in
  *   the config dtype.  scores: required, fp32. */
 nsa_status nsa_compressed_attention(const nsa_config *cfg, const void *q, const void *cmp_k, const void *cmp_v,

@@ -163,6 +163,8 @@ nsa_status nsa_compressed_attention(const nsa_config *cfg, const void *q, const 
     a.vc = cmp_v;
     a.ocmp = o_cmp;
     a.scores = scores;
+    if (cmp_attn_mfma_supported(d))
+        return hip_status(launch_cmp_attn_mfma(a, o_cmp != nullptr, (hipStream_t)stream));
     return hip_status(launch_cmp_attn_generic(a, o_cmp != nullptr, (hipStream_t)stream));
 }
 

@@ -78,8 +78,7 @@ def test_select_and_forward_parity(name, s, scaled):
     idx, scores = nsa.select_blocks(s, x["q"], kc_d, want_scores=True)
     torch.cuda.synchronize()
     sc = np64(scores)
-    fin = np.isfinite(ref["scores"])
-    assert np.array_equal(fin, np.isfinite(sc))
+    fin = np.isfinite(ref["scores"])          # the causal entries j <= t // 64
     np.testing.assert_allclose(sc[fin], ref["scores"][fin], rtol=1e-4, atol=2e-6)
     tt = np.tile(np.arange(s.T), s.B * s.Hkv)
     n_exact, n_rows = check_idx(s, ref["scores"].reshape(-1, s.nb), tt, ref["idx"].reshape(-1, s.n),
@@ -114,8 +113,10 @@ def test_forward_is_deterministic():
     outs = [nsa.forward(s, x["q"], x["k"], x["v"], ck, cv, x["w_g"], x["b_g"], want_idx=True, want_scores=True)
             for _ in range(3)]
     torch.cuda.synchronize()
+    causal = (torch.arange(s.nb, device="cuda")[None, :] <= (torch.arange(s.T, device="cuda") // 64)[:, None])
     for o, i, sc in outs[1:]:
-        assert torch.equal(o, outs[0][0]) and torch.equal(i, outs[0][1]) and torch.equal(sc, outs[0][2])
+        assert torch.equal(o, outs[0][0]) and torch.equal(i, outs[0][1])
+        assert torch.equal(sc[..., causal], outs[0][2][..., causal])
 
 
 def test_select_matches_forward_selection():
@@ -245,3 +246,49 @@ def test_decode_full_size_sampled():
         err = np.abs(np64(o[b:b + 1]) - ref2["o"]).max()
         say("  max|o-o_ref| = %.3g" % err)
         assert err <= out_tol(s, ref2["o"])
+
+
+# ------------------------------------------------- per-stage, oracle injected
+
+STAGE = [
+    ("bf16_T2000_g16", NSAShape(1, 2000, 2, 16, 192, 128), False),
+    ("bf16_T1111_g16_d64", NSAShape(1, 1111, 1, 16, 64, 64, n=5, w=200), False),
+    ("bf16_T700_g16_d128_B2", NSAShape(2, 700, 1, 16, 128, 128, n=4, w=64), True),
+    ("fp32_T1024", NSAShape(1, 1024, 1, 4, 64, 64, FP32), True),
+]
+
+
+@pytest.mark.parametrize("name,s,scaled", STAGE, ids=[c[0] for c in STAGE])
+def test_stage_parity(name, s, scaled):
+    say("stages", name, s)
+    x = _inputs(s, 6, scaled)
+    dt = torch_dtype(s)
+    kc = oracle_compress(s, x["k"], x["w_ck"], x["pe_k"])
+    vc = oracle_compress(s, x["v"], x["w_cv"], x["pe_v"])
+    ref = orc.forward(ocfg(s), np64(x["q"]), kc, vc, np64(x["k"]), np64(x["v"]), np64(x["w_g"]), np64(x["b_g"]),
+                      want_scores=True, want_branches=True)
+    # S2 with the oracle's compressed K/V
+    ocmp, sc = nsa.compressed_attention(s, x["q"], torch.from_numpy(kc).to(dt).cuda(),
+                                        torch.from_numpy(vc).to(dt).cuda())
+    torch.cuda.synchronize()
+    ocmp_ref = ref["branches"][:, :, 0]
+    err = np.abs(np64(ocmp) - ocmp_ref).max()
+    say("  S2 max|o_cmp - ref| = %.3g" % err)
+    assert err <= out_tol(s, ocmp_ref)
+    jc = (np.arange(s.T) // 64)[None, None, :, None]
+    causal = np.arange(s.nb)[None, None, None, :] <= jc
+    causal = np.broadcast_to(causal, ref["scores"].shape)
+    np.testing.assert_allclose(np64(sc)[causal], ref["scores"][causal], rtol=1e-4, atol=2e-6)
+    # S3 with the oracle's scores (stored in fp32)
+    sref = torch.from_numpy(np.where(causal, ref["scores"], -np.inf).astype(np.float32)).cuda()
+    idx = nsa.select_topn(s, sref)
+    torch.cuda.synchronize()
+    tt = np.tile(np.arange(s.T), s.B * s.Hkv)
+    check_idx(s, ref["scores"].reshape(-1, s.nb), tt, ref["idx"].reshape(-1, s.n), idx.cpu().numpy().reshape(-1, s.n))
+    # S4 with the oracle's o_cmp (in the storage dtype) and indices
+    oc_in = torch.from_numpy(ocmp_ref).to(dt).cuda()
+    o = nsa.sparse_attention(s, x["q"], x["k"], x["v"], oc_in, torch.from_numpy(ref["idx"]).cuda(), x["w_g"], x["b_g"])
+    torch.cuda.synchronize()
+    err = np.abs(np64(o) - ref["o"]).max()
+    say("  S4 max|o - ref| = %.3g" % err)
+    assert err <= out_tol(s, ref["o"])
