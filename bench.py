@@ -102,6 +102,7 @@ def main():
     scores = torch.empty((sp.B, sp.Hkv, sp.T, sp.nb), dtype=torch.float32, device=dev)
     idx = torch.empty((sp.B, sp.Hkv, sp.T, sp.n), dtype=torch.int32, device=dev)
     o = torch.empty((sp.B, sp.T, sp.Hq, sp.dv), dtype=torch.bfloat16, device=dev)
+    wss = nsa.workspace(sp, nsa.OP_SPARSE, dev)
 
     log("setup: decode caches (2 copies)", sd)
     dec = []
@@ -127,7 +128,7 @@ def main():
         mark(2)
         nsa.select_topn(sp, scores, idx)
         mark(3)
-        nsa.sparse_attention(sp, x["q"], x["k"], x["v"], ocmp, idx, x["w_g"], x["b_g"], o)
+        nsa.sparse_attention(sp, x["q"], x["k"], x["v"], ocmp, idx, x["w_g"], x["b_g"], o, wss)
         mark(4)
         y = dec[i % 2]
         nsa.decode_step(sd, y["seq_lens"], y["q"], y["k"], y["v"], y["ck"], y["cv"], y["w_g"], y["b_g"], None,

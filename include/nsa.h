@@ -72,7 +72,8 @@ typedef enum { NSA_FP32 = 0, NSA_BF16 = 1 } nsa_dtype;
 typedef enum {
     NSA_OP_FORWARD = 0, /* nsa_forward */
     NSA_OP_SELECT = 1,  /* nsa_select_blocks */
-    NSA_OP_DECODE = 2   /* nsa_decode_step */
+    NSA_OP_DECODE = 2,  /* nsa_decode_step */
+    NSA_OP_SPARSE = 3   /* nsa_sparse_attention */
 } nsa_op;
 
 /* Problem description.  Supported ranges (checked on every call):
@@ -136,10 +137,12 @@ nsa_status nsa_select_topn(const nsa_config *cfg, const float *scores, int32_t *
  *           newsletter, sliding window paragraph);
  *   o = sigmoid(w_g[h][0].q_h + b_g[h][0]) * o_cmp + sigmoid(w_g[h][1].q_h
  *       + b_g[h][1]) * o_slc + sigmoid(w_g[h][2].q_h + b_g[h][2]) * o_win.
- * o_cmp as written by nsa_compressed_attention. */
+ * o_cmp as written by nsa_compressed_attention.  ws: nsa_workspace_bytes(cfg,
+ * NSA_OP_SPARSE) bytes (it holds V transposed per 64-token block); may be
+ * NULL when that size is 0. */
 nsa_status nsa_sparse_attention(const nsa_config *cfg, const void *q, const void *k, const void *v,
                                 const void *o_cmp, const int32_t *idx, const void *w_g, const void *b_g, void *o,
-                                void *stream);
+                                void *ws, size_t ws_bytes, void *stream);
 
 /* S2 (scores only) followed by S3.  scores_out may be NULL (the workspace
  * holds them then); idx_out is required. */

@@ -1,0 +1,431 @@
+// Stage S4 on the matrix cores: sliding-window attention, selected-block
+// attention and the gated sum, for bf16 storage with 16 query heads per KV
+// head.
+//
+// deepdaiv newsletter on DeepSeek's NSA (deepdaiv.stibee.com/p/82): the
+// selected blocks are attended at full resolution and a fixed window of the
+// most recent tokens is attended densely; allinfo.ai.kr's DSA explainer
+// ("쉽게 이해하기"): the selected branch normalises over the selected set only.
+//
+// Two kernels, each shaped by its own bound:
+//  * k_window_mfma -- the window keys of neighbouring positions coincide, so a
+//    workgroup takes 8 positions x 16 heads (128 query rows) of one KV head
+//    and streams the window's 64-key tiles through LDS once for all of them
+//    (v_mfma_f32_32x32x16_bf16, S^T = K Q^T as in the compressed stage).  It
+//    writes o = g_cmp * o_cmp + g_win * o_win.
+//  * k_selected_mfma -- selected blocks differ from position to position, so
+//    one wavefront takes one position: its 16 heads are the N dimension of
+//    v_mfma_f32_16x16x32_bf16 (the GQA group shares every key fetch), and each
+//    selected 64-token block is read once, straight into registers.  This
+//    part is bound by how fast blocks can be gathered, not by the MFMA.  It
+//    adds g_slc * o_slc to o.
+// V enters the selected kernel as V^T per 64-token block (k_vt_blocks), so
+// every operand fetch is one 16-byte load.
+#include "mfma_util.h"
+#include "nsa_internal.h"
+
+namespace nsa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPos = 8;      // window kernel: query positions per workgroup
+constexpr int kTile = 64;
+
+__device__ __forceinline__ int krow(int k)
+{
+    int h = k >> 4, m = (k >> 2) & 3, u = k & 3;
+    return 8 * m + 4 * h + u;
+}
+
+__device__ __forceinline__ float sigmoid(float z) { return 1.f / (1.f + __expf(-z)); }
+
+// V [bg][T][DV] -> V^T per 64-token block [bg][NB][DV][64]; tokens past T are 0.
+template <int DV>
+__global__ __launch_bounds__(kThreads) void k_vt_blocks(const uint16_t *__restrict__ v, uint16_t *__restrict__ vt,
+                                                        int T, int NB)
+{
+    __shared__ uint16_t tile[kTile][DV + 2];
+    const int j = blockIdx.x, bg = blockIdx.y, tid = threadIdx.x;
+    const uint16_t *src = v + ((long)bg * T + (long)kTile * j) * DV;
+    for (int e = tid; e < kTile * DV / 8; e += kThreads) {
+        const int key = e / (DV / 8), ch = e % (DV / 8);
+        u32x4 x = {0, 0, 0, 0};
+        if (kTile * j + key < T) x = ld16(src + key * DV + ch * 8);
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            tile[key][ch * 8 + 2 * q] = (uint16_t)(x[q] & 0xffffu);
+            tile[key][ch * 8 + 2 * q + 1] = (uint16_t)(x[q] >> 16);
+        }
+    }
+    __syncthreads();
+    uint16_t *dst = vt + ((long)bg * NB + j) * DV * kTile;
+    for (int e = tid; e < DV * kTile / 8; e += kThreads) {
+        const int dv = e / (kTile / 8), kc = e % (kTile / 8);
+        u32x4 x;
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+            x[q] = (uint32_t)tile[kc * 8 + 2 * q][dv] | ((uint32_t)tile[kc * 8 + 2 * q + 1][dv] << 16);
+        st16(dst + dv * kTile + kc * 8, x);
+    }
+}
+
+template <int DK, int DV>
+struct WinLds {
+    static constexpr int KS = DK + 8;
+    static constexpr int VS = kTile + 8;
+    uint16_t k[kTile * KS];
+    uint16_t vt[DV * VS];
+};
+
+// ---------------------------------------------------------------------------
+// Window branch + compressed term.  Workgroups of one (b, g) pair take
+// consecutive position tiles on the same XCD, so the overlapping window tiles
+// are served from that XCD's L2.
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads) void k_window_mfma(RowArgs a, int ntp)
+{
+    constexpr int KSTEPS = DK / 16;
+    constexpr int DT = DV / 32;
+    using L = WinLds<DK, DV>;
+    __shared__ L sm;
+
+    const Dims &d = a.d;
+    const int BG = d.B * d.Hkv;
+    const long total = (long)BG * ntp;
+    const long per_xcd = (total + 7) / 8;
+    const long vid = (long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (vid >= total) return;
+    const int bg = (int)(vid / ntp), ptile = (int)(vid % ntp);
+    const int b = bg / d.Hkv, g = bg % d.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, row = lane & 31, head = row & 15;
+    const int pos0 = ptile * kPos;
+    const int t = pos0 + 2 * wave + (row >> 4);
+    const bool live = t < d.T;
+    const int lo = max(0, t - d.w + 1);
+    const int tlast = min(pos0 + kPos - 1, d.T - 1);
+    const int c_first = max(0, pos0 - d.w + 1) / kTile, c_last = tlast / kTile;
+    const float sl2 = d.scale * kLog2e;
+
+    bf16x8 qf[KSTEPS];
+    const uint16_t *qr = (const uint16_t *)a.q + (long)b * a.q_sb + (long)t * a.q_sr +
+                         (long)(g * 16 + head) * DK + 8 * h;
+    {
+        const u32x4 z = {0, 0, 0, 0};
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; kk++) qf[kk] = as_bf16x8(live ? ld16(qr + 16 * kk) : z);
+    }
+    // gates of this row: each lane half holds half of the dimensions
+    float gate[3] = {0.f, 0.f, 0.f};
+    if (live) {
+        const uint16_t *wr = (const uint16_t *)a.wg + (long)(g * 16 + head) * 3 * DK + 8 * h;
+#pragma unroll
+        for (int c = 0; c < 3; c++) {
+            float z = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; kk++) {
+                const u32x4 wv = ld16(wr + c * DK + 16 * kk);
+                const u32x4 qv = ld16(qr + 16 * kk);
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    z += __uint_as_float(wv[e] << 16) * __uint_as_float(qv[e] << 16);
+                    z += __uint_as_float(wv[e] & 0xffff0000u) * __uint_as_float(qv[e] & 0xffff0000u);
+                }
+            }
+            gate[c] = z;
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 3; c++) {
+        gate[c] += __shfl_xor(gate[c], 32, 64);
+        const uint16_t *bgp = (const uint16_t *)a.bg + (long)(g * 16 + head) * 3 + c;
+        gate[c] = live ? sigmoid(gate[c] + __uint_as_float((uint32_t)*bgp << 16)) : 0.f;
+    }
+
+    const uint16_t *kg = (const uint16_t *)a.k + (long)bg * d.T * DK;
+    const uint16_t *vg = (const uint16_t *)a.v + (long)bg * d.T * DV;
+    float m = -INFINITY, l = 0.f;
+    f32x16 oacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) oacc[dt][r] = 0.f;
+
+    for (int c = c_first; c <= c_last; c++) {
+        __syncthreads();
+        {
+            constexpr int CH = DK / 8;
+            for (int task = tid; task < kTile * CH; task += kThreads) {
+                const int key = task / CH, ch = task % CH;
+                const int r = (key & ~31) | krow(key & 31);
+                u32x4 x = {0, 0, 0, 0};
+                if (c * kTile + key < d.T) x = ld16(kg + (long)(c * kTile + key) * DK + ch * 8);
+                st16(&sm.k[r * L::KS + ch * 8], x);
+            }
+            constexpr int NDC = DV / 8;
+            for (int task = tid; task < 32 * NDC; task += kThreads) {
+                const int kp = task & 31, dc = task >> 5;
+                const int k0 = c * kTile + 2 * kp;
+                u32x4 v0 = {0, 0, 0, 0}, v1 = {0, 0, 0, 0};
+                if (k0 < d.T) v0 = ld16(vg + (long)k0 * DV + dc * 8);
+                if (k0 + 1 < d.T) v1 = ld16(vg + (long)(k0 + 1) * DV + dc * 8);
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const uint32_t x0 = (v0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                    const uint32_t x1 = (v1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                    *(uint32_t *)&sm.vt[(dc * 8 + e) * L::VS + 2 * kp] = x0 | (x1 << 16);
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int mt = 0; mt < 2; mt++) {
+            f32x16 acc;
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[r] = 0.f;
+            const uint16_t *kr = &sm.k[(32 * mt + row) * L::KS + 8 * h];
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; kk++) acc = mfma32(as_bf16x8(ld16(kr + 16 * kk)), qf[kk], acc);
+            const int kb = c * kTile + 32 * mt + 16 * h;
+            float s[16], mx = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int key = kb + r;
+                s[r] = (live && key >= lo && key <= t) ? acc[r] * sl2 : -INFINITY;
+                mx = fmaxf(mx, s[r]);
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            // rows that have seen no key yet keep m = -inf and add nothing;
+            // no branch, so the MFMAs below always run for the whole wave
+            const float mn = fmaxf(m, mx);
+            const bool any = mn != -INFINITY;
+            const float al = any ? fast_exp2(m - mn) : 1.f;
+            float p[16], sum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                p[r] = any ? fast_exp2(s[r] - mn) : 0.f;
+                sum += p[r];
+            }
+            l = l * al + sum;
+            m = any ? mn : m;
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) oacc[dt][r] *= al;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; s2++) {
+                const bf16x8 pb = pack8(&p[8 * s2]);
+#pragma unroll
+                for (int dt = 0; dt < DT; dt++) {
+                    const uint16_t *vr = &sm.vt[(32 * dt + row) * L::VS + 32 * mt + 16 * h + 8 * s2];
+                    oacc[dt] = mfma32(as_bf16x8(ld16(vr)), pb, oacc[dt]);
+                }
+            }
+        }
+    }
+    const float ltot = l + __shfl_xor(l, 32, 64);
+    if (!live) return;
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    const long ooff = (((long)b * a.R + t) * d.Hq + g * 16 + head) * DV;
+    const uint16_t *oc = (const uint16_t *)a.ocmp + ooff;
+    uint16_t *orow = (uint16_t *)a.o + ooff;
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++) {
+            const int dv = 32 * dt + 8 * q4 + 4 * h;
+            const uint2 cv = *(const uint2 *)(oc + dv);
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const uint32_t word = e < 2 ? cv.x : cv.y;
+                const float ocv = __uint_as_float(e & 1 ? word & 0xffff0000u : word << 16);
+                y[e] = gate[0] * ocv + gate[2] * oacc[dt][4 * q4 + e] * inv;
+            }
+            uint2 w;
+            w.x = pack_bf16x2(y[0], y[1]);
+            w.y = pack_bf16x2(y[2], y[3]);
+            *(uint2 *)(orow + dv) = w;
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Selected branch.  One wavefront per (b, g, position); lane l holds head
+// l%16 and, of every 32-key half block, keys 8*(l/16) .. 8*(l/16)+7: the two
+// 16-key MFMA row tiles of a half block take keys 8*(i/4) + i%4 (tile A) and
+// 8*(i/4) + 4 + i%4 (tile B) in row i, so their outputs are exactly the
+// B operand of O^T = V^T P^T.
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads) void k_selected_mfma(RowArgs a, const uint16_t *__restrict__ vt, int ntp)
+{
+    constexpr int KS = DK / 32;     // 16x16x32 steps over the head dim
+    constexpr int DT = DV / 16;     // 16-wide dv tiles
+    const Dims &d = a.d;
+    const int BG = d.B * d.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // workgroup -> (b, g, 4 positions), heaviest (latest) positions first
+    const long total = (long)BG * ntp;
+    const long per_xcd = (total + 7) / 8;
+    const long vid = (long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (vid >= total) return;
+    const int bg = (int)(vid / ntp), ptile = ntp - 1 - (int)(vid % ntp);
+    const int t = ptile * 4 + wave;
+    if (t >= d.T) return;
+    const int b = bg / d.Hkv, g = bg % d.Hkv;
+    const int q = lane >> 4, hd = lane & 15;
+    const int jcur = t / kTile;
+    const float sl2 = d.scale * kLog2e;
+
+    const uint16_t *qr = (const uint16_t *)a.q + (long)b * a.q_sb + (long)t * a.q_sr + (long)(g * 16 + hd) * DK + 8 * q;
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; kk++) qf[kk] = as_bf16x8(ld16(qr + 32 * kk));
+    float gsl;
+    {
+        const uint16_t *wr = (const uint16_t *)a.wg + ((long)(g * 16 + hd) * 3 + 1) * DK + 8 * q;
+        float z = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KS; kk++) {
+            const u32x4 wv = ld16(wr + 32 * kk);
+            const u32x4 qv = ld16(qr + 32 * kk);
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                z += __uint_as_float(wv[e] << 16) * __uint_as_float(qv[e] << 16);
+                z += __uint_as_float(wv[e] & 0xffff0000u) * __uint_as_float(qv[e] & 0xffff0000u);
+            }
+        }
+        z += __shfl_xor(z, 16, 64);
+        z += __shfl_xor(z, 32, 64);
+        const uint16_t *bp = (const uint16_t *)a.bg + (long)(g * 16 + hd) * 3 + 1;
+        gsl = sigmoid(z + __uint_as_float((uint32_t)*bp << 16));
+    }
+
+    // the row's blocks: valid (0..jcur) and first occurrence only
+    int jb = -1;
+    if (lane < d.n) jb = a.idx[((long)bg * a.R + t) * d.n + lane];
+    bool ok = jb >= 0 && jb <= jcur;
+    for (int u = 0; u < 16; u++) {
+        const int other = __shfl(jb, u, 64);
+        if (u < lane && other == jb) ok = false;
+    }
+    uint64_t todo = __ballot(ok);
+
+    const uint16_t *kg = (const uint16_t *)a.k + (long)bg * d.T * DK;
+    const uint16_t *vtg = vt + (long)bg * d.nb * DV * kTile;
+    const int krA = 8 * (hd >> 2) + (hd & 3);     // key of MFMA row hd in tile A
+    float m = -INFINITY, l = 0.f;
+    f32x4 oacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    while (todo) {
+        const int src = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        const int j = __shfl(jb, src, 64);
+        const int key0 = j * kTile;
+#pragma unroll
+        for (int s = 0; s < 2; s++) {
+            const int kA = min(key0 + 32 * s + krA, d.T - 1), kB = min(key0 + 32 * s + krA + 4, d.T - 1);
+            bf16x8 fa[KS], fb[KS];
+#pragma unroll
+            for (int kk = 0; kk < KS; kk++) {
+                fa[kk] = as_bf16x8(ld16(kg + (long)kA * DK + 32 * kk + 8 * q));
+                fb[kk] = as_bf16x8(ld16(kg + (long)kB * DK + 32 * kk + 8 * q));
+            }
+            bf16x8 fv[DT];
+            const uint16_t *vb = vtg + ((long)j * DV + hd) * kTile + 32 * s + 8 * q;
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) fv[dt] = as_bf16x8(ld16(vb + 16 * dt * kTile));
+            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KS; kk++) {
+                accA = mfma16(fa[kk], qf[kk], accA);
+                accB = mfma16(fb[kk], qf[kk], accB);
+            }
+            float sv[8], mx = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const int ka = key0 + 32 * s + 8 * q + u;
+                sv[u] = ka <= t ? accA[u] * sl2 : -INFINITY;
+                sv[4 + u] = ka + 4 <= t ? accB[u] * sl2 : -INFINITY;
+                mx = fmaxf(mx, fmaxf(sv[u], sv[4 + u]));
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float mn = fmaxf(m, mx);
+            if (mn == -INFINITY) continue;   // every key of this half block is past t: uniform over the wave
+            const float al = fast_exp2(m - mn);
+            float p[8], sum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                p[e] = fast_exp2(sv[e] - mn);
+                sum += p[e];
+            }
+            l = l * al + sum;
+            m = mn;
+            const bf16x8 pb = pack8(p);
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) {
+                oacc[dt] *= al;
+                oacc[dt] = mfma16(fv[dt], pb, oacc[dt]);
+            }
+        }
+    }
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float w = l > 0.f ? gsl / l : 0.f;
+    uint16_t *orow = (uint16_t *)a.o + (((long)b * a.R + t) * d.Hq + g * 16 + hd) * DV + 4 * q;
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++) {
+        uint2 cur = *(uint2 *)(orow + 16 * dt);
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const uint32_t word = e < 2 ? cur.x : cur.y;
+            y[e] = __uint_as_float(e & 1 ? word & 0xffff0000u : word << 16) + w * oacc[dt][e];
+        }
+        cur.x = pack_bf16x2(y[0], y[1]);
+        cur.y = pack_bf16x2(y[2], y[3]);
+        *(uint2 *)(orow + 16 * dt) = cur;
+    }
+}
+
+template <int DK, int DV>
+hipError_t launch_sparse_dims(const RowArgs &a, void *vt_ws, hipStream_t s)
+{
+    const Dims &d = a.d;
+    const int BG = d.B * d.Hkv;
+    hipLaunchKernelGGL(k_vt_blocks<DV>, dim3(d.nb, BG), dim3(kThreads), 0, s, (const uint16_t *)a.v,
+                       (uint16_t *)vt_ws, d.T, d.nb);
+    const int ntp = (a.R + kPos - 1) / kPos;
+    long nwg = (long)BG * ntp;
+    nwg = (nwg + 7) / 8 * 8;
+    hipLaunchKernelGGL((k_window_mfma<DK, DV>), dim3((unsigned)nwg), dim3(kThreads), 0, s, a, ntp);
+    const int ntp4 = (a.R + 3) / 4;
+    long nwg4 = ((long)BG * ntp4 + 7) / 8 * 8;
+    hipLaunchKernelGGL((k_selected_mfma<DK, DV>), dim3((unsigned)nwg4), dim3(kThreads), 0, s, a,
+                       (const uint16_t *)vt_ws, ntp4);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool sparse_mfma_supported(const Dims &d)
+{
+    return d.dtype == NSA_BF16 && d.G == 16 &&
+           ((d.dk == 192 && d.dv == 128) || (d.dk == 128 && d.dv == 128) || (d.dk == 64 && d.dv == 64));
+}
+
+size_t sparse_mfma_ws_bytes(const Dims &d) { return (size_t)d.B * d.Hkv * d.nb * 64 * d.dv * 2; }
+
+hipError_t launch_sparse_mfma(const RowArgs &a, void *vt_ws, hipStream_t s)
+{
+    const Dims &d = a.d;
+    if (d.dk == 192 && d.dv == 128) return launch_sparse_dims<192, 128>(a, vt_ws, s);
+    if (d.dk == 128 && d.dv == 128) return launch_sparse_dims<128, 128>(a, vt_ws, s);
+    if (d.dk == 64 && d.dv == 64) return launch_sparse_dims<64, 64>(a, vt_ws, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace nsa

@@ -53,8 +53,9 @@ nsa_status check_config(const nsa_config *c, Dims *out)
 //   ocmp   [B][R][Hq][dv]  storage dtype  compressed-branch output
 //   scores [B][Hkv][R][nb] fp32  importance scores (when the caller passes none)
 //   idx    [B][Hkv][R][n]  int32 selected blocks (when the caller passes none)
+//   vt     V^T per 64-token block, for the matrix-core sparse stage (prefill)
 struct Layout {
-    size_t ocmp, scores, idx, total;
+    size_t ocmp, scores, idx, vt, total;
 };
 
 Layout layout(const Dims &d, long R)
@@ -67,6 +68,8 @@ Layout layout(const Dims &d, long R)
     off = align_up(off + sizeof(float) * (size_t)d.B * d.Hkv * R * d.nb);
     L.idx = off;
     off = align_up(off + sizeof(int32_t) * (size_t)d.B * d.Hkv * R * d.n);
+    L.vt = off;
+    if (R == d.T && sparse_mfma_supported(d)) off = align_up(off + sparse_mfma_ws_bytes(d));
     L.total = off;
     return L;
 }
@@ -129,6 +132,8 @@ size_t nsa_workspace_bytes(const nsa_config *cfg, int op)
         return layout(d, d.T).total;
     case NSA_OP_DECODE:
         return layout(d, 1).total;
+    case NSA_OP_SPARSE:
+        return sparse_mfma_supported(d) ? align_up(sparse_mfma_ws_bytes(d)) : 0;
     default:
         return 0;
     }
@@ -183,13 +188,18 @@ nsa_status nsa_select_topn(const nsa_config *cfg, const float *scores, int32_t *
 
 nsa_status nsa_sparse_attention(const nsa_config *cfg, const void *q, const void *k, const void *v,
                                 const void *o_cmp, const int32_t *idx, const void *w_g, const void *b_g, void *o,
-                                void *stream)
+                                void *ws, size_t ws_bytes, void *stream)
 {
     Dims d;
     nsa_status st = check_config(cfg, &d);
     if (st != NSA_OK) return st;
     if (!q || !k || !v || !o_cmp || !idx || !w_g || !b_g || !o) return NSA_ERR_NULL;
     if (!all_aligned({q, k, v, o_cmp, idx, w_g, b_g, o})) return NSA_ERR_ALIGN;
+    const bool mfma = sparse_mfma_supported(d);
+    if (mfma) {
+        if (!ws || ws_bytes < sparse_mfma_ws_bytes(d)) return NSA_ERR_WORKSPACE;
+        if ((uintptr_t)ws % kAlign) return NSA_ERR_ALIGN;
+    }
     RowArgs a = prefill_args(d, q);
     a.k = k;
     a.v = v;
@@ -198,6 +208,7 @@ nsa_status nsa_sparse_attention(const nsa_config *cfg, const void *q, const void
     a.wg = w_g;
     a.bg = b_g;
     a.o = o;
+    if (mfma) return hip_status(launch_sparse_mfma(a, ws, (hipStream_t)stream));
     return hip_status(launch_sparse_generic(a, (hipStream_t)stream));
 }
 
@@ -242,7 +253,7 @@ nsa_status nsa_forward(const nsa_config *cfg, const void *q, const void *k, cons
         if ((st = nsa_select_topn(cfg, scores, sel, stream)) != NSA_OK) return st;
         idx = sel;
     }
-    return nsa_sparse_attention(cfg, q, k, v, ocmp, idx, w_g, b_g, o, stream);
+    return nsa_sparse_attention(cfg, q, k, v, ocmp, idx, w_g, b_g, o, w + L.vt, L.total - L.vt, stream);
 }
 
 nsa_status nsa_decode_step(const nsa_config *cfg, const int32_t *seq_lens, const void *q, const void *k_cache,

@@ -66,5 +66,8 @@ hipError_t launch_sparse_generic(const RowArgs &a, hipStream_t s);
 // Matrix-core kernels (bf16 storage, G = 16; prefill rows only).
 bool cmp_attn_mfma_supported(const Dims &d);
 hipError_t launch_cmp_attn_mfma(const RowArgs &a, bool with_v, hipStream_t s);
+bool sparse_mfma_supported(const Dims &d);
+size_t sparse_mfma_ws_bytes(const Dims &d);   // V^T per 64-token block
+hipError_t launch_sparse_mfma(const RowArgs &a, void *vt_ws, hipStream_t s);
 
 }  // namespace nsa

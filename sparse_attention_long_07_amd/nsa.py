@@ -17,7 +17,7 @@ from .config import BF16, FP32, NSAShape
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libnsa.so")
 
-OP_FORWARD, OP_SELECT, OP_DECODE = 0, 1, 2
+OP_FORWARD, OP_SELECT, OP_DECODE, OP_SPARSE = 0, 1, 2, 3
 STATUS = {0: "NSA_OK", -1: "NSA_ERR_NULL", -2: "NSA_ERR_SHAPE", -3: "NSA_ERR_DTYPE", -4: "NSA_ERR_PARAM",
           -5: "NSA_ERR_WORKSPACE", -6: "NSA_ERR_HIP", -7: "NSA_ERR_ALIGN"}
 
@@ -59,7 +59,7 @@ def lib() -> ctypes.CDLL:
         L.nsa_select_topn.restype = ctypes.c_int
         L.nsa_select_topn.argtypes = [ctypes.POINTER(Config)] + [_vp] * 3
         L.nsa_sparse_attention.restype = ctypes.c_int
-        L.nsa_sparse_attention.argtypes = [ctypes.POINTER(Config)] + [_vp] * 9
+        L.nsa_sparse_attention.argtypes = [ctypes.POINTER(Config)] + [_vp] * 9 + [ctypes.c_size_t, _vp]
         L.nsa_select_blocks.restype = ctypes.c_int
         L.nsa_select_blocks.argtypes = [ctypes.POINTER(Config), _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.nsa_forward.restype = ctypes.c_int
@@ -164,7 +164,7 @@ def select_topn(s: NSAShape, scores, idx=None):
     return idx
 
 
-def sparse_attention(s: NSAShape, q, k, v, o_cmp, idx, w_g, b_g, o=None):
+def sparse_attention(s: NSAShape, q, k, v, o_cmp, idx, w_g, b_g, o=None, ws=None):
     """Stage S4: selected + window attention and the gated sum."""
     dt = _dt(s)
     _req(q, "q", (s.B, s.T, s.Hq, s.dk), dt)
@@ -177,9 +177,12 @@ def sparse_attention(s: NSAShape, q, k, v, o_cmp, idx, w_g, b_g, o=None):
     if o is None:
         o = torch.empty((s.B, s.T, s.Hq, s.dv), dtype=dt, device=q.device)
     _req(o, "o", (s.B, s.T, s.Hq, s.dv), dt)
+    if ws is None:
+        ws = workspace(s, OP_SPARSE, q.device)
     c = config(s)
     _check("nsa_sparse_attention", lib().nsa_sparse_attention(ctypes.byref(c), _p(q), _p(k), _p(v), _p(o_cmp),
-                                                              _p(idx), _p(w_g), _p(b_g), _p(o), _stream()))
+                                                              _p(idx), _p(w_g), _p(b_g), _p(o), _p(ws), ws.numel(),
+                                                              _stream()))
     return o
 
 
