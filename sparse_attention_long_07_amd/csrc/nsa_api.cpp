@@ -131,7 +131,7 @@ size_t nsa_workspace_bytes(const nsa_config *cfg, int op)
     case NSA_OP_SELECT:
         return layout(d, d.T).total;
     case NSA_OP_DECODE:
-        return layout(d, 1).total;
+        return decode_mfma_supported(d) ? decode_mfma_layout(d, nullptr, nullptr) : layout(d, 1).total;
     case NSA_OP_SPARSE:
         return sparse_mfma_supported(d) ? align_up(sparse_mfma_ws_bytes(d)) : 0;
     default:
@@ -268,10 +268,34 @@ nsa_status nsa_decode_step(const nsa_config *cfg, const int32_t *seq_lens, const
     const void *ptrs[] = {seq_lens, q, k_cache, v_cache, cmp_k, cmp_v, w_g, b_g, idx_in, o, idx_out};
     for (const void *p : ptrs)
         if (!aligned16(p)) return NSA_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    if (decode_mfma_supported(d)) {
+        if (!ws || ws_bytes < decode_mfma_layout(d, nullptr, nullptr)) return NSA_ERR_WORKSPACE;
+        if ((uintptr_t)ws % kAlign) return NSA_ERR_ALIGN;
+        DecArgs A;
+        memset(&A, 0, sizeof A);
+        A.d = d;
+        A.seq_lens = seq_lens;
+        A.q = q;
+        A.k = k_cache;
+        A.v = v_cache;
+        A.kc = cmp_k;
+        A.vc = cmp_v;
+        A.wg = w_g;
+        A.bg = b_g;
+        A.idx_in = idx_in;
+        A.o = o;
+        decode_mfma_layout(d, ws, &A);
+        if (idx_out && !idx_in) A.idx = idx_out;
+        NSA_TRY(launch_decode_mfma(A, s));
+        if (idx_out && idx_in)
+            NSA_TRY(hipMemcpyAsync(idx_out, idx_in, sizeof(int32_t) * (size_t)d.B * d.Hkv * d.n,
+                                   hipMemcpyDeviceToDevice, s));
+        return NSA_OK;
+    }
     Layout L;
     if ((st = check_ws(d, 1, ws, ws_bytes, &L)) != NSA_OK) return st;
     char *w = (char *)ws;
-    hipStream_t s = (hipStream_t)stream;
     RowArgs a = row_args(d, 1);
     a.seq_lens = seq_lens;
     a.q = q;

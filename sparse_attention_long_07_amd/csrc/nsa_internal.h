@@ -56,6 +56,23 @@ struct RowArgs {
     long o_sb, o_sr;
 };
 
+// Arguments of the matrix-core decode step (one row per sequence).
+struct DecArgs {
+    Dims d;
+    const int32_t *seq_lens;      // device [B]
+    const void *q, *k, *v;        // q [B][Hq][dk]; caches [B][Hkv][T][dk|dv]
+    const void *kc, *vc;          // compressed caches [B][Hkv][npad][dk|dv]
+    const void *wg, *bg;
+    const int32_t *idx_in;        // [B][Hkv][n] or nullptr
+    void *o;                      // [B][Hq][dv]
+    int cs, ws, ss, nbp;          // compressed / window / selected splits; blocks per (b, g) in bx/by
+    float *pm, *pl, *po;          // phase-A partials [pair][cs+ws][16] (+[dv])
+    float *bx, *by;               // block importance terms [pair][16][nbp]
+    float *sm, *sl, *so;          // phase-C partials [pair][ss][16] (+[dv])
+    float *ocmp;                  // [pair][16][dv]
+    int32_t *idx;                 // selection output [B][Hkv][n]
+};
+
 // Generic kernels: plain VALU code, any supported shape, fp32 or bf16 storage.
 hipError_t launch_compress_generic(const Dims &d, const void *x, const void *W, const void *PE, void *out,
                                    int dim, hipStream_t s);
@@ -69,5 +86,8 @@ hipError_t launch_cmp_attn_mfma(const RowArgs &a, bool with_v, hipStream_t s);
 bool sparse_mfma_supported(const Dims &d);
 size_t sparse_mfma_ws_bytes(const Dims &d);   // V^T per 64-token block
 hipError_t launch_sparse_mfma(const RowArgs &a, void *vt_ws, hipStream_t s);
+bool decode_mfma_supported(const Dims &d);
+size_t decode_mfma_layout(const Dims &d, void *ws, DecArgs *A);   // bytes; fills A's buffers if ws
+hipError_t launch_decode_mfma(const DecArgs &A, hipStream_t s);
 
 }  // namespace nsa
