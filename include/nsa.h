@@ -138,8 +138,8 @@ nsa_status nsa_select_topn(const nsa_config *cfg, const float *scores, int32_t *
  *   o = sigmoid(w_g[h][0].q_h + b_g[h][0]) * o_cmp + sigmoid(w_g[h][1].q_h
  *       + b_g[h][1]) * o_slc + sigmoid(w_g[h][2].q_h + b_g[h][2]) * o_win.
  * o_cmp as written by nsa_compressed_attention.  ws: nsa_workspace_bytes(cfg,
- * NSA_OP_SPARSE) bytes (it holds V transposed per 64-token block); may be
- * NULL when that size is 0. */
+ * NSA_OP_SPARSE) bytes (it holds K and V repacked per 64-token block); may
+ * be NULL when that size is 0. */
 nsa_status nsa_sparse_attention(const nsa_config *cfg, const void *q, const void *k, const void *v,
                                 const void *o_cmp, const int32_t *idx, const void *w_g, const void *b_g, void *o,
                                 void *ws, size_t ws_bytes, void *stream);

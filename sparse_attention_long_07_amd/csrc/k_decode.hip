@@ -5,14 +5,18 @@
 // selected blocks and the window.  The step is bound by HBM bandwidth, so
 // the work is split along the keys across many workgroups (split-K) and
 // merged afterwards:
-//   phase A  compressed slots (512 per workgroup) and the window (512 keys
+//   phase A  compressed slots (256 per workgroup) and the window (256 keys
 //            per workgroup): per-workgroup (max, sum, unnormalised output),
 //            plus, for the compressed slots, each block's importance terms;
 //   phase B  per (sequence, KV head): exact log-sum-exp over the compressed
 //            splits, o_cmp, block scores (heads summed, weights 1,2,2,2,1)
 //            and the top-n selection;
 //   phase C  the selected blocks (4 per workgroup, one per wavefront);
-//   phase D  merge of the window and selected partials and the gated sum.
+//   phase D  merge of the compressed, window and selected partials and the
+//            gated sum.
+// Every wavefront issues all loads of its 64 keys (K into MFMA operand
+// registers, V into registers for the LDS transpose) before it computes, so
+// each one keeps 40 KB in flight.
 //
 // Lane view (one position, 16 heads, wave64): head hd = lane%16, key group
 // q = lane/16.  A 32-key step is two 16x16x32 S^T tiles whose rows hold keys
@@ -27,7 +31,7 @@ namespace nsa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kWaveKeys = 128;               // keys per wavefront in phase A
+constexpr int kWaveKeys = 64;                // keys per wavefront (two 32-key steps)
 constexpr int kSplitKeys = 4 * kWaveKeys;    // keys per phase-A workgroup
 constexpr int kSelPerWg = 4;                 // selected blocks per phase-C workgroup
 constexpr int kVtS = 40;                     // bf16 per V^T row in LDS (32 keys + pad)
@@ -69,19 +73,36 @@ __device__ __forceinline__ void logits_step(const uint16_t *K, int base, int kcl
     }
 }
 
-// V rows base .. base+31 -> vt[dv][key] (wave-private LDS tile).
+// V rows base .. base+31: four (key pair, 8-dv chunk) tasks per lane,
+// loaded into registers, later written transposed to vt[dv][key].
 template <int DV>
-__device__ __forceinline__ void stage_vt(const uint16_t *V, int base, int kclamp, uint16_t *vt, int lane)
+struct VRegs {
+    static constexpr int N = 16 * (DV / 8) / 64;   // tasks per lane
+    u32x4 v0[N], v1[N];
+};
+
+template <int DV>
+__device__ __forceinline__ void load_v(const uint16_t *V, int base, int kclamp, int lane, VRegs<DV> &r)
 {
-    for (int task = lane; task < 16 * (DV / 8); task += 64) {
-        const int kp = task & 15, dc = task >> 4;
+#pragma unroll
+    for (int i = 0; i < VRegs<DV>::N; i++) {
+        const int task = lane + 64 * i, kp = task & 15, dc = task >> 4;
         const int k0 = min(base + 2 * kp, kclamp), k1 = min(base + 2 * kp + 1, kclamp);
-        const u32x4 v0 = ld16(V + (long)k0 * DV + dc * 8);
-        const u32x4 v1 = ld16(V + (long)k1 * DV + dc * 8);
+        r.v0[i] = ld16(V + (long)k0 * DV + dc * 8);
+        r.v1[i] = ld16(V + (long)k1 * DV + dc * 8);
+    }
+}
+
+template <int DV>
+__device__ __forceinline__ void store_vt(const VRegs<DV> &r, uint16_t *vt, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < VRegs<DV>::N; i++) {
+        const int task = lane + 64 * i, kp = task & 15, dc = task >> 4;
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-            const uint32_t x0 = (v0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-            const uint32_t x1 = (v1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+            const uint32_t x0 = (r.v0[i][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+            const uint32_t x1 = (r.v1[i][e >> 1] >> (16 * (e & 1))) & 0xffffu;
             *(uint32_t *)&vt[(dc * 8 + e) * kVtS + 2 * kp] = x0 | (x1 << 16);
         }
     }
@@ -111,7 +132,7 @@ __device__ __forceinline__ float head_sum(float x)
 template <int DV>
 struct DecLds {
     union {
-        uint16_t vt[4][DV * kVtS];
+        uint16_t vt[4][2 * DV * kVtS];   // two 32-key steps per wavefront
         float ol[4][16][DV];
     } u;
     float mx[4][16];
@@ -179,12 +200,14 @@ __global__ __launch_bounds__(kThreads) void k_dec_phase_a(DecArgs A)
     bf16x8 qf[DK / 32];
     load_qf<DK>((const uint16_t *)A.q + ((long)b * d.Hq + g * 16 + hd) * DK, q, qf);
 
-    float s[4][8];
+    float s[2][8];
+    VRegs<DV> vr[2];
     float mx = -INFINITY;
 #pragma unroll
-    for (int st = 0; st < 4; st++) {
+    for (int st = 0; st < 2; st++) {
         const int base = kbeg + 32 * st;
-        if (base < kend) {
+        if (base < kend) {   // uniform over the wavefront
+            load_v<DV>(V, base, kclamp, lane, vr[st]);
             logits_step<DK>(K, base, kclamp, qf, hd, q, s[st]);
 #pragma unroll
             for (int e = 0; e < 8; e++) {
@@ -208,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_phase_a(DecArgs A)
     float *bx = A.bx + (long)pair * 16 * A.nbp + (long)hd * A.nbp;
     float *by = A.by + (long)pair * 16 * A.nbp + (long)hd * A.nbp;
 #pragma unroll
-    for (int st = 0; st < 4; st++) {
+    for (int st = 0; st < 2; st++) {
         const int base = kbeg + 32 * st;
         float p[8];
 #pragma unroll
@@ -225,8 +248,8 @@ __global__ __launch_bounds__(kThreads) void k_dec_phase_a(DecArgs A)
         if (base < kend) {   // uniform over the wavefront
 #pragma unroll
             for (int e = 0; e < 8; e++) l += p[e];
-            stage_vt<DV>(V, base, kclamp, vt, lane);
-            pv_step<DV>(vt, p, hd, q, oacc);
+            store_vt<DV>(vr[st], vt + st * DV * kVtS, lane);
+            pv_step<DV>(vt + st * DV * kVtS, p, hd, q, oacc);
         }
     }
     l = head_sum(l);
@@ -235,12 +258,13 @@ __global__ __launch_bounds__(kThreads) void k_dec_phase_a(DecArgs A)
 }
 
 // ---------------------------------------------------------------------------
-// Phase B.  One workgroup per (sequence, KV head).
+// Phase B.  One workgroup per (sequence, KV head): the exact log-sum-exp of
+// each head over the compressed splits, the block scores and the selection.
 template <int DV>
 __global__ __launch_bounds__(kThreads) void k_dec_phase_b(DecArgs A)
 {
     extern __shared__ float S[];   // [nb] block scores
-    __shared__ float wsp[64][16];  // weight of split s for head h (<= 64 splits)
+    __shared__ float wsp[64][16];  // weight exp2(m_split - lse) of split s for head h
     __shared__ float lse[16];
     const Dims &d = A.d;
     const int pair = blockIdx.x;
@@ -264,25 +288,24 @@ __global__ __launch_bounds__(kThreads) void k_dec_phase_b(DecArgs A)
         wsp[s][h] = lse[h] == -INFINITY ? 0.f : fast_exp2(pm[s * 16 + h] - lse[h]);
     }
     __syncthreads();
-    // o_cmp
-    const float *po = A.po + (long)pair * nsplit * 16 * DV;
-    for (int e = tid; e < 16 * DV; e += kThreads) {
-        const int h = e / DV;
-        float acc = 0.f;
-        for (int s = 0; s < A.cs; s++) acc += po[(long)s * 16 * DV + e] * wsp[s][h];
-        A.ocmp[(long)pair * 16 * DV + e] = acc;
-    }
-    // block scores
     // block j: its own keys 4j..4j+3 (X) plus key 4j-1 (Y of block j-1);
     // phase A wrote blocks 0..nbp-1, a block past them has no key of its own
     const float *bx = A.bx + (long)pair * 16 * A.nbp, *by = A.by + (long)pair * 16 * A.nbp;
     constexpr int kBlkPerSplit = kSplitKeys / 4;
     for (int j = tid; j <= jcur; j += kThreads) {
-        float acc = 0.f;
         const int sj = j / kBlkPerSplit, sp = (j - 1) / kBlkPerSplit;
+        const bool hx = j < A.nbp, hy = j > 0 && j - 1 < A.nbp;
+        float xv[16], yv[16];
+#pragma unroll
         for (int h = 0; h < 16; h++) {
-            if (j < A.nbp) acc += bx[(long)h * A.nbp + j] * wsp[sj][h];
-            if (j > 0 && j - 1 < A.nbp) acc += by[(long)h * A.nbp + j - 1] * wsp[sp][h];
+            xv[h] = hx ? bx[(long)h * A.nbp + j] : 0.f;
+            yv[h] = hy ? by[(long)h * A.nbp + j - 1] : 0.f;
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int h = 0; h < 16; h++) {
+            acc += xv[h] * wsp[sj][h];
+            if (hy) acc += yv[h] * wsp[sp][h];
         }
         S[j] = acc;
     }
@@ -376,12 +399,14 @@ __global__ __launch_bounds__(kThreads) void k_dec_phase_c(DecArgs A)
     bf16x8 qf[DK / 32];
     load_qf<DK>((const uint16_t *)A.q + ((long)b * d.Hq + g * 16 + hd) * DK, q, qf);
     float s[2][8];
+    VRegs<DV> vr[2];
     float mx = -INFINITY;
     const int kend = j < 0 ? 0 : min(64 * j + 64, t + 1);
 #pragma unroll
     for (int st = 0; st < 2; st++) {
         const int base = 64 * j + 32 * st;
         if (j >= 0 && base < kend) {
+            load_v<DV>(V, base, d.T - 1, lane, vr[st]);
             logits_step<DK>(K, base, d.T - 1, qf, hd, q, s[st]);
 #pragma unroll
             for (int e = 0; e < 8; e++) {
@@ -412,8 +437,8 @@ __global__ __launch_bounds__(kThreads) void k_dec_phase_c(DecArgs A)
                 p[e] = fast_exp2(s[st][e] - M);
                 l += p[e];
             }
-            stage_vt<DV>(V, base, d.T - 1, vt, lane);
-            pv_step<DV>(vt, p, hd, q, oacc);
+            store_vt<DV>(vr[st], vt + st * DV * kVtS, lane);
+            pv_step<DV>(vt + st * DV * kVtS, p, hd, q, oacc);
         }
     }
     l = head_sum(l);
@@ -422,54 +447,75 @@ __global__ __launch_bounds__(kThreads) void k_dec_phase_c(DecArgs A)
 }
 
 // ---------------------------------------------------------------------------
-// Phase D.  One workgroup per (sequence, KV head): merge the window and the
-// selected partials, gates, o = g_cmp o_cmp + g_slc o_slc + g_win o_win.
+// Phase D.  Four workgroups per (sequence, KV head), four heads each: merge
+// the compressed, window and selected partials, the gates, and
+// o = g_cmp o_cmp + g_slc o_slc + g_win o_win.
+constexpr int kDHeads = 4;
+
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void k_dec_phase_d(DecArgs A)
 {
-    __shared__ float wts[2][64][16];   // [branch][split][head] merge weights
-    __shared__ float gate[16][3];
+    __shared__ float wts[3][64][kDHeads];   // [branch][split][head] merge weights
+    __shared__ float gate[kDHeads][3];
     const Dims &d = A.d;
-    const int pair = blockIdx.x;
+    const int pair = blockIdx.x / (16 / kDHeads), h0 = (blockIdx.x % (16 / kDHeads)) * kDHeads;
     const int b = pair / d.Hkv, g = pair % d.Hkv;
     const int tid = threadIdx.x;
     const int nsplit = A.cs + A.ws;
-    // partial lists: window = phase-A splits cs.., selected = phase-C splits
-    const float *wm = A.pm + ((long)pair * nsplit + A.cs) * 16, *wl = A.pl + ((long)pair * nsplit + A.cs) * 16;
-    const float *wo = A.po + ((long)pair * nsplit + A.cs) * 16 * DV;
-    const float *sm_ = A.sm + (long)pair * A.ss * 16, *sl = A.sl + (long)pair * A.ss * 16;
-    const float *so = A.so + (long)pair * A.ss * 16 * DV;
-    if (tid < 32) {
-        const int br = tid >> 4, h = tid & 15;
-        const int ns = br ? A.ss : A.ws;
-        const float *pm = br ? sm_ : wm, *pl = br ? sl : wl;
+    const float *pmA = A.pm + (long)pair * nsplit * 16, *plA = A.pl + (long)pair * nsplit * 16;
+    const float *pmC = A.sm + (long)pair * A.ss * 16, *plC = A.sl + (long)pair * A.ss * 16;
+    if (tid < 3 * kDHeads) {
+        // branch 0: compressed (splits 0..cs-1), 1: window (cs..cs+ws-1), 2: selected
+        const int br = tid / kDHeads, h = h0 + tid % kDHeads;
+        const int ns = br == 0 ? A.cs : (br == 1 ? A.ws : A.ss);
+        const float *pm = br == 2 ? pmC : pmA + (br == 1 ? A.cs * 16 : 0);
+        const float *pl = br == 2 ? plC : plA + (br == 1 ? A.cs * 16 : 0);
         float M = -INFINITY;
         for (int s = 0; s < ns; s++) M = fmaxf(M, pm[s * 16 + h]);
         float L = 0.f;
         if (M != -INFINITY)
             for (int s = 0; s < ns; s++) L += pl[s * 16 + h] * fast_exp2(pm[s * 16 + h] - M);
         for (int s = 0; s < ns; s++)
-            wts[br][s][h] = (M == -INFINITY || L <= 0.f) ? 0.f : fast_exp2(pm[s * 16 + h] - M) / L;
+            wts[br][s][tid % kDHeads] = (M == -INFINITY || L <= 0.f) ? 0.f : fast_exp2(pm[s * 16 + h] - M) / L;
     }
-    if (tid >= 64 && tid < 64 + 48) {
-        const int h = (tid - 64) / 3, c = (tid - 64) % 3;
+    // gates: 16 threads per (head, gate) dot product of length DK
+    if (tid < 16 * 3 * kDHeads) {
+        const int dot = tid >> 4, part = tid & 15;
+        const int h = h0 + dot / 3, c = dot % 3;
         const uint16_t *qr = (const uint16_t *)A.q + ((long)b * d.Hq + g * 16 + h) * DK;
         const uint16_t *wr = (const uint16_t *)A.wg + ((long)(g * 16 + h) * 3 + c) * DK;
-        float z = __uint_as_float((uint32_t)((const uint16_t *)A.bg)[(g * 16 + h) * 3 + c] << 16);
-        for (int x = 0; x < DK; x++) z += __uint_as_float((uint32_t)wr[x] << 16) * __uint_as_float((uint32_t)qr[x] << 16);
-        gate[h][c] = sigmoidf_(z);
+        float z = 0.f;
+        for (int ch = part; ch < DK / 8; ch += 16) {
+            const u32x4 wv = ld16(wr + 8 * ch), qv = ld16(qr + 8 * ch);
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                z += __uint_as_float(wv[e] << 16) * __uint_as_float(qv[e] << 16);
+                z += __uint_as_float(wv[e] & 0xffff0000u) * __uint_as_float(qv[e] & 0xffff0000u);
+            }
+        }
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) z += __shfl_xor(z, off, 16);
+        if (part == 0) {
+            z += __uint_as_float((uint32_t)((const uint16_t *)A.bg)[(g * 16 + h) * 3 + c] << 16);
+            gate[dot / 3][c] = sigmoidf_(z);
+        }
     }
     __syncthreads();
-    const float *oc = A.ocmp + (long)pair * 16 * DV;
+    const float *poA = A.po + (long)pair * nsplit * 16 * DV, *poC = A.so + (long)pair * A.ss * 16 * DV;
     uint16_t *o = (uint16_t *)A.o + ((long)b * d.Hq + g * 16) * DV;
-    for (int e = tid; e < 16 * DV; e += kThreads) {
-        const int h = e / DV;
-        float ow = 0.f, os = 0.f;
-        for (int s = 0; s < A.ws; s++) ow += wo[(long)s * 16 * DV + e] * wts[0][s][h];
-        for (int s = 0; s < A.ss; s++) os += so[(long)s * 16 * DV + e] * wts[1][s][h];
-        const float y = gate[h][0] * oc[e] + gate[h][1] * os + gate[h][2] * ow;
+    for (int e = tid; e < kDHeads * DV; e += kThreads) {
+        const int hl = e / DV, h = h0 + hl, c = e % DV;
+        const long off = (long)h * DV + c;
+        float oc = 0.f, ow = 0.f, os = 0.f;
+#pragma unroll 4
+        for (int s = 0; s < A.cs; s++) oc += poA[(long)s * 16 * DV + off] * wts[0][s][hl];
+#pragma unroll 2
+        for (int s = 0; s < A.ws; s++) ow += poA[(long)(A.cs + s) * 16 * DV + off] * wts[1][s][hl];
+#pragma unroll 4
+        for (int s = 0; s < A.ss; s++) os += poC[(long)s * 16 * DV + off] * wts[2][s][hl];
+        const float y = gate[hl][0] * oc + gate[hl][1] * os + gate[hl][2] * ow;
         __bf16 yb = (__bf16)y;
-        o[e] = __builtin_bit_cast(uint16_t, yb);
+        o[off] = __builtin_bit_cast(uint16_t, yb);
     }
 }
 
@@ -481,7 +527,7 @@ hipError_t launch_decode_dims(const DecArgs &A, hipStream_t s)
     hipLaunchKernelGGL((k_dec_phase_a<DK, DV>), dim3(pairs * (A.cs + A.ws)), dim3(kThreads), 0, s, A);
     hipLaunchKernelGGL((k_dec_phase_b<DV>), dim3(pairs), dim3(kThreads), sizeof(float) * d.nb, s, A);
     hipLaunchKernelGGL((k_dec_phase_c<DK, DV>), dim3(pairs * A.ss), dim3(kThreads), 0, s, A);
-    hipLaunchKernelGGL((k_dec_phase_d<DK, DV>), dim3(pairs), dim3(kThreads), 0, s, A);
+    hipLaunchKernelGGL((k_dec_phase_d<DK, DV>), dim3(pairs * (16 / kDHeads)), dim3(kThreads), 0, s, A);
     return hipGetLastError();
 }
 

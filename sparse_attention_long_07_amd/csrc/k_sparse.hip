@@ -19,8 +19,10 @@
 //    selected 64-token block is read once, straight into registers.  This
 //    part is bound by how fast blocks can be gathered, not by the MFMA.  It
 //    adds g_slc * o_slc to o.
-// V enters the selected kernel as V^T per 64-token block (k_vt_blocks), so
-// every operand fetch is one 16-byte load.
+// K and V enter the selected kernel packed per 64-token block in the order the
+// MFMA operands are held by the lanes (k_pack_blocks): adjacent lanes read
+// adjacent 16 bytes, so each operand fetch is one coalesced 1 KB load instead
+// of sixteen scattered row pieces.
 #include "mfma_util.h"
 #include "nsa_internal.h"
 
@@ -40,33 +42,58 @@ __device__ __forceinline__ int krow(int k)
 
 __device__ __forceinline__ float sigmoid(float z) { return 1.f / (1.f + __expf(-z)); }
 
-// V [bg][T][DV] -> V^T per 64-token block [bg][NB][DV][64]; tokens past T are 0.
-template <int DV>
-__global__ __launch_bounds__(kThreads) void k_vt_blocks(const uint16_t *__restrict__ v, uint16_t *__restrict__ vt,
-                                                        int T, int NB)
+// Fragment-major packing of K and V per 64-token block, so that every operand
+// fetch of the selected-block kernel is one coalesced 1 KB wavefront load.
+// Half block s (keys 32s .. 32s+31 of block j), lane l = 16q + hd:
+//   Kp[bg][j][s][X][kk][l] = K[64j + 32s + r(hd) + 4X][32kk + 8q .. +8]
+//      with r(i) = 8*(i/4) + i%4, X = 0/1 the two 16-key MFMA row tiles
+//   Vp[bg][j][s][dt][l]    = V[64j + 32s + 8q .. +8][16dt + hd]   (V^T)
+// Tokens past T are 0.
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads) void k_pack_blocks(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+                                                          uint16_t *__restrict__ kp, uint16_t *__restrict__ vp, int T,
+                                                          int NB)
 {
-    __shared__ uint16_t tile[kTile][DV + 2];
+    constexpr int KS = DK / 32, DT = DV / 16;
+    __shared__ uint16_t kt[kTile][DK + 8];
+    __shared__ uint16_t vtile[kTile][DV + 2];
     const int j = blockIdx.x, bg = blockIdx.y, tid = threadIdx.x;
-    const uint16_t *src = v + ((long)bg * T + (long)kTile * j) * DV;
+    const uint16_t *ks = k + ((long)bg * T + (long)kTile * j) * DK;
+    const uint16_t *vs = v + ((long)bg * T + (long)kTile * j) * DV;
+    for (int e = tid; e < kTile * DK / 8; e += kThreads) {
+        const int key = e / (DK / 8), ch = e % (DK / 8);
+        u32x4 x = {0, 0, 0, 0};
+        if (kTile * j + key < T) x = ld16(ks + (long)key * DK + ch * 8);
+        st16(&kt[key][ch * 8], x);
+    }
     for (int e = tid; e < kTile * DV / 8; e += kThreads) {
         const int key = e / (DV / 8), ch = e % (DV / 8);
         u32x4 x = {0, 0, 0, 0};
-        if (kTile * j + key < T) x = ld16(src + key * DV + ch * 8);
+        if (kTile * j + key < T) x = ld16(vs + (long)key * DV + ch * 8);
 #pragma unroll
         for (int q = 0; q < 4; q++) {
-            tile[key][ch * 8 + 2 * q] = (uint16_t)(x[q] & 0xffffu);
-            tile[key][ch * 8 + 2 * q + 1] = (uint16_t)(x[q] >> 16);
+            vtile[key][ch * 8 + 2 * q] = (uint16_t)(x[q] & 0xffffu);
+            vtile[key][ch * 8 + 2 * q + 1] = (uint16_t)(x[q] >> 16);
         }
     }
     __syncthreads();
-    uint16_t *dst = vt + ((long)bg * NB + j) * DV * kTile;
-    for (int e = tid; e < DV * kTile / 8; e += kThreads) {
-        const int dv = e / (kTile / 8), kc = e % (kTile / 8);
+    uint16_t *kd = kp + ((long)bg * NB + j) * kTile * DK;
+    for (int e = tid; e < 2 * 2 * KS * 64; e += kThreads) {
+        const int l = e & 63, kk = (e >> 6) % KS, X = (e / (64 * KS)) & 1, s = e / (128 * KS);
+        const int q = l >> 4, hd = l & 15;
+        const int key = 32 * s + 8 * (hd >> 2) + (hd & 3) + 4 * X;
+        st16(kd + (long)e * 8, ld16(&kt[key][32 * kk + 8 * q]));
+    }
+    uint16_t *vd = vp + ((long)bg * NB + j) * kTile * DV;
+    for (int e = tid; e < 2 * DT * 64; e += kThreads) {
+        const int l = e & 63, dt = (e >> 6) % DT, s = e / (64 * DT);
+        const int q = l >> 4, hd = l & 15;
+        const int key0 = 32 * s + 8 * q, dv = 16 * dt + hd;
         u32x4 x;
 #pragma unroll
-        for (int q = 0; q < 4; q++)
-            x[q] = (uint32_t)tile[kc * 8 + 2 * q][dv] | ((uint32_t)tile[kc * 8 + 2 * q + 1][dv] << 16);
-        st16(dst + dv * kTile + kc * 8, x);
+        for (int u = 0; u < 4; u++)
+            x[u] = (uint32_t)vtile[key0 + 2 * u][dv] | ((uint32_t)vtile[key0 + 2 * u + 1][dv] << 16);
+        st16(vd + (long)e * 8, x);
     }
 }
 
@@ -257,7 +284,8 @@ __global__ __launch_bounds__(kThreads) void k_window_mfma(RowArgs a, int ntp)
 // 8*(i/4) + 4 + i%4 (tile B) in row i, so their outputs are exactly the
 // B operand of O^T = V^T P^T.
 template <int DK, int DV>
-__global__ __launch_bounds__(kThreads) void k_selected_mfma(RowArgs a, const uint16_t *__restrict__ vt, int ntp)
+__global__ __launch_bounds__(kThreads) void k_selected_mfma(RowArgs a, const uint16_t *__restrict__ kpk,
+                                                            const uint16_t *__restrict__ vpk, int ntp)
 {
     constexpr int KS = DK / 32;     // 16x16x32 steps over the head dim
     constexpr int DT = DV / 16;     // 16-wide dv tiles
@@ -301,7 +329,9 @@ __global__ __launch_bounds__(kThreads) void k_selected_mfma(RowArgs a, const uin
         gsl = sigmoid(z + __uint_as_float((uint32_t)*bp << 16));
     }
 
-    // the row's blocks: valid (0..jcur) and first occurrence only
+    // the row's blocks: valid (0..jcur) and first occurrence only, compacted
+    // into this wavefront's slot list
+    __shared__ int blist[4][16];
     int jb = -1;
     if (lane < d.n) jb = a.idx[((long)bg * a.R + t) * d.n + lane];
     bool ok = jb >= 0 && jb <= jcur;
@@ -309,68 +339,78 @@ __global__ __launch_bounds__(kThreads) void k_selected_mfma(RowArgs a, const uin
         const int other = __shfl(jb, u, 64);
         if (u < lane && other == jb) ok = false;
     }
-    uint64_t todo = __ballot(ok);
+    const uint64_t valid = __ballot(ok);
+    if (ok) blist[wave][__popcll(valid & __lanemask_lt())] = jb;
+    const int nitems = 2 * __popcll(valid);   // half blocks of 32 keys
 
-    const uint16_t *kg = (const uint16_t *)a.k + (long)bg * d.T * DK;
-    const uint16_t *vtg = vt + (long)bg * d.nb * DV * kTile;
-    const int krA = 8 * (hd >> 2) + (hd & 3);     // key of MFMA row hd in tile A
+    const uint16_t *kpg = kpk + (long)bg * d.nb * kTile * DK;
+    const uint16_t *vpg = vpk + (long)bg * d.nb * kTile * DV;
     float m = -INFINITY, l = 0.f;
     f32x4 oacc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; dt++) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    while (todo) {
-        const int src = __builtin_ctzll(todo);
-        todo &= todo - 1;
-        const int j = __shfl(jb, src, 64);
-        const int key0 = j * kTile;
+    // Half block `it` = keys 32*(it%2) .. +31 of block blist[it/2].  Loads of
+    // the next half block are issued before the current one is computed.
+    struct Stage {
+        bf16x8 fa[KS], fb[KS], fv[DT];
+    };
+    auto load_item = [&](int it, Stage &st) {
+        const int j = blist[wave][it >> 1], s = it & 1;
+        const uint16_t *kb = kpg + ((long)j * 2 + s) * 32 * DK + lane * 8;
 #pragma unroll
-        for (int s = 0; s < 2; s++) {
-            const int kA = min(key0 + 32 * s + krA, d.T - 1), kB = min(key0 + 32 * s + krA + 4, d.T - 1);
-            bf16x8 fa[KS], fb[KS];
-#pragma unroll
-            for (int kk = 0; kk < KS; kk++) {
-                fa[kk] = as_bf16x8(ld16(kg + (long)kA * DK + 32 * kk + 8 * q));
-                fb[kk] = as_bf16x8(ld16(kg + (long)kB * DK + 32 * kk + 8 * q));
-            }
-            bf16x8 fv[DT];
-            const uint16_t *vb = vtg + ((long)j * DV + hd) * kTile + 32 * s + 8 * q;
-#pragma unroll
-            for (int dt = 0; dt < DT; dt++) fv[dt] = as_bf16x8(ld16(vb + 16 * dt * kTile));
-            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KS; kk++) {
-                accA = mfma16(fa[kk], qf[kk], accA);
-                accB = mfma16(fb[kk], qf[kk], accB);
-            }
-            float sv[8], mx = -INFINITY;
-#pragma unroll
-            for (int u = 0; u < 4; u++) {
-                const int ka = key0 + 32 * s + 8 * q + u;
-                sv[u] = ka <= t ? accA[u] * sl2 : -INFINITY;
-                sv[4 + u] = ka + 4 <= t ? accB[u] * sl2 : -INFINITY;
-                mx = fmaxf(mx, fmaxf(sv[u], sv[4 + u]));
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float mn = fmaxf(m, mx);
-            if (mn == -INFINITY) continue;   // every key of this half block is past t: uniform over the wave
-            const float al = fast_exp2(m - mn);
-            float p[8], sum = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-                p[e] = fast_exp2(sv[e] - mn);
-                sum += p[e];
-            }
-            l = l * al + sum;
-            m = mn;
-            const bf16x8 pb = pack8(p);
-#pragma unroll
-            for (int dt = 0; dt < DT; dt++) {
-                oacc[dt] *= al;
-                oacc[dt] = mfma16(fv[dt], pb, oacc[dt]);
-            }
+        for (int kk = 0; kk < KS; kk++) {
+            st.fa[kk] = as_bf16x8(ld16(kb + kk * 512));
+            st.fb[kk] = as_bf16x8(ld16(kb + (KS + kk) * 512));
         }
+        const uint16_t *vb = vpg + ((long)j * 2 + s) * 32 * DV + lane * 8;
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) st.fv[dt] = as_bf16x8(ld16(vb + dt * 512));
+    };
+    auto compute_item = [&](int it, const Stage &st) {
+        const int key0 = blist[wave][it >> 1] * kTile + 32 * (it & 1);
+        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; kk++) {
+            accA = mfma16(st.fa[kk], qf[kk], accA);
+            accB = mfma16(st.fb[kk], qf[kk], accB);
+        }
+        float sv[8], mx = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int ka = key0 + 8 * q + u;
+            sv[u] = ka <= t ? accA[u] * sl2 : -INFINITY;
+            sv[4 + u] = ka + 4 <= t ? accB[u] * sl2 : -INFINITY;
+            mx = fmaxf(mx, fmaxf(sv[u], sv[4 + u]));
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mn = fmaxf(m, mx);
+        if (mn == -INFINITY) return;   // every key of this half block is past t: uniform over the wave
+        const float al = fast_exp2(m - mn);
+        float p[8], sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            p[e] = fast_exp2(sv[e] - mn);
+            sum += p[e];
+        }
+        l = l * al + sum;
+        m = mn;
+        const bf16x8 pb = pack8(p);
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) {
+            oacc[dt] *= al;
+            oacc[dt] = mfma16(st.fv[dt], pb, oacc[dt]);
+        }
+    };
+    Stage sa, sb;
+    if (nitems > 0) load_item(0, sa);
+    for (int it = 0; it < nitems; it += 2) {
+        if (it + 1 < nitems) load_item(it + 1, sb);
+        compute_item(it, sa);
+        if (it + 1 >= nitems) break;
+        if (it + 2 < nitems) load_item(it + 2, sa);
+        compute_item(it + 1, sb);
     }
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
@@ -396,16 +436,17 @@ hipError_t launch_sparse_dims(const RowArgs &a, void *vt_ws, hipStream_t s)
 {
     const Dims &d = a.d;
     const int BG = d.B * d.Hkv;
-    hipLaunchKernelGGL(k_vt_blocks<DV>, dim3(d.nb, BG), dim3(kThreads), 0, s, (const uint16_t *)a.v,
-                       (uint16_t *)vt_ws, d.T, d.nb);
+    uint16_t *kpk = (uint16_t *)vt_ws;
+    uint16_t *vpk = kpk + (size_t)BG * d.nb * kTile * DK;
+    hipLaunchKernelGGL((k_pack_blocks<DK, DV>), dim3(d.nb, BG), dim3(kThreads), 0, s, (const uint16_t *)a.k,
+                       (const uint16_t *)a.v, kpk, vpk, d.T, d.nb);
     const int ntp = (a.R + kPos - 1) / kPos;
     long nwg = (long)BG * ntp;
     nwg = (nwg + 7) / 8 * 8;
     hipLaunchKernelGGL((k_window_mfma<DK, DV>), dim3((unsigned)nwg), dim3(kThreads), 0, s, a, ntp);
     const int ntp4 = (a.R + 3) / 4;
     long nwg4 = ((long)BG * ntp4 + 7) / 8 * 8;
-    hipLaunchKernelGGL((k_selected_mfma<DK, DV>), dim3((unsigned)nwg4), dim3(kThreads), 0, s, a,
-                       (const uint16_t *)vt_ws, ntp4);
+    hipLaunchKernelGGL((k_selected_mfma<DK, DV>), dim3((unsigned)nwg4), dim3(kThreads), 0, s, a, kpk, vpk, ntp4);
     return hipGetLastError();
 }
 
@@ -417,7 +458,7 @@ bool sparse_mfma_supported(const Dims &d)
            ((d.dk == 192 && d.dv == 128) || (d.dk == 128 && d.dv == 128) || (d.dk == 64 && d.dv == 64));
 }
 
-size_t sparse_mfma_ws_bytes(const Dims &d) { return (size_t)d.B * d.Hkv * d.nb * 64 * d.dv * 2; }
+size_t sparse_mfma_ws_bytes(const Dims &d) { return (size_t)d.B * d.Hkv * d.nb * 64 * (d.dk + d.dv) * 2; }
 
 hipError_t launch_sparse_mfma(const RowArgs &a, void *vt_ws, hipStream_t s)
 {

@@ -84,7 +84,7 @@ hipError_t launch_sparse_generic(const RowArgs &a, hipStream_t s);
 bool cmp_attn_mfma_supported(const Dims &d);
 hipError_t launch_cmp_attn_mfma(const RowArgs &a, bool with_v, hipStream_t s);
 bool sparse_mfma_supported(const Dims &d);
-size_t sparse_mfma_ws_bytes(const Dims &d);   // V^T per 64-token block
+size_t sparse_mfma_ws_bytes(const Dims &d);   // K and V packed per 64-token block
 hipError_t launch_sparse_mfma(const RowArgs &a, void *vt_ws, hipStream_t s);
 bool decode_mfma_supported(const Dims &d);
 size_t decode_mfma_layout(const Dims &d, void *ws, DecArgs *A);   // bytes; fills A's buffers if ws
