@@ -41,7 +41,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(s, x, flops_total, rows_sample=192, seed=5):
+def cpu_baseline(s, x, flops_total, rows_sample=4096, seed=5):
     """The oracle on a bounded sample of the prefill workload: the full
     compression of all tokens plus `rows_sample` query positions drawn
     uniformly (every KV group); extrapolated to the whole workload."""
@@ -77,8 +77,21 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=192)
+    ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--traffic", type=float, default=None,
+                    help="HBM bytes per launch of the roofline kernel from FETCH_SIZE/WRITE_SIZE counters")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB once (counter calibration) and exit")
     args = ap.parse_args()
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": 4 * n}), flush=True)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this NSA build has no multi-GPU path (--gpus %d requested)"
               % args.gpus, flush=True)
@@ -169,13 +182,17 @@ def main():
                                   "TFLOP/s"),
         "decode_step": ("hbm", dec_bytes, PEAK_HBM_GBPS, "GB/s"),
     }
-    dom = stages[int(np.argmax(st_ms))]
+    # the roofline line is for the dominant single-kernel stage: S2 and S3 are
+    # one launch each (S1 launches its kernel twice, S4 runs three kernels,
+    # the decode step four; their times are in stage_ms)
+    single = {"S2_compressed_attention": "k_cmp_attn_mfma", "S3_select": "k_select_generic"}
+    dom = max(single, key=lambda k: st_ms[stages.index(k)])
     bound, units, peak, unit = work[dom]
     dur_s = st_ms[stages.index(dom)] * 1e-3
     achieved = units / dur_s / (1e12 if unit == "TFLOP/s" else 1e9)
-    roof = {"bound": bound, "kernel": dom, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": None,
-            "avg_launch_ms": round(float(dur_s * 1e3), 4)}
+    roof = {"bound": bound, "kernel": single[dom], "stage": dom, "achieved": round(achieved, 2), "peak": peak,
+            "unit": unit, "frac": round(achieved / peak, 4), "traffic": args.traffic,
+            "avg_launch_ms": round(float(dur_s * 1e3), 4), "algorithmic_per_launch": units}
 
     res = {
         "metric": "NSA fwd TFLOP/s @64k prefill",
