@@ -7,6 +7,7 @@
 // sizes from valuable12.com, "AI 모델의 '긴 문장 처리' 한계 돌파, 딥시크의 새
 // 어텐션 기술 화제", section II.
 #include "nsa_internal.h"
+#include "select_util.h"
 
 #include <math.h>
 
@@ -221,12 +222,7 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_generic(RowArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Top-n block selection, one wavefront per (row, KV head).  Candidates are
-// blocks 0..jc (jc = t/64).  Blocks 0, jc-1 and jc are always kept; the
-// remaining n - #forced picks are made one at a time by a wavefront argmax
-// (higher score first, lower block on ties) over the not-yet-chosen blocks;
-// lane L owns blocks L, L+64, ...  The chosen set is written in ascending
-// order with a ballot prefix count, then padded with -1.
+// Top-n block selection, one wavefront per (row, KV head): see select_util.h.
 __global__ __launch_bounds__(kThreads) void k_select_generic(RowArgs a)
 {
     const Dims &d = a.d;
@@ -237,57 +233,7 @@ __global__ __launch_bounds__(kThreads) void k_select_generic(RowArgs a)
     const int r = (int)(row % a.R);
     const int b = (int)(row / ((long)d.Hkv * a.R));
     const int t = row_t(a, b, r);
-    const float *S = a.scores + row * d.nb;
-    int32_t *out = a.idx_sel + row * d.n;
-    const int jcur = t / 64, ncand = jcur + 1;
-    const int nforced = jcur == 0 ? 1 : (jcur == 1 ? 2 : 3);
-    const int k = d.n - nforced;
-    const int RR = (ncand + kWave - 1) / kWave;   // <= 128 since nb <= 8192
-    uint64_t chosen[2] = {0, 0};
-    auto setbit = [&](int rr) { chosen[rr >> 6] |= 1ull << (rr & 63); };
-    auto getbit = [&](int rr) { return (chosen[rr >> 6] >> (rr & 63)) & 1ull; };
-    // forced blocks
-    if (lane == 0) setbit(0);
-    if (jcur >= 1 && (jcur - 1) % kWave == lane) setbit((jcur - 1) / kWave);
-    if (jcur % kWave == lane) setbit(jcur / kWave);
-    if (ncand - nforced <= k) {
-        for (int rr = 0; rr < RR; rr++)
-            if (lane + rr * kWave < ncand) setbit(rr);
-    } else {
-        for (int round = 0; round < k; round++) {
-            float bs = -INFINITY;
-            int bj = 0x7fffffff;
-            for (int rr = 0; rr < RR; rr++) {
-                int j = lane + rr * kWave;
-                if (j < ncand && !getbit(rr)) {
-                    float s = S[j];
-                    s = s == s ? s : -INFINITY;
-                    if (s > bs || (s == bs && j < bj)) {
-                        bs = s;
-                        bj = j;
-                    }
-                }
-            }
-            for (int off = 32; off > 0; off >>= 1) {
-                float os = __shfl_xor(bs, off, kWave);
-                int oj = __shfl_xor(bj, off, kWave);
-                if (os > bs || (os == bs && oj < bj)) {
-                    bs = os;
-                    bj = oj;
-                }
-            }
-            if (bj % kWave == lane) setbit(bj / kWave);
-        }
-    }
-    int base = 0;
-    const uint64_t lt = __lanemask_lt();
-    for (int rr = 0; rr < RR; rr++) {
-        bool bit = getbit(rr) && (lane + rr * kWave < ncand);
-        uint64_t bal = __ballot(bit);
-        if (bit) out[base + __popcll(bal & lt)] = lane + rr * kWave;
-        base += __popcll(bal);
-    }
-    for (int q = base + lane; q < d.n; q += kWave) out[q] = -1;
+    wave_select_topn(a.scores + row * d.nb, t / 64, d.n, a.idx_sel + row * d.n, lane);
 }
 
 // ---------------------------------------------------------------------------

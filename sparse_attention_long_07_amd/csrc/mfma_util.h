@@ -99,4 +99,15 @@ __device__ __forceinline__ float row_transpose_sum16(const float v[16], int lane
     return keep + dpp<kQuadXor1>(send);
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also fences
+// global memory, which makes every wave wait for its outstanding global loads
+// first and so cancels any prefetch in flight; the barriers in these kernels
+// only ever protect LDS data.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace nsa
