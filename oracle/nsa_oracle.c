@@ -44,11 +44,16 @@
  *    o = g_cmp*o_cmp + g_slc*o_slc + g_win*o_win.
  *  - an empty visible set (t < l - 1) gives o_cmp = 0 and zero scores.
  *  - decode: the query is the last cached token, t = seq_len - 1.
+ *  - backward ([deepdaiv]: the sparsity is learned in training, so the three
+ *    branches, the compression map and the gates are differentiated): the
+ *    block selection is piecewise constant and held fixed; the bf16 rounding
+ *    of the compressed K/V (bf16 configurations) is passed straight through.
  */
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
 #include <fenv.h>
+#include <omp.h>
 
 typedef struct {
     int B, T, Hkv, G, dk, dv; /* H_q = Hkv*G; query head h belongs to KV group h/G */
@@ -383,4 +388,260 @@ void orc_decode(const orc_cfg *c, const int *seq_lens, const double *q, const do
 int orc_select(const orc_cfg *c, int t, const double *S, int *idx)
 {
     return select_blocks(c, t, S, idx);
+}
+
+/* ------------------------------------------------------------------------
+ * Backward pass.  Reverse mode through the gates, the three attention
+ * branches and the compression, with the block selection held fixed (it is
+ * piecewise constant in the inputs, so no gradient flows through the
+ * importance scores).  The loss is L = sum(dO * o).
+ *
+ * Softmax attention over a key list with p = softmax(s), s_i = scale q.K_i,
+ * o = sum_i p_i V_i and output gradient do:
+ *   dV_i += p_i do;  dP_i = do.V_i;  D = sum_i p_i dP_i;  ds_i = p_i (dP_i - D)
+ *   dq += scale sum_i ds_i K_i;  dK_i += scale ds_i q
+ * Gate c of head h: g = sigmoid(z), z = W_g[h][c].q_h + b_g[h][c];
+ *   dz = (dO.o_c) g (1 - g);  dW_g[h][c] += dz q_h;  db_g[h][c] += dz;  dq_h += dz W_g[h][c]
+ * Compression: K_cmp[i] = W X_i with X_i = vec(x[16i .. 16i+31] + PE):
+ *   dW += dK_cmp[i] X_i^T;  dX_i = W^T dK_cmp[i];  dx[16i + tau] += dX_i[tau];  dPE[tau] += dX_i[tau]
+ * ------------------------------------------------------------------------ */
+
+/* p over an explicit key list (returns 0 and leaves p untouched if empty) */
+static int softmax_list(const double *qh, const double *K, int dk, double scale, const int *rows, int nrows,
+                        double *p)
+{
+    if (nrows == 0) return 0;
+    double mx = -INFINITY;
+    for (int r = 0; r < nrows; r++) {
+        const double *kr = K + (size_t)rows[r] * dk;
+        double dot = 0.0;
+        for (int e = 0; e < dk; e++) dot += qh[e] * kr[e];
+        p[r] = scale * dot;
+        if (p[r] > mx) mx = p[r];
+    }
+    double sum = 0.0;
+    for (int r = 0; r < nrows; r++) {
+        p[r] = exp(p[r] - mx);
+        sum += p[r];
+    }
+    for (int r = 0; r < nrows; r++) p[r] /= sum;
+    return nrows;
+}
+
+/* One attention branch for one head: forward output o and the backward
+ * contributions for output gradient do. */
+static void attend_backward(const double *qh, const double *K, const double *V, int dk, int dv, double scale,
+                            const int *rows, int nrows, const double *dout, double *p, double *o, double *dq,
+                            double *dK, double *dV)
+{
+    for (int cc = 0; cc < dv; cc++) o[cc] = 0.0;
+    if (!softmax_list(qh, K, dk, scale, rows, nrows, p)) return;
+    for (int r = 0; r < nrows; r++)
+        for (int cc = 0; cc < dv; cc++) o[cc] += p[r] * V[(size_t)rows[r] * dv + cc];
+    if (!dout || nrows <= 0) return;
+    double D = 0.0;
+    double *dP = (double *)malloc(sizeof(double) * (size_t)nrows);
+    for (int r = 0; r < nrows; r++) {
+        const double *vr = V + (size_t)rows[r] * dv;
+        double x = 0.0;
+        for (int cc = 0; cc < dv; cc++) x += dout[cc] * vr[cc];
+        dP[r] = x;
+        D += p[r] * x;
+    }
+    for (int r = 0; r < nrows; r++) {
+        const double ds = p[r] * (dP[r] - D);
+        const double *kr = K + (size_t)rows[r] * dk;
+        double *dkr = dK + (size_t)rows[r] * dk;
+        double *dvr = dV + (size_t)rows[r] * dv;
+        for (int e = 0; e < dk; e++) {
+            dq[e] += scale * ds * kr[e];
+            dkr[e] += scale * ds * qh[e];
+        }
+        for (int cc = 0; cc < dv; cc++) dvr[cc] += p[r] * dout[cc];
+    }
+    free(dP);
+}
+
+/* Compression backward for one tensor: dC [BH][N][dim] -> dW [dim][l*dim],
+ * dPE [l][dim], dx [BH][T][dim] (all accumulated).  With X_i the flattened
+ * block i plus PE:  dX_i = W^T dC[i];  dW = sum_i dC[i] X_i^T;  token 16i+tau
+ * and PE[tau] collect dX_i[tau].  dX for every block is formed first (blocks
+ * are independent), then added into dx and dPE in block order. */
+static void compress_backward(int BH, int T, int dim, int l, int d, int N, const double *x, const double *W,
+                              const double *PE, const double *dC, double *dW, double *dPE, double *dx)
+{
+    const int L = l * dim;
+    double *dX = (double *)malloc(sizeof(double) * (size_t)BH * N * L);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int bh = 0; bh < BH; bh++)
+        for (int i = 0; i < N; i++) {
+            const double *g = dC + ((size_t)bh * N + i) * dim;
+            double *dXi = dX + ((size_t)bh * N + i) * L;
+            for (int m = 0; m < L; m++) {
+                double acc = 0.0;
+                for (int c = 0; c < dim; c++) acc += W[(size_t)c * L + m] * g[c];
+                dXi[m] = acc;
+            }
+        }
+    for (int bh = 0; bh < BH; bh++)
+        for (int i = 0; i < N; i++) {
+            const double *dXi = dX + ((size_t)bh * N + i) * L;
+            double *dxs = dx + (size_t)bh * T * dim;
+            for (int m = 0; m < L; m++) {
+                dxs[(size_t)i * d * dim + m] += dXi[m];
+                dPE[m] += dXi[m];
+            }
+        }
+    /* each thread owns whole rows c of dW */
+#pragma omp parallel for schedule(static)
+    for (int c = 0; c < dim; c++)
+        for (int bh = 0; bh < BH; bh++)
+            for (int i = 0; i < N; i++) {
+                const double gc = dC[((size_t)bh * N + i) * dim + c];
+                if (gc == 0.0) continue;
+                const double *xs = x + ((size_t)bh * T + (size_t)i * d) * dim;
+                double *row = dW + (size_t)c * L;
+                for (int m = 0; m < L; m++) row[m] += gc * (xs[m] + PE[m]);
+            }
+    free(dX);
+}
+
+/* Full backward.  Layouts as in the forward; idx [B][Hkv][T][n] is the
+ * selection used by the forward.  Gradients are written (not accumulated):
+ * dq [B][T][Hq][dk], dk/dv [B][Hkv][T][dk|dv], dwck [dk][l*dk], dpek [l][dk],
+ * dwcv [dv][l*dv], dpev [l][dv], dwg [Hq][3][dk], dbg [Hq][3].  The
+ * compressed K/V are recomputed from k/v (rounded to bf16 if round_bf16, the
+ * rounding being passed straight through in reverse). */
+void orc_backward(const orc_cfg *c, const double *q, const double *k, const double *v, const double *wck,
+                  const double *pek, const double *wcv, const double *pev, const double *wg, const double *bg,
+                  const int *idx, const double *dO, int round_bf16, double *dq, double *dk, double *dv,
+                  double *dwck, double *dpek, double *dwcv, double *dpev, double *dwg, double *dbg)
+{
+    const int B = c->B, T = c->T, Hkv = c->Hkv, G = c->G, Hq = Hkv * G, dk_ = c->dk, dv_ = c->dv, n = c->n;
+    const int N = orc_n_cmp(T, c->l, c->d);
+    const int Nn = N > 0 ? N : 1;
+    double *kc = (double *)calloc((size_t)B * Hkv * Nn * dk_, sizeof(double));
+    double *vc = (double *)calloc((size_t)B * Hkv * Nn * dv_, sizeof(double));
+    orc_compress(B, Hkv, T, dk_, c->l, c->d, N, round_bf16, k, wck, pek, kc);
+    orc_compress(B, Hkv, T, dv_, c->l, c->d, N, round_bf16, v, wcv, pev, vc);
+    const size_t nq = (size_t)B * T * Hq * dk_, nk = (size_t)B * Hkv * T * dk_, nv = (size_t)B * Hkv * T * dv_;
+    const size_t nkc = (size_t)B * Hkv * Nn * dk_, nvc = (size_t)B * Hkv * Nn * dv_;
+    memset(dq, 0, sizeof(double) * nq);
+    memset(dk, 0, sizeof(double) * nk);
+    memset(dv, 0, sizeof(double) * nv);
+    memset(dwck, 0, sizeof(double) * (size_t)dk_ * c->l * dk_);
+    memset(dpek, 0, sizeof(double) * (size_t)c->l * dk_);
+    memset(dwcv, 0, sizeof(double) * (size_t)dv_ * c->l * dv_);
+    memset(dpev, 0, sizeof(double) * (size_t)c->l * dv_);
+    memset(dwg, 0, sizeof(double) * (size_t)Hq * 3 * dk_);
+    memset(dbg, 0, sizeof(double) * (size_t)Hq * 3);
+    double *dkc = (double *)calloc(nkc, sizeof(double));
+    double *dvc = (double *)calloc(nvc, sizeof(double));
+
+#pragma omp parallel
+    {
+        /* thread-private accumulators, reduced in thread order below */
+        double *a_dk = (double *)calloc(nk, sizeof(double));
+        double *a_dv = (double *)calloc(nv, sizeof(double));
+        double *a_dkc = (double *)calloc(nkc, sizeof(double));
+        double *a_dvc = (double *)calloc(nvc, sizeof(double));
+        double *a_dwg = (double *)calloc((size_t)Hq * 3 * dk_, sizeof(double));
+        double *a_dbg = (double *)calloc((size_t)Hq * 3, sizeof(double));
+        int *rows = (int *)malloc(sizeof(int) * (size_t)(T + Nn + 1));
+        double *p = (double *)malloc(sizeof(double) * (size_t)(T + Nn + 1));
+        double *o3 = (double *)malloc(sizeof(double) * 3 * (size_t)dv_);
+        double *dout = (double *)malloc(sizeof(double) * (size_t)dv_);
+#pragma omp for schedule(dynamic, 1)
+        for (long job = 0; job < (long)B * Hkv * T; job++) {
+            const int t = (int)(job % T), g = (int)((job / T) % Hkv), b = (int)(job / ((long)T * Hkv));
+            const size_t bg_ = (size_t)b * Hkv + g;
+            const double *kcg = kc + bg_ * Nn * dk_, *vcg = vc + bg_ * Nn * dv_;
+            const double *kg = k + bg_ * T * dk_, *vg = v + bg_ * T * dv_;
+            double *dkcg = a_dkc + bg_ * Nn * dk_, *dvcg = a_dvc + bg_ * Nn * dv_;
+            double *dkg = a_dk + bg_ * T * dk_, *dvg = a_dv + bg_ * T * dv_;
+            const int nvis = (t - (c->l - 1) >= 0) ? (t - (c->l - 1)) / c->d + 1 : 0;
+            const int lo = t - c->w + 1 > 0 ? t - c->w + 1 : 0;
+            /* selected token list (a set of blocks, causal) */
+            const int *ir = idx + (bg_ * T + t) * n;
+            int jcur = t / c->lsel;
+            /* a row with dO = 0 on every head of the group contributes nothing */
+            int live = 0;
+            for (size_t e = 0; e < (size_t)G * dv_ && !live; e++)
+                live = dO[((size_t)b * T + t) * Hq * dv_ + (size_t)g * G * dv_ + e] != 0.0;
+            if (!live) continue;
+            for (int hh = 0; hh < G; hh++) {
+                const int h = g * G + hh;
+                const double *qh = q + (((size_t)b * T + t) * Hq + h) * dk_;
+                const double *dOh = dO + (((size_t)b * T + t) * Hq + h) * dv_;
+                double *dqh = dq + (((size_t)b * T + t) * Hq + h) * dk_;
+                /* forward of the three branches */
+                int nr;
+                for (int i = 0; i < nvis; i++) rows[i] = i;
+                attend_backward(qh, kcg, vcg, dk_, dv_, c->scale, rows, nvis, NULL, p, o3, NULL, NULL, NULL);
+                nr = 0;
+                for (int jj = 0; jj <= jcur; jj++) {
+                    int in = 0;
+                    for (int u = 0; u < n; u++) in |= ir[u] == jj;
+                    if (!in) continue;
+                    for (int tau = jj * c->lsel; tau < (jj + 1) * c->lsel && tau <= t; tau++) rows[nr++] = tau;
+                }
+                attend_backward(qh, kg, vg, dk_, dv_, c->scale, rows, nr, NULL, p, o3 + dv_, NULL, NULL, NULL);
+                nr = 0;
+                for (int tau = lo; tau <= t; tau++) rows[nr++] = tau;
+                attend_backward(qh, kg, vg, dk_, dv_, c->scale, rows, nr, NULL, p, o3 + 2 * dv_, NULL, NULL, NULL);
+                /* gates */
+                double gate[3];
+                for (int cc = 0; cc < 3; cc++) {
+                    const double *wr = wg + ((size_t)h * 3 + cc) * dk_;
+                    double z = bg[h * 3 + cc];
+                    for (int e = 0; e < dk_; e++) z += wr[e] * qh[e];
+                    gate[cc] = 1.0 / (1.0 + exp(-z));
+                    double dg = 0.0;
+                    for (int e = 0; e < dv_; e++) dg += dOh[e] * o3[cc * dv_ + e];
+                    const double dz = dg * gate[cc] * (1.0 - gate[cc]);
+                    for (int e = 0; e < dk_; e++) {
+                        a_dwg[((size_t)h * 3 + cc) * dk_ + e] += dz * qh[e];
+                        dqh[e] += dz * wr[e];
+                    }
+                    a_dbg[h * 3 + cc] += dz;
+                }
+                /* backward of the three branches with do = g_c dO */
+                for (int e = 0; e < dv_; e++) dout[e] = gate[0] * dOh[e];
+                for (int i = 0; i < nvis; i++) rows[i] = i;
+                attend_backward(qh, kcg, vcg, dk_, dv_, c->scale, rows, nvis, dout, p, o3, dqh, dkcg, dvcg);
+                for (int e = 0; e < dv_; e++) dout[e] = gate[1] * dOh[e];
+                nr = 0;
+                for (int jj = 0; jj <= jcur; jj++) {
+                    int in = 0;
+                    for (int u = 0; u < n; u++) in |= ir[u] == jj;
+                    if (!in) continue;
+                    for (int tau = jj * c->lsel; tau < (jj + 1) * c->lsel && tau <= t; tau++) rows[nr++] = tau;
+                }
+                attend_backward(qh, kg, vg, dk_, dv_, c->scale, rows, nr, dout, p, o3 + dv_, dqh, dkg, dvg);
+                for (int e = 0; e < dv_; e++) dout[e] = gate[2] * dOh[e];
+                nr = 0;
+                for (int tau = lo; tau <= t; tau++) rows[nr++] = tau;
+                attend_backward(qh, kg, vg, dk_, dv_, c->scale, rows, nr, dout, p, o3 + 2 * dv_, dqh, dkg, dvg);
+            }
+        }
+        int nth = omp_get_num_threads(), me = omp_get_thread_num();
+        for (int turn = 0; turn < nth; turn++) {
+#pragma omp barrier
+            if (turn == me) {
+                for (size_t i = 0; i < nk; i++) dk[i] += a_dk[i];
+                for (size_t i = 0; i < nv; i++) dv[i] += a_dv[i];
+                for (size_t i = 0; i < nkc; i++) dkc[i] += a_dkc[i];
+                for (size_t i = 0; i < nvc; i++) dvc[i] += a_dvc[i];
+                for (size_t i = 0; i < (size_t)Hq * 3 * dk_; i++) dwg[i] += a_dwg[i];
+                for (size_t i = 0; i < (size_t)Hq * 3; i++) dbg[i] += a_dbg[i];
+            }
+        }
+        free(dout); free(o3); free(p); free(rows);
+        free(a_dbg); free(a_dwg); free(a_dvc); free(a_dkc); free(a_dv); free(a_dk);
+    }
+    if (N > 0) {
+        compress_backward(B * Hkv, T, dk_, c->l, c->d, N, k, wck, pek, dkc, dwck, dpek, dk);
+        compress_backward(B * Hkv, T, dv_, c->l, c->d, N, v, wcv, pev, dvc, dwcv, dpev, dv);
+    }
+    free(dvc); free(dkc); free(vc); free(kc);
 }

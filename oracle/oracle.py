@@ -57,6 +57,8 @@ def _load():
         lib.orc_forward_rows.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int, _ip, _ip, _dp, _dp, _dp,
                                          ctypes.c_int, _dp, _dp, _dp, _dp, _ip, _dp, _ip, _dp, ctypes.c_int,
                                          _dp, _dp]
+        lib.orc_backward.restype = None
+        lib.orc_backward.argtypes = [ctypes.POINTER(_Cfg)] + [_dp] * 9 + [_ip, _dp, ctypes.c_int] + [_dp] * 9
         lib.orc_select.restype = ctypes.c_int
         lib.orc_select.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int, _dp, _ip]
         _lib = lib
@@ -223,3 +225,33 @@ def select(cfg: Cfg, t: int, S):
     c = cfg.c()
     _load().orc_select(ctypes.byref(c), t, sp, idx.ctypes.data_as(_ip))
     return idx
+
+
+def backward(cfg: Cfg, q, k, v, wck, pek, wcv, pev, wg, bg, idx, dO, round_bf16: bool = False):
+    """Gradients of L = sum(dO * o) with the selection idx [B,Hkv,T,n] held
+    fixed.  q [B,T,Hq,dk], k [B,Hkv,T,dk], v [B,Hkv,T,dv], wck [dk,l*dk],
+    pek [l,dk], wcv [dv,l*dv], pev [l,dv], wg [Hq,3,dk], bg [Hq,3],
+    dO [B,T,Hq,dv].  The compressed K/V are recomputed from k/v (rounded to
+    bf16 when round_bf16, the rounding passed straight through in reverse).
+    Returns dict dq, dk, dv, dwck, dpek, dwcv, dpev, dwg, dbg (input layouts).
+    Rows whose dO is zero for all heads of a KV group are skipped (their
+    contribution is exactly zero)."""
+    B, T, Hkv, Hq, dk, dv, l = cfg.B, cfg.T, cfg.Hkv, cfg.Hq, cfg.dk, cfg.dv, cfg.l
+    arrs = []
+    for a, shp in ((q, (B, T, Hq, dk)), (k, (B, Hkv, T, dk)), (v, (B, Hkv, T, dv)), (wck, (dk, l * dk)),
+                   (pek, (l, dk)), (wcv, (dv, l * dv)), (pev, (l, dv)), (wg, (Hq, 3, dk)), (bg, (Hq, 3))):
+        a, _ = _d(a)
+        assert a.shape == shp, (a.shape, shp)
+        arrs.append(a)
+    idx, ip = _i(idx)
+    assert idx.shape == (B, Hkv, T, cfg.n)
+    dO, dop = _d(dO)
+    assert dO.shape == (B, T, Hq, dv)
+    out = {"dq": np.zeros((B, T, Hq, dk)), "dk": np.zeros((B, Hkv, T, dk)), "dv": np.zeros((B, Hkv, T, dv)),
+           "dwck": np.zeros((dk, l * dk)), "dpek": np.zeros((l, dk)), "dwcv": np.zeros((dv, l * dv)),
+           "dpev": np.zeros((l, dv)), "dwg": np.zeros((Hq, 3, dk)), "dbg": np.zeros((Hq, 3))}
+    c = cfg.c()
+    _load().orc_backward(ctypes.byref(c), *[a.ctypes.data_as(_dp) for a in arrs], ip, dop, int(round_bf16),
+                         *[out[n].ctypes.data_as(_dp) for n in ("dq", "dk", "dv", "dwck", "dpek", "dwcv",
+                                                                 "dpev", "dwg", "dbg")])
+    return out
