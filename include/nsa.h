@@ -1,6 +1,6 @@
 /*
- * nsa.h -- C ABI of libnsa: Native Sparse Attention (NSA) forward pass and
- * decode step on AMD MI355X (gfx950).
+ * nsa.h -- C ABI of libnsa: Native Sparse Attention (NSA) forward pass, decode
+ * step and backward pass on AMD MI355X (gfx950).
  *
  * NSA passes the same queries through three attention branches and sums
  * them with per-head gates (deepdaiv newsletter on DeepSeek's NSA,
@@ -73,7 +73,8 @@ typedef enum {
     NSA_OP_FORWARD = 0, /* nsa_forward */
     NSA_OP_SELECT = 1,  /* nsa_select_blocks */
     NSA_OP_DECODE = 2,  /* nsa_decode_step */
-    NSA_OP_SPARSE = 3   /* nsa_sparse_attention */
+    NSA_OP_SPARSE = 3,  /* nsa_sparse_attention */
+    NSA_OP_BACKWARD = 4 /* nsa_backward */
 } nsa_op;
 
 /* Problem description.  Supported ranges (checked on every call):
@@ -172,6 +173,27 @@ nsa_status nsa_decode_step(const nsa_config *cfg, const int32_t *seq_lens, const
                            const void *v_cache, const void *cmp_k, const void *cmp_v, const void *w_g,
                            const void *b_g, const int32_t *idx_in, void *o, int32_t *idx_out, void *ws,
                            size_t ws_bytes, void *stream);
+
+/* Backward pass of the prefill forward (deepdaiv newsletter, on native
+ * trainability: the sparse pattern is learned in training, so gradients flow
+ * through the three branches, the compression maps and the gates).  With
+ * L = sum(d_o * o) for the forward output o computed from these inputs and
+ * the block lists idx (held fixed: the selection is piecewise constant and
+ * passes no gradient to the importance scores), the call writes
+ *   d_q [B][T][Hq][dk], d_k [B][Hkv][T][dk], d_v [B][Hkv][T][dv]   config dtype
+ *   d_wck [dk][32*dk], d_pek [32][dk], d_wcv [dv][32*dv], d_pev [32][dv],
+ *   d_wg [Hq][3][dk], d_bg [Hq][3]                                  fp32
+ * (every element is written; nothing is accumulated into).  cmp_k / cmp_v
+ * must be what nsa_compress_kv makes of k / v with these maps: the gradient
+ * treats their bf16 rounding as the identity.  idx is what nsa_forward used
+ * (its idx_out, or the idx_in given to it); d_o [B][T][Hq][dv] config dtype.
+ * The result is deterministic (no floating-point atomics).
+ * ws: nsa_workspace_bytes(cfg, NSA_OP_BACKWARD) bytes.  B*H_kv <= 65535. */
+nsa_status nsa_backward(const nsa_config *cfg, const void *q, const void *k, const void *v, const void *cmp_k,
+                        const void *cmp_v, const void *w_ck, const void *pe_k, const void *w_cv, const void *pe_v,
+                        const void *w_g, const void *b_g, const int32_t *idx, const void *d_o, void *d_q,
+                        void *d_k, void *d_v, float *d_wck, float *d_pek, float *d_wcv, float *d_pev,
+                        float *d_wg, float *d_bg, void *ws, size_t ws_bytes, void *stream);
 
 /* Static description of a status code. */
 const char *nsa_status_string(int status);

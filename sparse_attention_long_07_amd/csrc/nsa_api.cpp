@@ -134,6 +134,8 @@ size_t nsa_workspace_bytes(const nsa_config *cfg, int op)
         return decode_mfma_supported(d) ? decode_mfma_layout(d, nullptr, nullptr) : layout(d, 1).total;
     case NSA_OP_SPARSE:
         return sparse_mfma_supported(d) ? align_up(sparse_mfma_ws_bytes(d)) : 0;
+    case NSA_OP_BACKWARD:
+        return backward_layout(d, nullptr, nullptr);
     default:
         return 0;
     }
@@ -325,6 +327,54 @@ nsa_status nsa_decode_step(const nsa_config *cfg, const int32_t *seq_lens, const
     }
     NSA_TRY(launch_sparse_generic(a, s));
     return NSA_OK;
+}
+
+nsa_status nsa_backward(const nsa_config *cfg, const void *q, const void *k, const void *v, const void *cmp_k,
+                        const void *cmp_v, const void *w_ck, const void *pe_k, const void *w_cv, const void *pe_v,
+                        const void *w_g, const void *b_g, const int32_t *idx, const void *d_o, void *d_q,
+                        void *d_k, void *d_v, float *d_wck, float *d_pek, float *d_wcv, float *d_pev,
+                        float *d_wg, float *d_bg, void *ws, size_t ws_bytes, void *stream)
+{
+    Dims d;
+    nsa_status st = check_config(cfg, &d);
+    if (st != NSA_OK) return st;
+    if ((long)d.B * d.Hkv > 65535) return NSA_ERR_SHAPE;
+    if (!q || !k || !v || !cmp_k || !cmp_v || !w_ck || !pe_k || !w_cv || !pe_v || !w_g || !b_g || !idx || !d_o ||
+        !d_q || !d_k || !d_v || !d_wck || !d_pek || !d_wcv || !d_pev || !d_wg || !d_bg)
+        return NSA_ERR_NULL;
+    if (!all_aligned({q, k, v, cmp_k, cmp_v, w_ck, pe_k, w_cv, pe_v, w_g, b_g, idx, d_o, d_q, d_k, d_v, d_wck,
+                      d_pek, d_wcv, d_pev, d_wg, d_bg}))
+        return NSA_ERR_ALIGN;
+    const size_t need = backward_layout(d, nullptr, nullptr);
+    if (!ws || ws_bytes < need) return NSA_ERR_WORKSPACE;
+    if ((uintptr_t)ws % kAlign) return NSA_ERR_ALIGN;
+    BwdArgs A;
+    memset(&A, 0, sizeof A);
+    A.d = d;
+    A.q = q;
+    A.k = k;
+    A.v = v;
+    A.kc = cmp_k;
+    A.vc = cmp_v;
+    A.wck = w_ck;
+    A.pek = pe_k;
+    A.wcv = w_cv;
+    A.pev = pe_v;
+    A.wg = w_g;
+    A.bg = b_g;
+    A.idx = idx;
+    A.dO = d_o;
+    A.dq = d_q;
+    A.dk = d_k;
+    A.dv = d_v;
+    A.dwck = d_wck;
+    A.dpek = d_pek;
+    A.dwcv = d_wcv;
+    A.dpev = d_pev;
+    A.dwg = d_wg;
+    A.dbg = d_bg;
+    backward_layout(d, ws, &A);
+    return hip_status(launch_backward(A, (hipStream_t)stream));
 }
 
 const char *nsa_status_string(int status)

@@ -73,6 +73,28 @@ struct DecArgs {
     int32_t *idx;                 // selection output [B][Hkv][n]
 };
 
+// Arguments of the backward pass.
+struct BwdArgs {
+    Dims d;
+    const void *q, *k, *v, *kc, *vc;        // forward inputs (storage dtype)
+    const void *wck, *pek, *wcv, *pev, *wg, *bg;
+    const int32_t *idx;                     // [B][Hkv][T][n] selection used by the forward
+    const void *dO;                         // [B][T][Hq][dv]
+    void *dq, *dk, *dv;                     // storage dtype, input layouts
+    float *dwck, *dpek, *dwcv, *dpev, *dwg, *dbg;
+    // workspace (fp32)
+    float *rs;        // [B][T][Hq][3][4] per row, head and branch: lse, D, gate, dz
+    float *dk_raw;    // [B][Hkv][T][dk] raw-key gradient from the window and selected branches
+    float *dv_raw;    // [B][Hkv][T][dv]
+    float *part;      // [nchunk][B*Hkv][npad][dk+dv] compressed K/V gradient per row chunk
+    float *kcv;       // [B*Hkv][npad][dk+dv] compressed K/V gradient
+    float *colsum;    // [dk+dv] sum of kcv over sequences, heads and blocks
+    float *gpart;     // [Hq][ngc][3][dk+1] gate gradient per row chunk
+    int nchunk, ngc;
+};
+size_t backward_layout(const Dims &d, void *ws, BwdArgs *A);   // bytes; carves A's buffers if ws
+hipError_t launch_backward(const BwdArgs &A, hipStream_t s);
+
 // Generic kernels: plain VALU code, any supported shape, fp32 or bf16 storage.
 hipError_t launch_compress_generic(const Dims &d, const void *x, const void *W, const void *PE, void *out,
                                    int dim, hipStream_t s);

@@ -17,12 +17,13 @@ from .config import BF16, FP32, NSAShape
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libnsa.so")
 
-OP_FORWARD, OP_SELECT, OP_DECODE, OP_SPARSE = 0, 1, 2, 3
+OP_FORWARD, OP_SELECT, OP_DECODE, OP_SPARSE, OP_BACKWARD = 0, 1, 2, 3, 4
 STATUS = {0: "NSA_OK", -1: "NSA_ERR_NULL", -2: "NSA_ERR_SHAPE", -3: "NSA_ERR_DTYPE", -4: "NSA_ERR_PARAM",
           -5: "NSA_ERR_WORKSPACE", -6: "NSA_ERR_HIP", -7: "NSA_ERR_ALIGN"}
 
 EXPORTS = ("nsa_workspace_bytes", "nsa_compress_kv", "nsa_compressed_attention", "nsa_select_topn",
-           "nsa_sparse_attention", "nsa_select_blocks", "nsa_forward", "nsa_decode_step", "nsa_status_string")
+           "nsa_sparse_attention", "nsa_select_blocks", "nsa_forward", "nsa_decode_step", "nsa_backward",
+           "nsa_status_string")
 
 
 class NSAError(RuntimeError):
@@ -66,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L.nsa_forward.argtypes = [ctypes.POINTER(Config)] + [_vp] * 12 + [ctypes.c_size_t, _vp]
         L.nsa_decode_step.restype = ctypes.c_int
         L.nsa_decode_step.argtypes = [ctypes.POINTER(Config)] + [_vp] * 12 + [ctypes.c_size_t, _vp]
+        L.nsa_backward.restype = ctypes.c_int
+        L.nsa_backward.argtypes = [ctypes.POINTER(Config)] + [_vp] * 23 + [ctypes.c_size_t, _vp]
         _lib = L
     return _lib
 
@@ -259,3 +262,41 @@ def decode_step(s: NSAShape, seq_lens, q, k_cache, v_cache, cmp_k, cmp_v, w_g, b
                                                     _p(v_cache), _p(cmp_k), _p(cmp_v), _p(w_g), _p(b_g),
                                                     _p(idx_in), _p(o), _p(idx), _p(ws), ws.numel(), _stream()))
     return (o, idx) if want_idx else o
+
+
+def backward(s: NSAShape, q, k, v, cmp_k, cmp_v, w_ck, pe_k, w_cv, pe_v, w_g, b_g, idx, d_o, ws=None):
+    """Gradients of sum(d_o * o) with the selection idx held fixed.  Returns a
+    dict d_q, d_k, d_v (config dtype) and d_wck, d_pek, d_wcv, d_pev, d_wg,
+    d_bg (fp32), in the layouts of the corresponding inputs."""
+    dt = _dt(s)
+    dev = q.device
+    _req(q, "q", (s.B, s.T, s.Hq, s.dk), dt)
+    _req(k, "k", (s.B, s.Hkv, s.T, s.dk), dt)
+    _req(v, "v", (s.B, s.Hkv, s.T, s.dv), dt)
+    _req(cmp_k, "cmp_k", (s.B, s.Hkv, s.n_pad, s.dk), dt)
+    _req(cmp_v, "cmp_v", (s.B, s.Hkv, s.n_pad, s.dv), dt)
+    _req(w_ck, "w_ck", (s.dk, s.l * s.dk), dt)
+    _req(pe_k, "pe_k", (s.l, s.dk), dt)
+    _req(w_cv, "w_cv", (s.dv, s.l * s.dv), dt)
+    _req(pe_v, "pe_v", (s.l, s.dv), dt)
+    _req(w_g, "w_g", (s.Hq, 3, s.dk), dt)
+    _req(b_g, "b_g", (s.Hq, 3), dt)
+    _req(idx, "idx", (s.B, s.Hkv, s.T, s.n), torch.int32)
+    _req(d_o, "d_o", (s.B, s.T, s.Hq, s.dv), dt)
+    g = {"d_q": torch.empty_like(q), "d_k": torch.empty_like(k), "d_v": torch.empty_like(v),
+         "d_wck": torch.empty(w_ck.shape, dtype=torch.float32, device=dev),
+         "d_pek": torch.empty(pe_k.shape, dtype=torch.float32, device=dev),
+         "d_wcv": torch.empty(w_cv.shape, dtype=torch.float32, device=dev),
+         "d_pev": torch.empty(pe_v.shape, dtype=torch.float32, device=dev),
+         "d_wg": torch.empty(w_g.shape, dtype=torch.float32, device=dev),
+         "d_bg": torch.empty(b_g.shape, dtype=torch.float32, device=dev)}
+    if ws is None:
+        ws = workspace(s, OP_BACKWARD, dev)
+    c = config(s)
+    st = lib().nsa_backward(ctypes.byref(c), _p(q), _p(k), _p(v), _p(cmp_k), _p(cmp_v), _p(w_ck), _p(pe_k),
+                            _p(w_cv), _p(pe_v), _p(w_g), _p(b_g), _p(idx), _p(d_o),
+                            *[_p(g[n]) for n in ("d_q", "d_k", "d_v", "d_wck", "d_pek", "d_wcv", "d_pev", "d_wg",
+                                                 "d_bg")],
+                            _p(ws), ws.numel(), _stream())
+    _check("nsa_backward", st)
+    return g

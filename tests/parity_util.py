@@ -96,3 +96,38 @@ def check_idx(s: NSAShape, scores_ref: np.ndarray, t_of_row, idx_ref: np.ndarray
         else:
             assert valid_topn(scores_ref[r], t, idx_gpu[r], s.n, s.lsel), (r, t, idx_gpu[r])
     return checked, R
+
+
+def grad_tol(s: NSAShape, ref: np.ndarray, scale: float | None = None) -> float:
+    """Gradient tolerance: 1e-4 of the tensor's largest magnitude for fp32
+    storage, 2e-2 of it for bf16 storage (the forward's bf16 rule applied per
+    gradient tensor).  A tensor that is zero in exact arithmetic (dPE_k: the
+    shift it applies to every compressed key cancels in the softmax) passes
+    the magnitude of its non-cancelling counterpart as `scale`."""
+    m = float(np.abs(ref).max()) if ref.size else 0.0
+    if scale is not None:
+        m = max(m, scale)
+    return (1e-4 if s.dtype != BF16 else 2e-2) * max(m, 1e-30)
+
+
+def random_selection(s: NSAShape, seed: int) -> np.ndarray:
+    """A seeded, valid block list per (b, g, t) for tests that hold the
+    selection fixed: the always-kept blocks {0, jc-1, jc} plus distinct random
+    others up to n, in random order, sometimes with one entry repeated,
+    padded with -1.  [B, Hkv, T, n] int32."""
+    rng = np.random.default_rng(seed)
+    idx = -np.ones((s.B, s.Hkv, s.T, s.n), dtype=np.int32)
+    for b in range(s.B):
+        for g in range(s.Hkv):
+            for t in range(s.T):
+                jc = t // s.lsel
+                sel = sorted(forced(t, s.lsel))
+                if jc + 1 > len(sel):
+                    others = np.setdiff1d(np.arange(jc + 1), sel)
+                    k = min(s.n - len(sel), others.size)
+                    sel += [int(j) for j in rng.choice(others, size=k, replace=False)]
+                if len(sel) < s.n and rng.random() < 0.3:
+                    sel.append(sel[0])
+                rng.shuffle(sel)
+                idx[b, g, t, :len(sel)] = sel
+    return idx

@@ -80,6 +80,7 @@ def test_bad_config_rejected_everywhere(kw, code):
     assert L.nsa_select_blocks(c, f[0], f[1], None, f[2], f[3], 1 << 40, None) == code
     assert L.nsa_forward(c, *f[:7], None, f[0], None, None, f[1], 1 << 40, None) == code
     assert L.nsa_decode_step(c, *f[:8], None, f[0], None, f[1], 1 << 40, None) == code
+    assert L.nsa_backward(c, *([FAKE] * 22), FAKE, 1 << 40, None) == code
 
 
 def test_null_config():
@@ -149,3 +150,31 @@ def test_binding_arity_matches_header():
         m = re.search(r"\b%s\s*\(([^)]*)\)" % name, text, re.S)
         nparams = len([p for p in m.group(1).split(",") if p.strip()])
         assert len(getattr(L, name).argtypes) == nparams, name
+
+
+@pytest.mark.parametrize("pos", range(22))
+def test_backward_required_pointers(pos):
+    L = nsa.lib()
+    c = ctypes.byref(cfg())
+    need = L.nsa_workspace_bytes(c, nsa.OP_BACKWARD)
+    args = [FAKE] * 22
+    args[pos] = None
+    assert L.nsa_backward(c, *args, FAKE, need, None) == NULL
+    args[pos] = MIS
+    assert L.nsa_backward(c, *args, FAKE, need, None) == ALIGN
+
+
+def test_backward_workspace_checks():
+    L = nsa.lib()
+    c = cfg()
+    need = L.nsa_workspace_bytes(ctypes.byref(c), nsa.OP_BACKWARD)
+    s = NSAShape(1, 256, 2, 4, 64, 32, "bf16")
+    # per-row statistics, raw-key gradients and compressed-key gradients at least
+    assert need >= 4 * (s.B * s.T * s.Hq * 12 + s.B * s.Hkv * s.T * (s.dk + s.dv))
+    assert need % 256 == 0
+    f = [FAKE] * 22
+    assert L.nsa_backward(ctypes.byref(c), *f, None, need, None) == WS
+    assert L.nsa_backward(ctypes.byref(c), *f, FAKE, need - 1, None) == WS
+    assert L.nsa_backward(ctypes.byref(c), *f, ctypes.c_void_p(0x10010), need, None) == ALIGN
+    # B * H_kv above the grid limit of the key passes
+    assert L.nsa_backward(ctypes.byref(cfg(B=70000, H_kv=1, group=1)), *f, FAKE, 1 << 40, None) == SHAPE
