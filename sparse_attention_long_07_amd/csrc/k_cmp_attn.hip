@@ -5,21 +5,29 @@
 // vector per compression block, and the block-importance scores that drive
 // selection come from that attention.  The 16 query heads of a KV group share
 // the group's compressed keys (ctol-kr.com article, "하드웨어 인식 설계":
-// group-centric loading with a shared KV fetch), so a workgroup takes 8
-// consecutive positions x 16 heads = 128 query rows of one KV group and
+// group-centric loading with a shared KV fetch), so a workgroup takes 16
+// consecutive positions x 16 heads = 256 query rows of one KV group and
 // streams the group's compressed keys through LDS once per pass for all of
 // them.
 //
 // Orientation: S^T = K Q^T with v_mfma_f32_32x32x16_bf16 -- 32 keys (M) by
-// 32 query rows (N, two positions x 16 heads per wave) -- so every lane owns
-// the softmax state of one query row.  K rows are stored in LDS permuted so
-// that the 16 accumulators a lane holds are 16 consecutive keys; P^T then
-// feeds O^T = V^T P^T directly as the B operand, with V^T transposed into LDS.
+// 32 query rows (N, two positions x 16 heads) -- so every lane owns the
+// softmax state of one query row; eight waves cover the 16 positions, two
+// waves per SIMD, so one wave's softmax arithmetic overlaps the other's
+// matrix work.  K rows are stored in LDS permuted so that the 16 accumulators a lane holds are
+// 16 consecutive keys; P^T then feeds O^T = V^T P^T directly as the B operand,
+// with V^T transposed into LDS.
 //
 // Pass 1 computes each row's exact log-sum-exp.  Pass 2 recomputes the logits
-// and forms exact probabilities, which give o_cmp and, summed over the 16
-// heads in fp32 (a DPP transpose-reduce over each 16-lane row), the group's
-// per-key importance; block j takes keys 4j-1 .. 4j+3 with weights 1,2,2,2,1.
+// and forms exact probabilities, which give o_cmp and the group's block
+// importance: block j takes keys 4j-1 .. 4j+3 with weights 1,2,2,2,1, so a
+// lane first folds its 16 keys into four block partials plus the weight-1
+// share of its last key in the next block, and the 16 heads are then summed
+// through LDS.
+//
+// Pipeline: the next tile's K (and V) is loaded into registers while the
+// current tile is computed, then written to the other LDS buffer; one
+// barrier per tile.  Causal masking is applied only on a wave's last tiles.
 #include "mfma_util.h"
 #include "nsa_internal.h"
 
@@ -27,18 +35,33 @@ namespace nsa {
 
 namespace {
 
-constexpr int kPos = 8;      // query positions per workgroup
+constexpr int kPos = 16;     // query positions per workgroup (2 per wave)
 constexpr int kTile = 64;    // compressed keys per LDS tile
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 
 template <int DK, int DV>
 struct CmpLds {
     static constexpr int KS = DK + 8;      // bf16 per K row (padded against bank conflicts)
     static constexpr int VS = kTile + 8;   // bf16 per V^T row
-    uint16_t k[kTile * KS];
-    uint16_t vt[DV * VS];
-    float pl[kPos][kTile];                 // head-summed probabilities of the current tile
+    uint16_t k[2][kTile * KS];
+    uint16_t vt[2][DV * VS];
+    // Per position and head: the tile's 16 block partials (entry 4*grp + u for
+    // block u of 16-key group grp) and the weight-1 shares of each group's last
+    // key in the next block (entries 16..19).  Laid out by sc_off.
+    float sc[2][kPos * 416];
 };
+
+// Float offset of (position, entry, head) in a score buffer.  Entries are 16
+// heads (64 B), padded by 16 floats after every 4 entries, positions 416
+// floats apart, and the four 4-head chunks of an entry rotated by entry/4.
+// Both the per-lane scalar writes (lanes: 16 heads x 2 positions x 2 groups)
+// and the reducer's 16-byte reads (16 lanes: the 16 entries of a position)
+// then touch every bank at most once.
+__device__ __forceinline__ int sc_off(int pos, int jj, int head)
+{
+    const int q = jj >> 2;
+    return pos * 416 + jj * 16 + q * 16 + ((((head >> 2) + q) & 3) << 2) + (head & 3);
+}
 
 // LDS row of key k (0..31) inside a 32-key M-tile.  MFMA output row i sits in
 // lane half (i/4)%2, register 4*(i/8) + i%4; putting key 16*h + r in row
@@ -49,9 +72,11 @@ __device__ __forceinline__ int krow(int k)
     return 8 * m + 4 * h + u;
 }
 
+__device__ __forceinline__ int n_visible(int t) { return t >= 31 ? (t - 31) / 16 + 1 : 0; }
+
 }  // namespace
 
-// Workgroup -> ((b, g) pair, tile of 8 positions).  When the (b, g) pairs
+// Workgroup -> ((b, g) pair, tile of positions).  When the (b, g) pairs
 // divide the 8 XCDs, each XCD works on one pair only (its compressed K/V
 // stays in that XCD's L2); tiles run heaviest (latest positions) first.
 __device__ __forceinline__ bool cmp_map_wg(int id, int BG, int ntp, int &bg, int &ptile)
@@ -75,6 +100,11 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
 {
     constexpr int KSTEPS = DK / 16;
     constexpr int DT = DV / 32;
+    constexpr int CH = DK / 8;                                  // 16-byte chunks per K row
+    constexpr int KTASKS = kTile * CH;
+    constexpr int KLD = (KTASKS + kThreads - 1) / kThreads;    // K chunks per thread per tile
+    constexpr int VTASKS = 32 * (DV / 8);                       // V^T tasks: two keys x 8 columns
+    constexpr int VTK = (VTASKS + kThreads - 1) / kThreads;
     using L = CmpLds<DK, DV>;
     __shared__ L sm;
 
@@ -90,10 +120,13 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
     const int pw = 2 * wave + (row >> 4);   // position inside the workgroup
     const int t = pos0 + pw;
     const bool live = t < d.T;
-    const int nvis = (live && t >= 31) ? (t - 31) / 16 + 1 : 0;
-    const int tlast = min(pos0 + kPos - 1, d.T - 1);
-    const int nvis_max = tlast >= 31 ? (tlast - 31) / 16 + 1 : 0;
-    const int ntiles = (nvis_max + kTile - 1) / kTile;
+    const int nv = live ? n_visible(t) : 0;
+    // wave-uniform tile counts: tiles below nfull need no causal mask (a wave
+    // with a row past the sequence end masks every tile)
+    const int tw0 = pos0 + 2 * wave;
+    const int nfull = tw0 + 1 < d.T ? n_visible(tw0) / kTile : 0;
+    const int ntw = tw0 < d.T ? (n_visible(min(tw0 + 1, d.T - 1)) + kTile - 1) / kTile : 0;
+    const int ntiles = (n_visible(min(pos0 + kPos - 1, d.T - 1)) + kTile - 1) / kTile;
     const float sl2 = d.scale * kLog2e;
 
     bf16x8 qf[KSTEPS];
@@ -107,35 +140,54 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
     const uint16_t *kc = (const uint16_t *)a.kc + (long)bg * d.npad * DK;
     const uint16_t *vc = (const uint16_t *)a.vc + (long)bg * d.npad * DV;
 
+    u32x4 kreg[KLD], vreg[VTK][2];
     auto load_k = [&](int c) {
-        constexpr int CH = DK / 8;
         const uint16_t *src = kc + (long)c * kTile * DK;
-        for (int task = tid; task < kTile * CH; task += kThreads) {
-            const int key = task / CH, ch = task % CH;
-            const int r = (key & ~31) | krow(key & 31);
-            st16(&sm.k[r * L::KS + ch * 8], ld16(src + key * DK + ch * 8));
+#pragma unroll
+        for (int u = 0; u < KLD; u++) {
+            const int task = tid + u * kThreads, key = task / CH, ch = task % CH;
+            if (KTASKS % kThreads == 0 || task < KTASKS) kreg[u] = ld16(src + key * DK + ch * 8);
         }
     };
-    auto load_vt = [&](int c) {
-        constexpr int NDC = DV / 8;
-        const uint16_t *src = vc + (long)c * kTile * DV;
-        for (int task = tid; task < 32 * NDC; task += kThreads) {
-            const int kp = task & 31, dc = task >> 5;
-            const u32x4 v0 = ld16(src + (2 * kp) * DV + dc * 8);
-            const u32x4 v1 = ld16(src + (2 * kp + 1) * DV + dc * 8);
+    auto store_k = [&](int buf) {
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                const uint32_t lo = (v0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                const uint32_t hi = (v1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                *(uint32_t *)&sm.vt[(dc * 8 + e) * L::VS + 2 * kp] = lo | (hi << 16);
+        for (int u = 0; u < KLD; u++) {
+            const int task = tid + u * kThreads, key = task / CH, ch = task % CH;
+            const int r = (key & ~31) | krow(key & 31);
+            if (KTASKS % kThreads == 0 || task < KTASKS) st16(&sm.k[buf][r * L::KS + ch * 8], kreg[u]);
+        }
+    };
+    auto load_v = [&](int c) {
+        const uint16_t *src = vc + (long)c * kTile * DV;
+#pragma unroll
+        for (int u = 0; u < VTK; u++) {
+            const int task = tid + u * kThreads, kp = task & 31, dc = task >> 5;
+            if (VTASKS % kThreads == 0 || task < VTASKS) {
+                vreg[u][0] = ld16(src + (2 * kp) * DV + dc * 8);
+                vreg[u][1] = ld16(src + (2 * kp + 1) * DV + dc * 8);
             }
         }
     };
-    auto logits = [&](int mt) {
+    auto store_vt = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < VTK; u++) {
+            const int task = tid + u * kThreads, kp = task & 31, dc = task >> 5;
+            if (VTASKS % kThreads == 0 || task < VTASKS) {
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    // keys 2kp and 2kp+1 of column dc*8+e, as one bf16 pair
+                    const uint32_t w = __builtin_amdgcn_perm(vreg[u][1][e >> 1], vreg[u][0][e >> 1],
+                                                             (e & 1) ? 0x07060302u : 0x05040100u);
+                    *(uint32_t *)&sm.vt[buf][(dc * 8 + e) * L::VS + 2 * kp] = w;
+                }
+            }
+        }
+    };
+    auto logits = [&](int buf, int mt) {
         f32x16 acc;
 #pragma unroll
         for (int r = 0; r < 16; r++) acc[r] = 0.f;
-        const uint16_t *kr = &sm.k[(32 * mt + row) * L::KS + 8 * h];
+        const uint16_t *kr = &sm.k[buf][(32 * mt + row) * L::KS + 8 * h];
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; kk++) acc = mfma32(as_bf16x8(ld16(kr + 16 * kk)), qf[kk], acc);
         return acc;
@@ -143,35 +195,45 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
 
     // ---- pass 1: log-sum-exp of every row (log2 domain)
     float m = -INFINITY, l = 0.f;
-    for (int c = 0; c < ntiles; c++) {
-        __syncthreads();
-        load_k(c);
-        __syncthreads();
+    // one tile; `masked` (wave-uniform) applies the causal limit
+    auto pass1_tile = [&](int c, bool masked) {
+        const int buf = c & 1;
 #pragma unroll
         for (int mt = 0; mt < 2; mt++) {
-            const f32x16 acc = logits(mt);
+            f32x16 acc = logits(buf, mt);
             const int kb = c * kTile + 32 * mt + 16 * h;
-            float s[16], mx = -INFINITY;
+            if (masked) {
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                s[r] = kb + r < nvis ? acc[r] * sl2 : -INFINITY;
-                mx = fmaxf(mx, s[r]);
+                for (int r = 0; r < 16; r++) acc[r] = kb + r < nv ? acc[r] : -INFINITY;
             }
-            const float mn = fmaxf(m, mx);
-            if (mn != -INFINITY) {
-                float sum = 0.f;
+            float mx = -INFINITY;
 #pragma unroll
-                for (int r = 0; r < 16; r++) sum += fast_exp2(s[r] - mn);
-                l = l * fast_exp2(m - mn) + sum;
-                m = mn;
-            }
+            for (int r = 0; r < 16; r++) mx = fmaxf(mx, acc[r]);
+            const float mn = fmaxf(m, mx * sl2);
+            const float ms = mn == -INFINITY ? 0.f : mn;   // rows with nothing visible yet
+            float sum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; r++) sum += fast_exp2(__builtin_fmaf(acc[r], sl2, -ms));
+            l = l * fast_exp2(m - ms) + sum;
+            m = mn;
         }
+    };
+    if (ntiles > 0) {
+        load_k(0);
+        store_k(0);
+        lds_barrier();
     }
-    float lse2 = -INFINITY;
+    for (int c = 0; c < ntiles; c++) {
+        if (c + 1 < ntiles) load_k(c + 1);
+        if (c < ntw) pass1_tile(c, c >= nfull);
+        if (c + 1 < ntiles) store_k((c + 1) & 1);
+        lds_barrier();
+    }
+    float lse2;
     {
         const float mo = __shfl_xor(m, 32, 64), lo = __shfl_xor(l, 32, 64);
         const float M = fmaxf(m, mo);
-        if (M != -INFINITY) lse2 = M + fast_log2(l * fast_exp2(m - M) + lo * fast_exp2(mo - M));
+        lse2 = M == -INFINITY ? -INFINITY : M + fast_log2(l * fast_exp2(m - M) + lo * fast_exp2(mo - M));
     }
 
     // ---- pass 2: probabilities -> o_cmp and block importance
@@ -180,48 +242,99 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
     for (int dt = 0; dt < DT; dt++)
 #pragma unroll
         for (int r = 0; r < 16; r++) oacc[dt][r] = 0.f;
-    float carry = 0.f;   // P of the previous tile's last key (threads forming block 16c)
-    float *scores = a.scores + (long)bg * a.R * d.nb;
-    for (int c = 0; c < ntiles; c++) {
-        __syncthreads();
-        load_k(c);
-        if (WITH_V) load_vt(c);
-        __syncthreads();
+    auto pass2_tile = [&](int c, bool masked) {
+        const int buf = c & 1;
 #pragma unroll
         for (int mt = 0; mt < 2; mt++) {
-            const f32x16 acc = logits(mt);
+            const f32x16 acc = logits(buf, mt);
             const int kb = c * kTile + 32 * mt + 16 * h;
             float p[16];
 #pragma unroll
-            for (int r = 0; r < 16; r++) p[r] = kb + r < nvis ? fast_exp2(acc[r] * sl2 - lse2) : 0.f;
+            for (int r = 0; r < 16; r++) p[r] = fast_exp2(__builtin_fmaf(acc[r], sl2, -lse2));
+            if (masked) {
+#pragma unroll
+                for (int r = 0; r < 16; r++) p[r] = kb + r < nv ? p[r] : 0.f;
+            }
             if (WITH_V) {
 #pragma unroll
                 for (int s2 = 0; s2 < 2; s2++) {
                     const bf16x8 pb = pack8(&p[8 * s2]);
 #pragma unroll
                     for (int dt = 0; dt < DT; dt++) {
-                        const uint16_t *vr = &sm.vt[(32 * dt + row) * L::VS + 32 * mt + 16 * h + 8 * s2];
-                        oacc[dt] = mfma32(as_bf16x8(ld16(vr)), pb, oacc[dt]);
+                        const bf16x8 af = as_bf16x8(
+                            ld16(&sm.vt[buf][(32 * dt + row) * L::VS + 32 * mt + 16 * h + 8 * s2]));
+                        oacc[dt] = mfma32(af, pb, oacc[dt]);
                     }
                 }
             }
-            sm.pl[pw][32 * mt + 16 * h + (lane & 15)] = row_transpose_sum16(p, lane);
+            const int grp = 2 * mt + h;
+            float *dst = sm.sc[buf];
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const float *q4 = &p[4 * u];
+                float v = __builtin_fmaf(2.f, q4[0] + q4[1] + q4[2], q4[3]);
+                if (u) v += q4[-1];
+                dst[sc_off(pw, 4 * grp + u, head)] = v;
+            }
+            dst[sc_off(pw, 16 + grp, head)] = p[15];
         }
-        __syncthreads();
-        if (tid < kPos * 16) {
-            const int pp = tid >> 4, jj = tid & 15;
-            const float *P = sm.pl[pp];
-            const float prev = jj ? P[4 * jj - 1] : carry;
-            const float S = prev + 2.f * (P[4 * jj] + P[4 * jj + 1] + P[4 * jj + 2]) + P[4 * jj + 3];
-            if (jj == 0) carry = P[kTile - 1];
-            const int tt = pos0 + pp, j = 16 * c + jj;
-            if (tt < d.T && j <= tt / 64) scores[(long)tt * d.nb + j] = S;
+    };
+    float carry = 0.f;   // head-summed weight-1 share of the previous tile's last key
+    float *scores = a.scores + (long)bg * a.R * d.nb;
+    const bool reducer = tid < kPos * 16;
+    const int rp = (tid >> 4) & (kPos - 1), rj = tid & 15;   // reducer: position, block of the tile
+    const int tr = pos0 + rp;
+    if (ntiles > 0) {
+        load_k(0);
+        if (WITH_V) load_v(0);
+        store_k(0);
+        if (WITH_V) store_vt(0);
+        lds_barrier();
+    }
+    for (int c = 0; c < ntiles; c++) {
+        if (c + 1 < ntiles) {
+            load_k(c + 1);
+            if (WITH_V) load_v(c + 1);
+        }
+        if (c < ntw) {
+            pass2_tile(c, c >= nfull);
+        } else {
+            // nothing visible to this wave in the tile: its rows contribute zero
+#pragma unroll
+            for (int jj = 2 * h; jj < 20; jj += 4) {
+                sm.sc[c & 1][sc_off(pw, jj, head)] = 0.f;
+                sm.sc[c & 1][sc_off(pw, jj + 1, head)] = 0.f;
+            }
+        }
+        if (c + 1 < ntiles) {
+            store_k((c + 1) & 1);
+            if (WITH_V) store_vt((c + 1) & 1);
+        }
+        lds_barrier();
+        if (reducer) {
+            // sum of the 16 heads of one entry: four 16-byte reads
+            const float *scb = sm.sc[c & 1];
+            auto head_sum = [&](int jj) {
+                float S = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const f32x4 v = *(const f32x4 *)&scb[sc_off(rp, jj, 4 * i)];
+                    S += (v[0] + v[1]) + (v[2] + v[3]);
+                }
+                return S;
+            };
+            const int grp = rj >> 2, u = rj & 3;
+            float S = head_sum(rj);
+            if (u == 0) S += grp ? head_sum(16 + grp - 1) : carry;
+            if (rj == 0) carry = head_sum(19);
+            const int j = 16 * c + rj;
+            if (tr < d.T && j <= tr / 64) scores[(long)tr * d.nb + j] = S;
         }
     }
     // the last key of the final tile also reaches block 16*ntiles
-    if (tid < kPos * 16 && (tid & 15) == 0) {
-        const int tt = pos0 + (tid >> 4), j = 16 * ntiles;
-        if (tt < d.T && j <= tt / 64) scores[(long)tt * d.nb + j] = carry;
+    if (reducer && rj == 0) {
+        const int j = 16 * ntiles;
+        if (tr < d.T && j <= tr / 64) scores[(long)tr * d.nb + j] = carry;
     }
 
     if (WITH_V && live) {

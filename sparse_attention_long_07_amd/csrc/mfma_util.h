@@ -18,6 +18,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -36,11 +38,13 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *(const u32x4 *)p; }
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *(u32x4 *)p = v; }
 
-// Pack two floats into a bf16 pair (round to nearest even).
+// Pack two floats into a bf16 pair (round to nearest even).  The vector
+// conversion becomes one v_cvt_pk_bf16_f32; converting the halves one at a
+// time costs two conversions plus a shift and an or.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    const f32x2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
 __device__ __forceinline__ bf16x8 pack8(const float *p)
