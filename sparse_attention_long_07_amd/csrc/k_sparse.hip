@@ -9,7 +9,7 @@
 //
 // Two kernels, each shaped by its own bound:
 //  * k_window_mfma -- the window keys of neighbouring positions coincide, so a
-//    workgroup takes 8 positions x 16 heads (128 query rows) of one KV head
+//    workgroup takes 16 positions x 16 heads (256 query rows) of one KV head
 //    and streams the window's 64-key tiles through LDS once for all of them
 //    (v_mfma_f32_32x32x16_bf16, S^T = K Q^T as in the compressed stage).  It
 //    writes o = g_cmp * o_cmp + g_win * o_win.
@@ -31,7 +31,8 @@ namespace nsa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPos = 8;      // window kernel: query positions per workgroup
+constexpr int kWPos = 16;    // window kernel: query positions per workgroup
+constexpr int kWThreads = 512;
 constexpr int kTile = 64;
 
 __device__ __forceinline__ int krow(int k)
@@ -101,19 +102,32 @@ template <int DK, int DV>
 struct WinLds {
     static constexpr int KS = DK + 8;
     static constexpr int VS = kTile + 8;
-    uint16_t k[kTile * KS];
-    uint16_t vt[DV * VS];
+    uint16_t k[2][kTile * KS];
+    uint16_t vt[2][DV * VS];
 };
 
 // ---------------------------------------------------------------------------
-// Window branch + compressed term.  Workgroups of one (b, g) pair take
-// consecutive position tiles on the same XCD, so the overlapping window tiles
-// are served from that XCD's L2.
+// Window branch + compressed term.  16 positions x 16 heads per workgroup,
+// 8 waves of 32 rows (two waves per SIMD); the window's 64-key tiles are
+// loaded into registers one tile ahead and written to the other LDS buffer,
+// one barrier per tile.  Only a wave's edge tiles are masked.  The running
+// maximum is raised only when a tile's maximum exceeds it by more than 2^8
+// (one wave-wide decision), so most tiles skip rescaling the accumulators;
+// p then stays below 2^8, which fp32 sums and bf16 operands hold exactly as
+// well as values below 1.  Workgroups of one (b, g) pair take consecutive
+// position tiles on the same XCD, so the overlapping window tiles are served
+// from that XCD's L2.
 template <int DK, int DV>
-__global__ __launch_bounds__(kThreads) void k_window_mfma(RowArgs a, int ntp)
+__global__ __launch_bounds__(kWThreads) void k_window_mfma(RowArgs a, int ntp)
 {
     constexpr int KSTEPS = DK / 16;
     constexpr int DT = DV / 32;
+    constexpr int CH = DK / 8;
+    constexpr int KTASKS = kTile * CH;
+    constexpr int KLD = (KTASKS + kWThreads - 1) / kWThreads;
+    constexpr int VTASKS = 32 * (DV / 8);
+    constexpr int VTK = (VTASKS + kWThreads - 1) / kWThreads;
+    constexpr float kLazy = 8.f;   // log2 headroom before the running max is raised
     using L = WinLds<DK, DV>;
     __shared__ L sm;
 
@@ -127,12 +141,18 @@ __global__ __launch_bounds__(kThreads) void k_window_mfma(RowArgs a, int ntp)
     const int b = bg / d.Hkv, g = bg % d.Hkv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, row = lane & 31, head = row & 15;
-    const int pos0 = ptile * kPos;
+    const int pos0 = ptile * kWPos;
     const int t = pos0 + 2 * wave + (row >> 4);
     const bool live = t < d.T;
     const int lo = max(0, t - d.w + 1);
-    const int tlast = min(pos0 + kPos - 1, d.T - 1);
+    const int tlast = min(pos0 + kWPos - 1, d.T - 1);
     const int c_first = max(0, pos0 - d.w + 1) / kTile, c_last = tlast / kTile;
+    // this wave's two positions: keys it needs and tiles it sees unmasked
+    const int tw0 = pos0 + 2 * wave, tw1 = tw0 + 1;
+    const bool wlive = tw0 < d.T;
+    const int wk_lo = max(0, tw0 - d.w + 1), wk_hi = min(tw1, d.T - 1);
+    const int full_lo = max(0, tw1 - d.w + 1);      // unmasked: full_lo <= 64c and 64c+63 <= tw0
+    const bool both = tw1 < d.T;
     const float sl2 = d.scale * kLog2e;
 
     bf16x8 qf[KSTEPS];
@@ -172,6 +192,50 @@ __global__ __launch_bounds__(kThreads) void k_window_mfma(RowArgs a, int ntp)
 
     const uint16_t *kg = (const uint16_t *)a.k + (long)bg * d.T * DK;
     const uint16_t *vg = (const uint16_t *)a.v + (long)bg * d.T * DV;
+    u32x4 kreg[KLD], vreg[VTK][2];
+    auto load_tile = [&](int c) {
+#pragma unroll
+        for (int u = 0; u < KLD; u++) {
+            const int task = tid + u * kWThreads, key = task / CH, ch = task % CH;
+            const u32x4 z = {0, 0, 0, 0};
+            kreg[u] = z;
+            if ((KTASKS % kWThreads == 0 || task < KTASKS) && c * kTile + key < d.T)
+                kreg[u] = ld16(kg + (long)(c * kTile + key) * DK + ch * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < VTK; u++) {
+            const int task = tid + u * kWThreads, kp = task & 31, dc = task >> 5;
+            const int k0 = c * kTile + 2 * kp;
+            const u32x4 z = {0, 0, 0, 0};
+            vreg[u][0] = z;
+            vreg[u][1] = z;
+            if (VTASKS % kWThreads == 0 || task < VTASKS) {
+                if (k0 < d.T) vreg[u][0] = ld16(vg + (long)k0 * DV + dc * 8);
+                if (k0 + 1 < d.T) vreg[u][1] = ld16(vg + (long)(k0 + 1) * DV + dc * 8);
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < KLD; u++) {
+            const int task = tid + u * kWThreads, key = task / CH, ch = task % CH;
+            const int r = (key & ~31) | krow(key & 31);
+            if (KTASKS % kWThreads == 0 || task < KTASKS) st16(&sm.k[buf][r * L::KS + ch * 8], kreg[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < VTK; u++) {
+            const int task = tid + u * kWThreads, kp = task & 31, dc = task >> 5;
+            if (VTASKS % kWThreads == 0 || task < VTASKS) {
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const uint32_t w = __builtin_amdgcn_perm(vreg[u][1][e >> 1], vreg[u][0][e >> 1],
+                                                             (e & 1) ? 0x07060302u : 0x05040100u);
+                    *(uint32_t *)&sm.vt[buf][(dc * 8 + e) * L::VS + 2 * kp] = w;
+                }
+            }
+        }
+    };
+
     float m = -INFINITY, l = 0.f;
     f32x16 oacc[DT];
 #pragma unroll
@@ -179,77 +243,67 @@ __global__ __launch_bounds__(kThreads) void k_window_mfma(RowArgs a, int ntp)
 #pragma unroll
         for (int r = 0; r < 16; r++) oacc[dt][r] = 0.f;
 
-    for (int c = c_first; c <= c_last; c++) {
-        __syncthreads();
-        {
-            constexpr int CH = DK / 8;
-            for (int task = tid; task < kTile * CH; task += kThreads) {
-                const int key = task / CH, ch = task % CH;
-                const int r = (key & ~31) | krow(key & 31);
-                u32x4 x = {0, 0, 0, 0};
-                if (c * kTile + key < d.T) x = ld16(kg + (long)(c * kTile + key) * DK + ch * 8);
-                st16(&sm.k[r * L::KS + ch * 8], x);
-            }
-            constexpr int NDC = DV / 8;
-            for (int task = tid; task < 32 * NDC; task += kThreads) {
-                const int kp = task & 31, dc = task >> 5;
-                const int k0 = c * kTile + 2 * kp;
-                u32x4 v0 = {0, 0, 0, 0}, v1 = {0, 0, 0, 0};
-                if (k0 < d.T) v0 = ld16(vg + (long)k0 * DV + dc * 8);
-                if (k0 + 1 < d.T) v1 = ld16(vg + (long)(k0 + 1) * DV + dc * 8);
-#pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const uint32_t x0 = (v0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                    const uint32_t x1 = (v1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                    *(uint32_t *)&sm.vt[(dc * 8 + e) * L::VS + 2 * kp] = x0 | (x1 << 16);
-                }
-            }
-        }
-        __syncthreads();
+    auto tile = [&](int c, bool masked) {
+        const int buf = c & 1;
 #pragma unroll
         for (int mt = 0; mt < 2; mt++) {
             f32x16 acc;
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[r] = 0.f;
-            const uint16_t *kr = &sm.k[(32 * mt + row) * L::KS + 8 * h];
+            const uint16_t *kr = &sm.k[buf][(32 * mt + row) * L::KS + 8 * h];
 #pragma unroll
             for (int kk = 0; kk < KSTEPS; kk++) acc = mfma32(as_bf16x8(ld16(kr + 16 * kk)), qf[kk], acc);
             const int kb = c * kTile + 32 * mt + 16 * h;
-            float s[16], mx = -INFINITY;
+            if (masked) {
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int key = kb + r;
+                    acc[r] = (live && key >= lo && key <= t) ? acc[r] : -INFINITY;
+                }
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; r++) mx = fmaxf(mx, acc[r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+            if (__any(mx > m + kLazy)) {
+                const float mn = fmaxf(m, mx);
+                const float al = mn == -INFINITY ? 1.f : fast_exp2(m - mn);
+                l *= al;
+#pragma unroll
+                for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) oacc[dt][r] *= al;
+                m = mn;
+            }
+            const float ms = m == -INFINITY ? 0.f : m;   // rows that have seen no key yet
+            float p[16];
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int key = kb + r;
-                s[r] = (live && key >= lo && key <= t) ? acc[r] * sl2 : -INFINITY;
-                mx = fmaxf(mx, s[r]);
+                p[r] = fast_exp2(__builtin_fmaf(acc[r], sl2, -ms));
+                l += p[r];
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            // rows that have seen no key yet keep m = -inf and add nothing;
-            // no branch, so the MFMAs below always run for the whole wave
-            const float mn = fmaxf(m, mx);
-            const bool any = mn != -INFINITY;
-            const float al = any ? fast_exp2(m - mn) : 1.f;
-            float p[16], sum = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                p[r] = any ? fast_exp2(s[r] - mn) : 0.f;
-                sum += p[r];
-            }
-            l = l * al + sum;
-            m = any ? mn : m;
-#pragma unroll
-            for (int dt = 0; dt < DT; dt++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) oacc[dt][r] *= al;
 #pragma unroll
             for (int s2 = 0; s2 < 2; s2++) {
                 const bf16x8 pb = pack8(&p[8 * s2]);
 #pragma unroll
                 for (int dt = 0; dt < DT; dt++) {
-                    const uint16_t *vr = &sm.vt[(32 * dt + row) * L::VS + 32 * mt + 16 * h + 8 * s2];
+                    const uint16_t *vr = &sm.vt[buf][(32 * dt + row) * L::VS + 32 * mt + 16 * h + 8 * s2];
                     oacc[dt] = mfma32(as_bf16x8(ld16(vr)), pb, oacc[dt]);
                 }
             }
         }
+    };
+
+    load_tile(c_first);
+    store_tile(c_first & 1);
+    lds_barrier();
+    for (int c = c_first; c <= c_last; c++) {
+        if (c < c_last) load_tile(c + 1);
+        const int k0 = c * kTile;
+        if (wlive && k0 + kTile - 1 >= wk_lo && k0 <= wk_hi)
+            tile(c, !(both && k0 >= full_lo && k0 + kTile - 1 <= tw0));
+        if (c < c_last) store_tile((c + 1) & 1);
+        lds_barrier();
     }
     const float ltot = l + __shfl_xor(l, 32, 64);
     if (!live) return;
@@ -440,10 +494,10 @@ hipError_t launch_sparse_dims(const RowArgs &a, void *vt_ws, hipStream_t s)
     uint16_t *vpk = kpk + (size_t)BG * d.nb * kTile * DK;
     hipLaunchKernelGGL((k_pack_blocks<DK, DV>), dim3(d.nb, BG), dim3(kThreads), 0, s, (const uint16_t *)a.k,
                        (const uint16_t *)a.v, kpk, vpk, d.T, d.nb);
-    const int ntp = (a.R + kPos - 1) / kPos;
+    const int ntp = (a.R + kWPos - 1) / kWPos;
     long nwg = (long)BG * ntp;
     nwg = (nwg + 7) / 8 * 8;
-    hipLaunchKernelGGL((k_window_mfma<DK, DV>), dim3((unsigned)nwg), dim3(kThreads), 0, s, a, ntp);
+    hipLaunchKernelGGL((k_window_mfma<DK, DV>), dim3((unsigned)nwg), dim3(kWThreads), 0, s, a, ntp);
     const int ntp4 = (a.R + 3) / 4;
     long nwg4 = ((long)BG * ntp4 + 7) / 8 * 8;
     hipLaunchKernelGGL((k_selected_mfma<DK, DV>), dim3((unsigned)nwg4), dim3(kThreads), 0, s, a, kpk, vpk, ntp4);
