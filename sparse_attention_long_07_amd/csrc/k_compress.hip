@@ -1,0 +1,154 @@
+// Token compression for bf16 storage (deepdaiv newsletter on DeepSeek's NSA,
+// deepdaiv.stibee.com/p/82, token compression paragraph: each block of l = 32
+// consecutive tokens, taken every d = 16 tokens, is summarised by one learned
+// map with an intra-block position encoding).
+//
+//   out[bh][i][c] = sum_{m < 32*dim} W[c][m] * (x[bh][16 i * dim + m] + PE[m])
+//                 = sum_m W[c][m] x[...] + sum_m W[c][m] PE[m]
+//
+// Block i flattened token-major is the 32*dim consecutive elements starting
+// at token 16 i, so the product is a plain matrix product whose rows overlap.
+// It runs on the vector ALUs with v_dot2c_f32_bf16 (two bf16 products added
+// into an fp32 accumulator per lane and instruction): the bf16 operands are
+// used as stored, and the position term is accumulated beside it so that
+// x + PE never has to be rounded.
+//
+// Tile: 128 blocks x 64 channels per workgroup, 64 input elements per step,
+// staged through LDS one step ahead (register prefetch, double buffer).  A
+// thread owns 8 blocks (16 apart) x 4 channels.
+#include "mfma_util.h"
+#include "nsa_internal.h"
+
+namespace nsa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTI = 128;     // blocks per tile
+constexpr int kTC = 64;      // channels per tile
+constexpr int kKS = 64;      // input elements per step
+constexpr int kRS = kKS + 8; // LDS row stride (bf16): 144 bytes, 9 x 16 B, so 16 rows hit 16 bank groups
+
+struct CompressLds {
+    uint16_t a[2][kTI * kRS];
+    uint16_t b[2][kTC * kRS];
+    uint16_t pe[2][kKS];
+};
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
+                                           false);
+}
+
+__global__ __launch_bounds__(kThreads) void k_compress_bf16(const uint16_t *__restrict__ x,
+                                                            const uint16_t *__restrict__ W,
+                                                            const uint16_t *__restrict__ PE,
+                                                            uint16_t *__restrict__ out, int T, int dim, int ncmp,
+                                                            int npad)
+{
+    __shared__ CompressLds sm;
+    const int bh = blockIdx.z, i0 = blockIdx.x * kTI, c0 = blockIdx.y * kTC;
+    const int tid = threadIdx.x, ti = tid & 15, tc = tid >> 4;
+    const long L = 32L * dim;
+    const uint16_t *xs = x + (long)bh * T * dim;
+    const int nsteps = (int)(L / kKS);
+
+    // prefetch registers: 4 A chunks, 2 B chunks, 1 PE chunk (threads 0..7)
+    u32x4 ra[4], rb[2], rp;
+    auto load = [&](int s) {
+        const long k0 = (long)s * kKS;
+        const u32x4 z = {0, 0, 0, 0};
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int task = tid + q * kThreads, row = task >> 3, ch = task & 7;
+            const int i = i0 + row;
+            ra[q] = i < ncmp ? ld16(xs + 16L * i * dim + k0 + ch * 8) : z;
+        }
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            const int task = tid + q * kThreads, row = task >> 3, ch = task & 7;
+            const int c = c0 + row;
+            rb[q] = c < dim ? ld16(W + (long)c * L + k0 + ch * 8) : z;
+        }
+        if (tid < 8) rp = ld16(PE + k0 + tid * 8);
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int task = tid + q * kThreads, row = task >> 3, ch = task & 7;
+            st16(&sm.a[buf][row * kRS + ch * 8], ra[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            const int task = tid + q * kThreads, row = task >> 3, ch = task & 7;
+            st16(&sm.b[buf][row * kRS + ch * 8], rb[q]);
+        }
+        if (tid < 8) st16(&sm.pe[buf][tid * 8], rp);
+    };
+
+    float acc[8][4], cacc[4];
+#pragma unroll
+    for (int u = 0; u < 8; u++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) acc[u][v] = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; v++) cacc[v] = 0.f;
+
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int s = 0; s < nsteps; s++) {
+        const int buf = s & 1;
+        if (s + 1 < nsteps) load(s + 1);
+#pragma unroll 2
+        for (int kc = 0; kc < kKS / 8; kc++) {
+            u32x4 av[8], bv[4];
+#pragma unroll
+            for (int u = 0; u < 8; u++) av[u] = ld16(&sm.a[buf][(ti + 16 * u) * kRS + kc * 8]);
+#pragma unroll
+            for (int v = 0; v < 4; v++) bv[v] = ld16(&sm.b[buf][(4 * tc + v) * kRS + kc * 8]);
+            const u32x4 pv = ld16(&sm.pe[buf][kc * 8]);
+#pragma unroll
+            for (int p = 0; p < 4; p++) {
+#pragma unroll
+                for (int u = 0; u < 8; u++)
+#pragma unroll
+                    for (int v = 0; v < 4; v++) acc[u][v] = dot2(av[u][p], bv[v][p], acc[u][v]);
+#pragma unroll
+                for (int v = 0; v < 4; v++) cacc[v] = dot2(pv[p], bv[v][p], cacc[v]);
+            }
+        }
+        if (s + 1 < nsteps) store(buf ^ 1);
+        lds_barrier();
+    }
+    // rows N_cmp .. npad-1 are written as zero
+    const int c = c0 + 4 * tc;
+    if (c >= dim) return;
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+        const int i = i0 + ti + 16 * u;
+        if (i >= npad) continue;
+        uint2 w = {0u, 0u};
+        if (i < ncmp) {
+            w.x = pack_bf16x2(acc[u][0] + cacc[0], acc[u][1] + cacc[1]);
+            w.y = pack_bf16x2(acc[u][2] + cacc[2], acc[u][3] + cacc[3]);
+        }
+        *(uint2 *)(out + ((long)bh * npad + i) * dim + c) = w;
+    }
+}
+
+}  // namespace
+
+bool compress_bf16_supported(const Dims &d) { return d.dtype == NSA_BF16; }
+
+hipError_t launch_compress_bf16(const Dims &d, const void *x, const void *W, const void *PE, void *out, int dim,
+                                hipStream_t s)
+{
+    dim3 grid((d.npad + kTI - 1) / kTI, (dim + kTC - 1) / kTC, d.B * d.Hkv);
+    hipLaunchKernelGGL(k_compress_bf16, grid, dim3(kThreads), 0, s, (const uint16_t *)x, (const uint16_t *)W,
+                       (const uint16_t *)PE, (uint16_t *)out, d.T, dim, d.ncmp, d.npad);
+    return hipGetLastError();
+}
+
+}  // namespace nsa

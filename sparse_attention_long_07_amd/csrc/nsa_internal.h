@@ -102,6 +102,11 @@ hipError_t launch_cmp_attn_generic(const RowArgs &a, bool with_v, hipStream_t s)
 hipError_t launch_select_generic(const RowArgs &a, hipStream_t s);
 hipError_t launch_sparse_generic(const RowArgs &a, hipStream_t s);
 
+// Token compression for bf16 storage on the vector ALUs (bf16 dot products).
+bool compress_bf16_supported(const Dims &d);
+hipError_t launch_compress_bf16(const Dims &d, const void *x, const void *W, const void *PE, void *out, int dim,
+                                hipStream_t s);
+
 // Matrix-core kernels (bf16 storage, G = 16; prefill rows only).
 bool cmp_attn_mfma_supported(const Dims &d);
 hipError_t launch_cmp_attn_mfma(const RowArgs &a, bool with_v, hipStream_t s);
