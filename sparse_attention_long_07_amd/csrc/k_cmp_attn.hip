@@ -137,6 +137,11 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; kk++) qf[kk] = as_bf16x8(live ? ld16(qr + 16 * kk) : z);
     }
+    // Let the query loads land before the tile loop: the compiler cannot tell
+    // them from the next tile's prefetch, and would otherwise wait for every
+    // outstanding load (the prefetch included) at the first matrix op of
+    // each tile.
+    wait_vmem_all();
     const uint16_t *kc = (const uint16_t *)a.kc + (long)bg * d.npad * DK;
     const uint16_t *vc = (const uint16_t *)a.vc + (long)bg * d.npad * DV;
 

@@ -190,6 +190,9 @@ __global__ __launch_bounds__(kWThreads) void k_window_mfma(RowArgs a, int ntp)
         gate[c] = live ? sigmoid(gate[c] + __uint_as_float((uint32_t)*bgp << 16)) : 0.f;
     }
 
+    // let the query and gate loads land before the tile loop (see the
+    // compressed-attention kernel: otherwise every tile waits for its prefetch)
+    wait_vmem_all();
     const uint16_t *kg = (const uint16_t *)a.k + (long)bg * d.T * DK;
     const uint16_t *vg = (const uint16_t *)a.v + (long)bg * d.T * DV;
     u32x4 kreg[KLD], vreg[VTK][2];

@@ -103,6 +103,10 @@ __device__ __forceinline__ float row_transpose_sum16(const float v[16], int lane
     return keep + dpp<kQuadXor1>(send);
 }
 
+// Wait until every outstanding vector-memory load of this wave has returned
+// (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima).
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Workgroup barrier that orders LDS only.  __syncthreads() also fences
 // global memory, which makes every wave wait for its outstanding global loads
 // first and so cancels any prefetch in flight; the barriers in these kernels
