@@ -409,6 +409,7 @@ template <int DV>
 __global__ __launch_bounds__(kThreads) void k_dec_phase_b(DecArgs A)
 {
     extern __shared__ float S[];   // [nb] block scores
+    __shared__ uint2 cand[64];      // selector scratch
     __shared__ float wsp[64][16];  // weight exp2(m_split - lse) of split s for head h
     __shared__ float lse[16];
     const Dims &d = A.d;
@@ -462,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_phase_b(DecArgs A)
     }
     lds_barrier();
     if (A.idx_in || wave != 0) return;
-    wave_select_topn(S, jcur, d.n, A.idx + (long)pair * d.n, lane);
+    wave_select_topn_fast(S, jcur, d.n, A.idx + (long)pair * d.n, lane, cand);
 }
 
 // ---------------------------------------------------------------------------

@@ -225,6 +225,7 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_generic(RowArgs a)
 // Top-n block selection, one wavefront per (row, KV head): see select_util.h.
 __global__ __launch_bounds__(kThreads) void k_select_generic(RowArgs a)
 {
+    __shared__ uint2 cand[kThreads / kWave][64];
     const Dims &d = a.d;
     const int lane = threadIdx.x % kWave;
     const long row = (long)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
@@ -233,7 +234,8 @@ __global__ __launch_bounds__(kThreads) void k_select_generic(RowArgs a)
     const int r = (int)(row % a.R);
     const int b = (int)(row / ((long)d.Hkv * a.R));
     const int t = row_t(a, b, r);
-    wave_select_topn(a.scores + row * d.nb, t / 64, d.n, a.idx_sel + row * d.n, lane);
+    wave_select_topn_fast(a.scores + row * d.nb, t / 64, d.n, a.idx_sel + row * d.n, lane,
+                          cand[threadIdx.x / kWave]);
 }
 
 // ---------------------------------------------------------------------------

@@ -3,12 +3,21 @@
 // 화제", section II: n blocks including the initial block and 2 local blocks).
 //
 // Candidates are blocks 0..jc (jc = t/64).  Blocks 0, jc-1 and jc are always
-// kept; the other n - #kept are chosen one at a time by a wavefront argmax
-// (higher score first, lower block on ties).  Lane L owns blocks L, L+64, ...;
-// the first 16 of them are cached in registers.  The argmax reduces within
-// each row of 16 lanes with DPP moves and across the four rows with
-// readlane.  The chosen set is written in ascending order with a ballot
-// prefix count and padded with -1.
+// kept; the other k = n - #kept are the highest-scoring remaining blocks
+// (lower block on ties).  Two routines give the same result:
+//  * wave_select_topn: k rounds of a wavefront argmax.  Lane L owns blocks
+//    L, L+64, ...; the first 16 of them are cached in registers.  The argmax
+//    reduces within each row of 16 lanes with DPP moves and across the four
+//    rows with readlane.  Any number of candidates.
+//  * wave_select_topn_fast (up to 1024 candidates): a threshold search.  The
+//    k-th largest of the 64 per-lane maxima bounds the k-th largest score from
+//    below, so every block scoring at least that much is a candidate (usually
+//    a few more than k).  Those are compacted into LDS in ascending block
+//    order, and the k-th largest score among them is found by bisection on the
+//    order-preserving integer image of the scores, counting with ballots; ties
+//    at that score go to the lowest blocks.  Falls back to the argmax rounds
+//    when more than 64 blocks pass the first threshold.
+// The chosen set is written in ascending order and padded with -1.
 #pragma once
 
 #include "mfma_util.h"
@@ -103,6 +112,97 @@ __device__ __forceinline__ void wave_select_topn(const float *S, int jcur, int n
         base += __popcll(bal);
     }
     for (int qq = base + lane; qq < n; qq += 64) out[qq] = -1;
+}
+
+// Integer image of a float that orders like the float (NaN maps below -inf).
+__device__ __forceinline__ uint32_t ordered_key(float v)
+{
+    if (v != v) return 0u;
+    const uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Largest x with at least k lanes (of those with `valid`) holding key >= x.
+// Requires at least k valid lanes.  32 bisection steps on wave-uniform bounds.
+__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t key, bool valid, int k)
+{
+    uint32_t lo = 0u, hi = 0xffffffffu;
+    while (lo < hi) {
+        const uint32_t mid = lo + (uint32_t)(((uint64_t)hi - lo + 1u) >> 1);
+        const int cnt = __popcll(__ballot(valid && key >= mid));
+        if (cnt >= k) lo = mid;
+        else hi = mid - 1u;
+    }
+    return lo;
+}
+
+// cand: 64 entries of LDS scratch owned by this wavefront.
+__device__ __forceinline__ void wave_select_topn_fast(const float *S, int jcur, int n, int32_t *out, int lane,
+                                                      uint2 *cand)
+{
+    const int ncand = jcur + 1;
+    const int nforced = jcur == 0 ? 1 : (jcur == 1 ? 2 : 3);
+    const int k = n - nforced;
+    if (ncand > 1024 || ncand - nforced <= k || k <= 0) {
+        wave_select_topn(S, jcur, n, out, lane);
+        return;
+    }
+    // keys of this lane's blocks j = lane + 64 rr; forced blocks and blocks past jc excluded
+    uint32_t key[16];
+    bool ok[16];
+    uint32_t lmax = 0u;
+    bool lvalid = false;
+#pragma unroll
+    for (int rr = 0; rr < 16; rr++) {
+        const int j = lane + 64 * rr;
+        ok[rr] = j < ncand && j != 0 && j != jcur && j != jcur - 1;
+        key[rr] = ok[rr] ? ordered_key(S[j]) : 0u;
+        if (ok[rr] && (!lvalid || key[rr] > lmax)) lmax = key[rr];
+        lvalid |= ok[rr];
+    }
+    // at least k lanes hold a free candidate (k <= 13 and every lane but the
+    // last few holds one once more than k + 3 blocks exist)
+    if (__popcll(__ballot(lvalid)) < k) {
+        wave_select_topn(S, jcur, n, out, lane);
+        return;
+    }
+    const uint32_t x = wave_kth_largest(lmax, lvalid, k);
+    // compact blocks with key >= x, ascending j
+    const uint64_t lt = __lanemask_lt();
+    int C = 0;
+#pragma unroll
+    for (int rr = 0; rr < 16; rr++) {
+        const bool p = ok[rr] && key[rr] >= x;
+        const uint64_t bal = __ballot(p);
+        const int pos = C + __popcll(bal & lt);
+        if (p && pos < 64) cand[pos] = make_uint2(key[rr], (uint32_t)(lane + 64 * rr));
+        C += __popcll(bal);
+    }
+    if (C > 64) {
+        wave_select_topn(S, jcur, n, out, lane);
+        return;
+    }
+    __builtin_amdgcn_wave_barrier();
+    const bool have = lane < C;
+    const uint2 cv = have ? cand[lane] : make_uint2(0u, 0u);
+    // k-th largest score among the candidates; all above it are taken, and
+    // the lowest blocks among those equal to it fill up to k
+    const uint32_t sk = wave_kth_largest(cv.x, have, k);
+    const bool above = have && cv.x > sk;
+    const int nabove = __popcll(__ballot(above));
+    const bool tie = have && cv.x == sk;
+    const uint64_t tb = __ballot(tie);
+    const bool take = above || (tie && __popcll(tb & lt) < k - nabove);
+    // Here jc >= 2, so the forced blocks are 0 < (chosen blocks) < jc-1 < jc:
+    // out = 0, the k chosen blocks ascending, jc-1, jc.
+    const uint64_t tk = __ballot(take);
+    if (take) out[1 + __popcll(tk & lt)] = (int)cv.y;
+    if (lane == 0) {
+        out[0] = 0;
+        out[k + 1] = jcur - 1;
+        out[k + 2] = jcur;
+    }
+    for (int q = nforced + k + lane; q < n; q += 64) out[q] = -1;
 }
 
 }  // namespace nsa

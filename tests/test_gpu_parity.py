@@ -292,3 +292,29 @@ def test_stage_parity(name, s, scaled):
     err = np.abs(np64(o) - ref["o"]).max()
     say("  S4 max|o - ref| = %.3g" % err)
     assert err <= out_tol(s, ref["o"])
+
+
+@pytest.mark.parametrize("mode", ["random", "quantized_ties", "all_equal", "huge_T"])
+def test_select_topn_exact_with_ties(mode):
+    """S3 alone on given scores: the selection must equal the oracle's on
+    every checked row, ties included (equal scores go to the lower block)."""
+    T = 70000 if mode == "huge_T" else 8192
+    s = NSAShape(1, T, 2, 16, 64, 64, n=16)
+    say("select ties", mode, s)
+    rng = np.random.default_rng(21)
+    shape = (s.B, s.Hkv, s.T, s.nb)
+    if mode == "random" or mode == "huge_T":
+        S = rng.random(shape, dtype=np.float32)
+    elif mode == "quantized_ties":
+        S = np.round(rng.random(shape) * 6).astype(np.float32) / 6
+    else:
+        S = np.full(shape, 0.25, dtype=np.float32)
+    idx = nsa.select_topn(s, torch.from_numpy(S).cuda())
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    rows = np.unique(np.concatenate([rng.integers(0, T, 600), np.arange(0, 200), [T - 1, T - 2, 4095, 4096]]))
+    c = ocfg(s)
+    for g in range(s.Hkv):
+        for t in rows:
+            ref = orc.select(c, int(t), S[0, g, t].astype(np.float64))
+            assert np.array_equal(got[0, g, t], ref), (mode, g, int(t), got[0, g, t], ref)
