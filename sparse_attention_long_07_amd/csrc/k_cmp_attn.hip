@@ -42,9 +42,9 @@ constexpr int kThreads = 512;
 template <int DK, int DV>
 struct CmpLds {
     static constexpr int KS = DK + 8;      // bf16 per K row (padded against bank conflicts)
-    static constexpr int VS = kTile + 8;   // bf16 per V^T row
+    static constexpr int VS = DV + 32;     // bf16 per V row: rows 64 B apart in the banks
     uint16_t k[2][kTile * KS];
-    uint16_t vt[2][DV * VS];
+    uint16_t v[2][kTile * VS];             // V key-major; V^T fragments come from transpose reads
     // Per position and head: the tile's 16 block partials (entry 4*grp + u for
     // block u of 16-key group grp) and the weight-1 shares of each group's last
     // key in the next block (entries 16..19).  Laid out by sc_off.
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
     constexpr int CH = DK / 8;                                  // 16-byte chunks per K row
     constexpr int KTASKS = kTile * CH;
     constexpr int KLD = (KTASKS + kThreads - 1) / kThreads;    // K chunks per thread per tile
-    constexpr int VTASKS = 32 * (DV / 8);                       // V^T tasks: two keys x 8 columns
+    constexpr int VTASKS = kTile * (DV / 8);                    // 16-byte V chunks per tile
     constexpr int VTK = (VTASKS + kThreads - 1) / kThreads;
     using L = CmpLds<DK, DV>;
     __shared__ L sm;
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
     const uint16_t *kc = (const uint16_t *)a.kc + (long)bg * d.npad * DK;
     const uint16_t *vc = (const uint16_t *)a.vc + (long)bg * d.npad * DV;
 
-    u32x4 kreg[KLD], vreg[VTK][2];
+    u32x4 kreg[KLD], vreg[VTK];
     auto load_k = [&](int c) {
         const uint16_t *src = kc + (long)c * kTile * DK;
 #pragma unroll
@@ -166,27 +166,28 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
         const uint16_t *src = vc + (long)c * kTile * DV;
 #pragma unroll
         for (int u = 0; u < VTK; u++) {
-            const int task = tid + u * kThreads, kp = task & 31, dc = task >> 5;
-            if (VTASKS % kThreads == 0 || task < VTASKS) {
-                vreg[u][0] = ld16(src + (2 * kp) * DV + dc * 8);
-                vreg[u][1] = ld16(src + (2 * kp + 1) * DV + dc * 8);
-            }
+            const int task = tid + u * kThreads;
+            if (VTASKS % kThreads == 0 || task < VTASKS) vreg[u] = ld16(src + (long)task * 8);
         }
     };
     auto store_vt = [&](int buf) {
+        constexpr int CV = DV / 8;
 #pragma unroll
         for (int u = 0; u < VTK; u++) {
-            const int task = tid + u * kThreads, kp = task & 31, dc = task >> 5;
-            if (VTASKS % kThreads == 0 || task < VTASKS) {
-#pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    // keys 2kp and 2kp+1 of column dc*8+e, as one bf16 pair
-                    const uint32_t w = __builtin_amdgcn_perm(vreg[u][1][e >> 1], vreg[u][0][e >> 1],
-                                                             (e & 1) ? 0x07060302u : 0x05040100u);
-                    *(uint32_t *)&sm.vt[buf][(dc * 8 + e) * L::VS + 2 * kp] = w;
-                }
-            }
+            const int task = tid + u * kThreads, key = task / CV, ch = task % CV;
+            if (VTASKS % kThreads == 0 || task < VTASKS) st16(&sm.v[buf][key * L::VS + ch * 8], vreg[u]);
         }
+    };
+    // V^T fragment of the PV product: dv rows 32*dt + (lane % 32), keys
+    // kb .. kb+7 with kb = 32*mt + 16*(lane/32) + 8*s2 (the 8 keys this lane's
+    // half of the 16-key step holds), read as two transposed 4-key pieces.
+    const int vg = lane >> 4, vs = lane & 15;
+    auto vt_frag = [&](int buf, int dt, int mt, int s2) {
+        const uint16_t *p = &sm.v[buf][(32 * mt + 16 * (vg >> 1) + 8 * s2 + (vs >> 2)) * L::VS + 32 * dt +
+                                       16 * (vg & 1) + 4 * (vs & 3)];
+        const uint2 lo = ld_tr16(p), hi = ld_tr16(p + 4 * L::VS);
+        const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
+        return as_bf16x8(w);
     };
     auto logits = [&](int buf, int mt) {
         f32x16 acc;
@@ -265,11 +266,7 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
                 for (int s2 = 0; s2 < 2; s2++) {
                     const bf16x8 pb = pack8(&p[8 * s2]);
 #pragma unroll
-                    for (int dt = 0; dt < DT; dt++) {
-                        const bf16x8 af = as_bf16x8(
-                            ld16(&sm.vt[buf][(32 * dt + row) * L::VS + 32 * mt + 16 * h + 8 * s2]));
-                        oacc[dt] = mfma32(af, pb, oacc[dt]);
-                    }
+                    for (int dt = 0; dt < DT; dt++) oacc[dt] = mfma32(vt_frag(buf, dt, mt, s2), pb, oacc[dt]);
                 }
             }
             const int grp = 2 * mt + h;

@@ -107,6 +107,21 @@ __device__ __forceinline__ float row_transpose_sum16(const float v[16], int lane
 // (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima).
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// LDS transpose read of 16-bit elements (ds_read_b64_tr_b16; lane mapping
+// checked on the device): within each group of 16 lanes, lane i receives
+// element (i % 4) of the 8-byte pieces addressed by lanes 4e + i/4, e = 0..3.
+// So if lane s of a group points at 4 consecutive columns 4*(s%4) .. +3 of
+// row r0 + s/4 of a row-major matrix, lane i gets column i of rows r0 .. r0+3
+// -- four consecutive rows of one column, the layout of half an MFMA operand
+// whose reduction index runs along those rows.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ uint2 ld_tr16(const uint16_t *p)
+{
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uint16_t *)p);
+    return __builtin_bit_cast(uint2, v);
+}
+
 // Workgroup barrier that orders LDS only.  __syncthreads() also fences
 // global memory, which makes every wave wait for its outstanding global loads
 // first and so cancels any prefetch in flight; the barriers in these kernels
