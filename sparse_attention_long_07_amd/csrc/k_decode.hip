@@ -14,14 +14,17 @@
 //   phase C  the selected blocks (4 per workgroup, one per wavefront);
 //   phase D  merge of the compressed, window and selected partials and the
 //            gated sum.
-// Every wavefront issues all (coalesced) loads of its 64 keys before it
-// computes, so each one keeps 40 KB in flight.
+// Phases A and C run one workgroup of 8 wavefronts per (pair, split) of 256
+// keys; each wavefront issues every load of its 32 keys on entry, so a CU
+// keeps several hundred KB in flight.
 //
 // Lane view (one position, 16 heads, wave64): head hd = lane%16, key group
 // q = lane/16.  A 32-key step is two 16x16x32 S^T tiles whose rows hold keys
 // 8*(i/4) + i%4 and 8*(i/4) + 4 + i%4, so lane (q, hd) ends with the logits
 // of keys 8q .. 8q+7 of the step for head hd: exactly the B operand of
-// O^T = V^T P^T.  K and V reach the operands through a per-wave LDS stage.
+// O^T = V^T P^T.  K is loaded straight into the A-operand registers of the
+// S^T tiles; V goes through a per-wavefront LDS region and comes back as V^T
+// operand fragments by transpose reads.
 #include "mfma_util.h"
 #include "nsa_internal.h"
 #include "select_util.h"
@@ -30,12 +33,11 @@ namespace nsa {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaveKeys = 64;                // keys per wavefront (two 32-key steps)
-constexpr int kSplitKeys = 4 * kWaveKeys;    // keys per phase-A workgroup
-constexpr int kSelPerWg = 4;                 // selected blocks per phase-C workgroup
-constexpr int kPersistentWgs = 256;         // split-K workgroups: one per CU (87 KB of LDS each)
-constexpr int kMaxItemsPerWg = 256;         // work items one split-K workgroup can take
+constexpr int kThreads = 256;               // phases B and D
+constexpr int kSThreads = 512;              // phases A and C: 8 wavefronts
+constexpr int kWaveKeys = 32;               // keys per wavefront (one 32-key step)
+constexpr int kSplitKeys = 8 * kWaveKeys;   // keys per phase-A workgroup
+constexpr int kSelPerWg = 4;                // selected blocks per phase-C workgroup (two waves each)
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.f / (1.f + __expf(-z)); }
 
@@ -53,114 +55,6 @@ __device__ __forceinline__ void load_qf(const uint16_t *qrow, int q, bf16x8 (&qf
     for (int kk = 0; kk < DK / 32; kk++) qf[kk] = as_bf16x8(ld16(qrow + 32 * kk + 8 * q));
 }
 
-// One 32-key step is fetched with coalesced 16-byte loads (adjacent lanes,
-// adjacent bytes) into registers, then written to the wavefront's LDS stage,
-// from where the MFMA operand fragments are read:
-//  * K row of key k goes to LDS row 16*((k%8)/4) + 4*(k/8) + k%4, so the two
-//    16-key S^T tiles (rows 8*(i/4) + i%4 and 8*(i/4) + 4 + i%4) are LDS rows
-//    0..15 and 16..31 and the 16 lanes of a fragment read 16 consecutive rows;
-//  * V stays key-major; eight 2-byte reads build each V^T fragment, and every
-//    group of 8 keys is shifted by 16 bytes so the four key groups of a read
-//    fall in different banks.
-template <int DK, int DV>
-struct StageRegs {
-    static constexpr int NK = DK / 16, NV = DV / 16;   // 16-byte chunks per lane per step
-    u32x4 k[NK], v[NV];
-};
-
-template <int DK, int DV>
-struct StageLds {
-    static constexpr int KS = DK + 8;                   // bf16 per K row
-    static constexpr int VS = DV + 8;                   // bf16 per V row
-    uint16_t k[32 * KS];
-    uint16_t v[32 * VS + 4 * 8];
-    __device__ static int vrow(int key) { return key * VS + (key >> 3) * 8; }
-};
-
-__device__ __forceinline__ int kperm(int k) { return 16 * ((k & 7) >> 2) + 4 * (k >> 3) + (k & 3); }
-
-template <int DK, int DV>
-__device__ __forceinline__ void stage_load_k(const uint16_t *K, int base, int kclamp, int lane, StageRegs<DK, DV> &r)
-{
-    constexpr int CK = DK / 8;
-#pragma unroll
-    for (int i = 0; i < StageRegs<DK, DV>::NK; i++) {
-        const int c = 64 * i + lane, key = c / CK, col = c % CK;
-        r.k[i] = ld16(K + (long)min(base + key, kclamp) * DK + col * 8);
-    }
-}
-
-template <int DK, int DV>
-__device__ __forceinline__ void stage_load_v(const uint16_t *V, int base, int kclamp, int lane, StageRegs<DK, DV> &r)
-{
-    constexpr int CV = DV / 8;
-#pragma unroll
-    for (int i = 0; i < StageRegs<DK, DV>::NV; i++) {
-        const int c = 64 * i + lane, key = c / CV, col = c % CV;
-        r.v[i] = ld16(V + (long)min(base + key, kclamp) * DV + col * 8);
-    }
-}
-
-template <int DK, int DV>
-__device__ __forceinline__ void stage_store_k(const StageRegs<DK, DV> &r, StageLds<DK, DV> &st, int lane)
-{
-    constexpr int CK = DK / 8;
-#pragma unroll
-    for (int i = 0; i < StageRegs<DK, DV>::NK; i++) {
-        const int c = 64 * i + lane, key = c / CK, col = c % CK;
-        st16(&st.k[kperm(key) * StageLds<DK, DV>::KS + col * 8], r.k[i]);
-    }
-}
-
-template <int DK, int DV>
-__device__ __forceinline__ void stage_store_v(const StageRegs<DK, DV> &r, StageLds<DK, DV> &st, int lane)
-{
-    constexpr int CV = DV / 8;
-#pragma unroll
-    for (int i = 0; i < StageRegs<DK, DV>::NV; i++) {
-        const int c = 64 * i + lane, key = c / CV, col = c % CV;
-        st16(&st.v[StageLds<DK, DV>::vrow(key) + col * 8], r.v[i]);
-    }
-}
-
-// Raw logits of keys 8q .. 8q+7 of the staged step for head hd.
-template <int DK, int DV>
-__device__ __forceinline__ void logits_lds(const StageLds<DK, DV> &st, const bf16x8 (&qf)[DK / 32], int hd, int q,
-                                           float (&s)[8])
-{
-    constexpr int KS = StageLds<DK, DV>::KS;
-    f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < DK / 32; kk++) {
-        accA = mfma16(as_bf16x8(ld16(&st.k[hd * KS + 32 * kk + 8 * q])), qf[kk], accA);
-        accB = mfma16(as_bf16x8(ld16(&st.k[(16 + hd) * KS + 32 * kk + 8 * q])), qf[kk], accB);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; u++) {
-        s[u] = accA[u];
-        s[4 + u] = accB[u];
-    }
-}
-
-// O^T += V^T P^T for the staged step (P^T = this lane's keys 8q .. 8q+7).
-template <int DK, int DV>
-__device__ __forceinline__ void pv_lds(const StageLds<DK, DV> &st, const float (&p)[8], int hd, int q,
-                                       f32x4 (&oacc)[DV / 16])
-{
-    const bf16x8 pb = pack8(p);
-#pragma unroll
-    for (int dt = 0; dt < DV / 16; dt++) {
-        u32x4 a;
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const uint32_t lo = st.v[StageLds<DK, DV>::vrow(8 * q + 2 * e) + 16 * dt + hd];
-            const uint32_t hi = st.v[StageLds<DK, DV>::vrow(8 * q + 2 * e + 1) + 16 * dt + hd];
-            a[e] = lo | (hi << 16);
-        }
-        oacc[dt] = mfma16(as_bf16x8(a), pb, oacc[dt]);
-    }
-}
-
 __device__ __forceinline__ float head_max(float x)
 {
     x = fmaxf(x, __shfl_xor(x, 16, 64));
@@ -172,233 +66,226 @@ __device__ __forceinline__ float head_sum(float x)
     return x + __shfl_xor(x, 32, 64);
 }
 
-template <int DK, int DV>
-struct DecLds {
-    union {
-        StageLds<DK, DV> st[4];     // one stage per wavefront
-        float ol[4][16][DV + 4];    // merge buffer; padded rows spread the 16 heads over banks
-    } u;
-    float mx[4][16];
-    float ls[4][16];
+// Per-wavefront LDS region: the step's V rows (key-major, DV bf16 = U units
+// of 32 bytes each), unit u of row r stored at unit u ^ sigma(r) with
+// sigma(r) = (r%4) | 4*((r/8)%2) (mod U).  The transpose reads of a V^T
+// fragment touch one unit of rows {8g + 0..3} (then + 4) for the four lane
+// groups g, and sigma spreads the rows of each half-wave over distinct units;
+// the 16-byte row stores fill whole rows.  Afterwards the same bytes hold the
+// wavefront's output for the workgroup merge.
+template <int DV>
+struct DecWaveLds {
+    static constexpr int U = DV / 16;                            // 32-byte units per V row
+    static constexpr int VBYTES = kWaveKeys * 2 * DV;
+    static constexpr int OBYTES = 16 * (DV + 4) * 4;             // [16][DV+4] fp32
+    static constexpr int BYTES = VBYTES > OBYTES ? VBYTES : OBYTES;
+    __device__ static int vaddr(int r, int unit, int byte)
+    {
+        const int sig = ((r & 3) | ((r >> 1) & 4)) & (U - 1);
+        return r * 2 * DV + ((unit ^ sig) << 5) + byte;
+    }
 };
 
-// Workgroup-level merge of four wavefronts that used the same max M:
-// sums l and O in wave order and writes (M, l, O) for the 16 heads.
-template <int DK, int DV>
-__device__ __forceinline__ void wg_store_partial(DecLds<DK, DV> &sm, int wave, int lane, float M, float l,
-                                                 const f32x4 (&oacc)[DV / 16], float *pm, float *pl, float *po)
-{
-    const int hd = lane & 15, q = lane >> 4;
-    lds_barrier();   // the stages alias the merge buffer
-#pragma unroll
-    for (int dt = 0; dt < DV / 16; dt++)
-#pragma unroll
-        for (int u = 0; u < 4; u++) sm.u.ol[wave][hd][16 * dt + 4 * q + u] = oacc[dt][u];
-    if (q == 0) sm.ls[wave][hd] = l;
-    lds_barrier();
-    const int tid = wave * 64 + lane;
-    for (int e = tid; e < 16 * DV; e += kThreads) {
-        const int h = e / DV, c = e % DV;
-        po[e] = sm.u.ol[0][h][c] + sm.u.ol[1][h][c] + sm.u.ol[2][h][c] + sm.u.ol[3][h][c];
-    }
-    if (tid < 16) {
-        pl[tid] = sm.ls[0][tid] + sm.ls[1][tid] + sm.ls[2][tid] + sm.ls[3][tid];
-        pm[tid] = M;   // every lane of every wave holds the same M for head tid; see callers
-    }
-}
+template <int DV>
+struct DecLds {
+    unsigned char wave[8][DecWaveLds<DV>::BYTES];
+    float mx[8][16];
+    float ls[8][16];
+};
 
-// ---------------------------------------------------------------------------
-// Phases A and C: persistent split-K workgroups.  Work item = (pair, slot);
-// workgroup w takes items w, w + gridDim.x, ...  Phase-A slots 0..cs-1 cover
-// compressed slots [256 s, 256 s + 256), slots cs.. cover window keys from
-// max(0, t-w+1); phase-C slot s covers the selected blocks 4s .. 4s+3 of the
-// pair's (deduplicated) list, one block per wavefront.  As soon as one item's
-// K (then V) registers are in the LDS stage, the next item's loads are issued
-// into them, so the memory system stays busy while the item computes.
 constexpr int kPhaseA = 0, kPhaseC = 1;
 
-struct WaveItem {
-    int pair, slot, t;
-    int kbeg, kend, kclamp;
-    bool cmp;
-    const uint16_t *K, *V;
-};
-
-// t and (phase C) the block list of the workgroup's k-th item come from LDS,
-// filled once at kernel start, so no item waits on a dependent global load.
+// Phases A and C.  Workgroup = (pair, slot): phase-A slots 0..cs-1 are the
+// compressed slots [256 s, 256 s + 256), slots cs.. the window keys from
+// max(0, t-w+1) in steps of 256; phase-C slot s holds the selected blocks
+// 4s .. 4s+3 of the pair's deduplicated list (two wavefronts per block).
+// Wavefront w takes keys kbeg .. kbeg+31; all 8 use the workgroup's maximum
+// per head, so the partial (max, sum, unnormalised output) is one sum.
 template <int DK, int DV, int KIND>
-__device__ __forceinline__ WaveItem wave_item(const DecArgs &A, int item, int k, const int *it_t, const int *it_idx,
-                                              int wave, int lane)
+__global__ __launch_bounds__(kSThreads) void k_dec_stream(DecArgs A)
 {
+    constexpr int KS = DK / 32;      // 16x16x32 steps over the head dim
+    constexpr int DT = DV / 16;      // 16-wide dv tiles
+    constexpr int VC = DV / 8;       // 16-byte chunks per V row
+    constexpr int VL = kWaveKeys * VC / 64;   // V chunks per lane
+    using WL = DecWaveLds<DV>;
+    __shared__ DecLds<DV> sm;
     const Dims &d = A.d;
-    WaveItem r;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hd = lane & 15, q = lane >> 4;
+    const float sl2 = d.scale * kLog2e;
+    const int nslots = KIND == kPhaseA ? A.cs + A.ws : A.ss;
+    const int pair = blockIdx.x / nslots, slot = blockIdx.x % nslots;
+    const int b = pair / d.Hkv;
+    const int t = dec_t(A.seq_lens, b, d.T);
+
+    // this wavefront's keys
+    int kbeg, kend, kclamp;
+    bool cmp = false;
+    const uint16_t *K, *V;
     if (KIND == kPhaseA) {
-        const int nsplit = A.cs + A.ws;
-        r.pair = item / nsplit;
-        r.slot = item % nsplit;
-        r.t = it_t[k];
-        r.cmp = r.slot < A.cs;
-        if (r.cmp) {
-            const int nvis = r.t >= 31 ? (r.t - 31) / 16 + 1 : 0;
-            r.kbeg = r.slot * kSplitKeys + wave * kWaveKeys;
-            r.kend = min(r.kbeg + kWaveKeys, nvis);
-            r.kclamp = d.npad - 1;
-            r.K = (const uint16_t *)A.kc + (long)r.pair * d.npad * DK;
-            r.V = (const uint16_t *)A.vc + (long)r.pair * d.npad * DV;
+        cmp = slot < A.cs;
+        if (cmp) {
+            const int nvis = t >= 31 ? (t - 31) / 16 + 1 : 0;
+            kbeg = slot * kSplitKeys + wave * kWaveKeys;
+            kend = min(kbeg + kWaveKeys, nvis);
+            kclamp = d.npad - 1;
+            K = (const uint16_t *)A.kc + (long)pair * d.npad * DK;
+            V = (const uint16_t *)A.vc + (long)pair * d.npad * DV;
         } else {
-            const int lo = max(0, r.t - d.w + 1);
-            r.kbeg = lo + (r.slot - A.cs) * kSplitKeys + wave * kWaveKeys;
-            r.kend = min(r.kbeg + kWaveKeys, r.t + 1);
-            r.kclamp = d.T - 1;
-            r.K = (const uint16_t *)A.k + (long)r.pair * d.T * DK;
-            r.V = (const uint16_t *)A.v + (long)r.pair * d.T * DV;
+            const int lo = max(0, t - d.w + 1);
+            kbeg = lo + (slot - A.cs) * kSplitKeys + wave * kWaveKeys;
+            kend = min(kbeg + kWaveKeys, t + 1);
+            kclamp = d.T - 1;
+            K = (const uint16_t *)A.k + (long)pair * d.T * DK;
+            V = (const uint16_t *)A.v + (long)pair * d.T * DV;
         }
     } else {
-        r.pair = item / A.ss;
-        r.slot = item % A.ss;
-        r.t = it_t[k];
-        r.cmp = false;
-        const int jcur = r.t / 64;
-        const int jb = lane < d.n ? it_idx[k * 16 + lane] : -1;
+        // the (2 slot + wave/2)-th distinct valid block of the pair's list
+        const int jcur = t / 64;
+        const int32_t *isrc = (A.idx_in ? A.idx_in : A.idx) + (long)pair * d.n;
+        const int jb = lane < d.n ? isrc[lane] : -1;
         bool ok = jb >= 0 && jb <= jcur;
         for (int u = 0; u < 16; u++) {
             const int other = __shfl(jb, u, 64);
             if (u < lane && other == jb) ok = false;
         }
         uint64_t v = __ballot(ok);
-        for (int c = 0; c < kSelPerWg * r.slot + wave && v; c++) v &= v - 1;
+        for (int c = 0; c < kSelPerWg * slot + (wave >> 1) && v; c++) v &= v - 1;
         const int j = v ? __shfl(jb, __builtin_ctzll(v), 64) : -1;
-        r.kbeg = j < 0 ? 0 : 64 * j;
-        r.kend = j < 0 ? 0 : min(64 * j + 64, r.t + 1);
-        r.kclamp = d.T - 1;
-        r.K = (const uint16_t *)A.k + (long)r.pair * d.T * DK;
-        r.V = (const uint16_t *)A.v + (long)r.pair * d.T * DV;
+        kbeg = j < 0 ? 0 : 64 * j + kWaveKeys * (wave & 1);
+        kend = j < 0 ? 0 : min(kbeg + kWaveKeys, t + 1);
+        kclamp = d.T - 1;
+        K = (const uint16_t *)A.k + (long)pair * d.T * DK;
+        V = (const uint16_t *)A.v + (long)pair * d.T * DV;
     }
-    return r;
-}
+    const bool active = kbeg < kend;   // uniform over the wavefront
 
-template <int DK, int DV, int KIND>
-__global__ __launch_bounds__(kThreads) void k_dec_splitk(DecArgs A, int total)
-{
-    __shared__ DecLds<DK, DV> sm;
-    const Dims &d = A.d;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int hd = lane & 15, q = lane >> 4;
-    const float sl2 = d.scale * kLog2e;
-    const int nslots = KIND == kPhaseA ? A.cs + A.ws : A.ss;
-    int item = blockIdx.x;
-    if (item >= total) return;
-    // per-item t (and block lists) of this workgroup's items, loaded at once
-    __shared__ int it_t[kMaxItemsPerWg];
-    __shared__ int it_idx[KIND == kPhaseC ? kMaxItemsPerWg * 16 : 1];
-    const int nitems = (total - 1 - blockIdx.x) / gridDim.x + 1;
-    for (int k = tid; k < nitems; k += kThreads) {
-        const int pair = (blockIdx.x + k * gridDim.x) / nslots;
-        it_t[k] = dec_t(A.seq_lens, pair / d.Hkv, d.T);
-    }
-    if (KIND == kPhaseC) {
-        const int32_t *isrc = A.idx_in ? A.idx_in : A.idx;
-        for (int e = tid; e < nitems * 16; e += kThreads) {
-            const int pair = (blockIdx.x + (e >> 4) * gridDim.x) / nslots;
-            it_idx[e] = (e & 15) < d.n ? isrc[(long)pair * d.n + (e & 15)] : -1;
+    // issue every load of the step: K into the S^T operand registers (tile A
+    // row i holds key 8(i/4) + i%4, tile B key 8(i/4) + 4 + i%4), V rows into
+    // registers for the LDS region, the query fragments
+    const int kA = kbeg + 8 * (hd >> 2) + (hd & 3);
+    u32x4 ka[KS], kb2[KS], vr[VL];
+    bf16x8 qf[KS];
+    if (active) {
+        const uint16_t *ra = K + (long)min(kA, kclamp) * DK + 8 * q;
+        const uint16_t *rb = K + (long)min(kA + 4, kclamp) * DK + 8 * q;
+#pragma unroll
+        for (int kk = 0; kk < KS; kk++) {
+            ka[kk] = ld16(ra + 32 * kk);
+            kb2[kk] = ld16(rb + 32 * kk);
         }
+#pragma unroll
+        for (int u = 0; u < VL; u++) {
+            const int c = 64 * u + lane, key = c / VC, ch = c % VC;
+            vr[u] = ld16(V + (long)min(kbeg + key, kclamp) * DV + ch * 8);
+        }
+        const uint16_t *qrow = (const uint16_t *)A.q + ((long)b * d.Hq + (pair % d.Hkv) * 16 + hd) * DK;
+#pragma unroll
+        for (int kk = 0; kk < KS; kk++) qf[kk] = as_bf16x8(ld16(qrow + 32 * kk + 8 * q));
     }
+
+    // logits of keys kbeg + 8q .. +7 for head hd
+    float s[8];
+    float mx = -INFINITY;
+    if (active) {
+        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; kk++) {
+            accA = mfma16(as_bf16x8(ka[kk]), qf[kk], accA);
+            accB = mfma16(as_bf16x8(kb2[kk]), qf[kk], accB);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            s[u] = kbeg + 8 * q + u < kend ? accA[u] * sl2 : -INFINITY;
+            s[4 + u] = kbeg + 8 * q + 4 + u < kend ? accB[u] * sl2 : -INFINITY;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e++) mx = fmaxf(mx, s[e]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; e++) s[e] = -INFINITY;
+    }
+    mx = head_max(mx);
+    if (q == 0) sm.mx[wave][hd] = mx;
     lds_barrier();
-    int k_it = 0;
-    WaveItem r = wave_item<DK, DV, KIND>(A, item, k_it, it_t, it_idx, wave, lane);
-    StageRegs<DK, DV> rg[2];
-    bf16x8 qf[DK / 32];
-    auto qrow = [&](const WaveItem &x) {
-        return (const uint16_t *)A.q + ((long)(x.pair / d.Hkv) * d.Hq + (x.pair % d.Hkv) * 16 + hd) * DK;
-    };
+    float M = sm.mx[0][hd];
 #pragma unroll
-    for (int st = 0; st < 2; st++)
-        if (r.kbeg + 32 * st < r.kend) {
-            stage_load_k<DK, DV>(r.K, r.kbeg + 32 * st, r.kclamp, lane, rg[st]);
-            stage_load_v<DK, DV>(r.V, r.kbeg + 32 * st, r.kclamp, lane, rg[st]);
+    for (int w = 1; w < 8; w++) M = fmaxf(M, sm.mx[w][hd]);
+
+    float p[8], l = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        p[e] = M == -INFINITY ? 0.f : fast_exp2(s[e] - M);
+        l += p[e];
+    }
+    if (KIND == kPhaseA && cmp) {
+        // block a = (kbeg + 8q)/4 gets keys 4a..4a+3 here (weights 2,2,2,1);
+        // its remaining weight-1 key 4a-1 is the previous block's Y term
+        float *bx = A.bx + (long)pair * 16 * A.nbp + (long)hd * A.nbp;
+        float *by = A.by + (long)pair * 16 * A.nbp + (long)hd * A.nbp;
+        const int a = (kbeg + 8 * q) >> 2;
+        if (a + 1 < A.nbp) {
+            *(float2 *)&bx[a] = make_float2(2.f * (p[0] + p[1] + p[2]) + p[3], 2.f * (p[4] + p[5] + p[6]) + p[7]);
+            *(float2 *)&by[a] = make_float2(p[3], p[7]);
         }
-    load_qf<DK>(qrow(r), q, qf);
-    StageLds<DK, DV> &stg = sm.u.st[wave];
-    while (true) {
-        const int nxt = item + gridDim.x;
-        const bool more = nxt < total;
-        WaveItem rn = r;
-        if (more) rn = wave_item<DK, DV, KIND>(A, nxt, k_it + 1, it_t, it_idx, wave, lane);
-        lds_barrier();   // the previous item's merge is done with the stage memory
-        float s[2][8];
-        float mx = -INFINITY;
+    }
+    l = head_sum(l);
+
+    // O^T += V^T P^T through this wavefront's LDS region
+    unsigned char *reg = sm.wave[wave];
+    f32x4 oacc[DT];
 #pragma unroll
-        for (int st = 0; st < 2; st++) {
-            const int base = r.kbeg + 32 * st;
-            if (base < r.kend) {   // uniform over the wavefront
-                stage_store_k<DK, DV>(rg[st], stg, lane);
-                logits_lds<DK, DV>(stg, qf, hd, q, s[st]);
+    for (int dt = 0; dt < DT; dt++) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (active) {
 #pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    s[st][e] = base + 8 * q + e < r.kend ? s[st][e] * sl2 : -INFINITY;
-                    mx = fmaxf(mx, s[st][e]);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; e++) s[st][e] = -INFINITY;
-            }
+        for (int u = 0; u < VL; u++) {
+            const int c = 64 * u + lane, key = c / VC, ch = c % VC;
+            st16(reg + WL::vaddr(key, ch >> 1, 16 * (ch & 1)), vr[u]);
         }
-        if (more) {   // K registers and q fragments are free: prefetch the next item's
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wavefront's stores are in LDS
+        __builtin_amdgcn_wave_barrier();
+        const bf16x8 pb = pack8(p);
+        // lane (g, s) of a 16-lane group points at columns 16dt + 4(s%4) of
+        // rows 8g + s/4 (then + 4): lane i then holds dv 16dt + i for keys
+        // 8g .. 8g+7, the A operand of O^T = V^T P^T
+        const int g = lane >> 4, sl = lane & 15;
+        const int r0 = 8 * g + (sl >> 2);
 #pragma unroll
-            for (int st = 0; st < 2; st++)
-                if (rn.kbeg + 32 * st < rn.kend) stage_load_k<DK, DV>(rn.K, rn.kbeg + 32 * st, rn.kclamp, lane, rg[st]);
-            load_qf<DK>(qrow(rn), q, qf);
+        for (int dt = 0; dt < DT; dt++) {
+            const uint2 lo = ld_tr16((const uint16_t *)(reg + WL::vaddr(r0, dt, 8 * (sl & 3))));
+            const uint2 hi = ld_tr16((const uint16_t *)(reg + WL::vaddr(r0 + 4, dt, 8 * (sl & 3))));
+            const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
+            oacc[dt] = mfma16(as_bf16x8(w), pb, oacc[dt]);
         }
-        mx = head_max(mx);
-        if (q == 0) sm.mx[wave][hd] = mx;
-        lds_barrier();
-        const float M = fmaxf(fmaxf(sm.mx[0][hd], sm.mx[1][hd]), fmaxf(sm.mx[2][hd], sm.mx[3][hd]));
-        float l = 0.f;
-        f32x4 oacc[DV / 16];
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // the transpose reads are done before the region is reused
+        __builtin_amdgcn_wave_barrier();
+    }
+    // merge of the 8 wavefronts (same M): O and l summed in wave order
+    float *ol = (float *)reg;   // [16][DV+4]
 #pragma unroll
-        for (int dt = 0; dt < DV / 16; dt++) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float *bx = A.bx + (long)r.pair * 16 * A.nbp + (long)hd * A.nbp;
-        float *by = A.by + (long)r.pair * 16 * A.nbp + (long)hd * A.nbp;
+    for (int dt = 0; dt < DT; dt++)
 #pragma unroll
-        for (int st = 0; st < 2; st++) {
-            const int base = r.kbeg + 32 * st;
-            float p[8];
+        for (int u = 0; u < 4; u++) ol[hd * (DV + 4) + 16 * dt + 4 * q + u] = oacc[dt][u];
+    if (q == 0) sm.ls[wave][hd] = l;
+    lds_barrier();
+    const long pidx = (long)pair * nslots + slot;
+    float *pm = (KIND == kPhaseA ? A.pm : A.sm) + pidx * 16;
+    float *pl = (KIND == kPhaseA ? A.pl : A.sl) + pidx * 16;
+    float *po = (KIND == kPhaseA ? A.po : A.so) + pidx * 16 * DV;
+    for (int e = tid; e < 16 * DV; e += kSThreads) {
+        const int h = e / DV, c = e % DV;
+        float acc = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; e++) p[e] = M == -INFINITY ? 0.f : fast_exp2(s[st][e] - M);
-            if (KIND == kPhaseA && r.cmp) {
-                // block a = (base + 8q)/4 gets keys 4a..4a+3 here (weights 2,2,2,1);
-                // its remaining weight-1 key 4a-1 is the previous block's Y term
-                const int a = (base + 8 * q) >> 2;
-                if (a + 1 < A.nbp) {
-                    *(float2 *)&bx[a] =
-                        make_float2(2.f * (p[0] + p[1] + p[2]) + p[3], 2.f * (p[4] + p[5] + p[6]) + p[7]);
-                    *(float2 *)&by[a] = make_float2(p[3], p[7]);
-                }
-            }
-            if (base < r.kend) {   // uniform over the wavefront
+        for (int w = 0; w < 8; w++) acc += ((const float *)sm.wave[w])[h * (DV + 4) + c];
+        po[e] = acc;
+    }
+    if (tid < 16) {
+        float L = 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; e++) l += p[e];
-                stage_store_v<DK, DV>(rg[st], stg, lane);
-                pv_lds<DK, DV>(stg, p, hd, q, oacc);
-            }
-        }
-        if (more) {
-#pragma unroll
-            for (int st = 0; st < 2; st++)
-                if (rn.kbeg + 32 * st < rn.kend) stage_load_v<DK, DV>(rn.V, rn.kbeg + 32 * st, rn.kclamp, lane, rg[st]);
-        }
-        l = head_sum(l);
-        const long pidx = (long)r.pair * nslots + r.slot;
-        if (KIND == kPhaseA)
-            wg_store_partial<DK, DV>(sm, wave, lane, M, l, oacc, A.pm + pidx * 16, A.pl + pidx * 16,
-                                     A.po + pidx * 16 * DV);
-        else
-            wg_store_partial<DK, DV>(sm, wave, lane, M, l, oacc, A.sm + pidx * 16, A.sl + pidx * 16,
-                                     A.so + pidx * 16 * DV);
-        if (!more) break;
-        item = nxt;
-        k_it++;
-        r = rn;
+        for (int w = 0; w < 8; w++) L += sm.ls[w][tid];
+        pl[tid] = L;
+        pm[tid] = M;   // the workgroup maximum of head tid (lane tid holds head tid)
     }
 }
 
@@ -555,9 +442,9 @@ hipError_t launch_decode_dims(const DecArgs &A, hipStream_t s)
     const Dims &d = A.d;
     const int pairs = d.B * d.Hkv;
     const int na = pairs * (A.cs + A.ws), nc = pairs * A.ss;
-    hipLaunchKernelGGL((k_dec_splitk<DK, DV, kPhaseA>), dim3(min(na, kPersistentWgs)), dim3(kThreads), 0, s, A, na);
+    hipLaunchKernelGGL((k_dec_stream<DK, DV, kPhaseA>), dim3(na), dim3(kSThreads), 0, s, A);
     hipLaunchKernelGGL((k_dec_phase_b<DV>), dim3(pairs), dim3(kThreads), sizeof(float) * d.nb, s, A);
-    hipLaunchKernelGGL((k_dec_splitk<DK, DV, kPhaseC>), dim3(min(nc, kPersistentWgs)), dim3(kThreads), 0, s, A, nc);
+    hipLaunchKernelGGL((k_dec_stream<DK, DV, kPhaseC>), dim3(nc), dim3(kSThreads), 0, s, A);
     hipLaunchKernelGGL((k_dec_phase_d<DK, DV>), dim3(pairs * (16 / kDHeads)), dim3(kThreads), 0, s, A);
     return hipGetLastError();
 }
@@ -571,8 +458,7 @@ bool decode_mfma_supported(const Dims &d)
     const int cs = (d.npad + kSplitKeys - 1) / kSplitKeys, ws = (d.w + kSplitKeys - 1) / kSplitKeys;
     const long pairs = (long)d.B * d.Hkv;
     const int ss = (d.n + kSelPerWg - 1) / kSelPerWg;
-    return cs + ws <= 64 && d.npad / 4 <= 16384 && pairs * (cs + ws) <= (long)kPersistentWgs * kMaxItemsPerWg &&
-           pairs * ss <= (long)kPersistentWgs * kMaxItemsPerWg;
+    return cs + ws <= 64 && d.npad / 4 <= 16384 && pairs * (cs + ws) <= 0x7fffffffL && pairs * ss <= 0x7fffffffL;
 }
 
 // Workspace of the matrix-core decode step, carved from `ws` when non-null.
