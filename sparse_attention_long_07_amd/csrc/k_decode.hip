@@ -9,11 +9,13 @@
 //            per workgroup): per-workgroup (max, sum, unnormalised output),
 //            plus, for the compressed slots, each block's importance terms;
 //   phase B  per (sequence, KV head): exact log-sum-exp over the compressed
-//            splits, o_cmp, block scores (heads summed, weights 1,2,2,2,1)
-//            and the top-n selection;
-//   phase C  the selected blocks (4 per workgroup, one per wavefront);
+//            splits, block scores (heads summed, weights 1,2,2,2,1) and the
+//            top-n selection;
+//   phase C  the selected blocks (one wavefront per block, online softmax);
 //   phase D  merge of the compressed, window and selected partials and the
 //            gated sum.
+// Phase A is one kernel; B, C and D run in a second one, one workgroup of 16
+// wavefronts per (sequence, KV head), so the step costs two launches.
 // Phases A and C run one workgroup of 8 wavefronts per (pair, split) of 256
 // keys; each wavefront issues every load of its 32 keys on entry, so a CU
 // keeps several hundred KB in flight.
@@ -290,115 +292,249 @@ __global__ __launch_bounds__(kSThreads) void k_dec_stream(DecArgs A)
 }
 
 // ---------------------------------------------------------------------------
-// Phase B.  One workgroup per (sequence, KV head): the exact log-sum-exp of
-// each head over the compressed splits, the block scores and the selection.
+// Phases B, C and D for one (sequence, KV head): one workgroup of 16
+// wavefronts.
+constexpr int kTailThreads = 1024;
+constexpr int kTailWaves = 16;
+
 template <int DV>
-__global__ __launch_bounds__(kThreads) void k_dec_phase_b(DecArgs A)
+struct TailLds {
+    union {
+        struct {                       // phase B
+            float lm[64][16], ll[64][16], wsp[64][16];
+            float lse[16];
+            uint2 cand[64];
+            float S[8192];             // block scores (nb <= 8192)
+        } b;
+        unsigned char wave[kTailWaves][DecWaveLds<DV>::BYTES];   // phase C
+        struct {                       // phase D
+            float lm[2][64][16], ll[2][64][16], wts[2][64][16];
+            float gate[16][3];
+        } d;
+    } u;
+    float os[16][DV];                  // selected branch: merged unnormalised output
+    float ms[16], lsum[16];            // and its max / sum per head
+    float wm[kTailWaves][16], wl[kTailWaves][16];
+    int blist[16];
+    int nblk;
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kTailThreads) void k_dec_tail(DecArgs A)
 {
-    extern __shared__ float S[];   // [nb] block scores
-    __shared__ uint2 cand[64];      // selector scratch
-    __shared__ float wsp[64][16];  // weight exp2(m_split - lse) of split s for head h
-    __shared__ float lse[16];
+    constexpr int KS = DK / 32, DT = DV / 16, VC = DV / 8, VL = kWaveKeys * VC / 64;
+    constexpr int NT = kTailThreads;
+    using WL = DecWaveLds<DV>;
+    __shared__ TailLds<DV> sm;
     const Dims &d = A.d;
-    const int pair = blockIdx.x;
-    const int b = pair / d.Hkv;
+    const int pair = blockIdx.x, b = pair / d.Hkv, g = pair % d.Hkv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hd = lane & 15, q = lane >> 4;
     const int t = dec_t(A.seq_lens, b, d.T);
     const int jcur = t / 64;
+    const float sl2 = d.scale * kLog2e;
     const int nsplit = A.cs + A.ws;
     const float *pm = A.pm + (long)pair * nsplit * 16, *pl = A.pl + (long)pair * nsplit * 16;
-    __shared__ float lm[64][16], ll[64][16];
-    for (int e = tid; e < A.cs * 16; e += kThreads) {   // all loads in flight at once
-        lm[e >> 4][e & 15] = pm[e];
-        ll[e >> 4][e & 15] = pl[e];
+
+    // ---- phase B: exact log-sum-exp per head, block scores, selection
+    const int32_t *ilist = A.idx_in ? A.idx_in + (long)pair * d.n : A.idx + (long)pair * d.n;
+    if (!A.idx_in) {
+        auto &B = sm.u.b;
+        for (int e = tid; e < A.cs * 16; e += NT) {
+            B.lm[e >> 4][e & 15] = pm[e];
+            B.ll[e >> 4][e & 15] = pl[e];
+        }
+        lds_barrier();
+        if (tid < 16) {
+            float M = -INFINITY;
+            for (int s2 = 0; s2 < A.cs; s2++) M = fmaxf(M, B.lm[s2][tid]);
+            float L = 0.f;
+            if (M != -INFINITY)
+                for (int s2 = 0; s2 < A.cs; s2++) L += B.ll[s2][tid] * fast_exp2(B.lm[s2][tid] - M);
+            B.lse[tid] = M == -INFINITY ? -INFINITY : M + fast_log2(L);
+        }
+        lds_barrier();
+        for (int e = tid; e < A.cs * 16; e += NT) {
+            const int s2 = e >> 4, h = e & 15;
+            B.wsp[s2][h] = B.lse[h] == -INFINITY ? 0.f : fast_exp2(B.lm[s2][h] - B.lse[h]);
+        }
+        lds_barrier();
+        // block j: its own keys 4j..4j+3 (X) plus key 4j-1 (Y of block j-1);
+        // phase A wrote blocks 0..nbp-1, a block past them has no key of its own
+        const float *bx = A.bx + (long)pair * 16 * A.nbp, *by = A.by + (long)pair * 16 * A.nbp;
+        constexpr int kBlkPerSplit = kSplitKeys / 4;
+        for (int j = tid; j <= jcur; j += NT) {
+            const int sj = j / kBlkPerSplit, sp = (j - 1) / kBlkPerSplit;
+            const bool hx = j < A.nbp, hy = j > 0 && j - 1 < A.nbp;
+            float xv[16], yv[16];
+#pragma unroll
+            for (int h = 0; h < 16; h++) {
+                xv[h] = hx ? bx[(long)h * A.nbp + j] : 0.f;
+                yv[h] = hy ? by[(long)h * A.nbp + j - 1] : 0.f;
+            }
+            float acc = 0.f;
+#pragma unroll
+            for (int h = 0; h < 16; h++) {
+                acc += xv[h] * B.wsp[sj][h];
+                if (hy) acc += yv[h] * B.wsp[sp][h];
+            }
+            B.S[j] = acc;
+        }
+        lds_barrier();
+        if (wave == 0) wave_select_topn_fast(B.S, jcur, d.n, A.idx + (long)pair * d.n, lane, B.cand);
+        __threadfence_block();   // the block list is read back below by other wavefronts
+        __syncthreads();
+    }
+    // the distinct valid blocks, ascending (the list is ascending unless supplied)
+    if (wave == 0) {
+        const int jb = lane < d.n ? ilist[lane] : -1;
+        bool ok = jb >= 0 && jb <= jcur;
+        for (int u2 = 0; u2 < 16; u2++) {
+            const int other = __shfl(jb, u2, 64);
+            if (u2 < lane && other == jb) ok = false;
+        }
+        const uint64_t v = __ballot(ok);
+        if (ok) sm.blist[__popcll(v & __lanemask_lt())] = jb;
+        if (lane == 0) sm.nblk = __popcll(v);
+    }
+    lds_barrier();
+
+    // ---- phase C: wavefront w attends to block blist[w] (two 32-key steps)
+    float m = -INFINITY, l = 0.f;
+    f32x4 oacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    unsigned char *reg = sm.u.wave[wave];
+    if (wave < sm.nblk) {
+        const int j = sm.blist[wave];
+        const uint16_t *K = (const uint16_t *)A.k + (long)pair * d.T * DK;
+        const uint16_t *V = (const uint16_t *)A.v + (long)pair * d.T * DV;
+        const uint16_t *qrow = (const uint16_t *)A.q + ((long)b * d.Hq + g * 16 + hd) * DK;
+        bf16x8 qf[KS];
+#pragma unroll
+        for (int kk = 0; kk < KS; kk++) qf[kk] = as_bf16x8(ld16(qrow + 32 * kk + 8 * q));
+        for (int st = 0; st < 2; st++) {
+            const int kbeg = 64 * j + kWaveKeys * st, kend = min(kbeg + kWaveKeys, t + 1);
+            if (kbeg >= kend) break;   // uniform over the wavefront
+            const int kA = min(kbeg + 8 * (hd >> 2) + (hd & 3), d.T - 1);
+            const int kB = min(kbeg + 8 * (hd >> 2) + (hd & 3) + 4, d.T - 1);
+            u32x4 ka[KS], kb2[KS], vr[VL];
+#pragma unroll
+            for (int kk = 0; kk < KS; kk++) {
+                ka[kk] = ld16(K + (long)kA * DK + 8 * q + 32 * kk);
+                kb2[kk] = ld16(K + (long)kB * DK + 8 * q + 32 * kk);
+            }
+#pragma unroll
+            for (int u = 0; u < VL; u++) {
+                const int c = 64 * u + lane, key = c / VC, ch = c % VC;
+                vr[u] = ld16(V + (long)min(kbeg + key, d.T - 1) * DV + ch * 8);
+            }
+            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KS; kk++) {
+                accA = mfma16(as_bf16x8(ka[kk]), qf[kk], accA);
+                accB = mfma16(as_bf16x8(kb2[kk]), qf[kk], accB);
+            }
+            float sv[8], mx = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                sv[u] = kbeg + 8 * q + u < kend ? accA[u] * sl2 : -INFINITY;
+                sv[4 + u] = kbeg + 8 * q + 4 + u < kend ? accB[u] * sl2 : -INFINITY;
+                mx = fmaxf(mx, fmaxf(sv[u], sv[4 + u]));
+            }
+            mx = head_max(mx);
+            const float mn = fmaxf(m, mx);   // finite: the step has a visible key
+            const float al = fast_exp2(m - mn);
+            float p[8], sum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                p[e] = fast_exp2(sv[e] - mn);
+                sum += p[e];
+            }
+            l = l * al + head_sum(sum);
+            m = mn;
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) oacc[dt] *= al;
+#pragma unroll
+            for (int u = 0; u < VL; u++) {
+                const int c = 64 * u + lane, key = c / VC, ch = c % VC;
+                st16(reg + WL::vaddr(key, ch >> 1, 16 * (ch & 1)), vr[u]);
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wavefront's stores are in LDS
+            __builtin_amdgcn_wave_barrier();
+            const bf16x8 pb = pack8(p);
+            const int gq = lane >> 4, sl = lane & 15, r0 = 8 * gq + (sl >> 2);
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) {
+                const uint2 lo = ld_tr16((const uint16_t *)(reg + WL::vaddr(r0, dt, 8 * (sl & 3))));
+                const uint2 hi = ld_tr16((const uint16_t *)(reg + WL::vaddr(r0 + 4, dt, 8 * (sl & 3))));
+                const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
+                oacc[dt] = mfma16(as_bf16x8(w), pb, oacc[dt]);
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // the region is rewritten by the next step
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+    // merge of the wavefronts: max, rescaled sums and outputs per head
+    float *ol = (float *)reg;   // [16][DV+4]
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+        for (int u = 0; u < 4; u++) ol[hd * (DV + 4) + 16 * dt + 4 * q + u] = oacc[dt][u];
+    if (q == 0) {
+        sm.wm[wave][hd] = m;
+        sm.wl[wave][hd] = l;
     }
     lds_barrier();
     if (tid < 16) {
         float M = -INFINITY;
-        for (int s = 0; s < A.cs; s++) M = fmaxf(M, lm[s][tid]);
+        for (int w = 0; w < kTailWaves; w++) M = fmaxf(M, sm.wm[w][tid]);
         float L = 0.f;
-        if (M != -INFINITY)
-            for (int s = 0; s < A.cs; s++) L += ll[s][tid] * fast_exp2(lm[s][tid] - M);
-        lse[tid] = M == -INFINITY ? -INFINITY : M + fast_log2(L);
+        for (int w = 0; w < kTailWaves; w++)
+            if (sm.wm[w][tid] != -INFINITY) L += sm.wl[w][tid] * fast_exp2(sm.wm[w][tid] - M);
+        sm.ms[tid] = M;
+        sm.lsum[tid] = L;
     }
     lds_barrier();
-    for (int e = tid; e < A.cs * 16; e += kThreads) {
-        const int s = e >> 4, h = e & 15;
-        wsp[s][h] = lse[h] == -INFINITY ? 0.f : fast_exp2(lm[s][h] - lse[h]);
-    }
-    lds_barrier();
-    // block j: its own keys 4j..4j+3 (X) plus key 4j-1 (Y of block j-1);
-    // phase A wrote blocks 0..nbp-1, a block past them has no key of its own
-    const float *bx = A.bx + (long)pair * 16 * A.nbp, *by = A.by + (long)pair * 16 * A.nbp;
-    constexpr int kBlkPerSplit = kSplitKeys / 4;
-    for (int j = tid; j <= jcur; j += kThreads) {
-        const int sj = j / kBlkPerSplit, sp = (j - 1) / kBlkPerSplit;
-        const bool hx = j < A.nbp, hy = j > 0 && j - 1 < A.nbp;
-        float xv[16], yv[16];
-#pragma unroll
-        for (int h = 0; h < 16; h++) {
-            xv[h] = hx ? bx[(long)h * A.nbp + j] : 0.f;
-            yv[h] = hy ? by[(long)h * A.nbp + j - 1] : 0.f;
-        }
+    for (int e = tid; e < 16 * DV; e += NT) {
+        const int h = e / DV, c = e % DV;
+        const float M = sm.ms[h];
         float acc = 0.f;
-#pragma unroll
-        for (int h = 0; h < 16; h++) {
-            acc += xv[h] * wsp[sj][h];
-            if (hy) acc += yv[h] * wsp[sp][h];
+        for (int w = 0; w < kTailWaves; w++) {
+            const float mw = sm.wm[w][h];
+            if (mw != -INFINITY) acc += ((const float *)sm.u.wave[w])[h * (DV + 4) + c] * fast_exp2(mw - M);
         }
-        S[j] = acc;
+        sm.os[h][c] = acc;
     }
     lds_barrier();
-    if (A.idx_in || wave != 0) return;
-    wave_select_topn_fast(S, jcur, d.n, A.idx + (long)pair * d.n, lane, cand);
-}
 
-// ---------------------------------------------------------------------------
-// Phase D.  Four workgroups per (sequence, KV head), four heads each: merge
-// the compressed, window and selected partials, the gates, and
-// o = g_cmp o_cmp + g_slc o_slc + g_win o_win.
-constexpr int kDHeads = 4;
-
-template <int DK, int DV>
-__global__ __launch_bounds__(kThreads) void k_dec_phase_d(DecArgs A)
-{
-    __shared__ float wts[3][64][kDHeads];   // [branch][split][head] merge weights
-    __shared__ float gate[kDHeads][3];
-    const Dims &d = A.d;
-    const int pair = blockIdx.x / (16 / kDHeads), h0 = (blockIdx.x % (16 / kDHeads)) * kDHeads;
-    const int b = pair / d.Hkv, g = pair % d.Hkv;
-    const int tid = threadIdx.x;
-    const int nsplit = A.cs + A.ws;
-    const float *pmA = A.pm + (long)pair * nsplit * 16, *plA = A.pl + (long)pair * nsplit * 16;
-    const float *pmC = A.sm + (long)pair * A.ss * 16, *plC = A.sl + (long)pair * A.ss * 16;
-    // (max, sum) of every split of the three branches into LDS, loads in parallel:
-    // branch 0 compressed (phase-A splits 0..cs-1), 1 window (cs..), 2 selected
-    __shared__ float lm[3][64][kDHeads], ll[3][64][kDHeads];
-    for (int e = tid; e < 3 * 64 * kDHeads; e += kThreads) {
-        const int br = e / (64 * kDHeads), s = (e / kDHeads) % 64, hl = e % kDHeads;
-        const int ns = br == 0 ? A.cs : (br == 1 ? A.ws : A.ss);
-        if (s < ns) {
-            const long src = (long)(br == 1 ? A.cs + s : s) * 16 + h0 + hl;
-            lm[br][s][hl] = br == 2 ? pmC[src] : pmA[src];
-            ll[br][s][hl] = br == 2 ? plC[src] : plA[src];
+    // ---- phase D: merge the compressed and window partials, gates, output
+    auto &D = sm.u.d;
+    for (int e = tid; e < 2 * 64 * 16; e += NT) {
+        const int br = e / (64 * 16), s2 = (e / 16) % 64, h = e % 16;
+        const int ns = br == 0 ? A.cs : A.ws;
+        if (s2 < ns) {
+            const long src = (long)(br == 1 ? A.cs + s2 : s2) * 16 + h;
+            D.lm[br][s2][h] = pm[src];
+            D.ll[br][s2][h] = pl[src];
         }
     }
     lds_barrier();
-    if (tid < 3 * kDHeads) {
-        const int br = tid / kDHeads, hl = tid % kDHeads;
-        const int ns = br == 0 ? A.cs : (br == 1 ? A.ws : A.ss);
+    if (tid < 2 * 16) {
+        const int br = tid / 16, h = tid % 16;
+        const int ns = br == 0 ? A.cs : A.ws;
         float M = -INFINITY;
-        for (int s = 0; s < ns; s++) M = fmaxf(M, lm[br][s][hl]);
+        for (int s2 = 0; s2 < ns; s2++) M = fmaxf(M, D.lm[br][s2][h]);
         float L = 0.f;
         if (M != -INFINITY)
-            for (int s = 0; s < ns; s++) L += ll[br][s][hl] * fast_exp2(lm[br][s][hl] - M);
-        for (int s = 0; s < ns; s++)
-            wts[br][s][hl] = (M == -INFINITY || L <= 0.f) ? 0.f : fast_exp2(lm[br][s][hl] - M) / L;
+            for (int s2 = 0; s2 < ns; s2++) L += D.ll[br][s2][h] * fast_exp2(D.lm[br][s2][h] - M);
+        for (int s2 = 0; s2 < ns; s2++)
+            D.wts[br][s2][h] = (M == -INFINITY || L <= 0.f) ? 0.f : fast_exp2(D.lm[br][s2][h] - M) / L;
     }
     // gates: 16 threads per (head, gate) dot product of length DK
-    if (tid < 16 * 3 * kDHeads) {
-        const int dot = tid >> 4, part = tid & 15;
-        const int h = h0 + dot / 3, c = dot % 3;
+    for (int task = tid; task < 16 * 3 * 16; task += NT) {
+        const int dot = task >> 4, part = task & 15;
+        const int h = dot / 3, c = dot % 3;
         const uint16_t *qr = (const uint16_t *)A.q + ((long)b * d.Hq + g * 16 + h) * DK;
         const uint16_t *wr = (const uint16_t *)A.wg + ((long)(g * 16 + h) * 3 + c) * DK;
         float z = 0.f;
@@ -414,25 +550,24 @@ __global__ __launch_bounds__(kThreads) void k_dec_phase_d(DecArgs A)
         for (int off = 8; off > 0; off >>= 1) z += __shfl_xor(z, off, 16);
         if (part == 0) {
             z += __uint_as_float((uint32_t)((const uint16_t *)A.bg)[(g * 16 + h) * 3 + c] << 16);
-            gate[dot / 3][c] = sigmoidf_(z);
+            D.gate[h][c] = sigmoidf_(z);
         }
     }
     lds_barrier();
-    const float *poA = A.po + (long)pair * nsplit * 16 * DV, *poC = A.so + (long)pair * A.ss * 16 * DV;
+    const float *po = A.po + (long)pair * nsplit * 16 * DV;
     uint16_t *o = (uint16_t *)A.o + ((long)b * d.Hq + g * 16) * DV;
-    for (int e = tid; e < kDHeads * DV; e += kThreads) {
-        const int hl = e / DV, h = h0 + hl, c = e % DV;
-        const long off = (long)h * DV + c;
-        float oc = 0.f, ow = 0.f, os = 0.f;
+    for (int e = tid; e < 16 * DV; e += NT) {
+        const int h = e / DV, c = e % DV;
+        float oc = 0.f, ow = 0.f;
 #pragma unroll 4
-        for (int s = 0; s < A.cs; s++) oc += poA[(long)s * 16 * DV + off] * wts[0][s][hl];
+        for (int s2 = 0; s2 < A.cs; s2++) oc += po[(long)s2 * 16 * DV + e] * D.wts[0][s2][h];
 #pragma unroll 2
-        for (int s = 0; s < A.ws; s++) ow += poA[(long)(A.cs + s) * 16 * DV + off] * wts[1][s][hl];
-#pragma unroll 4
-        for (int s = 0; s < A.ss; s++) os += poC[(long)s * 16 * DV + off] * wts[2][s][hl];
-        const float y = gate[hl][0] * oc + gate[hl][1] * os + gate[hl][2] * ow;
+        for (int s2 = 0; s2 < A.ws; s2++) ow += po[(long)(A.cs + s2) * 16 * DV + e] * D.wts[1][s2][h];
+        const float L = sm.lsum[h];
+        const float os = L > 0.f ? sm.os[h][c] / L : 0.f;
+        const float y = D.gate[h][0] * oc + D.gate[h][1] * os + D.gate[h][2] * ow;
         __bf16 yb = (__bf16)y;
-        o[off] = __builtin_bit_cast(uint16_t, yb);
+        o[e] = __builtin_bit_cast(uint16_t, yb);
     }
 }
 
@@ -443,9 +578,7 @@ hipError_t launch_decode_dims(const DecArgs &A, hipStream_t s)
     const int pairs = d.B * d.Hkv;
     const int na = pairs * (A.cs + A.ws), nc = pairs * A.ss;
     hipLaunchKernelGGL((k_dec_stream<DK, DV, kPhaseA>), dim3(na), dim3(kSThreads), 0, s, A);
-    hipLaunchKernelGGL((k_dec_phase_b<DV>), dim3(pairs), dim3(kThreads), sizeof(float) * d.nb, s, A);
-    hipLaunchKernelGGL((k_dec_stream<DK, DV, kPhaseC>), dim3(nc), dim3(kSThreads), 0, s, A);
-    hipLaunchKernelGGL((k_dec_phase_d<DK, DV>), dim3(pairs * (16 / kDHeads)), dim3(kThreads), 0, s, A);
+    hipLaunchKernelGGL((k_dec_tail<DK, DV>), dim3(pairs), dim3(kTailThreads), 0, s, A);
     return hipGetLastError();
 }
 
