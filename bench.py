@@ -128,7 +128,9 @@ def main():
     wsd = nsa.workspace(sd, nsa.OP_DECODE, dev)
     torch.cuda.synchronize()
 
-    stages = ["S1_compress", "S2_compressed_attention", "S3_select", "S4_sparse_window_gate", "decode_step"]
+    stages = ["S1_compress", "S2_compressed_attention", "S3_select", "S4a_pack_kv_blocks", "S4b_window_gate",
+              "S4c_selected_gate", "decode_step"]
+    nst = len(stages)
 
     def step(i, ev=None):
         def mark(j):
@@ -141,19 +143,25 @@ def main():
         mark(2)
         nsa.select_topn(sp, scores, idx)
         mark(3)
-        nsa.sparse_attention(sp, x["q"], x["k"], x["v"], ocmp, idx, x["w_g"], x["b_g"], o, wss)
+        # S4 in its three parts (the same kernels nsa_sparse_attention runs), so
+        # that each kernel is timed on its own
+        nsa.pack_kv_blocks(sp, x["k"], x["v"], wss)
         mark(4)
+        nsa.window_attention(sp, x["q"], x["k"], x["v"], ocmp, x["w_g"], x["b_g"], o)
+        mark(5)
+        nsa.selected_attention(sp, x["q"], x["k"], x["v"], idx, x["w_g"], x["b_g"], o, wss)
+        mark(6)
         y = dec[i % 2]
         nsa.decode_step(sd, y["seq_lens"], y["q"], y["k"], y["v"], y["ck"], y["cv"], y["w_g"], y["b_g"], None,
                         od, None, wsd)
-        mark(5)
+        mark(7)
 
     log("warmup", args.warmup)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
     log("timed steps", args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -161,38 +169,43 @@ def main():
         step(i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(5)] for e in evs])  # ms
+    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(nst)] for e in evs])  # ms
     st_ms = per.mean(axis=0)
-    step_ms = float(np.array([e[0].elapsed_time(e[5]) for e in evs]).mean())
+    step_ms = float(np.array([e[0].elapsed_time(e[nst]) for e in evs]).mean())
 
     fl = prefill_flops(sp)
-    prefill_ms = float(st_ms[:4].sum())
+    prefill_ms = float(st_ms[:nst - 1].sum())
     tflops = fl["total"] / (prefill_ms * 1e-3) / 1e12
     dec_bytes = decode_bytes(sd)
-    dec_us = float(st_ms[4] * 1e3)
+    dec_us = float(st_ms[nst - 1] * 1e3)
     dec_gbps = dec_bytes / (dec_us * 1e-6) / 1e9
 
-    # roofline of the dominant stage (each stage is one kernel launch, S1 two)
+    # roofline of the dominant kernel: every stage below is one kernel launch
+    # on the stream the events are recorded on (S1 launches its kernel twice,
+    # once for K and once for V; the decode step runs two kernels)
+    kv_bytes = 2 * sp.B * sp.Hkv * sp.T * (sp.dk + sp.dv)
     work = {
-        "S1_compress": ("alu", fl["compress"], PEAK_FP32_VALU_TFLOPS, "TFLOP/s"),
-        "S2_compressed_attention": ("mfma", fl["compressed"], PEAK_BF16_TFLOPS, "TFLOP/s"),
-        "S3_select": ("hbm", 4 * sp.B * sp.Hkv * sum(t // 64 + 1 for t in range(0, sp.T, 1)) +
+        "S2_compressed_attention": ("k_cmp_attn_mfma", "mfma", fl["compressed"], PEAK_BF16_TFLOPS, "TFLOP/s"),
+        "S3_select": ("k_select_generic", "hbm", 4 * sp.B * sp.Hkv * sum(t // 64 + 1 for t in range(0, sp.T, 1)) +
                       4 * sp.B * sp.Hkv * sp.T * sp.n, PEAK_HBM_GBPS, "GB/s"),
-        "S4_sparse_window_gate": ("mfma", fl["selected"] + fl["window"] + fl["gates"], PEAK_BF16_TFLOPS,
-                                  "TFLOP/s"),
-        "decode_step": ("hbm", dec_bytes, PEAK_HBM_GBPS, "GB/s"),
+        "S4a_pack_kv_blocks": ("k_pack_blocks", "hbm", 2 * kv_bytes, PEAK_HBM_GBPS, "GB/s"),
+        "S4b_window_gate": ("k_window_mfma", "mfma", fl["window"] + fl["gates"] * 2 // 3, PEAK_BF16_TFLOPS,
+                            "TFLOP/s"),
+        "S4c_selected_gate": ("k_selected_mfma", "mfma", fl["selected"] + fl["gates"] // 3, PEAK_BF16_TFLOPS,
+                              "TFLOP/s"),
     }
-    # the roofline line is for the dominant single-kernel stage: S2 and S3 are
-    # one launch each (S1 launches its kernel twice, S4 runs three kernels,
-    # the decode step four; their times are in stage_ms)
-    single = {"S2_compressed_attention": "k_cmp_attn_mfma", "S3_select": "k_select_generic"}
-    dom = max(single, key=lambda k: st_ms[stages.index(k)])
-    bound, units, peak, unit = work[dom]
+    dom = max(work, key=lambda k: st_ms[stages.index(k)])
+    kname, bound, units, peak, unit = work[dom]
     dur_s = st_ms[stages.index(dom)] * 1e-3
     achieved = units / dur_s / (1e12 if unit == "TFLOP/s" else 1e9)
-    roof = {"bound": bound, "kernel": single[dom], "stage": dom, "achieved": round(achieved, 2), "peak": peak,
+    roof = {"bound": bound, "kernel": kname, "stage": dom, "achieved": round(achieved, 2), "peak": peak,
             "unit": unit, "frac": round(achieved / peak, 4), "traffic": args.traffic,
             "avg_launch_ms": round(float(dur_s * 1e3), 4), "algorithmic_per_launch": units}
+    kernels = {}
+    for k, (kn, bd, u, pk, un) in work.items():
+        ach = u / (st_ms[stages.index(k)] * 1e-3) / (1e12 if un == "TFLOP/s" else 1e9)
+        kernels[kn] = {"ms": round(float(st_ms[stages.index(k)]), 4), "bound": bd, "achieved": round(ach, 2),
+                       "unit": un, "frac": round(ach / pk, 4)}
 
     res = {
         "metric": "NSA fwd TFLOP/s @64k prefill",
@@ -224,6 +237,7 @@ def main():
         "decode_gflop": round(decode_flops(sd) / 1e9, 3),
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
+        "kernels": kernels,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

@@ -145,6 +145,29 @@ nsa_status nsa_sparse_attention(const nsa_config *cfg, const void *q, const void
                                 const void *o_cmp, const int32_t *idx, const void *w_g, const void *b_g, void *o,
                                 void *ws, size_t ws_bytes, void *stream);
 
+/* Stage S4 in parts, for callers that schedule them separately (for
+ * example to overlap the window half with other work or to time each
+ * kernel).  nsa_sparse_attention equals nsa_pack_kv_blocks, then
+ * nsa_window_attention, then nsa_selected_attention on the same o, bit for
+ * bit.
+ *   nsa_pack_kv_blocks:     writes K and V, repacked per 64-token block,
+ *                           into ws (nsa_workspace_bytes(cfg,
+ *                           NSA_OP_SPARSE) bytes; nothing is written when
+ *                           that size is 0 and ws may then be NULL);
+ *   nsa_window_attention:   o = g_cmp * o_cmp + g_win * o_win (o written);
+ *   nsa_selected_attention: o += g_slc * o_slc (o read and written).  ws
+ *                           must hold what nsa_pack_kv_blocks wrote for the
+ *                           same k and v (it is read, not rewritten); k and
+ *                           v are read directly when the workspace size is 0.
+ * Definitions and layouts as for nsa_sparse_attention. */
+nsa_status nsa_pack_kv_blocks(const nsa_config *cfg, const void *k, const void *v, void *ws, size_t ws_bytes,
+                              void *stream);
+nsa_status nsa_window_attention(const nsa_config *cfg, const void *q, const void *k, const void *v,
+                                const void *o_cmp, const void *w_g, const void *b_g, void *o, void *stream);
+nsa_status nsa_selected_attention(const nsa_config *cfg, const void *q, const void *k, const void *v,
+                                  const int32_t *idx, const void *w_g, const void *b_g, void *o, void *ws,
+                                  size_t ws_bytes, void *stream);
+
 /* S2 (scores only) followed by S3.  scores_out may be NULL (the workspace
  * holds them then); idx_out is required. */
 nsa_status nsa_select_blocks(const nsa_config *cfg, const void *q, const void *cmp_k, float *scores_out,

@@ -14,11 +14,11 @@
 //   phase C  the selected blocks (one wavefront per block, online softmax);
 //   phase D  merge of the compressed, window and selected partials and the
 //            gated sum.
-// Phase A is one kernel; B, C and D run in a second one, one workgroup of 16
-// wavefronts per (sequence, KV head), so the step costs two launches.
-// Phases A and C run one workgroup of 8 wavefronts per (pair, split) of 256
-// keys; each wavefront issues every load of its 32 keys on entry, so a CU
-// keeps several hundred KB in flight.
+// Phase A is one kernel, one workgroup of 8 wavefronts per (pair, split) of
+// 256 keys; each wavefront issues every load of its 32 keys on entry, so a CU
+// keeps several hundred KB in flight.  B, C and D run in a second kernel, one
+// workgroup of 16 wavefronts per (sequence, KV head), so the step costs two
+// launches.
 //
 // Lane view (one position, 16 heads, wave64): head hd = lane%16, key group
 // q = lane/16.  A 32-key step is two 16x16x32 S^T tiles whose rows hold keys
@@ -35,11 +35,9 @@ namespace nsa {
 
 namespace {
 
-constexpr int kThreads = 256;               // phases B and D
-constexpr int kSThreads = 512;              // phases A and C: 8 wavefronts
+constexpr int kSThreads = 512;              // phase A: 8 wavefronts
 constexpr int kWaveKeys = 32;               // keys per wavefront (one 32-key step)
 constexpr int kSplitKeys = 8 * kWaveKeys;   // keys per phase-A workgroup
-constexpr int kSelPerWg = 4;                // selected blocks per phase-C workgroup (two waves each)
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.f / (1.f + __expf(-z)); }
 
@@ -95,15 +93,12 @@ struct DecLds {
     float ls[8][16];
 };
 
-constexpr int kPhaseA = 0, kPhaseC = 1;
-
-// Phases A and C.  Workgroup = (pair, slot): phase-A slots 0..cs-1 are the
-// compressed slots [256 s, 256 s + 256), slots cs.. the window keys from
-// max(0, t-w+1) in steps of 256; phase-C slot s holds the selected blocks
-// 4s .. 4s+3 of the pair's deduplicated list (two wavefronts per block).
-// Wavefront w takes keys kbeg .. kbeg+31; all 8 use the workgroup's maximum
-// per head, so the partial (max, sum, unnormalised output) is one sum.
-template <int DK, int DV, int KIND>
+// Phase A.  Workgroup = (pair, slot): slots 0..cs-1 are the compressed slots
+// [256 s, 256 s + 256), slots cs.. the window keys from max(0, t-w+1) in
+// steps of 256.  Wavefront w takes keys kbeg .. kbeg+31; all 8 use the
+// workgroup's maximum per head, so the partial (max, sum, unnormalised
+// output) is one sum.
+template <int DK, int DV>
 __global__ __launch_bounds__(kSThreads) void k_dec_stream(DecArgs A)
 {
     constexpr int KS = DK / 32;      // 16x16x32 steps over the head dim
@@ -116,47 +111,26 @@ __global__ __launch_bounds__(kSThreads) void k_dec_stream(DecArgs A)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hd = lane & 15, q = lane >> 4;
     const float sl2 = d.scale * kLog2e;
-    const int nslots = KIND == kPhaseA ? A.cs + A.ws : A.ss;
+    const int nslots = A.cs + A.ws;
     const int pair = blockIdx.x / nslots, slot = blockIdx.x % nslots;
     const int b = pair / d.Hkv;
     const int t = dec_t(A.seq_lens, b, d.T);
 
     // this wavefront's keys
     int kbeg, kend, kclamp;
-    bool cmp = false;
+    const bool cmp = slot < A.cs;
     const uint16_t *K, *V;
-    if (KIND == kPhaseA) {
-        cmp = slot < A.cs;
-        if (cmp) {
-            const int nvis = t >= 31 ? (t - 31) / 16 + 1 : 0;
-            kbeg = slot * kSplitKeys + wave * kWaveKeys;
-            kend = min(kbeg + kWaveKeys, nvis);
-            kclamp = d.npad - 1;
-            K = (const uint16_t *)A.kc + (long)pair * d.npad * DK;
-            V = (const uint16_t *)A.vc + (long)pair * d.npad * DV;
-        } else {
-            const int lo = max(0, t - d.w + 1);
-            kbeg = lo + (slot - A.cs) * kSplitKeys + wave * kWaveKeys;
-            kend = min(kbeg + kWaveKeys, t + 1);
-            kclamp = d.T - 1;
-            K = (const uint16_t *)A.k + (long)pair * d.T * DK;
-            V = (const uint16_t *)A.v + (long)pair * d.T * DV;
-        }
+    if (cmp) {
+        const int nvis = t >= 31 ? (t - 31) / 16 + 1 : 0;
+        kbeg = slot * kSplitKeys + wave * kWaveKeys;
+        kend = min(kbeg + kWaveKeys, nvis);
+        kclamp = d.npad - 1;
+        K = (const uint16_t *)A.kc + (long)pair * d.npad * DK;
+        V = (const uint16_t *)A.vc + (long)pair * d.npad * DV;
     } else {
-        // the (2 slot + wave/2)-th distinct valid block of the pair's list
-        const int jcur = t / 64;
-        const int32_t *isrc = (A.idx_in ? A.idx_in : A.idx) + (long)pair * d.n;
-        const int jb = lane < d.n ? isrc[lane] : -1;
-        bool ok = jb >= 0 && jb <= jcur;
-        for (int u = 0; u < 16; u++) {
-            const int other = __shfl(jb, u, 64);
-            if (u < lane && other == jb) ok = false;
-        }
-        uint64_t v = __ballot(ok);
-        for (int c = 0; c < kSelPerWg * slot + (wave >> 1) && v; c++) v &= v - 1;
-        const int j = v ? __shfl(jb, __builtin_ctzll(v), 64) : -1;
-        kbeg = j < 0 ? 0 : 64 * j + kWaveKeys * (wave & 1);
-        kend = j < 0 ? 0 : min(kbeg + kWaveKeys, t + 1);
+        const int lo = max(0, t - d.w + 1);
+        kbeg = lo + (slot - A.cs) * kSplitKeys + wave * kWaveKeys;
+        kend = min(kbeg + kWaveKeys, t + 1);
         kclamp = d.T - 1;
         K = (const uint16_t *)A.k + (long)pair * d.T * DK;
         V = (const uint16_t *)A.v + (long)pair * d.T * DV;
@@ -221,7 +195,7 @@ __global__ __launch_bounds__(kSThreads) void k_dec_stream(DecArgs A)
         p[e] = M == -INFINITY ? 0.f : fast_exp2(s[e] - M);
         l += p[e];
     }
-    if (KIND == kPhaseA && cmp) {
+    if (cmp) {
         // block a = (kbeg + 8q)/4 gets keys 4a..4a+3 here (weights 2,2,2,1);
         // its remaining weight-1 key 4a-1 is the previous block's Y term
         float *bx = A.bx + (long)pair * 16 * A.nbp + (long)hd * A.nbp;
@@ -272,9 +246,9 @@ __global__ __launch_bounds__(kSThreads) void k_dec_stream(DecArgs A)
     if (q == 0) sm.ls[wave][hd] = l;
     lds_barrier();
     const long pidx = (long)pair * nslots + slot;
-    float *pm = (KIND == kPhaseA ? A.pm : A.sm) + pidx * 16;
-    float *pl = (KIND == kPhaseA ? A.pl : A.sl) + pidx * 16;
-    float *po = (KIND == kPhaseA ? A.po : A.so) + pidx * 16 * DV;
+    float *pm = A.pm + pidx * 16;
+    float *pl = A.pl + pidx * 16;
+    float *po = A.po + pidx * 16 * DV;
     for (int e = tid; e < 16 * DV; e += kSThreads) {
         const int h = e / DV, c = e % DV;
         float acc = 0.f;
@@ -576,8 +550,8 @@ hipError_t launch_decode_dims(const DecArgs &A, hipStream_t s)
 {
     const Dims &d = A.d;
     const int pairs = d.B * d.Hkv;
-    const int na = pairs * (A.cs + A.ws), nc = pairs * A.ss;
-    hipLaunchKernelGGL((k_dec_stream<DK, DV, kPhaseA>), dim3(na), dim3(kSThreads), 0, s, A);
+    const int na = pairs * (A.cs + A.ws);
+    hipLaunchKernelGGL((k_dec_stream<DK, DV>), dim3(na), dim3(kSThreads), 0, s, A);
     hipLaunchKernelGGL((k_dec_tail<DK, DV>), dim3(pairs), dim3(kTailThreads), 0, s, A);
     return hipGetLastError();
 }
@@ -590,8 +564,7 @@ bool decode_mfma_supported(const Dims &d)
     if (!((d.dk == 192 && d.dv == 128) || (d.dk == 128 && d.dv == 128) || (d.dk == 64 && d.dv == 64))) return false;
     const int cs = (d.npad + kSplitKeys - 1) / kSplitKeys, ws = (d.w + kSplitKeys - 1) / kSplitKeys;
     const long pairs = (long)d.B * d.Hkv;
-    const int ss = (d.n + kSelPerWg - 1) / kSelPerWg;
-    return cs + ws <= 64 && d.npad / 4 <= 16384 && pairs * (cs + ws) <= 0x7fffffffL && pairs * ss <= 0x7fffffffL;
+    return cs + ws <= 64 && d.npad / 4 <= 16384 && pairs * (cs + ws) <= 0x7fffffffL;
 }
 
 // Workspace of the matrix-core decode step, carved from `ws` when non-null.
@@ -599,7 +572,6 @@ size_t decode_mfma_layout(const Dims &d, void *ws, DecArgs *A)
 {
     const long pairs = (long)d.B * d.Hkv;
     const int cs = (d.npad + kSplitKeys - 1) / kSplitKeys, wsplit = (d.w + kSplitKeys - 1) / kSplitKeys;
-    const int ss = (d.n + kSelPerWg - 1) / kSelPerWg;
     const int nbp = d.npad / 4;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -610,23 +582,17 @@ size_t decode_mfma_layout(const Dims &d, void *ws, DecArgs *A)
     const size_t o_pm = take(4 * pairs * (cs + wsplit) * 16), o_pl = take(4 * pairs * (cs + wsplit) * 16);
     const size_t o_po = take(4 * pairs * (cs + wsplit) * 16 * d.dv);
     const size_t o_bx = take(4 * pairs * 16 * nbp), o_by = take(4 * pairs * 16 * nbp);
-    const size_t o_sm = take(4 * pairs * ss * 16), o_sl = take(4 * pairs * ss * 16), o_so = take(4 * pairs * ss * 16 * d.dv);
-    const size_t o_oc = take(4 * pairs * 16 * d.dv), o_idx = take(4 * pairs * d.n);
+    const size_t o_idx = take(4 * pairs * d.n);
     if (A && ws) {
         char *w = (char *)ws;
         A->cs = cs;
         A->ws = wsplit;
-        A->ss = ss;
         A->nbp = nbp;
         A->pm = (float *)(w + o_pm);
         A->pl = (float *)(w + o_pl);
         A->po = (float *)(w + o_po);
         A->bx = (float *)(w + o_bx);
         A->by = (float *)(w + o_by);
-        A->sm = (float *)(w + o_sm);
-        A->sl = (float *)(w + o_sl);
-        A->so = (float *)(w + o_so);
-        A->ocmp = (float *)(w + o_oc);
         A->idx = (int32_t *)(w + o_idx);
     }
     return off;

@@ -495,15 +495,21 @@ hipError_t launch_sparse_dims(const RowArgs &a, void *vt_ws, hipStream_t s)
     const int BG = d.B * d.Hkv;
     uint16_t *kpk = (uint16_t *)vt_ws;
     uint16_t *vpk = kpk + (size_t)BG * d.nb * kTile * DK;
-    hipLaunchKernelGGL((k_pack_blocks<DK, DV>), dim3(d.nb, BG), dim3(kThreads), 0, s, (const uint16_t *)a.k,
-                       (const uint16_t *)a.v, kpk, vpk, d.T, d.nb);
-    const int ntp = (a.R + kWPos - 1) / kWPos;
-    long nwg = (long)BG * ntp;
-    nwg = (nwg + 7) / 8 * 8;
-    hipLaunchKernelGGL((k_window_mfma<DK, DV>), dim3((unsigned)nwg), dim3(kWThreads), 0, s, a, ntp);
-    const int ntp4 = (a.R + 3) / 4;
-    long nwg4 = ((long)BG * ntp4 + 7) / 8 * 8;
-    hipLaunchKernelGGL((k_selected_mfma<DK, DV>), dim3((unsigned)nwg4), dim3(kThreads), 0, s, a, kpk, vpk, ntp4);
+    if (a.part == 0 || a.part == 1) {
+        const int ntp = (a.R + kWPos - 1) / kWPos;
+        long nwg = (long)BG * ntp;
+        nwg = (nwg + 7) / 8 * 8;
+        hipLaunchKernelGGL((k_window_mfma<DK, DV>), dim3((unsigned)nwg), dim3(kWThreads), 0, s, a, ntp);
+    }
+    if (a.part == 0 || a.part == 3)
+        hipLaunchKernelGGL((k_pack_blocks<DK, DV>), dim3(d.nb, BG), dim3(kThreads), 0, s, (const uint16_t *)a.k,
+                           (const uint16_t *)a.v, kpk, vpk, d.T, d.nb);
+    if (a.part == 0 || a.part == 2) {
+        const int ntp4 = (a.R + 3) / 4;
+        long nwg4 = ((long)BG * ntp4 + 7) / 8 * 8;
+        hipLaunchKernelGGL((k_selected_mfma<DK, DV>), dim3((unsigned)nwg4), dim3(kThreads), 0, s, a, kpk, vpk,
+                           ntp4);
+    }
     return hipGetLastError();
 }
 

@@ -262,9 +262,10 @@ __global__ __launch_bounds__(kThreads) void k_sparse_generic(RowArgs a)
     const T *qrow = (const T *)a.q + b * a.q_sb + r * a.q_sr + (long)g * G * dk;
     for (int e = tid; e < G * dk; e += kThreads) qs[e] = to_f(qrow[e]);
     if (tid == 0) {
-        const int32_t *ir = a.idx + (((long)b * d.Hkv + g) * a.R + r) * d.n;
+        // the window-only part has no index list (a.idx is null there)
+        const int32_t *ir = a.part == 1 ? nullptr : a.idx + (((long)b * d.Hkv + g) * a.R + r) * d.n;
         int m = 0;
-        for (int q2 = 0; q2 < d.n; q2++) {
+        for (int q2 = 0; ir && q2 < d.n; q2++) {
             int j = ir[q2];
             if (j < 0 || j > jcur) continue;
             int pos = m;                       // insertion sort, skipping repeats
@@ -298,6 +299,12 @@ __global__ __launch_bounds__(kThreads) void k_sparse_generic(RowArgs a)
     const int lo = t - d.w + 1 > 0 ? t - d.w + 1 : 0;
 
     for (int br = 0; br < 2; br++) {
+        // part 1 computes only the window (br 1), part 2 only the selected branch (br 0)
+        if ((a.part == 1 && br == 0) || (a.part == 2 && br == 1)) {
+#pragma unroll
+            for (int u = 0; u < 16; u++) res[br][u] = 0.f;
+            continue;
+        }
         float acc[16];
 #pragma unroll
         for (int u = 0; u < 16; u++) acc[u] = 0.f;
@@ -366,7 +373,9 @@ __global__ __launch_bounds__(kThreads) void k_sparse_generic(RowArgs a)
         int e = tid + u * kThreads;
         if (e < G * dv) {
             int h = e / dv;
-            float y = gate_s[h * 3] * to_f(oc[e]) + gate_s[h * 3 + 1] * res[0][u] + gate_s[h * 3 + 2] * res[1][u];
+            float y;
+            if (a.part == 2) y = to_f(orow[e]) + gate_s[h * 3 + 1] * res[0][u];
+            else y = gate_s[h * 3] * to_f(oc[e]) + gate_s[h * 3 + 1] * res[0][u] + gate_s[h * 3 + 2] * res[1][u];
             orow[e] = from_f<T>(y);
         }
     }

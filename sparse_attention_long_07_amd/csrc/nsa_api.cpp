@@ -219,6 +219,70 @@ nsa_status nsa_sparse_attention(const nsa_config *cfg, const void *q, const void
     return hip_status(launch_sparse_generic(a, (hipStream_t)stream));
 }
 
+nsa_status nsa_pack_kv_blocks(const nsa_config *cfg, const void *k, const void *v, void *ws, size_t ws_bytes,
+                              void *stream)
+{
+    Dims d;
+    nsa_status st = check_config(cfg, &d);
+    if (st != NSA_OK) return st;
+    if (!k || !v) return NSA_ERR_NULL;
+    if (!all_aligned({k, v})) return NSA_ERR_ALIGN;
+    if (!sparse_mfma_supported(d)) return NSA_OK;     // the generic path reads K and V as they are
+    if (!ws || ws_bytes < sparse_mfma_ws_bytes(d)) return NSA_ERR_WORKSPACE;
+    if ((uintptr_t)ws % kAlign) return NSA_ERR_ALIGN;
+    RowArgs a = prefill_args(d, nullptr);
+    a.k = k;
+    a.v = v;
+    a.part = 3;
+    return hip_status(launch_sparse_mfma(a, ws, (hipStream_t)stream));
+}
+
+nsa_status nsa_window_attention(const nsa_config *cfg, const void *q, const void *k, const void *v,
+                                const void *o_cmp, const void *w_g, const void *b_g, void *o, void *stream)
+{
+    Dims d;
+    nsa_status st = check_config(cfg, &d);
+    if (st != NSA_OK) return st;
+    if (!q || !k || !v || !o_cmp || !w_g || !b_g || !o) return NSA_ERR_NULL;
+    if (!all_aligned({q, k, v, o_cmp, w_g, b_g, o})) return NSA_ERR_ALIGN;
+    RowArgs a = prefill_args(d, q);
+    a.k = k;
+    a.v = v;
+    a.ocmp = (void *)o_cmp;
+    a.wg = w_g;
+    a.bg = b_g;
+    a.o = o;
+    a.part = 1;
+    if (sparse_mfma_supported(d)) return hip_status(launch_sparse_mfma(a, nullptr, (hipStream_t)stream));
+    return hip_status(launch_sparse_generic(a, (hipStream_t)stream));
+}
+
+nsa_status nsa_selected_attention(const nsa_config *cfg, const void *q, const void *k, const void *v,
+                                  const int32_t *idx, const void *w_g, const void *b_g, void *o, void *ws,
+                                  size_t ws_bytes, void *stream)
+{
+    Dims d;
+    nsa_status st = check_config(cfg, &d);
+    if (st != NSA_OK) return st;
+    if (!q || !k || !v || !idx || !w_g || !b_g || !o) return NSA_ERR_NULL;
+    if (!all_aligned({q, k, v, idx, w_g, b_g, o})) return NSA_ERR_ALIGN;
+    const bool mfma = sparse_mfma_supported(d);
+    if (mfma) {
+        if (!ws || ws_bytes < sparse_mfma_ws_bytes(d)) return NSA_ERR_WORKSPACE;
+        if ((uintptr_t)ws % kAlign) return NSA_ERR_ALIGN;
+    }
+    RowArgs a = prefill_args(d, q);
+    a.k = k;
+    a.v = v;
+    a.idx = idx;
+    a.wg = w_g;
+    a.bg = b_g;
+    a.o = o;
+    a.part = 2;
+    if (mfma) return hip_status(launch_sparse_mfma(a, ws, (hipStream_t)stream));
+    return hip_status(launch_sparse_generic(a, (hipStream_t)stream));
+}
+
 nsa_status nsa_select_blocks(const nsa_config *cfg, const void *q, const void *cmp_k, float *scores_out,
                              int32_t *idx_out, void *ws, size_t ws_bytes, void *stream)
 {

@@ -54,6 +54,8 @@ struct RowArgs {
     int32_t *idx_sel;           // [B][Hkv][R][n] written by the selector
     void *o;                    // row (b, r) head h at o + b*o_sb + r*o_sr + h*dv
     long o_sb, o_sr;
+    int part;                   // sparse stage: 0 everything, 1 window (o written), 2 selected from packed blocks
+                                // (added to o), 3 pack K/V blocks only
 };
 
 // Arguments of the matrix-core decode step (one row per sequence).
@@ -65,11 +67,9 @@ struct DecArgs {
     const void *wg, *bg;
     const int32_t *idx_in;        // [B][Hkv][n] or nullptr
     void *o;                      // [B][Hq][dv]
-    int cs, ws, ss, nbp;          // compressed / window / selected splits; blocks per (b, g) in bx/by
+    int cs, ws, nbp;              // compressed / window splits; blocks per (b, g) in bx/by
     float *pm, *pl, *po;          // phase-A partials [pair][cs+ws][16] (+[dv])
     float *bx, *by;               // block importance terms [pair][16][nbp]
-    float *sm, *sl, *so;          // phase-C partials [pair][ss][16] (+[dv])
-    float *ocmp;                  // [pair][16][dv]
     int32_t *idx;                 // selection output [B][Hkv][n]
 };
 
@@ -112,7 +112,7 @@ bool cmp_attn_mfma_supported(const Dims &d);
 hipError_t launch_cmp_attn_mfma(const RowArgs &a, bool with_v, hipStream_t s);
 bool sparse_mfma_supported(const Dims &d);
 size_t sparse_mfma_ws_bytes(const Dims &d);   // K and V packed per 64-token block
-hipError_t launch_sparse_mfma(const RowArgs &a, void *vt_ws, hipStream_t s);
+hipError_t launch_sparse_mfma(const RowArgs &a, void *vt_ws, hipStream_t s);   // honours a.part
 bool decode_mfma_supported(const Dims &d);
 size_t decode_mfma_layout(const Dims &d, void *ws, DecArgs *A);   // bytes; fills A's buffers if ws
 hipError_t launch_decode_mfma(const DecArgs &A, hipStream_t s);

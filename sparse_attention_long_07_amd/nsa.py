@@ -22,8 +22,8 @@ STATUS = {0: "NSA_OK", -1: "NSA_ERR_NULL", -2: "NSA_ERR_SHAPE", -3: "NSA_ERR_DTY
           -5: "NSA_ERR_WORKSPACE", -6: "NSA_ERR_HIP", -7: "NSA_ERR_ALIGN"}
 
 EXPORTS = ("nsa_workspace_bytes", "nsa_compress_kv", "nsa_compressed_attention", "nsa_select_topn",
-           "nsa_sparse_attention", "nsa_select_blocks", "nsa_forward", "nsa_decode_step", "nsa_backward",
-           "nsa_status_string")
+           "nsa_sparse_attention", "nsa_pack_kv_blocks", "nsa_window_attention", "nsa_selected_attention", "nsa_select_blocks",
+           "nsa_forward", "nsa_decode_step", "nsa_backward", "nsa_status_string")
 
 
 class NSAError(RuntimeError):
@@ -61,6 +61,12 @@ def lib() -> ctypes.CDLL:
         L.nsa_select_topn.argtypes = [ctypes.POINTER(Config)] + [_vp] * 3
         L.nsa_sparse_attention.restype = ctypes.c_int
         L.nsa_sparse_attention.argtypes = [ctypes.POINTER(Config)] + [_vp] * 9 + [ctypes.c_size_t, _vp]
+        L.nsa_pack_kv_blocks.restype = ctypes.c_int
+        L.nsa_pack_kv_blocks.argtypes = [ctypes.POINTER(Config), _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.nsa_window_attention.restype = ctypes.c_int
+        L.nsa_window_attention.argtypes = [ctypes.POINTER(Config)] + [_vp] * 8
+        L.nsa_selected_attention.restype = ctypes.c_int
+        L.nsa_selected_attention.argtypes = [ctypes.POINTER(Config)] + [_vp] * 8 + [ctypes.c_size_t, _vp]
         L.nsa_select_blocks.restype = ctypes.c_int
         L.nsa_select_blocks.argtypes = [ctypes.POINTER(Config), _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.nsa_forward.restype = ctypes.c_int
@@ -186,6 +192,56 @@ def sparse_attention(s: NSAShape, q, k, v, o_cmp, idx, w_g, b_g, o=None, ws=None
     _check("nsa_sparse_attention", lib().nsa_sparse_attention(ctypes.byref(c), _p(q), _p(k), _p(v), _p(o_cmp),
                                                               _p(idx), _p(w_g), _p(b_g), _p(o), _p(ws), ws.numel(),
                                                               _stream()))
+    return o
+
+
+def pack_kv_blocks(s: NSAShape, k, v, ws=None):
+    """K and V repacked per 64-token block for selected_attention; returns
+    the workspace that holds them (empty on shapes that read K/V directly)."""
+    dt = _dt(s)
+    _req(k, "k", (s.B, s.Hkv, s.T, s.dk), dt)
+    _req(v, "v", (s.B, s.Hkv, s.T, s.dv), dt)
+    if ws is None:
+        ws = workspace(s, OP_SPARSE, k.device)
+    c = config(s)
+    _check("nsa_pack_kv_blocks", lib().nsa_pack_kv_blocks(ctypes.byref(c), _p(k), _p(v), _p(ws), ws.numel(),
+                                                          _stream()))
+    return ws
+
+
+def window_attention(s: NSAShape, q, k, v, o_cmp, w_g, b_g, o=None):
+    """Window half of stage S4: o = g_cmp o_cmp + g_win o_win."""
+    dt = _dt(s)
+    _req(q, "q", (s.B, s.T, s.Hq, s.dk), dt)
+    _req(k, "k", (s.B, s.Hkv, s.T, s.dk), dt)
+    _req(v, "v", (s.B, s.Hkv, s.T, s.dv), dt)
+    _req(o_cmp, "o_cmp", (s.B, s.T, s.Hq, s.dv), dt)
+    _req(w_g, "w_g", (s.Hq, 3, s.dk), dt)
+    _req(b_g, "b_g", (s.Hq, 3), dt)
+    if o is None:
+        o = torch.empty((s.B, s.T, s.Hq, s.dv), dtype=dt, device=q.device)
+    _req(o, "o", (s.B, s.T, s.Hq, s.dv), dt)
+    c = config(s)
+    _check("nsa_window_attention", lib().nsa_window_attention(ctypes.byref(c), _p(q), _p(k), _p(v), _p(o_cmp),
+                                                              _p(w_g), _p(b_g), _p(o), _stream()))
+    return o
+
+
+def selected_attention(s: NSAShape, q, k, v, idx, w_g, b_g, o, ws):
+    """Selected half of stage S4: o += g_slc o_slc (o updated in place);
+    ws is what pack_kv_blocks returned for the same k and v."""
+    dt = _dt(s)
+    _req(q, "q", (s.B, s.T, s.Hq, s.dk), dt)
+    _req(k, "k", (s.B, s.Hkv, s.T, s.dk), dt)
+    _req(v, "v", (s.B, s.Hkv, s.T, s.dv), dt)
+    _req(idx, "idx", (s.B, s.Hkv, s.T, s.n), torch.int32)
+    _req(w_g, "w_g", (s.Hq, 3, s.dk), dt)
+    _req(b_g, "b_g", (s.Hq, 3), dt)
+    _req(o, "o", (s.B, s.T, s.Hq, s.dv), dt)
+    c = config(s)
+    _check("nsa_selected_attention", lib().nsa_selected_attention(ctypes.byref(c), _p(q), _p(k), _p(v), _p(idx),
+                                                                   _p(w_g), _p(b_g), _p(o), _p(ws), ws.numel(),
+                                                                   _stream()))
     return o
 
 

@@ -81,6 +81,10 @@ def test_bad_config_rejected_everywhere(kw, code):
     assert L.nsa_forward(c, *f[:7], None, f[0], None, None, f[1], 1 << 40, None) == code
     assert L.nsa_decode_step(c, *f[:8], None, f[0], None, f[1], 1 << 40, None) == code
     assert L.nsa_backward(c, *([FAKE] * 22), FAKE, 1 << 40, None) == code
+    assert L.nsa_sparse_attention(c, *f[:8], f[0], 1 << 40, None) == code
+    assert L.nsa_window_attention(c, *f[:7], None) == code
+    assert L.nsa_pack_kv_blocks(c, f[0], f[1], f[2], 1 << 40, None) == code
+    assert L.nsa_selected_attention(c, *f[:7], f[0], 1 << 40, None) == code
 
 
 def test_null_config():
@@ -178,3 +182,46 @@ def test_backward_workspace_checks():
     assert L.nsa_backward(ctypes.byref(c), *f, ctypes.c_void_p(0x10010), need, None) == ALIGN
     # B * H_kv above the grid limit of the key passes
     assert L.nsa_backward(ctypes.byref(cfg(B=70000, H_kv=1, group=1)), *f, FAKE, 1 << 40, None) == SHAPE
+
+
+@pytest.mark.parametrize("pos", range(8))
+def test_sparse_stage_required_pointers(pos):
+    """S4 and its two halves reject null and misaligned operands."""
+    L = nsa.lib()
+    c = ctypes.byref(cfg())
+    args = [FAKE] * 8           # q k v o_cmp idx w_g b_g o
+    args[pos] = None
+    assert L.nsa_sparse_attention(c, *args, FAKE, 1 << 40, None) == NULL
+    args[pos] = MIS
+    assert L.nsa_sparse_attention(c, *args, FAKE, 1 << 40, None) == ALIGN
+    win = [FAKE] * 7            # q k v o_cmp w_g b_g o
+    sel = [FAKE] * 7            # q k v idx w_g b_g o
+    if pos < 7:
+        win[pos] = None
+        sel[pos] = None
+        assert L.nsa_window_attention(c, *win, None) == NULL
+        assert L.nsa_selected_attention(c, *sel, FAKE, 1 << 40, None) == NULL
+        win[pos] = MIS
+        sel[pos] = MIS
+        assert L.nsa_window_attention(c, *win, None) == ALIGN
+        assert L.nsa_selected_attention(c, *sel, FAKE, 1 << 40, None) == ALIGN
+
+
+def test_selected_attention_workspace_checks():
+    L = nsa.lib()
+    c = nsa.config(NSAShape(1, 256, 2, 16, 128, 128, "bf16"))      # a shape with packed K/V blocks
+    need = L.nsa_workspace_bytes(ctypes.byref(c), nsa.OP_SPARSE)
+    assert need > 0
+    f = [FAKE] * 7
+    assert L.nsa_selected_attention(ctypes.byref(c), *f, None, need, None) == WS
+    assert L.nsa_selected_attention(ctypes.byref(c), *f, FAKE, need - 1, None) == WS
+    assert L.nsa_selected_attention(ctypes.byref(c), *f, ctypes.c_void_p(0x10010), need, None) == ALIGN
+    assert L.nsa_sparse_attention(ctypes.byref(c), *([FAKE] * 8), FAKE, need - 1, None) == WS
+    assert L.nsa_pack_kv_blocks(ctypes.byref(c), FAKE, FAKE, FAKE, need - 1, None) == WS
+    assert L.nsa_pack_kv_blocks(ctypes.byref(c), FAKE, FAKE, None, need, None) == WS
+    assert L.nsa_pack_kv_blocks(ctypes.byref(c), None, FAKE, FAKE, need, None) == NULL
+    assert L.nsa_pack_kv_blocks(ctypes.byref(c), FAKE, MIS, FAKE, need, None) == ALIGN
+    # a shape that reads K and V directly needs no workspace: nothing to pack, no launch
+    c2 = nsa.config(NSAShape(1, 256, 2, 4, 64, 32, "bf16"))
+    assert L.nsa_workspace_bytes(ctypes.byref(c2), nsa.OP_SPARSE) == 0
+    assert L.nsa_pack_kv_blocks(ctypes.byref(c2), FAKE, FAKE, None, 0, None) == 0

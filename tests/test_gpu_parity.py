@@ -292,6 +292,18 @@ def test_stage_parity(name, s, scaled):
     err = np.abs(np64(o) - ref["o"]).max()
     say("  S4 max|o - ref| = %.3g" % err)
     assert err <= out_tol(s, ref["o"])
+    # S4 in parts: pack K/V blocks, window (writes o), then selected (adds to o)
+    idx_in = torch.from_numpy(ref["idx"]).cuda()
+    ws = nsa.pack_kv_blocks(s, x["k"], x["v"])
+    o2 = nsa.window_attention(s, x["q"], x["k"], x["v"], oc_in, x["w_g"], x["b_g"])
+    nsa.selected_attention(s, x["q"], x["k"], x["v"], idx_in, x["w_g"], x["b_g"], o2, ws)
+    torch.cuda.synchronize()
+    err2 = np.abs(np64(o2) - ref["o"]).max()
+    say("  S4 split max|o - ref| = %.3g" % err2)
+    assert err2 <= out_tol(s, ref["o"])
+    if nsa.workspace_bytes(s, nsa.OP_SPARSE) > 0:
+        # packed-block (matrix core) path: the combined call runs the same two kernels in the same order
+        assert torch.equal(o2, o)
 
 
 @pytest.mark.parametrize("mode", ["random", "quantized_ties", "all_equal", "huge_T"])
