@@ -4,7 +4,7 @@ One step = the whole hot path over one batch of synthetic input:
   * the 64k prefill forward (B=1, T=65536, 4 KV heads x 16 query heads,
     d_k=192, d_v=128, bf16): compression (S1), compressed attention with
     block importance (S2), top-n selection (S3), selected + window attention
-    with the gated sum (S4);
+    with the gated sum (S4, timed as its three kernels: pack, window, selected);
   * one decode step on 32 sequences with 65,536-token caches (same heads).
 Inputs are resident in HBM before timing starts.  Each stage is bracketed by
 HIP events on the stream the kernels run on; the printed JSON line carries
@@ -16,6 +16,7 @@ roofline of the dominant kernel and the CPU oracle on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -35,6 +36,24 @@ from sparse_attention_long_07_amd.inputs import make_decode, make_prefill  # noq
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_FP32_VALU_TFLOPS = 157.3
 PEAK_HBM_GBPS = 8000.0
+
+# HBM bytes per launch of a kernel from the FETCH_SIZE and WRITE_SIZE counters
+# (scaled by a plain device copy's readings), with the source file they were
+# taken on and its SHA-256: the figure is reported only while that source is
+# unchanged.
+MEASURED_TRAFFIC = {
+    "k_selected_mfma": ("sparse_attention_long_07_amd/csrc/k_sparse.hip",
+                        "2ccd7f994725c66276a3837860157671d85c99e6b702143e6ae9216077091f09", 63.81e9),
+}
+
+
+def measured_traffic(kernel):
+    ent = MEASURED_TRAFFIC.get(kernel)
+    if ent is None:
+        return None
+    path, sha, nbytes = ent
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return nbytes if hashlib.sha256(f.read()).hexdigest() == sha else None
 
 
 def log(*a):
@@ -198,8 +217,9 @@ def main():
     kname, bound, units, peak, unit = work[dom]
     dur_s = st_ms[stages.index(dom)] * 1e-3
     achieved = units / dur_s / (1e12 if unit == "TFLOP/s" else 1e9)
+    traffic = args.traffic if args.traffic is not None else measured_traffic(kname)
     roof = {"bound": bound, "kernel": kname, "stage": dom, "achieved": round(achieved, 2), "peak": peak,
-            "unit": unit, "frac": round(achieved / peak, 4), "traffic": args.traffic,
+            "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
             "avg_launch_ms": round(float(dur_s * 1e3), 4), "algorithmic_per_launch": units}
     kernels = {}
     for k, (kn, bd, u, pk, un) in work.items():
