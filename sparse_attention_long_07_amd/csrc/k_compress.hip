@@ -8,14 +8,15 @@
 //
 // Block i flattened token-major is the 32*dim consecutive elements starting
 // at token 16 i, so the product is a plain matrix product whose rows overlap.
-// It runs on the vector ALUs with v_dot2c_f32_bf16 (two bf16 products added
-// into an fp32 accumulator per lane and instruction): the bf16 operands are
-// used as stored, and the position term is accumulated beside it so that
-// x + PE never has to be rounded.
+// The bf16 operands are used as stored and the position term is accumulated
+// beside the main product, so x + PE never has to be rounded.
 //
-// Tile: 128 blocks x 64 channels per workgroup, 64 input elements per step,
-// staged through LDS one step ahead (register prefetch, double buffer).  A
-// thread owns 8 blocks (16 apart) x 4 channels.
+// k_compress_mfma (d = 64, 128, 192): v_mfma_f32_32x32x16_bf16.  A workgroup
+// takes 63 blocks plus one extra operand row that holds PE, so the same
+// matrix product yields sum_m W[c][m] PE[m] in that row; 64 rows x all d
+// channels, 64-element K steps staged through LDS one step ahead.
+// k_compress_bf16 (other d): the same sums on the vector ALUs with
+// v_dot2c_f32_bf16, 128 blocks x 64 channels per workgroup.
 #include "mfma_util.h"
 #include "nsa_internal.h"
 
@@ -138,6 +139,113 @@ __global__ __launch_bounds__(kThreads) void k_compress_bf16(const uint16_t *__re
     }
 }
 
+constexpr int kMRows = 64;        // operand rows per workgroup: 63 blocks + the PE row
+constexpr int kMBlocks = kMRows - 1;
+constexpr int kMK = 64;           // K elements per step
+constexpr int kMS = kMK + 8;      // LDS row stride (bf16)
+
+template <int DIM>
+struct CompressMfmaLds {
+    uint16_t a[2][kMRows * kMS];
+    uint16_t b[2][DIM * kMS];
+    float pe[DIM];                // sum_m W[c][m] PE[m]
+};
+
+// 4 waves: wave w takes operand rows 32 (w % 2) .. +31 and channels
+// (w / 2) * DIM/2 .. +DIM/2 (DIM/64 tiles of 32 x 32).
+template <int DIM>
+__global__ __launch_bounds__(kThreads) void k_compress_mfma(const uint16_t *__restrict__ x,
+                                                            const uint16_t *__restrict__ W,
+                                                            const uint16_t *__restrict__ PE,
+                                                            uint16_t *__restrict__ out, int T, int ncmp, int npad)
+{
+    constexpr int NT = DIM / 64;                 // 32-channel tiles per wave
+    constexpr int L = 32 * DIM;
+    constexpr int BTASK = DIM * (kMK / 8) / kThreads;
+    __shared__ CompressMfmaLds<DIM> sm;
+    const int bh = blockIdx.y, i0 = blockIdx.x * kMBlocks;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rw = 32 * (wave & 1), cw = (wave >> 1) * (DIM / 2);
+    const uint16_t *xs = x + (long)bh * T * DIM;
+
+    u32x4 ra[2], rb[BTASK];
+    auto load = [&](int st) {
+        const int k0 = st * kMK;
+        const u32x4 z = {0, 0, 0, 0};
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            const int task = tid + q * kThreads, row = task >> 3, ch = task & 7;
+            const int i = i0 + row;
+            if (row == kMBlocks) ra[q] = ld16(PE + k0 + ch * 8);
+            else ra[q] = i < ncmp ? ld16(xs + 16L * i * DIM + k0 + ch * 8) : z;
+        }
+#pragma unroll
+        for (int q = 0; q < BTASK; q++) {
+            const int task = tid + q * kThreads, c = task >> 3, ch = task & 7;
+            rb[q] = ld16(W + (long)c * L + k0 + ch * 8);
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            const int task = tid + q * kThreads, row = task >> 3, ch = task & 7;
+            st16(&sm.a[buf][row * kMS + ch * 8], ra[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < BTASK; q++) {
+            const int task = tid + q * kThreads, c = task >> 3, ch = task & 7;
+            st16(&sm.b[buf][c * kMS + ch * 8], rb[q]);
+        }
+    };
+
+    f32x16 acc[NT];
+#pragma unroll
+    for (int n = 0; n < NT; n++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[n][r] = 0.f;
+
+    constexpr int nsteps = L / kMK;
+    load(0);
+    store(0);
+    lds_barrier();
+    const int fr = lane & 31, fk = 8 * (lane >> 5);   // operand row / K offset of this lane
+    for (int st = 0; st < nsteps; st++) {
+        const int buf = st & 1;
+        if (st + 1 < nsteps) load(st + 1);
+#pragma unroll
+        for (int ks = 0; ks < kMK / 16; ks++) {
+            const bf16x8 af = as_bf16x8(ld16(&sm.a[buf][(rw + fr) * kMS + 16 * ks + fk]));
+#pragma unroll
+            for (int n = 0; n < NT; n++) {
+                const bf16x8 bf = as_bf16x8(ld16(&sm.b[buf][(cw + 32 * n + fr) * kMS + 16 * ks + fk]));
+                acc[n] = mfma32(af, bf, acc[n]);
+            }
+        }
+        if (st + 1 < nsteps) store(buf ^ 1);
+        lds_barrier();
+    }
+    // lane l holds channel cw + 32n + l%32 of rows rw + 8(e/4) + 4(l/32) + e%4;
+    // operand row 63 (the PE row) is e = 15 of the upper lane half of wave 1/3
+    if ((wave & 1) && lane >= 32) {
+#pragma unroll
+        for (int n = 0; n < NT; n++) sm.pe[cw + 32 * n + (lane & 31)] = acc[n][15];
+    }
+    lds_barrier();
+#pragma unroll
+    for (int n = 0; n < NT; n++) {
+        const int c = cw + 32 * n + (lane & 31);
+        const float pc = sm.pe[c];
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+            const int row = rw + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            const int i = i0 + row;
+            if (row == kMBlocks || i >= npad) continue;
+            const __bf16 y = i < ncmp ? (__bf16)(acc[n][e] + pc) : (__bf16)0.f;
+            out[((long)bh * npad + i) * DIM + c] = __builtin_bit_cast(uint16_t, y);
+        }
+    }
+}
+
 }  // namespace
 
 bool compress_bf16_supported(const Dims &d) { return d.dtype == NSA_BF16; }
@@ -145,9 +253,19 @@ bool compress_bf16_supported(const Dims &d) { return d.dtype == NSA_BF16; }
 hipError_t launch_compress_bf16(const Dims &d, const void *x, const void *W, const void *PE, void *out, int dim,
                                 hipStream_t s)
 {
-    dim3 grid((d.npad + kTI - 1) / kTI, (dim + kTC - 1) / kTC, d.B * d.Hkv);
-    hipLaunchKernelGGL(k_compress_bf16, grid, dim3(kThreads), 0, s, (const uint16_t *)x, (const uint16_t *)W,
-                       (const uint16_t *)PE, (uint16_t *)out, d.T, dim, d.ncmp, d.npad);
+    const dim3 mgrid((d.npad + kMBlocks - 1) / kMBlocks, d.B * d.Hkv);
+    const uint16_t *xs = (const uint16_t *)x, *Ws = (const uint16_t *)W, *ps = (const uint16_t *)PE;
+    uint16_t *o = (uint16_t *)out;
+    if (dim == 192) {
+        hipLaunchKernelGGL(k_compress_mfma<192>, mgrid, dim3(kThreads), 0, s, xs, Ws, ps, o, d.T, d.ncmp, d.npad);
+    } else if (dim == 128) {
+        hipLaunchKernelGGL(k_compress_mfma<128>, mgrid, dim3(kThreads), 0, s, xs, Ws, ps, o, d.T, d.ncmp, d.npad);
+    } else if (dim == 64) {
+        hipLaunchKernelGGL(k_compress_mfma<64>, mgrid, dim3(kThreads), 0, s, xs, Ws, ps, o, d.T, d.ncmp, d.npad);
+    } else {
+        dim3 grid((d.npad + kTI - 1) / kTI, (dim + kTC - 1) / kTC, d.B * d.Hkv);
+        hipLaunchKernelGGL(k_compress_bf16, grid, dim3(kThreads), 0, s, xs, Ws, ps, o, d.T, dim, d.ncmp, d.npad);
+    }
     return hipGetLastError();
 }
 
