@@ -77,11 +77,14 @@ __device__ __forceinline__ void wave_select_topn(const float *S, int jcur, int n
         for (int rr = 0; rr < RR; rr++)
             if (lane + rr * 64 < ncand) setbit(rr);
     } else {
+        // unconditional loads at clamped (valid) indices, so all 16 are in
+        // flight at once; entries past jc are masked afterwards
         float cache[16];
 #pragma unroll
         for (int rr = 0; rr < 16; rr++) {
             const int j = lane + 64 * rr;
-            float v = j < ncand ? S[j] : -INFINITY;
+            const float sv = S[j < ncand ? j : ncand - 1];
+            const float v = j < ncand ? sv : -INFINITY;
             cache[rr] = v == v ? v : -INFINITY;
         }
         for (int round = 0; round < k; round++) {
@@ -155,8 +158,9 @@ __device__ __forceinline__ void wave_select_topn_fast(const float *S, int jcur, 
 #pragma unroll
     for (int rr = 0; rr < 16; rr++) {
         const int j = lane + 64 * rr;
+        const float sv = S[j < ncand ? j : ncand - 1];   // unconditional: all loads in flight at once
         ok[rr] = j < ncand && j != 0 && j != jcur && j != jcur - 1;
-        key[rr] = ok[rr] ? ordered_key(S[j]) : 0u;
+        key[rr] = ok[rr] ? ordered_key(sv) : 0u;
         if (ok[rr] && (!lvalid || key[rr] > lmax)) lmax = key[rr];
         lvalid |= ok[rr];
     }
