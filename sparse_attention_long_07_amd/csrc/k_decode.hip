@@ -275,19 +275,17 @@ template <int DV>
 struct TailLds {
     union {
         struct {                       // phase B
-            float lm[64][16], ll[64][16], wsp[64][16];
+            float lm[64][16], ll[64][16], wsp[64][16];   // compressed splits: max, sum, merge weight
+            float wm[64][16], wl[64][16], wwp[64][16];   // window splits
             float lse[16];
             uint2 cand[64];
             float S[8192];             // block scores (nb <= 8192)
         } b;
         unsigned char wave[kTailWaves][DecWaveLds<DV>::BYTES];   // phase C
-        struct {                       // phase D
-            float lm[2][64][16], ll[2][64][16], wts[2][64][16];
-            float gate[16][3];
-        } d;
     } u;
-    float os[16][DV];                  // selected branch: merged unnormalised output
-    float ms[16], lsum[16];            // and its max / sum per head
+    float2 ocw[16][DV];                // merged compressed and window outputs (normalised)
+    float gate[16][3];
+    float ms[16], lsum[16];            // selected branch: max / sum per head
     float wm[kTailWaves][16], wl[kTailWaves][16];
     int blist[16];
     int nblk;
@@ -310,29 +308,41 @@ __global__ __launch_bounds__(kTailThreads) void k_dec_tail(DecArgs A)
     const int nsplit = A.cs + A.ws;
     const float *pm = A.pm + (long)pair * nsplit * 16, *pl = A.pl + (long)pair * nsplit * 16;
 
-    // ---- phase B: exact log-sum-exp per head, block scores, selection
+    // ---- phase B: exact log-sum-exp per head and branch, merge weights of
+    // the splits, block scores; then wavefront 0 selects the blocks while the
+    // others merge the compressed and window partials and form the gates
     const int32_t *ilist = A.idx_in ? A.idx_in + (long)pair * d.n : A.idx + (long)pair * d.n;
+    auto &B = sm.u.b;
+    for (int e = tid; e < nsplit * 16; e += NT) {
+        const int s2 = e >> 4, h = e & 15;
+        if (s2 < A.cs) {
+            B.lm[s2][h] = pm[e];
+            B.ll[s2][h] = pl[e];
+        } else {
+            B.wm[s2 - A.cs][h] = pm[e];
+            B.wl[s2 - A.cs][h] = pl[e];
+        }
+    }
+    lds_barrier();
+    if (tid < 32) {
+        // lanes 0-15: compressed branch of head tid; 16-31: window branch of head tid-16
+        const int h = tid & 15;
+        const bool cmpb = tid < 16;
+        const int ns = cmpb ? A.cs : A.ws;
+        float(*lm)[16] = cmpb ? B.lm : B.wm;
+        float(*ll)[16] = cmpb ? B.ll : B.wl;
+        float(*wp)[16] = cmpb ? B.wsp : B.wwp;
+        float M = -INFINITY;
+        for (int s2 = 0; s2 < ns; s2++) M = fmaxf(M, lm[s2][h]);
+        float L = 0.f;
+        if (M != -INFINITY)
+            for (int s2 = 0; s2 < ns; s2++) L += ll[s2][h] * fast_exp2(lm[s2][h] - M);
+        const float lse = M == -INFINITY || L <= 0.f ? -INFINITY : M + fast_log2(L);
+        for (int s2 = 0; s2 < ns; s2++) wp[s2][h] = lse == -INFINITY ? 0.f : fast_exp2(lm[s2][h] - lse);
+        if (cmpb) B.lse[h] = lse;
+    }
+    lds_barrier();
     if (!A.idx_in) {
-        auto &B = sm.u.b;
-        for (int e = tid; e < A.cs * 16; e += NT) {
-            B.lm[e >> 4][e & 15] = pm[e];
-            B.ll[e >> 4][e & 15] = pl[e];
-        }
-        lds_barrier();
-        if (tid < 16) {
-            float M = -INFINITY;
-            for (int s2 = 0; s2 < A.cs; s2++) M = fmaxf(M, B.lm[s2][tid]);
-            float L = 0.f;
-            if (M != -INFINITY)
-                for (int s2 = 0; s2 < A.cs; s2++) L += B.ll[s2][tid] * fast_exp2(B.lm[s2][tid] - M);
-            B.lse[tid] = M == -INFINITY ? -INFINITY : M + fast_log2(L);
-        }
-        lds_barrier();
-        for (int e = tid; e < A.cs * 16; e += NT) {
-            const int s2 = e >> 4, h = e & 15;
-            B.wsp[s2][h] = B.lse[h] == -INFINITY ? 0.f : fast_exp2(B.lm[s2][h] - B.lse[h]);
-        }
-        lds_barrier();
         // block j: its own keys 4j..4j+3 (X) plus key 4j-1 (Y of block j-1);
         // phase A wrote blocks 0..nbp-1, a block past them has no key of its own
         const float *bx = A.bx + (long)pair * 16 * A.nbp, *by = A.by + (long)pair * 16 * A.nbp;
@@ -355,12 +365,16 @@ __global__ __launch_bounds__(kTailThreads) void k_dec_tail(DecArgs A)
             B.S[j] = acc;
         }
         lds_barrier();
-        if (wave == 0) wave_select_topn_fast(B.S, jcur, d.n, A.idx + (long)pair * d.n, lane, B.cand);
-        __threadfence_block();   // the block list is read back below by other wavefronts
-        __syncthreads();
     }
-    // the distinct valid blocks, ascending (the list is ascending unless supplied)
+    const float *po = A.po + (long)pair * nsplit * 16 * DV;
     if (wave == 0) {
+        if (!A.idx_in) {
+            wave_select_topn_fast(B.S, jcur, d.n, A.idx + (long)pair * d.n, lane, B.cand);
+            // the list is read back below by this wavefront's lanes
+            __builtin_amdgcn_s_waitcnt(0);
+            __threadfence_block();
+        }
+        // the distinct valid blocks, ascending (the list is ascending unless supplied)
         const int jb = lane < d.n ? ilist[lane] : -1;
         bool ok = jb >= 0 && jb <= jcur;
         for (int u2 = 0; u2 < 16; u2++) {
@@ -370,6 +384,40 @@ __global__ __launch_bounds__(kTailThreads) void k_dec_tail(DecArgs A)
         const uint64_t v = __ballot(ok);
         if (ok) sm.blist[__popcll(v & __lanemask_lt())] = jb;
         if (lane == 0) sm.nblk = __popcll(v);
+    } else {
+        const int t1 = tid - 64;   // 0 .. NT-65
+        // gates: 16 threads per (head, gate) dot product of length DK
+        for (int task = t1; task < 16 * 3 * 16; task += NT - 64) {
+            const int dot = task >> 4, part = task & 15;
+            const int h = dot / 3, c = dot % 3;
+            const uint16_t *qr = (const uint16_t *)A.q + ((long)b * d.Hq + g * 16 + h) * DK;
+            const uint16_t *wr = (const uint16_t *)A.wg + ((long)(g * 16 + h) * 3 + c) * DK;
+            float z = 0.f;
+            for (int ch = part; ch < DK / 8; ch += 16) {
+                const u32x4 wv = ld16(wr + 8 * ch), qv = ld16(qr + 8 * ch);
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    z += __uint_as_float(wv[e] << 16) * __uint_as_float(qv[e] << 16);
+                    z += __uint_as_float(wv[e] & 0xffff0000u) * __uint_as_float(qv[e] & 0xffff0000u);
+                }
+            }
+#pragma unroll
+            for (int off = 8; off > 0; off >>= 1) z += __shfl_xor(z, off, 16);
+            if (part == 0) {
+                z += __uint_as_float((uint32_t)((const uint16_t *)A.bg)[(g * 16 + h) * 3 + c] << 16);
+                sm.gate[h][c] = sigmoidf_(z);
+            }
+        }
+        // compressed and window outputs: the splits' partials, weighted
+        for (int e = t1; e < 16 * DV; e += NT - 64) {
+            const int h = e / DV, c = e % DV;
+            float oc = 0.f, ow = 0.f;
+#pragma unroll 4
+            for (int s2 = 0; s2 < A.cs; s2++) oc += po[(long)s2 * 16 * DV + e] * B.wsp[s2][h];
+#pragma unroll 2
+            for (int s2 = 0; s2 < A.ws; s2++) ow += po[(long)(A.cs + s2) * 16 * DV + e] * B.wwp[s2][h];
+            sm.ocw[h][c] = make_float2(oc, ow);
+        }
     }
     lds_barrier();
 
@@ -470,76 +518,19 @@ __global__ __launch_bounds__(kTailThreads) void k_dec_tail(DecArgs A)
         sm.lsum[tid] = L;
     }
     lds_barrier();
+    // ---- phase D: selected branch merged over the wavefronts, gated sum
+    uint16_t *o = (uint16_t *)A.o + ((long)b * d.Hq + g * 16) * DV;
     for (int e = tid; e < 16 * DV; e += NT) {
         const int h = e / DV, c = e % DV;
-        const float M = sm.ms[h];
+        const float M = sm.ms[h], L = sm.lsum[h];
         float acc = 0.f;
         for (int w = 0; w < kTailWaves; w++) {
             const float mw = sm.wm[w][h];
             if (mw != -INFINITY) acc += ((const float *)sm.u.wave[w])[h * (DV + 4) + c] * fast_exp2(mw - M);
         }
-        sm.os[h][c] = acc;
-    }
-    lds_barrier();
-
-    // ---- phase D: merge the compressed and window partials, gates, output
-    auto &D = sm.u.d;
-    for (int e = tid; e < 2 * 64 * 16; e += NT) {
-        const int br = e / (64 * 16), s2 = (e / 16) % 64, h = e % 16;
-        const int ns = br == 0 ? A.cs : A.ws;
-        if (s2 < ns) {
-            const long src = (long)(br == 1 ? A.cs + s2 : s2) * 16 + h;
-            D.lm[br][s2][h] = pm[src];
-            D.ll[br][s2][h] = pl[src];
-        }
-    }
-    lds_barrier();
-    if (tid < 2 * 16) {
-        const int br = tid / 16, h = tid % 16;
-        const int ns = br == 0 ? A.cs : A.ws;
-        float M = -INFINITY;
-        for (int s2 = 0; s2 < ns; s2++) M = fmaxf(M, D.lm[br][s2][h]);
-        float L = 0.f;
-        if (M != -INFINITY)
-            for (int s2 = 0; s2 < ns; s2++) L += D.ll[br][s2][h] * fast_exp2(D.lm[br][s2][h] - M);
-        for (int s2 = 0; s2 < ns; s2++)
-            D.wts[br][s2][h] = (M == -INFINITY || L <= 0.f) ? 0.f : fast_exp2(D.lm[br][s2][h] - M) / L;
-    }
-    // gates: 16 threads per (head, gate) dot product of length DK
-    for (int task = tid; task < 16 * 3 * 16; task += NT) {
-        const int dot = task >> 4, part = task & 15;
-        const int h = dot / 3, c = dot % 3;
-        const uint16_t *qr = (const uint16_t *)A.q + ((long)b * d.Hq + g * 16 + h) * DK;
-        const uint16_t *wr = (const uint16_t *)A.wg + ((long)(g * 16 + h) * 3 + c) * DK;
-        float z = 0.f;
-        for (int ch = part; ch < DK / 8; ch += 16) {
-            const u32x4 wv = ld16(wr + 8 * ch), qv = ld16(qr + 8 * ch);
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                z += __uint_as_float(wv[e] << 16) * __uint_as_float(qv[e] << 16);
-                z += __uint_as_float(wv[e] & 0xffff0000u) * __uint_as_float(qv[e] & 0xffff0000u);
-            }
-        }
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) z += __shfl_xor(z, off, 16);
-        if (part == 0) {
-            z += __uint_as_float((uint32_t)((const uint16_t *)A.bg)[(g * 16 + h) * 3 + c] << 16);
-            D.gate[h][c] = sigmoidf_(z);
-        }
-    }
-    lds_barrier();
-    const float *po = A.po + (long)pair * nsplit * 16 * DV;
-    uint16_t *o = (uint16_t *)A.o + ((long)b * d.Hq + g * 16) * DV;
-    for (int e = tid; e < 16 * DV; e += NT) {
-        const int h = e / DV, c = e % DV;
-        float oc = 0.f, ow = 0.f;
-#pragma unroll 4
-        for (int s2 = 0; s2 < A.cs; s2++) oc += po[(long)s2 * 16 * DV + e] * D.wts[0][s2][h];
-#pragma unroll 2
-        for (int s2 = 0; s2 < A.ws; s2++) ow += po[(long)(A.cs + s2) * 16 * DV + e] * D.wts[1][s2][h];
-        const float L = sm.lsum[h];
-        const float os = L > 0.f ? sm.os[h][c] / L : 0.f;
-        const float y = D.gate[h][0] * oc + D.gate[h][1] * os + D.gate[h][2] * ow;
+        const float os = L > 0.f ? acc / L : 0.f;
+        const float2 cw = sm.ocw[h][c];
+        const float y = sm.gate[h][0] * cw.x + sm.gate[h][1] * os + sm.gate[h][2] * cw.y;
         __bf16 yb = (__bf16)y;
         o[e] = __builtin_bit_cast(uint16_t, yb);
     }
