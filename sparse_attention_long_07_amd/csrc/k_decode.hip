@@ -275,8 +275,8 @@ template <int DV>
 struct TailLds {
     union {
         struct {                       // phase B
-            float lm[64][16], ll[64][16], wsp[64][16];   // compressed splits: max, sum, merge weight
-            float wm[64][16], wl[64][16], wwp[64][16];   // window splits
+            float wsp[64][16];         // merge weight of each compressed split (per head)
+            float wwp[64][16];         // ... and window split
             float lse[16];
             uint2 cand[64];
             float S[8192];             // block scores (nb <= 8192)
@@ -313,49 +313,48 @@ __global__ __launch_bounds__(kTailThreads) void k_dec_tail(DecArgs A)
     // others merge the compressed and window partials and form the gates
     const int32_t *ilist = A.idx_in ? A.idx_in + (long)pair * d.n : A.idx + (long)pair * d.n;
     auto &B = sm.u.b;
-    for (int e = tid; e < nsplit * 16; e += NT) {
-        const int s2 = e >> 4, h = e & 15;
-        if (s2 < A.cs) {
-            B.lm[s2][h] = pm[e];
-            B.ll[s2][h] = pl[e];
-        } else {
-            B.wm[s2 - A.cs][h] = pm[e];
-            B.wl[s2 - A.cs][h] = pl[e];
+    // block j: its own keys 4j..4j+3 (X) plus key 4j-1 (Y of block j-1);
+    // phase A wrote blocks 0..nbp-1, a block past them has no key of its own.
+    // Thread tid's first block is loaded now, so that these loads overlap the
+    // log-sum-exp below.
+    const float *bx = A.bx + (long)pair * 16 * A.nbp, *by = A.by + (long)pair * 16 * A.nbp;
+    float xv[16], yv[16];
+    auto load_terms = [&](int j) {
+        const bool hx = j < A.nbp, hy = j > 0 && j - 1 < A.nbp;
+#pragma unroll
+        for (int h = 0; h < 16; h++) {
+            xv[h] = hx ? bx[(long)h * A.nbp + j] : 0.f;
+            yv[h] = hy ? by[(long)h * A.nbp + j - 1] : 0.f;
         }
-    }
-    lds_barrier();
-    if (tid < 32) {
-        // lanes 0-15: compressed branch of head tid; 16-31: window branch of head tid-16
-        const int h = tid & 15;
-        const bool cmpb = tid < 16;
-        const int ns = cmpb ? A.cs : A.ws;
-        float(*lm)[16] = cmpb ? B.lm : B.wm;
-        float(*ll)[16] = cmpb ? B.ll : B.wl;
-        float(*wp)[16] = cmpb ? B.wsp : B.wwp;
-        float M = -INFINITY;
-        for (int s2 = 0; s2 < ns; s2++) M = fmaxf(M, lm[s2][h]);
-        float L = 0.f;
-        if (M != -INFINITY)
-            for (int s2 = 0; s2 < ns; s2++) L += ll[s2][h] * fast_exp2(lm[s2][h] - M);
-        const float lse = M == -INFINITY || L <= 0.f ? -INFINITY : M + fast_log2(L);
-        for (int s2 = 0; s2 < ns; s2++) wp[s2][h] = lse == -INFINITY ? 0.f : fast_exp2(lm[s2][h] - lse);
-        if (cmpb) B.lse[h] = lse;
+    };
+    if (!A.idx_in && tid <= jcur) load_terms(tid);
+    {
+        // wavefront h: head h; lane s holds split s of each branch (cs, ws <= 64)
+        const int h = wave;
+        auto branch = [&](int s0, int ns, float(*wp)[16]) {
+            const float mv = lane < ns ? pm[(long)(s0 + lane) * 16 + h] : -INFINITY;
+            const float lv = lane < ns ? pl[(long)(s0 + lane) * 16 + h] : 0.f;
+            float M = mv;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+            float L = M == -INFINITY ? 0.f : lv * fast_exp2(mv - M);
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off, 64);
+            const float lse = M == -INFINITY || L <= 0.f ? -INFINITY : M + fast_log2(L);
+            if (lane < ns) wp[lane][h] = lse == -INFINITY ? 0.f : fast_exp2(mv - lse);
+            return lse;
+        };
+        const float lse = branch(0, A.cs, B.wsp);
+        branch(A.cs, A.ws, B.wwp);
+        if (lane == 0) B.lse[h] = lse;
     }
     lds_barrier();
     if (!A.idx_in) {
-        // block j: its own keys 4j..4j+3 (X) plus key 4j-1 (Y of block j-1);
-        // phase A wrote blocks 0..nbp-1, a block past them has no key of its own
-        const float *bx = A.bx + (long)pair * 16 * A.nbp, *by = A.by + (long)pair * 16 * A.nbp;
         constexpr int kBlkPerSplit = kSplitKeys / 4;
         for (int j = tid; j <= jcur; j += NT) {
+            if (j != tid) load_terms(j);
             const int sj = j / kBlkPerSplit, sp = (j - 1) / kBlkPerSplit;
-            const bool hx = j < A.nbp, hy = j > 0 && j - 1 < A.nbp;
-            float xv[16], yv[16];
-#pragma unroll
-            for (int h = 0; h < 16; h++) {
-                xv[h] = hx ? bx[(long)h * A.nbp + j] : 0.f;
-                yv[h] = hy ? by[(long)h * A.nbp + j - 1] : 0.f;
-            }
+            const bool hy = j > 0 && j - 1 < A.nbp;
             float acc = 0.f;
 #pragma unroll
             for (int h = 0; h < 16; h++) {
