@@ -60,7 +60,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(s, x, flops_total, rows_sample=4096, seed=5):
+def cpu_baseline(s, x, flops_total, rows_sample=10240, seed=5):
     """The oracle on a bounded sample of the prefill workload: the full
     compression of all tokens plus `rows_sample` query positions drawn
     uniformly (every KV group); extrapolated to the whole workload."""
@@ -96,7 +96,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--cpu-rows", type=int, default=10240)
     ap.add_argument("--traffic", type=float, default=None,
                     help="HBM bytes per launch of the roofline kernel from FETCH_SIZE/WRITE_SIZE counters")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
