@@ -194,8 +194,17 @@ def test_prefill_full_size_sampled(wname):
     x = make_prefill(s, 1000, "cuda", unit_scaled=wl.unit_scaled)
     ck, cv = nsa.compress_kv(s, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"])
     o, idx = nsa.forward(s, x["q"], x["k"], x["v"], ck, cv, x["w_g"], x["b_g"], want_idx=True)
+    # the stage-by-stage calls that bench.py times give the same result, bit for bit
+    ocmp, sc = nsa.compressed_attention(s, x["q"], ck, cv)
+    idx2 = nsa.select_topn(s, sc)
+    ws = nsa.pack_kv_blocks(s, x["k"], x["v"])
+    o2 = nsa.window_attention(s, x["q"], x["k"], x["v"], ocmp, x["w_g"], x["b_g"])
+    nsa.selected_attention(s, x["q"], x["k"], x["v"], idx2, x["w_g"], x["b_g"], o2, ws)
     torch.cuda.synchronize()
-    say("  gpu done; oracle compression")
+    assert torch.equal(idx2, idx)
+    assert torch.equal(o2, o)
+    del ocmp, sc, idx2, ws, o2
+    say("  gpu done (staged path identical); oracle compression")
     kc = oracle_compress(s, x["k"], x["w_ck"], x["pe_k"])
     vc = oracle_compress(s, x["v"], x["w_cv"], x["pe_v"])
     for got, ref in ((ck, kc), (cv, vc)):
