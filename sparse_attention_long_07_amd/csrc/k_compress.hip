@@ -11,7 +11,8 @@
 // The bf16 operands are used as stored and the position term is accumulated
 // beside the main product, so x + PE never has to be rounded.
 //
-// k_compress_mfma (d = 64, 128, 192): v_mfma_f32_32x32x16_bf16.  A workgroup
+// k_compress_mfma_kv (d = 64, 128, 192; K and V in one launch):
+// v_mfma_f32_32x32x16_bf16.  A workgroup
 // takes 63 blocks plus one extra operand row that holds PE, so the same
 // matrix product yields sum_m W[c][m] PE[m] in that row; 64 rows x all d
 // channels, 64-element K steps staged through LDS one step ahead.
@@ -151,19 +152,19 @@ struct CompressMfmaLds {
     float pe[DIM];                // sum_m W[c][m] PE[m]
 };
 
-// 4 waves: wave w takes operand rows 32 (w % 2) .. +31 and channels
-// (w / 2) * DIM/2 .. +DIM/2 (DIM/64 tiles of 32 x 32).
+// One workgroup tile (63 blocks of one (b, KV head)).  4 waves: wave w takes
+// operand rows 32 (w % 2) .. +31 and channels (w / 2) * DIM/2 .. +DIM/2
+// (DIM/64 tiles of 32 x 32).
 template <int DIM>
-__global__ __launch_bounds__(kThreads) void k_compress_mfma(const uint16_t *__restrict__ x,
-                                                            const uint16_t *__restrict__ W,
-                                                            const uint16_t *__restrict__ PE,
-                                                            uint16_t *__restrict__ out, int T, int ncmp, int npad)
+__device__ __forceinline__ void compress_mfma_tile(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W,
+                                                   const uint16_t *__restrict__ PE, uint16_t *__restrict__ out,
+                                                   int T, int ncmp, int npad, int bh, int tile,
+                                                   CompressMfmaLds<DIM> &sm)
 {
     constexpr int NT = DIM / 64;                 // 32-channel tiles per wave
     constexpr int L = 32 * DIM;
     constexpr int BTASK = DIM * (kMK / 8) / kThreads;
-    __shared__ CompressMfmaLds<DIM> sm;
-    const int bh = blockIdx.y, i0 = blockIdx.x * kMBlocks;
+    const int i0 = tile * kMBlocks;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rw = 32 * (wave & 1), cw = (wave >> 1) * (DIM / 2);
     const uint16_t *xs = x + (long)bh * T * DIM;
@@ -246,25 +247,62 @@ __global__ __launch_bounds__(kThreads) void k_compress_mfma(const uint16_t *__re
     }
 }
 
+// K and V of every (b, KV head) in one launch: grid.y 0 .. BH-1 take K
+// (d = DK), BH .. 2BH-1 take V (d = DV), so the two products share the chip.
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads) void k_compress_mfma_kv(const uint16_t *__restrict__ k,
+                                                               const uint16_t *__restrict__ v,
+                                                               const uint16_t *__restrict__ Wk,
+                                                               const uint16_t *__restrict__ PEk,
+                                                               const uint16_t *__restrict__ Wv,
+                                                               const uint16_t *__restrict__ PEv,
+                                                               uint16_t *__restrict__ ok, uint16_t *__restrict__ ov,
+                                                               int T, int ncmp, int npad, int BH)
+{
+    constexpr size_t SK = sizeof(CompressMfmaLds<DK>), SV = sizeof(CompressMfmaLds<DV>);
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SK > SV ? SK : SV];
+    const int y = blockIdx.y;
+    if (y < BH) {
+        if ((int)blockIdx.x * kMBlocks >= npad) return;
+        compress_mfma_tile<DK>(k, Wk, PEk, ok, T, ncmp, npad, y, blockIdx.x,
+                               *reinterpret_cast<CompressMfmaLds<DK> *>(smem));
+    } else {
+        if ((int)blockIdx.x * kMBlocks >= npad) return;
+        compress_mfma_tile<DV>(v, Wv, PEv, ov, T, ncmp, npad, y - BH, blockIdx.x,
+                               *reinterpret_cast<CompressMfmaLds<DV> *>(smem));
+    }
+}
+
 }  // namespace
 
 bool compress_bf16_supported(const Dims &d) { return d.dtype == NSA_BF16; }
 
-hipError_t launch_compress_bf16(const Dims &d, const void *x, const void *W, const void *PE, void *out, int dim,
-                                hipStream_t s)
+hipError_t launch_compress_bf16(const Dims &d, const void *k, const void *v, const void *Wk, const void *PEk,
+                                const void *Wv, const void *PEv, void *ok, void *ov, hipStream_t s)
 {
-    const dim3 mgrid((d.npad + kMBlocks - 1) / kMBlocks, d.B * d.Hkv);
-    const uint16_t *xs = (const uint16_t *)x, *Ws = (const uint16_t *)W, *ps = (const uint16_t *)PE;
-    uint16_t *o = (uint16_t *)out;
-    if (dim == 192) {
-        hipLaunchKernelGGL(k_compress_mfma<192>, mgrid, dim3(kThreads), 0, s, xs, Ws, ps, o, d.T, d.ncmp, d.npad);
-    } else if (dim == 128) {
-        hipLaunchKernelGGL(k_compress_mfma<128>, mgrid, dim3(kThreads), 0, s, xs, Ws, ps, o, d.T, d.ncmp, d.npad);
-    } else if (dim == 64) {
-        hipLaunchKernelGGL(k_compress_mfma<64>, mgrid, dim3(kThreads), 0, s, xs, Ws, ps, o, d.T, d.ncmp, d.npad);
+    const int BH = d.B * d.Hkv;
+    const dim3 mgrid((d.npad + kMBlocks - 1) / kMBlocks, 2 * BH);
+    const uint16_t *ks = (const uint16_t *)k, *vs = (const uint16_t *)v;
+    const uint16_t *wk = (const uint16_t *)Wk, *pk = (const uint16_t *)PEk, *wv = (const uint16_t *)Wv,
+                   *pv = (const uint16_t *)PEv;
+    uint16_t *oks = (uint16_t *)ok, *ovs = (uint16_t *)ov;
+    if (d.dk == 192 && d.dv == 128) {
+        hipLaunchKernelGGL((k_compress_mfma_kv<192, 128>), mgrid, dim3(kThreads), 0, s, ks, vs, wk, pk, wv, pv, oks,
+                           ovs, d.T, d.ncmp, d.npad, BH);
+    } else if (d.dk == 128 && d.dv == 128) {
+        hipLaunchKernelGGL((k_compress_mfma_kv<128, 128>), mgrid, dim3(kThreads), 0, s, ks, vs, wk, pk, wv, pv, oks,
+                           ovs, d.T, d.ncmp, d.npad, BH);
+    } else if (d.dk == 64 && d.dv == 64) {
+        hipLaunchKernelGGL((k_compress_mfma_kv<64, 64>), mgrid, dim3(kThreads), 0, s, ks, vs, wk, pk, wv, pv, oks,
+                           ovs, d.T, d.ncmp, d.npad, BH);
     } else {
-        dim3 grid((d.npad + kTI - 1) / kTI, (dim + kTC - 1) / kTC, d.B * d.Hkv);
-        hipLaunchKernelGGL(k_compress_bf16, grid, dim3(kThreads), 0, s, xs, Ws, ps, o, d.T, dim, d.ncmp, d.npad);
+        // other widths: the vector-ALU kernel, one launch per tensor
+        for (int u = 0; u < 2; u++) {
+            const int dim = u == 0 ? d.dk : d.dv;
+            dim3 grid((d.npad + kTI - 1) / kTI, (dim + kTC - 1) / kTC, BH);
+            hipLaunchKernelGGL(k_compress_bf16, grid, dim3(kThreads), 0, s, u == 0 ? ks : vs, u == 0 ? wk : wv,
+                               u == 0 ? pk : pv, u == 0 ? oks : ovs, d.T, dim, d.ncmp, d.npad);
+        }
     }
     return hipGetLastError();
 }

@@ -153,8 +153,7 @@ nsa_status nsa_compress_kv(const nsa_config *cfg, const void *k, const void *v, 
         if (!aligned16(p)) return NSA_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
     if (compress_bf16_supported(d)) {
-        NSA_TRY(launch_compress_bf16(d, k, w_ck, pe_k, cmp_k, d.dk, s));
-        NSA_TRY(launch_compress_bf16(d, v, w_cv, pe_v, cmp_v, d.dv, s));
+        NSA_TRY(launch_compress_bf16(d, k, v, w_ck, pe_k, w_cv, pe_v, cmp_k, cmp_v, s));
         return NSA_OK;
     }
     NSA_TRY(launch_compress_generic(d, k, w_ck, pe_k, cmp_k, d.dk, s));

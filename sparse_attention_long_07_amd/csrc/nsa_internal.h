@@ -104,8 +104,8 @@ hipError_t launch_sparse_generic(const RowArgs &a, hipStream_t s);
 
 // Token compression for bf16 storage on the vector ALUs (bf16 dot products).
 bool compress_bf16_supported(const Dims &d);
-hipError_t launch_compress_bf16(const Dims &d, const void *x, const void *W, const void *PE, void *out, int dim,
-                                hipStream_t s);
+hipError_t launch_compress_bf16(const Dims &d, const void *k, const void *v, const void *Wk, const void *PEk,
+                                const void *Wv, const void *PEv, void *ok, void *ov, hipStream_t s);
 
 // Matrix-core kernels (bf16 storage, G = 16; prefill rows only).
 bool cmp_attn_mfma_supported(const Dims &d);
