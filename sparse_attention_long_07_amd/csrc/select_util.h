@@ -129,6 +129,9 @@ __device__ __forceinline__ uint32_t ordered_key(float v)
 // Requires at least k valid lanes.  32 bisection steps on wave-uniform bounds.
 __device__ __forceinline__ uint32_t wave_kth_largest(uint32_t key, bool valid, int k)
 {
+    // k is the same on every lane; saying so keeps the bounds and the loop in
+    // scalar registers (otherwise every step runs as a divergent vector loop)
+    k = __builtin_amdgcn_readfirstlane(k);
     uint32_t lo = 0u, hi = 0xffffffffu;
     while (lo < hi) {
         const uint32_t mid = lo + (uint32_t)(((uint64_t)hi - lo + 1u) >> 1);
@@ -143,6 +146,8 @@ __device__ __forceinline__ uint32_t wave_kth_largest(uint32_t key, bool valid, i
 __device__ __forceinline__ void wave_select_topn_fast(const float *S, int jcur, int n, int32_t *out, int lane,
                                                       uint2 *cand)
 {
+    jcur = __builtin_amdgcn_readfirstlane(jcur);   // one row per wavefront: uniform
+    n = __builtin_amdgcn_readfirstlane(n);
     const int ncand = jcur + 1;
     const int nforced = jcur == 0 ? 1 : (jcur == 1 ? 2 : 3);
     const int k = n - nforced;
