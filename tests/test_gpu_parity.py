@@ -160,6 +160,13 @@ def test_decode_parity(name, s, seq):
     err = np.abs(np64(o) - ref2["o"]).max()
     say("  max|o-o_ref| = %.3g" % err)
     assert err <= out_tol(s, ref2["o"])
+    # the oracle's block lists injected: the selection is skipped, the rest is the same
+    idx_ref = torch.from_numpy(np.ascontiguousarray(ref["idx"]).astype(np.int32)).cuda()
+    o3 = nsa.decode_step(s, x["seq_lens"], x["q"], x["k"], x["v"], kc_d, vc_d, x["w_g"], x["b_g"], idx_in=idx_ref)
+    torch.cuda.synchronize()
+    err3 = np.abs(np64(o3) - ref["o"]).max()
+    say("  idx_in: max|o-o_ref| = %.3g" % err3)
+    assert err3 <= out_tol(s, ref["o"])
     # decode row == prefill row of the same tokens (GPU against GPU)
     b = 1
     L = seq[b]
