@@ -38,6 +38,13 @@ namespace {
 constexpr int kPos = 16;     // query positions per workgroup (2 per wave)
 constexpr int kTile = 64;    // compressed keys per LDS tile
 constexpr int kThreads = 512;
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSgValu = 0x402;      // VALU, transcendental included
+constexpr int kSgTrans = 0x400;
+constexpr int kSgMfma = 0x008;
+constexpr int kSgVmemRead = 0x020;
+constexpr int kSgDsRead = 0x100;
+constexpr int kSgDsWrite = 0x200;
 
 template <int DK, int DV>
 struct CmpLds {
@@ -127,6 +134,10 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
     const int nfull = tw0 + 1 < d.T ? n_visible(tw0) / kTile : 0;
     const int ntw = tw0 < d.T ? (n_visible(min(tw0 + 1, d.T - 1)) + kTile - 1) / kTile : 0;
     const int ntiles = (n_visible(min(pos0 + kPos - 1, d.T - 1)) + kTile - 1) / kTile;
+    // Tiles below nmain are unmasked for every wave and have a successor to
+    // prefetch: their loop bodies are straight-line code, so the exponentials
+    // of one 32-key M-tile can be scheduled under the matrix work of the next.
+    const int nmain = pos0 + kPos - 1 < d.T ? min(n_visible(pos0) / kTile, ntiles - 1) : 0;
     const float sl2 = d.scale * kLog2e;
 
     bf16x8 qf[KSTEPS];
@@ -201,6 +212,20 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
 
     // ---- pass 1: log-sum-exp of every row (log2 domain)
     float m = -INFINITY, l = 0.f;
+    // online update with the 16 logits one lane holds of a 32-key M-tile
+    // (masked keys already -inf); a tile of -inf leaves m = -inf, l = 0 as is
+    auto lse_update = [&](const f32x16 &acc) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; r++) mx = fmaxf(mx, acc[r]);
+        const float mn = fmaxf(m, mx * sl2);
+        const float ms = mn == -INFINITY ? 0.f : mn;   // rows with nothing visible yet
+        float sum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r++) sum += fast_exp2(__builtin_fmaf(acc[r], sl2, -ms));
+        l = l * fast_exp2(m - ms) + sum;
+        m = mn;
+    };
     // one tile; `masked` (wave-uniform) applies the causal limit
     auto pass1_tile = [&](int c, bool masked) {
         const int buf = c & 1;
@@ -212,16 +237,7 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
 #pragma unroll
                 for (int r = 0; r < 16; r++) acc[r] = kb + r < nv ? acc[r] : -INFINITY;
             }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < 16; r++) mx = fmaxf(mx, acc[r]);
-            const float mn = fmaxf(m, mx * sl2);
-            const float ms = mn == -INFINITY ? 0.f : mn;   // rows with nothing visible yet
-            float sum = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; r++) sum += fast_exp2(__builtin_fmaf(acc[r], sl2, -ms));
-            l = l * fast_exp2(m - ms) + sum;
-            m = mn;
+            lse_update(acc);
         }
     };
     if (ntiles > 0) {
@@ -229,7 +245,38 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
         store_k(0);
         lds_barrier();
     }
-    for (int c = 0; c < ntiles; c++) {
+    // Main tiles run software-pipelined: the softmax of the previous tile's
+    // second M-tile is issued under this tile's first 32x32 product chain and
+    // the first M-tile's under the second chain.  The updates keep key order.
+    int c1 = 0;
+    {
+        f32x16 pend;
+#pragma unroll
+        for (int r = 0; r < 16; r++) pend[r] = -INFINITY;
+        for (; c1 < nmain; c1++) {
+            load_k(c1 + 1);
+            const f32x16 a0 = logits(c1 & 1, 0);
+            lse_update(pend);
+            const f32x16 a1 = logits(c1 & 1, 1);
+            lse_update(a0);
+            store_k((c1 + 1) & 1);
+            lds_barrier();
+            pend = a1;
+            // issue order: the prefetch loads, three LDS fragment reads
+            // ahead, then per product the product, the next read and a
+            // share of the softmax
+            __builtin_amdgcn_sched_group_barrier(kSgVmemRead, KLD, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgDsRead, 3, 0);
+#pragma unroll
+            for (int i = 0; i < 2 * KSTEPS; i++) {
+                __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSgValu, 6, 0);
+            }
+        }
+        lse_update(pend);
+    }
+    for (int c = c1; c < ntiles; c++) {
         if (c + 1 < ntiles) load_k(c + 1);
         if (c < ntw) pass1_tile(c, c >= nfull);
         if (c + 1 < ntiles) store_k((c + 1) & 1);
@@ -248,37 +295,51 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
     for (int dt = 0; dt < DT; dt++)
 #pragma unroll
         for (int r = 0; r < 16; r++) oacc[dt][r] = 0.f;
+    // probabilities of one lane's 16 keys of M-tile `mt`
+    auto probs = [&](const f32x16 &acc, int kb, bool masked, float *p) {
+#pragma unroll
+        for (int r = 0; r < 16; r++) p[r] = fast_exp2(__builtin_fmaf(acc[r], sl2, -lse2));
+        if (masked) {
+#pragma unroll
+            for (int r = 0; r < 16; r++) p[r] = kb + r < nv ? p[r] : 0.f;
+        }
+    };
+    auto pv = [&](int buf, int mt, const float *p) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; s2++) {
+            const bf16x8 pb = pack8(&p[8 * s2]);
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) oacc[dt] = mfma32(vt_frag(buf, dt, mt, s2), pb, oacc[dt]);
+        }
+    };
+    auto pv_packed = [&](int buf, int mt, const bf16x8 *pb) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; s2++)
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) oacc[dt] = mfma32(vt_frag(buf, dt, mt, s2), pb[s2], oacc[dt]);
+    };
+    // the M-tile's block partials of this row into the score buffer
+    auto importance = [&](int buf, int mt, const float *p) {
+        const int grp = 2 * mt + h;
+        float *dst = sm.sc[buf];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const float *q4 = &p[4 * u];
+            float v = __builtin_fmaf(2.f, q4[0] + q4[1] + q4[2], q4[3]);
+            if (u) v += q4[-1];
+            dst[sc_off(pw, 4 * grp + u, head)] = v;
+        }
+        dst[sc_off(pw, 16 + grp, head)] = p[15];
+    };
     auto pass2_tile = [&](int c, bool masked) {
         const int buf = c & 1;
 #pragma unroll
         for (int mt = 0; mt < 2; mt++) {
             const f32x16 acc = logits(buf, mt);
-            const int kb = c * kTile + 32 * mt + 16 * h;
             float p[16];
-#pragma unroll
-            for (int r = 0; r < 16; r++) p[r] = fast_exp2(__builtin_fmaf(acc[r], sl2, -lse2));
-            if (masked) {
-#pragma unroll
-                for (int r = 0; r < 16; r++) p[r] = kb + r < nv ? p[r] : 0.f;
-            }
-            if (WITH_V) {
-#pragma unroll
-                for (int s2 = 0; s2 < 2; s2++) {
-                    const bf16x8 pb = pack8(&p[8 * s2]);
-#pragma unroll
-                    for (int dt = 0; dt < DT; dt++) oacc[dt] = mfma32(vt_frag(buf, dt, mt, s2), pb, oacc[dt]);
-                }
-            }
-            const int grp = 2 * mt + h;
-            float *dst = sm.sc[buf];
-#pragma unroll
-            for (int u = 0; u < 4; u++) {
-                const float *q4 = &p[4 * u];
-                float v = __builtin_fmaf(2.f, q4[0] + q4[1] + q4[2], q4[3]);
-                if (u) v += q4[-1];
-                dst[sc_off(pw, 4 * grp + u, head)] = v;
-            }
-            dst[sc_off(pw, 16 + grp, head)] = p[15];
+            probs(acc, c * kTile + 32 * mt + 16 * h, masked, p);
+            if (WITH_V) pv(buf, mt, p);
+            importance(buf, mt, p);
         }
     };
     float carry = 0.f;   // head-summed weight-1 share of the previous tile's last key
@@ -293,26 +354,8 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
         if (WITH_V) store_vt(0);
         lds_barrier();
     }
-    for (int c = 0; c < ntiles; c++) {
-        if (c + 1 < ntiles) {
-            load_k(c + 1);
-            if (WITH_V) load_v(c + 1);
-        }
-        if (c < ntw) {
-            pass2_tile(c, c >= nfull);
-        } else {
-            // nothing visible to this wave in the tile: its rows contribute zero
-#pragma unroll
-            for (int jj = 2 * h; jj < 20; jj += 4) {
-                sm.sc[c & 1][sc_off(pw, jj, head)] = 0.f;
-                sm.sc[c & 1][sc_off(pw, jj + 1, head)] = 0.f;
-            }
-        }
-        if (c + 1 < ntiles) {
-            store_k((c + 1) & 1);
-            if (WITH_V) store_vt((c + 1) & 1);
-        }
-        lds_barrier();
+    // the reducers' head sums of tile c (after the barrier that follows it)
+    auto reduce_tile = [&](int c) {
         if (reducer) {
             // sum of the 16 heads of one entry: four 16-byte reads
             const float *scb = sm.sc[c & 1];
@@ -332,6 +375,84 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
             const int j = 16 * c + rj;
             if (tr < d.T && j <= tr / 64) scores[(long)tr * d.nb + j] = S;
         }
+    };
+    int c2 = 0;
+    for (; c2 < nmain; c2++) {
+        load_k(c2 + 1);
+        if (WITH_V) load_v(c2 + 1);
+        // Four scheduling regions per tile: the first logit chain; the second
+        // chain under the first M-tile's exponentials and importance sums;
+        // the first PV chain under the second M-tile's; the second PV chain.
+        // Only the packed bf16 probabilities stay live into the PV chains.
+        const int buf = c2 & 1;
+        const f32x16 s0 = logits(buf, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        const f32x16 s1 = logits(buf, 1);
+        bf16x8 pb0[2], pb1[2];
+        {
+            float p0[16];
+            probs(s0, 0, false, p0);
+            pb0[0] = pack8(&p0[0]);
+            pb0[1] = pack8(&p0[8]);
+            importance(buf, 0, p0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 3, 0);
+#pragma unroll
+        for (int i = 0; i < KSTEPS; i++) {
+            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgValu, 5, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // the next tile's buffer is free all iteration: storing the prefetch
+        // here ends the staging registers' live range before the PV chains
+        store_k((c2 + 1) & 1);
+        if (WITH_V) store_vt((c2 + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (WITH_V) pv_packed(buf, 0, pb0);
+        {
+            float p1[16];
+            probs(s1, 0, false, p1);
+            pb1[0] = pack8(&p1[0]);
+            pb1[1] = pack8(&p1[8]);
+            importance(buf, 1, p1);
+        }
+        if constexpr (WITH_V) {
+            __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
+#pragma unroll
+            for (int i = 0; i < 2 * DT; i++) {
+                __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(kSgValu, 7, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            pv_packed(buf, 1, pb1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        lds_barrier();
+        reduce_tile(c2);
+    }
+    for (int c = c2; c < ntiles; c++) {
+        if (c + 1 < ntiles) {
+            load_k(c + 1);
+            if (WITH_V) load_v(c + 1);
+        }
+        if (c < ntw) {
+            pass2_tile(c, c >= nfull);
+        } else {
+            // nothing visible to this wave in the tile: its rows contribute zero
+#pragma unroll
+            for (int jj = 2 * h; jj < 20; jj += 4) {
+                sm.sc[c & 1][sc_off(pw, jj, head)] = 0.f;
+                sm.sc[c & 1][sc_off(pw, jj + 1, head)] = 0.f;
+            }
+        }
+        if (c + 1 < ntiles) {
+            store_k((c + 1) & 1);
+            if (WITH_V) store_vt((c + 1) & 1);
+        }
+        lds_barrier();
+        reduce_tile(c);
     }
     // the last key of the final tile also reaches block 16*ntiles
     if (reducer && rj == 0) {
