@@ -52,22 +52,17 @@ struct CmpLds {
     static constexpr int VS = DV + 32;     // bf16 per V row: rows 64 B apart in the banks
     uint16_t k[2][kTile * KS];
     uint16_t v[2][kTile * VS];             // V key-major; V^T fragments come from transpose reads
-    // Per position and head: the tile's 16 block partials (entry 4*grp + u for
-    // block u of 16-key group grp) and the weight-1 shares of each group's last
-    // key in the next block (entries 16..19).  Laid out by sc_off.
-    float sc[2][kPos * 416];
 };
 
-// Float offset of (position, entry, head) in a score buffer.  Entries are 16
-// heads (64 B), padded by 16 floats after every 4 entries, positions 416
-// floats apart, and the four 4-head chunks of an entry rotated by entry/4.
-// Both the per-lane scalar writes (lanes: 16 heads x 2 positions x 2 groups)
-// and the reducer's 16-byte reads (16 lanes: the 16 entries of a position)
-// then touch every bank at most once.
-__device__ __forceinline__ int sc_off(int pos, int jj, int head)
+// Sum over the 16 lanes of each DPP row (row rotations by 8, 4, 2, 1).  Every
+// step adds two values in either order, so all 16 lanes end with the same bits.
+__device__ __forceinline__ float row_sum16(float x)
 {
-    const int q = jj >> 2;
-    return pos * 416 + jj * 16 + q * 16 + ((((head >> 2) + q) & 3) << 2) + (head & 3);
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+    return x;
 }
 
 // LDS row of key k (0..31) inside a 32-key M-tile.  MFMA output row i sits in
@@ -318,18 +313,45 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
 #pragma unroll
             for (int dt = 0; dt < DT; dt++) oacc[dt] = mfma32(vt_frag(buf, dt, mt, s2), pb[s2], oacc[dt]);
     };
-    // the M-tile's block partials of this row into the score buffer
-    auto importance = [&](int buf, int mt, const float *p) {
-        const int grp = 2 * mt + h;
-        float *dst = sm.sc[buf];
+    // Block importance of M-tile `mt` of tile c.  The 16 lanes of a DPP row
+    // hold the 16 heads of one position for the same 16 keys (group
+    // grp = 2*mt + h of the tile), so the head sum is a row reduction.  Block
+    // 16c + 4*grp + u takes keys 4u-1 .. 4u+3 of the group with weights
+    // 1,2,2,2,1; key -1 is the previous group's last key, which lives in the
+    // other lane half (h = 1) or, for h = 0, in `carry` from the previous
+    // M-tile.  Lanes (l % 16) < 4 store the group's four blocks.
+    float carry = 0.f;
+    float *srow = a.scores + ((long)bg * a.R + t) * d.nb;
+    const int tb = t / 64;   // last causal block of this row
+    // The stores go through a buffer resource over the workgroup's 16 score
+    // rows: a lane with nothing to store gets an offset past the range, which
+    // the hardware drops, so no branch splits the scheduled regions.
+    const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+        a.scores + ((long)bg * a.R + pos0) * d.nb, 0, kPos * d.nb * 4, 0x00020000);
+    constexpr int kDropOffset = 0x7fffffff;
+    auto importance = [&](int c, int mt, const float *p) {
+        float v[4];
 #pragma unroll
         for (int u = 0; u < 4; u++) {
             const float *q4 = &p[4 * u];
-            float v = __builtin_fmaf(2.f, q4[0] + q4[1] + q4[2], q4[3]);
-            if (u) v += q4[-1];
-            dst[sc_off(pw, 4 * grp + u, head)] = v;
+            v[u] = __builtin_fmaf(2.f, q4[0] + q4[1] + q4[2], q4[3]);
+            if (u) v[u] += q4[-1];
+            v[u] = row_sum16(v[u]);
         }
-        dst[sc_off(pw, 16 + grp, head)] = p[15];
+        const float last = row_sum16(p[15]);
+        const float other = __shfl_xor(last, 32, 64);
+        v[0] += h ? other : carry;
+        carry = other;   // kept by the h = 0 lanes: the h = 1 group's last key
+        const int u = lane & 15;
+        const int j = 16 * c + 4 * (2 * mt + h) + u;
+        // the empty asm keeps the sums materialised, so the selects below
+        // stay v_cndmask instead of becoming branches
+#pragma unroll
+        for (int q = 0; q < 4; q++) asm volatile("" : "+v"(v[q]));
+        const float lo = (u & 1) ? v[1] : v[0], hi = (u & 1) ? v[3] : v[2];
+        const float val = (u & 2) ? hi : lo;
+        const int off = u < 4 && live && j <= tb ? (pw * d.nb + j) * 4 : kDropOffset;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), srsrc, off, 0, 0);
     };
     auto pass2_tile = [&](int c, bool masked) {
         const int buf = c & 1;
@@ -339,14 +361,9 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
             float p[16];
             probs(acc, c * kTile + 32 * mt + 16 * h, masked, p);
             if (WITH_V) pv(buf, mt, p);
-            importance(buf, mt, p);
+            importance(c, mt, p);
         }
     };
-    float carry = 0.f;   // head-summed weight-1 share of the previous tile's last key
-    float *scores = a.scores + (long)bg * a.R * d.nb;
-    const bool reducer = tid < kPos * 16;
-    const int rp = (tid >> 4) & (kPos - 1), rj = tid & 15;   // reducer: position, block of the tile
-    const int tr = pos0 + rp;
     if (ntiles > 0) {
         load_k(0);
         if (WITH_V) load_v(0);
@@ -354,28 +371,6 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
         if (WITH_V) store_vt(0);
         lds_barrier();
     }
-    // the reducers' head sums of tile c (after the barrier that follows it)
-    auto reduce_tile = [&](int c) {
-        if (reducer) {
-            // sum of the 16 heads of one entry: four 16-byte reads
-            const float *scb = sm.sc[c & 1];
-            auto head_sum = [&](int jj) {
-                float S = 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const f32x4 v = *(const f32x4 *)&scb[sc_off(rp, jj, 4 * i)];
-                    S += (v[0] + v[1]) + (v[2] + v[3]);
-                }
-                return S;
-            };
-            const int grp = rj >> 2, u = rj & 3;
-            float S = head_sum(rj);
-            if (u == 0) S += grp ? head_sum(16 + grp - 1) : carry;
-            if (rj == 0) carry = head_sum(19);
-            const int j = 16 * c + rj;
-            if (tr < d.T && j <= tr / 64) scores[(long)tr * d.nb + j] = S;
-        }
-    };
     int c2 = 0;
     for (; c2 < nmain; c2++) {
         load_k(c2 + 1);
@@ -394,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
             probs(s0, 0, false, p0);
             pb0[0] = pack8(&p0[0]);
             pb0[1] = pack8(&p0[8]);
-            importance(buf, 0, p0);
+            importance(c2, 0, p0);
         }
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, 3, 0);
 #pragma unroll
@@ -415,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
             probs(s1, 0, false, p1);
             pb1[0] = pack8(&p1[0]);
             pb1[1] = pack8(&p1[8]);
-            importance(buf, 1, p1);
+            importance(c2, 1, p1);
         }
         if constexpr (WITH_V) {
             __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
@@ -430,35 +425,23 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
             __builtin_amdgcn_sched_barrier(0);
         }
         lds_barrier();
-        reduce_tile(c2);
     }
     for (int c = c2; c < ntiles; c++) {
         if (c + 1 < ntiles) {
             load_k(c + 1);
             if (WITH_V) load_v(c + 1);
         }
-        if (c < ntw) {
-            pass2_tile(c, c >= nfull);
-        } else {
-            // nothing visible to this wave in the tile: its rows contribute zero
-#pragma unroll
-            for (int jj = 2 * h; jj < 20; jj += 4) {
-                sm.sc[c & 1][sc_off(pw, jj, head)] = 0.f;
-                sm.sc[c & 1][sc_off(pw, jj + 1, head)] = 0.f;
-            }
-        }
+        if (c < ntw) pass2_tile(c, c >= nfull);
         if (c + 1 < ntiles) {
             store_k((c + 1) & 1);
             if (WITH_V) store_vt((c + 1) & 1);
         }
         lds_barrier();
-        reduce_tile(c);
     }
-    // the last key of the final tile also reaches block 16*ntiles
-    if (reducer && rj == 0) {
-        const int j = 16 * ntiles;
-        if (tr < d.T && j <= tr / 64) scores[(long)tr * d.nb + j] = carry;
-    }
+    // The last key of the wave's final tile also reaches block 16*ntw, the
+    // only later block a row of this wave can see (its first key is not
+    // visible to it).
+    if (h == 0 && (lane & 15) == 0 && live && 16 * ntw <= tb) srow[16 * ntw] = carry;
 
     if (WITH_V && live) {
         uint16_t *orow = (uint16_t *)a.ocmp + (((long)b * a.R + t) * d.Hq + g * 16 + head) * DV;
