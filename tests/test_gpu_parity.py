@@ -270,6 +270,8 @@ STAGE = [
     ("bf16_T2000_g16", NSAShape(1, 2000, 2, 16, 192, 128), False),
     ("bf16_T1111_g16_d64", NSAShape(1, 1111, 1, 16, 64, 64, n=5, w=200), False),
     ("bf16_T700_g16_d128_B2", NSAShape(2, 700, 1, 16, 128, 128, n=4, w=64), True),
+    # long enough that S2 runs its unmasked main tiles (t >= 1039) before the masked tail
+    ("bf16_T2100_g16_d128_B2", NSAShape(2, 2100, 1, 16, 128, 128, n=8, w=256), False),
     ("fp32_T1024", NSAShape(1, 1024, 1, 4, 64, 64, FP32), True),
 ]
 
@@ -295,6 +297,11 @@ def test_stage_parity(name, s, scaled):
     causal = np.arange(s.nb)[None, None, None, :] <= jc
     causal = np.broadcast_to(causal, ref["scores"].shape)
     np.testing.assert_allclose(np64(sc)[causal], ref["scores"][causal], rtol=1e-4, atol=2e-6)
+    # the scores-only S2 (the block-selection call) computes the same scores bit for bit
+    _, sc_only = nsa.compressed_attention(s, x["q"], torch.from_numpy(kc).to(dt).cuda())
+    torch.cuda.synchronize()
+    causal_t = torch.from_numpy(np.ascontiguousarray(causal)).cuda()
+    assert torch.equal(sc_only[causal_t], sc[causal_t])
     # S3 with the oracle's scores (stored in fp32)
     sref = torch.from_numpy(np.where(causal, ref["scores"], -np.inf).astype(np.float32)).cuda()
     idx = nsa.select_topn(s, sref)
