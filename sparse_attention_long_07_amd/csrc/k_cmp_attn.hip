@@ -135,19 +135,6 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
     const int nmain = pos0 + kPos - 1 < d.T ? min(n_visible(pos0) / kTile, ntiles - 1) : 0;
     const float sl2 = d.scale * kLog2e;
 
-    bf16x8 qf[KSTEPS];
-    {
-        const uint16_t *qr = (const uint16_t *)a.q + (long)b * a.q_sb + (long)t * a.q_sr +
-                             (long)(g * 16 + head) * DK + 8 * h;
-        const u32x4 z = {0, 0, 0, 0};
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; kk++) qf[kk] = as_bf16x8(live ? ld16(qr + 16 * kk) : z);
-    }
-    // Let the query loads land before the tile loop: the compiler cannot tell
-    // them from the next tile's prefetch, and would otherwise wait for every
-    // outstanding load (the prefetch included) at the first matrix op of
-    // each tile.
-    wait_vmem_all();
     const uint16_t *kc = (const uint16_t *)a.kc + (long)bg * d.npad * DK;
     const uint16_t *vc = (const uint16_t *)a.vc + (long)bg * d.npad * DV;
 
@@ -184,6 +171,21 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
             if (VTASKS % kThreads == 0 || task < VTASKS) st16(&sm.v[buf][key * L::VS + ch * 8], vreg[u]);
         }
     };
+    // the first K tile is in flight while the query loads land
+    if (ntiles > 0) load_k(0);
+    bf16x8 qf[KSTEPS];
+    {
+        const uint16_t *qr = (const uint16_t *)a.q + (long)b * a.q_sb + (long)t * a.q_sr +
+                             (long)(g * 16 + head) * DK + 8 * h;
+        const u32x4 z = {0, 0, 0, 0};
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; kk++) qf[kk] = as_bf16x8(live ? ld16(qr + 16 * kk) : z);
+    }
+    // Let the query loads land before the tile loop: the compiler cannot tell
+    // them from the next tile's prefetch, and would otherwise wait for every
+    // outstanding load (the prefetch included) at the first matrix op of
+    // each tile.
+    wait_vmem_all();
     // V^T fragment of the PV product: dv rows 32*dt + (lane % 32), keys
     // kb .. kb+7 with kb = 32*mt + 16*(lane/32) + 8*s2 (the 8 keys this lane's
     // half of the 16-key step holds), read as two transposed 4-key pieces.
@@ -236,7 +238,6 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
         }
     };
     if (ntiles > 0) {
-        load_k(0);
         store_k(0);
         lds_barrier();
     }

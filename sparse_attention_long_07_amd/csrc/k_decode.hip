@@ -394,11 +394,7 @@ __global__ __launch_bounds__(kTailThreads) void k_dec_tail(DecArgs A)
             float z = 0.f;
             for (int ch = part; ch < DK / 8; ch += 16) {
                 const u32x4 wv = ld16(wr + 8 * ch), qv = ld16(qr + 8 * ch);
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    z += __uint_as_float(wv[e] << 16) * __uint_as_float(qv[e] << 16);
-                    z += __uint_as_float(wv[e] & 0xffff0000u) * __uint_as_float(qv[e] & 0xffff0000u);
-                }
+                z = dot8_bf16(wv, qv, z);
             }
 #pragma unroll
             for (int off = 8; off > 0; off >>= 1) z += __shfl_xor(z, off, 16);

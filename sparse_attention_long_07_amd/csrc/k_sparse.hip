@@ -155,44 +155,6 @@ __global__ __launch_bounds__(kWThreads) void k_window_mfma(RowArgs a, int ntp)
     const bool both = tw1 < d.T;
     const float sl2 = d.scale * kLog2e;
 
-    bf16x8 qf[KSTEPS];
-    const uint16_t *qr = (const uint16_t *)a.q + (long)b * a.q_sb + (long)t * a.q_sr +
-                         (long)(g * 16 + head) * DK + 8 * h;
-    {
-        const u32x4 z = {0, 0, 0, 0};
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; kk++) qf[kk] = as_bf16x8(live ? ld16(qr + 16 * kk) : z);
-    }
-    // gates of this row: each lane half holds half of the dimensions
-    float gate[3] = {0.f, 0.f, 0.f};
-    if (live) {
-        const uint16_t *wr = (const uint16_t *)a.wg + (long)(g * 16 + head) * 3 * DK + 8 * h;
-#pragma unroll
-        for (int c = 0; c < 3; c++) {
-            float z = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS; kk++) {
-                const u32x4 wv = ld16(wr + c * DK + 16 * kk);
-                const u32x4 qv = ld16(qr + 16 * kk);
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    z += __uint_as_float(wv[e] << 16) * __uint_as_float(qv[e] << 16);
-                    z += __uint_as_float(wv[e] & 0xffff0000u) * __uint_as_float(qv[e] & 0xffff0000u);
-                }
-            }
-            gate[c] = z;
-        }
-    }
-#pragma unroll
-    for (int c = 0; c < 3; c++) {
-        gate[c] += __shfl_xor(gate[c], 32, 64);
-        const uint16_t *bgp = (const uint16_t *)a.bg + (long)(g * 16 + head) * 3 + c;
-        gate[c] = live ? sigmoid(gate[c] + __uint_as_float((uint32_t)*bgp << 16)) : 0.f;
-    }
-
-    // let the query and gate loads land before the tile loop (see the
-    // compressed-attention kernel: otherwise every tile waits for its prefetch)
-    wait_vmem_all();
     const uint16_t *kg = (const uint16_t *)a.k + (long)bg * d.T * DK;
     const uint16_t *vg = (const uint16_t *)a.v + (long)bg * d.T * DV;
     u32x4 kreg[KLD], vreg[VTK][2];
@@ -239,6 +201,43 @@ __global__ __launch_bounds__(kWThreads) void k_window_mfma(RowArgs a, int ntp)
         }
     };
 
+    // the first K/V tile is in flight while the query and gate loads land
+    load_tile(c_first);
+
+    bf16x8 qf[KSTEPS];
+    const uint16_t *qr = (const uint16_t *)a.q + (long)b * a.q_sb + (long)t * a.q_sr +
+                         (long)(g * 16 + head) * DK + 8 * h;
+    {
+        const u32x4 z = {0, 0, 0, 0};
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; kk++) qf[kk] = as_bf16x8(live ? ld16(qr + 16 * kk) : z);
+    }
+    // gates of this row: each lane half holds half of the dimensions
+    float gate[3] = {0.f, 0.f, 0.f};
+    if (live) {
+        const uint16_t *wr = (const uint16_t *)a.wg + (long)(g * 16 + head) * 3 * DK + 8 * h;
+#pragma unroll
+        for (int c = 0; c < 3; c++) {
+            float z = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; kk++) {
+                const u32x4 wv = ld16(wr + c * DK + 16 * kk);
+                const u32x4 qv = ld16(qr + 16 * kk);
+                z = dot8_bf16(wv, qv, z);
+            }
+            gate[c] = z;
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 3; c++) {
+        gate[c] += __shfl_xor(gate[c], 32, 64);
+        const uint16_t *bgp = (const uint16_t *)a.bg + (long)(g * 16 + head) * 3 + c;
+        gate[c] = live ? sigmoid(gate[c] + __uint_as_float((uint32_t)*bgp << 16)) : 0.f;
+    }
+
+    // let the query and gate loads land before the tile loop (see the
+    // compressed-attention kernel: otherwise every tile waits for its prefetch)
+    wait_vmem_all();
     float m = -INFINITY, l = 0.f;
     f32x16 oacc[DT];
 #pragma unroll
@@ -297,7 +296,6 @@ __global__ __launch_bounds__(kWThreads) void k_window_mfma(RowArgs a, int ntp)
         }
     };
 
-    load_tile(c_first);
     store_tile(c_first & 1);
     lds_barrier();
     for (int c = c_first; c <= c_last; c++) {
@@ -362,6 +360,10 @@ __global__ __launch_bounds__(kThreads) void k_selected_mfma(RowArgs a, const uin
     const int jcur = t / kTile;
     const float sl2 = d.scale * kLog2e;
 
+    // the row's block list first: the first gathers wait on it, and its load
+    // then overlaps the query and gate loads
+    int jb = -1;
+    if (lane < d.n) jb = a.idx[((long)bg * a.R + t) * d.n + lane];
     const uint16_t *qr = (const uint16_t *)a.q + (long)b * a.q_sb + (long)t * a.q_sr + (long)(g * 16 + hd) * DK + 8 * q;
     bf16x8 qf[KS];
 #pragma unroll
@@ -374,11 +376,7 @@ __global__ __launch_bounds__(kThreads) void k_selected_mfma(RowArgs a, const uin
         for (int kk = 0; kk < KS; kk++) {
             const u32x4 wv = ld16(wr + 32 * kk);
             const u32x4 qv = ld16(qr + 32 * kk);
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                z += __uint_as_float(wv[e] << 16) * __uint_as_float(qv[e] << 16);
-                z += __uint_as_float(wv[e] & 0xffff0000u) * __uint_as_float(qv[e] & 0xffff0000u);
-            }
+            z = dot8_bf16(wv, qv, z);
         }
         z += __shfl_xor(z, 16, 64);
         z += __shfl_xor(z, 32, 64);
@@ -389,8 +387,6 @@ __global__ __launch_bounds__(kThreads) void k_selected_mfma(RowArgs a, const uin
     // the row's blocks: valid (0..jcur) and first occurrence only, compacted
     // into this wavefront's slot list
     __shared__ int blist[4][16];
-    int jb = -1;
-    if (lane < d.n) jb = a.idx[((long)bg * a.R + t) * d.n + lane];
     bool ok = jb >= 0 && jb <= jcur;
     for (int u = 0; u < 16; u++) {
         const int other = __shfl(jb, u, 64);

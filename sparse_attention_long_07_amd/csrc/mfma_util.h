@@ -57,6 +57,20 @@ __device__ __forceinline__ bf16x8 pack8(const float *p)
     return as_bf16x8(v);
 }
 
+// c + sum of the 8 products of two rows of 8 bf16 (4 packed words each), in
+// fp32: four v_dot2_f32_bf16, no unpacking of the halves.  Each word is copied
+// to a scalar before the bit cast: a bit cast applied to the vector element
+// expression itself reads the vector's first word for every element.
+__device__ __forceinline__ float dot8_bf16(u32x4 a, u32x4 b, float c)
+{
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const uint32_t x = a[e], y = b[e];
+        c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y), c, false);
+    }
+    return c;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
