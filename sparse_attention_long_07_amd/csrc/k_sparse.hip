@@ -102,8 +102,10 @@ template <int DK, int DV>
 struct WinLds {
     static constexpr int KS = DK + 8;
     static constexpr int VS = kTile + 8;
+    static constexpr int GS = 3 * DK + 8;   // bf16 per head's three gate rows (padded)
     uint16_t k[2][kTile * KS];
     uint16_t vt[2][DV * VS];
+    uint16_t wg[16 * GS];                   // gate weights of the group's 16 heads
 };
 
 // ---------------------------------------------------------------------------
@@ -212,32 +214,34 @@ __global__ __launch_bounds__(kWThreads) void k_window_mfma(RowArgs a, int ntp)
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; kk++) qf[kk] = as_bf16x8(live ? ld16(qr + 16 * kk) : z);
     }
-    // gates of this row: each lane half holds half of the dimensions
-    float gate[3] = {0.f, 0.f, 0.f};
-    if (live) {
-        const uint16_t *wr = (const uint16_t *)a.wg + (long)(g * 16 + head) * 3 * DK + 8 * h;
+    // The gate rows of the group's 16 heads (16 x 3 x DK bf16) are staged in
+    // LDS once per workgroup: every lane needs its head's three rows and 16
+    // lanes share each head, so per-lane loads would fetch each row 16 times.
+    constexpr int GCH = 16 * 3 * DK / 8;          // 16-byte chunks
+    constexpr int GLD = (GCH + kWThreads - 1) / kWThreads;
+    u32x4 greg[GLD];
+    {
+        const uint16_t *src = (const uint16_t *)a.wg + (long)g * 16 * 3 * DK;
 #pragma unroll
-        for (int c = 0; c < 3; c++) {
-            float z = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS; kk++) {
-                const u32x4 wv = ld16(wr + c * DK + 16 * kk);
-                const u32x4 qv = ld16(qr + 16 * kk);
-                z = dot8_bf16(wv, qv, z);
-            }
-            gate[c] = z;
+        for (int u = 0; u < GLD; u++) {
+            const int task = tid + u * kWThreads;
+            if (GCH % kWThreads == 0 || task < GCH) greg[u] = ld16(src + (long)task * 8);
         }
     }
+    float gbias[3];
 #pragma unroll
-    for (int c = 0; c < 3; c++) {
-        gate[c] += __shfl_xor(gate[c], 32, 64);
-        const uint16_t *bgp = (const uint16_t *)a.bg + (long)(g * 16 + head) * 3 + c;
-        gate[c] = live ? sigmoid(gate[c] + __uint_as_float((uint32_t)*bgp << 16)) : 0.f;
-    }
+    for (int c = 0; c < 3; c++)
+        gbias[c] = __uint_as_float((uint32_t)((const uint16_t *)a.bg)[(g * 16 + head) * 3 + c] << 16);
 
     // let the query and gate loads land before the tile loop (see the
     // compressed-attention kernel: otherwise every tile waits for its prefetch)
     wait_vmem_all();
+#pragma unroll
+    for (int u = 0; u < GLD; u++) {
+        const int task = tid + u * kWThreads;
+        const int hh = task / (3 * DK / 8), off = task % (3 * DK / 8);
+        if (GCH % kWThreads == 0 || task < GCH) st16(&sm.wg[hh * L::GS + off * 8], greg[u]);
+    }
     float m = -INFINITY, l = 0.f;
     f32x16 oacc[DT];
 #pragma unroll
@@ -298,6 +302,21 @@ __global__ __launch_bounds__(kWThreads) void k_window_mfma(RowArgs a, int ntp)
 
     store_tile(c_first & 1);
     lds_barrier();
+    // gates of this row from the staged rows: each lane half holds half of
+    // the dimensions
+    float gate[3];
+    {
+        const uint16_t *wr = &sm.wg[head * L::GS + 8 * h];
+#pragma unroll
+        for (int c = 0; c < 3; c++) {
+            float z = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; kk++)
+                z = dot8_bf16(ld16(wr + c * DK + 16 * kk), __builtin_bit_cast(u32x4, qf[kk]), z);
+            z += __shfl_xor(z, 32, 64);
+            gate[c] = live ? sigmoid(z + gbias[c]) : 0.f;
+        }
+    }
     for (int c = c_first; c <= c_last; c++) {
         if (c < c_last) load_tile(c + 1);
         const int k0 = c * kTile;
