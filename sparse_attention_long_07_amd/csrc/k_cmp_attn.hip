@@ -220,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
         float sum = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; r++) sum += fast_exp2(__builtin_fmaf(acc[r], sl2, -ms));
-        l = l * fast_exp2(m - ms) + sum;
+        l = __builtin_fmaf(l, fast_exp2(m - ms), sum);
         m = mn;
     };
     // one tile; `masked` (wave-uniform) applies the causal limit
@@ -280,9 +280,13 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
     }
     float lse2;
     {
+        // the two lane halves combine their partial sums in the same order
+        // (half 0 first), so both hold the same bits of the row's value
         const float mo = __shfl_xor(m, 32, 64), lo = __shfl_xor(l, 32, 64);
-        const float M = fmaxf(m, mo);
-        lse2 = M == -INFINITY ? -INFINITY : M + fast_log2(l * fast_exp2(m - M) + lo * fast_exp2(mo - M));
+        const float m0 = h ? mo : m, l0 = h ? lo : l, m1 = h ? m : mo, l1 = h ? l : lo;
+        const float M = fmaxf(m0, m1);
+        lse2 = M == -INFINITY ? -INFINITY
+                              : M + fast_log2(__builtin_fmaf(l0, fast_exp2(m0 - M), l1 * fast_exp2(m1 - M)));
     }
 
     // ---- pass 2: probabilities -> o_cmp and block importance
