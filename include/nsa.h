@@ -61,7 +61,7 @@ typedef enum {
     NSA_ERR_NULL = -1,      /* a required pointer is NULL */
     NSA_ERR_SHAPE = -2,     /* a size is out of the supported range */
     NSA_ERR_DTYPE = -3,     /* dtype is not NSA_FP32 or NSA_BF16 */
-    NSA_ERR_PARAM = -4,     /* l, d, l_sel, n, w or scale unsupported */
+    NSA_ERR_PARAM = -4,     /* l, d, l_sel, n, w, scale or a scalar argument unsupported */
     NSA_ERR_WORKSPACE = -5, /* workspace NULL or smaller than nsa_workspace_bytes */
     NSA_ERR_HIP = -6,       /* a HIP launch failed */
     NSA_ERR_ALIGN = -7      /* a pointer is not aligned as required */
@@ -103,6 +103,25 @@ size_t nsa_workspace_bytes(const nsa_config *cfg, int op);
 nsa_status nsa_compress_kv(const nsa_config *cfg, const void *k, const void *v, const void *w_ck,
                            const void *pe_k, const void *w_cv, const void *pe_v, void *cmp_k, void *cmp_v,
                            void *stream);
+
+/* Incremental compression of caches that grow token by token (the decode
+ * step of valuable12.com section III.3 reads compressed entries for every
+ * complete block; with the token compression of the deepdaiv newsletter a
+ * new block completes every 16 tokens).  cfg->T is the cache capacity; the
+ * caches are laid out as k/v and cmp_k/cmp_v above with T = capacity.
+ * For each sequence b, the blocks i with 16i+31 < len_new[b] that were not
+ * complete at len_old[b] tokens (16i+31 >= len_old[b]) are computed from
+ * k_cache/v_cache as nsa_compress_kv defines them and written to cmp_k /
+ * cmp_v; no other entry is touched.  len_old, len_new: device int32 [B],
+ * clamped to 0 <= len_old <= len_new <= T; len_old may be NULL (all zero:
+ * the hand-off of a prompt's caches to decoding).  max_append (host, 1..T):
+ * an upper bound on len_new[b] - len_old[b] that only sizes the launch; the
+ * result does not depend on it.  Each block comes out bit for bit as
+ * nsa_compress_kv writes it for the same tokens. */
+nsa_status nsa_compress_append(const nsa_config *cfg, const int32_t *len_old, const int32_t *len_new,
+                               int32_t max_append, const void *k_cache, const void *v_cache, const void *w_ck,
+                               const void *pe_k, const void *w_cv, const void *pe_v, void *cmp_k, void *cmp_v,
+                               void *stream);
 
 /* Stage S2 -- compressed attention and block importance (deepdaiv
  * newsletter, token compression and token selection paragraphs: the block

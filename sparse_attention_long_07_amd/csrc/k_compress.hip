@@ -43,14 +43,11 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
                                            false);
 }
 
-__global__ __launch_bounds__(kThreads) void k_compress_bf16(const uint16_t *__restrict__ x,
-                                                            const uint16_t *__restrict__ W,
-                                                            const uint16_t *__restrict__ PE,
-                                                            uint16_t *__restrict__ out, int T, int dim, int ncmp,
-                                                            int npad)
+__device__ __forceinline__ void compress_bf16_tile(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W,
+                                                   const uint16_t *__restrict__ PE, uint16_t *__restrict__ out,
+                                                   int T, int dim, int ncmp, int npad, int bh, int i0, int c0,
+                                                   int wlo, int whi, CompressLds &sm)
 {
-    __shared__ CompressLds sm;
-    const int bh = blockIdx.z, i0 = blockIdx.x * kTI, c0 = blockIdx.y * kTC;
     const int tid = threadIdx.x, ti = tid & 15, tc = tid >> 4;
     const long L = 32L * dim;
     const uint16_t *xs = x + (long)bh * T * dim;
@@ -124,19 +121,40 @@ __global__ __launch_bounds__(kThreads) void k_compress_bf16(const uint16_t *__re
         if (s + 1 < nsteps) store(buf ^ 1);
         lds_barrier();
     }
-    // rows N_cmp .. npad-1 are written as zero
+    // rows wlo <= i < whi are written, as zero from ncmp on
     const int c = c0 + 4 * tc;
     if (c >= dim) return;
 #pragma unroll
     for (int u = 0; u < 8; u++) {
         const int i = i0 + ti + 16 * u;
-        if (i >= npad) continue;
+        if (i < wlo || i >= whi || i >= npad) continue;
         uint2 w = {0u, 0u};
         if (i < ncmp) {
             w.x = pack_bf16x2(acc[u][0] + cacc[0], acc[u][1] + cacc[1]);
             w.y = pack_bf16x2(acc[u][2] + cacc[2], acc[u][3] + cacc[3]);
         }
         *(uint2 *)(out + ((long)bh * npad + i) * dim + c) = w;
+    }
+}
+
+// Block ranges as in k_compress_mfma_kv: all blocks (pads written as 0), or
+// with lengths only the blocks an append completes.
+__global__ __launch_bounds__(kThreads) void k_compress_bf16(const uint16_t *__restrict__ x,
+                                                            const uint16_t *__restrict__ W,
+                                                            const uint16_t *__restrict__ PE,
+                                                            uint16_t *__restrict__ out, int T, int dim, int ncmp,
+                                                            int npad, int Hkv, const int32_t *len_old,
+                                                            const int32_t *len_new)
+{
+    __shared__ CompressLds sm;
+    const int bh = blockIdx.z, c0 = blockIdx.y * kTC;
+    int lo = 0, hi = ncmp;
+    if (len_new) append_range(len_old, len_new, bh / Hkv, T, lo, hi);
+    const int wend = len_new ? hi : npad;
+    for (int i0 = lo + (int)blockIdx.x * kTI; i0 < wend; i0 += (int)gridDim.x * kTI) {
+        compress_bf16_tile(x, W, PE, out, T, dim, hi, npad, bh, i0, c0, len_new ? lo : i0, wend, sm);
+        if (!len_new) break;
+        __syncthreads();
     }
 }
 
@@ -152,19 +170,21 @@ struct CompressMfmaLds {
     float pe[DIM];                // sum_m W[c][m] PE[m]
 };
 
-// One workgroup tile (63 blocks of one (b, KV head)).  4 waves: wave w takes
+// One workgroup tile: blocks i0 .. i0+62 of one (b, KV head).  Blocks below
+// ncmp are loaded; rows wlo <= i < whi are written, as 0 when i >= ncmp.  Each
+// output row depends only on its own operand row and W, so a block comes out
+// bit for bit the same whichever tile computes it.  4 waves: wave w takes
 // operand rows 32 (w % 2) .. +31 and channels (w / 2) * DIM/2 .. +DIM/2
 // (DIM/64 tiles of 32 x 32).
 template <int DIM>
 __device__ __forceinline__ void compress_mfma_tile(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W,
                                                    const uint16_t *__restrict__ PE, uint16_t *__restrict__ out,
-                                                   int T, int ncmp, int npad, int bh, int tile,
+                                                   int T, int ncmp, int npad, int bh, int i0, int wlo, int whi,
                                                    CompressMfmaLds<DIM> &sm)
 {
     constexpr int NT = DIM / 64;                 // 32-channel tiles per wave
     constexpr int L = 32 * DIM;
     constexpr int BTASK = DIM * (kMK / 8) / kThreads;
-    const int i0 = tile * kMBlocks;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rw = 32 * (wave & 1), cw = (wave >> 1) * (DIM / 2);
     const uint16_t *xs = x + (long)bh * T * DIM;
@@ -240,7 +260,7 @@ __device__ __forceinline__ void compress_mfma_tile(const uint16_t *__restrict__ 
         for (int e = 0; e < 16; e++) {
             const int row = rw + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
             const int i = i0 + row;
-            if (row == kMBlocks || i >= npad) continue;
+            if (row == kMBlocks || i < wlo || i >= whi || i >= npad) continue;
             const __bf16 y = i < ncmp ? (__bf16)(acc[n][e] + pc) : (__bf16)0.f;
             out[((long)bh * npad + i) * DIM + c] = __builtin_bit_cast(uint16_t, y);
         }
@@ -249,6 +269,9 @@ __device__ __forceinline__ void compress_mfma_tile(const uint16_t *__restrict__ 
 
 // K and V of every (b, KV head) in one launch: grid.y 0 .. BH-1 take K
 // (d = DK), BH .. 2BH-1 take V (d = DV), so the two products share the chip.
+// Without lengths: every block of the T-token sequences, pads written as 0.
+// With lengths (a cache of capacity T): only the blocks that are complete at
+// len_new[b] tokens but not at len_old[b]; workgroups stride over those tiles.
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void k_compress_mfma_kv(const uint16_t *__restrict__ k,
                                                                const uint16_t *__restrict__ v,
@@ -257,19 +280,25 @@ __global__ __launch_bounds__(kThreads) void k_compress_mfma_kv(const uint16_t *_
                                                                const uint16_t *__restrict__ Wv,
                                                                const uint16_t *__restrict__ PEv,
                                                                uint16_t *__restrict__ ok, uint16_t *__restrict__ ov,
-                                                               int T, int ncmp, int npad, int BH)
+                                                               int T, int ncmp, int npad, int BH, int Hkv,
+                                                               const int32_t *len_old, const int32_t *len_new)
 {
     constexpr size_t SK = sizeof(CompressMfmaLds<DK>), SV = sizeof(CompressMfmaLds<DV>);
     __shared__ __attribute__((aligned(16))) unsigned char smem[SK > SV ? SK : SV];
     const int y = blockIdx.y;
-    if (y < BH) {
-        if ((int)blockIdx.x * kMBlocks >= npad) return;
-        compress_mfma_tile<DK>(k, Wk, PEk, ok, T, ncmp, npad, y, blockIdx.x,
-                               *reinterpret_cast<CompressMfmaLds<DK> *>(smem));
-    } else {
-        if ((int)blockIdx.x * kMBlocks >= npad) return;
-        compress_mfma_tile<DV>(v, Wv, PEv, ov, T, ncmp, npad, y - BH, blockIdx.x,
-                               *reinterpret_cast<CompressMfmaLds<DV> *>(smem));
+    const int bh = y < BH ? y : y - BH;
+    int lo = 0, hi = ncmp;
+    if (len_new) append_range(len_old, len_new, bh / Hkv, T, lo, hi);
+    for (int i0 = lo + (int)blockIdx.x * kMBlocks; i0 < (len_new ? hi : npad); i0 += (int)gridDim.x * kMBlocks) {
+        const int wlo = len_new ? lo : i0, whi = len_new ? hi : npad;
+        if (y < BH)
+            compress_mfma_tile<DK>(k, Wk, PEk, ok, T, hi, npad, bh, i0, wlo, whi,
+                                   *reinterpret_cast<CompressMfmaLds<DK> *>(smem));
+        else
+            compress_mfma_tile<DV>(v, Wv, PEv, ov, T, hi, npad, bh, i0, wlo, whi,
+                                   *reinterpret_cast<CompressMfmaLds<DV> *>(smem));
+        if (!len_new) break;   // one tile per workgroup: the grid covers every block
+        lds_barrier();         // the next tile reuses the LDS buffers
     }
 }
 
@@ -278,30 +307,36 @@ __global__ __launch_bounds__(kThreads) void k_compress_mfma_kv(const uint16_t *_
 bool compress_bf16_supported(const Dims &d) { return d.dtype == NSA_BF16; }
 
 hipError_t launch_compress_bf16(const Dims &d, const void *k, const void *v, const void *Wk, const void *PEk,
-                                const void *Wv, const void *PEv, void *ok, void *ov, hipStream_t s)
+                                const void *Wv, const void *PEv, void *ok, void *ov, hipStream_t s,
+                                const int32_t *len_old, const int32_t *len_new, int max_new_blocks)
 {
     const int BH = d.B * d.Hkv;
-    const dim3 mgrid((d.npad + kMBlocks - 1) / kMBlocks, 2 * BH);
+    // append: enough workgroups for max_new_blocks; each strides over its tiles
+    auto tiles = [&](int per) {
+        return len_new ? (max_new_blocks + per - 1) / per : (d.npad + per - 1) / per;
+    };
+    const dim3 mgrid(tiles(kMBlocks), 2 * BH);
     const uint16_t *ks = (const uint16_t *)k, *vs = (const uint16_t *)v;
     const uint16_t *wk = (const uint16_t *)Wk, *pk = (const uint16_t *)PEk, *wv = (const uint16_t *)Wv,
                    *pv = (const uint16_t *)PEv;
     uint16_t *oks = (uint16_t *)ok, *ovs = (uint16_t *)ov;
     if (d.dk == 192 && d.dv == 128) {
         hipLaunchKernelGGL((k_compress_mfma_kv<192, 128>), mgrid, dim3(kThreads), 0, s, ks, vs, wk, pk, wv, pv, oks,
-                           ovs, d.T, d.ncmp, d.npad, BH);
+                           ovs, d.T, d.ncmp, d.npad, BH, d.Hkv, len_old, len_new);
     } else if (d.dk == 128 && d.dv == 128) {
         hipLaunchKernelGGL((k_compress_mfma_kv<128, 128>), mgrid, dim3(kThreads), 0, s, ks, vs, wk, pk, wv, pv, oks,
-                           ovs, d.T, d.ncmp, d.npad, BH);
+                           ovs, d.T, d.ncmp, d.npad, BH, d.Hkv, len_old, len_new);
     } else if (d.dk == 64 && d.dv == 64) {
         hipLaunchKernelGGL((k_compress_mfma_kv<64, 64>), mgrid, dim3(kThreads), 0, s, ks, vs, wk, pk, wv, pv, oks,
-                           ovs, d.T, d.ncmp, d.npad, BH);
+                           ovs, d.T, d.ncmp, d.npad, BH, d.Hkv, len_old, len_new);
     } else {
         // other widths: the vector-ALU kernel, one launch per tensor
         for (int u = 0; u < 2; u++) {
             const int dim = u == 0 ? d.dk : d.dv;
-            dim3 grid((d.npad + kTI - 1) / kTI, (dim + kTC - 1) / kTC, BH);
+            dim3 grid(tiles(kTI), (dim + kTC - 1) / kTC, BH);
             hipLaunchKernelGGL(k_compress_bf16, grid, dim3(kThreads), 0, s, u == 0 ? ks : vs, u == 0 ? wk : wv,
-                               u == 0 ? pk : pv, u == 0 ? oks : ovs, d.T, dim, d.ncmp, d.npad);
+                               u == 0 ? pk : pv, u == 0 ? oks : ovs, d.T, dim, d.ncmp, d.npad, d.Hkv, len_old,
+                               len_new);
         }
     }
     return hipGetLastError();

@@ -151,10 +151,14 @@ __global__ __launch_bounds__(kSThreads) void k_dec_stream(DecArgs A)
             ka[kk] = ld16(ra + 32 * kk);
             kb2[kk] = ld16(rb + 32 * kk);
         }
+        // Keys past kend enter the PV product with probability 0; their V
+        // rows are read from key kend-1 instead, a slot or token the caller
+        // has written, because the rows past it need not be finite and
+        // 0 * NaN would reach the output.
 #pragma unroll
         for (int u = 0; u < VL; u++) {
             const int c = 64 * u + lane, key = c / VC, ch = c % VC;
-            vr[u] = ld16(V + (long)min(kbeg + key, kclamp) * DV + ch * 8);
+            vr[u] = ld16(V + (long)min(kbeg + key, kend - 1) * DV + ch * 8);
         }
         const uint16_t *qrow = (const uint16_t *)A.q + ((long)b * d.Hq + (pair % d.Hkv) * 16 + hd) * DK;
 #pragma unroll
@@ -444,7 +448,8 @@ __global__ __launch_bounds__(kTailThreads) void k_dec_tail(DecArgs A)
 #pragma unroll
             for (int u = 0; u < VL; u++) {
                 const int c = 64 * u + lane, key = c / VC, ch = c % VC;
-                vr[u] = ld16(V + (long)min(kbeg + key, d.T - 1) * DV + ch * 8);
+                // tokens past t read from token t's row (see phase A)
+                vr[u] = ld16(V + (long)min(kbeg + key, kend - 1) * DV + ch * 8);
             }
             f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll

@@ -45,13 +45,11 @@ __device__ __forceinline__ int row_t(const RowArgs &a, int b, int r)
 // m = tau*dim + e.  Tile: 64 blocks x 64 channels, 32 inputs per step; each
 // thread owns a 4x4 patch of the tile.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_compress_generic(const T *__restrict__ x, const T *__restrict__ W,
-                                                              const T *__restrict__ PE, T *__restrict__ out,
-                                                              int seqlen, int dim, int ncmp, int npad)
+__device__ __forceinline__ void compress_generic_tile(const T *__restrict__ x, const T *__restrict__ W,
+                                                      const T *__restrict__ PE, T *__restrict__ out, int seqlen,
+                                                      int dim, int ncmp, int npad, int bh, int i0, int c0, int wlo,
+                                                      int whi, float (&Xs)[32][65], float (&Ws)[32][65])
 {
-    __shared__ float Xs[32][65];
-    __shared__ float Ws[32][65];
-    const int bh = blockIdx.z, i0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
     const T *xs = x + (long)bh * seqlen * dim;
     const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
     const long K = 32L * dim;
@@ -85,8 +83,32 @@ __global__ __launch_bounds__(kThreads) void k_compress_generic(const T *__restri
 #pragma unroll
         for (int w = 0; w < 4; w++) {
             int i = i0 + ty * 4 + u, c = c0 + tx * 4 + w;
-            if (i < npad && c < dim) out[((long)bh * npad + i) * dim + c] = from_f<T>(i < ncmp ? acc[u][w] : 0.f);
+            if (i >= wlo && i < whi && i < npad && c < dim)
+                out[((long)bh * npad + i) * dim + c] = from_f<T>(i < ncmp ? acc[u][w] : 0.f);
         }
+}
+
+// Without lengths every block of the seqlen-token sequences is written (pads as
+// 0); with lengths (a cache of capacity seqlen) only the blocks that an append
+// from len_old[b] to len_new[b] tokens completes, workgroups striding over
+// them.  A block's value does not depend on the tile that computes it.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_compress_generic(const T *__restrict__ x, const T *__restrict__ W,
+                                                              const T *__restrict__ PE, T *__restrict__ out,
+                                                              int seqlen, int dim, int ncmp, int npad, int Hkv,
+                                                              const int32_t *len_old, const int32_t *len_new)
+{
+    __shared__ float Xs[32][65];
+    __shared__ float Ws[32][65];
+    const int bh = blockIdx.z, c0 = blockIdx.y * 64;
+    int lo = 0, hi = ncmp;
+    if (len_new) append_range(len_old, len_new, bh / Hkv, seqlen, lo, hi);
+    const int wend = len_new ? hi : npad;
+    for (int i0 = lo + (int)blockIdx.x * 64; i0 < wend; i0 += (int)gridDim.x * 64) {
+        compress_generic_tile<T>(x, W, PE, out, seqlen, dim, hi, npad, bh, i0, c0, len_new ? lo : i0, wend, Xs, Ws);
+        if (!len_new) break;
+        __syncthreads();
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -385,15 +407,18 @@ __global__ __launch_bounds__(kThreads) void k_sparse_generic(RowArgs a)
 
 // ---------------------------------------------------------------------------
 hipError_t launch_compress_generic(const Dims &d, const void *x, const void *W, const void *PE, void *out,
-                                   int dim, hipStream_t s)
+                                   int dim, hipStream_t s, const int32_t *len_old, const int32_t *len_new,
+                                   int tiles)
 {
-    dim3 grid(d.npad / 64, (dim + 63) / 64, d.B * d.Hkv);
+    dim3 grid(len_new ? tiles : d.npad / 64, (dim + 63) / 64, d.B * d.Hkv);
     if (d.dtype == NSA_FP32)
         hipLaunchKernelGGL(k_compress_generic<float>, grid, dim3(kThreads), 0, s, (const float *)x,
-                           (const float *)W, (const float *)PE, (float *)out, d.T, dim, d.ncmp, d.npad);
+                           (const float *)W, (const float *)PE, (float *)out, d.T, dim, d.ncmp, d.npad, d.Hkv,
+                           len_old, len_new);
     else
         hipLaunchKernelGGL(k_compress_generic<bf16_t>, grid, dim3(kThreads), 0, s, (const bf16_t *)x,
-                           (const bf16_t *)W, (const bf16_t *)PE, (bf16_t *)out, d.T, dim, d.ncmp, d.npad);
+                           (const bf16_t *)W, (const bf16_t *)PE, (bf16_t *)out, d.T, dim, d.ncmp, d.npad, d.Hkv,
+                           len_old, len_new);
     return hipGetLastError();
 }
 

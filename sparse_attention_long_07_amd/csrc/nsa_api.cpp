@@ -1,5 +1,6 @@
 // C ABI of libnsa: argument checks, workspace layout and launch order.
 // Every check runs on the host before anything is enqueued.
+#include <algorithm>
 #include <math.h>
 #include <string.h>
 
@@ -158,6 +159,34 @@ nsa_status nsa_compress_kv(const nsa_config *cfg, const void *k, const void *v, 
     }
     NSA_TRY(launch_compress_generic(d, k, w_ck, pe_k, cmp_k, d.dk, s));
     NSA_TRY(launch_compress_generic(d, v, w_cv, pe_v, cmp_v, d.dv, s));
+    return NSA_OK;
+}
+
+nsa_status nsa_compress_append(const nsa_config *cfg, const int32_t *len_old, const int32_t *len_new,
+                               int32_t max_append, const void *k_cache, const void *v_cache, const void *w_ck,
+                               const void *pe_k, const void *w_cv, const void *pe_v, void *cmp_k, void *cmp_v,
+                               void *stream)
+{
+    Dims d;
+    nsa_status st = check_config(cfg, &d);
+    if (st != NSA_OK) return st;
+    if (!len_new || !k_cache || !v_cache || !w_ck || !pe_k || !w_cv || !pe_v || !cmp_k || !cmp_v)
+        return NSA_ERR_NULL;
+    if (max_append < 1 || max_append > d.T) return NSA_ERR_PARAM;
+    const void *ptrs[] = {k_cache, v_cache, w_ck, pe_k, w_cv, pe_v, cmp_k, cmp_v};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return NSA_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    // appending a tokens completes at most a/16 + 1 blocks (capped by the cache)
+    const int max_blocks = std::min(max_append / 16 + 1, d.npad);
+    if (compress_bf16_supported(d)) {
+        NSA_TRY(launch_compress_bf16(d, k_cache, v_cache, w_ck, pe_k, w_cv, pe_v, cmp_k, cmp_v, s, len_old, len_new,
+                                     max_blocks));
+        return NSA_OK;
+    }
+    const int tiles = (max_blocks + 63) / 64;
+    NSA_TRY(launch_compress_generic(d, k_cache, w_ck, pe_k, cmp_k, d.dk, s, len_old, len_new, tiles));
+    NSA_TRY(launch_compress_generic(d, v_cache, w_cv, pe_v, cmp_v, d.dv, s, len_old, len_new, tiles));
     return NSA_OK;
 }
 

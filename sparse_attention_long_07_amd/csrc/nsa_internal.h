@@ -26,6 +26,23 @@ template <typename T> __device__ __forceinline__ T from_f(float x);
 template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float x) { return f2bf(x); }
 
+// Compression blocks complete in a sequence of len tokens: block i covers
+// tokens 16i .. 16i+31.
+__device__ __forceinline__ int cmp_blocks(int len) { return len >= 32 ? (len - 32) / 16 + 1 : 0; }
+
+// Blocks that an append from len_old[b] to len_new[b] tokens completes, as
+// [lo, hi); lengths are clamped to 0 <= len_old <= len_new <= T.
+__device__ __forceinline__ void append_range(const int32_t *len_old, const int32_t *len_new, int b, int T, int &lo,
+                                             int &hi)
+{
+    int ln = len_new[b];
+    ln = ln < 0 ? 0 : (ln > T ? T : ln);
+    int lo_len = len_old ? len_old[b] : 0;
+    lo_len = lo_len < 0 ? 0 : (lo_len > ln ? ln : lo_len);
+    lo = cmp_blocks(lo_len);
+    hi = cmp_blocks(ln);
+}
+
 // Resolved problem sizes (from nsa_config after validation).
 struct Dims {
     int B, T, Hkv, G, Hq, dk, dv, n, w;
@@ -96,8 +113,13 @@ size_t backward_layout(const Dims &d, void *ws, BwdArgs *A);   // bytes; carves 
 hipError_t launch_backward(const BwdArgs &A, hipStream_t s);
 
 // Generic kernels: plain VALU code, any supported shape, fp32 or bf16 storage.
+// Compression launchers: every block of the T-token sequences when len_new is
+// null; otherwise (caches of capacity T) the blocks an append from len_old[b]
+// to len_new[b] tokens completes, with `tiles` workgroups per (b, head)
+// striding over them.
 hipError_t launch_compress_generic(const Dims &d, const void *x, const void *W, const void *PE, void *out,
-                                   int dim, hipStream_t s);
+                                   int dim, hipStream_t s, const int32_t *len_old = nullptr,
+                                   const int32_t *len_new = nullptr, int tiles = 0);
 hipError_t launch_cmp_attn_generic(const RowArgs &a, bool with_v, hipStream_t s);
 hipError_t launch_select_generic(const RowArgs &a, hipStream_t s);
 hipError_t launch_sparse_generic(const RowArgs &a, hipStream_t s);
@@ -105,7 +127,9 @@ hipError_t launch_sparse_generic(const RowArgs &a, hipStream_t s);
 // Token compression for bf16 storage on the vector ALUs (bf16 dot products).
 bool compress_bf16_supported(const Dims &d);
 hipError_t launch_compress_bf16(const Dims &d, const void *k, const void *v, const void *Wk, const void *PEk,
-                                const void *Wv, const void *PEv, void *ok, void *ov, hipStream_t s);
+                                const void *Wv, const void *PEv, void *ok, void *ov, hipStream_t s,
+                                const int32_t *len_old = nullptr, const int32_t *len_new = nullptr,
+                                int max_new_blocks = 0);
 
 // Matrix-core kernels (bf16 storage, G = 16; prefill rows only).
 bool cmp_attn_mfma_supported(const Dims &d);

@@ -21,7 +21,8 @@ OP_FORWARD, OP_SELECT, OP_DECODE, OP_SPARSE, OP_BACKWARD = 0, 1, 2, 3, 4
 STATUS = {0: "NSA_OK", -1: "NSA_ERR_NULL", -2: "NSA_ERR_SHAPE", -3: "NSA_ERR_DTYPE", -4: "NSA_ERR_PARAM",
           -5: "NSA_ERR_WORKSPACE", -6: "NSA_ERR_HIP", -7: "NSA_ERR_ALIGN"}
 
-EXPORTS = ("nsa_workspace_bytes", "nsa_compress_kv", "nsa_compressed_attention", "nsa_select_topn",
+EXPORTS = ("nsa_workspace_bytes", "nsa_compress_kv", "nsa_compress_append", "nsa_compressed_attention",
+           "nsa_select_topn",
            "nsa_sparse_attention", "nsa_pack_kv_blocks", "nsa_window_attention", "nsa_selected_attention", "nsa_select_blocks",
            "nsa_forward", "nsa_decode_step", "nsa_backward", "nsa_status_string")
 
@@ -55,6 +56,8 @@ def lib() -> ctypes.CDLL:
         L.nsa_status_string.argtypes = [ctypes.c_int]
         L.nsa_compress_kv.restype = ctypes.c_int
         L.nsa_compress_kv.argtypes = [ctypes.POINTER(Config)] + [_vp] * 9
+        L.nsa_compress_append.restype = ctypes.c_int
+        L.nsa_compress_append.argtypes = [ctypes.POINTER(Config), _vp, _vp, ctypes.c_int32] + [_vp] * 9
         L.nsa_compressed_attention.restype = ctypes.c_int
         L.nsa_compressed_attention.argtypes = [ctypes.POINTER(Config)] + [_vp] * 6
         L.nsa_select_topn.restype = ctypes.c_int
@@ -138,6 +141,31 @@ def compress_kv(s: NSAShape, k, v, w_ck, pe_k, w_cv, pe_v, cmp_k=None, cmp_v=Non
     c = config(s)
     _check("nsa_compress_kv", lib().nsa_compress_kv(ctypes.byref(c), _p(k), _p(v), _p(w_ck), _p(pe_k), _p(w_cv),
                                                     _p(pe_v), _p(cmp_k), _p(cmp_v), _stream()))
+    return cmp_k, cmp_v
+
+
+def compress_append(s: NSAShape, len_old, len_new, max_append, k_cache, v_cache, w_ck, pe_k, w_cv, pe_v, cmp_k,
+                    cmp_v):
+    """Compressed entries of the blocks that growing each cache from len_old[b]
+    to len_new[b] tokens completes (s.T = cache capacity; len_old may be None
+    for all zero).  cmp_k / cmp_v are updated in place and returned."""
+    dt = _dt(s)
+    if len_old is not None:
+        _req(len_old, "len_old", (s.B,), torch.int32)
+    _req(len_new, "len_new", (s.B,), torch.int32)
+    _req(k_cache, "k_cache", (s.B, s.Hkv, s.T, s.dk), dt)
+    _req(v_cache, "v_cache", (s.B, s.Hkv, s.T, s.dv), dt)
+    _req(w_ck, "w_ck", (s.dk, s.l * s.dk), dt)
+    _req(pe_k, "pe_k", (s.l, s.dk), dt)
+    _req(w_cv, "w_cv", (s.dv, s.l * s.dv), dt)
+    _req(pe_v, "pe_v", (s.l, s.dv), dt)
+    _req(cmp_k, "cmp_k", (s.B, s.Hkv, s.n_pad, s.dk), dt)
+    _req(cmp_v, "cmp_v", (s.B, s.Hkv, s.n_pad, s.dv), dt)
+    c = config(s)
+    _check("nsa_compress_append",
+           lib().nsa_compress_append(ctypes.byref(c), _p(len_old), _p(len_new), int(max_append), _p(k_cache),
+                                     _p(v_cache), _p(w_ck), _p(pe_k), _p(w_cv), _p(pe_v), _p(cmp_k), _p(cmp_v),
+                                     _stream()))
     return cmp_k, cmp_v
 
 

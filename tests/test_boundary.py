@@ -77,6 +77,7 @@ def test_bad_config_rejected_everywhere(kw, code):
     c = ctypes.byref(cfg(**kw))
     f = [FAKE] * 16
     assert L.nsa_compress_kv(c, *f[:8], None) == code
+    assert L.nsa_compress_append(c, f[0], f[1], 1, *f[:8], None) == code
     assert L.nsa_select_blocks(c, f[0], f[1], None, f[2], f[3], 1 << 40, None) == code
     assert L.nsa_forward(c, *f[:7], None, f[0], None, None, f[1], 1 << 40, None) == code
     assert L.nsa_decode_step(c, *f[:8], None, f[0], None, f[1], 1 << 40, None) == code
@@ -102,6 +103,24 @@ def test_compress_null_and_misaligned(pos):
     assert L.nsa_compress_kv(c, *args, None) == NULL
     args[pos] = MIS
     assert L.nsa_compress_kv(c, *args, None) == ALIGN
+
+
+@pytest.mark.parametrize("pos", range(9))
+def test_compress_append_checks(pos):
+    """len_new and the eight tensors are required (len_old may be NULL); every
+    failing call returns before anything is enqueued."""
+    L = nsa.lib()
+    c = ctypes.byref(cfg())
+    args = [FAKE] * 9           # len_new | k_cache v_cache w_ck pe_k w_cv pe_v cmp_k cmp_v
+    args[pos] = None
+    assert L.nsa_compress_append(c, None, args[0], 16, *args[1:], None) == NULL
+    if pos > 0:
+        args[pos] = MIS
+        assert L.nsa_compress_append(c, FAKE, args[0], 16, *args[1:], None) == ALIGN
+    # max_append must lie in 1..T (T = 256 here)
+    f = [FAKE] * 8
+    for bad in (0, -1, 257):
+        assert L.nsa_compress_append(c, FAKE, FAKE, bad, *f, None) == PARAM
 
 
 @pytest.mark.parametrize("pos", range(8))

@@ -1,0 +1,134 @@
+"""Incremental compression of growing caches (nsa_compress_append) and the
+decode step on caches whose unwritten tails hold NaN.
+
+Appending from len_old to len_new tokens must write exactly the compressed
+entries of the blocks that become complete, bit for bit as nsa_compress_kv
+writes them for the same tokens, and nothing else.  The decode step may only
+read what the caller has written: entries past a sequence's length are
+filled with NaN here, and the output must equal the one on clean caches."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from sparse_attention_long_07_amd import nsa
+from sparse_attention_long_07_amd.config import FP32, NSAShape
+from sparse_attention_long_07_amd.inputs import make_decode
+from tests.parity_util import compressed_close, np64, oracle_compress
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    nsa.lib()
+
+
+def nblk(L: int) -> int:
+    return (L - 32) // 16 + 1 if L >= 32 else 0
+
+
+CASES = [
+    # matrix-core compression and decode
+    ("bf16_g16_d192", NSAShape(3, 1100, 2, 16, 192, 128), [1100, 777, 45], [1000, 700, 0]),
+    ("bf16_g16_d64", NSAShape(2, 700, 1, 16, 64, 64, n=5, w=200), [700, 129], [600, 31]),
+    # vector-ALU compression (other widths), generic decode
+    ("bf16_odd", NSAShape(2, 400, 3, 3, 24, 40, n=5, w=100), [400, 250], [300, 200]),
+    # fp32 storage: generic kernels throughout
+    ("fp32", NSAShape(2, 600, 1, 4, 64, 64, FP32), [600, 333], [500, 17]),
+]
+
+
+def _grow(s, x, lens0, lens, ck, cv):
+    """Hand-off of the first lens0 tokens, one jump of up to 37 tokens, then
+    one token per call up to lens."""
+    dev = x["k"].device
+    cur = torch.tensor(lens0, dtype=torch.int32, device=dev)
+    nsa.compress_append(s, None, cur, max(max(lens0), 1), x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"],
+                        x["pe_v"], ck, cv)
+    target = torch.tensor(lens, dtype=torch.int32, device=dev)
+    nxt = torch.minimum(cur + 37, target)
+    nsa.compress_append(s, cur, nxt, 37, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"], ck, cv)
+    cur = nxt
+    while bool((cur < target).any()):
+        nxt = torch.minimum(cur + 1, target)
+        nsa.compress_append(s, cur, nxt, 1, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"], ck, cv)
+        cur = nxt
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name,s,lens,lens0", CASES, ids=[c[0] for c in CASES])
+def test_append_matches_full_compression(name, s, lens, lens0):
+    say("append", name, s, lens, lens0)
+    x = make_decode(s, 41, "cuda", seq_lens=lens)
+    dt = x["k"].dtype
+    ref_k, ref_v = nsa.compress_kv(s, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"])
+    ck = torch.full((s.B, s.Hkv, s.n_pad, s.dk), float("nan"), dtype=dt, device="cuda")
+    cv = torch.full((s.B, s.Hkv, s.n_pad, s.dv), float("nan"), dtype=dt, device="cuda")
+    _grow(s, x, lens0, lens, ck, cv)
+    ok_k = oracle_compress(s, x["k"], x["w_ck"], x["pe_k"])
+    ok_v = oracle_compress(s, x["v"], x["w_cv"], x["pe_v"])
+    for b, L in enumerate(lens):
+        n = nblk(L)
+        # the completed blocks, bit for bit as the whole-sequence compression
+        assert torch.equal(ck[b, :, :n], ref_k[b, :, :n]), (name, b)
+        assert torch.equal(cv[b, :, :n], ref_v[b, :, :n]), (name, b)
+        # and within the oracle's tolerance
+        assert compressed_close(s, np64(ck[b, :, :n]), ok_k[b, :, :n])
+        assert compressed_close(s, np64(cv[b, :, :n]), ok_v[b, :, :n])
+        # nothing past them is written
+        assert bool(torch.isnan(ck[b, :, n:].float()).all()) and bool(torch.isnan(cv[b, :, n:].float()).all())
+
+
+def test_append_clamps_lengths():
+    """Lengths outside 0 <= len_old <= len_new <= T are clamped: a length
+    past the capacity acts as T, a decreasing pair writes nothing."""
+    s = NSAShape(2, 300, 1, 16, 64, 64, n=5, w=100)
+    x = make_decode(s, 43, "cuda")
+    ref_k, ref_v = nsa.compress_kv(s, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"])
+    ck = torch.full((s.B, s.Hkv, s.n_pad, s.dk), float("nan"), dtype=x["k"].dtype, device="cuda")
+    cv = torch.full((s.B, s.Hkv, s.n_pad, s.dv), float("nan"), dtype=x["k"].dtype, device="cuda")
+    old = torch.tensor([-5, 200], dtype=torch.int32, device="cuda")
+    new = torch.tensor([10000, 100], dtype=torch.int32, device="cuda")
+    nsa.compress_append(s, old, new, s.T, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"], ck, cv)
+    torch.cuda.synchronize()
+    n0 = nblk(s.T)
+    assert torch.equal(ck[0, :, :n0], ref_k[0, :, :n0]) and torch.equal(cv[0, :, :n0], ref_v[0, :, :n0])
+    assert bool(torch.isnan(ck[0, :, n0:].float()).all())
+    assert bool(torch.isnan(ck[1].float()).all()) and bool(torch.isnan(cv[1].float()).all())
+
+
+@pytest.mark.parametrize("name,s,lens,lens0", CASES, ids=[c[0] for c in CASES])
+def test_decode_ignores_unwritten_cache_tails(name, s, lens, lens0):
+    """Decode on caches grown by appends, with every raw token past a
+    sequence's length and every compressed entry past its complete blocks
+    set to NaN, equals decode on fully written caches with the same valid
+    contents (a key past the length enters with probability 0)."""
+    say("decode tails", name, s, lens)
+    x = make_decode(s, 47, "cuda", seq_lens=lens)
+    dt = x["k"].dtype
+    ref_k, ref_v = nsa.compress_kv(s, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"])
+    o_ref, i_ref = nsa.decode_step(s, x["seq_lens"], x["q"], x["k"], x["v"], ref_k, ref_v, x["w_g"], x["b_g"],
+                                   want_idx=True)
+    k2, v2 = x["k"].clone(), x["v"].clone()
+    for b, L in enumerate(lens):
+        k2[b, :, L:] = float("nan")
+        v2[b, :, L:] = float("nan")
+    ck = torch.full((s.B, s.Hkv, s.n_pad, s.dk), float("nan"), dtype=dt, device="cuda")
+    cv = torch.full((s.B, s.Hkv, s.n_pad, s.dv), float("nan"), dtype=dt, device="cuda")
+    _grow(s, {**x, "k": k2, "v": v2}, lens0, lens, ck, cv)
+    o, i = nsa.decode_step(s, x["seq_lens"], x["q"], k2, v2, ck, cv, x["w_g"], x["b_g"], want_idx=True)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o.float()).all())
+    assert torch.equal(i, i_ref)
+    assert torch.equal(o, o_ref)
