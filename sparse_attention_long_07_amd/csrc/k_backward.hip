@@ -20,10 +20,12 @@
 //                     three branches (log-sum-exp, output), forms D, the gate
 //                     terms and the complete dq; stores the per-row
 //                     statistics for the key-side passes.
-//  2. k_bwd_keys<raw> one 16-key tile per workgroup: dK, dV from the window
-//                     rows and from every row whose selection holds the tile's
-//                     block (found by scanning idx, in ascending row order).
-//  3. k_bwd_keys<cmp> one 16-block tile of compressed keys per workgroup and
+//  2. k_bwd_keys_blk  one 64-key block per workgroup: dK, dV from the window
+//                     rows and then from every row whose selection holds the
+//                     block, in ascending row order, read from a bitmap of
+//                     (block, row) pairs built by k_bwd_selmap (integer OR, so
+//                     the bitmap does not depend on the order of the writes).
+//  3. k_bwd_keys_cmp  one 16-block tile of compressed keys per workgroup and
 //                     row chunk; the chunk partials are summed in order.
 //  4. tiled GEMMs     dW and the token gradient of the compression map; the
 //                     token gradient is added to the raw-key gradient and
@@ -33,6 +35,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace nsa {
 
 namespace {
@@ -40,9 +44,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWave = 64;
 constexpr int kChunk = 64;       // keys per chunk of the row pass
-constexpr int kKeyTile = 16;     // keys per workgroup of the key passes
+constexpr int kKeyTile = 16;     // compressed blocks per workgroup of pass 3
 constexpr int kRowChunk = 1024;  // rows per partial of the compressed-key gradient
 constexpr int kGateRows = 256;   // rows per partial of the gate gradient
+constexpr size_t kLdsBytes = 160 * 1024;   // LDS of one workgroup on gfx950
 constexpr int kStat = 12;        // per (row, head): {lse, D, gate, dz} for each of the 3 branches
 
 __device__ __forceinline__ float wave_max(float v)
@@ -56,22 +61,83 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
+// LDS row stride (elements) of a staged key or value row: rows start on
+// 16-byte boundaries, and for widths that are multiples of 64 the stride is
+// 4 words past a multiple of 32, so 8 lanes reading 16 bytes of 8 different
+// rows at the same column cover all 32 banks once.
+template <typename T> constexpr int stage_stride(int dim) { return sizeof(T) == 2 ? dim + 8 : dim + 4; }
+
+// sum_x a[x] * r[x] over n elements (n a multiple of 8; a and r 16-byte
+// aligned): 16-byte reads, two accumulators
+__device__ __forceinline__ float dot_staged(const float *a, const bf16_t *r, int n)
+{
+    float z0 = 0.f, z1 = 0.f;
+#pragma unroll 4
+    for (int x = 0; x < n; x += 8) {
+        const uint4 w = *(const uint4 *)(r + x);
+        const float4 a0 = *(const float4 *)(a + x), a1 = *(const float4 *)(a + x + 4);
+        z0 = __builtin_fmaf(a0.x, __uint_as_float(w.x << 16), z0);
+        z1 = __builtin_fmaf(a0.y, __uint_as_float(w.x & 0xffff0000u), z1);
+        z0 = __builtin_fmaf(a0.z, __uint_as_float(w.y << 16), z0);
+        z1 = __builtin_fmaf(a0.w, __uint_as_float(w.y & 0xffff0000u), z1);
+        z0 = __builtin_fmaf(a1.x, __uint_as_float(w.z << 16), z0);
+        z1 = __builtin_fmaf(a1.y, __uint_as_float(w.z & 0xffff0000u), z1);
+        z0 = __builtin_fmaf(a1.z, __uint_as_float(w.w << 16), z0);
+        z1 = __builtin_fmaf(a1.w, __uint_as_float(w.w & 0xffff0000u), z1);
+    }
+    return z0 + z1;
+}
+__device__ __forceinline__ float dot_staged(const float *a, const float *r, int n)
+{
+    float z0 = 0.f, z1 = 0.f;
+#pragma unroll 4
+    for (int x = 0; x < n; x += 8) {
+        const float4 r0 = *(const float4 *)(r + x), r1 = *(const float4 *)(r + x + 4);
+        const float4 a0 = *(const float4 *)(a + x), a1 = *(const float4 *)(a + x + 4);
+        z0 = __builtin_fmaf(a0.x, r0.x, z0);
+        z1 = __builtin_fmaf(a0.y, r0.y, z1);
+        z0 = __builtin_fmaf(a0.z, r0.z, z0);
+        z1 = __builtin_fmaf(a0.w, r0.w, z1);
+        z0 = __builtin_fmaf(a1.x, r1.x, z0);
+        z1 = __builtin_fmaf(a1.y, r1.y, z1);
+        z0 = __builtin_fmaf(a1.z, r1.z, z0);
+        z1 = __builtin_fmaf(a1.w, r1.w, z1);
+    }
+    return z0 + z1;
+}
+
+// rows key0 .. key0+lim-1 of src ([key][dim]) into dst with stride ds; 16-byte
+// global loads (dim is a multiple of 8 and rows are 16-byte aligned)
+template <typename T>
+__device__ __forceinline__ void stage_rows(T *dst, int ds, const T *src, int key0, int lim, int dim)
+{
+    constexpr int PER = 16 / sizeof(T);
+    const int cpr = dim / PER;   // 16-byte pieces per row
+    for (int e = threadIdx.x; e < lim * cpr; e += kThreads) {
+        const int r = e / cpr, c = e % cpr;
+        *(uint4 *)(dst + r * ds + c * PER) = *(const uint4 *)(src + (long)(key0 + r) * dim + c * PER);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Pass 1.  Per (b, t, g): for each branch (0 compressed, 1 selected, 2
 // window) an online-softmax sweep gives the log-sum-exp and o_c, then a
 // second sweep recomputes p and accumulates dq.  Key chunks as in the
 // forward: compressed blocks [0, nvis) with 16i+31 <= t; the distinct valid
 // selected blocks in ascending order, tokens <= t; the window [t-w+1, t].
-template <typename T>
+template <typename T, bool STAGED>
 __global__ __launch_bounds__(kThreads) void k_bwd_rows(BwdArgs a)
 {
-    extern __shared__ float smem[];
+    extern __shared__ __align__(16) float smem[];
     const Dims &d = a.d;
     const int G = d.G, dk = d.dk, dv = d.dv;
+    const int KSt = stage_stride<T>(dk), VSt = stage_stride<T>(dv);
     float *qs = smem;              // [G][dk]
     float *dos = qs + G * dk;      // [G][dv]  output gradient (not gated)
     float *sb = dos + G * dv;      // [G][64]  logits, then probabilities, then ds
     float *ob = sb + G * kChunk;   // [G][dv]  branch output
+    T *Ks = (T *)(ob + G * dv);    // [64][KSt] the chunk's keys, staged once for all heads (STAGED)
+    T *Vs = Ks + kChunk * KSt;     // [64][VSt] and values
     __shared__ float m_s[16], l_s[16], al_s[16], lse_s[16], D_s[16], gate_s[48], dz_s[48];
     __shared__ int blk[64];
     __shared__ int nblk_s;
@@ -118,6 +184,23 @@ __global__ __launch_bounds__(kThreads) void k_bwd_rows(BwdArgs a)
     const T *Vr = (const T *)a.v + bgi * d.T * dv;
     const T *Kc = (const T *)a.kc + bgi * d.npad * dk;
     const T *Vc = (const T *)a.vc + bgi * d.npad * dv;
+    // the chunk's K and V rows: staged in LDS, or read in place when the
+    // staging buffers would not fit (fp32 with wide heads)
+    auto chunk_rows = [&](const T *K, const T *V, int key0, int lim, const T *&Kx, const T *&Vx, int &kst, int &vst) {
+        if constexpr (STAGED) {
+            stage_rows<T>(Ks, KSt, K, key0, lim, dk);
+            stage_rows<T>(Vs, VSt, V, key0, lim, dv);
+            Kx = Ks;
+            Vx = Vs;
+            kst = KSt;
+            vst = VSt;
+        } else {
+            Kx = K + (long)key0 * dk;
+            Vx = V + (long)key0 * dv;
+            kst = dk;
+            vst = dv;
+        }
+    };
     const int nvis = t >= 31 ? (t - 31) / 16 + 1 : 0;
     const int lo = t - d.w + 1 > 0 ? t - d.w + 1 : 0;
     const int nq = (G * dk + kThreads - 1) / kThreads;
@@ -151,16 +234,13 @@ __global__ __launch_bounds__(kThreads) void k_bwd_rows(BwdArgs a)
         for (int ch = 0; ch < nch; ch++) {
             int key0, lim;
             chunk(ch, key0, lim);
+            const T *Kx, *Vx;
+            int kst, vst;
+            chunk_rows(K, V, key0, lim, Kx, Vx, kst, vst);
+            __syncthreads();
             for (int e = tid; e < G * kChunk; e += kThreads) {
                 const int h = e / kChunk, ii = e % kChunk;
-                float s = -INFINITY;
-                if (ii < lim) {
-                    const T *kr = K + (long)(key0 + ii) * dk;
-                    float z = 0.f;
-                    for (int x = 0; x < dk; x++) z += qs[h * dk + x] * to_f(kr[x]);
-                    s = z * d.scale;
-                }
-                sb[e] = s;
+                sb[e] = ii < lim ? dot_staged(qs + h * dk, Kx + ii * kst, dk) * d.scale : -INFINITY;
             }
             __syncthreads();
             for (int h = wave; h < G; h += kThreads / kWave) {
@@ -184,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_rows(BwdArgs a)
                 if (u < no && e < G * dv) {
                     const int h = e / dv, c = e % dv;
                     float z = acc[u] * al_s[h];
-                    for (int ii = 0; ii < lim; ii++) z += sb[h * kChunk + ii] * to_f(V[(long)(key0 + ii) * dv + c]);
+                    for (int ii = 0; ii < lim; ii++) z += sb[h * kChunk + ii] * to_f(Vx[ii * vst + c]);
                     acc[u] = z;
                 }
             }
@@ -216,15 +296,16 @@ __global__ __launch_bounds__(kThreads) void k_bwd_rows(BwdArgs a)
         for (int ch = 0; ch < nch; ch++) {
             int key0, lim;
             chunk(ch, key0, lim);
+            const T *Kx, *Vx;
+            int kst, vst;
+            chunk_rows(K, V, key0, lim, Kx, Vx, kst, vst);
+            __syncthreads();
             for (int e = tid; e < G * kChunk; e += kThreads) {
                 const int h = e / kChunk, ii = e % kChunk;
                 float ds = 0.f;
                 if (ii < lim) {
-                    const T *kr = K + (long)(key0 + ii) * dk;
-                    const T *vr = V + (long)(key0 + ii) * dv;
-                    float z = 0.f, y = 0.f;
-                    for (int x = 0; x < dk; x++) z += qs[h * dk + x] * to_f(kr[x]);
-                    for (int c = 0; c < dv; c++) y += dos[h * dv + c] * to_f(vr[c]);
+                    const float z = dot_staged(qs + h * dk, Kx + ii * kst, dk);
+                    const float y = dot_staged(dos + h * dv, Vx + ii * vst, dv);
                     const float p = __expf(z * d.scale - lse_s[h]);
                     ds = p * (gate_s[h * 3 + br] * y - D_s[h]);
                 }
@@ -237,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_rows(BwdArgs a)
                 if (u < nq && e < G * dk) {
                     const int h = e / dk, x = e % dk;
                     float z = 0.f;
-                    for (int ii = 0; ii < lim; ii++) z += sb[h * kChunk + ii] * to_f(K[(long)(key0 + ii) * dk + x]);
+                    for (int ii = 0; ii < lim; ii++) z += sb[h * kChunk + ii] * to_f(Kx[ii * kst + x]);
                     dq[u] += d.scale * z;
                 }
             }
@@ -267,16 +348,16 @@ __global__ __launch_bounds__(kThreads) void k_bwd_rows(BwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Passes 2 and 3.  A workgroup owns kKeyTile consecutive keys of one (b, g):
-// raw tokens (CMP = false) or compressed blocks (CMP = true).  Keys and values
-// sit in LDS; the rows that attend to them are visited one at a time, all G
-// heads of a row together.  Thread (key = tid % 16, h = tid / 16) forms p and
+// Pass 3.  A workgroup owns kKeyTile consecutive compressed blocks of one
+// (b, g) and one chunk of kRowChunk rows.  Keys and values sit in LDS; the
+// rows that attend to them are visited one at a time, all G heads of a row
+// together.  Thread (key = tid % 16, h = tid / 16) forms p and
 // ds of head h; then thread (key, part = tid / 16) adds every head's
 // contribution to the columns part, part + 16, ... of dK and dV.
-template <typename T, bool CMP>
-__global__ __launch_bounds__(kThreads) void k_bwd_keys(BwdArgs a)
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_bwd_keys_cmp(BwdArgs a)
 {
-    extern __shared__ float smem[];
+    extern __shared__ __align__(16) float smem[];
     const Dims &d = a.d;
     const int G = d.G, dk = d.dk, dv = d.dv, KS = dk + 1, VS = dv + 1;
     float *Ks = smem;                  // [16][dk+1]
@@ -286,16 +367,14 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys(BwdArgs a)
     float *ps = dos + G * dv;          // [G][16]  gate * p
     float *dss = ps + G * kKeyTile;    // [G][16]  scale * ds
     __shared__ float st_lse[16], st_D[16], st_g[16];
-    __shared__ int rowlist[kThreads];
-    __shared__ int wcount[kThreads / kWave];
 
     const int tid = threadIdx.x;
     const int bgi = blockIdx.z;                       // b * Hkv + g
     const int b = bgi / d.Hkv, g = bgi % d.Hkv;
     const int key0 = blockIdx.x * kKeyTile;
-    const int nkeys = CMP ? d.ncmp : d.T;
-    const T *K = CMP ? (const T *)a.kc + (long)bgi * d.npad * dk : (const T *)a.k + (long)bgi * d.T * dk;
-    const T *V = CMP ? (const T *)a.vc + (long)bgi * d.npad * dv : (const T *)a.v + (long)bgi * d.T * dv;
+    const int nkeys = d.ncmp;
+    const T *K = (const T *)a.kc + (long)bgi * d.npad * dk;
+    const T *V = (const T *)a.vc + (long)bgi * d.npad * dv;
     for (int e = tid; e < kKeyTile * dk; e += kThreads) {
         const int r = e / dk, x = e % dk;
         Ks[r * KS + x] = key0 + r < nkeys ? to_f(K[(long)(key0 + r) * dk + x]) : 0.f;
@@ -311,23 +390,21 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys(BwdArgs a)
 #pragma unroll
     for (int u = 0; u < 16; u++) adk[u] = adv[u] = 0.f;
 
-    // One attending row t of branch br: every thread calls this together.
-    auto row = [&](int t, int br) {
+    // One attending row t: every thread calls this together.
+    auto row = [&](int t) {
         const long row0 = ((long)b * d.T + t) * d.Hq + (long)g * G;
         const T *qrow = (const T *)a.q + row0 * dk;
         const T *dorow = (const T *)a.dO + row0 * dv;
         for (int e = tid; e < G * dk; e += kThreads) qs[e] = to_f(qrow[e]);
         for (int e = tid; e < G * dv; e += kThreads) dos[e] = to_f(dorow[e]);
         if (tid < G) {
-            const float *st = a.rs + (row0 + tid) * kStat + br * 4;
+            const float *st = a.rs + (row0 + tid) * kStat;   // branch 0
             st_lse[tid] = st[0];
             st_D[tid] = st[1];
             st_g[tid] = st[2];
         }
         __syncthreads();
-        bool vis;
-        if (CMP) vis = kk < d.ncmp && 16 * kk + 31 <= t;
-        else vis = kk <= t && (br == 1 || kk >= t - d.w + 1);
+        const bool vis = kk < d.ncmp && 16 * kk + 31 <= t;
         const int h = part;
         if (h < G) {
             float p = 0.f, ds = 0.f;
@@ -355,52 +432,227 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys(BwdArgs a)
         __syncthreads();
     };
 
-    if (CMP) {
-        const int chunk = blockIdx.y;
-        const int t_lo = max(chunk * kRowChunk, 16 * key0 + 31), t_hi = min(d.T, (chunk + 1) * kRowChunk);
-        for (int t = t_lo; t < t_hi; t++) row(t, 0);
-        if (kk < d.npad) {
-            float *out = a.part + (((long)chunk * d.B * d.Hkv + bgi) * d.npad + kk) * (dk + dv);
+    const int chunk = blockIdx.y;
+    const int t_lo = max(chunk * kRowChunk, 16 * key0 + 31), t_hi = min(d.T, (chunk + 1) * kRowChunk);
+    for (int t = t_lo; t < t_hi; t++) row(t);
+    if (kk < d.npad) {
+        float *out = a.part + (((long)chunk * d.B * d.Hkv + bgi) * d.npad + kk) * (dk + dv);
 #pragma unroll
-            for (int u = 0; u < 16; u++) {
-                if (u < ndk) out[part + 16 * u] = adk[u];
-                if (u < ndv) out[dk + part + 16 * u] = adv[u];
+        for (int u = 0; u < 16; u++) {
+            if (u < ndk) out[part + 16 * u] = adk[u];
+            if (u < ndv) out[dk + part + 16 * u] = adv[u];
+        }
+    }
+}
+
+// Selection bitmap: bit t % 32 of word [bg][j][t / 32] is set when row t of
+// (b, KV head) bg selected block j (only blocks j <= t / 64 count).
+__global__ __launch_bounds__(kThreads) void k_bwd_fill_u32(uint32_t *p, long n)
+{
+    for (long i = (long)blockIdx.x * kThreads + threadIdx.x; i < n; i += (long)gridDim.x * kThreads) p[i] = 0u;
+}
+
+__global__ __launch_bounds__(kThreads) void k_bwd_selmap(BwdArgs a)
+{
+    const Dims &d = a.d;
+    const int t = blockIdx.x * kThreads + threadIdx.x, bgi = blockIdx.y;
+    if (t >= d.T) return;
+    const int nw = (d.T + 31) / 32;
+    const int32_t *ir = a.idx + ((long)bgi * d.T + t) * d.n;
+    for (int u = 0; u < d.n; u++) {
+        const int j = ir[u];
+        if (j >= 0 && j <= t / 64)
+            atomicOr(a.selbm + ((long)bgi * d.nb + j) * nw + t / 32, 1u << (t & 31));
+    }
+}
+
+// Raw-key gradients of one 64-key block (b, KV head, block jb).  K and V of
+// the block are staged once; the rows that attend to it come in a fixed
+// order: the window rows t = key0 .. key0+63+w-1, then the rows that selected
+// the block, ascending.  Each row's q and dO are loaded one row ahead.  Thread
+// (key = tid % 64, part = tid / 64) keeps dK, dV columns part, part+4, ...
+template <typename T, bool STAGED>
+__global__ __launch_bounds__(kThreads) void k_bwd_keys_blk(BwdArgs a)
+{
+    constexpr int kBK = 64;                       // keys per block
+    constexpr int kMaxCols = 64;                  // dk / 4 and dv / 4 for d <= 256
+    constexpr int PER = 16 / sizeof(T);           // elements per 16-byte load
+    extern __shared__ __align__(16) float smem[];
+    const Dims &d = a.d;
+    const int G = d.G, dk = d.dk, dv = d.dv;
+    const int KSt = stage_stride<T>(dk), VSt = stage_stride<T>(dv);
+    float *qs = smem;                   // [G][dk]
+    float *dos = qs + G * dk;           // [G][dv]
+    float *ps = dos + G * dv;           // [G][64] gate * p
+    float *dss = ps + G * kBK;          // [G][64] scale * ds
+    T *Ks = (T *)(dss + G * kBK);       // [64][KSt] (STAGED)
+    T *Vs = Ks + kBK * KSt;             // [64][VSt]
+    __shared__ float st_lse[16], st_D[16], st_g[16];
+    __shared__ uint16_t rows[kThreads * 32];  // selected rows of one bitmap chunk, less 32 * its first word
+    __shared__ int wcnt[kThreads];
+    __shared__ int nrows_s;
+
+    const int tid = threadIdx.x, jb = blockIdx.x, bgi = blockIdx.y;
+    const int b = bgi / d.Hkv, g = bgi % d.Hkv;
+    const int key0 = jb * kBK, nk = min(kBK, d.T - key0);
+    const T *K = (const T *)a.k + (long)bgi * d.T * dk;
+    const T *V = (const T *)a.v + (long)bgi * d.T * dv;
+    // the block's K and V rows: staged, or read in place when the staging
+    // buffers would not fit (fp32 with wide heads)
+    const T *Kx = K + (long)key0 * dk, *Vx = V + (long)key0 * dv;
+    int kst = dk, vst = dv;
+    if constexpr (STAGED) {
+        stage_rows<T>(Ks, KSt, K, key0, nk, dk);
+        stage_rows<T>(Vs, VSt, V, key0, nk, dv);
+        Kx = Ks;
+        Vx = Vs;
+        kst = KSt;
+        vst = VSt;
+    }
+    const int key = tid % kBK, part = tid / kBK, kk = key0 + key;
+    // this thread's dK and dV columns: whole groups of 4 columns, the groups
+    // split into 4 ranges (reads of q and dO are wave-uniform, 16 bytes)
+    const int gk = (dk / 4 + 3) / 4, gv = (dv / 4 + 3) / 4;        // groups per part, at most 16
+    const int ck0 = 4 * gk * part, cv0 = 4 * gv * part;              // first column
+    const int nk4 = max(0, min(4 * gk, dk - ck0)), nv4 = max(0, min(4 * gv, dv - cv0));   // columns owned
+    float adk[kMaxCols], adv[kMaxCols];
+#pragma unroll
+    for (int u = 0; u < kMaxCols; u++) adk[u] = adv[u] = 0.f;
+
+    // q / dO of a row into registers (16-byte pieces; at most 4 per thread)
+    const int qch = G * dk / PER, dch = G * dv / PER;
+    uint4 qreg[4], dreg[4];
+    float sreg[3];
+    auto fetch = [&](int t, int br) {
+        const long row0 = ((long)b * d.T + t) * d.Hq + (long)g * G;
+        const T *qrow = (const T *)a.q + row0 * dk;
+        const T *dorow = (const T *)a.dO + row0 * dv;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int c = tid + i * kThreads;
+            if (c < qch) qreg[i] = *(const uint4 *)(qrow + (long)c * PER);
+            if (c < dch) dreg[i] = *(const uint4 *)(dorow + (long)c * PER);
+        }
+        if (tid < G) {
+            const float *st = a.rs + (row0 + tid) * kStat + br * 4;
+            sreg[0] = st[0];
+            sreg[1] = st[1];
+            sreg[2] = st[2];
+        }
+    };
+    auto unpack = [&](float *dst, const uint4 &v) {
+        if constexpr (sizeof(T) == 2) {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                dst[2 * e] = __uint_as_float(w[e] << 16);
+                dst[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+            }
+        } else {
+            dst[0] = __uint_as_float(v.x);
+            dst[1] = __uint_as_float(v.y);
+            dst[2] = __uint_as_float(v.z);
+            dst[3] = __uint_as_float(v.w);
+        }
+    };
+    // one attending row, its q/dO already in registers; next = the row to
+    // fetch meanwhile (t < 0: none)
+    auto row = [&](int t, int br, int tn, int brn) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int c = tid + i * kThreads;
+            if (c < qch) unpack(qs + c * PER, qreg[i]);
+            if (c < dch) unpack(dos + c * PER, dreg[i]);
+        }
+        if (tid < G) {
+            st_lse[tid] = sreg[0];
+            st_D[tid] = sreg[1];
+            st_g[tid] = sreg[2];
+        }
+        __syncthreads();
+        if (tn >= 0) fetch(tn, brn);
+        const bool vis = kk < d.T && kk <= t && (br == 1 || kk >= t - d.w + 1);
+        for (int h = part; h < G; h += kThreads / kBK) {
+            float p = 0.f, ds = 0.f;
+            if (vis) {
+                const float z = dot_staged(qs + h * dk, Kx + key * kst, dk);
+                const float y = dot_staged(dos + h * dv, Vx + key * vst, dv);
+                const float gv = st_g[h];
+                p = __expf(z * d.scale - st_lse[h]);
+                ds = p * (gv * y - st_D[h]);
+                p *= gv;
+            }
+            ps[h * kBK + key] = p;
+            dss[h * kBK + key] = ds * d.scale;
+        }
+        __syncthreads();
+        for (int hh = 0; hh < G; hh++) {
+            const float pk = ps[hh * kBK + key], sk = dss[hh * kBK + key];
+            const float4 *dr = (const float4 *)(dos + hh * dv + cv0);
+            const float4 *qr = (const float4 *)(qs + hh * dk + ck0);
+#pragma unroll
+            for (int u4 = 0; u4 < kMaxCols / 4; u4++) {
+                if (4 * u4 < nv4) {
+                    const float4 x = dr[u4];
+                    adv[4 * u4] += pk * x.x;
+                    adv[4 * u4 + 1] += pk * x.y;
+                    adv[4 * u4 + 2] += pk * x.z;
+                    adv[4 * u4 + 3] += pk * x.w;
+                }
+                if (4 * u4 < nk4) {
+                    const float4 x = qr[u4];
+                    adk[4 * u4] += sk * x.x;
+                    adk[4 * u4 + 1] += sk * x.y;
+                    adk[4 * u4 + 2] += sk * x.z;
+                    adk[4 * u4 + 3] += sk * x.w;
+                }
             }
         }
-    } else {
-        // window rows: the tile's keys are in the window of t for t in [key0, key0+15+w-1]
-        const int whi = min(d.T - 1, key0 + kKeyTile - 1 + d.w - 1);
-        for (int t = key0; t <= whi; t++) row(t, 2);
-        // selected rows: t >= key0 whose list holds the tile's block
-        const int jb = key0 / 64;
-        const int32_t *ib = a.idx + (long)bgi * d.T * d.n;
-        const int wv = tid / kWave, ln = tid % kWave;
-        for (int base = key0; base < d.T; base += kThreads) {
-            const int t = base + tid;
-            bool mem = false;
-            if (t < d.T)
-                for (int u = 0; u < d.n; u++) mem |= ib[(long)t * d.n + u] == jb;
-            const unsigned long long bal = __ballot(mem);
-            if (ln == 0) wcount[wv] = __popcll(bal);
-            __syncthreads();
-            int off = 0, cnt = 0;
-            for (int w2 = 0; w2 < kThreads / kWave; w2++) {
-                off += w2 < wv ? wcount[w2] : 0;
-                cnt += wcount[w2];
+        __syncthreads();
+    };
+
+    // window rows
+    const int whi = min(d.T - 1, key0 + kBK - 1 + d.w - 1);
+    fetch(key0, 2);
+    for (int t = key0; t <= whi; t++) row(t, 2, t < whi ? t + 1 : -1, 2);
+    // selected rows, one bitmap chunk (kThreads words = 8192 rows) at a time
+    const int nw = (d.T + 31) / 32;
+    const uint32_t *bm = a.selbm + ((long)bgi * d.nb + jb) * nw;
+    for (int w0 = key0 / 32; w0 < nw; w0 += kThreads) {
+        const int w = w0 + tid;
+        const uint32_t word = w < nw ? bm[w] : 0u;
+        wcnt[tid] = __popc(word);
+        __syncthreads();
+        if (tid == 0) {
+            int acc = 0;
+            for (int i = 0; i < kThreads; i++) {
+                const int c = wcnt[i];
+                wcnt[i] = acc;
+                acc += c;
             }
-            if (mem) rowlist[off + __popcll(bal & ((1ull << ln) - 1ull))] = t;
-            __syncthreads();
-            for (int r = 0; r < cnt; r++) row(rowlist[r], 1);
-            __syncthreads();
+            nrows_s = acc;
         }
-        if (kk < d.T) {
-            float *ok = a.dk_raw + ((long)bgi * d.T + kk) * dk;
-            float *ov = a.dv_raw + ((long)bgi * d.T + kk) * dv;
+        __syncthreads();
+        {
+            int o = wcnt[tid];
+            for (uint32_t x = word; x; x &= x - 1) rows[o++] = (uint16_t)(32 * tid + __ffs(x) - 1);
+        }
+        __syncthreads();
+        const int nr = nrows_s;
+        const int tb = 32 * w0;
+        if (nr > 0) fetch(tb + rows[0], 1);
+        for (int r = 0; r < nr; r++) row(tb + rows[r], 1, r + 1 < nr ? tb + rows[r + 1] : -1, 1);
+        __syncthreads();
+    }
+    if (kk < d.T) {
+        float *ok = a.dk_raw + ((long)bgi * d.T + kk) * dk;
+        float *ov = a.dv_raw + ((long)bgi * d.T + kk) * dv;
 #pragma unroll
-            for (int u = 0; u < 16; u++) {
-                if (u < ndk) ok[part + 16 * u] = adk[u];
-                if (u < ndv) ov[part + 16 * u] = adv[u];
-            }
+        for (int u4 = 0; u4 < kMaxCols / 4; u4++) {
+            if (4 * u4 < nk4)
+                *(float4 *)(ok + ck0 + 4 * u4) = make_float4(adk[4 * u4], adk[4 * u4 + 1], adk[4 * u4 + 2], adk[4 * u4 + 3]);
+            if (4 * u4 < nv4)
+                *(float4 *)(ov + cv0 + 4 * u4) = make_float4(adv[4 * u4], adv[4 * u4 + 1], adv[4 * u4 + 2], adv[4 * u4 + 3]);
         }
     }
 }
@@ -586,6 +838,16 @@ hipError_t set_lds(K kernel, size_t bytes)
     return hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
+// whether a launch with `bytes` of dynamic LDS fits a workgroup's 160 KB
+// next to the kernel's static LDS
+template <typename K>
+bool fits_lds(K kernel, size_t bytes)
+{
+    hipFuncAttributes fa;
+    if (hipFuncGetAttributes(&fa, (const void *)kernel) != hipSuccess) return false;
+    return fa.sharedSizeBytes + bytes <= kLdsBytes;
+}
+
 template <typename T>
 hipError_t launch_all(const BwdArgs &A, hipStream_t s)
 {
@@ -594,21 +856,41 @@ hipError_t launch_all(const BwdArgs &A, hipStream_t s)
     hipError_t e;
     // 1. rows
     {
-        const size_t lds = sizeof(float) * ((size_t)d.G * (d.dk + 2 * d.dv + kChunk));
-        if ((e = set_lds(k_bwd_rows<T>, lds)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k_bwd_rows<T>, dim3(d.T, d.Hkv, d.B), dim3(kThreads), lds, s, A);
+        const size_t lds = sizeof(float) * ((size_t)d.G * (d.dk + 2 * d.dv + kChunk)) +
+                           sizeof(T) * (size_t)kChunk * (stage_stride<T>(d.dk) + stage_stride<T>(d.dv));
+        const size_t lds0 = sizeof(float) * ((size_t)d.G * (d.dk + 2 * d.dv + kChunk));
+        if (fits_lds(k_bwd_rows<T, true>, lds)) {
+            if ((e = set_lds(k_bwd_rows<T, true>, lds)) != hipSuccess) return e;
+            hipLaunchKernelGGL((k_bwd_rows<T, true>), dim3(d.T, d.Hkv, d.B), dim3(kThreads), lds, s, A);
+        } else {
+            if ((e = set_lds(k_bwd_rows<T, false>, lds0)) != hipSuccess) return e;
+            hipLaunchKernelGGL((k_bwd_rows<T, false>), dim3(d.T, d.Hkv, d.B), dim3(kThreads), lds0, s, A);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const size_t klds = sizeof(float) * ((size_t)kKeyTile * (d.dk + d.dv + 2) + (size_t)d.G * (d.dk + d.dv) +
                                          2 * (size_t)d.G * kKeyTile);
-    // 2. raw keys
-    if ((e = set_lds(k_bwd_keys<T, false>, klds)) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_bwd_keys<T, false>), dim3((d.T + kKeyTile - 1) / kKeyTile, 1, BH), dim3(kThreads), klds,
-                       s, A);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // 2. raw keys: the selection bitmap, then one workgroup per 64-key block
+    {
+        const long nwords = (long)BH * d.nb * ((d.T + 31) / 32);
+        hipLaunchKernelGGL(k_bwd_fill_u32, dim3((unsigned)std::min<long>((nwords + kThreads - 1) / kThreads, 4096)),
+                           dim3(kThreads), 0, s, A.selbm, nwords);
+        hipLaunchKernelGGL(k_bwd_selmap, dim3((d.T + kThreads - 1) / kThreads, BH), dim3(kThreads), 0, s, A);
+        const size_t blds = sizeof(float) * ((size_t)d.G * (d.dk + d.dv) + 2 * (size_t)d.G * 64) +
+                            sizeof(T) * (size_t)64 * (stage_stride<T>(d.dk) + stage_stride<T>(d.dv));
+        const size_t blds0 = sizeof(float) * ((size_t)d.G * (d.dk + d.dv) + 2 * (size_t)d.G * 64);
+        if (fits_lds(k_bwd_keys_blk<T, true>, blds)) {
+            if ((e = set_lds(k_bwd_keys_blk<T, true>, blds)) != hipSuccess) return e;
+            hipLaunchKernelGGL((k_bwd_keys_blk<T, true>), dim3(d.nb, BH), dim3(kThreads), blds, s, A);
+        } else {
+            if ((e = set_lds(k_bwd_keys_blk<T, false>, blds0)) != hipSuccess) return e;
+            hipLaunchKernelGGL((k_bwd_keys_blk<T, false>), dim3(d.nb, BH), dim3(kThreads), blds0, s, A);
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     // 3. compressed keys, then the sum over row chunks
-    if ((e = set_lds(k_bwd_keys<T, true>, klds)) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_bwd_keys<T, true>), dim3(d.npad / kKeyTile, A.nchunk, BH), dim3(kThreads), klds, s, A);
+    if ((e = set_lds(k_bwd_keys_cmp<T>, klds)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_bwd_keys_cmp<T>, dim3(d.npad / kKeyTile, A.nchunk, BH), dim3(kThreads), klds, s, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {
         const long n = (long)BH * d.npad * (d.dk + d.dv);
@@ -685,6 +967,7 @@ size_t backward_layout(const Dims &d, void *ws, BwdArgs *A)
     const size_t o_kcv = carve((size_t)BH * d.npad * (d.dk + d.dv));
     const size_t o_cs = carve((size_t)(d.dk + d.dv));
     const size_t o_gp = carve((size_t)d.Hq * ngc * 3 * (d.dk + 1));
+    const size_t o_bm = carve((size_t)BH * d.nb * ((d.T + 31) / 32));   // 32-bit words
     if (ws && A) {
         char *w = (char *)ws;
         A->rs = (float *)(w + o_rs);
@@ -694,6 +977,7 @@ size_t backward_layout(const Dims &d, void *ws, BwdArgs *A)
         A->kcv = (float *)(w + o_kcv);
         A->colsum = (float *)(w + o_cs);
         A->gpart = (float *)(w + o_gp);
+        A->selbm = (uint32_t *)(w + o_bm);
         A->nchunk = nchunk;
         A->ngc = ngc;
     }

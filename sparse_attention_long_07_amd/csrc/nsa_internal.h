@@ -107,6 +107,7 @@ struct BwdArgs {
     float *kcv;       // [B*Hkv][npad][dk+dv] compressed K/V gradient
     float *colsum;    // [dk+dv] sum of kcv over sequences, heads and blocks
     float *gpart;     // [Hq][ngc][3][dk+1] gate gradient per row chunk
+    uint32_t *selbm;  // [B*Hkv][NB][ceil(T/32)] bit t of row j: row t selected block j
     int nchunk, ngc;
 };
 size_t backward_layout(const Dims &d, void *ws, BwdArgs *A);   // bytes; carves A's buffers if ws

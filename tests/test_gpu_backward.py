@@ -90,6 +90,8 @@ SMALL = [
     ("fp32_T300_g5_w64", NSAShape(1, 300, 2, 5, 32, 16, FP32, n=3, w=64), False, False),
     ("bf16_T31", NSAShape(1, 31, 1, 2, 16, 16), False, False),
     ("fp32_T1", NSAShape(1, 1, 1, 1, 8, 8, FP32), True, False),
+    # K/V of a key chunk too wide to stage in LDS: read in place
+    ("fp32_T260_g16_d256_unstaged", NSAShape(1, 260, 1, 16, 256, 256, FP32, n=4, w=100), False, True),
 ]
 
 
