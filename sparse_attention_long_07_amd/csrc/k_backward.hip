@@ -48,7 +48,7 @@ constexpr int kKeyTile = 16;     // compressed blocks per workgroup of pass 3
 constexpr int kRowChunk = 1024;  // rows per partial of the compressed-key gradient
 constexpr int kGateRows = 256;   // rows per partial of the gate gradient
 constexpr size_t kLdsBytes = 160 * 1024;   // LDS of one workgroup on gfx950
-constexpr int kStat = 12;        // per (row, head): {lse, D, gate, dz} for each of the 3 branches
+constexpr int kStat = kBwdStat;  // per (row, head): {lse, D, gate, dz} for each of the 3 branches
 
 __device__ __forceinline__ float wave_max(float v)
 {
@@ -876,17 +876,21 @@ hipError_t launch_all(const BwdArgs &A, hipStream_t s)
         hipLaunchKernelGGL(k_bwd_fill_u32, dim3((unsigned)std::min<long>((nwords + kThreads - 1) / kThreads, 4096)),
                            dim3(kThreads), 0, s, A.selbm, nwords);
         hipLaunchKernelGGL(k_bwd_selmap, dim3((d.T + kThreads - 1) / kThreads, BH), dim3(kThreads), 0, s, A);
-        const size_t blds = sizeof(float) * ((size_t)d.G * (d.dk + d.dv) + 2 * (size_t)d.G * 64) +
-                            sizeof(T) * (size_t)64 * (stage_stride<T>(d.dk) + stage_stride<T>(d.dv));
-        const size_t blds0 = sizeof(float) * ((size_t)d.G * (d.dk + d.dv) + 2 * (size_t)d.G * 64);
-        if (fits_lds(k_bwd_keys_blk<T, true>, blds)) {
-            if ((e = set_lds(k_bwd_keys_blk<T, true>, blds)) != hipSuccess) return e;
-            hipLaunchKernelGGL((k_bwd_keys_blk<T, true>), dim3(d.nb, BH), dim3(kThreads), blds, s, A);
+        if (bwd_keys_mfma_ok(d)) {
+            if ((e = launch_bwd_keys_mfma(A, s)) != hipSuccess) return e;
         } else {
-            if ((e = set_lds(k_bwd_keys_blk<T, false>, blds0)) != hipSuccess) return e;
-            hipLaunchKernelGGL((k_bwd_keys_blk<T, false>), dim3(d.nb, BH), dim3(kThreads), blds0, s, A);
+            const size_t blds = sizeof(float) * ((size_t)d.G * (d.dk + d.dv) + 2 * (size_t)d.G * 64) +
+                                sizeof(T) * (size_t)64 * (stage_stride<T>(d.dk) + stage_stride<T>(d.dv));
+            const size_t blds0 = sizeof(float) * ((size_t)d.G * (d.dk + d.dv) + 2 * (size_t)d.G * 64);
+            if (fits_lds(k_bwd_keys_blk<T, true>, blds)) {
+                if ((e = set_lds(k_bwd_keys_blk<T, true>, blds)) != hipSuccess) return e;
+                hipLaunchKernelGGL((k_bwd_keys_blk<T, true>), dim3(d.nb, BH), dim3(kThreads), blds, s, A);
+            } else {
+                if ((e = set_lds(k_bwd_keys_blk<T, false>, blds0)) != hipSuccess) return e;
+                hipLaunchKernelGGL((k_bwd_keys_blk<T, false>), dim3(d.nb, BH), dim3(kThreads), blds0, s, A);
+            }
+            if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // 3. compressed keys, then the sum over row chunks
     if ((e = set_lds(k_bwd_keys_cmp<T>, klds)) != hipSuccess) return e;
@@ -968,6 +972,10 @@ size_t backward_layout(const Dims &d, void *ws, BwdArgs *A)
     const size_t o_cs = carve((size_t)(d.dk + d.dv));
     const size_t o_gp = carve((size_t)d.Hq * ngc * 3 * (d.dk + 1));
     const size_t o_bm = carve((size_t)BH * d.nb * ((d.T + 31) / 32));   // 32-bit words
+    int krc = 0, nkc = 0;
+    size_t kp_floats = 0;
+    if (bwd_keys_mfma_ok(d)) bwd_key_chunks(d, &krc, &nkc, &kp_floats);
+    const size_t o_kp = carve(kp_floats);
     if (ws && A) {
         char *w = (char *)ws;
         A->rs = (float *)(w + o_rs);
@@ -978,6 +986,9 @@ size_t backward_layout(const Dims &d, void *ws, BwdArgs *A)
         A->colsum = (float *)(w + o_cs);
         A->gpart = (float *)(w + o_gp);
         A->selbm = (uint32_t *)(w + o_bm);
+        A->kpart = (float *)(w + o_kp);
+        A->krc = krc;
+        A->nkc = nkc;
         A->nchunk = nchunk;
         A->ngc = ngc;
     }

@@ -108,10 +108,20 @@ struct BwdArgs {
     float *colsum;    // [dk+dv] sum of kcv over sequences, heads and blocks
     float *gpart;     // [Hq][ngc][3][dk+1] gate gradient per row chunk
     uint32_t *selbm;  // [B*Hkv][NB][ceil(T/32)] bit t of row j: row t selected block j
+    float *kpart;     // matrix-core key pass: per row chunk c, [B*Hkv][min(T, (c+1) krc)][dk+dv] partial raw dK, dV
     int nchunk, ngc;
+    int krc, nkc;     // rows per chunk and chunks of the matrix-core key pass
 };
+// per (row, head) row statistics of the backward: {lse, D, gate, dz} for each
+// of the 3 branches (compressed, selected, window)
+constexpr int kBwdStat = 12;
 size_t backward_layout(const Dims &d, void *ws, BwdArgs *A);   // bytes; carves A's buffers if ws
 hipError_t launch_backward(const BwdArgs &A, hipStream_t s);
+// raw-key gradients on the matrix cores (bf16, 16 heads per KV head, the
+// forward's (d_k, d_v) pairs); needs selbm built and rs filled
+bool bwd_keys_mfma_ok(const Dims &d);
+void bwd_key_chunks(const Dims &d, int *rc, int *nkc, size_t *part_floats);
+hipError_t launch_bwd_keys_mfma(const BwdArgs &A, hipStream_t s);
 
 // Generic kernels: plain VALU code, any supported shape, fp32 or bf16 storage.
 // Compression launchers: every block of the T-token sequences when len_new is

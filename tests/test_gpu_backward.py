@@ -90,6 +90,9 @@ SMALL = [
     ("fp32_T300_g5_w64", NSAShape(1, 300, 2, 5, 32, 16, FP32, n=3, w=64), False, False),
     ("bf16_T31", NSAShape(1, 31, 1, 2, 16, 16), False, False),
     ("fp32_T1", NSAShape(1, 1, 1, 1, 8, 8, FP32), True, False),
+    # matrix-core raw-key pass at the other head widths, over 2 and 3 row chunks
+    ("bf16_T1500_g16_d64_B2H2_randsel", NSAShape(2, 1500, 2, 16, 64, 64, n=6, w=200), False, True),
+    ("bf16_T2100_g16_d128_randsel", NSAShape(1, 2100, 1, 16, 128, 128, n=8, w=256), False, True),
     # K/V of a key chunk too wide to stage in LDS: read in place
     ("fp32_T260_g16_d256_unstaged", NSAShape(1, 260, 1, 16, 256, 256, FP32, n=4, w=100), False, True),
 ]
