@@ -45,7 +45,7 @@ constexpr int kThreads = 256;
 constexpr int kWave = 64;
 constexpr int kChunk = 64;       // keys per chunk of the row pass
 constexpr int kKeyTile = 16;     // compressed blocks per workgroup of pass 3
-constexpr int kRowChunk = 1024;  // rows per partial of the compressed-key gradient
+constexpr int kRowChunk = kBwdRowChunk;  // rows per partial of the compressed-key gradient
 constexpr int kGateRows = 256;   // rows per partial of the gate gradient
 constexpr size_t kLdsBytes = 160 * 1024;   // LDS of one workgroup on gfx950
 constexpr int kStat = kBwdStat;  // per (row, head): {lse, D, gate, dz} for each of the 3 branches
@@ -893,9 +893,13 @@ hipError_t launch_all(const BwdArgs &A, hipStream_t s)
         }
     }
     // 3. compressed keys, then the sum over row chunks
-    if ((e = set_lds(k_bwd_keys_cmp<T>, klds)) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_bwd_keys_cmp<T>, dim3(d.npad / kKeyTile, A.nchunk, BH), dim3(kThreads), klds, s, A);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (bwd_keys_mfma_ok(d)) {
+        if ((e = launch_bwd_cmp_keys_mfma(A, s)) != hipSuccess) return e;
+    } else {
+        if ((e = set_lds(k_bwd_keys_cmp<T>, klds)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k_bwd_keys_cmp<T>, dim3(d.npad / kKeyTile, A.nchunk, BH), dim3(kThreads), klds, s, A);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     {
         const long n = (long)BH * d.npad * (d.dk + d.dv);
         hipLaunchKernelGGL(k_bwd_sum_parts, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,

@@ -1,6 +1,7 @@
-// Raw-key gradients of the window and selected branches on the matrix cores
-// (bf16 storage, 16 query heads per KV head, (d_k, d_v) = (192, 128),
-// (128, 128) or (64, 64)).
+// Key-side gradients on the matrix cores (bf16 storage, 16 query heads per KV
+// head, (d_k, d_v) = (192, 128), (128, 128) or (64, 64)): raw keys from the
+// window and selected branches, and compressed keys from the compressed
+// branch (row t sees compressed key i when 16 i + 31 <= t).
 //
 // Per KV head, a query row t attends to raw key s in the selected branch when
 // s's 64-token block is in t's selection and s <= t, and in the window branch
@@ -10,9 +11,10 @@
 // summed over the rows and heads that attend to s.
 //
 // One workgroup owns one 64-key block j and one chunk of RC consecutive rows.
-// It visits the chunk's window rows of the block, then the chunk's rows whose
-// selection holds j (read from the (block, row) bitmap in ascending order), in
-// tiles of 4 rows x 16 heads = 64 query vectors.  Wave w keeps the fragments
+// Raw keys: it visits the chunk's window rows of the block, then the chunk's
+// rows whose selection holds j (read from the (block, row) bitmap in ascending
+// order); compressed keys: the chunk's rows from 16 (64 j) + 31 on.  Rows come
+// in tiles of 4 rows x 16 heads = 64 query vectors.  Wave w keeps the fragments
 // of keys 16w .. 16w+15 in registers and per tile forms
 //   S = Q K^T, dP = dO V^T              (16x16x32 MFMA, A from LDS)
 //   P, dS                               (fp32, packed to bf16 in place)
@@ -54,7 +56,7 @@ __host__ __device__ __forceinline__ long part_base(int c, int rc, long BH, int D
     return (long)rc * c * (c + 1) / 2 * BH * DD;
 }
 
-template <int DK, int DV>
+template <int DK, int DV, bool CMP>
 __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
 {
     constexpr int QS = DK + 16, OS = DV + 16;   // LDS row strides (bf16): 16-byte rows, transposing reads conflict-free
@@ -73,23 +75,26 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
     const int jb = blockIdx.x, c = blockIdx.y, bgi = blockIdx.z;
     const int b = bgi / d.Hkv, g = bgi % d.Hkv;
     const int key0 = jb * 64;
-    const int rc = a.krc;
+    const int rc = CMP ? kBwdRowChunk : a.krc;
     const int rbeg = c * rc, rend = min(d.T, rbeg + rc);
-    if (rend <= key0) return;   // rows before the block: nothing attends, and no partial is read
+    // raw keys: rows before the block do not attend, and no partial is read
+    // for such a chunk; compressed keys: every chunk's partial is summed
+    if (!CMP && rend <= key0) return;
     const long BH = (long)d.B * d.Hkv;
-    const int kend = rend;      // keys held by this chunk's partial
-    float *outp = a.kpart + part_base(c, rc, BH, DD) + ((long)bgi * kend) * DD;
+    float *outp = CMP ? a.part + ((long)c * BH + bgi) * d.npad * DD
+                      : a.kpart + part_base(c, rc, BH, DD) + ((long)bgi * rend) * DD;   // rend keys per head
 
     // this lane's key and its K, V fragments (B operands of S and dP)
     const int kk = key0 + 16 * wave + li;
+    const int nkeys = CMP ? d.ncmp : d.T, kstride = CMP ? d.npad : d.T;
     u32x4 kf[NQ], vf[NO];
     {
-        const uint16_t *K = (const uint16_t *)a.k + ((long)bgi * d.T + kk) * DK + 8 * lg;
-        const uint16_t *V = (const uint16_t *)a.v + ((long)bgi * d.T + kk) * DV + 8 * lg;
+        const uint16_t *K = (const uint16_t *)(CMP ? a.kc : a.k) + ((long)bgi * kstride + kk) * DK + 8 * lg;
+        const uint16_t *V = (const uint16_t *)(CMP ? a.vc : a.v) + ((long)bgi * kstride + kk) * DV + 8 * lg;
 #pragma unroll
-        for (int i = 0; i < NQ; i++) kf[i] = kk < d.T ? ld16(K + 32 * i) : u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < NQ; i++) kf[i] = kk < nkeys ? ld16(K + 32 * i) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int i = 0; i < NO; i++) vf[i] = kk < d.T ? ld16(V + 32 * i) : u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < NO; i++) vf[i] = kk < nkeys ? ld16(V + 32 * i) : u32x4{0u, 0u, 0u, 0u};
     }
     f32x4 acck[DK / 16], accv[DV / 16];
 #pragma unroll
@@ -148,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
             s_g[tid] = st2;
         }
     };
-    // one tile from LDS; tr = its rows (-1: empty slot), br = branch (1 selected, 2 window)
+    // one tile from LDS; tr = its rows (-1: empty slot), br = branch (0 compressed, 1 selected, 2 window)
     auto tile = [&](const int *tr, int br) {
         f32x4 S[kRows], P[kRows];
 #pragma unroll
@@ -171,7 +176,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
 #pragma unroll
         for (int r = 0; r < kRows; r++) {
             const int t = tr[r];
-            const bool vis = kk <= t && (br == 1 || kk > t - d.w);
+            bool vis;
+            if constexpr (CMP) vis = kk < d.ncmp && 16 * kk + 31 <= t;
+            else vis = kk <= t && (br == 1 || kk > t - d.w);
             const f32x4 l4 = *(const f32x4 *)(s_lse + 16 * r + 4 * lg);
             const f32x4 D4 = *(const f32x4 *)(s_D + 16 * r + 4 * lg);
             const f32x4 g4 = *(const f32x4 *)(s_g + 16 * r + 4 * lg);
@@ -242,6 +249,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
         }
     };
 
+    if constexpr (CMP) {
+        const int lo = max(rbeg, 16 * key0 + 31);
+        run(rend - lo, 0, [&](int i) { return lo + i; });
+    } else {
     // window rows of the block in this chunk
     {
         const int lo = max(key0, rbeg), hi = min(min(d.T - 1, key0 + 63 + d.w - 1), rend - 1);
@@ -278,8 +289,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
             run(nsel_s, 1, [&](int i) { return base + (int)rows[i]; });
         }
     }
+    }
     // partial dK, dV of the block: C[i = column][j = key] sits in lane j + 16 (i / 4), element i % 4
-    if (kk < d.T) {
+    if (kk < kstride) {
         float *o = outp + (long)kk * DD;
 #pragma unroll
         for (int dt = 0; dt < DK / 16; dt++) *(f32x4 *)(o + 16 * dt + 4 * lg) = acck[dt];
@@ -312,11 +324,20 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_sum(BwdArgs a)
 }
 
 template <int DK, int DV>
+hipError_t launch_cmp_dims(const BwdArgs &A, hipStream_t s)
+{
+    const Dims &d = A.d;
+    hipLaunchKernelGGL((k_bwd_keys_mfma<DK, DV, true>), dim3(d.npad / 64, A.nchunk, d.B * d.Hkv), dim3(kThreads), 0, s,
+                       A);
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
 hipError_t launch_dims(const BwdArgs &A, hipStream_t s)
 {
     const Dims &d = A.d;
     const int BH = d.B * d.Hkv;
-    hipLaunchKernelGGL((k_bwd_keys_mfma<DK, DV>), dim3(d.nb, A.nkc, BH), dim3(kThreads), 0, s, A);
+    hipLaunchKernelGGL((k_bwd_keys_mfma<DK, DV, false>), dim3(d.nb, A.nkc, BH), dim3(kThreads), 0, s, A);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long n4 = (long)BH * d.T * ((DK + DV) / 4);
@@ -348,6 +369,14 @@ hipError_t launch_bwd_keys_mfma(const BwdArgs &A, hipStream_t s)
     if (d.dk == 192) return launch_dims<192, 128>(A, s);
     if (d.dk == 128) return launch_dims<128, 128>(A, s);
     return launch_dims<64, 64>(A, s);
+}
+
+hipError_t launch_bwd_cmp_keys_mfma(const BwdArgs &A, hipStream_t s)
+{
+    const Dims &d = A.d;
+    if (d.dk == 192) return launch_cmp_dims<192, 128>(A, s);
+    if (d.dk == 128) return launch_cmp_dims<128, 128>(A, s);
+    return launch_cmp_dims<64, 64>(A, s);
 }
 
 }  // namespace nsa

@@ -115,6 +115,8 @@ struct BwdArgs {
 // per (row, head) row statistics of the backward: {lse, D, gate, dz} for each
 // of the 3 branches (compressed, selected, window)
 constexpr int kBwdStat = 12;
+// rows per partial of the compressed-key gradient
+constexpr int kBwdRowChunk = 1024;
 size_t backward_layout(const Dims &d, void *ws, BwdArgs *A);   // bytes; carves A's buffers if ws
 hipError_t launch_backward(const BwdArgs &A, hipStream_t s);
 // raw-key gradients on the matrix cores (bf16, 16 heads per KV head, the
@@ -122,6 +124,8 @@ hipError_t launch_backward(const BwdArgs &A, hipStream_t s);
 bool bwd_keys_mfma_ok(const Dims &d);
 void bwd_key_chunks(const Dims &d, int *rc, int *nkc, size_t *part_floats);
 hipError_t launch_bwd_keys_mfma(const BwdArgs &A, hipStream_t s);
+// compressed-key gradient partials (part) on the matrix cores, same shapes
+hipError_t launch_bwd_cmp_keys_mfma(const BwdArgs &A, hipStream_t s);
 
 // Generic kernels: plain VALU code, any supported shape, fp32 or bf16 storage.
 // Compression launchers: every block of the T-token sequences when len_new is
