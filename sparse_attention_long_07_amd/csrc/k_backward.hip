@@ -14,8 +14,10 @@
 // + PE)): dW = sum_i dK_cmp[i] (x_i + PE)^T, dPE = W^T sum_i dK_cmp[i] and
 // token 16i + tau collects (W^T dK_cmp[i]) at slot tau.
 //
-// Passes, all plain VALU arithmetic in fp32 and free of float atomics, so the
-// result is the same bit for bit on every run:
+// Passes, free of float atomics, so the result is the same bit for bit on
+// every run.  For bf16 storage with 16 query heads per KV head and the
+// forward's (d_k, d_v) pairs, passes 1-3 run on the matrix cores
+// (k_backward_mfma.hip); every other shape takes the fp32 VALU kernels here:
 //  1. k_bwd_rows      one (position, KV head) per workgroup: recomputes the
 //                     three branches (log-sum-exp, output), forms D, the gate
 //                     terms and the complete dq; stores the per-row
@@ -859,7 +861,9 @@ hipError_t launch_all(const BwdArgs &A, hipStream_t s)
         const size_t lds = sizeof(float) * ((size_t)d.G * (d.dk + 2 * d.dv + kChunk)) +
                            sizeof(T) * (size_t)kChunk * (stage_stride<T>(d.dk) + stage_stride<T>(d.dv));
         const size_t lds0 = sizeof(float) * ((size_t)d.G * (d.dk + 2 * d.dv + kChunk));
-        if (fits_lds(k_bwd_rows<T, true>, lds)) {
+        if (bwd_keys_mfma_ok(d)) {
+            if ((e = launch_bwd_rows_mfma(A, s)) != hipSuccess) return e;
+        } else if (fits_lds(k_bwd_rows<T, true>, lds)) {
             if ((e = set_lds(k_bwd_rows<T, true>, lds)) != hipSuccess) return e;
             hipLaunchKernelGGL((k_bwd_rows<T, true>), dim3(d.T, d.Hkv, d.B), dim3(kThreads), lds, s, A);
         } else {

@@ -107,31 +107,31 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
     // query vector each) log2-scaled lse, D and gate
     u32x4 qr[NQ], orr[NO];
     float st0 = 0.f, st1 = 0.f, st2 = 0.f;
+    // row of slot r (r depends on the thread: a select chain, not an indexed array)
+    auto slot = [](const int *tr, int r) { return r == 0 ? tr[0] : r == 1 ? tr[1] : r == 2 ? tr[2] : tr[3]; };
     auto fetch = [&](const int *tr, int br) {
 #pragma unroll
         for (int i = 0; i < NQ; i++) {
             const int p = tid + kThreads * i;          // piece: row slot p / (2 DK), offset 8 (p % (2 DK))
-            const int r = p / (2 * DK), e = 8 * (p % (2 * DK));
-            qr[i] = tr[r] >= 0 ? ld16((const uint16_t *)a.q + ((long)b * d.T + tr[r]) * d.Hq * DK + (long)g * 16 * DK + e)
-                               : u32x4{0u, 0u, 0u, 0u};
+            const int r = p / (2 * DK), e = 8 * (p % (2 * DK)), t = slot(tr, r);
+            qr[i] = t >= 0 ? ld16((const uint16_t *)a.q + ((long)b * d.T + t) * d.Hq * DK + (long)g * 16 * DK + e)
+                           : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int i = 0; i < NO; i++) {
             const int p = tid + kThreads * i;
-            const int r = p / (2 * DV), e = 8 * (p % (2 * DV));
-            orr[i] = tr[r] >= 0 ? ld16((const uint16_t *)a.dO + ((long)b * d.T + tr[r]) * d.Hq * DV + (long)g * 16 * DV + e)
-                                : u32x4{0u, 0u, 0u, 0u};
+            const int r = p / (2 * DV), e = 8 * (p % (2 * DV)), t = slot(tr, r);
+            orr[i] = t >= 0 ? ld16((const uint16_t *)a.dO + ((long)b * d.T + t) * d.Hq * DV + (long)g * 16 * DV + e)
+                            : u32x4{0u, 0u, 0u, 0u};
         }
         if (tid < kM) {
-            const int r = tid >> 4, h = tid & 15;
-            if (tr[r] >= 0) {
-                const float *st = a.rs + (((long)b * d.T + tr[r]) * d.Hq + g * 16 + h) * kBwdStat + br * 4;
-                st0 = st[0] * kLog2e;
-                st1 = st[1];
-                st2 = st[2];
-            } else {
-                st0 = st1 = st2 = 0.f;
-            }
+            const int r = tid >> 4, h = tid & 15, t = slot(tr, r);
+            // an empty slot reads row 0 and keeps zeros (no branch around the loads)
+            const float *st = a.rs + (((long)b * d.T + max(t, 0)) * d.Hq + g * 16 + h) * kBwdStat + br * 4;
+            const float x0 = st[0], x1 = st[1], x2 = st[2];
+            st0 = t >= 0 ? x0 * kLog2e : 0.f;
+            st1 = t >= 0 ? x1 : 0.f;
+            st2 = t >= 0 ? x2 : 0.f;
         }
     };
     auto stash = [&]() {
@@ -300,6 +300,231 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
     }
 }
 
+// Row pass: one wave per (b, t, KV head) with its 16 heads; per branch (0
+// compressed, 1 selected, 2 window) two sweeps over 64-key chunks:
+//   1. S^T = K Q^T and dP^T = V dO^T; online max m, sum l of exp(S) and sum of
+//      exp(S) dP, which give lse and dO . o_branch = (sum p dP) / l without
+//      forming o_branch; then D = gate dO . o and the gate's logit gradient.
+//   2. S^T, dP^T again; dS^T = scale p (gate dP - D) feeds dQ^T += K^T dS^T
+//      directly from the score layout; K reaches the A operand through a
+//      wave-private 32-key LDS buffer read with transposing reads.
+// Chunks (as in the forward): compressed blocks [0, nvis), 16 i + 31 <= t;
+// the distinct valid selected blocks in ascending order, tokens <= t; the
+// window [t - w + 1, t].  Loads of keys outside a chunk's valid range read the
+// nearest valid key instead, so no unwritten or stale value enters a product.
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads) void k_bwd_rows_mfma(BwdArgs a)
+{
+    constexpr int KS = DK + 16;
+    constexpr int NQ = DK / 32, NO = DV / 32;
+    __shared__ __align__(16) uint16_t kws[kThreads / 64][32 * KS];
+    __shared__ int blks[kThreads / 64][16];
+    const Dims &d = a.d;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int t = blockIdx.x * (kThreads / 64) + wave, g = blockIdx.y, b = blockIdx.z;
+    if (t >= d.T) return;   // waves never wait for each other
+    uint16_t *kw = kws[wave];
+    int *blk = blks[wave];
+    const long bgi = (long)b * d.Hkv + g;
+    const long row0 = ((long)b * d.T + t) * d.Hq + (long)g * 16;
+    const int h = li;   // the head of this lane in the B operands and the score layout
+
+    // B operands Q^T, dO^T: head li, columns 32 c + 8 lg .. +7
+    u32x4 qf[NQ], of[NO];
+#pragma unroll
+    for (int c = 0; c < NQ; c++) qf[c] = ld16((const uint16_t *)a.q + (row0 + h) * DK + 32 * c + 8 * lg);
+#pragma unroll
+    for (int c = 0; c < NO; c++) of[c] = ld16((const uint16_t *)a.dO + (row0 + h) * DV + 32 * c + 8 * lg);
+    float gate[3];
+#pragma unroll
+    for (int br = 0; br < 3; br++) {
+        const uint16_t *wr = (const uint16_t *)a.wg + (((long)g * 16 + h) * 3 + br) * DK + 8 * lg;
+        float z = 0.f;
+#pragma unroll
+        for (int c = 0; c < NQ; c++) z = dot8_bf16(qf[c], ld16(wr + 32 * c), z);
+        z += __shfl_xor(z, 16);
+        z += __shfl_xor(z, 32);
+        z += bf2f(((const uint16_t *)a.bg)[((long)g * 16 + h) * 3 + br]);
+        gate[br] = 1.f / (1.f + __expf(-z));
+    }
+    // the distinct valid selected blocks, ascending
+    int nsel;
+    {
+        const int jcur = t / 64;
+        const int j = lane < d.n ? a.idx[(bgi * d.T + t) * d.n + lane] : -1;
+        bool keep = j >= 0 && j <= jcur;
+        for (int u = 0; u < d.n; u++) {
+            const int x = __shfl(j, u);
+            if (u < lane && x == j) keep = false;
+        }
+        const int kx = keep ? j : 0x7fffffff;
+        int rank = 0;
+        nsel = 0;
+        for (int u = 0; u < d.n; u++) {
+            const int x = __shfl(kx, u);
+            rank += x < kx;
+            nsel += x != 0x7fffffff;
+        }
+        if (keep) blk[rank] = j;
+    }
+
+    const float sl2 = d.scale * kLog2e;
+    const int nvis = t >= 31 ? (t - 31) / 16 + 1 : 0;
+    const int wlo = max(0, t - d.w + 1);
+    // S^T and dP^T of one 16-key tile; kfr gets its K rows (A operand layout:
+    // key li, columns 32 c + 8 lg .. +7)
+    auto scores = [&](const uint16_t *K, const uint16_t *V, int k16, int klo, int khi, f32x4 &S, f32x4 &P,
+                      u32x4 *kfr) {
+        const int kl = min(max(k16 + li, klo), khi);
+        S = f32x4{0.f, 0.f, 0.f, 0.f};
+        P = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NQ; c++) {
+            kfr[c] = ld16(K + (long)kl * DK + 32 * c + 8 * lg);
+            S = mfma16(as_bf16x8(kfr[c]), as_bf16x8(qf[c]), S);
+        }
+#pragma unroll
+        for (int c = 0; c < NO; c++)
+            P = mfma16(as_bf16x8(ld16(V + (long)kl * DV + 32 * c + 8 * lg)), as_bf16x8(of[c]), P);
+    };
+    f32x4 dqa[DK / 16];
+#pragma unroll
+    for (int i = 0; i < DK / 16; i++) dqa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float dzs[3];
+    const int trow = li >> 2, tcol = 4 * (li & 3);
+    for (int br = 0; br < 3; br++) {
+        const uint16_t *K = br == 0 ? (const uint16_t *)a.kc + bgi * d.npad * DK : (const uint16_t *)a.k + bgi * d.T * DK;
+        const uint16_t *V = br == 0 ? (const uint16_t *)a.vc + bgi * d.npad * DV : (const uint16_t *)a.v + bgi * d.T * DV;
+        const int nch = br == 0 ? (nvis + 63) / 64 : br == 1 ? nsel : (t - wlo + 64) / 64;
+        auto chunk = [&](int ch, int &key0, int &klo, int &khi) {
+            if (br == 0) {
+                key0 = 64 * ch;
+                klo = 0;
+                khi = nvis - 1;
+            } else if (br == 1) {
+                key0 = 64 * blk[ch];
+                klo = key0;
+                khi = min(t, key0 + 63);
+            } else {
+                key0 = wlo + 64 * ch;
+                klo = wlo;
+                khi = t;
+            }
+        };
+        // sweep 1
+        float m = -INFINITY, l = 0.f, acc = 0.f;
+        for (int ch = 0; ch < nch; ch++) {
+            int key0, klo, khi;
+            chunk(ch, key0, klo, khi);
+            float sc[4][4], dp[4][4];
+            float mc = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 4; kt++) {
+                f32x4 S, P;
+                u32x4 kfr[NQ];
+                scores(K, V, key0 + 16 * kt, klo, khi, S, P, kfr);
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int key = key0 + 16 * kt + 4 * lg + e;
+                    sc[kt][e] = key >= klo && key <= khi ? S[e] * sl2 : -INFINITY;
+                    dp[kt][e] = P[e];
+                    mc = fmaxf(mc, sc[kt][e]);
+                }
+            }
+            mc = fmaxf(mc, __shfl_xor(mc, 16));
+            mc = fmaxf(mc, __shfl_xor(mc, 32));
+            const float mn = fmaxf(m, mc);
+            const float al = fast_exp2(m - mn);
+            float ls = 0.f, as = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < 4; kt++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const float p = fast_exp2(sc[kt][e] - mn);
+                    ls += p;
+                    as = __builtin_fmaf(p, sc[kt][e] == -INFINITY ? 0.f : dp[kt][e], as);
+                }
+            l = __builtin_fmaf(l, al, ls);
+            acc = __builtin_fmaf(acc, al, as);
+            m = mn;
+        }
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        acc += __shfl_xor(acc, 16);
+        acc += __shfl_xor(acc, 32);
+        const float lse2 = l > 0.f ? m + fast_log2(l) : -INFINITY;
+        const float dOo = l > 0.f ? acc / l : 0.f;
+        const float gv = gate[br];
+        const float D = gv * dOo;
+        dzs[br] = dOo * gv * (1.f - gv);
+        if (lg == 0) {
+            float *st = a.rs + (row0 + h) * kBwdStat + br * 4;
+            st[0] = lse2 * 0.6931471805599453f;
+            st[1] = D;
+            st[2] = gv;
+            st[3] = dzs[br];
+        }
+        // sweep 2
+        for (int ch = 0; ch < nch; ch++) {
+            int key0, klo, khi;
+            chunk(ch, key0, klo, khi);
+#pragma unroll
+            for (int half = 0; half < 2; half++) {
+                float ds[2][4];
+#pragma unroll
+                for (int kh = 0; kh < 2; kh++) {
+                    f32x4 S, P;
+                    u32x4 kfr[NQ];
+                    const int k16 = key0 + 32 * half + 16 * kh;
+                    scores(K, V, k16, klo, khi, S, P, kfr);
+#pragma unroll
+                    for (int c = 0; c < NQ; c++) st16(kw + (16 * kh + li) * KS + 32 * c + 8 * lg, kfr[c]);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const int key = k16 + 4 * lg + e;
+                        const float p =
+                            key >= klo && key <= khi ? fast_exp2(__builtin_fmaf(S[e], sl2, -lse2)) : 0.f;
+                        ds[kh][e] = p * __builtin_fmaf(gv, P[e], -D) * d.scale;
+                    }
+                }
+                // contraction slot 8 lg + e <-> key 4 lg + e (e < 4) or 16 + 4 lg + e - 4 of the 32
+                u32x4 y;
+                y[0] = pack_bf16x2(ds[0][0], ds[0][1]);
+                y[1] = pack_bf16x2(ds[0][2], ds[0][3]);
+                y[2] = pack_bf16x2(ds[1][0], ds[1][1]);
+                y[3] = pack_bf16x2(ds[1][2], ds[1][3]);
+                const bf16x8 bs = as_bf16x8(y);
+                const int r0 = 4 * lg + trow;
+#pragma unroll
+                for (int dt = 0; dt < DK / 16; dt++) {
+                    const uint2 lo = ld_tr16(kw + r0 * KS + 16 * dt + tcol);
+                    const uint2 hi = ld_tr16(kw + (r0 + 16) * KS + 16 * dt + tcol);
+                    dqa[dt] = mfma16(as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y}), bs, dqa[dt]);
+                }
+            }
+        }
+    }
+    // dq = dQ^T (C[i = column][j = head]: lane j + 16 (i / 4), element i % 4)
+    // plus the gate terms sum_c dz_c W_g[h][c]
+    uint16_t *dq = (uint16_t *)a.dq + (row0 + h) * DK;
+    const uint16_t *wg = (const uint16_t *)a.wg + ((long)g * 16 + h) * 3 * DK;
+#pragma unroll
+    for (int dt = 0; dt < DK / 16; dt++) {
+        const int col = 16 * dt + 4 * lg;
+        float z[4] = {dqa[dt][0], dqa[dt][1], dqa[dt][2], dqa[dt][3]};
+#pragma unroll
+        for (int br = 0; br < 3; br++) {
+            const uint2 w = *(const uint2 *)(wg + br * DK + col);
+            z[0] = __builtin_fmaf(dzs[br], bf2f((uint16_t)(w.x & 0xffffu)), z[0]);
+            z[1] = __builtin_fmaf(dzs[br], bf2f((uint16_t)(w.x >> 16)), z[1]);
+            z[2] = __builtin_fmaf(dzs[br], bf2f((uint16_t)(w.y & 0xffffu)), z[2]);
+            z[3] = __builtin_fmaf(dzs[br], bf2f((uint16_t)(w.y >> 16)), z[3]);
+        }
+        *(uint2 *)(dq + col) = uint2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+    }
+}
+
 // dk_raw, dv_raw = sum over the row chunks that hold the key, in chunk order.
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void k_bwd_keys_sum(BwdArgs a)
@@ -369,6 +594,16 @@ hipError_t launch_bwd_keys_mfma(const BwdArgs &A, hipStream_t s)
     if (d.dk == 192) return launch_dims<192, 128>(A, s);
     if (d.dk == 128) return launch_dims<128, 128>(A, s);
     return launch_dims<64, 64>(A, s);
+}
+
+hipError_t launch_bwd_rows_mfma(const BwdArgs &A, hipStream_t s)
+{
+    const Dims &d = A.d;
+    const dim3 grid((d.T + kThreads / 64 - 1) / (kThreads / 64), d.Hkv, d.B);
+    if (d.dk == 192) hipLaunchKernelGGL((k_bwd_rows_mfma<192, 128>), grid, dim3(kThreads), 0, s, A);
+    else if (d.dk == 128) hipLaunchKernelGGL((k_bwd_rows_mfma<128, 128>), grid, dim3(kThreads), 0, s, A);
+    else hipLaunchKernelGGL((k_bwd_rows_mfma<64, 64>), grid, dim3(kThreads), 0, s, A);
+    return hipGetLastError();
 }
 
 hipError_t launch_bwd_cmp_keys_mfma(const BwdArgs &A, hipStream_t s)

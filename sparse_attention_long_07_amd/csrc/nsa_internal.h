@@ -126,6 +126,8 @@ void bwd_key_chunks(const Dims &d, int *rc, int *nkc, size_t *part_floats);
 hipError_t launch_bwd_keys_mfma(const BwdArgs &A, hipStream_t s);
 // compressed-key gradient partials (part) on the matrix cores, same shapes
 hipError_t launch_bwd_cmp_keys_mfma(const BwdArgs &A, hipStream_t s);
+// the row pass (rs and dq) on the matrix cores, same shapes
+hipError_t launch_bwd_rows_mfma(const BwdArgs &A, hipStream_t s);
 
 // Generic kernels: plain VALU code, any supported shape, fp32 or bf16 storage.
 // Compression launchers: every block of the T-token sequences when len_new is
