@@ -111,6 +111,38 @@ void orc_compress(int B, int H, int T, int dim, int l, int d, int n_out, int rou
         }
 }
 
+/* Compression by a small two-layer network ([deepdaiv], token-compression
+ * paragraph: a small neural network with an intra-block position encoding
+ * summarises each block; the pages give no layer count, width or activation,
+ * so this reading takes two layers, hidden width = dim, ReLU, no biases):
+ *   a   = W1 vec(x_i + PE), exactly as orc_compress with W = W1, rounded to
+ *         bf16 when round_bf16 (the hidden layer is stored like a summary)
+ *   h   = max(a, 0)
+ *   out = W2 h, rounded to bf16 when round_bf16
+ *   W1 [dim][l*dim], PE [l][dim], W2 [dim][dim] (out[c] = sum_j W2[c][j] h[j]);
+ *   entries past N_cmp are zero. */
+void orc_compress_mlp(int B, int H, int T, int dim, int l, int d, int n_out, int round_bf16, const double *x,
+                      const double *W1, const double *PE, const double *W2, double *out)
+{
+    orc_compress(B, H, T, dim, l, d, n_out, round_bf16, x, W1, PE, out);
+    int ncmp = orc_n_cmp(T, l, d);
+#pragma omp parallel for collapse(3) schedule(static)
+    for (int b = 0; b < B; b++)
+        for (int h = 0; h < H; h++)
+            for (int i = 0; i < n_out; i++) {
+                double *row = out + (((size_t)b * H + h) * (size_t)n_out + i) * dim;
+                if (i >= ncmp) continue;
+                double *hid = (double *)malloc(sizeof(double) * (size_t)dim);
+                for (int j = 0; j < dim; j++) hid[j] = row[j] > 0.0 ? row[j] : 0.0;
+                for (int c = 0; c < dim; c++) {
+                    double acc = 0.0;
+                    for (int j = 0; j < dim; j++) acc += W2[(size_t)c * dim + j] * hid[j];
+                    row[c] = round_bf16 ? orc_round_bf16(acc) : acc;
+                }
+                free(hid);
+            }
+}
+
 static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
 
 /* Softmax attention of one query vector over an explicit list of key rows.

@@ -53,6 +53,8 @@ def _load():
         lib.orc_round_bf16.argtypes = [ctypes.c_double]
         lib.orc_compress.restype = None
         lib.orc_compress.argtypes = [ctypes.c_int] * 8 + [_dp, _dp, _dp, _dp]
+        lib.orc_compress_mlp.restype = None
+        lib.orc_compress_mlp.argtypes = [ctypes.c_int] * 8 + [_dp] * 5
         lib.orc_forward_rows.restype = None
         lib.orc_forward_rows.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int, _ip, _ip, _dp, _dp, _dp,
                                          ctypes.c_int, _dp, _dp, _dp, _dp, _ip, _dp, _ip, _dp, ctypes.c_int,
@@ -125,6 +127,23 @@ def compress(x, W, PE, l: int = 32, d: int = 16, n_out: int | None = None, round
         n_out = n_cmp(T, l, d)
     out = np.zeros((B, H, n_out, dim))
     _load().orc_compress(B, H, T, dim, l, d, n_out, int(round_bf16), xp, wp, pp, out.ctypes.data_as(_dp))
+    return out
+
+
+def compress_mlp(x, W1, PE, W2, l: int = 32, d: int = 16, n_out: int | None = None, round_bf16: bool = False):
+    """Two-layer compression: x [B,H,T,dim], W1 [dim, l*dim], PE [l, dim],
+    W2 [dim, dim] -> [B,H,n_out,dim] = W2 relu(W1 vec(block + PE)), the hidden
+    layer and the output rounded to bf16 when round_bf16."""
+    x, xp = _d(x)
+    B, H, T, dim = x.shape
+    W1, w1p = _d(W1)
+    PE, pp = _d(PE)
+    W2, w2p = _d(W2)
+    assert W1.shape == (dim, l * dim) and PE.shape == (l, dim) and W2.shape == (dim, dim)
+    if n_out is None:
+        n_out = n_cmp(T, l, d)
+    out = np.zeros((B, H, n_out, dim))
+    _load().orc_compress_mlp(B, H, T, dim, l, d, n_out, int(round_bf16), xp, w1p, pp, w2p, out.ctypes.data_as(_dp))
     return out
 
 
