@@ -29,7 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from sparse_attention_long_07_amd import nsa  # noqa: E402
-from sparse_attention_long_07_amd.config import (WORKLOADS, decode_bytes, decode_flops,  # noqa: E402
+from sparse_attention_long_07_amd.config import (WORKLOADS, backward_flops, decode_bytes, decode_flops,  # noqa: E402
                                                  decode_slots, prefill_flops)
 from sparse_attention_long_07_amd.inputs import make_decode, make_prefill  # noqa: E402
 
@@ -54,6 +54,48 @@ def measured_traffic(kernel):
     path, sha, nbytes = ent
     with open(os.path.join(ROOT, path), "rb") as f:
         return nbytes if hashlib.sha256(f.read()).hexdigest() == sha else None
+
+
+def fwd_bwd(steps):
+    """Forward (compression, the three branches, selection) and backward with
+    the forward's selection at T=16384, timed apart from the headline step."""
+    w = WORKLOADS["bf16_fwdbwd_T16384"]
+    s = w.shape
+    dev = torch.device("cuda:0")
+    log("setup: fwd+bwd inputs", s)
+    x = make_prefill(s, 1005, dev, unit_scaled=w.unit_scaled, with_grad=True)
+    ws = nsa.workspace(s, nsa.OP_BACKWARD, dev)
+
+    def fwd():
+        ck, cv = nsa.compress_kv(s, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"])
+        o, idx = nsa.forward(s, x["q"], x["k"], x["v"], ck, cv, x["w_g"], x["b_g"], want_idx=True)
+        return ck, cv, idx
+
+    def bwd(ck, cv, idx):
+        return nsa.backward(s, x["q"], x["k"], x["v"], ck, cv, x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"],
+                            x["w_g"], x["b_g"], idx, x["do"], ws=ws)
+
+    bwd(*fwd())
+    torch.cuda.synchronize()
+    tf, tb = [], []
+    log("timed fwd+bwd", steps)
+    for _ in range(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        ck, cv, idx = fwd()
+        e[1].record()
+        bwd(ck, cv, idx)
+        e[2].record()
+        torch.cuda.synchronize()
+        tf.append(e[0].elapsed_time(e[1]))
+        tb.append(e[1].elapsed_time(e[2]))
+    fms, bms = float(np.mean(tf)), float(np.mean(tb))
+    ff, bf = prefill_flops(s)["total"], backward_flops(s)["total"]
+    return {"workload": "NSA fwd+bwd bf16 T=16384 (B=1, 4 KV x 16 q heads, d_k=192, d_v=128), dO ~ N(0,1)",
+            "fwd_ms": round(fms, 3), "bwd_ms": round(bms, 3), "bwd_over_fwd": round(bms / fms, 2),
+            "fwd_tflops": round(ff / (fms * 1e-3) / 1e12, 2), "bwd_algorithmic_tflop": round(bf / 1e12, 4),
+            "bwd_tflops": round(bf / (bms * 1e-3) / 1e12, 2),
+            "bwd_mfma_frac": round(bf / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def log(*a):
@@ -97,6 +139,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=10240)
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the fwd+bwd T=16384 measurement reported beside the headline line")
     ap.add_argument("--traffic", type=float, default=None,
                     help="HBM bytes per launch of the roofline kernel from FETCH_SIZE/WRITE_SIZE counters")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -259,6 +303,7 @@ def main():
         "roofline": roof,
         "kernels": kernels,
     }
+    res["fwd_bwd_T16384"] = None if args.no_backward else fwd_bwd(args.steps)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(sp, x, fl["total"], rows_sample=args.cpu_rows)

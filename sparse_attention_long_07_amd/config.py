@@ -125,6 +125,22 @@ def prefill_flops(s: NSAShape) -> dict:
     return out
 
 
+def backward_flops(s: NSAShape) -> dict:
+    """Algorithmic flops of one backward pass with the selection held fixed.
+
+    Per attended (query head, key) pair of a branch the gradient takes five
+    products: the scores again (d_k), dP = dO V^T (d_v), dV (d_v), dK (d_k)
+    and dq (d_k), i.e. 2 (3 d_k + 2 d_v) flops against 2 (d_k + d_v) forward.
+    The compression map's backward is two products per forward one (dW and
+    the token gradient), the gates' likewise (dW_g and the dq term)."""
+    f = prefill_flops(s)
+    ratio = (3 * s.dk + 2 * s.dv) / (s.dk + s.dv)
+    attn = (f["compressed"] + f["selected"] + f["window"]) * ratio
+    out = {"attention": int(attn), "compress": 2 * f["compress"], "gates": 2 * f["gates"]}
+    out["total"] = sum(out.values())
+    return out
+
+
 def dense_causal_flops(s: NSAShape) -> int:
     """Flops of full causal attention at the same shape (for the pages' speedup context)."""
     return s.T * (s.T + 1) // 2 * 2 * (s.dk + s.dv) * s.Hq * s.B

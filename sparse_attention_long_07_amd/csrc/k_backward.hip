@@ -671,7 +671,31 @@ __global__ __launch_bounds__(kThreads) void k_bwd_sum_parts(BwdArgs a)
     a.kcv[e] = s;
 }
 
-// colsum[c] = sum over sequences, KV heads and complete blocks of kcv[..][c].
+// colsum[c] = sum over sequences, KV heads and complete blocks of kcv[..][c],
+// in two fixed-order levels: workgroup (column group of 64, row chunk y of
+// kColChunks) sums its chunk of the (b, head, block) rows, each wave a
+// quarter of it in row order, the quarters in order; then the chunk
+// partials are added in chunk order.
+constexpr int kColChunks = 32;
+__global__ __launch_bounds__(kThreads) void k_bwd_colsum_part(BwdArgs a)
+{
+    const Dims &d = a.d;
+    const int W = d.dk + d.dv;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int c = blockIdx.x * kWave + lane;
+    const long R = (long)d.B * d.Hkv * d.ncmp;   // rows r = bh * ncmp + i
+    const long per = (R + kColChunks - 1) / kColChunks;
+    const long r0 = blockIdx.y * per, r1 = r0 + per < R ? r0 + per : R;
+    const long q = (r1 - r0 + 3) / 4;
+    const long lo = r0 + wave * q, hi = lo + q < r1 ? lo + q : r1;
+    float s = 0.f;
+    if (c < W)
+        for (long r = lo; r < hi; r++) s += a.kcv[((r / d.ncmp) * d.npad + r % d.ncmp) * W + c];
+    __shared__ float ws[kThreads / kWave][kWave];
+    ws[wave][lane] = s;
+    __syncthreads();
+    if (wave == 0 && c < W) a.cspart[(long)blockIdx.y * W + c] = ((ws[0][lane] + ws[1][lane]) + ws[2][lane]) + ws[3][lane];
+}
 __global__ __launch_bounds__(kThreads) void k_bwd_colsum(BwdArgs a)
 {
     const Dims &d = a.d;
@@ -679,8 +703,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_colsum(BwdArgs a)
     const int c = blockIdx.x * kThreads + threadIdx.x;
     if (c >= W) return;
     float s = 0.f;
-    for (int bh = 0; bh < d.B * d.Hkv; bh++)
-        for (int i = 0; i < d.ncmp; i++) s += a.kcv[((long)bh * d.npad + i) * W + c];
+    for (int y = 0; y < kColChunks; y++) s += a.cspart[(long)y * W + c];
     a.colsum[c] = s;
 }
 
@@ -908,6 +931,8 @@ hipError_t launch_all(const BwdArgs &A, hipStream_t s)
         const long n = (long)BH * d.npad * (d.dk + d.dv);
         hipLaunchKernelGGL(k_bwd_sum_parts, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
                            A);
+        hipLaunchKernelGGL(k_bwd_colsum_part, dim3((d.dk + d.dv + kWave - 1) / kWave, kColChunks), dim3(kThreads), 0, s,
+                           A);
         hipLaunchKernelGGL(k_bwd_colsum, dim3((d.dk + d.dv + kThreads - 1) / kThreads), dim3(kThreads), 0, s, A);
         hipLaunchKernelGGL(k_bwd_dpe<T>, dim3((32 * (d.dk > d.dv ? d.dk : d.dv) + kThreads - 1) / kThreads, 2),
                            dim3(kThreads), 0, s, A);
@@ -978,6 +1003,7 @@ size_t backward_layout(const Dims &d, void *ws, BwdArgs *A)
     const size_t o_part = carve((size_t)nchunk * BH * d.npad * (d.dk + d.dv));
     const size_t o_kcv = carve((size_t)BH * d.npad * (d.dk + d.dv));
     const size_t o_cs = carve((size_t)(d.dk + d.dv));
+    const size_t o_csp = carve((size_t)kColChunks * (d.dk + d.dv));
     const size_t o_gp = carve((size_t)d.Hq * ngc * 3 * (d.dk + 1));
     const size_t o_bm = carve((size_t)BH * d.nb * ((d.T + 31) / 32));   // 32-bit words
     int krc = 0, nkc = 0;
@@ -992,6 +1018,7 @@ size_t backward_layout(const Dims &d, void *ws, BwdArgs *A)
         A->part = (float *)(w + o_part);
         A->kcv = (float *)(w + o_kcv);
         A->colsum = (float *)(w + o_cs);
+        A->cspart = (float *)(w + o_csp);
         A->gpart = (float *)(w + o_gp);
         A->selbm = (uint32_t *)(w + o_bm);
         A->kpart = (float *)(w + o_kp);

@@ -106,6 +106,7 @@ struct BwdArgs {
     float *part;      // [nchunk][B*Hkv][npad][dk+dv] compressed K/V gradient per row chunk
     float *kcv;       // [B*Hkv][npad][dk+dv] compressed K/V gradient
     float *colsum;    // [dk+dv] sum of kcv over sequences, heads and blocks
+    float *cspart;    // [32][dk+dv] colsum partials per row chunk
     float *gpart;     // [Hq][ngc][3][dk+1] gate gradient per row chunk
     uint32_t *selbm;  // [B*Hkv][NB][ceil(T/32)] bit t of row j: row t selected block j
     float *kpart;     // matrix-core key pass: per row chunk c, [B*Hkv][min(T, (c+1) krc)][dk+dv] partial raw dK, dV
@@ -138,6 +139,9 @@ hipError_t launch_compress_generic(const Dims &d, const void *x, const void *W, 
                                    int dim, hipStream_t s, const int32_t *len_old = nullptr,
                                    const int32_t *len_new = nullptr, int tiles = 0);
 hipError_t launch_cmp_attn_generic(const RowArgs &a, bool with_v, hipStream_t s);
+// second layer of the two-layer compression, in place: rows <- W2 relu(rows)
+hipError_t launch_compress_mlp2(const Dims &d, const void *W2k, const void *W2v, void *cmp_k, void *cmp_v,
+                                hipStream_t s);
 hipError_t launch_select_generic(const RowArgs &a, hipStream_t s);
 hipError_t launch_sparse_generic(const RowArgs &a, hipStream_t s);
 
