@@ -104,6 +104,25 @@ nsa_status nsa_compress_kv(const nsa_config *cfg, const void *k, const void *v, 
                            const void *pe_k, const void *w_cv, const void *pe_v, void *cmp_k, void *cmp_v,
                            void *stream);
 
+/* Token compression by a small two-layer network (deepdaiv newsletter, token
+ * compression paragraph: a small neural network with a position encoding
+ * summarises each block; the page gives no layer count, width or
+ * activation, and this variant takes two layers of width d, ReLU, no
+ * biases).  For every (b, h) and block i < N_cmp:
+ *   a[j]   = sum_{tau<32, e<dk} w1_k[j][tau*dk+e] * (k[b][h][16i+tau][e] + pe_k[tau][e])
+ *   cmp_k[b][h][i][c] = sum_{j<dk} w2_k[c][j] * max(a[j], 0)
+ * and likewise cmp_v from v, w1_v, pe_v, w2_v (w2_v [dv][dv]).  a is rounded
+ * to the storage type (a bf16 hidden layer for bf16 storage), the output to
+ * nearest even; fp32 accumulation.  Rows N_cmp..N_pad-1 are written as 0.
+ * w1_k, pe_k, w1_v, pe_v have the shapes of w_ck, pe_k, w_cv, pe_v above;
+ * w2_k [dk][dk], w2_v [dv][dv] row-major, storage dtype, 16-byte aligned.
+ * The compressed outputs feed nsa_compressed_attention, nsa_forward and
+ * nsa_decode_step unchanged; nsa_compress_append and nsa_backward take the
+ * linear map only. */
+nsa_status nsa_compress_kv_mlp(const nsa_config *cfg, const void *k, const void *v, const void *w1_k,
+                               const void *pe_k, const void *w2_k, const void *w1_v, const void *pe_v,
+                               const void *w2_v, void *cmp_k, void *cmp_v, void *stream);
+
 /* Incremental compression of caches that grow token by token (the decode
  * step of valuable12.com section III.3 reads compressed entries for every
  * complete block; with the token compression of the deepdaiv newsletter a

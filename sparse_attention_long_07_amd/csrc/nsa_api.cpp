@@ -162,6 +162,30 @@ nsa_status nsa_compress_kv(const nsa_config *cfg, const void *k, const void *v, 
     return NSA_OK;
 }
 
+nsa_status nsa_compress_kv_mlp(const nsa_config *cfg, const void *k, const void *v, const void *w1_k,
+                               const void *pe_k, const void *w2_k, const void *w1_v, const void *pe_v,
+                               const void *w2_v, void *cmp_k, void *cmp_v, void *stream)
+{
+    Dims d;
+    nsa_status st = check_config(cfg, &d);
+    if (st != NSA_OK) return st;
+    if (!k || !v || !w1_k || !pe_k || !w2_k || !w1_v || !pe_v || !w2_v || !cmp_k || !cmp_v) return NSA_ERR_NULL;
+    const void *ptrs[] = {k, v, w1_k, pe_k, w2_k, w1_v, pe_v, w2_v, cmp_k, cmp_v};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return NSA_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    // first layer: the linear compression with W1, pre-activations in cmp_k / cmp_v
+    if (compress_bf16_supported(d)) {
+        NSA_TRY(launch_compress_bf16(d, k, v, w1_k, pe_k, w1_v, pe_v, cmp_k, cmp_v, s));
+    } else {
+        NSA_TRY(launch_compress_generic(d, k, w1_k, pe_k, cmp_k, d.dk, s));
+        NSA_TRY(launch_compress_generic(d, v, w1_v, pe_v, cmp_v, d.dv, s));
+    }
+    // second layer in place
+    NSA_TRY(launch_compress_mlp2(d, w2_k, w2_v, cmp_k, cmp_v, s));
+    return NSA_OK;
+}
+
 nsa_status nsa_compress_append(const nsa_config *cfg, const int32_t *len_old, const int32_t *len_new,
                                int32_t max_append, const void *k_cache, const void *v_cache, const void *w_ck,
                                const void *pe_k, const void *w_cv, const void *pe_v, void *cmp_k, void *cmp_v,

@@ -52,6 +52,20 @@ def make_weights(s: NSAShape, gen, device, dtype):
     }
 
 
+def make_mlp_weights(s: NSAShape, seed: int, device="cpu", nonneg: bool = False):
+    """Second-layer weights of the two-layer compression map, drawn in this
+    order: W2_k ~ N(0,1)/sqrt(d_k) [d_k, d_k], W2_v ~ N(0,1)/sqrt(d_v) [d_v, d_v]
+    (absolute values when nonneg).  The first layer and PE use the linear
+    map's tensors (W_ck, PE_k, W_cv, PE_v), whose shapes it shares."""
+    g = _gen(seed, device)
+    dt = torch_dtype(s)
+    w2k = _randn((s.dk, s.dk), 1 / math.sqrt(s.dk), g, device, dt)
+    w2v = _randn((s.dv, s.dv), 1 / math.sqrt(s.dv), g, device, dt)
+    if nonneg:
+        w2k, w2v = w2k.abs(), w2v.abs()
+    return {"w2_k": w2k, "w2_v": w2v}
+
+
 def make_prefill(s: NSAShape, seed: int, device="cpu", unit_scaled: bool = True, with_grad: bool = False):
     """q [B,T,Hq,dk], k [B,Hkv,T,dk], v [B,Hkv,T,dv] plus the weights."""
     dt = torch_dtype(s)

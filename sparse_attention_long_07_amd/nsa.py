@@ -21,7 +21,7 @@ OP_FORWARD, OP_SELECT, OP_DECODE, OP_SPARSE, OP_BACKWARD = 0, 1, 2, 3, 4
 STATUS = {0: "NSA_OK", -1: "NSA_ERR_NULL", -2: "NSA_ERR_SHAPE", -3: "NSA_ERR_DTYPE", -4: "NSA_ERR_PARAM",
           -5: "NSA_ERR_WORKSPACE", -6: "NSA_ERR_HIP", -7: "NSA_ERR_ALIGN"}
 
-EXPORTS = ("nsa_workspace_bytes", "nsa_compress_kv", "nsa_compress_append", "nsa_compressed_attention",
+EXPORTS = ("nsa_workspace_bytes", "nsa_compress_kv", "nsa_compress_kv_mlp", "nsa_compress_append", "nsa_compressed_attention",
            "nsa_select_topn",
            "nsa_sparse_attention", "nsa_pack_kv_blocks", "nsa_window_attention", "nsa_selected_attention", "nsa_select_blocks",
            "nsa_forward", "nsa_decode_step", "nsa_backward", "nsa_status_string")
@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
         L.nsa_status_string.argtypes = [ctypes.c_int]
         L.nsa_compress_kv.restype = ctypes.c_int
         L.nsa_compress_kv.argtypes = [ctypes.POINTER(Config)] + [_vp] * 9
+        L.nsa_compress_kv_mlp.restype = ctypes.c_int
+        L.nsa_compress_kv_mlp.argtypes = [ctypes.POINTER(Config)] + [_vp] * 11
         L.nsa_compress_append.restype = ctypes.c_int
         L.nsa_compress_append.argtypes = [ctypes.POINTER(Config), _vp, _vp, ctypes.c_int32] + [_vp] * 9
         L.nsa_compressed_attention.restype = ctypes.c_int
@@ -141,6 +143,30 @@ def compress_kv(s: NSAShape, k, v, w_ck, pe_k, w_cv, pe_v, cmp_k=None, cmp_v=Non
     c = config(s)
     _check("nsa_compress_kv", lib().nsa_compress_kv(ctypes.byref(c), _p(k), _p(v), _p(w_ck), _p(pe_k), _p(w_cv),
                                                     _p(pe_v), _p(cmp_k), _p(cmp_v), _stream()))
+    return cmp_k, cmp_v
+
+
+def compress_kv_mlp(s: NSAShape, k, v, w1_k, pe_k, w2_k, w1_v, pe_v, w2_v, cmp_k=None, cmp_v=None):
+    """Two-layer compression: cmp = W2 relu(W1 vec(block + PE)) for K and V."""
+    dt = _dt(s)
+    _req(k, "k", (s.B, s.Hkv, s.T, s.dk), dt)
+    _req(v, "v", (s.B, s.Hkv, s.T, s.dv), dt)
+    _req(w1_k, "w1_k", (s.dk, s.l * s.dk), dt)
+    _req(pe_k, "pe_k", (s.l, s.dk), dt)
+    _req(w2_k, "w2_k", (s.dk, s.dk), dt)
+    _req(w1_v, "w1_v", (s.dv, s.l * s.dv), dt)
+    _req(pe_v, "pe_v", (s.l, s.dv), dt)
+    _req(w2_v, "w2_v", (s.dv, s.dv), dt)
+    if cmp_k is None:
+        cmp_k = torch.empty((s.B, s.Hkv, s.n_pad, s.dk), dtype=dt, device=k.device)
+    if cmp_v is None:
+        cmp_v = torch.empty((s.B, s.Hkv, s.n_pad, s.dv), dtype=dt, device=k.device)
+    _req(cmp_k, "cmp_k", (s.B, s.Hkv, s.n_pad, s.dk), dt)
+    _req(cmp_v, "cmp_v", (s.B, s.Hkv, s.n_pad, s.dv), dt)
+    c = config(s)
+    _check("nsa_compress_kv_mlp",
+           lib().nsa_compress_kv_mlp(ctypes.byref(c), _p(k), _p(v), _p(w1_k), _p(pe_k), _p(w2_k), _p(w1_v),
+                                     _p(pe_v), _p(w2_v), _p(cmp_k), _p(cmp_v), _stream()))
     return cmp_k, cmp_v
 
 

@@ -77,6 +77,7 @@ def test_bad_config_rejected_everywhere(kw, code):
     c = ctypes.byref(cfg(**kw))
     f = [FAKE] * 16
     assert L.nsa_compress_kv(c, *f[:8], None) == code
+    assert L.nsa_compress_kv_mlp(c, *f[:10], None) == code
     assert L.nsa_compress_append(c, f[0], f[1], 1, *f[:8], None) == code
     assert L.nsa_select_blocks(c, f[0], f[1], None, f[2], f[3], 1 << 40, None) == code
     assert L.nsa_forward(c, *f[:7], None, f[0], None, None, f[1], 1 << 40, None) == code
@@ -103,6 +104,18 @@ def test_compress_null_and_misaligned(pos):
     assert L.nsa_compress_kv(c, *args, None) == NULL
     args[pos] = MIS
     assert L.nsa_compress_kv(c, *args, None) == ALIGN
+
+
+@pytest.mark.parametrize("pos", range(10))
+def test_compress_mlp_null_and_misaligned(pos):
+    """k v w1_k pe_k w2_k w1_v pe_v w2_v cmp_k cmp_v: all required, 16-byte aligned."""
+    L = nsa.lib()
+    c = ctypes.byref(cfg())
+    args = [FAKE] * 10
+    args[pos] = None
+    assert L.nsa_compress_kv_mlp(c, *args, None) == NULL
+    args[pos] = MIS
+    assert L.nsa_compress_kv_mlp(c, *args, None) == ALIGN
 
 
 @pytest.mark.parametrize("pos", range(9))
