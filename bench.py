@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 from sparse_attention_long_07_amd import nsa  # noqa: E402
 from sparse_attention_long_07_amd.config import (WORKLOADS, backward_flops, decode_bytes, decode_flops,  # noqa: E402
                                                  decode_slots, prefill_flops)
-from sparse_attention_long_07_amd.inputs import make_decode, make_prefill  # noqa: E402
+from sparse_attention_long_07_amd.inputs import make_decode, make_mlp_weights, make_prefill  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_FP32_VALU_TFLOPS = 157.3
@@ -54,6 +54,42 @@ def measured_traffic(kernel):
     path, sha, nbytes = ent
     with open(os.path.join(ROOT, path), "rb") as f:
         return nbytes if hashlib.sha256(f.read()).hexdigest() == sha else None
+
+
+def mlp_compress(s, x, steps):
+    """The two-layer compression map at the prefill shape (first layer: the
+    linear compression kernel with W1; second layer in place), beside the
+    linear map, timed apart from the headline step."""
+    dev = x["k"].device
+    w = make_mlp_weights(s, 1004, dev)
+    ck = torch.empty((s.B, s.Hkv, s.n_pad, s.dk), dtype=torch.bfloat16, device=dev)
+    cv = torch.empty((s.B, s.Hkv, s.n_pad, s.dv), dtype=torch.bfloat16, device=dev)
+
+    def lin():
+        nsa.compress_kv(s, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"], ck, cv)
+
+    def mlp():
+        nsa.compress_kv_mlp(s, x["k"], x["v"], x["w_ck"], x["pe_k"], w["w2_k"], x["w_cv"], x["pe_v"], w["w2_v"],
+                            ck, cv)
+
+    def timed(f):
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    lin_ms, mlp_ms = timed(lin), timed(mlp)
+    fl = prefill_flops(s)["compress"]
+    fl2 = 2 * s.n_cmp * (s.dk * s.dk + s.dv * s.dv) * s.Hkv * s.B
+    return {"workload": "two-layer compression map, bf16 T=65536, 4 KV heads, d_k=192, d_v=128",
+            "linear_ms": round(lin_ms, 4), "mlp_ms": round(mlp_ms, 4), "second_layer_ms": round(mlp_ms - lin_ms, 4),
+            "mlp_algorithmic_gflop": round((fl + fl2) / 1e9, 3),
+            "mlp_tflops": round((fl + fl2) / (mlp_ms * 1e-3) / 1e12, 2)}
 
 
 def fwd_bwd(steps):
@@ -303,6 +339,7 @@ def main():
         "roofline": roof,
         "kernels": kernels,
     }
+    res["mlp_compress_T65536"] = mlp_compress(sp, x, args.steps)
     res["fwd_bwd_T16384"] = None if args.no_backward else fwd_bwd(args.steps)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
