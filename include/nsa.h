@@ -74,7 +74,8 @@ typedef enum {
     NSA_OP_SELECT = 1,  /* nsa_select_blocks */
     NSA_OP_DECODE = 2,  /* nsa_decode_step */
     NSA_OP_SPARSE = 3,  /* nsa_sparse_attention */
-    NSA_OP_BACKWARD = 4 /* nsa_backward */
+    NSA_OP_BACKWARD = 4, /* nsa_backward */
+    NSA_OP_DSA_DECODE = 5 /* nsa_dsa_decode: B*T fp32 indexer scores */
 } nsa_op;
 
 /* Problem description.  Supported ranges (checked on every call):
@@ -255,6 +256,37 @@ nsa_status nsa_backward(const nsa_config *cfg, const void *q, const void *k, con
                         const void *w_g, const void *b_g, const int32_t *idx, const void *d_o, void *d_q,
                         void *d_k, void *d_v, float *d_wck, float *d_pek, float *d_wcv, float *d_pev,
                         float *d_wg, float *d_bg, void *ws, size_t ws_bytes, void *stream);
+
+/* DSA-style decode step (DSA explainer, allinfo.ai.kr, section "쉽게
+ * 이해하기": a lightning indexer with several small heads and one key per
+ * token shared by the heads scores every cached token by a weighted sum of
+ * ReLU dot products; a selector keeps the top-k tokens (2,048 on the page)
+ * for each query; attention runs over the selected tokens only, the softmax
+ * denominator summed over that set).  One query per sequence, the token at
+ * t = clamp(seq_lens[b], 1, T) - 1; the cached tokens s <= t are candidates.
+ *   I[b][s] = sum_{j<idx_heads} w_idx[b][j] * max(q_idx[b][j] . k_idx[b][s], 0)
+ *   sel[b]  = the topk positions with the highest I (equal scores: the lower
+ *             position first; all of them when t + 1 <= topk), ascending,
+ *             -1 padded; one selection per sequence, shared by every head
+ *   o[b][h] = sum_{s in sel[b]} softmax_s(scale q[b][h] . k[b][g][s]) v[b][g][s],
+ *             g = h / group
+ * cfg: B, T (cache capacity), H_kv, group, d_k, d_v, scale and dtype are
+ * used (the NSA fields must still be valid); supported: bf16, group = 16,
+ * (d_k, d_v) = (192, 128), (128, 128) or (64, 64), else NSA_ERR_SHAPE.
+ * idx_heads 1..16, idx_dim 8..256 (a multiple of 8), topk 1..8192, else
+ * NSA_ERR_PARAM.  Layouts (bf16): q_idx [B][idx_heads][idx_dim], w_idx
+ * [B][idx_heads], k_idx [B][T][idx_dim], q [B][Hq][d_k], k [B][H_kv][T][d_k],
+ * v [B][H_kv][T][d_v], o [B][Hq][d_v]; seq_lens device int32 [B]; sel
+ * device int32 [B][topk].  fp32 arithmetic.  With sel_in (a selection as
+ * above: entries -1 or positions below seq_lens[b]; entries outside 0..T-1
+ * count as -1) the indexer and selector are skipped and q_idx, w_idx, k_idx,
+ * sel_out and ws may be NULL; otherwise sel_out receives the selection and
+ * ws holds nsa_workspace_bytes(cfg, NSA_OP_DSA_DECODE) bytes.  q_idx, k_idx,
+ * q, k, v, o 16-byte aligned. */
+nsa_status nsa_dsa_decode(const nsa_config *cfg, int32_t idx_heads, int32_t idx_dim, int32_t topk,
+                          const int32_t *seq_lens, const void *q_idx, const void *w_idx, const void *k_idx,
+                          const void *q, const void *k, const void *v, const int32_t *sel_in, int32_t *sel_out,
+                          void *o, void *ws, size_t ws_bytes, void *stream);
 
 /* Static description of a status code. */
 const char *nsa_status_string(int status);

@@ -66,6 +66,17 @@ def make_mlp_weights(s: NSAShape, seed: int, device="cpu", nonneg: bool = False)
     return {"w2_k": w2k, "w2_v": w2v}
 
 
+def make_dsa_indexer(s: NSAShape, seed: int, device="cpu", idx_heads: int = 4, idx_dim: int = 64):
+    """Indexer inputs of a DSA-style decode step, drawn in this order:
+    q_idx ~ N(0,1)/sqrt(idx_dim) [B, idx_heads, idx_dim], w_idx ~ N(0,1)/sqrt(idx_heads)
+    [B, idx_heads], k_idx ~ N(0,1) [B, T, idx_dim] (s.T = cache capacity)."""
+    g = _gen(seed, device)
+    dt = torch_dtype(s)
+    return {"q_idx": _randn((s.B, idx_heads, idx_dim), 1 / math.sqrt(idx_dim), g, device, dt),
+            "w_idx": _randn((s.B, idx_heads), 1 / math.sqrt(idx_heads), g, device, dt),
+            "k_idx": _randn((s.B, s.T, idx_dim), 1.0, g, device, dt)}
+
+
 def make_prefill(s: NSAShape, seed: int, device="cpu", unit_scaled: bool = True, with_grad: bool = False):
     """q [B,T,Hq,dk], k [B,Hkv,T,dk], v [B,Hkv,T,dv] plus the weights."""
     dt = torch_dtype(s)

@@ -83,6 +83,7 @@ def test_bad_config_rejected_everywhere(kw, code):
     assert L.nsa_forward(c, *f[:7], None, f[0], None, None, f[1], 1 << 40, None) == code
     assert L.nsa_decode_step(c, *f[:8], None, f[0], None, f[1], 1 << 40, None) == code
     assert L.nsa_backward(c, *([FAKE] * 22), FAKE, 1 << 40, None) == code
+    assert L.nsa_dsa_decode(c, 4, 64, 16, *([FAKE] * 10), FAKE, 1 << 40, None) == code
     assert L.nsa_sparse_attention(c, *f[:8], f[0], 1 << 40, None) == code
     assert L.nsa_window_attention(c, *f[:7], None) == code
     assert L.nsa_pack_kv_blocks(c, f[0], f[1], f[2], 1 << 40, None) == code
@@ -168,6 +169,41 @@ def test_select_and_decode_checks():
     f = [FAKE] * 7
     assert L.nsa_decode_step(ctypes.byref(c), None, *f, None, FAKE, None, FAKE, need, None) == NULL
     assert L.nsa_decode_step(ctypes.byref(c), FAKE, *f, None, FAKE, None, FAKE, need - 256, None) == WS
+
+
+def test_dsa_decode_checks():
+    """Shapes the matrix-core attention takes, indexer sizes, required
+    pointers (the indexer's only without sel_in), alignment, workspace."""
+    L = nsa.lib()
+    ok = cfg(group=16, d_k=192, d_v=128, dtype=1)
+    c = ctypes.byref(ok)
+    f = [FAKE] * 7     # q_idx w_idx k_idx q k v | sel_in
+    need = L.nsa_workspace_bytes(c, 5)
+    assert need >= 4 * ok.B * ok.T
+    # unsupported attention shapes
+    for bad in (cfg(group=16, d_k=192, d_v=128, dtype=0), cfg(group=8, d_k=192, d_v=128, dtype=1),
+                cfg(group=16, d_k=96, d_v=96, dtype=1)):
+        assert L.nsa_dsa_decode(ctypes.byref(bad), 4, 64, 2048, FAKE, *f[:6], None, FAKE, FAKE, FAKE, need,
+                                None) == SHAPE
+    # indexer sizes and k
+    for hi, di, k in ((0, 64, 16), (17, 64, 16), (4, 4, 16), (4, 260, 16), (4, 60, 16), (4, 64, 0), (4, 64, 8193)):
+        assert L.nsa_dsa_decode(c, hi, di, k, FAKE, *f[:6], None, FAKE, FAKE, FAKE, need, None) == PARAM
+    # required pointers
+    assert L.nsa_dsa_decode(c, 4, 64, 16, None, *f[:6], None, FAKE, FAKE, FAKE, need, None) == NULL
+    for pos in range(6):
+        a = list(f[:6])
+        a[pos] = None
+        assert L.nsa_dsa_decode(c, 4, 64, 16, FAKE, *a, None, FAKE, FAKE, FAKE, need, None) == NULL
+    assert L.nsa_dsa_decode(c, 4, 64, 16, FAKE, *f[:6], None, None, FAKE, FAKE, need, None) == NULL   # sel_out
+    assert L.nsa_dsa_decode(c, 4, 64, 16, FAKE, *f[:6], None, FAKE, None, FAKE, need, None) == NULL   # o
+    # with sel_in the indexer's inputs, sel_out and ws may be NULL; misalignment still caught
+    assert L.nsa_dsa_decode(c, 4, 64, 16, FAKE, None, None, None, MIS, FAKE, FAKE, FAKE, None, FAKE, None, 0,
+                            None) == ALIGN
+    assert L.nsa_dsa_decode(c, 4, 64, 16, FAKE, MIS, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, need,
+                            None) == ALIGN
+    # workspace
+    assert L.nsa_dsa_decode(c, 4, 64, 16, FAKE, *f[:6], None, FAKE, FAKE, None, need, None) == WS
+    assert L.nsa_dsa_decode(c, 4, 64, 16, FAKE, *f[:6], None, FAKE, FAKE, FAKE, need - 256, None) == WS
 
 
 def test_binding_rejects_host_tensors():
