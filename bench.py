@@ -31,7 +31,8 @@ sys.path.insert(0, ROOT)
 from sparse_attention_long_07_amd import nsa  # noqa: E402
 from sparse_attention_long_07_amd.config import (WORKLOADS, backward_flops, decode_bytes, decode_flops,  # noqa: E402
                                                  decode_slots, prefill_flops)
-from sparse_attention_long_07_amd.inputs import make_decode, make_mlp_weights, make_prefill  # noqa: E402
+from sparse_attention_long_07_amd.inputs import (make_decode, make_dsa_indexer, make_mlp_weights,  # noqa: E402
+                                                 make_prefill)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_FP32_VALU_TFLOPS = 157.3
@@ -54,6 +55,36 @@ def measured_traffic(kernel):
     path, sha, nbytes = ent
     with open(os.path.join(ROOT, path), "rb") as f:
         return nbytes if hashlib.sha256(f.read()).hexdigest() == sha else None
+
+
+def dsa_decode(s, y, steps, topk=2048, hi=4, di=64):
+    """The DSA-style decode step (indexer, top-k tokens, attention over them)
+    on the decode workload's caches, timed apart from the headline step."""
+    dev = y["k"].device
+    ix = make_dsa_indexer(s, 1006, dev, hi, di)
+    sel = torch.empty((s.B, topk), dtype=torch.int32, device=dev)
+    o = torch.empty((s.B, s.Hq, s.dv), dtype=torch.bfloat16, device=dev)
+    ws = nsa.workspace(s, nsa.OP_DSA_DECODE, dev)
+
+    def step():
+        nsa.dsa_decode(s, hi, di, topk, y["seq_lens"], ix["q_idx"], ix["w_idx"], ix["k_idx"], y["q"], y["k"], y["v"],
+                       sel=sel, o=o, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    L = s.T
+    nbytes = s.B * (L * di * 2 + 2 * L * 4 + min(topk, L) * s.Hkv * (s.dk + s.dv) * 2)
+    return {"workload": "DSA-style decode step, bf16 B=32 @65536-token caches, 4 KV x 16 q heads, d_k=192, d_v=128; "
+                        "indexer 4 heads x 64, top-2048",
+            "us_per_step": round(us, 2), "algorithmic_MB": round(nbytes / 1e6, 2),
+            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
 
 
 def mlp_compress(s, x, steps):
@@ -340,6 +371,7 @@ def main():
         "kernels": kernels,
     }
     res["mlp_compress_T65536"] = mlp_compress(sp, x, args.steps)
+    res["dsa_decode_B32_T65536"] = dsa_decode(sd, dec[0], args.steps)
     res["fwd_bwd_T16384"] = None if args.no_backward else fwd_bwd(args.steps)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

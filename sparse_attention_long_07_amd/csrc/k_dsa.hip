@@ -6,13 +6,15 @@
 // summed over that set.  One selection per sequence serves every query head
 // and KV group.  bf16 storage, fp32 arithmetic.
 //
-// k_dsa_index  one thread per cached token: I[s] = sum_j w_j relu(q_j . k_s)
-//              (HBM: the indexer keys are read once).
+// k_dsa_index  I[s] = sum_j w_j relu(q_j . k_s): the lanes of a group each
+//              read one 16-byte piece of a key (HBM: the indexer keys are read
+//              once, whole rows per load).
 // k_dsa_topk   one 1024-thread workgroup per sequence: radix select of the
-//              k-th largest score over order-preserving 32-bit keys (four
-//              8-bit digits, histograms with integer LDS atomics), then an
-//              ordered compaction: every key above the threshold and the
-//              lowest-position keys equal to it, ascending, -1 padded.
+//              k-th largest score over order-preserving 32-bit keys (digits
+//              of 12, 12 and 8 bits, histograms with integer LDS atomics),
+//              then an ordered compaction by wave ballots: every key above
+//              the threshold and the lowest-position keys equal to it,
+//              ascending (exactly k of them, since more than k candidates).
 // k_dsa_attn   one 8-wave workgroup per (sequence, KV head); wave w takes
 //              selected slots [w k/8, (w+1) k/8) in sub-chunks of 32 tokens:
 //              S^T = K Q^T on gathered K rows (16x16x32 MFMA, the 16 heads
@@ -36,46 +38,60 @@ __device__ __forceinline__ int seq_len_of(const int32_t *seq_lens, int b, int T)
     return L < 1 ? 1 : (L > T ? T : L);
 }
 
-// q_idx [B][HI][DI], w_idx [B][HI], k_idx [B][T][DI] (bf16); scores [B][T] fp32
+// q_idx [B][HI][DI], w_idx [B][HI], k_idx [B][T][DI] (bf16); scores [B][T] fp32.
+// PW = lanes per key, a power of two >= DI / 8: lane p of a key's group reads
+// the key's 16-byte piece p (p < DI / 8), so a wave reads 64 / PW whole rows
+// per load; each wave takes 64 keys in PW rounds, all loads issued first;
+// the per-head partial dots are summed over the group by butterfly shuffles.
+template <int PW>
 __global__ __launch_bounds__(kThreads) void k_dsa_index(const uint16_t *__restrict__ q_idx,
                                                         const uint16_t *__restrict__ w_idx,
                                                         const uint16_t *__restrict__ k_idx,
                                                         const int32_t *__restrict__ seq_lens, float *__restrict__ scores,
                                                         int T, int HI, int DI)
 {
+    constexpr int KPR = 64 / PW;   // keys per wave and round
     __shared__ float qs[16 * 256];
     __shared__ float ws[16];
-    const int b = blockIdx.y, tid = threadIdx.x;
+    const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int e = tid; e < HI * DI; e += kThreads) qs[e] = bf2f(q_idx[(long)b * HI * DI + e]);
     if (tid < HI) ws[tid] = bf2f(w_idx[(long)b * HI + tid]);
     __syncthreads();
     const int L = seq_len_of(seq_lens, b, T);
-    const int s = blockIdx.x * kThreads + tid;
-    if (s >= L) return;
-    const uint16_t *kr = k_idx + ((long)b * T + s) * DI;
-    float dot[16];
+    const int p = lane % PW, kl = lane / PW;
+    const int key0 = blockIdx.x * kThreads + wave * 64;   // this wave's 64 keys
+    if (key0 >= L) return;
+    const bool piece = 8 * p < DI;
+    u32x4 v[PW];
 #pragma unroll
-    for (int j = 0; j < 16; j++) dot[j] = 0.f;
-    for (int e0 = 0; e0 < DI; e0 += 8) {
-        const u32x4 v = ld16(kr + e0);
+    for (int r = 0; r < PW; r++) {
+        const int s = key0 + r * KPR + kl;
+        v[r] = piece && s < L ? ld16(k_idx + ((long)b * T + s) * DI + 8 * p) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int r = 0; r < PW; r++) {
         float x[8];
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            const uint32_t w = v[e];
+            const uint32_t w = v[r][e];
             x[2 * e] = __uint_as_float(w << 16);
             x[2 * e + 1] = __uint_as_float(w & 0xffff0000u);
         }
+        float I = 0.f;
+        for (int j = 0; j < HI; j++) {
+            float dot = 0.f;
+            if (piece) {
+                const float *qj = qs + j * DI + 8 * p;
 #pragma unroll
-        for (int j = 0; j < 16; j++)
-            if (j < HI)
+                for (int e = 0; e < 8; e++) dot = __builtin_fmaf(qj[e], x[e], dot);
+            }
 #pragma unroll
-                for (int e = 0; e < 8; e++) dot[j] = __builtin_fmaf(qs[j * DI + e0 + e], x[e], dot[j]);
+            for (int o = 1; o < PW; o <<= 1) dot += __shfl_xor(dot, o);
+            I = __builtin_fmaf(ws[j], fmaxf(dot, 0.f), I);
+        }
+        const int s = key0 + r * KPR + kl;
+        if (p == 0 && s < L) scores[(long)b * T + s] = I;
     }
-    float I = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; j++)
-        if (j < HI) I = __builtin_fmaf(ws[j], fmaxf(dot[j], 0.f), I);
-    scores[(long)b * T + s] = I;
 }
 
 // larger float -> larger key (no NaN among the scores)
@@ -113,11 +129,13 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(const float *__restri
                                                            const int32_t *__restrict__ seq_lens,
                                                            int32_t *__restrict__ sel, int T, int topk)
 {
-    __shared__ int hist[256];
-    __shared__ int wsum[kTopkThreads / 64];
+    constexpr int kWaves = kTopkThreads / 64;
+    __shared__ int hist[4096];
+    __shared__ int wsum[kWaves];
+    __shared__ int wgt[kWaves], weq[kWaves];
     __shared__ uint32_t s_prefix;
     __shared__ int s_remain;
-    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int L = seq_len_of(seq_lens, b, T);
     const float *sc = scores + (long)b * T;
     int32_t *out = sel + (long)b * topk;
@@ -125,74 +143,80 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(const float *__restri
         for (int i = tid; i < topk; i += kTopkThreads) out[i] = i < L ? i : -1;
         return;
     }
-    // radix select: prefix/mask of the k-th largest key, digit by digit
+    // radix select of the k-th largest key: digits of 12, 12 and 8 bits
     uint32_t prefix = 0, mask = 0;
     int remain = topk;   // how many of the keys matching the prefix are still to be taken
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
+    for (int pass = 0; pass < 3; pass++) {
+        const int shift = pass == 0 ? 20 : pass == 1 ? 8 : 0;
+        const int bins = pass == 2 ? 256 : 4096;
+        for (int i = tid; i < bins; i += kTopkThreads) hist[i] = 0;
         __syncthreads();
         for (int s = tid; s < L; s += kTopkThreads) {
             const uint32_t u = order_key(sc[s]);
-            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1);
+            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & (bins - 1)], 1);
         }
         __syncthreads();
-        if (tid < 64) {
-            // lane l owns digits 255-4l .. 252-4l (high to low); inclusive
-            // suffix sums from digit 255 down
-            int c[4], own = 0;
+        // thread t owns digits bins-1-4t .. bins-4-4t (high to low)
+        int c[4], own = 0;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                c[i] = hist[255 - 4 * lane - i];
-                own += c[i];
-            }
-            int x = own;
+        for (int i = 0; i < 4; i++) {
+            const int dgt = bins - 1 - 4 * tid - i;
+            c[i] = dgt >= 0 ? hist[dgt] : 0;
+            own += c[i];
+        }
+        int tot;
+        int above = block_exscan(own, wsum, &tot);   // keys with a higher digit than this thread's first
 #pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int y = __shfl_up(x, o);
-                if (lane >= o) x += y;
+        for (int i = 0; i < 4; i++) {
+            if (above < remain && above + c[i] >= remain) {
+                s_prefix = prefix | ((uint32_t)(bins - 1 - 4 * tid - i) << shift);
+                s_remain = remain - above;
             }
-            int above = x - own;   // keys with a higher digit than this lane's first
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                if (above < remain && above + c[i] >= remain) {
-                    s_prefix = prefix | ((uint32_t)(255 - 4 * lane - i) << shift);
-                    s_remain = remain - above;
-                }
-                above += c[i];
-            }
+            above += c[i];
         }
         __syncthreads();
         prefix = s_prefix;
         remain = s_remain;
-        mask |= 255u << shift;
+        mask |= (uint32_t)(bins - 1) << shift;
         __syncthreads();
     }
-    // ordered compaction over contiguous ranges: keys above the threshold,
-    // then the first `remain` keys equal to it in position order
-    const int per = (L + kTopkThreads - 1) / kTopkThreads;
-    const int lo = min(L, tid * per), hi = min(L, lo + per);
-    int gt = 0, eq = 0;
-    for (int s = lo; s < hi; s++) {
-        const uint32_t u = order_key(sc[s]);
-        gt += u > prefix;
-        eq += u == prefix;
+    // ordered compaction: wave w takes a contiguous 64-aligned range, reads it
+    // coalesced, counts (ballots), then writes its kept positions in order
+    const int per = ((L + kWaves - 1) / kWaves + 63) / 64 * 64;
+    const int lo = min(L, wave * per), hi = min(L, lo + per);
+    int ngt = 0, neq = 0;
+    for (int i0 = lo; i0 < hi; i0 += 64) {
+        const int s = i0 + lane;
+        const uint32_t u = s < hi ? order_key(sc[s]) : 0u;
+        ngt += __popcll(__ballot(s < hi && u > prefix));
+        neq += __popcll(__ballot(s < hi && u == prefix));
     }
-    int tot;
-    const int eq_before = block_exscan(eq, wsum, &tot);
-    const int take_eq = max(0, min(eq, remain - eq_before));
-    const int pos0 = block_exscan(gt + take_eq, wsum, &tot);
-    int pos = pos0, eq_taken = 0;
-    for (int s = lo; s < hi; s++) {
-        const uint32_t u = order_key(sc[s]);
-        bool keep = u > prefix;
-        if (u == prefix) {
-            keep = eq_taken < take_eq;
-            eq_taken++;
-        }
-        if (keep) out[pos++] = s;
+    if (lane == 0) {
+        wgt[wave] = ngt;
+        weq[wave] = neq;
     }
-    for (int i = tot + tid; i < topk; i += kTopkThreads) out[i] = -1;
-    (void)lane;
+    __syncthreads();
+    int eq_before = 0, pos = 0;
+    for (int w = 0; w < wave; w++) {
+        const int take = max(0, min(weq[w], remain - eq_before));
+        pos += wgt[w] + take;
+        eq_before += weq[w];
+    }
+    const int take_eq = max(0, min(neq, remain - eq_before));
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int eq_seen = 0;
+    for (int i0 = lo; i0 < hi; i0 += 64) {
+        const int s = i0 + lane;
+        const uint32_t u = s < hi ? order_key(sc[s]) : 0u;
+        const bool g = s < hi && u > prefix, e = s < hi && u == prefix;
+        const unsigned long long em = __ballot(e);
+        const bool keep = g || (e && eq_seen + __popcll(em & below) < take_eq);
+        const unsigned long long km = __ballot(keep);
+        if (keep) out[pos + __popcll(km & below)] = s;
+        pos += __popcll(km);
+        eq_seen += __popcll(em);
+    }
+    (void)tid;
 }
 
 template <int DK, int DV>
@@ -326,9 +350,15 @@ bool dsa_supported(const Dims &d)
 hipError_t launch_dsa_select(const Dims &d, int HI, int DI, int topk, const int32_t *seq_lens, const void *q_idx,
                              const void *w_idx, const void *k_idx, float *scores, int32_t *sel, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_dsa_index, dim3((d.T + kThreads - 1) / kThreads, d.B), dim3(kThreads), 0, s,
-                       (const uint16_t *)q_idx, (const uint16_t *)w_idx, (const uint16_t *)k_idx, seq_lens, scores, d.T,
-                       HI, DI);
+    const dim3 grid((d.T + kThreads - 1) / kThreads, d.B);
+    const uint16_t *qi = (const uint16_t *)q_idx, *wi = (const uint16_t *)w_idx, *ki = (const uint16_t *)k_idx;
+    const int pieces = DI / 8;
+    if (pieces <= 1) hipLaunchKernelGGL(k_dsa_index<1>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI);
+    else if (pieces <= 2) hipLaunchKernelGGL(k_dsa_index<2>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI);
+    else if (pieces <= 4) hipLaunchKernelGGL(k_dsa_index<4>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI);
+    else if (pieces <= 8) hipLaunchKernelGGL(k_dsa_index<8>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI);
+    else if (pieces <= 16) hipLaunchKernelGGL(k_dsa_index<16>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI);
+    else hipLaunchKernelGGL(k_dsa_index<32>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_dsa_topk, dim3(d.B), dim3(kTopkThreads), 0, s, scores, seq_lens, sel, d.T, topk);
