@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
     __shared__ __align__(16) uint16_t ot[kM * OS];
     __shared__ __align__(16) float s_lse[kM], s_D[kM], s_g[kM];
     __shared__ uint16_t rows[kBatchWords * 32];   // selected rows of a batch, less its first row
-    __shared__ int wcnt[kThreads];
+    __shared__ int wcnt[kThreads / 64];
     __shared__ int nsel_s;
 
     const Dims &d = a.d;
@@ -267,23 +267,25 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
             const int w = w0 + tid;
             uint32_t word = w < whi ? bm[w] : 0u;
             if (32 * w + 32 > rend) word &= (1u << (rend - 32 * w)) - 1u;   // a partial last word (rend = T)
-            lds_barrier();   // rows of the previous batch are no longer read
-            wcnt[tid] = __popc(word);
-            lds_barrier();
-            if (tid == 0) {
-                int acc = 0;
-                for (int i = 0; i < kThreads; i++) {
-                    const int x = wcnt[i];
-                    wcnt[i] = acc;
-                    acc += x;
-                }
-                nsel_s = acc;
+            // exclusive prefix of the words' bit counts: within each wave by
+            // shuffles, then over the 4 waves' totals
+            const int cnt = __popc(word);
+            int incl = cnt;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(incl, o);
+                if (lane >= o) incl += y;
             }
+            lds_barrier();   // rows and wave totals of the previous batch are no longer read
+            if (lane == 63) wcnt[wave] = incl;
             lds_barrier();
+            int before = 0;
+            for (int w2 = 0; w2 < wave; w2++) before += wcnt[w2];
             {
-                int o = wcnt[tid];
+                int o = before + incl - cnt;
                 for (uint32_t x = word; x; x &= x - 1) rows[o++] = (uint16_t)(32 * tid + __ffs(x) - 1);
             }
+            if (tid == 0) nsel_s = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
             lds_barrier();
             const int base = 32 * w0;
             run(nsel_s, 1, [&](int i) { return base + (int)rows[i]; });
@@ -300,31 +302,45 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
     }
 }
 
-// Row pass: one wave per (b, t, KV head) with its 16 heads; per branch (0
-// compressed, 1 selected, 2 window) two sweeps over 64-key chunks:
+// Row pass: one wave per (b, t, KV head) with its 16 heads, 4 consecutive
+// positions per workgroup; per branch (0 compressed, 1 selected, 2 window)
+// two sweeps over 64-key chunks:
 //   1. S^T = K Q^T and dP^T = V dO^T; online max m, sum l of exp(S) and sum of
 //      exp(S) dP, which give lse and dO . o_branch = (sum p dP) / l without
 //      forming o_branch; then D = gate dO . o and the gate's logit gradient.
 //   2. S^T, dP^T again; dS^T = scale p (gate dP - D) feeds dQ^T += K^T dS^T
-//      directly from the score layout; K reaches the A operand through a
-//      wave-private 32-key LDS buffer read with transposing reads.
+//      directly from the score layout; K reaches the A operand through LDS,
+//      read with transposing reads.
 // Chunks (as in the forward): compressed blocks [0, nvis), 16 i + 31 <= t;
 // the distinct valid selected blocks in ascending order, tokens <= t; the
-// window [t - w + 1, t].  Loads of keys outside a chunk's valid range read the
-// nearest valid key instead, so no unwritten or stale value enters a product.
+// window [t - w + 1, t].  The compressed and window chunks of the 4 positions
+// nearly coincide, so the workgroup walks one chunk sequence for all of them
+// (up to the last position's range) and stages each chunk's K and V in LDS
+// once; each wave masks the keys its position does not see and skips chunks
+// with none.  Selected blocks differ per position: each wave loads its own
+// and passes K through a private 32-key LDS buffer.  Loads of keys outside a
+// range read the nearest valid key instead, so no unwritten or stale value
+// enters a product.
 template <int DK, int DV>
-__global__ __launch_bounds__(kThreads) void k_bwd_rows_mfma(BwdArgs a)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_rows_mfma(BwdArgs a)
 {
-    constexpr int KS = DK + 16;
+    constexpr int KS = DK + 16, VS = DV + 16;
     constexpr int NQ = DK / 32, NO = DV / 32;
-    __shared__ __align__(16) uint16_t kws[kThreads / 64][32 * KS];
+    constexpr int kShared = 64 * KS + 64 * VS, kPrivate = (kThreads / 64) * 32 * KS;
+    // one buffer, two uses: the shared K and V chunk (compressed, window) or
+    // the waves' private K buffers (selected)
+    __shared__ __align__(16) uint16_t lds[kShared > kPrivate ? kShared : kPrivate];
     __shared__ int blks[kThreads / 64][16];
+    uint16_t *ksh = lds, *vsh = lds + 64 * KS;
     const Dims &d = a.d;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const int t = blockIdx.x * (kThreads / 64) + wave, g = blockIdx.y, b = blockIdx.z;
-    if (t >= d.T) return;   // waves never wait for each other
-    uint16_t *kw = kws[wave];
+    const int g = blockIdx.y, b = blockIdx.z;
+    const int t_lo = blockIdx.x * (kThreads / 64), t_hi = min(d.T - 1, t_lo + kThreads / 64 - 1);
+    // a wave past the sequence computes position T-1 and stores nothing
+    const bool act = t_lo + wave < d.T;
+    const int t = act ? t_lo + wave : d.T - 1;
+    uint16_t *kw = lds + wave * 32 * KS;
     int *blk = blks[wave];
     const long bgi = (long)b * d.Hkv + g;
     const long row0 = ((long)b * d.T + t) * d.Hq + (long)g * 16;
@@ -371,104 +387,203 @@ __global__ __launch_bounds__(kThreads) void k_bwd_rows_mfma(BwdArgs a)
 
     const float sl2 = d.scale * kLog2e;
     const int nvis = t >= 31 ? (t - 31) / 16 + 1 : 0;
-    const int wlo = max(0, t - d.w + 1);
-    // S^T and dP^T of one 16-key tile; kfr gets its K rows (A operand layout:
-    // key li, columns 32 c + 8 lg .. +7)
-    auto scores = [&](const uint16_t *K, const uint16_t *V, int k16, int klo, int khi, f32x4 &S, f32x4 &P,
-                      u32x4 *kfr) {
-        const int kl = min(max(k16 + li, klo), khi);
-        S = f32x4{0.f, 0.f, 0.f, 0.f};
-        P = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < NQ; c++) {
-            kfr[c] = ld16(K + (long)kl * DK + 32 * c + 8 * lg);
-            S = mfma16(as_bf16x8(kfr[c]), as_bf16x8(qf[c]), S);
-        }
-#pragma unroll
-        for (int c = 0; c < NO; c++)
-            P = mfma16(as_bf16x8(ld16(V + (long)kl * DV + 32 * c + 8 * lg)), as_bf16x8(of[c]), P);
-    };
+    const int nvis_hi = t_hi >= 31 ? (t_hi - 31) / 16 + 1 : 0;
+    const int wlo = max(0, t - d.w + 1), wlo0 = max(0, t_lo - d.w + 1);
     f32x4 dqa[DK / 16];
 #pragma unroll
     for (int i = 0; i < DK / 16; i++) dqa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float dzs[3];
     const int trow = li >> 2, tcol = 4 * (li & 3);
-    for (int br = 0; br < 3; br++) {
-        const uint16_t *K = br == 0 ? (const uint16_t *)a.kc + bgi * d.npad * DK : (const uint16_t *)a.k + bgi * d.T * DK;
-        const uint16_t *V = br == 0 ? (const uint16_t *)a.vc + bgi * d.npad * DV : (const uint16_t *)a.v + bgi * d.T * DV;
-        const int nch = br == 0 ? (nvis + 63) / 64 : br == 1 ? nsel : (t - wlo + 64) / 64;
-        auto chunk = [&](int ch, int &key0, int &klo, int &khi) {
-            if (br == 0) {
-                key0 = 64 * ch;
-                klo = 0;
-                khi = nvis - 1;
-            } else if (br == 1) {
-                key0 = 64 * blk[ch];
-                klo = key0;
-                khi = min(t, key0 + 63);
-            } else {
-                key0 = wlo + 64 * ch;
-                klo = wlo;
-                khi = t;
-            }
-        };
-        // sweep 1
-        float m = -INFINITY, l = 0.f, acc = 0.f;
-        for (int ch = 0; ch < nch; ch++) {
-            int key0, klo, khi;
-            chunk(ch, key0, klo, khi);
-            float sc[4][4], dp[4][4];
-            float mc = -INFINITY;
+
+    // S^T and dP^T of one 16-key tile from K rows kr (A operand layout: key
+    // li, columns 32 c + 8 lg .. +7) and V rows vr; kfr keeps the K pieces
+    auto tile_scores = [&](const uint16_t *kr, long ks, const uint16_t *vr, long vs, f32x4 &S, f32x4 &P, u32x4 *kfr) {
+        S = f32x4{0.f, 0.f, 0.f, 0.f};
+        P = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kt = 0; kt < 4; kt++) {
-                f32x4 S, P;
-                u32x4 kfr[NQ];
-                scores(K, V, key0 + 16 * kt, klo, khi, S, P, kfr);
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int key = key0 + 16 * kt + 4 * lg + e;
-                    sc[kt][e] = key >= klo && key <= khi ? S[e] * sl2 : -INFINITY;
-                    dp[kt][e] = P[e];
-                    mc = fmaxf(mc, sc[kt][e]);
-                }
-            }
-            mc = fmaxf(mc, __shfl_xor(mc, 16));
-            mc = fmaxf(mc, __shfl_xor(mc, 32));
-            const float mn = fmaxf(m, mc);
-            const float al = fast_exp2(m - mn);
-            float ls = 0.f, as = 0.f;
-#pragma unroll
-            for (int kt = 0; kt < 4; kt++)
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const float p = fast_exp2(sc[kt][e] - mn);
-                    ls += p;
-                    as = __builtin_fmaf(p, sc[kt][e] == -INFINITY ? 0.f : dp[kt][e], as);
-                }
-            l = __builtin_fmaf(l, al, ls);
-            acc = __builtin_fmaf(acc, al, as);
-            m = mn;
+        for (int c = 0; c < NQ; c++) {
+            kfr[c] = ld16(kr + li * ks + 32 * c + 8 * lg);
+            S = mfma16(as_bf16x8(kfr[c]), as_bf16x8(qf[c]), S);
         }
+#pragma unroll
+        for (int c = 0; c < NO; c++) P = mfma16(as_bf16x8(ld16(vr + li * vs + 32 * c + 8 * lg)), as_bf16x8(of[c]), P);
+    };
+    // sweep-1 update over a 64-key chunk: sc, dp hold its scores (log2 units,
+    // -inf where masked) and dP
+    auto online = [&](float (&sc)[4][4], float (&dp)[4][4], float &m, float &l, float &acc) {
+        float mc = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; kt++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) mc = fmaxf(mc, sc[kt][e]);
+        mc = fmaxf(mc, __shfl_xor(mc, 16));
+        mc = fmaxf(mc, __shfl_xor(mc, 32));
+        const float mn = fmaxf(m, mc);
+        const float al = fast_exp2(m - mn);
+        float ls = 0.f, as = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 4; kt++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const float p = fast_exp2(sc[kt][e] - mn);
+                ls += p;
+                as = __builtin_fmaf(p, sc[kt][e] == -INFINITY ? 0.f : dp[kt][e], as);
+            }
+        l = __builtin_fmaf(l, al, ls);
+        acc = __builtin_fmaf(acc, al, as);
+        m = mn;
+    };
+    // the branch's statistics from its sweep-1 sums
+    auto finish = [&](int br, float m, float l, float acc, float &lse2, float &D) {
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
         acc += __shfl_xor(acc, 16);
         acc += __shfl_xor(acc, 32);
-        const float lse2 = l > 0.f ? m + fast_log2(l) : -INFINITY;
+        lse2 = l > 0.f ? m + fast_log2(l) : -INFINITY;
         const float dOo = l > 0.f ? acc / l : 0.f;
         const float gv = gate[br];
-        const float D = gv * dOo;
+        D = gv * dOo;
         dzs[br] = dOo * gv * (1.f - gv);
-        if (lg == 0) {
+        if (act && lg == 0) {
             float *st = a.rs + (row0 + h) * kBwdStat + br * 4;
             st[0] = lse2 * 0.6931471805599453f;
             st[1] = D;
             st[2] = gv;
             st[3] = dzs[br];
         }
-        // sweep 2
+    };
+    // ds of a tile's 4 keys per lane, scaled
+    auto tile_ds = [&](const f32x4 &S, const f32x4 &P, int k16, int klo, int khi, float lse2, float gv, float D,
+                       float *ds) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int key = k16 + 4 * lg + e;
+            const float p = key >= klo && key <= khi ? fast_exp2(__builtin_fmaf(S[e], sl2, -lse2)) : 0.f;
+            ds[e] = p * __builtin_fmaf(gv, P[e], -D) * d.scale;
+        }
+    };
+    // dQ^T += K^T dS^T over 32 keys whose K rows sit at kb (stride KS):
+    // contraction slot 8 lg + e <-> key 4 lg + e (e < 4) or 16 + 4 lg + e - 4
+    auto dq_step = [&](const uint16_t *kb, const float *ds0, const float *ds1) {
+        u32x4 y;
+        y[0] = pack_bf16x2(ds0[0], ds0[1]);
+        y[1] = pack_bf16x2(ds0[2], ds0[3]);
+        y[2] = pack_bf16x2(ds1[0], ds1[1]);
+        y[3] = pack_bf16x2(ds1[2], ds1[3]);
+        const bf16x8 bs = as_bf16x8(y);
+        const int r0 = 4 * lg + trow;
+#pragma unroll
+        for (int dt = 0; dt < DK / 16; dt++) {
+            const uint2 lo = ld_tr16(kb + r0 * KS + 16 * dt + tcol);
+            const uint2 hi = ld_tr16(kb + (r0 + 16) * KS + 16 * dt + tcol);
+            dqa[dt] = mfma16(as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y}), bs, dqa[dt]);
+        }
+    };
+
+    for (int br = 0; br < 3; br++) {
+        const float gv = gate[br];
+        if (br == 1) {
+            // selected: every wave on its own blocks, K via its private buffer
+            lds_barrier();   // the shared chunk of the compressed branch is no longer read
+            const uint16_t *K = (const uint16_t *)a.k + bgi * d.T * DK;
+            const uint16_t *V = (const uint16_t *)a.v + bgi * d.T * DV;
+            float m = -INFINITY, l = 0.f, acc = 0.f;
+            for (int ch = 0; ch < nsel; ch++) {
+                const int key0 = 64 * blk[ch], khi = min(t, key0 + 63);
+                float sc[4][4], dp[4][4];
+#pragma unroll
+                for (int kt = 0; kt < 4; kt++) {
+                    f32x4 S, P;
+                    u32x4 kfr[NQ];
+                    const int row = min(key0 + 16 * kt + li, khi);   // rows past the range read its last key
+                    tile_scores(K + (long)(row - li) * DK, DK, V + (long)(row - li) * DV, DV, S, P, kfr);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const int key = key0 + 16 * kt + 4 * lg + e;
+                        sc[kt][e] = key <= khi ? S[e] * sl2 : -INFINITY;
+                        dp[kt][e] = P[e];
+                    }
+                }
+                online(sc, dp, m, l, acc);
+            }
+            float lse2, D;
+            finish(1, m, l, acc, lse2, D);
+            for (int ch = 0; ch < nsel; ch++) {
+                const int key0 = 64 * blk[ch], khi = min(t, key0 + 63);
+#pragma unroll
+                for (int half = 0; half < 2; half++) {
+                    float ds[2][4];
+#pragma unroll
+                    for (int kh = 0; kh < 2; kh++) {
+                        f32x4 S, P;
+                        u32x4 kfr[NQ];
+                        const int k16 = key0 + 32 * half + 16 * kh;
+                        const int row = min(k16 + li, khi);
+                        tile_scores(K + (long)(row - li) * DK, DK, V + (long)(row - li) * DV, DV, S, P, kfr);
+#pragma unroll
+                        for (int c = 0; c < NQ; c++) st16(kw + (16 * kh + li) * KS + 32 * c + 8 * lg, kfr[c]);
+                        tile_ds(S, P, k16, key0, khi, lse2, gv, D, ds[kh]);
+                    }
+                    dq_step(kw, ds[0], ds[1]);
+                }
+            }
+            continue;
+        }
+        // compressed or window: one chunk sequence for the workgroup
+        const uint16_t *K = br == 0 ? (const uint16_t *)a.kc + bgi * d.npad * DK : (const uint16_t *)a.k + bgi * d.T * DK;
+        const uint16_t *V = br == 0 ? (const uint16_t *)a.vc + bgi * d.npad * DV : (const uint16_t *)a.v + bgi * d.T * DV;
+        const int glo = br == 0 ? 0 : wlo0, ghi = br == 0 ? nvis_hi - 1 : t_hi;   // keys loaded
+        const int klo = br == 0 ? 0 : wlo, khi = br == 0 ? nvis - 1 : t;          // keys this row sees
+        const int nch = ghi >= glo ? (ghi - glo + 64) / 64 : 0;
+        auto stage = [&](int key0) {
+            // 64 K rows and 64 V rows, rows past the range read its last key
+#pragma unroll
+            for (int i = 0; i < (64 * DK / 8 + kThreads - 1) / kThreads; i++) {
+                const int pc = tid + kThreads * i;
+                if (pc < 64 * DK / 8) {
+                    const int r = pc / (DK / 8), cc = 8 * (pc % (DK / 8));
+                    st16(ksh + r * KS + cc, ld16(K + (long)min(key0 + r, ghi) * DK + cc));
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < (64 * DV / 8 + kThreads - 1) / kThreads; i++) {
+                const int pc = tid + kThreads * i;
+                if (pc < 64 * DV / 8) {
+                    const int r = pc / (DV / 8), cc = 8 * (pc % (DV / 8));
+                    st16(vsh + r * VS + cc, ld16(V + (long)min(key0 + r, ghi) * DV + cc));
+                }
+            }
+        };
+        float m = -INFINITY, l = 0.f, acc = 0.f;
         for (int ch = 0; ch < nch; ch++) {
-            int key0, klo, khi;
-            chunk(ch, key0, klo, khi);
+            const int key0 = glo + 64 * ch;
+            lds_barrier();
+            stage(key0);
+            lds_barrier();
+            if (max(key0, klo) > min(key0 + 63, khi)) continue;   // nothing this row sees
+            float sc[4][4], dp[4][4];
+#pragma unroll
+            for (int kt = 0; kt < 4; kt++) {
+                f32x4 S, P;
+                u32x4 kfr[NQ];
+                tile_scores(ksh + 16 * kt * KS, KS, vsh + 16 * kt * VS, VS, S, P, kfr);
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int key = key0 + 16 * kt + 4 * lg + e;
+                    sc[kt][e] = key >= klo && key <= khi ? S[e] * sl2 : -INFINITY;
+                    dp[kt][e] = P[e];
+                }
+            }
+            online(sc, dp, m, l, acc);
+        }
+        float lse2, D;
+        finish(br, m, l, acc, lse2, D);
+        for (int ch = 0; ch < nch; ch++) {
+            const int key0 = glo + 64 * ch;
+            lds_barrier();
+            stage(key0);
+            lds_barrier();
+            if (max(key0, klo) > min(key0 + 63, khi)) continue;
 #pragma unroll
             for (int half = 0; half < 2; half++) {
                 float ds[2][4];
@@ -476,35 +591,15 @@ __global__ __launch_bounds__(kThreads) void k_bwd_rows_mfma(BwdArgs a)
                 for (int kh = 0; kh < 2; kh++) {
                     f32x4 S, P;
                     u32x4 kfr[NQ];
-                    const int k16 = key0 + 32 * half + 16 * kh;
-                    scores(K, V, k16, klo, khi, S, P, kfr);
-#pragma unroll
-                    for (int c = 0; c < NQ; c++) st16(kw + (16 * kh + li) * KS + 32 * c + 8 * lg, kfr[c]);
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        const int key = k16 + 4 * lg + e;
-                        const float p =
-                            key >= klo && key <= khi ? fast_exp2(__builtin_fmaf(S[e], sl2, -lse2)) : 0.f;
-                        ds[kh][e] = p * __builtin_fmaf(gv, P[e], -D) * d.scale;
-                    }
+                    const int r16 = 32 * half + 16 * kh;
+                    tile_scores(ksh + r16 * KS, KS, vsh + r16 * VS, VS, S, P, kfr);
+                    tile_ds(S, P, key0 + r16, klo, khi, lse2, gv, D, ds[kh]);
                 }
-                // contraction slot 8 lg + e <-> key 4 lg + e (e < 4) or 16 + 4 lg + e - 4 of the 32
-                u32x4 y;
-                y[0] = pack_bf16x2(ds[0][0], ds[0][1]);
-                y[1] = pack_bf16x2(ds[0][2], ds[0][3]);
-                y[2] = pack_bf16x2(ds[1][0], ds[1][1]);
-                y[3] = pack_bf16x2(ds[1][2], ds[1][3]);
-                const bf16x8 bs = as_bf16x8(y);
-                const int r0 = 4 * lg + trow;
-#pragma unroll
-                for (int dt = 0; dt < DK / 16; dt++) {
-                    const uint2 lo = ld_tr16(kw + r0 * KS + 16 * dt + tcol);
-                    const uint2 hi = ld_tr16(kw + (r0 + 16) * KS + 16 * dt + tcol);
-                    dqa[dt] = mfma16(as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y}), bs, dqa[dt]);
-                }
+                dq_step(ksh + 32 * half * KS, ds[0], ds[1]);
             }
         }
     }
+    if (!act) return;
     // dq = dQ^T (C[i = column][j = head]: lane j + 16 (i / 4), element i % 4)
     // plus the gate terms sum_c dz_c W_g[h][c]
     uint16_t *dq = (uint16_t *)a.dq + (row0 + h) * DK;
