@@ -54,16 +54,6 @@ struct CmpLds {
     uint16_t v[2][kTile * VS];             // V key-major; V^T fragments come from transpose reads
 };
 
-// Sum over the 16 lanes of each DPP row (row rotations by 8, 4, 2, 1).  Every
-// step adds two values in either order, so all 16 lanes end with the same bits.
-__device__ __forceinline__ float row_sum16(float x)
-{
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
-    return x;
-}
 
 // LDS row of key k (0..31) inside a 32-key M-tile.  MFMA output row i sits in
 // lane half (i/4)%2, register 4*(i/8) + i%4; putting key 16*h + r in row

@@ -6,9 +6,9 @@
 // summed over that set.  One selection per sequence serves every query head
 // and KV group.  bf16 storage, fp32 arithmetic.
 //
-// k_dsa_index  I[s] = sum_j w_j relu(q_j . k_s): the lanes of a group each
-//              read one 16-byte piece of a key (HBM: the indexer keys are read
-//              once, whole rows per load).
+// k_dsa_index  I[s] = sum_j w_j relu(q_j . k_s) on the matrix cores (keys as
+//              M, indexer heads as N), the head sum by DPP row reductions
+//              (HBM: the indexer keys are read once).
 // k_dsa_topk   one 1024-thread workgroup per sequence: radix select of the
 //              k-th largest score over order-preserving 32-bit keys (digits
 //              of 12, 12 and 8 bits, histograms with integer LDS atomics),
@@ -39,58 +39,57 @@ __device__ __forceinline__ int seq_len_of(const int32_t *seq_lens, int b, int T)
 }
 
 // q_idx [B][HI][DI], w_idx [B][HI], k_idx [B][T][DI] (bf16); scores [B][T] fp32.
-// PW = lanes per key, a power of two >= DI / 8: lane p of a key's group reads
-// the key's 16-byte piece p (p < DI / 8), so a wave reads 64 / PW whole rows
-// per load; each wave takes 64 keys in PW rounds, all loads issued first;
-// the per-head partial dots are summed over the group by butterfly shuffles.
-template <int PW>
+// Scores^T = K Q^T on the matrix cores: 16 keys as M, the indexer heads as N
+// (zero past HI), DI as the contraction in NC steps of 32 (zero past DI).
+// Lane (key li, group lg) loads its key's 8 columns per step; in the result
+// lane (head li, group lg) holds keys 4 lg .. 4 lg + 3, so the weighted ReLU
+// sum over heads is a 16-lane row sum.  Each wave takes 64 keys, all loads
+// issued first.
+template <int NC>
 __global__ __launch_bounds__(kThreads) void k_dsa_index(const uint16_t *__restrict__ q_idx,
                                                         const uint16_t *__restrict__ w_idx,
                                                         const uint16_t *__restrict__ k_idx,
                                                         const int32_t *__restrict__ seq_lens, float *__restrict__ scores,
                                                         int T, int HI, int DI)
 {
-    constexpr int KPR = 64 / PW;   // keys per wave and round
-    __shared__ float qs[16 * 256];
-    __shared__ float ws[16];
-    const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int e = tid; e < HI * DI; e += kThreads) qs[e] = bf2f(q_idx[(long)b * HI * DI + e]);
-    if (tid < HI) ws[tid] = bf2f(w_idx[(long)b * HI + tid]);
-    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int b = blockIdx.y;
     const int L = seq_len_of(seq_lens, b, T);
-    const int p = lane % PW, kl = lane / PW;
-    const int key0 = blockIdx.x * kThreads + wave * 64;   // this wave's 64 keys
-    if (key0 >= L) return;
-    const bool piece = 8 * p < DI;
-    u32x4 v[PW];
+    const int key0 = blockIdx.x * kThreads + wave * 64;
+    if (key0 >= L) return;   // no barriers in this kernel
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    u32x4 ka[4][NC], qb[NC];
 #pragma unroll
-    for (int r = 0; r < PW; r++) {
-        const int s = key0 + r * KPR + kl;
-        v[r] = piece && s < L ? ld16(k_idx + ((long)b * T + s) * DI + 8 * p) : u32x4{0u, 0u, 0u, 0u};
+    for (int kt = 0; kt < 4; kt++) {
+        const int sl = min(key0 + 16 * kt + li, L - 1);   // keys past the length read the last one
+#pragma unroll
+        for (int c = 0; c < NC; c++) {
+            const int e0 = 32 * c + 8 * lg;
+            ka[kt][c] = e0 < DI ? ld16(k_idx + ((long)b * T + sl) * DI + e0) : z;
+        }
     }
 #pragma unroll
-    for (int r = 0; r < PW; r++) {
-        float x[8];
+    for (int c = 0; c < NC; c++) {
+        const int e0 = 32 * c + 8 * lg;
+        qb[c] = li < HI && e0 < DI ? ld16(q_idx + ((long)b * HI + li) * DI + e0) : z;
+    }
+    const float wj = li < HI ? bf2f(w_idx[(long)b * HI + li]) : 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const uint32_t w = v[r][e];
-            x[2 * e] = __uint_as_float(w << 16);
-            x[2 * e + 1] = __uint_as_float(w & 0xffff0000u);
-        }
-        float I = 0.f;
-        for (int j = 0; j < HI; j++) {
-            float dot = 0.f;
-            if (piece) {
-                const float *qj = qs + j * DI + 8 * p;
+    for (int kt = 0; kt < 4; kt++) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int e = 0; e < 8; e++) dot = __builtin_fmaf(qj[e], x[e], dot);
+        for (int c = 0; c < NC; c++) acc = mfma16(as_bf16x8(ka[kt][c]), as_bf16x8(qb[c]), acc);
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) v[e] = row_sum16(wj * fmaxf(acc[e], 0.f));
+        if (li == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int s = key0 + 16 * kt + 4 * lg + e;
+                if (s < L) scores[(long)b * T + s] = v[e];
             }
-#pragma unroll
-            for (int o = 1; o < PW; o <<= 1) dot += __shfl_xor(dot, o);
-            I = __builtin_fmaf(ws[j], fmaxf(dot, 0.f), I);
         }
-        const int s = key0 + r * KPR + kl;
-        if (p == 0 && s < L) scores[(long)b * T + s] = I;
     }
 }
 
@@ -352,13 +351,10 @@ hipError_t launch_dsa_select(const Dims &d, int HI, int DI, int topk, const int3
 {
     const dim3 grid((d.T + kThreads - 1) / kThreads, d.B);
     const uint16_t *qi = (const uint16_t *)q_idx, *wi = (const uint16_t *)w_idx, *ki = (const uint16_t *)k_idx;
-    const int pieces = DI / 8;
-    if (pieces <= 1) hipLaunchKernelGGL(k_dsa_index<1>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI);
-    else if (pieces <= 2) hipLaunchKernelGGL(k_dsa_index<2>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI);
-    else if (pieces <= 4) hipLaunchKernelGGL(k_dsa_index<4>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI);
-    else if (pieces <= 8) hipLaunchKernelGGL(k_dsa_index<8>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI);
-    else if (pieces <= 16) hipLaunchKernelGGL(k_dsa_index<16>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI);
-    else hipLaunchKernelGGL(k_dsa_index<32>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI);
+    if (DI <= 32) hipLaunchKernelGGL(k_dsa_index<1>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI);
+    else if (DI <= 64) hipLaunchKernelGGL(k_dsa_index<2>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI);
+    else if (DI <= 128) hipLaunchKernelGGL(k_dsa_index<4>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI);
+    else hipLaunchKernelGGL(k_dsa_index<8>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_dsa_topk, dim3(d.B), dim3(kTopkThreads), 0, s, scores, seq_lens, sel, d.T, topk);

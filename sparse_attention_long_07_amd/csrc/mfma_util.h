@@ -117,6 +117,17 @@ __device__ __forceinline__ float row_transpose_sum16(const float v[16], int lane
     return keep + dpp<kQuadXor1>(send);
 }
 
+// Sum over the 16 lanes of each DPP row (row rotations by 8, 4, 2, 1).  Every
+// step adds two values in either order, so all 16 lanes end with the same bits.
+__device__ __forceinline__ float row_sum16(float x)
+{
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+    return x;
+}
+
 // Wait until every outstanding vector-memory load of this wave has returned
 // (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima).
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
