@@ -150,9 +150,18 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(const float *__restri
         const int bins = pass == 2 ? 256 : 4096;
         for (int i = tid; i < bins; i += kTopkThreads) hist[i] = 0;
         __syncthreads();
-        for (int s = tid; s < L; s += kTopkThreads) {
-            const uint32_t u = order_key(sc[s]);
-            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & (bins - 1)], 1);
+        // 8 loads in flight per thread before their atomics
+        for (int s0 = tid; s0 < L; s0 += 8 * kTopkThreads) {
+            uint32_t u[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int s = s0 + i * kTopkThreads;
+                u[i] = s < L ? order_key(sc[s]) : 0u;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                if (s0 + i * kTopkThreads < L && (u[i] & mask) == prefix) atomicAdd(&hist[(u[i] >> shift) & (bins - 1)], 1);
+            }
         }
         __syncthreads();
         // thread t owns digits bins-1-4t .. bins-4-4t (high to low)
@@ -184,11 +193,19 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(const float *__restri
     const int per = ((L + kWaves - 1) / kWaves + 63) / 64 * 64;
     const int lo = min(L, wave * per), hi = min(L, lo + per);
     int ngt = 0, neq = 0;
-    for (int i0 = lo; i0 < hi; i0 += 64) {
-        const int s = i0 + lane;
-        const uint32_t u = s < hi ? order_key(sc[s]) : 0u;
-        ngt += __popcll(__ballot(s < hi && u > prefix));
-        neq += __popcll(__ballot(s < hi && u == prefix));
+    for (int i0 = lo; i0 < hi; i0 += 4 * 64) {
+        uint32_t u[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int s = i0 + 64 * i + lane;
+            u[i] = s < hi ? order_key(sc[s]) : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int s = i0 + 64 * i + lane;
+            ngt += __popcll(__ballot(s < hi && u[i] > prefix));
+            neq += __popcll(__ballot(s < hi && u[i] == prefix));
+        }
     }
     if (lane == 0) {
         wgt[wave] = ngt;
@@ -204,16 +221,24 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(const float *__restri
     const int take_eq = max(0, min(neq, remain - eq_before));
     const unsigned long long below = (1ull << lane) - 1ull;
     int eq_seen = 0;
-    for (int i0 = lo; i0 < hi; i0 += 64) {
-        const int s = i0 + lane;
-        const uint32_t u = s < hi ? order_key(sc[s]) : 0u;
-        const bool g = s < hi && u > prefix, e = s < hi && u == prefix;
-        const unsigned long long em = __ballot(e);
-        const bool keep = g || (e && eq_seen + __popcll(em & below) < take_eq);
-        const unsigned long long km = __ballot(keep);
-        if (keep) out[pos + __popcll(km & below)] = s;
-        pos += __popcll(km);
-        eq_seen += __popcll(em);
+    for (int i0 = lo; i0 < hi; i0 += 4 * 64) {
+        uint32_t u[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int s = i0 + 64 * i + lane;
+            u[i] = s < hi ? order_key(sc[s]) : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int s = i0 + 64 * i + lane;
+            const bool g = s < hi && u[i] > prefix, e = s < hi && u[i] == prefix;
+            const unsigned long long em = __ballot(e);
+            const bool keep = g || (e && eq_seen + __popcll(em & below) < take_eq);
+            const unsigned long long km = __ballot(keep);
+            if (keep) out[pos + __popcll(km & below)] = s;
+            pos += __popcll(km);
+            eq_seen += __popcll(em);
+        }
     }
     (void)tid;
 }
