@@ -954,8 +954,12 @@ hipError_t launch_all(const BwdArgs &A, hipStream_t s)
         pw.ncmp = d.ncmp;
         pw.npad = d.npad;
         pw.out = isk ? A.dwck : A.dwcv;
-        hipLaunchKernelGGL(k_gemm<DwProblem<T>>, dim3((pw.M + 63) / 64, (pw.N + 63) / 64, 1), dim3(kThreads), 0, s,
-                           pw);
+        if (bwd_keys_mfma_ok(d)) {
+            if ((e = launch_bwd_dw_mfma(A, isk == 1, s)) != hipSuccess) return e;
+        } else {
+            hipLaunchKernelGGL(k_gemm<DwProblem<T>>, dim3((pw.M + 63) / 64, (pw.N + 63) / 64, 1), dim3(kThreads), 0,
+                               s, pw);
+        }
         DxProblem<T> px;
         px.M = (d.T + 15) / 16;
         px.N = 16 * dim;

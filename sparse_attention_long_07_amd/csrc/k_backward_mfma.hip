@@ -643,6 +643,79 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_sum(BwdArgs a)
     else *(f32x4 *)(a.dv_raw + (bgi * d.T + kk) * DV + 4 * q4 - DK) = s;
 }
 
+// Weight gradient of one compression map on the matrix cores:
+//   dW[c][m] = sum_r G[r][c] x_r[m] + colsum[c] PE[m],  r = (b, head, block i < ncmp),
+// x_r = the 32 dim tokens of block i flattened, G = the compressed-key (or
+// -value) gradient, colsum[c] = sum_r G[r][c].  A workgroup owns a 64 x 64
+// tile of dW (wave w: channels 16 w .. 16 w + 15); per 64-row step G (as
+// bf16) and x are staged in LDS and both operands are read with transposing
+// reads (the contraction index r is the row index of both).
+template <int DIM>
+__global__ __launch_bounds__(kThreads) void k_bwd_dw_mfma(const float *__restrict__ G, int gs,
+                                                          const uint16_t *__restrict__ x, const uint16_t *__restrict__ pe,
+                                                          const float *__restrict__ colsum, float *__restrict__ out,
+                                                          int T, int ncmp, int npad, int rows)
+{
+    constexpr int RS = 72;   // LDS row stride (bf16) of the staged tiles
+    constexpr int N = 32 * DIM;
+    __shared__ __align__(16) uint16_t gt[64 * RS], xt[64 * RS];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int c0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
+    f32x4 acc[4];
+#pragma unroll
+    for (int n = 0; n < 4; n++) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // staging: thread -> (row tid / 4, 16 columns from 16 (tid % 4))
+    const int sr = tid >> 2, sc = 16 * (tid & 3);
+    const int trow = li >> 2, tcol = 4 * (li & 3);
+    for (int r0 = 0; r0 < rows; r0 += 64) {
+        const int r = r0 + sr;
+        u32x4 gv0 = {0u, 0u, 0u, 0u}, gv1 = {0u, 0u, 0u, 0u}, xv0 = {0u, 0u, 0u, 0u}, xv1 = {0u, 0u, 0u, 0u};
+        if (r < rows) {
+            const int bh = r / ncmp, i = r % ncmp;
+            const float *gr = G + ((long)bh * npad + i) * gs + c0 + sc;
+            const float4 f0 = *(const float4 *)gr, f1 = *(const float4 *)(gr + 4);
+            const float4 f2 = *(const float4 *)(gr + 8), f3 = *(const float4 *)(gr + 12);
+            gv0 = u32x4{pack_bf16x2(f0.x, f0.y), pack_bf16x2(f0.z, f0.w), pack_bf16x2(f1.x, f1.y), pack_bf16x2(f1.z, f1.w)};
+            gv1 = u32x4{pack_bf16x2(f2.x, f2.y), pack_bf16x2(f2.z, f2.w), pack_bf16x2(f3.x, f3.y), pack_bf16x2(f3.z, f3.w)};
+            const uint16_t *xr = x + ((long)bh * T + 16L * i) * DIM + m0 + sc;
+            xv0 = ld16(xr);
+            xv1 = ld16(xr + 8);
+        }
+        lds_barrier();   // the previous step's reads are done
+        st16(gt + sr * RS + sc, gv0);
+        st16(gt + sr * RS + sc + 8, gv1);
+        st16(xt + sr * RS + sc, xv0);
+        st16(xt + sr * RS + sc + 8, xv1);
+        lds_barrier();
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++) {
+            // A[i = channel][k = row]: rows 32 ks + 8 lg .. +7 of channel 16 wave + li
+            const int ra = 32 * ks + 8 * lg + trow;
+            const uint2 a0 = ld_tr16(gt + ra * RS + 16 * wave + tcol);
+            const uint2 a1 = ld_tr16(gt + (ra + 4) * RS + 16 * wave + tcol);
+            const bf16x8 av = as_bf16x8(u32x4{a0.x, a0.y, a1.x, a1.y});
+#pragma unroll
+            for (int n = 0; n < 4; n++) {
+                const uint2 b0 = ld_tr16(xt + ra * RS + 16 * n + tcol);
+                const uint2 b1 = ld_tr16(xt + (ra + 4) * RS + 16 * n + tcol);
+                acc[n] = mfma16(av, as_bf16x8(u32x4{b0.x, b0.y, b1.x, b1.y}), acc[n]);
+            }
+        }
+    }
+    // C[i = channel][j = column]: lane j + 16 (i / 4), element i % 4
+#pragma unroll
+    for (int n = 0; n < 4; n++) {
+        const int m = m0 + 16 * n + li;
+        const float pm = bf2f(pe[m]);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int c = c0 + 16 * wave + 4 * lg + e;
+            out[(long)c * N + m] = __builtin_fmaf(colsum[c], pm, acc[n][e]);
+        }
+    }
+}
+
 template <int DK, int DV>
 hipError_t launch_cmp_dims(const BwdArgs &A, hipStream_t s)
 {
@@ -698,6 +771,23 @@ hipError_t launch_bwd_rows_mfma(const BwdArgs &A, hipStream_t s)
     if (d.dk == 192) hipLaunchKernelGGL((k_bwd_rows_mfma<192, 128>), grid, dim3(kThreads), 0, s, A);
     else if (d.dk == 128) hipLaunchKernelGGL((k_bwd_rows_mfma<128, 128>), grid, dim3(kThreads), 0, s, A);
     else hipLaunchKernelGGL((k_bwd_rows_mfma<64, 64>), grid, dim3(kThreads), 0, s, A);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dw_mfma(const BwdArgs &A, bool isk, hipStream_t s)
+{
+    const Dims &d = A.d;
+    const int dim = isk ? d.dk : d.dv;
+    const float *G = A.kcv + (isk ? 0 : d.dk);
+    const uint16_t *x = (const uint16_t *)(isk ? A.k : A.v), *pe = (const uint16_t *)(isk ? A.pek : A.pev);
+    const float *cs = A.colsum + (isk ? 0 : d.dk);
+    float *out = isk ? A.dwck : A.dwcv;
+    const int rows = d.B * d.Hkv * d.ncmp;
+    const dim3 grid(dim / 64, 32 * dim / 64);
+    const int gs = d.dk + d.dv;
+    if (dim == 192) hipLaunchKernelGGL(k_bwd_dw_mfma<192>, grid, dim3(kThreads), 0, s, G, gs, x, pe, cs, out, d.T, d.ncmp, d.npad, rows);
+    else if (dim == 128) hipLaunchKernelGGL(k_bwd_dw_mfma<128>, grid, dim3(kThreads), 0, s, G, gs, x, pe, cs, out, d.T, d.ncmp, d.npad, rows);
+    else hipLaunchKernelGGL(k_bwd_dw_mfma<64>, grid, dim3(kThreads), 0, s, G, gs, x, pe, cs, out, d.T, d.ncmp, d.npad, rows);
     return hipGetLastError();
 }
 

@@ -127,6 +127,9 @@ void bwd_key_chunks(const Dims &d, int *rc, int *nkc, size_t *part_floats);
 hipError_t launch_bwd_keys_mfma(const BwdArgs &A, hipStream_t s);
 // compressed-key gradient partials (part) on the matrix cores, same shapes
 hipError_t launch_bwd_cmp_keys_mfma(const BwdArgs &A, hipStream_t s);
+// weight gradient of the K (isk) or V compression map on the matrix cores,
+// same shapes; needs kcv and colsum
+hipError_t launch_bwd_dw_mfma(const BwdArgs &A, bool isk, hipStream_t s);
 // the row pass (rs and dq) on the matrix cores, same shapes
 hipError_t launch_bwd_rows_mfma(const BwdArgs &A, hipStream_t s);
 
