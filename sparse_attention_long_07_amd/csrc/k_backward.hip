@@ -824,7 +824,9 @@ struct DxProblem {
 };
 
 // Gate gradients per chunk of kGateRows rows of one head: element e of
-// [3][dk+1] (column dk is the bias) sums dz_c * q (or dz_c).
+// [3][dk+1] (column dk is the bias) sums dz_c * q (or dz_c).  A thread owns
+// column x for all three branches (q read once) and keeps 8 rows' loads in
+// flight; rows are summed in order.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_bwd_gate_part(BwdArgs a)
 {
@@ -832,14 +834,30 @@ __global__ __launch_bounds__(kThreads) void k_bwd_gate_part(BwdArgs a)
     const int h = blockIdx.x, chunk = blockIdx.y;
     const int W1 = d.dk + 1;
     const long r0 = (long)chunk * kGateRows, r1 = min((long)d.B * d.T, r0 + kGateRows);
-    for (int e = threadIdx.x; e < 3 * W1; e += kThreads) {
-        const int c = e / W1, x = e % W1;
-        float s = 0.f;
-        for (long r = r0; r < r1; r++) {
-            const float dz = a.rs[(r * d.Hq + h) * kStat + c * 4 + 3];
-            s += dz * (x < d.dk ? to_f(((const T *)a.q)[(r * d.Hq + h) * d.dk + x]) : 1.f);
+    for (int x = threadIdx.x; x < W1; x += kThreads) {
+        float s0 = 0.f, s1 = 0.f, s2 = 0.f;
+        for (long rb = r0; rb < r1; rb += 8) {
+            float qv[8], z0[8], z1[8], z2[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                const long r = rb + u < r1 ? rb + u : r1 - 1;
+                const float *st = a.rs + (r * d.Hq + h) * kStat;
+                z0[u] = rb + u < r1 ? st[3] : 0.f;
+                z1[u] = rb + u < r1 ? st[7] : 0.f;
+                z2[u] = rb + u < r1 ? st[11] : 0.f;
+                qv[u] = x < d.dk ? to_f(((const T *)a.q)[(r * d.Hq + h) * d.dk + x]) : 1.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                s0 += z0[u] * qv[u];
+                s1 += z1[u] * qv[u];
+                s2 += z2[u] * qv[u];
+            }
         }
-        a.gpart[((long)h * a.ngc + chunk) * 3 * W1 + e] = s;
+        float *gp = a.gpart + ((long)h * a.ngc + chunk) * 3 * W1;
+        gp[x] = s0;
+        gp[W1 + x] = s1;
+        gp[2 * W1 + x] = s2;
     }
 }
 
