@@ -161,16 +161,29 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
             S[r] = f32x4{0.f, 0.f, 0.f, 0.f};
             P[r] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        // A fragments of step i + 1 are read while step i's products run
+        {
+            u32x4 an[kRows], cur[kRows];
 #pragma unroll
-        for (int i = 0; i < NQ; i++)
+            for (int r = 0; r < kRows; r++) an[r] = ld16(qt + (16 * r + li) * QS + 8 * lg);
 #pragma unroll
-            for (int r = 0; r < kRows; r++)
-                S[r] = mfma16(as_bf16x8(ld16(qt + (16 * r + li) * QS + 32 * i + 8 * lg)), as_bf16x8(kf[i]), S[r]);
+            for (int i = 0; i < NQ + NO; i++) {
 #pragma unroll
-        for (int i = 0; i < NO; i++)
+                for (int r = 0; r < kRows; r++) cur[r] = an[r];
+                if (i + 1 < NQ + NO) {
+                    const int j = i + 1;
 #pragma unroll
-            for (int r = 0; r < kRows; r++)
-                P[r] = mfma16(as_bf16x8(ld16(ot + (16 * r + li) * OS + 32 * i + 8 * lg)), as_bf16x8(vf[i]), P[r]);
+                    for (int r = 0; r < kRows; r++)
+                        an[r] = j < NQ ? ld16(qt + (16 * r + li) * QS + 32 * j + 8 * lg)
+                                       : ld16(ot + (16 * r + li) * OS + 32 * (j - NQ) + 8 * lg);
+                }
+#pragma unroll
+                for (int r = 0; r < kRows; r++) {
+                    if (i < NQ) S[r] = mfma16(as_bf16x8(cur[r]), as_bf16x8(kf[i]), S[r]);
+                    else P[r] = mfma16(as_bf16x8(cur[r]), as_bf16x8(vf[i - NQ]), P[r]);
+                }
+            }
+        }
         // p and ds of (head 4 lg + e of row r, key kk)
         float pg[kRows][4], ds[kRows][4];
 #pragma unroll
@@ -210,20 +223,33 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
         // columns 4 (li % 4) .. +3 of the column tile, and receives column li
         // of rows r0 .. r0 + 3
         const int trow = li >> 2, tcol = 4 * (li & 3);
+        // transposing reads in groups of 4 column tiles, issued before their products
 #pragma unroll
         for (int s2 = 0; s2 < 2; s2++) {
             const int r0 = 32 * s2 + 4 * lg + trow, r1 = r0 + 16;
 #pragma unroll
-            for (int dt = 0; dt < DV / 16; dt++) {
-                const uint2 lo = ld_tr16(ot + r0 * OS + 16 * dt + tcol);
-                const uint2 hi = ld_tr16(ot + r1 * OS + 16 * dt + tcol);
-                accv[dt] = mfma16(as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y}), bp[s2], accv[dt]);
+            for (int d0 = 0; d0 < DV / 16; d0 += 4) {
+                uint2 lo[4], hi[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    lo[u] = ld_tr16(ot + r0 * OS + 16 * (d0 + u) + tcol);
+                    hi[u] = ld_tr16(ot + r1 * OS + 16 * (d0 + u) + tcol);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    accv[d0 + u] = mfma16(as_bf16x8(u32x4{lo[u].x, lo[u].y, hi[u].x, hi[u].y}), bp[s2], accv[d0 + u]);
             }
 #pragma unroll
-            for (int dt = 0; dt < DK / 16; dt++) {
-                const uint2 lo = ld_tr16(qt + r0 * QS + 16 * dt + tcol);
-                const uint2 hi = ld_tr16(qt + r1 * QS + 16 * dt + tcol);
-                acck[dt] = mfma16(as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y}), bs[s2], acck[dt]);
+            for (int d0 = 0; d0 < DK / 16; d0 += 4) {
+                uint2 lo[4], hi[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    lo[u] = ld_tr16(qt + r0 * QS + 16 * (d0 + u) + tcol);
+                    hi[u] = ld_tr16(qt + r1 * QS + 16 * (d0 + u) + tcol);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    acck[d0 + u] = mfma16(as_bf16x8(u32x4{lo[u].x, lo[u].y, hi[u].x, hi[u].y}), bs[s2], acck[d0 + u]);
             }
         }
     };
