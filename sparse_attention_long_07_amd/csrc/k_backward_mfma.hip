@@ -426,13 +426,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     auto tile_scores = [&](const uint16_t *kr, long ks, const uint16_t *vr, long vs, f32x4 &S, f32x4 &P, u32x4 *kfr) {
         S = f32x4{0.f, 0.f, 0.f, 0.f};
         P = f32x4{0.f, 0.f, 0.f, 0.f};
+        // every read issued before the products that use them
+        u32x4 vfr[NO];
 #pragma unroll
-        for (int c = 0; c < NQ; c++) {
-            kfr[c] = ld16(kr + li * ks + 32 * c + 8 * lg);
-            S = mfma16(as_bf16x8(kfr[c]), as_bf16x8(qf[c]), S);
-        }
+        for (int c = 0; c < NQ; c++) kfr[c] = ld16(kr + li * ks + 32 * c + 8 * lg);
 #pragma unroll
-        for (int c = 0; c < NO; c++) P = mfma16(as_bf16x8(ld16(vr + li * vs + 32 * c + 8 * lg)), as_bf16x8(of[c]), P);
+        for (int c = 0; c < NO; c++) vfr[c] = ld16(vr + li * vs + 32 * c + 8 * lg);
+#pragma unroll
+        for (int c = 0; c < NQ; c++) S = mfma16(as_bf16x8(kfr[c]), as_bf16x8(qf[c]), S);
+#pragma unroll
+        for (int c = 0; c < NO; c++) P = mfma16(as_bf16x8(vfr[c]), as_bf16x8(of[c]), P);
     };
     // sweep-1 update over a 64-key chunk: sc, dp hold its scores (log2 units,
     // -inf where masked) and dP
@@ -499,10 +502,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const bf16x8 bs = as_bf16x8(y);
         const int r0 = 4 * lg + trow;
 #pragma unroll
-        for (int dt = 0; dt < DK / 16; dt++) {
-            const uint2 lo = ld_tr16(kb + r0 * KS + 16 * dt + tcol);
-            const uint2 hi = ld_tr16(kb + (r0 + 16) * KS + 16 * dt + tcol);
-            dqa[dt] = mfma16(as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y}), bs, dqa[dt]);
+        for (int d0 = 0; d0 < DK / 16; d0 += 4) {
+            uint2 lo[4], hi[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                lo[u] = ld_tr16(kb + r0 * KS + 16 * (d0 + u) + tcol);
+                hi[u] = ld_tr16(kb + (r0 + 16) * KS + 16 * (d0 + u) + tcol);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                dqa[d0 + u] = mfma16(as_bf16x8(u32x4{lo[u].x, lo[u].y, hi[u].x, hi[u].y}), bs, dqa[d0 + u]);
         }
     };
 
