@@ -75,7 +75,8 @@ typedef enum {
     NSA_OP_DECODE = 2,  /* nsa_decode_step */
     NSA_OP_SPARSE = 3,  /* nsa_sparse_attention */
     NSA_OP_BACKWARD = 4, /* nsa_backward */
-    NSA_OP_DSA_DECODE = 5 /* nsa_dsa_decode: B*T fp32 indexer scores */
+    NSA_OP_DSA_DECODE = 5, /* nsa_dsa_decode: B*T fp32 indexer scores */
+    NSA_OP_DSA_PREFILL = 6 /* nsa_dsa_prefill: B*T*T fp32 indexer scores */
 } nsa_op;
 
 /* Problem description.  Supported ranges (checked on every call):
@@ -287,6 +288,21 @@ nsa_status nsa_dsa_decode(const nsa_config *cfg, int32_t idx_heads, int32_t idx_
                           const int32_t *seq_lens, const void *q_idx, const void *w_idx, const void *k_idx,
                           const void *q, const void *k, const void *v, const int32_t *sel_in, int32_t *sel_out,
                           void *o, void *ws, size_t ws_bytes, void *stream);
+
+/* DSA-style attention for every position of B sequences of T tokens (the
+ * prefill form of nsa_dsa_decode: the same indexer, selector and attention,
+ * each position t a query whose candidates are the tokens s <= t of its own
+ * sequence; the DSA explainer (allinfo.ai.kr) has the selection made for each
+ * query position independently).  Layouts (bf16): q_idx [B][T][idx_heads]
+ * [idx_dim], w_idx [B][T][idx_heads], k_idx [B][T][idx_dim], q [B][T][Hq][d_k],
+ * k [B][H_kv][T][d_k], v [B][H_kv][T][d_v], o [B][T][Hq][d_v]; sel device
+ * int32 [B][T][topk] (ascending, -1 padded: position t has min(t + 1, topk)
+ * entries).  Shapes, sizes, sel_in and alignment as nsa_dsa_decode; ws holds
+ * nsa_workspace_bytes(cfg, NSA_OP_DSA_PREFILL) bytes (B*T*T fp32 scores)
+ * unless sel_in is given.  B*T*H_kv < 2^31. */
+nsa_status nsa_dsa_prefill(const nsa_config *cfg, int32_t idx_heads, int32_t idx_dim, int32_t topk, const void *q_idx,
+                           const void *w_idx, const void *k_idx, const void *q, const void *k, const void *v,
+                           const int32_t *sel_in, int32_t *sel_out, void *o, void *ws, size_t ws_bytes, void *stream);
 
 /* Static description of a status code. */
 const char *nsa_status_string(int status);

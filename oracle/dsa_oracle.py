@@ -88,3 +88,21 @@ def dsa_decode(q_idx, w_idx, k_idx, q, k, v, seq_lens, topk: int, G: int, scale:
             sel[b] = np.asarray(sel_in[b])
         o[b] = attend(q[b], k[b], v[b], sel[b], G, scale)
     return sel, o
+
+
+def dsa_prefill(q_idx, w_idx, k_idx, q, k, v, topk: int, G: int, scale: float, sel_in=None, rows=None):
+    """Every position t of B sequences as a query over its tokens s <= t.
+    q_idx [B, T, H_I, d_I], w_idx [B, T, H_I], k_idx [B, T, d_I], q [B, T, Hq,
+    d_k], k [B, Hkv, T, d_k], v [B, Hkv, T, d_v].  rows: (b, t) pairs to
+    compute (default all).  Returns {(b, t): (sel [topk], o [Hq, d_v])}."""
+    B, T = np.shape(q)[0], np.shape(q)[1]
+    rows = rows if rows is not None else [(b, t) for b in range(B) for t in range(T)]
+    out = {}
+    for b, t in rows:
+        if sel_in is None:
+            sel = select_topk(index_scores(q_idx[b][t], w_idx[b][t], k_idx[b], t + 1), topk)
+        else:
+            sel = np.asarray(sel_in[b][t])
+        out[(b, t)] = (sel, attend(q[b][t], k[b], v[b], sel, G, scale))
+    return out
+

@@ -1,10 +1,12 @@
-// DSA-style decode step (DSA explainer, allinfo.ai.kr, section "쉽게 이해하기"):
+// DSA-style decode step and prefill (DSA explainer, allinfo.ai.kr, section "쉽게 이해하기"):
 // a lightning indexer scores every cached token with a weighted sum of ReLU
 // dot products over several small heads that share one key per token; a
 // selector keeps the top-k positions (2,048 on the page) for the query; the
 // attention runs over the selected tokens only, its softmax denominator
-// summed over that set.  One selection per sequence serves every query head
-// and KV group.  bf16 storage, fp32 arithmetic.
+// summed over that set.  One selection per query serves every query head and
+// KV group.  bf16 storage, fp32 arithmetic.  A "row" is one query: a
+// sequence's last token (decode: cache b, length seq_lens[b]) or one position
+// of a prefill (row r = b T + t: cache b, length t + 1).
 //
 // k_dsa_index  I[s] = sum_j w_j relu(q_j . k_s) on the matrix cores (keys as
 //              M, indexer heads as N), the head sum by DPP row reductions
@@ -50,13 +52,14 @@ __global__ __launch_bounds__(kThreads) void k_dsa_index(const uint16_t *__restri
                                                         const uint16_t *__restrict__ w_idx,
                                                         const uint16_t *__restrict__ k_idx,
                                                         const int32_t *__restrict__ seq_lens, float *__restrict__ scores,
-                                                        int T, int HI, int DI)
+                                                        int T, int HI, int DI, int prefill)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const int b = blockIdx.y;
-    const int L = seq_len_of(seq_lens, b, T);
-    const int key0 = blockIdx.x * kThreads + wave * 64;
+    const int b = blockIdx.x;   // the row: a sequence (decode) or a position (prefill)
+    const int cb = prefill ? b / T : b;
+    const int L = prefill ? b % T + 1 : seq_len_of(seq_lens, b, T);
+    const int key0 = blockIdx.y * kThreads + wave * 64;
     if (key0 >= L) return;   // no barriers in this kernel
     const u32x4 z = {0u, 0u, 0u, 0u};
     u32x4 ka[4][NC], qb[NC];
@@ -66,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void k_dsa_index(const uint16_t *__restri
 #pragma unroll
         for (int c = 0; c < NC; c++) {
             const int e0 = 32 * c + 8 * lg;
-            ka[kt][c] = e0 < DI ? ld16(k_idx + ((long)b * T + sl) * DI + e0) : z;
+            ka[kt][c] = e0 < DI ? ld16(k_idx + ((long)cb * T + sl) * DI + e0) : z;
         }
     }
 #pragma unroll
@@ -126,7 +129,7 @@ __device__ __forceinline__ int block_exscan(int v, int *wsum, int *tot)
 
 __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(const float *__restrict__ scores,
                                                            const int32_t *__restrict__ seq_lens,
-                                                           int32_t *__restrict__ sel, int T, int topk)
+                                                           int32_t *__restrict__ sel, int T, int topk, int prefill)
 {
     constexpr int kWaves = kTopkThreads / 64;
     __shared__ int hist[4096];
@@ -135,7 +138,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(const float *__restri
     __shared__ uint32_t s_prefix;
     __shared__ int s_remain;
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int L = seq_len_of(seq_lens, b, T);
+    const int L = prefill ? b % T + 1 : seq_len_of(seq_lens, b, T);
     const float *sc = scores + (long)b * T;
     int32_t *out = sel + (long)b * topk;
     if (L <= topk) {
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_dsa_attn(const uint16_t *__
                                                              const uint16_t *__restrict__ k,
                                                              const uint16_t *__restrict__ v,
                                                              const int32_t *__restrict__ sel, uint16_t *__restrict__ o,
-                                                             int T, int Hkv, int topk, float scale)
+                                                             int T, int Hkv, int topk, float scale, int prefill)
 {
     constexpr int NQ = DK / 32, NO = DV / 16, VS = DV + 16;
     constexpr int kStage = 32 * VS;                       // bf16 per wave
@@ -266,8 +269,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_dsa_attn(const uint16_t *__
 #pragma unroll
     for (int c = 0; c < NQ; c++) qf[c] = ld16(q + qrow + 32 * c + 8 * lg);
     __syncthreads();
-    const uint16_t *K = k + (long)bg * T * DK;
-    const uint16_t *V = v + (long)bg * T * DV;
+    const long cbg = (long)(prefill ? b / T : b) * Hkv + g;   // the cache of this row
+    const uint16_t *K = k + cbg * T * DK;
+    const uint16_t *V = v + cbg * T * DV;
     uint16_t *vw = vst[wave];
     const float sl2 = scale * kLog2e;
     f32x4 acc[NO];
@@ -372,29 +376,32 @@ bool dsa_supported(const Dims &d)
 }
 
 hipError_t launch_dsa_select(const Dims &d, int HI, int DI, int topk, const int32_t *seq_lens, const void *q_idx,
-                             const void *w_idx, const void *k_idx, float *scores, int32_t *sel, hipStream_t s)
+                             const void *w_idx, const void *k_idx, float *scores, int32_t *sel, hipStream_t s,
+                             bool prefill)
 {
-    const dim3 grid((d.T + kThreads - 1) / kThreads, d.B);
+    const int rows = prefill ? d.B * d.T : d.B, pf = prefill ? 1 : 0;
+    const dim3 grid(rows, (d.T + kThreads - 1) / kThreads);
     const uint16_t *qi = (const uint16_t *)q_idx, *wi = (const uint16_t *)w_idx, *ki = (const uint16_t *)k_idx;
-    if (DI <= 32) hipLaunchKernelGGL(k_dsa_index<1>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI);
-    else if (DI <= 64) hipLaunchKernelGGL(k_dsa_index<2>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI);
-    else if (DI <= 128) hipLaunchKernelGGL(k_dsa_index<4>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI);
-    else hipLaunchKernelGGL(k_dsa_index<8>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI);
+    if (DI <= 32) hipLaunchKernelGGL(k_dsa_index<1>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI, pf);
+    else if (DI <= 64) hipLaunchKernelGGL(k_dsa_index<2>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI, pf);
+    else if (DI <= 128) hipLaunchKernelGGL(k_dsa_index<4>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI, pf);
+    else hipLaunchKernelGGL(k_dsa_index<8>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI, pf);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_dsa_topk, dim3(d.B), dim3(kTopkThreads), 0, s, scores, seq_lens, sel, d.T, topk);
+    hipLaunchKernelGGL(k_dsa_topk, dim3(rows), dim3(kTopkThreads), 0, s, scores, seq_lens, sel, d.T, topk, pf);
     return hipGetLastError();
 }
 
 hipError_t launch_dsa_attn(const Dims &d, int topk, const void *q, const void *k, const void *v, const int32_t *sel,
-                           void *o, hipStream_t s)
+                           void *o, hipStream_t s, bool prefill)
 {
-    const dim3 grid(d.B * d.Hkv), block(kAttnWaves * 64);
+    const int pf = prefill ? 1 : 0;
+    const dim3 grid((unsigned)((prefill ? (long)d.B * d.T : (long)d.B) * d.Hkv)), block(kAttnWaves * 64);
     const uint16_t *qq = (const uint16_t *)q, *kk = (const uint16_t *)k, *vv = (const uint16_t *)v;
     uint16_t *oo = (uint16_t *)o;
-    if (d.dk == 192) hipLaunchKernelGGL((k_dsa_attn<192, 128>), grid, block, 0, s, qq, kk, vv, sel, oo, d.T, d.Hkv, topk, d.scale);
-    else if (d.dk == 128) hipLaunchKernelGGL((k_dsa_attn<128, 128>), grid, block, 0, s, qq, kk, vv, sel, oo, d.T, d.Hkv, topk, d.scale);
-    else hipLaunchKernelGGL((k_dsa_attn<64, 64>), grid, block, 0, s, qq, kk, vv, sel, oo, d.T, d.Hkv, topk, d.scale);
+    if (d.dk == 192) hipLaunchKernelGGL((k_dsa_attn<192, 128>), grid, block, 0, s, qq, kk, vv, sel, oo, d.T, d.Hkv, topk, d.scale, pf);
+    else if (d.dk == 128) hipLaunchKernelGGL((k_dsa_attn<128, 128>), grid, block, 0, s, qq, kk, vv, sel, oo, d.T, d.Hkv, topk, d.scale, pf);
+    else hipLaunchKernelGGL((k_dsa_attn<64, 64>), grid, block, 0, s, qq, kk, vv, sel, oo, d.T, d.Hkv, topk, d.scale, pf);
     return hipGetLastError();
 }
 

@@ -139,6 +139,8 @@ size_t nsa_workspace_bytes(const nsa_config *cfg, int op)
         return backward_layout(d, nullptr, nullptr);
     case NSA_OP_DSA_DECODE:
         return align_up(sizeof(float) * (size_t)d.B * d.T);
+    case NSA_OP_DSA_PREFILL:
+        return align_up(sizeof(float) * (size_t)d.B * d.T * d.T);
     default:
         return 0;
     }
@@ -211,6 +213,32 @@ nsa_status nsa_dsa_decode(const nsa_config *cfg, int32_t idx_heads, int32_t idx_
         NSA_TRY(launch_dsa_select(d, idx_heads, idx_dim, topk, seq_lens, q_idx, w_idx, k_idx, (float *)ws, sel_out, s));
     }
     NSA_TRY(launch_dsa_attn(d, topk, q, k, v, sel_in ? sel_in : sel_out, o, s));
+    return NSA_OK;
+}
+
+nsa_status nsa_dsa_prefill(const nsa_config *cfg, int32_t idx_heads, int32_t idx_dim, int32_t topk, const void *q_idx,
+                           const void *w_idx, const void *k_idx, const void *q, const void *k, const void *v,
+                           const int32_t *sel_in, int32_t *sel_out, void *o, void *ws, size_t ws_bytes, void *stream)
+{
+    Dims d;
+    nsa_status st = check_config(cfg, &d);
+    if (st != NSA_OK) return st;
+    if (!dsa_supported(d) || (long)d.B * d.T * d.Hkv >= (1L << 31)) return NSA_ERR_SHAPE;
+    if (idx_heads < 1 || idx_heads > 16 || idx_dim < 8 || idx_dim > 256 || idx_dim % 8 || topk < 1 || topk > 8192)
+        return NSA_ERR_PARAM;
+    if (!q || !k || !v || !o) return NSA_ERR_NULL;
+    if (!sel_in && (!q_idx || !w_idx || !k_idx || !sel_out)) return NSA_ERR_NULL;
+    const void *ptrs[] = {q, k, v, o};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return NSA_ERR_ALIGN;
+    if (!sel_in && (!aligned16(q_idx) || !aligned16(k_idx))) return NSA_ERR_ALIGN;
+    if (!sel_in && (!ws || ws_bytes < nsa_workspace_bytes(cfg, NSA_OP_DSA_PREFILL))) return NSA_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    if (!sel_in) {
+        NSA_TRY(launch_dsa_select(d, idx_heads, idx_dim, topk, nullptr, q_idx, w_idx, k_idx, (float *)ws, sel_out, s,
+                                  true));
+    }
+    NSA_TRY(launch_dsa_attn(d, topk, q, k, v, sel_in ? sel_in : sel_out, o, s, true));
     return NSA_OK;
 }
 

@@ -145,10 +145,12 @@ hipError_t launch_cmp_attn_generic(const RowArgs &a, bool with_v, hipStream_t s)
 // DSA-style decode step: indexer scores + top-k selection, and attention over
 // the selected tokens (bf16, 16 heads per KV head, the MFMA (d_k, d_v) pairs)
 bool dsa_supported(const Dims &d);
+// (prefill: every position of the B sequences is a query row)
 hipError_t launch_dsa_select(const Dims &d, int HI, int DI, int topk, const int32_t *seq_lens, const void *q_idx,
-                             const void *w_idx, const void *k_idx, float *scores, int32_t *sel, hipStream_t s);
+                             const void *w_idx, const void *k_idx, float *scores, int32_t *sel, hipStream_t s,
+                             bool prefill = false);
 hipError_t launch_dsa_attn(const Dims &d, int topk, const void *q, const void *k, const void *v, const int32_t *sel,
-                           void *o, hipStream_t s);
+                           void *o, hipStream_t s, bool prefill = false);
 // second layer of the two-layer compression, in place: rows <- W2 relu(rows)
 hipError_t launch_compress_mlp2(const Dims &d, const void *W2k, const void *W2v, void *cmp_k, void *cmp_v,
                                 hipStream_t s);

@@ -17,14 +17,14 @@ from .config import BF16, FP32, NSAShape
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libnsa.so")
 
-OP_FORWARD, OP_SELECT, OP_DECODE, OP_SPARSE, OP_BACKWARD, OP_DSA_DECODE = 0, 1, 2, 3, 4, 5
+OP_FORWARD, OP_SELECT, OP_DECODE, OP_SPARSE, OP_BACKWARD, OP_DSA_DECODE, OP_DSA_PREFILL = 0, 1, 2, 3, 4, 5, 6
 STATUS = {0: "NSA_OK", -1: "NSA_ERR_NULL", -2: "NSA_ERR_SHAPE", -3: "NSA_ERR_DTYPE", -4: "NSA_ERR_PARAM",
           -5: "NSA_ERR_WORKSPACE", -6: "NSA_ERR_HIP", -7: "NSA_ERR_ALIGN"}
 
 EXPORTS = ("nsa_workspace_bytes", "nsa_compress_kv", "nsa_compress_kv_mlp", "nsa_compress_append", "nsa_compressed_attention",
            "nsa_select_topn",
            "nsa_sparse_attention", "nsa_pack_kv_blocks", "nsa_window_attention", "nsa_selected_attention", "nsa_select_blocks",
-           "nsa_forward", "nsa_decode_step", "nsa_backward", "nsa_dsa_decode", "nsa_status_string")
+           "nsa_forward", "nsa_decode_step", "nsa_backward", "nsa_dsa_decode", "nsa_dsa_prefill", "nsa_status_string")
 
 
 class NSAError(RuntimeError):
@@ -59,6 +59,9 @@ def lib() -> ctypes.CDLL:
         L.nsa_dsa_decode.restype = ctypes.c_int
         L.nsa_dsa_decode.argtypes = ([ctypes.POINTER(Config), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
                                      + [_vp] * 10 + [_vp, ctypes.c_size_t, _vp])
+        L.nsa_dsa_prefill.restype = ctypes.c_int
+        L.nsa_dsa_prefill.argtypes = ([ctypes.POINTER(Config), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+                                      + [_vp] * 9 + [_vp, ctypes.c_size_t, _vp])
         L.nsa_compress_kv_mlp.restype = ctypes.c_int
         L.nsa_compress_kv_mlp.argtypes = [ctypes.POINTER(Config)] + [_vp] * 11
         L.nsa_compress_append.restype = ctypes.c_int
@@ -407,6 +410,37 @@ def dsa_decode(s: NSAShape, idx_heads, idx_dim, topk, seq_lens, q_idx, w_idx, k_
                                                   _p(w_idx), _p(k_idx), _p(q), _p(k_cache), _p(v_cache),
                                                   _p(sel_in), _p(sel), _p(o), _p(ws),
                                                   0 if ws is None else ws.numel(), _stream()))
+    return (sel_in if sel_in is not None else sel), o
+
+
+def dsa_prefill(s: NSAShape, idx_heads, idx_dim, topk, q_idx, w_idx, k_idx, q, k, v, sel_in=None, sel=None, o=None,
+                ws=None):
+    """DSA-style attention for every position: indexer scores, top-k tokens
+    per position (skipped with sel_in) and attention over them.  Returns
+    (sel [B,T,topk] int32 or sel_in, o [B,T,Hq,dv])."""
+    dt = _dt(s)
+    dev = q.device
+    _req(q, "q", (s.B, s.T, s.Hq, s.dk), dt)
+    _req(k, "k", (s.B, s.Hkv, s.T, s.dk), dt)
+    _req(v, "v", (s.B, s.Hkv, s.T, s.dv), dt)
+    if sel_in is not None:
+        _req(sel_in, "sel_in", (s.B, s.T, topk), torch.int32)
+    else:
+        _req(q_idx, "q_idx", (s.B, s.T, idx_heads, idx_dim), dt)
+        _req(w_idx, "w_idx", (s.B, s.T, idx_heads), dt)
+        _req(k_idx, "k_idx", (s.B, s.T, idx_dim), dt)
+        if sel is None:
+            sel = torch.empty((s.B, s.T, topk), dtype=torch.int32, device=dev)
+        _req(sel, "sel", (s.B, s.T, topk), torch.int32)
+        if ws is None:
+            ws = workspace(s, OP_DSA_PREFILL, dev)
+    if o is None:
+        o = torch.empty((s.B, s.T, s.Hq, s.dv), dtype=dt, device=dev)
+    _req(o, "o", (s.B, s.T, s.Hq, s.dv), dt)
+    c = config(s)
+    _check("nsa_dsa_prefill", lib().nsa_dsa_prefill(ctypes.byref(c), idx_heads, idx_dim, topk, _p(q_idx), _p(w_idx),
+                                                    _p(k_idx), _p(q), _p(k), _p(v), _p(sel_in), _p(sel), _p(o),
+                                                    _p(ws), 0 if ws is None else ws.numel(), _stream()))
     return (sel_in if sel_in is not None else sel), o
 
 

@@ -84,6 +84,7 @@ def test_bad_config_rejected_everywhere(kw, code):
     assert L.nsa_decode_step(c, *f[:8], None, f[0], None, f[1], 1 << 40, None) == code
     assert L.nsa_backward(c, *([FAKE] * 22), FAKE, 1 << 40, None) == code
     assert L.nsa_dsa_decode(c, 4, 64, 16, *([FAKE] * 10), FAKE, 1 << 40, None) == code
+    assert L.nsa_dsa_prefill(c, 4, 64, 16, *([FAKE] * 9), FAKE, 1 << 40, None) == code
     assert L.nsa_sparse_attention(c, *f[:8], f[0], 1 << 40, None) == code
     assert L.nsa_window_attention(c, *f[:7], None) == code
     assert L.nsa_pack_kv_blocks(c, f[0], f[1], f[2], 1 << 40, None) == code
@@ -204,6 +205,22 @@ def test_dsa_decode_checks():
     # workspace
     assert L.nsa_dsa_decode(c, 4, 64, 16, FAKE, *f[:6], None, FAKE, FAKE, None, need, None) == WS
     assert L.nsa_dsa_decode(c, 4, 64, 16, FAKE, *f[:6], None, FAKE, FAKE, FAKE, need - 256, None) == WS
+
+
+def test_dsa_prefill_checks():
+    L = nsa.lib()
+    ok = cfg(group=16, d_k=128, d_v=128, dtype=1)
+    c = ctypes.byref(ok)
+    need = L.nsa_workspace_bytes(c, 6)
+    assert need >= 4 * ok.B * ok.T * ok.T
+    f = [FAKE] * 6     # q_idx w_idx k_idx q k v
+    assert L.nsa_dsa_prefill(ctypes.byref(cfg(group=4, d_k=128, d_v=128, dtype=1)), 4, 64, 16, *f, None, FAKE, FAKE,
+                             FAKE, need, None) == SHAPE
+    assert L.nsa_dsa_prefill(c, 4, 64, 0, *f, None, FAKE, FAKE, FAKE, need, None) == PARAM
+    assert L.nsa_dsa_prefill(c, 4, 64, 16, *f, None, None, FAKE, FAKE, need, None) == NULL
+    assert L.nsa_dsa_prefill(c, 4, 64, 16, *f, None, FAKE, FAKE, FAKE, need - 256, None) == WS
+    assert L.nsa_dsa_prefill(c, 4, 64, 16, FAKE, FAKE, FAKE, MIS, FAKE, FAKE, None, FAKE, FAKE, FAKE, need,
+                             None) == ALIGN
 
 
 def test_binding_rejects_host_tensors():

@@ -141,3 +141,52 @@ def test_dsa_decode_full_size_sampled():
     for b in range(4):
         ref = dsa.attend(q[b], k[b], v[b], ref_sel[b], s.G, 1 / math.sqrt(s.dk))
         assert np.abs(np64(o2[b]) - ref).max() <= out_tol(s, ref), b
+
+
+PREFILL = [
+    ("d192_T700_k128_B1H2", NSAShape(1, 700, 2, 16, 192, 128), 128, 4, 64),
+    ("d64_T300_k64_B2H1", NSAShape(2, 300, 1, 16, 64, 64), 64, 8, 32),
+]
+
+
+@pytest.mark.parametrize("name,s,topk,hi,di", PREFILL, ids=[c[0] for c in PREFILL])
+def test_dsa_prefill_parity(name, s, topk, hi, di):
+    """Every position a query: sampled positions' selections against the
+    oracle (as in the decode test), end to end where they agree, and the
+    attention of every sampled position with the oracle's selection
+    injected for all positions."""
+    say("dsa prefill", name, s, topk)
+    g = torch.Generator(device="cuda").manual_seed(91)
+    dt = torch.bfloat16
+    qi = (torch.randn((s.B, s.T, hi, di), generator=g, device="cuda") / math.sqrt(di)).to(dt)
+    wi = (torch.randn((s.B, s.T, hi), generator=g, device="cuda") / math.sqrt(hi)).to(dt)
+    ki = torch.randn((s.B, s.T, di), generator=g, device="cuda").to(dt)
+    q = torch.randn((s.B, s.T, s.Hq, s.dk), generator=g, device="cuda").to(dt)
+    k = torch.randn((s.B, s.Hkv, s.T, s.dk), generator=g, device="cuda").to(dt)
+    v = torch.randn((s.B, s.Hkv, s.T, s.dv), generator=g, device="cuda").to(dt)
+    sel, o = nsa.dsa_prefill(s, hi, di, topk, qi, wi, ki, q, k, v)
+    torch.cuda.synchronize()
+    sel = sel.cpu().numpy()
+    Q, K, V = np64(q), np64(k), np64(v)
+    QI, WI, KI = np64(qi), np64(wi), np64(ki)
+    scale = 1 / math.sqrt(s.dk)
+    rng = np.random.default_rng(92)
+    rows = sorted({(b, int(t)) for b in range(s.B) for t in
+                   list(rng.integers(0, s.T, 12)) + [0, topk - 1, topk, s.T - 1]})
+    n_same = 0
+    for b, t in rows:
+        sc = dsa.index_scores(QI[b, t], WI[b, t], KI[b], t + 1)
+        if _check_selection(sc, QI[b, t], WI[b, t], KI[b], t + 1, sel[b, t], topk, (name, b, t)):
+            n_same += 1
+            ref = dsa.attend(Q[b, t], K[b], V[b], sel[b, t], s.G, scale)
+            assert np.abs(np64(o[b, t]) - ref).max() <= out_tol(s, ref), (name, b, t)
+    assert n_same >= 1
+    # injected oracle selection for every position
+    ref_all = dsa.dsa_prefill(QI, WI, KI, Q, K, V, topk, s.G, scale)
+    sin = np.stack([np.stack([ref_all[(b, t)][0] for t in range(s.T)]) for b in range(s.B)]).astype(np.int32)
+    _, o2 = nsa.dsa_prefill(s, hi, di, topk, None, None, None, q, k, v, sel_in=torch.from_numpy(sin).cuda())
+    torch.cuda.synchronize()
+    O2 = np64(o2)
+    for b, t in rows:
+        ref = ref_all[(b, t)][1]
+        assert np.abs(O2[b, t] - ref).max() <= out_tol(s, ref), ("injected", name, b, t)

@@ -106,3 +106,24 @@ def test_golden_page_numbers():
     share = 100.0 * g["selected_tokens"] / g["context_tokens"]
     assert round(share, 1) == g["selected_share_percent"]                       # 1.5625% -> 1.6%
     assert g["context_tokens"] // g["selected_tokens"] == g["sparse_vs_full_ops_ratio"]   # 64x
+
+
+def test_prefill_rows_are_decode_steps_and_causal_below_k():
+    # position t of a prefill is the decode step at seq_len t + 1 on the same
+    # cache; positions with t + 1 <= k select everything: causal attention
+    rng = np.random.default_rng(6)
+    B, Hkv, G, T, dk, dv, HI, dI, k = 1, 2, 2, 50, 8, 8, 3, 8, 20
+    qi, wi, ki = rng.standard_normal((B, T, HI, dI)), rng.standard_normal((B, T, HI)), rng.standard_normal((B, T, dI))
+    q, kk, v = rng.standard_normal((B, T, Hkv * G, dk)), rng.standard_normal((B, Hkv, T, dk)), rng.standard_normal((B, Hkv, T, dv))
+    out = dsa.dsa_prefill(qi, wi, ki, q, kk, v, k, G, 0.3)
+    for t in (0, 7, 19, 20, 49):
+        sel_d, o_d = dsa.dsa_decode(qi[:, t], wi[:, t], ki, q[:, t], kk, v, [t + 1], k, G, 0.3)
+        assert np.array_equal(out[(0, t)][0], sel_d[0]) and np.allclose(out[(0, t)][1], o_d[0], rtol=0, atol=1e-14)
+    mask = torch.ones(T, T, dtype=torch.bool).tril()
+    for h in range(Hkv * G):
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q[0, :, h][None, None]),
+                                             torch.from_numpy(kk[0, h // G][None, None]),
+                                             torch.from_numpy(v[0, h // G][None, None]), attn_mask=mask[None, None],
+                                             scale=0.3)[0, 0].numpy()
+        for t in range(k):
+            np.testing.assert_allclose(out[(0, t)][1][h], ref[t], rtol=1e-12, atol=1e-12)
