@@ -16,6 +16,7 @@ roofline of the dominant kernel and the CPU oracle on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import math
 import hashlib
 import json
 import os
@@ -85,6 +86,43 @@ def dsa_decode(s, y, steps, topk=2048, hi=4, di=64):
                         "indexer 4 heads x 64, top-2048",
             "us_per_step": round(us, 2), "algorithmic_MB": round(nbytes / 1e6, 2),
             "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+
+
+def dsa_prefill(steps, topk=2048, hi=4, di=64):
+    """DSA-style attention for every position of T=16384 tokens (its own
+    top-2,048), timed apart from the headline step."""
+    s = WORKLOADS["bf16_fwdbwd_T16384"].shape
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(1007)
+    dt = torch.bfloat16
+    qi = (torch.randn((s.B, s.T, hi, di), generator=g, device=dev) / math.sqrt(di)).to(dt)
+    wi = (torch.randn((s.B, s.T, hi), generator=g, device=dev) / math.sqrt(hi)).to(dt)
+    ki = torch.randn((s.B, s.T, di), generator=g, device=dev).to(dt)
+    q = torch.randn((s.B, s.T, s.Hq, s.dk), generator=g, device=dev).to(dt)
+    k = torch.randn((s.B, s.Hkv, s.T, s.dk), generator=g, device=dev).to(dt)
+    v = torch.randn((s.B, s.Hkv, s.T, s.dv), generator=g, device=dev).to(dt)
+    sel = torch.empty((s.B, s.T, topk), dtype=torch.int32, device=dev)
+    o = torch.empty((s.B, s.T, s.Hq, s.dv), dtype=dt, device=dev)
+    ws = nsa.workspace(s, nsa.OP_DSA_PREFILL, dev)
+
+    def step():
+        nsa.dsa_prefill(s, hi, di, topk, qi, wi, ki, q, k, v, sel=sel, o=o, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    pairs = sum(min(t + 1, topk) for t in range(s.T)) * s.B
+    flops = s.B * s.T * (s.T + 1) // 2 * hi * di * 2 + pairs * s.Hq * (s.dk + s.dv) * 2
+    return {"workload": "DSA-style attention for every position, bf16 T=16384, 4 KV x 16 q heads, d_k=192, d_v=128; "
+                        "indexer 4 heads x 64, top-2048 per position",
+            "ms": round(ms, 3), "algorithmic_tflop": round(flops / 1e12, 4),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
 
 
 def mlp_compress(s, x, steps):
@@ -372,6 +410,7 @@ def main():
     }
     res["mlp_compress_T65536"] = mlp_compress(sp, x, args.steps)
     res["dsa_decode_B32_T65536"] = dsa_decode(sd, dec[0], args.steps)
+    res["dsa_prefill_T16384"] = None if args.no_backward else dsa_prefill(args.steps)
     res["fwd_bwd_T16384"] = None if args.no_backward else fwd_bwd(args.steps)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

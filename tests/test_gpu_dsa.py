@@ -190,3 +190,36 @@ def test_dsa_prefill_parity(name, s, topk, hi, di):
     for b, t in rows:
         ref = ref_all[(b, t)][1]
         assert np.abs(O2[b, t] - ref).max() <= out_tol(s, ref), ("injected", name, b, t)
+
+
+def test_dsa_prefill_full_size_sampled():
+    """T=16384, 4 KV heads x 16, d_k=192, d_v=128, top-2,048 with 4 indexer
+    heads of 64 (the fwd+bwd workload's shape): 12 positions' selections and
+    their attention (the oracle's selection injected at those positions)."""
+    s = WORKLOADS["bf16_fwdbwd_T16384"].shape
+    say("dsa prefill full size", s)
+    topk, hi, di = 2048, 4, 64
+    g = torch.Generator(device="cuda").manual_seed(93)
+    dt = torch.bfloat16
+    qi = (torch.randn((s.B, s.T, hi, di), generator=g, device="cuda") / math.sqrt(di)).to(dt)
+    wi = (torch.randn((s.B, s.T, hi), generator=g, device="cuda") / math.sqrt(hi)).to(dt)
+    ki = torch.randn((s.B, s.T, di), generator=g, device="cuda").to(dt)
+    q = torch.randn((s.B, s.T, s.Hq, s.dk), generator=g, device="cuda").to(dt)
+    k = torch.randn((s.B, s.Hkv, s.T, s.dk), generator=g, device="cuda").to(dt)
+    v = torch.randn((s.B, s.Hkv, s.T, s.dv), generator=g, device="cuda").to(dt)
+    sel, o = nsa.dsa_prefill(s, hi, di, topk, qi, wi, ki, q, k, v)
+    torch.cuda.synchronize()
+    QI, WI, KI = np64(qi), np64(wi), np64(ki)
+    rows = [0, 1, 2047, 2048, 5000, 9999, 12345, 16383] + list(np.random.default_rng(94).integers(0, s.T, 4))
+    sel_np = sel.cpu().numpy()
+    sin = sel.clone()
+    for t in rows:
+        sc = dsa.index_scores(QI[0, t], WI[0, t], KI[0], t + 1)
+        _check_selection(sc, QI[0, t], WI[0, t], KI[0], t + 1, sel_np[0, t], topk, ("full", t))
+        sin[0, t] = torch.from_numpy(dsa.select_topk(sc, topk).astype(np.int32)).cuda()
+    _, o2 = nsa.dsa_prefill(s, hi, di, topk, None, None, None, q, k, v, sel_in=sin)
+    torch.cuda.synchronize()
+    Kb, Vb = np64(k[0]), np64(v[0])
+    for t in rows:
+        ref = dsa.attend(np64(q[0, t]), Kb, Vb, sin[0, t].cpu().numpy(), s.G, 1 / math.sqrt(s.dk))
+        assert np.abs(np64(o2[0, t]) - ref).max() <= out_tol(s, ref), t
