@@ -300,7 +300,7 @@ def test_stage_parity(name, s, scaled):
     # the scores-only S2 (the block-selection call) computes the same scores bit for bit
     _, sc_only = nsa.compressed_attention(s, x["q"], torch.from_numpy(kc).to(dt).cuda())
     torch.cuda.synchronize()
-    causal_t = torch.from_numpy(np.ascontiguousarray(causal)).cuda()
+    causal_t = torch.from_numpy(np.array(causal, copy=True)).cuda()
     assert torch.equal(sc_only[causal_t], sc[causal_t])
     # S3 with the oracle's scores (stored in fp32)
     sref = torch.from_numpy(np.where(causal, ref["scores"], -np.inf).astype(np.float32)).cuda()
