@@ -282,8 +282,12 @@ nsa_status nsa_backward(const nsa_config *cfg, const void *q, const void *k, con
  * above: entries -1 or positions below seq_lens[b]; entries outside 0..T-1
  * count as -1) the indexer and selector are skipped and q_idx, w_idx, k_idx,
  * sel_out and ws may be NULL; otherwise sel_out receives the selection and
- * ws holds nsa_workspace_bytes(cfg, NSA_OP_DSA_DECODE) bytes.  q_idx, k_idx,
- * q, k, v, o 16-byte aligned. */
+ * ws holds nsa_workspace_bytes(cfg, NSA_OP_DSA_DECODE) bytes.  A 16-byte
+ * aligned ws of at least 4*B*H_kv*2*(32 + 16*d_v) bytes (always the case with
+ * sel_in == NULL once T >= H_kv*2*(32 + 16*d_v)) also serves the attention:
+ * each KV group's slots are then split over two workgroups and merged, which
+ * changes only the fp32 summation order.  q_idx, k_idx, q, k, v, o 16-byte
+ * aligned. */
 nsa_status nsa_dsa_decode(const nsa_config *cfg, int32_t idx_heads, int32_t idx_dim, int32_t topk,
                           const int32_t *seq_lens, const void *q_idx, const void *w_idx, const void *k_idx,
                           const void *q, const void *k, const void *v, const int32_t *sel_in, int32_t *sel_out,

@@ -22,7 +22,11 @@
 //              S^T = K Q^T on gathered K rows (16x16x32 MFMA, the 16 heads
 //              as N), online softmax, O^T += V^T P^T with V staged in a
 //              wave-private LDS buffer and read by transposing reads; the
-//              waves' (max, sum, O) are merged in LDS.
+//              waves' (max, sum, O) are merged in LDS.  With nsplit = 2 two
+//              workgroups on two CUs take the two halves of the slots and
+//              leave (max, sum, unnormalised O) per head in a workspace that
+//              k_dsa_merge combines (decode: 128 workgroups would otherwise
+//              leave half the chip idle).
 #include "mfma_util.h"
 #include "nsa_internal.h"
 
@@ -251,7 +255,8 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_dsa_attn(const uint16_t *__
                                                              const uint16_t *__restrict__ k,
                                                              const uint16_t *__restrict__ v,
                                                              const int32_t *__restrict__ sel, uint16_t *__restrict__ o,
-                                                             int T, int Hkv, int topk, float scale, int prefill)
+                                                             int T, int Hkv, int topk, float scale, int prefill,
+                                                             int nsplit, float *__restrict__ part)
 {
     constexpr int NQ = DK / 32, NO = DV / 16, VS = DV + 16;
     constexpr int kStage = 32 * VS;                       // bf16 per wave
@@ -261,7 +266,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_dsa_attn(const uint16_t *__
     __shared__ float s_m[kAttnWaves][16], s_l[kAttnWaves][16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const int bg = blockIdx.x, b = bg / Hkv, g = bg % Hkv;
+    const int bg = blockIdx.x / nsplit, half = blockIdx.x % nsplit, b = bg / Hkv, g = bg % Hkv;
     for (int i = tid; i < topk; i += kAttnWaves * 64) ss[i] = sel[(long)b * topk + i];
     // B operand Q^T: head li of the group, columns 32 c + 8 lg .. +7
     u32x4 qf[NQ];
@@ -278,8 +283,10 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_dsa_attn(const uint16_t *__
 #pragma unroll
     for (int i = 0; i < NO; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.f;
-    const int per = (topk + kAttnWaves - 1) / kAttnWaves;
-    const int beg = wave * per, end = min(topk, beg + per);
+    const int span = (topk + nsplit - 1) / nsplit;
+    const int h0 = half * span, h1 = min(topk, h0 + span);
+    const int per = (max(h1 - h0, 0) + kAttnWaves - 1) / kAttnWaves;
+    const int beg = h0 + wave * per, end = min(h1, beg + per);
     const int trow = li >> 2, tcol = 4 * (li & 3);
     for (int c0 = beg; c0 < end; c0 += 32) {
         float sc[2][4];
@@ -363,7 +370,34 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_dsa_attn(const uint16_t *__
             num = __builtin_fmaf(f, ((const float *)vst[w])[i], num);
             den = __builtin_fmaf(f, s_l[w][h], den);
         }
-        o[((long)b * Hkv * 16 + g * 16) * DV + i] = f2bf(den > 0.f ? num / den : 0.f);
+        if (nsplit == 1) {
+            o[((long)b * Hkv * 16 + g * 16) * DV + i] = f2bf(den > 0.f ? num / den : 0.f);
+        } else {
+            // [16 max][16 sum][16][DV] unnormalised O, per (group, half)
+            float *pw = part + (long)blockIdx.x * (32 + 16 * DV);
+            if (i % DV == 0) {
+                pw[h] = M;
+                pw[16 + h] = den;
+            }
+            pw[32 + i] = num;
+        }
+    }
+}
+
+// o = the two halves' (max, sum, O) combined, per (sequence, KV group)
+template <int DV>
+__global__ __launch_bounds__(kThreads) void k_dsa_merge(const float *__restrict__ part, uint16_t *__restrict__ o)
+{
+    const int bg = blockIdx.x;
+    const float *p0 = part + (long)(2 * bg) * (32 + 16 * DV), *p1 = p0 + (32 + 16 * DV);
+    {
+        const int i = blockIdx.y * kThreads + threadIdx.x, h = i / DV;   // grid.y = 16 DV / 256
+        const float m0 = p0[h], m1 = p1[h], M = fmaxf(m0, m1);
+        const float f0 = m0 == -INFINITY ? 0.f : fast_exp2(m0 - M);
+        const float f1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - M);
+        const float num = __builtin_fmaf(f1, p1[32 + i], f0 * p0[32 + i]);
+        const float den = __builtin_fmaf(f1, p1[16 + h], f0 * p0[16 + h]);
+        o[(long)bg * 16 * DV + i] = f2bf(den > 0.f ? num / den : 0.f);
     }
 }
 
@@ -392,16 +426,27 @@ hipError_t launch_dsa_select(const Dims &d, int HI, int DI, int topk, const int3
     return hipGetLastError();
 }
 
-hipError_t launch_dsa_attn(const Dims &d, int topk, const void *q, const void *k, const void *v, const int32_t *sel,
-                           void *o, hipStream_t s, bool prefill)
+size_t dsa_split_bytes(const Dims &d)
 {
-    const int pf = prefill ? 1 : 0;
-    const dim3 grid((unsigned)((prefill ? (long)d.B * d.T : (long)d.B) * d.Hkv)), block(kAttnWaves * 64);
+    return sizeof(float) * (size_t)d.B * d.Hkv * 2 * (32 + 16 * (size_t)d.dv);
+}
+
+hipError_t launch_dsa_attn(const Dims &d, int topk, const void *q, const void *k, const void *v, const int32_t *sel,
+                           void *o, hipStream_t s, bool prefill, void *part)
+{
+    const int pf = prefill ? 1 : 0, ns = part ? 2 : 1;
+    const long groups = (prefill ? (long)d.B * d.T : (long)d.B) * d.Hkv;
+    const dim3 grid((unsigned)(groups * ns)), block(kAttnWaves * 64);
     const uint16_t *qq = (const uint16_t *)q, *kk = (const uint16_t *)k, *vv = (const uint16_t *)v;
     uint16_t *oo = (uint16_t *)o;
-    if (d.dk == 192) hipLaunchKernelGGL((k_dsa_attn<192, 128>), grid, block, 0, s, qq, kk, vv, sel, oo, d.T, d.Hkv, topk, d.scale, pf);
-    else if (d.dk == 128) hipLaunchKernelGGL((k_dsa_attn<128, 128>), grid, block, 0, s, qq, kk, vv, sel, oo, d.T, d.Hkv, topk, d.scale, pf);
-    else hipLaunchKernelGGL((k_dsa_attn<64, 64>), grid, block, 0, s, qq, kk, vv, sel, oo, d.T, d.Hkv, topk, d.scale, pf);
+    float *pp = (float *)part;
+    if (d.dk == 192) hipLaunchKernelGGL((k_dsa_attn<192, 128>), grid, block, 0, s, qq, kk, vv, sel, oo, d.T, d.Hkv, topk, d.scale, pf, ns, pp);
+    else if (d.dk == 128) hipLaunchKernelGGL((k_dsa_attn<128, 128>), grid, block, 0, s, qq, kk, vv, sel, oo, d.T, d.Hkv, topk, d.scale, pf, ns, pp);
+    else hipLaunchKernelGGL((k_dsa_attn<64, 64>), grid, block, 0, s, qq, kk, vv, sel, oo, d.T, d.Hkv, topk, d.scale, pf, ns, pp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || ns == 1) return e;
+    if (d.dv == 128) hipLaunchKernelGGL(k_dsa_merge<128>, dim3((unsigned)groups, 16 * 128 / kThreads), dim3(kThreads), 0, s, pp, oo);
+    else hipLaunchKernelGGL(k_dsa_merge<64>, dim3((unsigned)groups, 16 * 64 / kThreads), dim3(kThreads), 0, s, pp, oo);
     return hipGetLastError();
 }
 

@@ -212,7 +212,10 @@ nsa_status nsa_dsa_decode(const nsa_config *cfg, int32_t idx_heads, int32_t idx_
     if (!sel_in) {
         NSA_TRY(launch_dsa_select(d, idx_heads, idx_dim, topk, seq_lens, q_idx, w_idx, k_idx, (float *)ws, sel_out, s));
     }
-    NSA_TRY(launch_dsa_attn(d, topk, q, k, v, sel_in ? sel_in : sel_out, o, s));
+    // a workspace that holds the partial results (the scores are consumed by
+    // then, on the same stream) lets two workgroups share each KV group
+    void *part = ws && aligned16(ws) && ws_bytes >= dsa_split_bytes(d) ? ws : nullptr;
+    NSA_TRY(launch_dsa_attn(d, topk, q, k, v, sel_in ? sel_in : sel_out, o, s, false, part));
     return NSA_OK;
 }
 

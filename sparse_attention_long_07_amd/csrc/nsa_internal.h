@@ -150,7 +150,9 @@ hipError_t launch_dsa_select(const Dims &d, int HI, int DI, int topk, const int3
                              const void *w_idx, const void *k_idx, float *scores, int32_t *sel, hipStream_t s,
                              bool prefill = false);
 hipError_t launch_dsa_attn(const Dims &d, int topk, const void *q, const void *k, const void *v, const int32_t *sel,
-                           void *o, hipStream_t s, bool prefill = false);
+                           void *o, hipStream_t s, bool prefill = false, void *part = nullptr);
+// bytes of the partial results a two-way slot split of the decode attention needs
+size_t dsa_split_bytes(const Dims &d);
 // second layer of the two-layer compression, in place: rows <- W2 relu(rows)
 hipError_t launch_compress_mlp2(const Dims &d, const void *W2k, const void *W2v, void *cmp_k, void *cmp_v,
                                 hipStream_t s);

@@ -101,18 +101,27 @@ def test_dsa_decode_parity(name, s, lens, topk, hi, di):
     assert n_same >= 1, name
 
 
+def _split_ws(s):
+    """A workspace that holds the two-way split's partial results: per (sequence,
+    KV group, half) 16 maxima, 16 sums and 16 x d_v outputs in fp32."""
+    return torch.empty(4 * s.B * s.Hkv * 2 * (32 + 16 * s.dv), dtype=torch.uint8, device="cuda")
+
+
+@pytest.mark.parametrize("split", [False, True], ids=["one_wg", "split2"])
 @pytest.mark.parametrize("name,s,lens,topk,hi,di", CASES, ids=[c[0] for c in CASES])
-def test_dsa_attention_with_injected_selection(name, s, lens, topk, hi, di):
+def test_dsa_attention_with_injected_selection(name, s, lens, topk, hi, di, split):
     """The oracle's selection injected: attention parity independent of
-    selection near-ties."""
-    say("dsa attention", name, s, lens, topk)
+    selection near-ties; with a workspace each KV group's slots run as two
+    halves merged afterwards."""
+    say("dsa attention", name, s, lens, topk, "split" if split else "")
     x = make_decode(s, 83, "cuda", seq_lens=lens)
     ix = make_dsa_indexer(s, 84, "cuda", hi, di)
     qi, wi, ki = np64(ix["q_idx"]), np64(ix["w_idx"]), np64(ix["k_idx"])
     ref_sel, ref_o = dsa.dsa_decode(qi, wi, ki, np64(x["q"]), np64(x["k"]), np64(x["v"]),
                                     [_clamp_len(L, s.T) for L in lens], topk, s.G, 1 / math.sqrt(s.dk))
     sel_in = torch.from_numpy(ref_sel.astype(np.int32)).cuda()
-    _, o = nsa.dsa_decode(s, hi, di, topk, x["seq_lens"], None, None, None, x["q"], x["k"], x["v"], sel_in=sel_in)
+    _, o = nsa.dsa_decode(s, hi, di, topk, x["seq_lens"], None, None, None, x["q"], x["k"], x["v"], sel_in=sel_in,
+                          ws=_split_ws(s) if split else None)
     torch.cuda.synchronize()
     got = np64(o)
     assert np.all(np.isfinite(got))
@@ -135,7 +144,8 @@ def test_dsa_decode_full_size_sampled():
     sel_in = torch.full((s.B, 2048), -1, dtype=torch.int32, device="cuda")
     sel_in[:4] = torch.from_numpy(ref_sel.astype(np.int32)).cuda()
     sel_in[4:] = torch.from_numpy(sel[4:]).cuda()
-    _, o2 = nsa.dsa_decode(s, 4, 64, 2048, x["seq_lens"], None, None, None, x["q"], x["k"], x["v"], sel_in=sel_in)
+    _, o2 = nsa.dsa_decode(s, 4, 64, 2048, x["seq_lens"], None, None, None, x["q"], x["k"], x["v"], sel_in=sel_in,
+                           ws=_split_ws(s))
     torch.cuda.synchronize()
     q, k, v = np64(x["q"][:4]), np64(x["k"][:4]), np64(x["v"][:4])
     for b in range(4):
