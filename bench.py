@@ -203,6 +203,51 @@ def fwd_bwd(steps):
             "bwd_mfma_frac": round(bf / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+def small_prefill(wname, steps):
+    """Throughput of a smaller prefill workload end to end (compression, the
+    three branches, selection, gates), timed apart from the headline step."""
+    w = WORKLOADS[wname]
+    s = w.shape
+    dev = torch.device("cuda:0")
+    x = make_prefill(s, 1000, dev, unit_scaled=w.unit_scaled)
+    ws = nsa.workspace(s, nsa.OP_FORWARD, dev)
+    dt = torch.float32 if s.dtype == "fp32" else torch.bfloat16
+    ck = torch.empty((s.B, s.Hkv, s.n_pad, s.dk), dtype=dt, device=dev)
+    cv = torch.empty((s.B, s.Hkv, s.n_pad, s.dv), dtype=dt, device=dev)
+    o = torch.empty((s.B, s.T, s.Hq, s.dv), dtype=dt, device=dev)
+
+    def step():
+        nsa.compress_kv(s, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"], ck, cv)
+        nsa.forward(s, x["q"], x["k"], x["v"], ck, cv, x["w_g"], x["b_g"], o=o, ws=ws)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(steps, 20)
+    e0.record()
+    for _ in range(n):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    fl = prefill_flops(s)["total"]
+    return {"workload": w.description, "dtype": s.dtype, "ms": round(ms, 4),
+            "tokens_per_s": round(s.B * s.T / (ms * 1e-3), 1), "algorithmic_gflop": round(fl / 1e9, 3),
+            "tflops": round(fl / (ms * 1e-3) / 1e12, 3)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -231,6 +276,7 @@ def cpu_baseline(s, x, flops_total, rows_sample=10240, seed=5):
     est = t_cmp + t_rows * s.T / rows_sample
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": flops_total / est / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": "compression of all %d tokens (%.1f s) + %d uniformly drawn query positions x %d KV groups "
                       "(%.1f s), extrapolated to all %d positions: %.0f s for the step"
                       % (s.T, t_cmp, rows_sample, s.Hkv, t_rows, s.T, est),
@@ -408,6 +454,8 @@ def main():
         "roofline": roof,
         "kernels": kernels,
     }
+    res["prefill_fp32_T1024"] = small_prefill("fp32_T1024", args.steps)
+    res["prefill_bf16_T8192"] = small_prefill("bf16_T8192", args.steps)
     res["mlp_compress_T65536"] = mlp_compress(sp, x, args.steps)
     res["dsa_decode_B32_T65536"] = dsa_decode(sd, dec[0], args.steps)
     res["dsa_prefill_T16384"] = None if args.no_backward else dsa_prefill(args.steps)

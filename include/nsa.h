@@ -75,8 +75,8 @@ typedef enum {
     NSA_OP_DECODE = 2,  /* nsa_decode_step */
     NSA_OP_SPARSE = 3,  /* nsa_sparse_attention */
     NSA_OP_BACKWARD = 4, /* nsa_backward */
-    NSA_OP_DSA_DECODE = 5, /* nsa_dsa_decode: B*T fp32 indexer scores */
-    NSA_OP_DSA_PREFILL = 6 /* nsa_dsa_prefill: B*T*T fp32 indexer scores */
+    NSA_OP_DSA_DECODE = 5, /* nsa_dsa_decode: B*T fp32 indexer scores, then the split attention's partials */
+    NSA_OP_DSA_PREFILL = 6 /* nsa_dsa_prefill: the indexer scores of one chunk of rows (<= 256 MiB) */
 } nsa_op;
 
 /* Problem description.  Supported ranges (checked on every call):
@@ -208,17 +208,28 @@ nsa_status nsa_selected_attention(const nsa_config *cfg, const void *q, const vo
                                   const int32_t *idx, const void *w_g, const void *b_g, void *o, void *ws,
                                   size_t ws_bytes, void *stream);
 
-/* S2 (scores only) followed by S3.  scores_out may be NULL (the workspace
- * holds them then); idx_out is required. */
+/* Block selection alone: S2 (scores only) followed by S3, i.e. the
+ * importance of each selection block derived from the compressed branch's
+ * attention (deepdaiv newsletter, token selection paragraph) and the top-n
+ * blocks with the initial and the 2 local blocks always kept (valuable12.com
+ * section II).  Definitions, layouts and the scores written as for
+ * nsa_compressed_attention and nsa_select_topn.  scores_out may be NULL (the
+ * workspace holds them then); idx_out is required.  ws:
+ * nsa_workspace_bytes(cfg, NSA_OP_SELECT) bytes, 256-byte aligned. */
 nsa_status nsa_select_blocks(const nsa_config *cfg, const void *q, const void *cmp_k, float *scores_out,
                              int32_t *idx_out, void *ws, size_t ws_bytes, void *stream);
 
-/* Full NSA forward for every position of every sequence: S2, S3 (unless
- * idx_in is given), S4.  idx_in: if non-NULL, these block lists
+/* Full NSA forward for every position of every sequence: the three branches
+ * over the same queries combined by per-head gates (deepdaiv newsletter,
+ * paragraphs on token compression, token selection and the sliding window;
+ * valuable12.com section II for l=32, d=16, l'=64, n=16, w=512), i.e. S2, S3
+ * (unless idx_in is given), S4 as defined above.  idx_in: if non-NULL, these block lists
  * ([B][Hkv][T][n]) replace the selection.  idx_out / scores_out: optional
  * copies of the indices used / the scores (scores exist only when
  * selecting).  cmp_k/cmp_v as written by nsa_compress_kv.  The workspace
- * holds o_cmp and, when not supplied by the caller, scores and indices. */
+ * (nsa_workspace_bytes(cfg, NSA_OP_FORWARD) bytes, 256-byte aligned) holds
+ * o_cmp, the repacked K/V blocks and, when not supplied by the caller, scores
+ * and indices. */
 nsa_status nsa_forward(const nsa_config *cfg, const void *q, const void *k, const void *v, const void *cmp_k,
                        const void *cmp_v, const void *w_g, const void *b_g, const int32_t *idx_in, void *o,
                        int32_t *idx_out, float *scores_out, void *ws, size_t ws_bytes, void *stream);
@@ -282,12 +293,13 @@ nsa_status nsa_backward(const nsa_config *cfg, const void *q, const void *k, con
  * above: entries -1 or positions below seq_lens[b]; entries outside 0..T-1
  * count as -1) the indexer and selector are skipped and q_idx, w_idx, k_idx,
  * sel_out and ws may be NULL; otherwise sel_out receives the selection and
- * ws holds nsa_workspace_bytes(cfg, NSA_OP_DSA_DECODE) bytes.  A 16-byte
- * aligned ws of at least 4*B*H_kv*2*(32 + 16*d_v) bytes (always the case with
- * sel_in == NULL once T >= H_kv*2*(32 + 16*d_v)) also serves the attention:
- * each KV group's slots are then split over two workgroups and merged, which
- * changes only the fp32 summation order.  q_idx, k_idx, q, k, v, o 16-byte
- * aligned. */
+ * ws holds nsa_workspace_bytes(cfg, NSA_OP_DSA_DECODE) bytes.  A non-NULL ws
+ * must be 256-byte aligned (else NSA_ERR_ALIGN).  A ws of at least
+ * 4*B*H_kv*2*(32 + 16*d_v) bytes (always the case with the size
+ * nsa_workspace_bytes reports) also serves the attention: each KV group's
+ * slots are then split over two workgroups and merged, which changes only the
+ * fp32 summation order; with sel_in and a NULL or smaller ws one workgroup
+ * takes each KV group.  q_idx, k_idx, q, k, v, o 16-byte aligned. */
 nsa_status nsa_dsa_decode(const nsa_config *cfg, int32_t idx_heads, int32_t idx_dim, int32_t topk,
                           const int32_t *seq_lens, const void *q_idx, const void *w_idx, const void *k_idx,
                           const void *q, const void *k, const void *v, const int32_t *sel_in, int32_t *sel_out,
@@ -302,8 +314,11 @@ nsa_status nsa_dsa_decode(const nsa_config *cfg, int32_t idx_heads, int32_t idx_
  * k [B][H_kv][T][d_k], v [B][H_kv][T][d_v], o [B][T][Hq][d_v]; sel device
  * int32 [B][T][topk] (ascending, -1 padded: position t has min(t + 1, topk)
  * entries).  Shapes, sizes, sel_in and alignment as nsa_dsa_decode; ws holds
- * nsa_workspace_bytes(cfg, NSA_OP_DSA_PREFILL) bytes (B*T*T fp32 scores)
- * unless sel_in is given.  B*T*H_kv < 2^31. */
+ * nsa_workspace_bytes(cfg, NSA_OP_DSA_PREFILL) bytes unless sel_in is given:
+ * the indexer and selector run over the B*T rows in chunks of
+ * min(B*T, floor(2^28 / (4*T))) rows, one chunk's fp32 scores at a time, so
+ * the workspace stays within 256 MiB whatever B and T are; the result does
+ * not depend on the chunking.  B*T*H_kv < 2^31. */
 nsa_status nsa_dsa_prefill(const nsa_config *cfg, int32_t idx_heads, int32_t idx_dim, int32_t topk, const void *q_idx,
                            const void *w_idx, const void *k_idx, const void *q, const void *k, const void *v,
                            const int32_t *sel_in, int32_t *sel_out, void *o, void *ws, size_t ws_bytes, void *stream);

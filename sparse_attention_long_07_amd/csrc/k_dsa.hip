@@ -27,6 +27,8 @@
 //              leave (max, sum, unnormalised O) per head in a workspace that
 //              k_dsa_merge combines (decode: 128 workgroups would otherwise
 //              leave half the chip idle).
+#include <algorithm>
+
 #include "mfma_util.h"
 #include "nsa_internal.h"
 
@@ -56,11 +58,12 @@ __global__ __launch_bounds__(kThreads) void k_dsa_index(const uint16_t *__restri
                                                         const uint16_t *__restrict__ w_idx,
                                                         const uint16_t *__restrict__ k_idx,
                                                         const int32_t *__restrict__ seq_lens, float *__restrict__ scores,
-                                                        int T, int HI, int DI, int prefill)
+                                                        int T, int HI, int DI, int prefill, int row0)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const int b = blockIdx.x;   // the row: a sequence (decode) or a position (prefill)
+    const int b = row0 + blockIdx.x;   // the row: a sequence (decode) or a position (prefill)
+    float *srow = scores + (long)blockIdx.x * T;   // the scores of this launch's rows
     const int cb = prefill ? b / T : b;
     const int L = prefill ? b % T + 1 : seq_len_of(seq_lens, b, T);
     const int key0 = blockIdx.y * kThreads + wave * 64;
@@ -94,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void k_dsa_index(const uint16_t *__restri
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int s = key0 + 16 * kt + 4 * lg + e;
-                if (s < L) scores[(long)b * T + s] = v[e];
+                if (s < L) srow[s] = v[e];
             }
         }
     }
@@ -133,7 +136,8 @@ __device__ __forceinline__ int block_exscan(int v, int *wsum, int *tot)
 
 __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(const float *__restrict__ scores,
                                                            const int32_t *__restrict__ seq_lens,
-                                                           int32_t *__restrict__ sel, int T, int topk, int prefill)
+                                                           int32_t *__restrict__ sel, int T, int topk, int prefill,
+                                                           int row0)
 {
     constexpr int kWaves = kTopkThreads / 64;
     __shared__ int hist[4096];
@@ -141,9 +145,9 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(const float *__restri
     __shared__ int wgt[kWaves], weq[kWaves];
     __shared__ uint32_t s_prefix;
     __shared__ int s_remain;
-    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = row0 + blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int L = prefill ? b % T + 1 : seq_len_of(seq_lens, b, T);
-    const float *sc = scores + (long)b * T;
+    const float *sc = scores + (long)blockIdx.x * T;
     int32_t *out = sel + (long)b * topk;
     if (L <= topk) {
         for (int i = tid; i < topk; i += kTopkThreads) out[i] = i < L ? i : -1;
@@ -411,19 +415,27 @@ bool dsa_supported(const Dims &d)
 
 hipError_t launch_dsa_select(const Dims &d, int HI, int DI, int topk, const int32_t *seq_lens, const void *q_idx,
                              const void *w_idx, const void *k_idx, float *scores, int32_t *sel, hipStream_t s,
-                             bool prefill)
+                             bool prefill, int row0, int rows)
 {
-    const int rows = prefill ? d.B * d.T : d.B, pf = prefill ? 1 : 0;
+    const int pf = prefill ? 1 : 0;
+    if (rows < 0) rows = prefill ? d.B * d.T : d.B;
     const dim3 grid(rows, (d.T + kThreads - 1) / kThreads);
     const uint16_t *qi = (const uint16_t *)q_idx, *wi = (const uint16_t *)w_idx, *ki = (const uint16_t *)k_idx;
-    if (DI <= 32) hipLaunchKernelGGL(k_dsa_index<1>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI, pf);
-    else if (DI <= 64) hipLaunchKernelGGL(k_dsa_index<2>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI, pf);
-    else if (DI <= 128) hipLaunchKernelGGL(k_dsa_index<4>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI, pf);
-    else hipLaunchKernelGGL(k_dsa_index<8>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI, pf);
+    if (DI <= 32) hipLaunchKernelGGL(k_dsa_index<1>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI, pf, row0);
+    else if (DI <= 64) hipLaunchKernelGGL(k_dsa_index<2>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI, pf, row0);
+    else if (DI <= 128) hipLaunchKernelGGL(k_dsa_index<4>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI, pf, row0);
+    else hipLaunchKernelGGL(k_dsa_index<8>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI, pf, row0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_dsa_topk, dim3(rows), dim3(kTopkThreads), 0, s, scores, seq_lens, sel, d.T, topk, pf);
+    hipLaunchKernelGGL(k_dsa_topk, dim3(rows), dim3(kTopkThreads), 0, s, scores, seq_lens, sel, d.T, topk, pf, row0);
     return hipGetLastError();
+}
+
+int dsa_prefill_chunk_rows(const Dims &d)
+{
+    const long total = (long)d.B * d.T;
+    const long fit = (long)(kDsaScoreBudget / (sizeof(float) * (size_t)d.T));
+    return (int)std::max(1L, std::min(total, fit));
 }
 
 size_t dsa_split_bytes(const Dims &d)

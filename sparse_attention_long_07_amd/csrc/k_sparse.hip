@@ -413,6 +413,9 @@ __global__ __launch_bounds__(kThreads) void k_selected_mfma(RowArgs a, const uin
     }
     const uint64_t valid = __ballot(ok);
     if (ok) blist[wave][__popcll(valid & __lanemask_lt())] = jb;
+    // other lanes of this wavefront read the list: the stores are in LDS first
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
     const int nitems = 2 * __popcll(valid);   // half blocks of 32 keys
 
     const uint16_t *kpg = kpk + (long)bg * d.nb * kTile * DK;

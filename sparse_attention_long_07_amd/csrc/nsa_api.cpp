@@ -138,9 +138,11 @@ size_t nsa_workspace_bytes(const nsa_config *cfg, int op)
     case NSA_OP_BACKWARD:
         return backward_layout(d, nullptr, nullptr);
     case NSA_OP_DSA_DECODE:
-        return align_up(sizeof(float) * (size_t)d.B * d.T);
+        // the indexer scores, later reused for the two-way split's partials
+        return dsa_supported(d) ? align_up(std::max(sizeof(float) * (size_t)d.B * d.T, dsa_split_bytes(d))) : 0;
     case NSA_OP_DSA_PREFILL:
-        return align_up(sizeof(float) * (size_t)d.B * d.T * d.T);
+        // the indexer scores of one chunk of rows
+        return dsa_supported(d) ? align_up(sizeof(float) * (size_t)dsa_prefill_chunk_rows(d) * d.T) : 0;
     default:
         return 0;
     }
@@ -208,13 +210,14 @@ nsa_status nsa_dsa_decode(const nsa_config *cfg, int32_t idx_heads, int32_t idx_
         if (!aligned16(p)) return NSA_ERR_ALIGN;
     if (!sel_in && (!aligned16(q_idx) || !aligned16(k_idx))) return NSA_ERR_ALIGN;
     if (!sel_in && (!ws || ws_bytes < nsa_workspace_bytes(cfg, NSA_OP_DSA_DECODE))) return NSA_ERR_WORKSPACE;
+    if (ws && (uintptr_t)ws % kAlign) return NSA_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
     if (!sel_in) {
         NSA_TRY(launch_dsa_select(d, idx_heads, idx_dim, topk, seq_lens, q_idx, w_idx, k_idx, (float *)ws, sel_out, s));
     }
     // a workspace that holds the partial results (the scores are consumed by
     // then, on the same stream) lets two workgroups share each KV group
-    void *part = ws && aligned16(ws) && ws_bytes >= dsa_split_bytes(d) ? ws : nullptr;
+    void *part = ws && ws_bytes >= dsa_split_bytes(d) ? ws : nullptr;
     NSA_TRY(launch_dsa_attn(d, topk, q, k, v, sel_in ? sel_in : sel_out, o, s, false, part));
     return NSA_OK;
 }
@@ -236,10 +239,14 @@ nsa_status nsa_dsa_prefill(const nsa_config *cfg, int32_t idx_heads, int32_t idx
         if (!aligned16(p)) return NSA_ERR_ALIGN;
     if (!sel_in && (!aligned16(q_idx) || !aligned16(k_idx))) return NSA_ERR_ALIGN;
     if (!sel_in && (!ws || ws_bytes < nsa_workspace_bytes(cfg, NSA_OP_DSA_PREFILL))) return NSA_ERR_WORKSPACE;
+    if (ws && (uintptr_t)ws % kAlign) return NSA_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
     if (!sel_in) {
-        NSA_TRY(launch_dsa_select(d, idx_heads, idx_dim, topk, nullptr, q_idx, w_idx, k_idx, (float *)ws, sel_out, s,
-                                  true));
+        // the rows in chunks whose scores fit the workspace, in order on the stream
+        const int total = d.B * d.T, chunk = dsa_prefill_chunk_rows(d);
+        for (int r0 = 0; r0 < total; r0 += chunk)
+            NSA_TRY(launch_dsa_select(d, idx_heads, idx_dim, topk, nullptr, q_idx, w_idx, k_idx, (float *)ws, sel_out,
+                                      s, true, r0, std::min(chunk, total - r0)));
     }
     NSA_TRY(launch_dsa_attn(d, topk, q, k, v, sel_in ? sel_in : sel_out, o, s, true));
     return NSA_OK;

@@ -146,9 +146,15 @@ hipError_t launch_cmp_attn_generic(const RowArgs &a, bool with_v, hipStream_t s)
 // the selected tokens (bf16, 16 heads per KV head, the MFMA (d_k, d_v) pairs)
 bool dsa_supported(const Dims &d);
 // (prefill: every position of the B sequences is a query row)
+// Indexer scores and top-k selection of rows row0 .. row0+rows-1 (rows < 0:
+// every row); scores holds the rows' T fp32 scores each, in launch order.
 hipError_t launch_dsa_select(const Dims &d, int HI, int DI, int topk, const int32_t *seq_lens, const void *q_idx,
                              const void *w_idx, const void *k_idx, float *scores, int32_t *sel, hipStream_t s,
-                             bool prefill = false);
+                             bool prefill = false, int row0 = 0, int rows = -1);
+// The prefill's indexer scores are held for this many bytes' worth of rows
+// at a time (the last chunk may be shorter).
+constexpr size_t kDsaScoreBudget = 256u << 20;
+int dsa_prefill_chunk_rows(const Dims &d);
 hipError_t launch_dsa_attn(const Dims &d, int topk, const void *q, const void *k, const void *v, const int32_t *sel,
                            void *o, hipStream_t s, bool prefill = false, void *part = nullptr);
 // bytes of the partial results a two-way slot split of the decode attention needs

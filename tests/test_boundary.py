@@ -89,6 +89,8 @@ def test_bad_config_rejected_everywhere(kw, code):
     assert L.nsa_window_attention(c, *f[:7], None) == code
     assert L.nsa_pack_kv_blocks(c, f[0], f[1], f[2], 1 << 40, None) == code
     assert L.nsa_selected_attention(c, *f[:7], f[0], 1 << 40, None) == code
+    assert L.nsa_compressed_attention(c, *f[:5], None) == code
+    assert L.nsa_select_topn(c, f[0], f[1], None) == code
 
 
 def test_null_config():
@@ -205,6 +207,14 @@ def test_dsa_decode_checks():
     # workspace
     assert L.nsa_dsa_decode(c, 4, 64, 16, FAKE, *f[:6], None, FAKE, FAKE, None, need, None) == WS
     assert L.nsa_dsa_decode(c, 4, 64, 16, FAKE, *f[:6], None, FAKE, FAKE, FAKE, need - 256, None) == WS
+    # the reported size always holds the two-way split's partials (per (b, g, half): 16 maxima,
+    # 16 sums, 16 x d_v outputs in fp32), so the selection and the split run together
+    assert need >= 4 * ok.B * ok.H_kv * 2 * (32 + 16 * ok.d_v) and need % 256 == 0
+    # a workspace not 256-byte aligned is rejected, with or without sel_in
+    W16 = ctypes.c_void_p(0x10010)
+    assert L.nsa_dsa_decode(c, 4, 64, 16, FAKE, *f[:6], None, FAKE, FAKE, W16, need, None) == ALIGN
+    assert L.nsa_dsa_decode(c, 4, 64, 16, FAKE, None, None, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, W16, need,
+                            None) == ALIGN
 
 
 def test_dsa_prefill_checks():
@@ -221,6 +231,13 @@ def test_dsa_prefill_checks():
     assert L.nsa_dsa_prefill(c, 4, 64, 16, *f, None, FAKE, FAKE, FAKE, need - 256, None) == WS
     assert L.nsa_dsa_prefill(c, 4, 64, 16, FAKE, FAKE, FAKE, MIS, FAKE, FAKE, None, FAKE, FAKE, FAKE, need,
                              None) == ALIGN
+    assert L.nsa_dsa_prefill(c, 4, 64, 16, *f, None, FAKE, FAKE, ctypes.c_void_p(0x10010), need, None) == ALIGN
+    # the indexer scores are held one chunk of rows at a time: bounded at any length
+    big = ctypes.byref(cfg(B=2, T=524288, group=16, d_k=192, d_v=128, dtype=1))
+    nb = L.nsa_workspace_bytes(big, 6)
+    assert 4 * 524288 <= nb <= 256 << 20 and nb % 256 == 0
+    mid = ctypes.byref(cfg(B=1, T=65536, group=16, d_k=192, d_v=128, dtype=1))
+    assert L.nsa_workspace_bytes(mid, 6) == 256 << 20
 
 
 def test_binding_rejects_host_tensors():
@@ -310,3 +327,34 @@ def test_selected_attention_workspace_checks():
     c2 = nsa.config(NSAShape(1, 256, 2, 4, 64, 32, "bf16"))
     assert L.nsa_workspace_bytes(ctypes.byref(c2), nsa.OP_SPARSE) == 0
     assert L.nsa_pack_kv_blocks(ctypes.byref(c2), FAKE, FAKE, None, 0, None) == 0
+
+
+@pytest.mark.parametrize("pos", range(3))
+def test_compressed_attention_checks(pos):
+    """q, cmp_k and scores are required; cmp_v and o_cmp are both given or both
+    NULL (scores only); every pointer 16-byte aligned."""
+    L = nsa.lib()
+    c = ctypes.byref(cfg())
+    req = [FAKE] * 3            # q cmp_k scores
+    req[pos] = None
+    q, ck, sc = req
+    assert L.nsa_compressed_attention(c, q, ck, FAKE, FAKE, sc, None) == NULL
+    assert L.nsa_compressed_attention(c, q, ck, None, None, sc, None) == NULL
+    req[pos] = MIS
+    q, ck, sc = req
+    assert L.nsa_compressed_attention(c, q, ck, FAKE, FAKE, sc, None) == ALIGN
+    # one of cmp_v / o_cmp without the other
+    assert L.nsa_compressed_attention(c, FAKE, FAKE, FAKE, None, FAKE, None) == NULL
+    assert L.nsa_compressed_attention(c, FAKE, FAKE, None, FAKE, FAKE, None) == NULL
+    assert L.nsa_compressed_attention(c, FAKE, FAKE, MIS, FAKE, FAKE, None) == ALIGN
+    assert L.nsa_compressed_attention(c, FAKE, FAKE, FAKE, MIS, FAKE, None) == ALIGN
+
+
+def test_select_topn_checks():
+    L = nsa.lib()
+    c = ctypes.byref(cfg())
+    assert L.nsa_select_topn(c, None, FAKE, None) == NULL
+    assert L.nsa_select_topn(c, FAKE, None, None) == NULL
+    assert L.nsa_select_topn(c, MIS, FAKE, None) == ALIGN
+    assert L.nsa_select_topn(c, FAKE, MIS, None) == ALIGN
+    assert L.nsa_select_topn(None, FAKE, FAKE, None) == NULL

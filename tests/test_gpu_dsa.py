@@ -130,26 +130,38 @@ def test_dsa_attention_with_injected_selection(name, s, lens, topk, hi, di, spli
 
 def test_dsa_decode_full_size_sampled():
     """32 sequences at 65,536-token caches (the NSA decode workload's shape),
-    top-2,048 with 4 indexer heads of 64: the selection of 4 sequences and
-    their attention (oracle selection injected) against the oracle."""
+    top-2,048 with 4 indexer heads of 64, as bench.py times it (selection
+    into the workspace, then the two-way split attention reusing it): the
+    selection of 4 sequences against the oracle, their output against the
+    oracle's attention over the GPU's selection, and the output of every
+    other sequence equal bit for bit to the split attention run with the same
+    selection injected."""
     s = WORKLOADS["bf16_decode_B32_T65536"].shape
     say("dsa decode full size", s)
     lens = [s.T] * s.B
     x, ix, sel, o = _run(s, lens, 2048, 4, 64, 85)
     qi, wi, ki = np64(ix["q_idx"][:4]), np64(ix["w_idx"][:4]), np64(ix["k_idx"][:4])
+    q, k, v = np64(x["q"][:4]), np64(x["k"][:4]), np64(x["v"][:4])
+    scale = 1 / math.sqrt(s.dk)
+    ref_sel = []
     for b in range(4):
         sc = dsa.index_scores(qi[b], wi[b], ki[b], s.T)
         _check_selection(sc, qi[b], wi[b], ki[b], s.T, sel[b], 2048, ("full", b))
-    ref_sel = np.stack([dsa.select_topk(dsa.index_scores(qi[b], wi[b], ki[b], s.T), 2048) for b in range(4)])
+        ref_sel.append(dsa.select_topk(sc, 2048))
+        # the timed path's own output: the oracle's attention over the GPU's selection
+        ref = dsa.attend(q[b], k[b], v[b], sel[b], s.G, scale)
+        assert np.abs(np64(o[b]) - ref).max() <= out_tol(s, ref), ("own selection", b)
+    ref_sel = np.stack(ref_sel)
     sel_in = torch.full((s.B, 2048), -1, dtype=torch.int32, device="cuda")
     sel_in[:4] = torch.from_numpy(ref_sel.astype(np.int32)).cuda()
     sel_in[4:] = torch.from_numpy(sel[4:]).cuda()
     _, o2 = nsa.dsa_decode(s, 4, 64, 2048, x["seq_lens"], None, None, None, x["q"], x["k"], x["v"], sel_in=sel_in,
                            ws=_split_ws(s))
     torch.cuda.synchronize()
-    q, k, v = np64(x["q"][:4]), np64(x["k"][:4]), np64(x["v"][:4])
+    # same selection, same split kernels: the same bits
+    assert torch.equal(o[4:], o2[4:])
     for b in range(4):
-        ref = dsa.attend(q[b], k[b], v[b], ref_sel[b], s.G, 1 / math.sqrt(s.dk))
+        ref = dsa.attend(q[b], k[b], v[b], ref_sel[b], s.G, scale)
         assert np.abs(np64(o2[b]) - ref).max() <= out_tol(s, ref), b
 
 
@@ -202,11 +214,13 @@ def test_dsa_prefill_parity(name, s, topk, hi, di):
         assert np.abs(O2[b, t] - ref).max() <= out_tol(s, ref), ("injected", name, b, t)
 
 
-def test_dsa_prefill_full_size_sampled():
-    """T=16384, 4 KV heads x 16, d_k=192, d_v=128, top-2,048 with 4 indexer
-    heads of 64 (the fwd+bwd workload's shape): 12 positions' selections and
+@pytest.mark.parametrize("T", [16384, 65536])
+def test_dsa_prefill_full_size_sampled(T):
+    """4 KV heads x 16, d_k=192, d_v=128, top-2,048 with 4 indexer heads of
+    64 at T=16384 (the fwd+bwd workload's shape) and T=65536 (the indexer
+    scores held one chunk of rows at a time): 12 positions' selections and
     their attention (the oracle's selection injected at those positions)."""
-    s = WORKLOADS["bf16_fwdbwd_T16384"].shape
+    s = WORKLOADS["bf16_fwdbwd_T16384"].shape.with_(T=T)
     say("dsa prefill full size", s)
     topk, hi, di = 2048, 4, 64
     g = torch.Generator(device="cuda").manual_seed(93)
@@ -217,10 +231,12 @@ def test_dsa_prefill_full_size_sampled():
     q = torch.randn((s.B, s.T, s.Hq, s.dk), generator=g, device="cuda").to(dt)
     k = torch.randn((s.B, s.Hkv, s.T, s.dk), generator=g, device="cuda").to(dt)
     v = torch.randn((s.B, s.Hkv, s.T, s.dv), generator=g, device="cuda").to(dt)
-    sel, o = nsa.dsa_prefill(s, hi, di, topk, qi, wi, ki, q, k, v)
+    ws = nsa.workspace(s, nsa.OP_DSA_PREFILL, "cuda")
+    assert ws.numel() <= 256 << 20
+    sel, o = nsa.dsa_prefill(s, hi, di, topk, qi, wi, ki, q, k, v, ws=ws)
     torch.cuda.synchronize()
     QI, WI, KI = np64(qi), np64(wi), np64(ki)
-    rows = [0, 1, 2047, 2048, 5000, 9999, 12345, 16383] + list(np.random.default_rng(94).integers(0, s.T, 4))
+    rows = [0, 1, 2047, 2048, 5000, 9999, 12345, T - 1] + list(np.random.default_rng(94).integers(0, s.T, 4))
     sel_np = sel.cpu().numpy()
     sin = sel.clone()
     for t in rows:
@@ -233,3 +249,7 @@ def test_dsa_prefill_full_size_sampled():
     for t in rows:
         ref = dsa.attend(np64(q[0, t]), Kb, Vb, sin[0, t].cpu().numpy(), s.G, 1 / math.sqrt(s.dk))
         assert np.abs(np64(o2[0, t]) - ref).max() <= out_tol(s, ref), t
+    # rows whose selection was left as the GPU's own: the same bits as the first run
+    keep = torch.ones(s.T, dtype=torch.bool, device="cuda")
+    keep[torch.tensor(rows, device="cuda")] = False
+    assert torch.equal(o2[0, keep], o[0, keep])

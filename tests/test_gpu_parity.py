@@ -13,7 +13,7 @@ from oracle import oracle as orc
 from sparse_attention_long_07_amd import nsa
 from sparse_attention_long_07_amd.config import BF16, FP32, WORKLOADS, NSAShape
 from sparse_attention_long_07_amd.inputs import make_decode, make_prefill, torch_dtype
-from tests.parity_util import check_idx, compressed_close, np64, ocfg, oracle_compress, out_tol
+from tests.parity_util import check_idx, compressed_close, margin_ok, np64, ocfg, oracle_compress, out_tol
 
 pytestmark = pytest.mark.gpu
 
@@ -187,18 +187,47 @@ def test_decode_parity(name, s, seq):
 
 # ------------------------------------------------------------------ full size
 
-def _sample_rows(T, rng, extra=12):
-    base = [0, 1, 31, 32, 63, 64, 127, 128, 1023, 1024, 1087, T // 2, T - 65, T - 64, T - 2, T - 1]
-    base += list(rng.integers(0, T, extra))
-    return np.array(sorted(set(t for t in base if 0 <= t < T)), dtype=np.int32)
+def _edge_rows(T):
+    return [0, 1, 31, 32, 63, 64, 127, 128, 1023, 1024, 1087, T // 2, T - 65, T - 64, T - 2, T - 1]
 
 
-@pytest.mark.parametrize("wname", ["bf16_T8192", "bf16_T65536"])
-def test_prefill_full_size_sampled(wname):
+# (name, workload, unit-scaled inputs, rows: None = every row, else the row stride,
+#  floor on the fraction of rows with a real choice whose block indices are compared exactly).
+# The floors sit below what the oracle gives on draws of the same distributions
+# (unscaled T=8192: 90% of such rows clear the 1e-3 margin; T=65536: 85%); the
+# unit-scaled T=8192 inputs give near-uniform compressed attention, so almost
+# no row clears the margin there and its count is only reported.
+FULL = [
+    ("bf16_T8192_scaled_all_rows", "bf16_T8192", True, None, None),
+    ("bf16_T8192_unscaled_all_rows", "bf16_T8192", False, None, 0.80),
+    ("bf16_T65536_every_32nd_row", "bf16_T65536", False, 32, 0.75),
+]
+
+
+def _exact_fraction(s, scores, t_rows, idx_ref, idx_gpu):
+    """(rows with a real choice checked exactly, rows with a real choice, rows checked exactly, rows)"""
+    n_exact, n_all = check_idx(s, scores, t_rows, idx_ref, idx_gpu)
+    real = exact_real = 0
+    for r, t in enumerate(t_rows):
+        jc = int(t) // s.lsel
+        nforced = len({0, jc - 1, jc} & set(range(jc + 1)))
+        if jc + 1 - nforced > s.n - nforced:
+            real += 1
+            exact_real += margin_ok(scores[r], int(t), s.n, s.lsel)
+    return exact_real, real, n_exact, n_all
+
+
+@pytest.mark.parametrize("name,wname,scaled,stride,floor", FULL, ids=[c[0] for c in FULL])
+def test_prefill_full_size(name, wname, scaled, stride, floor):
+    """The prefill workloads at full size: the staged calls that bench.py times
+    equal the forward call bit for bit; the oracle's block indices injected,
+    every sampled row's output within tolerance; the GPU's own selection
+    exact on every row the margin decides and a valid top-n set elsewhere,
+    and its output within tolerance of the oracle's for that selection."""
     wl = WORKLOADS[wname]
     s = wl.shape
-    say("full-size prefill", wname, s)
-    x = make_prefill(s, 1000, "cuda", unit_scaled=wl.unit_scaled)
+    say("full-size prefill", name, s)
+    x = make_prefill(s, 1000 if scaled == wl.unit_scaled else 1010, "cuda", unit_scaled=scaled)
     ck, cv = nsa.compress_kv(s, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"])
     o, idx = nsa.forward(s, x["q"], x["k"], x["v"], ck, cv, x["w_g"], x["b_g"], want_idx=True)
     # the stage-by-stage calls that bench.py times give the same result, bit for bit
@@ -216,52 +245,110 @@ def test_prefill_full_size_sampled(wname):
     vc = oracle_compress(s, x["v"], x["w_cv"], x["pe_v"])
     for got, ref in ((ck, kc), (cv, vc)):
         assert compressed_close(s, np64(got), ref)
-    rows = _sample_rows(s.T, np.random.default_rng(7))
+    if stride is None:
+        rows = np.arange(s.T, dtype=np.int32)
+    else:
+        rows = np.array(sorted(set(range(0, s.T, stride)) | set(_edge_rows(s.T))), dtype=np.int32)
     say("  oracle rows", len(rows))
-    qr = np64(x["q"][0, torch.from_numpy(rows).long().cuda()])
+    rows_t = torch.from_numpy(rows).long().cuda()
+    qr = np64(x["q"][0, rows_t])
     k64, v64 = np64(x["k"]), np64(x["v"])
     wg, bg = np64(x["w_g"]), np64(x["b_g"])
     oc = ocfg(s)
     zeros = np.zeros(len(rows), np.int32)
     ref = orc.forward_rows(oc, zeros, rows, qr, kc, vc, k64, v64, wg, bg, want_scores=True)
     ig = idx.cpu().numpy()[0][:, rows].transpose(1, 0, 2)          # [R,Hkv,n]
-    n_exact, n_all = check_idx(s, ref["scores"].reshape(-1, s.nb), np.repeat(rows, s.Hkv),
-                               ref["idx"].reshape(-1, s.n), ig.reshape(-1, s.n))
-    say("  idx rows checked exactly: %d / %d" % (n_exact, n_all))
-    ref2 = orc.forward_rows(oc, zeros, rows, qr, kc, vc, k64, v64, wg, bg, idx_in=ig)
-    og = np64(o[0, torch.from_numpy(rows).long().cuda()])
-    err = np.abs(og - ref2["o"]).max()
-    say("  max|o-o_ref| = %.3g (tol %.3g)" % (err, out_tol(s, ref2["o"])))
-    assert err <= out_tol(s, ref2["o"])
+    ex_real, real, n_exact, n_all = _exact_fraction(s, ref["scores"].reshape(-1, s.nb), np.repeat(rows, s.Hkv),
+                                                    ref["idx"].reshape(-1, s.n), ig.reshape(-1, s.n))
+    say("  idx rows checked exactly: %d / %d; of the rows with a real choice: %d / %d (%.1f%%)"
+        % (n_exact, n_all, ex_real, real, 100.0 * ex_real / max(real, 1)))
+    if floor is not None:
+        assert ex_real >= floor * real, (ex_real, real)
+    # the oracle's indices injected at the sampled rows (the GPU's own elsewhere)
+    inj = idx.clone()
+    inj[0][:, rows_t] = torch.from_numpy(np.ascontiguousarray(ref["idx"].transpose(1, 0, 2))).cuda()
+    o_inj = nsa.forward(s, x["q"], x["k"], x["v"], ck, cv, x["w_g"], x["b_g"], idx_in=inj)
+    torch.cuda.synchronize()
+    err = np.abs(np64(o_inj[0, rows_t]) - ref["o"]).max()
+    tol = out_tol(s, ref["o"])
+    say("  oracle idx injected: max|o-o_ref| = %.3g (tol %.3g)" % (err, tol))
+    assert err <= tol
+    # the GPU's own selection: where it equals the oracle's the reference is
+    # the oracle's output, elsewhere the oracle is rerun with the GPU's lists
+    og = np64(o[0, rows_t])
+    same = np.all(ig == ref["idx"], axis=(1, 2))
+    err = np.abs(og[same] - ref["o"][same]).max() if same.any() else 0.0
+    if (~same).any():
+        d = np.nonzero(~same)[0]
+        ref2 = orc.forward_rows(oc, zeros[d], rows[d], qr[d], kc, vc, k64, v64, wg, bg, idx_in=ig[d])
+        err = max(err, np.abs(og[d] - ref2["o"]).max())
+    say("  own selection: %d of %d rows select as the oracle; max|o-o_ref| = %.3g" % (same.sum(), len(rows), err))
+    assert err <= tol
 
 
-def test_decode_full_size_sampled():
+@pytest.fixture(scope="module")
+def decode_full():
+    """The 32 x 65,536 decode workload on the GPU: its own selection, and the
+    inputs for the per-sequence oracle checks."""
     wl = WORKLOADS["bf16_decode_B32_T65536"]
     s = wl.shape
-    say("full-size decode", s)
     x = make_decode(s, 1003, "cuda", unit_scaled=wl.unit_scaled)
     ck, cv = nsa.compress_kv(s, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"])
     o, idx = nsa.decode_step(s, x["seq_lens"], x["q"], x["k"], x["v"], ck, cv, x["w_g"], x["b_g"], want_idx=True)
     torch.cuda.synchronize()
-    for b in (0, 21):
-        say("  oracle sequence", b)
-        s1 = s.with_(B=1)
+    return {"s": s, "x": x, "ck": ck, "cv": cv, "o": o, "idx": idx, "stats": []}
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_decode_full_size(decode_full, part):
+    """All 32 sequences of the decode workload, 8 per test: the GPU's
+    compressed caches against the oracle's; the block indices exact where the
+    margin decides; the output within tolerance of the oracle's for the GPU's
+    own selection and, with the oracle's selection injected, of the oracle's
+    own output."""
+    D = decode_full
+    s, x = D["s"], D["x"]
+    seqs = list(range(8 * part, 8 * part + 8))
+    say("full-size decode, sequences", seqs)
+    s1 = s.with_(B=1)
+    oc = ocfg(s1)
+    t = np.array([s.T - 1], np.int32)
+    wg, bg = np64(x["w_g"]), np64(x["b_g"])
+    ref_idx = {}
+    ref_o = {}
+    for b in seqs:
         kb, vb = x["k"][b:b + 1], x["v"][b:b + 1]
         kc = oracle_compress(s1, kb, x["w_ck"], x["pe_k"])
         vc = oracle_compress(s1, vb, x["w_cv"], x["pe_v"])
-        assert compressed_close(s, np64(ck[b:b + 1]), kc)
-        oc = ocfg(s1)
-        t = np.array([s.T - 1], np.int32)
+        assert compressed_close(s, np64(D["ck"][b:b + 1]), kc)
+        assert compressed_close(s, np64(D["cv"][b:b + 1]), vc)
         qb = np64(x["q"][b:b + 1])
         k64, v64 = np64(kb), np64(vb)
-        ref = orc.forward_rows(oc, [0], t, qb, kc, vc, k64, v64, np64(x["w_g"]), np64(x["b_g"]), want_scores=True)
-        check_idx(s1, ref["scores"].reshape(-1, s.nb), np.repeat(t, s.Hkv), ref["idx"].reshape(-1, s.n),
-                  idx[b:b + 1].cpu().numpy().reshape(-1, s.n))
-        ref2 = orc.forward_rows(oc, [0], t, qb, kc, vc, k64, v64, np64(x["w_g"]), np64(x["b_g"]),
-                                idx_in=idx[b:b + 1].cpu().numpy())
-        err = np.abs(np64(o[b:b + 1]) - ref2["o"]).max()
-        say("  max|o-o_ref| = %.3g" % err)
+        ref = orc.forward_rows(oc, [0], t, qb, kc, vc, k64, v64, wg, bg, want_scores=True)
+        ig = D["idx"][b:b + 1].cpu().numpy()
+        ex_real, real, _, _ = _exact_fraction(s1, ref["scores"].reshape(-1, s.nb), np.repeat(t, s.Hkv),
+                                              ref["idx"].reshape(-1, s.n), ig.reshape(-1, s.n))
+        D["stats"].append((ex_real, real))
+        ref2 = ref if np.array_equal(ig, ref["idx"]) else orc.forward_rows(oc, [0], t, qb, kc, vc, k64, v64, wg, bg,
+                                                                           idx_in=ig)
+        err = np.abs(np64(D["o"][b:b + 1]) - ref2["o"]).max()
+        say("  sequence %d: idx exact on %d of %d KV heads; max|o-o_ref| = %.3g" % (b, ex_real, real, err))
         assert err <= out_tol(s, ref2["o"])
+        ref_idx[b], ref_o[b] = ref["idx"][0], ref["o"][0]
+    inj = D["idx"].clone()
+    for b in seqs:
+        inj[b] = torch.from_numpy(np.ascontiguousarray(ref_idx[b])).cuda()
+    o_inj = nsa.decode_step(s, x["seq_lens"], x["q"], x["k"], x["v"], D["ck"], D["cv"], x["w_g"], x["b_g"],
+                            idx_in=inj)
+    torch.cuda.synchronize()
+    for b in seqs:
+        err = np.abs(np64(o_inj[b]) - ref_o[b]).max()
+        assert err <= out_tol(s, ref_o[b]), (b, err)
+    done = D["stats"]
+    if len(done) == s.B:
+        ex, real = sum(a for a, _ in done), sum(r for _, r in done)
+        say("  all 32 sequences: idx exact on %d of %d (sequence, KV head) rows" % (ex, real))
+        assert ex >= 0.75 * real
 
 
 # ------------------------------------------------- per-stage, oracle injected
