@@ -75,7 +75,11 @@ struct RowArgs {
                                 // (added to o), 3 pack K/V blocks only
 };
 
-// Arguments of the matrix-core decode step (one row per sequence).
+// Arguments of the matrix-core decode step (one row per sequence).  Each
+// (sequence, KV head) pair has nslot = nq + nw + 1 + ns partial slots of
+// [16 max][16 sum][16][dv] fp32 (unnormalised outputs): the compressed cache
+// in nq ranges, the window in nw ranges, the always-kept selected blocks, the
+// other selected blocks in ns groups.
 struct DecArgs {
     Dims d;
     const int32_t *seq_lens;      // device [B]
@@ -84,9 +88,14 @@ struct DecArgs {
     const void *wg, *bg;
     const int32_t *idx_in;        // [B][Hkv][n] or nullptr
     void *o;                      // [B][Hq][dv]
-    int cs, ws, nbp;              // compressed / window splits; blocks per (b, g) in bx/by
-    float *pm, *pl, *po;          // phase-A partials [pair][cs+ws][16] (+[dv])
-    float *bx, *by;               // block importance terms [pair][16][nbp]
+    int nq, nw, ns, nslot;        // partial slots per pair (see above)
+    int cmp_keys;                 // compressed slots per k_dec_cmp workgroup
+    int ngrp, nbp;                // 32-slot groups and 4-slot blocks of the compressed cache
+    float *part;                  // [pair][nq+nw+ns][32 + 16 dv]
+    float *bt;                    // [pair][nbp][16] block-importance terms (see k_decode.hip)
+    float *gmax;                  // [pair][ngrp][16] softmax reference of each group's terms
+    float *gtail;                 // [pair][ngrp][16] the group's last-slot probability
+    float *gates;                 // [pair][16][3]
     int32_t *idx;                 // selection output [B][Hkv][n]
 };
 

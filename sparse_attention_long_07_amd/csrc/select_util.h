@@ -17,6 +17,14 @@
 //    order-preserving integer image of the scores, counting with ballots; ties
 //    at that score go to the lowest blocks.  Falls back to the argmax rounds
 //    when more than 64 blocks pass the first threshold.
+//  * wave_select_topn_sort (any number of candidates): the same threshold
+//    idea with sorts instead of bisections.  Each candidate gets a distinct
+//    64-bit key, its score's order-preserving image above the complement of
+//    its block, so a larger key is a better block and equal scores rank the
+//    lower block first.  A bitonic sort of the 64 lane maxima gives the
+//    threshold; the candidates at or above it are compacted and sorted, and
+//    the first k are taken.  Two 21-stage sorts replace two 32-step
+//    bisections whose every step waited on a ballot.
 // The chosen set is written in ascending order and padded with -1.
 #pragma once
 
@@ -206,6 +214,115 @@ __device__ __forceinline__ void wave_select_topn_fast(const float *S, int jcur, 
     // out = 0, the k chosen blocks ascending, jc-1, jc.
     const uint64_t tk = __ballot(take);
     if (take) out[1 + __popcll(tk & lt)] = (int)cv.y;
+    if (lane == 0) {
+        out[0] = 0;
+        out[k + 1] = jcur - 1;
+        out[k + 2] = jcur;
+    }
+    for (int q = nforced + k + lane; q < n; q += 64) out[q] = -1;
+}
+
+// Candidate key: the score's order-preserving image above the complement of
+// the block, so distinct blocks have distinct keys, larger is better and
+// equal scores rank the lower block first.  0 is no candidate.
+__device__ __forceinline__ uint64_t cand_key(float s, int j)
+{
+    return ((uint64_t)ordered_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m)
+{
+    const int lo = __shfl_xor((int)(uint32_t)v, m, 64), hi = __shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo;
+}
+
+// Bitonic sort of one 64-bit key per lane over the wavefront, descending
+// (lane 0 ends with the largest).  At stage (k, j) lane i and lane i ^ j
+// compare; within a run of k lanes that ends descending the lower lane keeps
+// the larger key.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v, int lane)
+{
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint64_t o = shfl_xor64(v, j);
+            const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
+            v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
+        }
+    return v;
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l)
+{
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// cand: 64 entries of LDS scratch owned by this wavefront.  Same result as
+// wave_select_topn.
+__device__ __forceinline__ void wave_select_topn_sort(const float *S, int jcur, int n, int32_t *out, int lane,
+                                                      uint64_t *cand)
+{
+    jcur = __builtin_amdgcn_readfirstlane(jcur);   // one row per wavefront: uniform
+    n = __builtin_amdgcn_readfirstlane(n);
+    const int ncand = jcur + 1;
+    const int nforced = jcur == 0 ? 1 : (jcur == 1 ? 2 : 3);
+    const int k = n - nforced;
+    if (ncand - nforced <= k || k <= 0) {
+        wave_select_topn(S, jcur, n, out, lane);   // every block is taken
+        return;
+    }
+    const int RR = (ncand + 63) / 64;
+    auto key_of = [&](int j) -> uint64_t {
+        const float v = S[j < ncand ? j : ncand - 1];   // unconditional: the loads go out together
+        const bool ok = j < ncand && j != 0 && j != jcur && j != jcur - 1;
+        return ok ? cand_key(v, j) : 0ull;
+    };
+    // this lane's blocks j = lane + 64 rr: the first 16 kept in registers
+    uint64_t kc[16];
+    uint64_t lmax = 0ull;
+#pragma unroll
+    for (int rr = 0; rr < 16; rr++) {
+        kc[rr] = key_of(lane + 64 * rr);
+        lmax = kc[rr] > lmax ? kc[rr] : lmax;
+    }
+    for (int rr = 16; rr < RR; rr++) {
+        const uint64_t kv = key_of(lane + 64 * rr);
+        lmax = kv > lmax ? kv : lmax;
+    }
+    // the k-th largest lane maximum: at least k candidates reach it
+    const uint64_t x = readlane64(wave_sort_desc(lmax, lane), k - 1);
+    // the candidates at or above it, compacted in block order
+    const uint64_t lt = __lanemask_lt();
+    int C = 0;
+    auto take = [&](uint64_t kv) {
+        const bool p = kv != 0ull && kv >= x;
+        const uint64_t bal = __ballot(p);
+        const int pos = C + __popcll(bal & lt);
+        if (p && pos < 64) cand[pos] = kv;
+        C += __popcll(bal);
+    };
+#pragma unroll
+    for (int rr = 0; rr < 16; rr++) take(kc[rr]);
+    for (int rr = 16; rr < RR; rr++) take(key_of(lane + 64 * rr));
+    if (x == 0ull || C > 64) {
+        wave_select_topn(S, jcur, n, out, lane);
+        return;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the compacted keys are in LDS
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t top = wave_sort_desc(lane < C ? cand[lane] : 0ull, lane);
+    // lanes 0 .. k-1 hold the picks; write them in ascending block order
+    const int jl = (int)(0xFFFFFFFFu - (uint32_t)top);
+    int rank = 0;
+    for (int m = 0; m < k; m++) {
+        const int jm = __builtin_amdgcn_readlane(jl, m);
+        rank += jm < jl ? 1 : 0;
+    }
+    // Here jc >= 2, so the forced blocks are 0 < (chosen blocks) < jc-1 < jc
+    if (lane < k) out[1 + rank] = jl;
     if (lane == 0) {
         out[0] = 0;
         out[k + 1] = jcur - 1;
