@@ -248,6 +248,22 @@ nsa_status nsa_decode_step(const nsa_config *cfg, const int32_t *seq_lens, const
                            const void *b_g, const int32_t *idx_in, void *o, int32_t *idx_out, void *ws,
                            size_t ws_bytes, void *stream);
 
+/* nsa_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and
+ * harnesses that forbid allocation).  It allocates nothing: the workspace is
+ * a 32 MiB array in the library's device memory, one per device the library
+ * runs on, held until the process ends.  Arguments, results and errors as
+ * nsa_decode_step; NSA_ERR_WORKSPACE when nsa_workspace_bytes(cfg,
+ * NSA_OP_DECODE) exceeds 32 MiB (at 65,536-token caches, 16 heads per KV
+ * head and d_v = 128, up to about 180 (sequence, KV head) pairs); NSA_ERR_HIP
+ * if the array's address cannot be looked up.  Every call on a device uses
+ * the same array, so calls that overlap on one device (two streams, two host
+ * threads) race; calls ordered on one stream do not. */
+nsa_status nsa_decode_step_noalloc(const nsa_config *cfg, const int32_t *seq_lens, const void *q,
+                                   const void *k_cache, const void *v_cache, const void *cmp_k, const void *cmp_v,
+                                   const void *w_g, const void *b_g, const int32_t *idx_in, void *o,
+                                   int32_t *idx_out, void *stream);
+
 /* Backward pass of the prefill forward (deepdaiv newsletter, on native
  * trainability: the sparse pattern is learned in training, so gradients flow
  * through the three branches, the compression maps and the gates).  With

@@ -24,7 +24,7 @@ STATUS = {0: "NSA_OK", -1: "NSA_ERR_NULL", -2: "NSA_ERR_SHAPE", -3: "NSA_ERR_DTY
 EXPORTS = ("nsa_workspace_bytes", "nsa_compress_kv", "nsa_compress_kv_mlp", "nsa_compress_append", "nsa_compressed_attention",
            "nsa_select_topn",
            "nsa_sparse_attention", "nsa_pack_kv_blocks", "nsa_window_attention", "nsa_selected_attention", "nsa_select_blocks",
-           "nsa_forward", "nsa_decode_step", "nsa_backward", "nsa_dsa_decode", "nsa_dsa_prefill", "nsa_status_string")
+           "nsa_forward", "nsa_decode_step", "nsa_decode_step_noalloc", "nsa_backward", "nsa_dsa_decode", "nsa_dsa_prefill", "nsa_status_string")
 
 
 class NSAError(RuntimeError):
@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.nsa_forward.argtypes = [ctypes.POINTER(Config)] + [_vp] * 12 + [ctypes.c_size_t, _vp]
         L.nsa_decode_step.restype = ctypes.c_int
         L.nsa_decode_step.argtypes = [ctypes.POINTER(Config)] + [_vp] * 12 + [ctypes.c_size_t, _vp]
+        L.nsa_decode_step_noalloc.restype = ctypes.c_int
+        L.nsa_decode_step_noalloc.argtypes = [ctypes.POINTER(Config)] + [_vp] * 12
         L.nsa_backward.restype = ctypes.c_int
         L.nsa_backward.argtypes = [ctypes.POINTER(Config)] + [_vp] * 23 + [ctypes.c_size_t, _vp]
         _lib = L
@@ -377,6 +379,32 @@ def decode_step(s: NSAShape, seq_lens, q, k_cache, v_cache, cmp_k, cmp_v, w_g, b
     _check("nsa_decode_step", lib().nsa_decode_step(ctypes.byref(c), _p(seq_lens), _p(q), _p(k_cache),
                                                     _p(v_cache), _p(cmp_k), _p(cmp_v), _p(w_g), _p(b_g),
                                                     _p(idx_in), _p(o), _p(idx), _p(ws), ws.numel(), _stream()))
+    return (o, idx) if want_idx else o
+
+
+def decode_step_noalloc(s: NSAShape, seq_lens, q, k_cache, v_cache, cmp_k, cmp_v, w_g, b_g, idx_in=None, o=None,
+                        want_idx=False):
+    """decode_step with the library's own static scratch as the workspace
+    (nsa_decode_step_noalloc: no allocation by the library)."""
+    dt = _dt(s)
+    _req(seq_lens, "seq_lens", (s.B,), torch.int32)
+    _req(q, "q", (s.B, s.Hq, s.dk), dt)
+    _req(k_cache, "k_cache", (s.B, s.Hkv, s.T, s.dk), dt)
+    _req(v_cache, "v_cache", (s.B, s.Hkv, s.T, s.dv), dt)
+    _req(cmp_k, "cmp_k", (s.B, s.Hkv, s.n_pad, s.dk), dt)
+    _req(cmp_v, "cmp_v", (s.B, s.Hkv, s.n_pad, s.dv), dt)
+    _req(w_g, "w_g", (s.Hq, 3, s.dk), dt)
+    _req(b_g, "b_g", (s.Hq, 3), dt)
+    if idx_in is not None:
+        _req(idx_in, "idx_in", (s.B, s.Hkv, s.n), torch.int32)
+    if o is None:
+        o = torch.empty((s.B, s.Hq, s.dv), dtype=dt, device=q.device)
+    _req(o, "o", (s.B, s.Hq, s.dv), dt)
+    idx = torch.empty((s.B, s.Hkv, s.n), dtype=torch.int32, device=q.device) if want_idx else None
+    c = config(s)
+    _check("nsa_decode_step_noalloc",
+           lib().nsa_decode_step_noalloc(ctypes.byref(c), _p(seq_lens), _p(q), _p(k_cache), _p(v_cache), _p(cmp_k),
+                                         _p(cmp_v), _p(w_g), _p(b_g), _p(idx_in), _p(o), _p(idx), _stream()))
     return (o, idx) if want_idx else o
 
 

@@ -358,3 +358,30 @@ def test_select_topn_checks():
     assert L.nsa_select_topn(c, MIS, FAKE, None) == ALIGN
     assert L.nsa_select_topn(c, FAKE, MIS, None) == ALIGN
     assert L.nsa_select_topn(None, FAKE, FAKE, None) == NULL
+
+
+def test_decode_noalloc_checks():
+    """The allocation-free decode step checks its arguments before any HIP
+    call: bad configurations, NULL and misaligned pointers, and a workspace
+    need above its 32 MiB scratch array."""
+    L = nsa.lib()
+    c = ctypes.byref(cfg())
+    f = [FAKE] * 8          # seq_lens q k_cache v_cache cmp_k cmp_v w_g b_g
+    assert L.nsa_decode_step_noalloc(ctypes.byref(cfg(T=0)), *f, None, FAKE, None, None) == SHAPE
+    assert L.nsa_decode_step_noalloc(None, *f, None, FAKE, None, None) == NULL
+    for pos in range(8):
+        a = list(f)
+        a[pos] = None
+        assert L.nsa_decode_step_noalloc(c, *a, None, FAKE, None, None) == NULL
+        a[pos] = MIS
+        assert L.nsa_decode_step_noalloc(c, *a, None, FAKE, None, None) == ALIGN
+    assert L.nsa_decode_step_noalloc(c, *f, None, None, None, None) == NULL          # o
+    assert L.nsa_decode_step_noalloc(c, *f, MIS, FAKE, None, None) == ALIGN          # idx_in
+    assert L.nsa_decode_step_noalloc(c, *f, None, FAKE, MIS, None) == ALIGN          # idx_out
+    # 4,096 sequences of 65,536 tokens need far more than the 32 MiB array
+    big = nsa.config(NSAShape(4096, 65536, 4, 16, 192, 128))
+    assert L.nsa_workspace_bytes(ctypes.byref(big), nsa.OP_DECODE) > 32 << 20
+    assert L.nsa_decode_step_noalloc(ctypes.byref(big), *f, None, FAKE, None, None) == WS
+    # the decode workload (32 x 65,536) fits
+    wl = nsa.config(WORKLOADS["bf16_decode_B32_T65536"].shape)
+    assert 0 < L.nsa_workspace_bytes(ctypes.byref(wl), nsa.OP_DECODE) <= 32 << 20
