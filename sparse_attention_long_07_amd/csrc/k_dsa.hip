@@ -17,6 +17,8 @@
 //              then an ordered compaction by wave ballots: every key above
 //              the threshold and the lowest-position keys equal to it,
 //              ascending (exactly k of them, since more than k candidates).
+//              Rows up to 65,536 positions are read once into registers (up
+//              to 64 scores per lane) and every pass runs from them.
 // k_dsa_attn   one 8-wave workgroup per (sequence, KV head); wave w takes
 //              selected slots [w k/8, (w+1) k/8) in sub-chunks of 32 tokens:
 //              S^T = K Q^T on gathered K rows (16x16x32 MFMA, the 16 heads
@@ -134,24 +136,211 @@ __device__ __forceinline__ int block_exscan(int v, int *wsum, int *tot)
     return base + x - v;
 }
 
+// hist[bin] += 1 for the active lanes, the lanes that share the first
+// active lane's bin with one atomic: with many equal keys (ties) per-lane
+// atomics on one address serialise across the wave
+__device__ __forceinline__ void hist_add(int *hist, int bin, bool active)
+{
+    const unsigned long long am = __ballot(active);
+    if (am == 0ull) return;
+    const int lane = threadIdx.x & 63, first = (int)__builtin_ctzll(am);
+    const int b0 = __shfl(bin, first, 64);
+    const unsigned long long same = __ballot(active && bin == b0);
+    if (lane == first) atomicAdd(&hist[b0], (int)__popcll(same));
+    else if (active && bin != b0) atomicAdd(&hist[bin], 1);
+}
+
+// the lowest n set bits of x (none for n <= 0; __popc is unsigned, so the
+// comparison is made in int)
+__device__ __forceinline__ uint32_t lowest_bits(uint32_t x, int n)
+{
+    if (n <= 0) return 0u;
+    if (n >= (int)__popc(x)) return x;
+    uint32_t r = 0;
+    for (int k = 0; k < n; k++) {
+        r |= x & (0u - x);
+        x &= x - 1;
+    }
+    return r;
+}
+
+// NR > 0: every score of the row is loaded once into registers (NR per lane,
+// rows of at most 1024 NR positions).  A sample of one register step in
+// eight bounds the k-th score from below by a first digit; the keys at or
+// above it (a few more than k) are compacted into LDS, the radix select runs
+// over them only, and the kept positions go out through a bitmap in
+// ascending order.  When the candidates are fewer than k (an unlucky sample)
+// or more than the LDS list holds, the five passes run over all registers.
+// NR = 0: each pass reads the scores again (rows of any length).
+template <int NR>
 __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(const float *__restrict__ scores,
                                                            const int32_t *__restrict__ seq_lens,
                                                            int32_t *__restrict__ sel, int T, int topk, int prefill,
                                                            int row0)
 {
     constexpr int kWaves = kTopkThreads / 64;
-    __shared__ int hist[4096];
+    constexpr int kCap = NR > 0 ? 12288 : 1;   // candidate list: keys, positions
+    __shared__ int hist[4096];   // histograms; in the candidate path then two position bitmaps
+    __shared__ uint32_t cand_k[kCap];
+    __shared__ uint16_t cand_p[kCap];
     __shared__ int wsum[kWaves];
     __shared__ int wgt[kWaves], weq[kWaves];
     __shared__ uint32_t s_prefix;
-    __shared__ int s_remain;
-    const int b = row0 + blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ int s_remain, s_nbin, s_found, s_cnt;
+    const int b = row0 + blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the range bounds stay scalar
     const int L = prefill ? b % T + 1 : seq_len_of(seq_lens, b, T);
     const float *sc = scores + (long)blockIdx.x * T;
     int32_t *out = sel + (long)b * topk;
     if (L <= topk) {
         for (int i = tid; i < topk; i += kTopkThreads) out[i] = i < L ? i : -1;
         return;
+    }
+    // wave w owns the contiguous 64-aligned range [lo, hi): the compaction
+    // reads it in order, and with NR > 0 its lane l caches positions lo + 64 i + l
+    const int per = ((L + kWaves - 1) / kWaves + 63) / 64 * 64;
+    const int lo = min(L, wave * per), hi = min(L, lo + per);
+    // Key 0 marks a slot past the range: every real score's key is at least
+    // order_key(-inf) = 0x007fffff (top digit 7), so with more than k real
+    // keys the k-th largest never falls to it; after the first digit it
+    // matches no prefix, and it is never kept.
+    // The loads go through a buffer resource bounded by the row's length (the
+    // hardware returns 0 past it), one address register and a constant offset
+    // each, so they are issued back to back without a branch each.
+    uint32_t uc[NR > 0 ? NR : 1];
+    int nch = (hi - lo + 63) >> 6;   // 64-slot steps of this wave's range
+    if constexpr (NR > 0) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)sc, 0, L * 4, 0x00020000);
+        const int voff = (lo + lane) * 4;
+#pragma clang loop unroll(full)
+        for (int i = 0; i < NR; i++) uc[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, 256 * i, 0);
+#pragma clang loop unroll(full)
+        for (int i = 0; i < NR; i++) {
+            asm volatile("" : "+v"(uc[i]));   // every load issued unconditionally, none sunk into a branch
+            uc[i] = lane < hi - lo - 64 * i ? order_key(__uint_as_float(uc[i])) : 0u;
+            asm volatile("" : "+v"(uc[i]));   // the key formed once, not again at every use
+        }
+    }
+    const unsigned long long below = (1ull << lane) - 1ull;
+    // After a histogram of `bins` digits at `shift` under prefix `pre`: the
+    // digit holding the rem-th largest counted key (s_found stays 0 when fewer
+    // than rem keys were counted), and how many keys share it.
+    auto find_digit = [&](int bins, int shift, uint32_t pre, int rem) {
+        int c[4], own = 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int dgt = bins - 1 - 4 * tid - i;
+            c[i] = dgt >= 0 ? hist[dgt] : 0;
+            own += c[i];
+        }
+        int tot;
+        int above = block_exscan(own, wsum, &tot);   // keys with a higher digit than this thread's first
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            if (above < rem && above + c[i] >= rem) {
+                s_prefix = pre | ((uint32_t)(bins - 1 - 4 * tid - i) << shift);
+                s_remain = rem - above;
+                s_nbin = c[i];
+                s_found = 1;
+            }
+            above += c[i];
+        }
+        __syncthreads();
+    };
+    if constexpr (NR > 0) {
+        // (a) the sample's first digits
+        for (int i = tid; i < 4096; i += kTopkThreads) hist[i] = 0;
+        if (tid == 0) {
+            s_found = 0;
+            s_cnt = 0;
+        }
+        __syncthreads();
+        asm volatile("" : "+s"(nch));
+#pragma clang loop unroll(full)
+        for (int i = 0; i < NR; i += 8)
+            if (i < nch) hist_add(hist, (int)(uc[i] >> 20), uc[i] != 0u);
+        __syncthreads();
+        // about 4 standard deviations above the sample's expected share of k
+        find_digit(4096, 20, 0u, topk / 8 + topk / 32 + 16);
+        const uint32_t tau = s_found ? max(s_prefix, 1u) : 1u;   // key 0 (past the range) never qualifies
+        // (b) candidates into LDS: each wave counts, reserves its slots, writes
+        // (key 0, past the range, is below tau >= 1, so no range test is needed)
+        int cw = 0;
+#pragma clang loop unroll(full)
+        for (int i = 0; i < NR; i++) cw += __popcll(__ballot(uc[i] >= tau));
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&s_cnt, cw);
+        base = __builtin_amdgcn_readfirstlane(base);
+        int pos0 = lo + lane;
+        uint32_t tau2 = tau;
+        // positions formed at the writes, and the comparisons made again rather
+        // than NR ballots held in scalar registers from the counting loop
+        asm volatile("" : "+v"(pos0), "+v"(tau2));
+#pragma clang loop unroll(full)
+        for (int i = 0; i < NR; i++) {
+            const bool c = uc[i] >= tau2;
+            const unsigned long long m = __ballot(c);
+            const int at = base + (int)__popcll(m & below);
+            if (c && at < kCap) {
+                cand_k[at] = uc[i];
+                cand_p[at] = (uint16_t)(pos0 + 64 * i);
+            }
+            base += __popcll(m);
+        }
+        __syncthreads();
+        const int C = s_cnt;
+        if (C >= topk && C <= kCap) {
+            // (c) radix select among the candidates: the k-th largest of the
+            // row is the k-th largest of them, every other key being smaller
+            uint32_t prefix = 0, mask = 0;
+            int remain = topk, nbin = 0;
+            for (int pass = 0; pass < 3; pass++) {
+                const int shift = pass == 0 ? 20 : pass == 1 ? 8 : 0;
+                const int bins = pass == 2 ? 256 : 4096;
+                for (int i = tid; i < bins; i += kTopkThreads) hist[i] = 0;
+                __syncthreads();
+                for (int j0 = 0; j0 < C; j0 += kTopkThreads) {   // whole waves, for the aggregation
+                    const int j = j0 + tid;
+                    const uint32_t u = j < C ? cand_k[j] : 0u;
+                    hist_add(hist, (int)((u >> shift) & (bins - 1)), j < C && (u & mask) == prefix);
+                }
+                __syncthreads();
+                find_digit(bins, shift, prefix, remain);
+                prefix = s_prefix;
+                remain = s_remain;
+                nbin = s_nbin;
+                mask |= (uint32_t)(bins - 1) << shift;
+                __syncthreads();
+            }
+            // (d) kept positions as bits (A: above the k-th key, and the keys
+            // equal to it when all of them are kept; B: the equal keys when
+            // only the lowest `remain` positions among them are), then out in
+            // ascending order, two bitmap words per thread
+            uint32_t *A = (uint32_t *)hist, *Bq = (uint32_t *)hist + 2048;
+            for (int i = tid; i < 4096; i += kTopkThreads) hist[i] = 0;
+            __syncthreads();
+            const bool all_eq = nbin == remain;
+            for (int j = tid; j < C; j += kTopkThreads) {
+                const uint32_t u = cand_k[j], p = cand_p[j];
+                if (u > prefix || (u == prefix && all_eq)) atomicOr(&A[p >> 5], 1u << (p & 31));
+                else if (u == prefix) atomicOr(&Bq[p >> 5], 1u << (p & 31));
+            }
+            __syncthreads();
+            const int w0 = 2 * tid, w1 = w0 + 1;
+            uint32_t a0 = A[w0], a1 = A[w1];
+            int tot;
+            if (!all_eq) {
+                const uint32_t b0 = Bq[w0], b1 = Bq[w1];
+                int ex = block_exscan(__popc(b0) + __popc(b1), wsum, &tot);
+                a0 |= lowest_bits(b0, remain - ex);
+                ex += __popc(b0);
+                a1 |= lowest_bits(b1, remain - ex);
+            }
+            int at = block_exscan(__popc(a0) + __popc(a1), wsum, &tot);
+            for (uint32_t bits = a0; bits; bits &= bits - 1) out[at++] = 32 * w0 + __builtin_ctz(bits);
+            for (uint32_t bits = a1; bits; bits &= bits - 1) out[at++] = 32 * w1 + __builtin_ctz(bits);
+            return;
+        }
     }
     // radix select of the k-th largest key: digits of 12, 12 and 8 bits
     uint32_t prefix = 0, mask = 0;
@@ -161,17 +350,27 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(const float *__restri
         const int bins = pass == 2 ? 256 : 4096;
         for (int i = tid; i < bins; i += kTopkThreads) hist[i] = 0;
         __syncthreads();
-        // 8 loads in flight per thread before their atomics
-        for (int s0 = tid; s0 < L; s0 += 8 * kTopkThreads) {
-            uint32_t u[8];
+        if constexpr (NR > 0) {
+            // a fresh copy of the step count per pass keeps the compiler from
+            // holding NR loop-invariant conditions in scalar registers
+            asm volatile("" : "+s"(nch));
+#pragma clang loop unroll(full)
+            for (int i = 0; i < NR; i++)   // key 0 adds to digit 0, below every real key's digit
+                if (i < nch) hist_add(hist, (int)((uc[i] >> shift) & (bins - 1)), (uc[i] & mask) == prefix);
+        } else {
+            // 8 loads in flight per thread before their atomics
+            for (int s0 = tid; s0 < L; s0 += 8 * kTopkThreads) {
+                uint32_t u[8];
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const int s = s0 + i * kTopkThreads;
-                u[i] = s < L ? order_key(sc[s]) : 0u;
-            }
+                for (int i = 0; i < 8; i++) {
+                    const int s = s0 + i * kTopkThreads;
+                    u[i] = s < L ? order_key(sc[s]) : 0u;
+                }
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                if (s0 + i * kTopkThreads < L && (u[i] & mask) == prefix) atomicAdd(&hist[(u[i] >> shift) & (bins - 1)], 1);
+                for (int i = 0; i < 8; i++) {
+                    if (s0 + i * kTopkThreads < L && (u[i] & mask) == prefix)
+                        atomicAdd(&hist[(u[i] >> shift) & (bins - 1)], 1);
+                }
             }
         }
         __syncthreads();
@@ -199,23 +398,32 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(const float *__restri
         mask |= (uint32_t)(bins - 1) << shift;
         __syncthreads();
     }
-    // ordered compaction: wave w takes a contiguous 64-aligned range, reads it
-    // coalesced, counts (ballots), then writes its kept positions in order
-    const int per = ((L + kWaves - 1) / kWaves + 63) / 64 * 64;
-    const int lo = min(L, wave * per), hi = min(L, lo + per);
+    // ordered compaction: each wave counts its range (ballots), then writes
+    // its kept positions in order after those of the waves before it
     int ngt = 0, neq = 0;
-    for (int i0 = lo; i0 < hi; i0 += 4 * 64) {
-        uint32_t u[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int s = i0 + 64 * i + lane;
-            u[i] = s < hi ? order_key(sc[s]) : 0u;
+    if constexpr (NR > 0) {
+        asm volatile("" : "+s"(nch));
+#pragma clang loop unroll(full)
+        for (int i = 0; i < NR; i++) {
+            if (i < nch) {
+                ngt += __popcll(__ballot(uc[i] > prefix));
+                neq += __popcll(__ballot(uc[i] == prefix));
+            }
         }
+    } else {
+        for (int i0 = lo; i0 < hi; i0 += 4 * 64) {
+            uint32_t u[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int s = i0 + 64 * i + lane;
-            ngt += __popcll(__ballot(s < hi && u[i] > prefix));
-            neq += __popcll(__ballot(s < hi && u[i] == prefix));
+            for (int i = 0; i < 4; i++) {
+                const int s = i0 + 64 * i + lane;
+                u[i] = s < hi ? order_key(sc[s]) : 0u;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int s = i0 + 64 * i + lane;
+                ngt += __popcll(__ballot(s < hi && u[i] > prefix));
+                neq += __popcll(__ballot(s < hi && u[i] == prefix));
+            }
         }
     }
     if (lane == 0) {
@@ -230,28 +438,33 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(const float *__restri
         eq_before += weq[w];
     }
     const int take_eq = max(0, min(neq, remain - eq_before));
-    const unsigned long long below = (1ull << lane) - 1ull;
     int eq_seen = 0;
-    for (int i0 = lo; i0 < hi; i0 += 4 * 64) {
-        uint32_t u[4];
+    auto emit = [&](int s, uint32_t u) {   // u = 0 past the range (never kept)
+        const bool g = u > prefix, e = u == prefix;
+        const unsigned long long em = __ballot(e);
+        const bool keep = g || (e && eq_seen + (int)__popcll(em & below) < take_eq);
+        const unsigned long long km = __ballot(keep);
+        if (keep) out[pos + __popcll(km & below)] = s;
+        pos += __popcll(km);
+        eq_seen += __popcll(em);
+    };
+    if constexpr (NR > 0) {
+        asm volatile("" : "+s"(nch));
+#pragma clang loop unroll(full)
+        for (int i = 0; i < NR; i++)
+            if (i < nch) emit(lo + 64 * i + lane, uc[i]);
+    } else {
+        for (int i0 = lo; i0 < hi; i0 += 4 * 64) {
+            uint32_t u[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int s = i0 + 64 * i + lane;
-            u[i] = s < hi ? order_key(sc[s]) : 0u;
-        }
+            for (int i = 0; i < 4; i++) {
+                const int s = i0 + 64 * i + lane;
+                u[i] = s < hi ? order_key(sc[s]) : 0u;
+            }
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int s = i0 + 64 * i + lane;
-            const bool g = s < hi && u[i] > prefix, e = s < hi && u[i] == prefix;
-            const unsigned long long em = __ballot(e);
-            const bool keep = g || (e && eq_seen + __popcll(em & below) < take_eq);
-            const unsigned long long km = __ballot(keep);
-            if (keep) out[pos + __popcll(km & below)] = s;
-            pos += __popcll(km);
-            eq_seen += __popcll(em);
+            for (int i = 0; i < 4; i++) emit(i0 + 64 * i + lane, u[i]);
         }
     }
-    (void)tid;
 }
 
 template <int DK, int DV>
@@ -427,7 +640,12 @@ hipError_t launch_dsa_select(const Dims &d, int HI, int DI, int topk, const int3
     else hipLaunchKernelGGL(k_dsa_index<8>, grid, dim3(kThreads), 0, s, qi, wi, ki, seq_lens, scores, d.T, HI, DI, pf, row0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_dsa_topk, dim3(rows), dim3(kTopkThreads), 0, s, scores, seq_lens, sel, d.T, topk, pf, row0);
+    // register-cached selection while a row fits in 64 scores per lane
+    const dim3 tg(rows), tb(kTopkThreads);
+    if (d.T <= 16 * kTopkThreads) hipLaunchKernelGGL(k_dsa_topk<16>, tg, tb, 0, s, scores, seq_lens, sel, d.T, topk, pf, row0);
+    else if (d.T <= 32 * kTopkThreads) hipLaunchKernelGGL(k_dsa_topk<32>, tg, tb, 0, s, scores, seq_lens, sel, d.T, topk, pf, row0);
+    else if (d.T <= 64 * kTopkThreads) hipLaunchKernelGGL(k_dsa_topk<64>, tg, tb, 0, s, scores, seq_lens, sel, d.T, topk, pf, row0);
+    else hipLaunchKernelGGL(k_dsa_topk<0>, tg, tb, 0, s, scores, seq_lens, sel, d.T, topk, pf, row0);
     return hipGetLastError();
 }
 

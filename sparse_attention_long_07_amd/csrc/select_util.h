@@ -209,7 +209,7 @@ __device__ __forceinline__ void wave_select_topn_fast(const float *S, int jcur, 
     const int nabove = __popcll(__ballot(above));
     const bool tie = have && cv.x == sk;
     const uint64_t tb = __ballot(tie);
-    const bool take = above || (tie && __popcll(tb & lt) < k - nabove);
+    const bool take = above || (tie && (int)__popcll(tb & lt) < k - nabove);
     // Here jc >= 2, so the forced blocks are 0 < (chosen blocks) < jc-1 < jc:
     // out = 0, the k chosen blocks ascending, jc-1, jc.
     const uint64_t tk = __ballot(take);

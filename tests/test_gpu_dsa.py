@@ -152,6 +152,11 @@ def test_dsa_decode_full_size_sampled():
         ref = dsa.attend(q[b], k[b], v[b], sel[b], s.G, scale)
         assert np.abs(np64(o[b]) - ref).max() <= out_tol(s, ref), ("own selection", b)
     ref_sel = np.stack(ref_sel)
+    # the selection of every other sequence against the oracle's scores too
+    QI, WI, KI = np64(ix["q_idx"]), np64(ix["w_idx"]), np64(ix["k_idx"])
+    for b in range(4, s.B):
+        sc = dsa.index_scores(QI[b], WI[b], KI[b], s.T)
+        _check_selection(sc, QI[b], WI[b], KI[b], s.T, sel[b], 2048, ("full", b))
     sel_in = torch.full((s.B, 2048), -1, dtype=torch.int32, device="cuda")
     sel_in[:4] = torch.from_numpy(ref_sel.astype(np.int32)).cuda()
     sel_in[4:] = torch.from_numpy(sel[4:]).cuda()
@@ -163,6 +168,38 @@ def test_dsa_decode_full_size_sampled():
     for b in range(4):
         ref = dsa.attend(q[b], k[b], v[b], ref_sel[b], s.G, scale)
         assert np.abs(np64(o2[b]) - ref).max() <= out_tol(s, ref), b
+
+
+@pytest.mark.parametrize("T,ncls", [(3000, 5), (20000, 5), (40000, 5), (40000, 2), (70000, 5)])
+def test_dsa_decode_selection_ties(T, ncls):
+    """Selection with massive exact ties: every cached indexer key is one of
+    `ncls` rows, so a sequence's scores take that many values (identical bits
+    on the GPU, whose every key runs the same products) and the k-th score is
+    shared by thousands of positions; the list must be exactly the oracle's,
+    which takes the tied positions lowest first.  The capacities span the
+    selector's register-cached forms (16, 32 and 64 scores per lane; with two
+    classes of 20,000 the candidates overflow the LDS list and the full passes
+    run) and its re-reading form (T above 65,536)."""
+    s = NSAShape(2, T, 1, 16, 64, 64)
+    say("dsa ties", s, ncls)
+    hi, di, topk = 4, 64, 2048
+    ix = make_dsa_indexer(s, 87, "cuda", hi, di)
+    base = ix["k_idx"][:, :ncls].clone()
+    reps = torch.arange(T, device="cuda") % ncls
+    ix["k_idx"] = base[:, reps].contiguous()
+    lens = [T, T // 2 + 7]
+    x = make_decode(s, 88, "cuda", seq_lens=lens)
+    sel, _ = nsa.dsa_decode(s, hi, di, topk, x["seq_lens"], ix["q_idx"], ix["w_idx"], ix["k_idx"], x["q"], x["k"],
+                            x["v"])
+    torch.cuda.synchronize()
+    sel = sel.cpu().numpy()
+    qi, wi, ki = np64(ix["q_idx"]), np64(ix["w_idx"]), np64(ix["k_idx"])
+    for b in range(s.B):
+        L = lens[b]
+        sc = dsa.index_scores(qi[b], wi[b], ki[b], L)
+        vals = np.unique(sc)
+        assert len(vals) <= ncls
+        assert np.array_equal(sel[b], dsa.select_topk(sc, topk)), (T, b)
 
 
 PREFILL = [
