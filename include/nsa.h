@@ -311,11 +311,12 @@ nsa_status nsa_backward(const nsa_config *cfg, const void *q, const void *k, con
  * sel_out and ws may be NULL; otherwise sel_out receives the selection and
  * ws holds nsa_workspace_bytes(cfg, NSA_OP_DSA_DECODE) bytes.  A non-NULL ws
  * must be 256-byte aligned (else NSA_ERR_ALIGN).  A ws of at least
- * 4*B*H_kv*2*(32 + 16*d_v) bytes (always the case with the size
- * nsa_workspace_bytes reports) also serves the attention: each KV group's
- * slots are then split over two workgroups and merged, which changes only the
- * fp32 summation order; with sel_in and a NULL or smaller ws one workgroup
- * takes each KV group.  q_idx, k_idx, q, k, v, o 16-byte aligned. */
+ * 4*B*H_kv*S*(32 + 16*d_v) bytes also serves the attention: each KV group's
+ * slots are then split over S workgroups and merged, which changes only the
+ * fp32 summation order; S = 4 when ws holds that much (always the case with
+ * the size nsa_workspace_bytes reports), else S = 2 when it holds that much;
+ * with sel_in and a NULL or smaller ws one workgroup takes each KV group.
+ * q_idx, k_idx, q, k, v, o 16-byte aligned. */
 nsa_status nsa_dsa_decode(const nsa_config *cfg, int32_t idx_heads, int32_t idx_dim, int32_t topk,
                           const int32_t *seq_lens, const void *q_idx, const void *w_idx, const void *k_idx,
                           const void *q, const void *k, const void *v, const int32_t *sel_in, int32_t *sel_out,

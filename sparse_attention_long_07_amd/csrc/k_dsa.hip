@@ -24,11 +24,12 @@
 //              S^T = K Q^T on gathered K rows (16x16x32 MFMA, the 16 heads
 //              as N), online softmax, O^T += V^T P^T with V staged in a
 //              wave-private LDS buffer and read by transposing reads; the
-//              waves' (max, sum, O) are merged in LDS.  With nsplit = 2 two
-//              workgroups on two CUs take the two halves of the slots and
-//              leave (max, sum, unnormalised O) per head in a workspace that
+//              waves' (max, sum, O) are merged in LDS.  With nsplit = 2 or 4
+//              that many workgroups take equal shares of the slots and leave
+//              (max, sum, unnormalised O) per head in a workspace that
 //              k_dsa_merge combines (decode: 128 workgroups would otherwise
-//              leave half the chip idle).
+//              leave half the chip idle; with 4 the selection share in LDS is
+//              small enough for two workgroups per CU).
 #include <algorithm>
 
 #include "mfma_util.h"
@@ -87,22 +88,23 @@ __global__ __launch_bounds__(kThreads) void k_dsa_index(const uint16_t *__restri
         qb[c] = li < HI && e0 < DI ? ld16(q_idx + ((long)b * HI + li) * DI + e0) : z;
     }
     const float wj = li < HI ? bf2f(w_idx[(long)b * HI + li]) : 0.f;
+    // the row sums leave every lane of a row with all four sums, so lane
+    // (li, lg) can store key 16 (li / 4) + 4 lg + li % 4: one store for the
+    // wave's 64 keys
+    float mine = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; kt++) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < NC; c++) acc = mfma16(as_bf16x8(ka[kt][c]), as_bf16x8(qb[c]), acc);
-        float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; e++) v[e] = row_sum16(wj * fmaxf(acc[e], 0.f));
-        if (li == 0) {
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int s = key0 + 16 * kt + 4 * lg + e;
-                if (s < L) srow[s] = v[e];
-            }
+        for (int e = 0; e < 4; e++) {
+            const float v = row_sum16(wj * fmaxf(acc[e], 0.f));
+            if (li == 4 * kt + e) mine = v;
         }
     }
+    const int s = key0 + 16 * (li >> 2) + 4 * lg + (li & 3);
+    if (s < L) srow[s] = mine;
 }
 
 // larger float -> larger key (no NaN among the scores)
@@ -263,29 +265,35 @@ __global__ __launch_bounds__(kTopkThreads) void k_dsa_topk(const float *__restri
         // about 4 standard deviations above the sample's expected share of k
         find_digit(4096, 20, 0u, topk / 8 + topk / 32 + 16);
         const uint32_t tau = s_found ? max(s_prefix, 1u) : 1u;   // key 0 (past the range) never qualifies
-        // (b) candidates into LDS: each wave counts, reserves its slots, writes
-        // (key 0, past the range, is below tau >= 1, so no range test is needed)
-        int cw = 0;
+        // (b) candidates into LDS: each lane counts its own, a wave scan gives
+        // each lane its offset after one reservation per wave, and each lane
+        // writes its candidates in turn (the list's order does not matter).
+        // Key 0, past the range, is below tau >= 1: no range test is needed.
+        int cl = 0;
 #pragma clang loop unroll(full)
-        for (int i = 0; i < NR; i++) cw += __popcll(__ballot(uc[i] >= tau));
+        for (int i = 0; i < NR; i++) cl += uc[i] >= tau ? 1 : 0;
+        int x = cl;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o);
+            if (lane >= o) x += y;
+        }
         int base = 0;
-        if (lane == 0) base = atomicAdd(&s_cnt, cw);
-        base = __builtin_amdgcn_readfirstlane(base);
+        if (lane == 63) base = atomicAdd(&s_cnt, x);   // x is the wave's total in lane 63
+        int off = __shfl(base, 63) + x - cl;
         int pos0 = lo + lane;
         uint32_t tau2 = tau;
-        // positions formed at the writes, and the comparisons made again rather
-        // than NR ballots held in scalar registers from the counting loop
+        // positions formed at the writes, and the comparisons made again
+        // rather than NR flags held from the counting loop
         asm volatile("" : "+v"(pos0), "+v"(tau2));
 #pragma clang loop unroll(full)
         for (int i = 0; i < NR; i++) {
             const bool c = uc[i] >= tau2;
-            const unsigned long long m = __ballot(c);
-            const int at = base + (int)__popcll(m & below);
-            if (c && at < kCap) {
-                cand_k[at] = uc[i];
-                cand_p[at] = (uint16_t)(pos0 + 64 * i);
+            if (c && off < kCap) {
+                cand_k[off] = uc[i];
+                cand_p[off] = (uint16_t)(pos0 + 64 * i);
             }
-            base += __popcll(m);
+            off += c ? 1 : 0;
         }
         __syncthreads();
         const int C = s_cnt;
@@ -479,12 +487,14 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_dsa_attn(const uint16_t *__
     constexpr int kStage = 32 * VS;                       // bf16 per wave
     constexpr int kMerge = 16 * DV * (int)sizeof(float) / 2;   // the same bytes, counted in bf16
     __shared__ __align__(16) uint16_t vst[kAttnWaves][kStage > kMerge ? kStage : kMerge];
-    __shared__ int ss[8192];
+    extern __shared__ int ss[];   // this workgroup's share of the selection (dynamic: ceil(topk / nsplit))
     __shared__ float s_m[kAttnWaves][16], s_l[kAttnWaves][16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
     const int bg = blockIdx.x / nsplit, half = blockIdx.x % nsplit, b = bg / Hkv, g = bg % Hkv;
-    for (int i = tid; i < topk; i += kAttnWaves * 64) ss[i] = sel[(long)b * topk + i];
+    const int span = (topk + nsplit - 1) / nsplit;
+    const int h0 = half * span, h1 = min(topk, h0 + span);
+    for (int i = tid; i < h1 - h0; i += kAttnWaves * 64) ss[i] = sel[(long)b * topk + h0 + i];
     // B operand Q^T: head li of the group, columns 32 c + 8 lg .. +7
     u32x4 qf[NQ];
     const long qrow = ((long)b * Hkv * 16 + g * 16 + li) * DK;
@@ -500,8 +510,6 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_dsa_attn(const uint16_t *__
 #pragma unroll
     for (int i = 0; i < NO; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.f;
-    const int span = (topk + nsplit - 1) / nsplit;
-    const int h0 = half * span, h1 = min(topk, h0 + span);
     const int per = (max(h1 - h0, 0) + kAttnWaves - 1) / kAttnWaves;
     const int beg = h0 + wave * per, end = min(h1, beg + per);
     const int trow = li >> 2, tcol = 4 * (li & 3);
@@ -512,7 +520,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_dsa_attn(const uint16_t *__
             // A operand K: slot c0 + 16 kt + li (an empty slot, or an entry
             // outside the cache, reads token 0 and is masked below)
             const int slot = c0 + 16 * kt + li;
-            const int tok = slot < end ? ss[slot] : -1;
+            const int tok = slot < end ? ss[slot - h0] : -1;
             const int tl = tok >= 0 && tok < T ? tok : 0;
             f32x4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -523,7 +531,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_dsa_attn(const uint16_t *__
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int sl = c0 + 16 * kt + 4 * lg + e;
-                const bool ok = sl < end && ss[sl] >= 0 && ss[sl] < T;
+                const bool ok = sl < end && ss[sl - h0] >= 0 && ss[sl - h0] < T;
                 sc[kt][e] = ok ? S[e] * sl2 : -INFINITY;
             }
         }
@@ -590,7 +598,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_dsa_attn(const uint16_t *__
         if (nsplit == 1) {
             o[((long)b * Hkv * 16 + g * 16) * DV + i] = f2bf(den > 0.f ? num / den : 0.f);
         } else {
-            // [16 max][16 sum][16][DV] unnormalised O, per (group, half)
+            // [16 max][16 sum][16][DV] unnormalised O, per (group, split)
             float *pw = part + (long)blockIdx.x * (32 + 16 * DV);
             if (i % DV == 0) {
                 pw[h] = M;
@@ -601,21 +609,24 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_dsa_attn(const uint16_t *__
     }
 }
 
-// o = the two halves' (max, sum, O) combined, per (sequence, KV group)
+// o = the splits' (max, sum, O) combined, per (sequence, KV group)
 template <int DV>
-__global__ __launch_bounds__(kThreads) void k_dsa_merge(const float *__restrict__ part, uint16_t *__restrict__ o)
+__global__ __launch_bounds__(kThreads) void k_dsa_merge(const float *__restrict__ part, uint16_t *__restrict__ o,
+                                                        int nsplit)
 {
     const int bg = blockIdx.x;
-    const float *p0 = part + (long)(2 * bg) * (32 + 16 * DV), *p1 = p0 + (32 + 16 * DV);
-    {
-        const int i = blockIdx.y * kThreads + threadIdx.x, h = i / DV;   // grid.y = 16 DV / 256
-        const float m0 = p0[h], m1 = p1[h], M = fmaxf(m0, m1);
-        const float f0 = m0 == -INFINITY ? 0.f : fast_exp2(m0 - M);
-        const float f1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - M);
-        const float num = __builtin_fmaf(f1, p1[32 + i], f0 * p0[32 + i]);
-        const float den = __builtin_fmaf(f1, p1[16 + h], f0 * p0[16 + h]);
-        o[(long)bg * 16 * DV + i] = f2bf(den > 0.f ? num / den : 0.f);
+    const float *p0 = part + (long)(nsplit * bg) * (32 + 16 * DV);
+    const int i = blockIdx.y * kThreads + threadIdx.x, h = i / DV;   // grid.y = 16 DV / 256
+    float M = -INFINITY;
+    for (int r = 0; r < nsplit; r++) M = fmaxf(M, p0[r * (32 + 16 * DV) + h]);
+    float num = 0.f, den = 0.f;
+    for (int r = 0; r < nsplit; r++) {
+        const float *pr = p0 + r * (32 + 16 * DV);
+        const float f = pr[h] == -INFINITY ? 0.f : fast_exp2(pr[h] - M);
+        num = __builtin_fmaf(f, pr[32 + i], num);
+        den = __builtin_fmaf(f, pr[16 + h], den);
     }
+    o[(long)bg * 16 * DV + i] = f2bf(den > 0.f ? num / den : 0.f);
 }
 
 }  // namespace
@@ -656,27 +667,28 @@ int dsa_prefill_chunk_rows(const Dims &d)
     return (int)std::max(1L, std::min(total, fit));
 }
 
-size_t dsa_split_bytes(const Dims &d)
+size_t dsa_split_bytes(const Dims &d, int nsplit)
 {
-    return sizeof(float) * (size_t)d.B * d.Hkv * 2 * (32 + 16 * (size_t)d.dv);
+    return sizeof(float) * (size_t)d.B * d.Hkv * nsplit * (32 + 16 * (size_t)d.dv);
 }
 
 hipError_t launch_dsa_attn(const Dims &d, int topk, const void *q, const void *k, const void *v, const int32_t *sel,
-                           void *o, hipStream_t s, bool prefill, void *part)
+                           void *o, hipStream_t s, bool prefill, void *part, int nsplit)
 {
-    const int pf = prefill ? 1 : 0, ns = part ? 2 : 1;
+    const int pf = prefill ? 1 : 0, ns = part ? nsplit : 1;
     const long groups = (prefill ? (long)d.B * d.T : (long)d.B) * d.Hkv;
     const dim3 grid((unsigned)(groups * ns)), block(kAttnWaves * 64);
+    const size_t lds = sizeof(int) * (size_t)((topk + ns - 1) / ns);
     const uint16_t *qq = (const uint16_t *)q, *kk = (const uint16_t *)k, *vv = (const uint16_t *)v;
     uint16_t *oo = (uint16_t *)o;
     float *pp = (float *)part;
-    if (d.dk == 192) hipLaunchKernelGGL((k_dsa_attn<192, 128>), grid, block, 0, s, qq, kk, vv, sel, oo, d.T, d.Hkv, topk, d.scale, pf, ns, pp);
-    else if (d.dk == 128) hipLaunchKernelGGL((k_dsa_attn<128, 128>), grid, block, 0, s, qq, kk, vv, sel, oo, d.T, d.Hkv, topk, d.scale, pf, ns, pp);
-    else hipLaunchKernelGGL((k_dsa_attn<64, 64>), grid, block, 0, s, qq, kk, vv, sel, oo, d.T, d.Hkv, topk, d.scale, pf, ns, pp);
+    if (d.dk == 192) hipLaunchKernelGGL((k_dsa_attn<192, 128>), grid, block, lds, s, qq, kk, vv, sel, oo, d.T, d.Hkv, topk, d.scale, pf, ns, pp);
+    else if (d.dk == 128) hipLaunchKernelGGL((k_dsa_attn<128, 128>), grid, block, lds, s, qq, kk, vv, sel, oo, d.T, d.Hkv, topk, d.scale, pf, ns, pp);
+    else hipLaunchKernelGGL((k_dsa_attn<64, 64>), grid, block, lds, s, qq, kk, vv, sel, oo, d.T, d.Hkv, topk, d.scale, pf, ns, pp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1) return e;
-    if (d.dv == 128) hipLaunchKernelGGL(k_dsa_merge<128>, dim3((unsigned)groups, 16 * 128 / kThreads), dim3(kThreads), 0, s, pp, oo);
-    else hipLaunchKernelGGL(k_dsa_merge<64>, dim3((unsigned)groups, 16 * 64 / kThreads), dim3(kThreads), 0, s, pp, oo);
+    if (d.dv == 128) hipLaunchKernelGGL(k_dsa_merge<128>, dim3((unsigned)groups, 16 * 128 / kThreads), dim3(kThreads), 0, s, pp, oo, ns);
+    else hipLaunchKernelGGL(k_dsa_merge<64>, dim3((unsigned)groups, 16 * 64 / kThreads), dim3(kThreads), 0, s, pp, oo, ns);
     return hipGetLastError();
 }
 

@@ -138,8 +138,9 @@ size_t nsa_workspace_bytes(const nsa_config *cfg, int op)
     case NSA_OP_BACKWARD:
         return backward_layout(d, nullptr, nullptr);
     case NSA_OP_DSA_DECODE:
-        // the indexer scores, later reused for the two-way split's partials
-        return dsa_supported(d) ? align_up(std::max(sizeof(float) * (size_t)d.B * d.T, dsa_split_bytes(d))) : 0;
+        // the indexer scores, later reused for the split attention's partials
+        return dsa_supported(d) ? align_up(std::max(sizeof(float) * (size_t)d.B * d.T, dsa_split_bytes(d, kDsaMaxSplit)))
+                                : 0;
     case NSA_OP_DSA_PREFILL:
         // the indexer scores of one chunk of rows
         return dsa_supported(d) ? align_up(sizeof(float) * (size_t)dsa_prefill_chunk_rows(d) * d.T) : 0;
@@ -216,9 +217,10 @@ nsa_status nsa_dsa_decode(const nsa_config *cfg, int32_t idx_heads, int32_t idx_
         NSA_TRY(launch_dsa_select(d, idx_heads, idx_dim, topk, seq_lens, q_idx, w_idx, k_idx, (float *)ws, sel_out, s));
     }
     // a workspace that holds the partial results (the scores are consumed by
-    // then, on the same stream) lets two workgroups share each KV group
-    void *part = ws && ws_bytes >= dsa_split_bytes(d) ? ws : nullptr;
-    NSA_TRY(launch_dsa_attn(d, topk, q, k, v, sel_in ? sel_in : sel_out, o, s, false, part));
+    // then, on the same stream) lets four (or two) workgroups share each KV
+    // group's slots
+    const int ns = !ws ? 1 : ws_bytes >= dsa_split_bytes(d, 4) ? 4 : ws_bytes >= dsa_split_bytes(d, 2) ? 2 : 1;
+    NSA_TRY(launch_dsa_attn(d, topk, q, k, v, sel_in ? sel_in : sel_out, o, s, false, ns > 1 ? ws : nullptr, ns));
     return NSA_OK;
 }
 

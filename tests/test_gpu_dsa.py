@@ -101,19 +101,19 @@ def test_dsa_decode_parity(name, s, lens, topk, hi, di):
     assert n_same >= 1, name
 
 
-def _split_ws(s):
-    """A workspace that holds the two-way split's partial results: per (sequence,
-    KV group, half) 16 maxima, 16 sums and 16 x d_v outputs in fp32."""
-    return torch.empty(4 * s.B * s.Hkv * 2 * (32 + 16 * s.dv), dtype=torch.uint8, device="cuda")
+def _split_ws(s, n):
+    """A workspace that holds an n-way split's partial results: per (sequence,
+    KV group, share) 16 maxima, 16 sums and 16 x d_v outputs in fp32."""
+    return torch.empty(4 * s.B * s.Hkv * n * (32 + 16 * s.dv), dtype=torch.uint8, device="cuda")
 
 
-@pytest.mark.parametrize("split", [False, True], ids=["one_wg", "split2"])
+@pytest.mark.parametrize("split", [1, 2, 4], ids=["one_wg", "split2", "split4"])
 @pytest.mark.parametrize("name,s,lens,topk,hi,di", CASES, ids=[c[0] for c in CASES])
 def test_dsa_attention_with_injected_selection(name, s, lens, topk, hi, di, split):
     """The oracle's selection injected: attention parity independent of
-    selection near-ties; with a workspace each KV group's slots run as two
-    halves merged afterwards."""
-    say("dsa attention", name, s, lens, topk, "split" if split else "")
+    selection near-ties; with a workspace that holds an n-way split's partials
+    each KV group's slots run as n shares merged afterwards."""
+    say("dsa attention", name, s, lens, topk, "split", split)
     x = make_decode(s, 83, "cuda", seq_lens=lens)
     ix = make_dsa_indexer(s, 84, "cuda", hi, di)
     qi, wi, ki = np64(ix["q_idx"]), np64(ix["w_idx"]), np64(ix["k_idx"])
@@ -121,7 +121,7 @@ def test_dsa_attention_with_injected_selection(name, s, lens, topk, hi, di, spli
                                     [_clamp_len(L, s.T) for L in lens], topk, s.G, 1 / math.sqrt(s.dk))
     sel_in = torch.from_numpy(ref_sel.astype(np.int32)).cuda()
     _, o = nsa.dsa_decode(s, hi, di, topk, x["seq_lens"], None, None, None, x["q"], x["k"], x["v"], sel_in=sel_in,
-                          ws=_split_ws(s) if split else None)
+                          ws=_split_ws(s, split) if split > 1 else None)
     torch.cuda.synchronize()
     got = np64(o)
     assert np.all(np.isfinite(got))
@@ -131,7 +131,7 @@ def test_dsa_attention_with_injected_selection(name, s, lens, topk, hi, di, spli
 def test_dsa_decode_full_size_sampled():
     """32 sequences at 65,536-token caches (the NSA decode workload's shape),
     top-2,048 with 4 indexer heads of 64, as bench.py times it (selection
-    into the workspace, then the two-way split attention reusing it): the
+    into the workspace, then the four-way split attention reusing it): the
     selection of 4 sequences against the oracle, their output against the
     oracle's attention over the GPU's selection, and the output of every
     other sequence equal bit for bit to the split attention run with the same
@@ -161,7 +161,7 @@ def test_dsa_decode_full_size_sampled():
     sel_in[:4] = torch.from_numpy(ref_sel.astype(np.int32)).cuda()
     sel_in[4:] = torch.from_numpy(sel[4:]).cuda()
     _, o2 = nsa.dsa_decode(s, 4, 64, 2048, x["seq_lens"], None, None, None, x["q"], x["k"], x["v"], sel_in=sel_in,
-                           ws=_split_ws(s))
+                           ws=_split_ws(s, 4))
     torch.cuda.synchronize()
     # same selection, same split kernels: the same bits
     assert torch.equal(o[4:], o2[4:])
