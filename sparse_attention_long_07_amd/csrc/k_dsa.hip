@@ -79,7 +79,9 @@ __global__ __launch_bounds__(kThreads) void k_dsa_index(const uint16_t *__restri
 #pragma unroll
         for (int c = 0; c < NC; c++) {
             const int e0 = 32 * c + 8 * lg;
-            ka[kt][c] = e0 < DI ? ld16(k_idx + ((long)cb * T + sl) * DI + e0) : z;
+            // read once per step: a non-temporal load keeps the keys from
+            // displacing other data in the caches
+            ka[kt][c] = e0 < DI ? __builtin_nontemporal_load((const u32x4 *)(k_idx + ((long)cb * T + sl) * DI + e0)) : z;
         }
     }
 #pragma unroll
