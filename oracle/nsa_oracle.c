@@ -538,37 +538,19 @@ static void compress_backward(int BH, int T, int dim, int l, int d, int N, const
     free(dX);
 }
 
-/* Full backward.  Layouts as in the forward; idx [B][Hkv][T][n] is the
- * selection used by the forward.  Gradients are written (not accumulated):
- * dq [B][T][Hq][dk], dk/dv [B][Hkv][T][dk|dv], dwck [dk][l*dk], dpek [l][dk],
- * dwcv [dv][l*dv], dpev [l][dv], dwg [Hq][3][dk], dbg [Hq][3].  The
- * compressed K/V are recomputed from k/v (rounded to bf16 if round_bf16, the
- * rounding being passed straight through in reverse). */
-void orc_backward(const orc_cfg *c, const double *q, const double *k, const double *v, const double *wck,
-                  const double *pek, const double *wcv, const double *pev, const double *wg, const double *bg,
-                  const int *idx, const double *dO, int round_bf16, double *dq, double *dk, double *dv,
-                  double *dwck, double *dpek, double *dwcv, double *dpev, double *dwg, double *dbg)
+/* The three branches and the gates, backward, for given compressed K/V
+ * (kc, vc: [B][Hkv][max(N,1)][dk|dv]).  Writes dq, dwg, dbg and adds into dk,
+ * dv (raw keys) and dkc, dvc (compressed keys); all must start at zero. */
+static void branches_backward(const orc_cfg *c, const double *q, const double *k, const double *v,
+                              const double *kc, const double *vc, const double *wg, const double *bg,
+                              const int *idx, const double *dO, double *dq, double *dk, double *dv,
+                              double *dkc, double *dvc, double *dwg, double *dbg)
 {
     const int B = c->B, T = c->T, Hkv = c->Hkv, G = c->G, Hq = Hkv * G, dk_ = c->dk, dv_ = c->dv, n = c->n;
     const int N = orc_n_cmp(T, c->l, c->d);
     const int Nn = N > 0 ? N : 1;
-    double *kc = (double *)calloc((size_t)B * Hkv * Nn * dk_, sizeof(double));
-    double *vc = (double *)calloc((size_t)B * Hkv * Nn * dv_, sizeof(double));
-    orc_compress(B, Hkv, T, dk_, c->l, c->d, N, round_bf16, k, wck, pek, kc);
-    orc_compress(B, Hkv, T, dv_, c->l, c->d, N, round_bf16, v, wcv, pev, vc);
-    const size_t nq = (size_t)B * T * Hq * dk_, nk = (size_t)B * Hkv * T * dk_, nv = (size_t)B * Hkv * T * dv_;
+    const size_t nk = (size_t)B * Hkv * T * dk_, nv = (size_t)B * Hkv * T * dv_;
     const size_t nkc = (size_t)B * Hkv * Nn * dk_, nvc = (size_t)B * Hkv * Nn * dv_;
-    memset(dq, 0, sizeof(double) * nq);
-    memset(dk, 0, sizeof(double) * nk);
-    memset(dv, 0, sizeof(double) * nv);
-    memset(dwck, 0, sizeof(double) * (size_t)dk_ * c->l * dk_);
-    memset(dpek, 0, sizeof(double) * (size_t)c->l * dk_);
-    memset(dwcv, 0, sizeof(double) * (size_t)dv_ * c->l * dv_);
-    memset(dpev, 0, sizeof(double) * (size_t)c->l * dv_);
-    memset(dwg, 0, sizeof(double) * (size_t)Hq * 3 * dk_);
-    memset(dbg, 0, sizeof(double) * (size_t)Hq * 3);
-    double *dkc = (double *)calloc(nkc, sizeof(double));
-    double *dvc = (double *)calloc(nvc, sizeof(double));
 
 #pragma omp parallel
     {
@@ -671,9 +653,121 @@ void orc_backward(const orc_cfg *c, const double *q, const double *k, const doub
         free(dout); free(o3); free(p); free(rows);
         free(a_dbg); free(a_dwg); free(a_dvc); free(a_dkc); free(a_dv); free(a_dk);
     }
+}
+
+/* Zeroes the gradients the backward writes. */
+static void zero_grads(const orc_cfg *c, double *dq, double *dk, double *dv, double *dwck, double *dpek,
+                       double *dwcv, double *dpev, double *dwg, double *dbg)
+{
+    const int B = c->B, T = c->T, Hkv = c->Hkv, Hq = Hkv * c->G, dk_ = c->dk, dv_ = c->dv;
+    memset(dq, 0, sizeof(double) * (size_t)B * T * Hq * dk_);
+    memset(dk, 0, sizeof(double) * (size_t)B * Hkv * T * dk_);
+    memset(dv, 0, sizeof(double) * (size_t)B * Hkv * T * dv_);
+    memset(dwck, 0, sizeof(double) * (size_t)dk_ * c->l * dk_);
+    memset(dpek, 0, sizeof(double) * (size_t)c->l * dk_);
+    memset(dwcv, 0, sizeof(double) * (size_t)dv_ * c->l * dv_);
+    memset(dpev, 0, sizeof(double) * (size_t)c->l * dv_);
+    memset(dwg, 0, sizeof(double) * (size_t)Hq * 3 * dk_);
+    memset(dbg, 0, sizeof(double) * (size_t)Hq * 3);
+}
+
+/* Full backward.  Layouts as in the forward; idx [B][Hkv][T][n] is the
+ * selection used by the forward.  Gradients are written (not accumulated):
+ * dq [B][T][Hq][dk], dk/dv [B][Hkv][T][dk|dv], dwck [dk][l*dk], dpek [l][dk],
+ * dwcv [dv][l*dv], dpev [l][dv], dwg [Hq][3][dk], dbg [Hq][3].  The
+ * compressed K/V are recomputed from k/v (rounded to bf16 if round_bf16, the
+ * rounding being passed straight through in reverse). */
+void orc_backward(const orc_cfg *c, const double *q, const double *k, const double *v, const double *wck,
+                  const double *pek, const double *wcv, const double *pev, const double *wg, const double *bg,
+                  const int *idx, const double *dO, int round_bf16, double *dq, double *dk, double *dv,
+                  double *dwck, double *dpek, double *dwcv, double *dpev, double *dwg, double *dbg)
+{
+    const int B = c->B, T = c->T, Hkv = c->Hkv, dk_ = c->dk, dv_ = c->dv;
+    const int N = orc_n_cmp(T, c->l, c->d);
+    const int Nn = N > 0 ? N : 1;
+    double *kc = (double *)calloc((size_t)B * Hkv * Nn * dk_, sizeof(double));
+    double *vc = (double *)calloc((size_t)B * Hkv * Nn * dv_, sizeof(double));
+    orc_compress(B, Hkv, T, dk_, c->l, c->d, N, round_bf16, k, wck, pek, kc);
+    orc_compress(B, Hkv, T, dv_, c->l, c->d, N, round_bf16, v, wcv, pev, vc);
+    zero_grads(c, dq, dk, dv, dwck, dpek, dwcv, dpev, dwg, dbg);
+    double *dkc = (double *)calloc((size_t)B * Hkv * Nn * dk_, sizeof(double));
+    double *dvc = (double *)calloc((size_t)B * Hkv * Nn * dv_, sizeof(double));
+    branches_backward(c, q, k, v, kc, vc, wg, bg, idx, dO, dq, dk, dv, dkc, dvc, dwg, dbg);
     if (N > 0) {
         compress_backward(B * Hkv, T, dk_, c->l, c->d, N, k, wck, pek, dkc, dwck, dpek, dk);
         compress_backward(B * Hkv, T, dv_, c->l, c->d, N, v, wcv, pev, dvc, dwcv, dpev, dv);
     }
     free(dvc); free(dkc); free(vc); free(kc);
+}
+
+/* Backward of the two-layer map's second layer for one tensor ([deepdaiv],
+ * token compression: a small network summarises each block; its layers are
+ * those of orc_compress_mlp).  With a [BH][N][dim] the first layer's output
+ * (as the forward rounds it) and dC the gradient of the compressed rows:
+ *   dW2[c][j] += sum_{bh,i} dC[bh][i][c] * max(a[bh][i][j], 0)
+ *   dA[bh][i][j] = (sum_c W2[c][j] * dC[bh][i][c]) * (a[bh][i][j] > 0)
+ * (the ReLU's derivative taken as 0 at 0). */
+static void mlp2_backward(int BH, int N, int dim, const double *a, const double *W2, const double *dC,
+                          double *dW2, double *dA)
+{
+#pragma omp parallel for schedule(static)
+    for (int cc = 0; cc < dim; cc++)
+        for (int j = 0; j < dim; j++) {
+            double acc = 0.0;
+            for (int bh = 0; bh < BH; bh++)
+                for (int i = 0; i < N; i++) {
+                    const double h = a[((size_t)bh * N + i) * dim + j];
+                    acc += dC[((size_t)bh * N + i) * dim + cc] * (h > 0.0 ? h : 0.0);
+                }
+            dW2[(size_t)cc * dim + j] += acc;
+        }
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int bh = 0; bh < BH; bh++)
+        for (int i = 0; i < N; i++) {
+            const double *g = dC + ((size_t)bh * N + i) * dim;
+            const double *ar = a + ((size_t)bh * N + i) * dim;
+            double *out = dA + ((size_t)bh * N + i) * dim;
+            for (int j = 0; j < dim; j++) {
+                double acc = 0.0;
+                for (int cc = 0; cc < dim; cc++) acc += W2[(size_t)cc * dim + j] * g[cc];
+                out[j] = ar[j] > 0.0 ? acc : 0.0;
+            }
+        }
+}
+
+/* Full backward with the two-layer compression map (orc_compress_mlp) for K
+ * and V: as orc_backward, the first layer's weights and position encodings
+ * taking the place of the linear map's (dw1k, dpek, dw1v, dpev), plus the
+ * second layers' gradients dw2k [dk][dk], dw2v [dv][dv].  The hidden layer
+ * and the compressed K/V are recomputed from k/v, each rounded to bf16 if
+ * round_bf16, the roundings passed straight through in reverse. */
+void orc_backward_mlp(const orc_cfg *c, const double *q, const double *k, const double *v, const double *w1k,
+                      const double *pek, const double *w2k, const double *w1v, const double *pev,
+                      const double *w2v, const double *wg, const double *bg, const int *idx, const double *dO,
+                      int round_bf16, double *dq, double *dk, double *dv, double *dw1k, double *dpek,
+                      double *dw2k, double *dw1v, double *dpev, double *dw2v, double *dwg, double *dbg)
+{
+    const int B = c->B, T = c->T, Hkv = c->Hkv, dk_ = c->dk, dv_ = c->dv;
+    const int N = orc_n_cmp(T, c->l, c->d);
+    const int Nn = N > 0 ? N : 1;
+    const size_t nkc = (size_t)B * Hkv * Nn * dk_, nvc = (size_t)B * Hkv * Nn * dv_;
+    double *ak = (double *)calloc(nkc, sizeof(double)), *av = (double *)calloc(nvc, sizeof(double));
+    double *kc = (double *)calloc(nkc, sizeof(double)), *vc = (double *)calloc(nvc, sizeof(double));
+    orc_compress(B, Hkv, T, dk_, c->l, c->d, N, round_bf16, k, w1k, pek, ak);
+    orc_compress(B, Hkv, T, dv_, c->l, c->d, N, round_bf16, v, w1v, pev, av);
+    orc_compress_mlp(B, Hkv, T, dk_, c->l, c->d, N, round_bf16, k, w1k, pek, w2k, kc);
+    orc_compress_mlp(B, Hkv, T, dv_, c->l, c->d, N, round_bf16, v, w1v, pev, w2v, vc);
+    zero_grads(c, dq, dk, dv, dw1k, dpek, dw1v, dpev, dwg, dbg);
+    memset(dw2k, 0, sizeof(double) * (size_t)dk_ * dk_);
+    memset(dw2v, 0, sizeof(double) * (size_t)dv_ * dv_);
+    double *dkc = (double *)calloc(nkc, sizeof(double)), *dvc = (double *)calloc(nvc, sizeof(double));
+    double *dak = (double *)calloc(nkc, sizeof(double)), *dav = (double *)calloc(nvc, sizeof(double));
+    branches_backward(c, q, k, v, kc, vc, wg, bg, idx, dO, dq, dk, dv, dkc, dvc, dwg, dbg);
+    if (N > 0) {
+        mlp2_backward(B * Hkv, N, dk_, ak, w2k, dkc, dw2k, dak);
+        mlp2_backward(B * Hkv, N, dv_, av, w2v, dvc, dw2v, dav);
+        compress_backward(B * Hkv, T, dk_, c->l, c->d, N, k, w1k, pek, dak, dw1k, dpek, dk);
+        compress_backward(B * Hkv, T, dv_, c->l, c->d, N, v, w1v, pev, dav, dw1v, dpev, dv);
+    }
+    free(dav); free(dak); free(dvc); free(dkc); free(vc); free(kc); free(av); free(ak);
 }

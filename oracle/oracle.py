@@ -61,6 +61,8 @@ def _load():
                                          _dp, _dp]
         lib.orc_backward.restype = None
         lib.orc_backward.argtypes = [ctypes.POINTER(_Cfg)] + [_dp] * 9 + [_ip, _dp, ctypes.c_int] + [_dp] * 9
+        lib.orc_backward_mlp.restype = None
+        lib.orc_backward_mlp.argtypes = [ctypes.POINTER(_Cfg)] + [_dp] * 11 + [_ip, _dp, ctypes.c_int] + [_dp] * 11
         lib.orc_select.restype = ctypes.c_int
         lib.orc_select.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int, _dp, _ip]
         _lib = lib
@@ -273,4 +275,33 @@ def backward(cfg: Cfg, q, k, v, wck, pek, wcv, pev, wg, bg, idx, dO, round_bf16:
     _load().orc_backward(ctypes.byref(c), *[a.ctypes.data_as(_dp) for a in arrs], ip, dop, int(round_bf16),
                          *[out[n].ctypes.data_as(_dp) for n in ("dq", "dk", "dv", "dwck", "dpek", "dwcv",
                                                                  "dpev", "dwg", "dbg")])
+    return out
+
+
+def backward_mlp(cfg: Cfg, q, k, v, w1k, pek, w2k, w1v, pev, w2v, wg, bg, idx, dO, round_bf16: bool = False):
+    """backward() with the two-layer compression map of compress_mlp for K
+    and V: w1k [dk,l*dk], pek [l,dk], w2k [dk,dk], w1v [dv,l*dv], pev [l,dv],
+    w2v [dv,dv].  Returns dict dq, dk, dv, dw1k, dpek, dw2k, dw1v, dpev, dw2v,
+    dwg, dbg (input layouts); the hidden layer and the compressed K/V are
+    recomputed (rounded to bf16 when round_bf16, the roundings passed straight
+    through in reverse)."""
+    B, T, Hkv, Hq, dk, dv, l = cfg.B, cfg.T, cfg.Hkv, cfg.Hq, cfg.dk, cfg.dv, cfg.l
+    arrs = []
+    for a, shp in ((q, (B, T, Hq, dk)), (k, (B, Hkv, T, dk)), (v, (B, Hkv, T, dv)), (w1k, (dk, l * dk)),
+                   (pek, (l, dk)), (w2k, (dk, dk)), (w1v, (dv, l * dv)), (pev, (l, dv)), (w2v, (dv, dv)),
+                   (wg, (Hq, 3, dk)), (bg, (Hq, 3))):
+        a, _ = _d(a)
+        assert a.shape == shp, (a.shape, shp)
+        arrs.append(a)
+    idx, ip = _i(idx)
+    assert idx.shape == (B, Hkv, T, cfg.n)
+    dO, dop = _d(dO)
+    assert dO.shape == (B, T, Hq, dv)
+    names = ("dq", "dk", "dv", "dw1k", "dpek", "dw2k", "dw1v", "dpev", "dw2v", "dwg", "dbg")
+    shapes = ((B, T, Hq, dk), (B, Hkv, T, dk), (B, Hkv, T, dv), (dk, l * dk), (l, dk), (dk, dk), (dv, l * dv),
+              (l, dv), (dv, dv), (Hq, 3, dk), (Hq, 3))
+    out = {n: np.zeros(sh) for n, sh in zip(names, shapes)}
+    c = cfg.c()
+    _load().orc_backward_mlp(ctypes.byref(c), *[a.ctypes.data_as(_dp) for a in arrs], ip, dop, int(round_bf16),
+                             *[out[n].ctypes.data_as(_dp) for n in names])
     return out

@@ -145,3 +145,124 @@ def test_backward_no_compressed_block():
         assert not np.any(gr[gn])
     assert not np.any(gr["dbg"][:, 0]) and not np.any(gr["dwg"][:, 0])
     assert np.all(gr["dbg"][:, 1:] != 0)
+
+
+# ---------------------------------------------------------------------------
+# The two-layer compression map (compress_mlp): first layer w1 with the
+# position encoding, ReLU, second layer w2.
+
+MLP_NAMES = ("q", "k", "v", "w1k", "pek", "w2k", "w1v", "pev", "w2v", "wg", "bg")
+MLP_GRADS = ("dq", "dk", "dv", "dw1k", "dpek", "dw2k", "dw1v", "dpev", "dw2v", "dwg", "dbg")
+
+
+def make_mlp(T, seed=1, **kw):
+    cfg, x, idx, dO = make(T, seed=seed, **kw)
+    rng = np.random.default_rng(seed + 100)
+    dk, dv = cfg.dk, cfg.dv
+    x = dict(x)
+    x["w1k"] = x.pop("wck")
+    x["w1v"] = x.pop("wcv")
+    x["w2k"] = rng.standard_normal((dk, dk)) / math.sqrt(dk)
+    x["w2v"] = rng.standard_normal((dv, dv)) / math.sqrt(dv)
+    return cfg, x, idx, dO
+
+
+def loss_mlp(cfg, x, idx, dO):
+    npad = max(64, -(-orc.n_cmp(cfg.T) // 64) * 64)
+    kc = orc.compress_mlp(x["k"], x["w1k"], x["pek"], x["w2k"], n_out=npad)
+    vc = orc.compress_mlp(x["v"], x["w1v"], x["pev"], x["w2v"], n_out=npad)
+    o = orc.forward(cfg, x["q"], kc, vc, x["k"], x["v"], x["wg"], x["bg"], idx_in=idx)["o"]
+    return float(np.sum(o * dO))
+
+
+def grads_mlp(cfg, x, idx, dO):
+    return orc.backward_mlp(cfg, *[x[nm] for nm in MLP_NAMES], idx, dO)
+
+
+@pytest.mark.parametrize("case", ["T250_w48_n4", "T200_B2_w100_n16"])
+def test_backward_mlp_matches_finite_differences(case):
+    """Every input of the two-layer map's backward against central
+    differences of the oracle's forward (compress_mlp feeding forward).  The
+    ReLU's kink is crossed by no difference quotient here: the smallest
+    |hidden value| of these inputs is far above eps times its directional
+    derivative."""
+    cfg, x, idx, dO = make_mlp(**CASES[case])
+    gr = grads_mlp(cfg, x, idx, dO)
+    rng = np.random.default_rng(98)
+    eps = 1e-5
+    floor = 1e-9 * (1.0 + abs(loss_mlp(cfg, x, idx, dO)))
+    for nm, gn in zip(MLP_NAMES, MLP_GRADS):
+        u = rng.standard_normal(x[nm].shape)
+        xp = dict(x)
+        xm = dict(x)
+        xp[nm] = x[nm] + eps * u
+        xm[nm] = x[nm] - eps * u
+        fd = (loss_mlp(cfg, xp, idx, dO) - loss_mlp(cfg, xm, idx, dO)) / (2 * eps)
+        an = float(np.sum(gr[gn] * u))
+        scale = float(np.sum(np.abs(gr[gn] * u))) + 1e-12
+        assert abs(fd - an) <= 1e-7 * scale + floor, (nm, fd, an)
+
+
+def test_backward_mlp_single_elements():
+    """Element-wise differences in both layers' weights, a position encoding
+    slot and a token two compression blocks share."""
+    cfg, x, idx, dO = make_mlp(T=250, w=48, n=4)
+    gr = grads_mlp(cfg, x, idx, dO)
+    eps = 1e-5
+    picks = [("w2k", "dw2k", (3, 11)), ("w2v", "dw2v", (7, 0)), ("w1k", "dw1k", (5, 16 * 20 + 3)),
+             ("w1v", "dw1v", (2, 8 * 31 + 7)), ("pev", "dpev", (31, 1)), ("k", "dk", (0, 1, 40, 5)),
+             ("v", "dv", (0, 0, 249, 7))]
+    for nm, gn, ix in picks:
+        xp = dict(x)
+        xm = dict(x)
+        xp[nm] = x[nm].copy()
+        xm[nm] = x[nm].copy()
+        xp[nm][ix] += eps
+        xm[nm][ix] -= eps
+        fd = (loss_mlp(cfg, xp, idx, dO) - loss_mlp(cfg, xm, idx, dO)) / (2 * eps)
+        assert abs(fd - gr[gn][ix]) <= 1e-7 * (abs(fd) + 1.0), (nm, ix, fd, gr[gn][ix])
+
+
+def test_backward_mlp_reduces_to_linear():
+    """With w2 = I and every hidden value positive (non-negative tokens, first
+    layer weights and position encodings), the two-layer map is the linear
+    map with w1: every gradient the linear backward reports is the same.  The
+    second layer's gradient is dw2 = sum_i dC_i a_i^T with a_i = w1 X_i, while
+    the linear backward gives dwc = sum_i dC_i X_i^T, so dw2 = dwc w1^T."""
+    cfg, x, idx, dO = make_mlp(T=200, B=2, w=100, n=16, seed=3)
+    for nm in ("k", "v", "w1k", "w1v", "pek", "pev"):
+        x[nm] = np.abs(x[nm])
+    x["w2k"] = np.eye(cfg.dk)
+    x["w2v"] = np.eye(cfg.dv)
+    gm = grads_mlp(cfg, x, idx, dO)
+    gl = orc.backward(cfg, x["q"], x["k"], x["v"], x["w1k"], x["pek"], x["w1v"], x["pev"], x["wg"], x["bg"], idx, dO)
+    for a, b in (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dw1k", "dwck"), ("dpek", "dpek"),
+                 ("dw1v", "dwcv"), ("dpev", "dpev"), ("dwg", "dwg"), ("dbg", "dbg")):
+        # dpek is zero up to rounding (PE_k shifts every compressed key alike),
+        # so the scale is the weight gradient's for it
+        ref = max(np.abs(gl[b]).max(), np.abs(gl["dwck"]).max() * (b == "dpek"))
+        assert np.abs(gm[a] - gl[b]).max() <= 1e-12 * ref, a
+    # a = w1 X for each row, so sum_i dC_i a_i^T = (sum_i dC_i X_i^T) w1^T = dwc w1^T
+    for a, b, w in (("dw2k", "dwck", "w1k"), ("dw2v", "dwcv", "w1v")):
+        ref = gl[b] @ x[w].T
+        assert np.abs(gm[a] - ref).max() <= 1e-10 * (np.abs(ref).max() + 1e-30), a
+
+
+def test_backward_mlp_dead_hidden_layer():
+    """Every hidden value negative (non-negative tokens and position encodings,
+    non-positive first layer): the compressed keys and values are all zero, so
+    neither layer nor the position encodings get a gradient, and the raw-key,
+    query and gate gradients equal those of a linear map whose weights are
+    zero."""
+    cfg, x, idx, dO = make_mlp(T=250, w=48, n=4, seed=4)
+    for nm in ("k", "v", "pek", "pev"):
+        x[nm] = np.abs(x[nm])
+    for nm in ("w1k", "w1v"):
+        x[nm] = -np.abs(x[nm]) - 1e-3
+    gm = grads_mlp(cfg, x, idx, dO)
+    for nm in ("dw1k", "dpek", "dw2k", "dw1v", "dpev", "dw2v"):
+        assert np.all(gm[nm] == 0.0), nm
+    z = {nm: np.zeros_like(x[nm]) for nm in ("w1k", "w1v")}
+    gl = orc.backward(cfg, x["q"], x["k"], x["v"], z["w1k"], x["pek"], z["w1v"], x["pev"], x["wg"], x["bg"], idx, dO)
+    for nm in ("dq", "dk", "dv", "dwg", "dbg"):
+        assert np.abs(gm[nm] - gl[nm]).max() <= 1e-12 * (np.abs(gl[nm]).max() + 1e-30), nm
