@@ -210,8 +210,31 @@ def fwd_bwd(steps):
         tb.append(e[1].elapsed_time(e[2]))
     fms, bms = float(np.mean(tf)), float(np.mean(tb))
     ff, bf = prefill_flops(s)["total"], backward_flops(s)["total"]
+    # the same backward with the two-layer compression map (its second layers,
+    # the recomputed hidden layers and the ReLU added to the linear map's work)
+    wm = make_mlp_weights(s, 1007, dev)
+    wsm = nsa.workspace(s, nsa.OP_BACKWARD_MLP, dev)
+    ckm, cvm = nsa.compress_kv_mlp(s, x["k"], x["v"], x["w_ck"], x["pe_k"], wm["w2_k"], x["w_cv"], x["pe_v"],
+                                   wm["w2_v"])
+
+    def bwd_mlp():
+        return nsa.backward_mlp(s, x["q"], x["k"], x["v"], ckm, cvm, x["w_ck"], x["pe_k"], wm["w2_k"], x["w_cv"],
+                                x["pe_v"], wm["w2_v"], x["w_g"], x["b_g"], idx, x["do"], ws=wsm)
+
+    bwd_mlp()
+    torch.cuda.synchronize()
+    tm = []
+    for _ in range(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        bwd_mlp()
+        e[1].record()
+        torch.cuda.synchronize()
+        tm.append(e[0].elapsed_time(e[1]))
+    mms = float(np.mean(tm))
     return {"workload": "NSA fwd+bwd bf16 T=16384 (B=1, 4 KV x 16 q heads, d_k=192, d_v=128), dO ~ N(0,1)",
-            "fwd_ms": round(fms, 3), "bwd_ms": round(bms, 3), "bwd_over_fwd": round(bms / fms, 2),
+            "fwd_ms": round(fms, 3), "bwd_ms": round(bms, 3), "bwd_mlp_map_ms": round(mms, 3),
+            "bwd_over_fwd": round(bms / fms, 2),
             "fwd_tflops": round(ff / (fms * 1e-3) / 1e12, 2), "bwd_algorithmic_tflop": round(bf / 1e12, 4),
             "bwd_tflops": round(bf / (bms * 1e-3) / 1e12, 2),
             "bwd_mfma_frac": round(bf / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}

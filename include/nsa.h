@@ -76,7 +76,8 @@ typedef enum {
     NSA_OP_SPARSE = 3,  /* nsa_sparse_attention */
     NSA_OP_BACKWARD = 4, /* nsa_backward */
     NSA_OP_DSA_DECODE = 5, /* nsa_dsa_decode: B*T fp32 indexer scores, then the split attention's partials */
-    NSA_OP_DSA_PREFILL = 6 /* nsa_dsa_prefill: the indexer scores of one chunk of rows (<= 256 MiB) */
+    NSA_OP_DSA_PREFILL = 6, /* nsa_dsa_prefill: the indexer scores of one chunk of rows (<= 256 MiB) */
+    NSA_OP_BACKWARD_MLP = 7 /* nsa_backward_mlp */
 } nsa_op;
 
 /* Problem description.  Supported ranges (checked on every call):
@@ -119,8 +120,8 @@ nsa_status nsa_compress_kv(const nsa_config *cfg, const void *k, const void *v, 
  * w1_k, pe_k, w1_v, pe_v have the shapes of w_ck, pe_k, w_cv, pe_v above;
  * w2_k [dk][dk], w2_v [dv][dv] row-major, storage dtype, 16-byte aligned.
  * The compressed outputs feed nsa_compressed_attention, nsa_forward and
- * nsa_decode_step unchanged; nsa_compress_append and nsa_backward take the
- * linear map only. */
+ * nsa_decode_step unchanged; nsa_backward_mlp is the backward pass with this
+ * map (nsa_compress_append takes the linear map only). */
 nsa_status nsa_compress_kv_mlp(const nsa_config *cfg, const void *k, const void *v, const void *w1_k,
                                const void *pe_k, const void *w2_k, const void *w1_v, const void *pe_v,
                                const void *w2_v, void *cmp_k, void *cmp_v, void *stream);
@@ -255,7 +256,7 @@ nsa_status nsa_decode_step(const nsa_config *cfg, const int32_t *seq_lens, const
  * runs on, held until the process ends.  Arguments, results and errors as
  * nsa_decode_step; NSA_ERR_WORKSPACE when nsa_workspace_bytes(cfg,
  * NSA_OP_DECODE) exceeds 32 MiB (at 65,536-token caches, 16 heads per KV
- * head and d_v = 128, up to about 180 (sequence, KV head) pairs); NSA_ERR_HIP
+ * head and d_v = 128, more than 192 (sequence, KV head) pairs); NSA_ERR_HIP
  * if the array's address cannot be looked up.  Every call on a device uses
  * the same array, so calls that overlap on one device (two streams, two host
  * threads) race; calls ordered on one stream do not. */
@@ -284,6 +285,25 @@ nsa_status nsa_backward(const nsa_config *cfg, const void *q, const void *k, con
                         const void *w_g, const void *b_g, const int32_t *idx, const void *d_o, void *d_q,
                         void *d_k, void *d_v, float *d_wck, float *d_pek, float *d_wcv, float *d_pev,
                         float *d_wg, float *d_bg, void *ws, size_t ws_bytes, void *stream);
+
+/* Backward pass with the two-layer compression map of nsa_compress_kv_mlp
+ * (deepdaiv newsletter: a small network summarises each block, and the
+ * method is trained natively, so gradients reach that network's weights).
+ * As nsa_backward, with cmp_k / cmp_v what nsa_compress_kv_mlp makes of k / v
+ * with w1_k, pe_k, w2_k, w1_v, pe_v, w2_v (shapes as there), and
+ *   d_w1k [dk][32*dk], d_pek [32][dk], d_w2k [dk][dk],
+ *   d_w1v [dv][32*dv], d_pev [32][dv], d_w2v [dv][dv]              fp32
+ * in place of the linear map's gradients.  The hidden layer is recomputed;
+ * its bf16 rounding and the output's are treated as the identity, and the
+ * ReLU's derivative is taken as 0 at 0.  Deterministic.  ws:
+ * nsa_workspace_bytes(cfg, NSA_OP_BACKWARD_MLP) bytes (nsa_backward's plus
+ * the hidden layers and their gradient), 256-byte aligned.  B*H_kv <= 65535. */
+nsa_status nsa_backward_mlp(const nsa_config *cfg, const void *q, const void *k, const void *v, const void *cmp_k,
+                            const void *cmp_v, const void *w1_k, const void *pe_k, const void *w2_k,
+                            const void *w1_v, const void *pe_v, const void *w2_v, const void *w_g, const void *b_g,
+                            const int32_t *idx, const void *d_o, void *d_q, void *d_k, void *d_v, float *d_w1k,
+                            float *d_pek, float *d_w2k, float *d_w1v, float *d_pev, float *d_w2v, float *d_wg,
+                            float *d_bg, void *ws, size_t ws_bytes, void *stream);
 
 /* DSA-style decode step (DSA explainer, allinfo.ai.kr, section "쉽게
  * 이해하기": a lightning indexer with several small heads and one key per

@@ -823,6 +823,50 @@ struct DxProblem {
     }
 };
 
+// Two-layer compression map, second layer (c = W2 max(h, 0)), backward.
+// dW2[c][j] = sum over (bh, i < ncmp) of G[bh][i][c] max(h[bh][i][j], 0):
+// M = N = dim, K = B*Hkv*ncmp.
+template <typename T>
+struct Dw2Problem {
+    int M, N, K;
+    const float *G;   // kcv with column offset applied
+    int gs;
+    const T *h;       // hidden layer [B*Hkv][npad][dim]
+    int dim, ncmp, npad;
+    float *out;
+    __device__ float a(int, int m, int k) const
+    {
+        const int bh = k / ncmp, i = k % ncmp;
+        return G[((long)bh * npad + i) * gs + m];
+    }
+    __device__ float b(int, int k, int n) const
+    {
+        const int bh = k / ncmp, i = k % ncmp;
+        return fmaxf(to_f(h[((long)bh * npad + i) * dim + n]), 0.f);
+    }
+    __device__ void store(int, int m, int n, float v) const { out[(long)m * N + n] = v; }
+};
+
+// dA[z][i][j] = (sum_c G[z][i][c] W2[c][j]) [h[z][i][j] > 0] for sequence and
+// head z (the ReLU's derivative taken as 0 at 0), rows i >= ncmp zero:
+// M = npad, N = K = dim.  Written in kcv's layout (column offset applied).
+template <typename T>
+struct DaProblem {
+    int M, N, K;
+    const float *G;
+    int gs;
+    const T *W2, *h;
+    float *da;
+    int dim, ncmp, npad;
+    __device__ float a(int z, int m, int k) const { return m < ncmp ? G[((long)z * npad + m) * gs + k] : 0.f; }
+    __device__ float b(int, int k, int n) const { return to_f(W2[(long)k * dim + n]); }
+    __device__ void store(int z, int m, int n, float v) const
+    {
+        const bool open = m < ncmp && to_f(h[((long)z * npad + m) * dim + n]) > 0.f;
+        da[((long)z * npad + m) * gs + n] = open ? v : 0.f;
+    }
+};
+
 // Gate gradients per chunk of kGateRows rows of one head: element e of
 // [3][dk+1] (column dk is the bias) sums dz_c * q (or dz_c).  A thread owns
 // column x for all three branches (q read once) and keeps 8 rows' loads in
@@ -949,11 +993,59 @@ hipError_t launch_all(const BwdArgs &A, hipStream_t s)
         const long n = (long)BH * d.npad * (d.dk + d.dv);
         hipLaunchKernelGGL(k_bwd_sum_parts, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
                            A);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    // Two-layer map: kcv holds the gradient G of the compressed K/V.  The
+    // hidden layers are recomputed (the first layers' compression), the
+    // second layers' gradients formed, and G is carried through the second
+    // layer and the ReLU into da, which then takes kcv's place for the first
+    // layers' (the linear map's) gradients below.
+    BwdArgs Am = A;
+    if (A.mlp) {
+        if (compress_bf16_supported(d)) {
+            if ((e = launch_compress_bf16(d, A.k, A.v, A.wck, A.pek, A.wcv, A.pev, A.hk, A.hv, s)) != hipSuccess)
+                return e;
+        } else {
+            if ((e = launch_compress_generic(d, A.k, A.wck, A.pek, A.hk, d.dk, s)) != hipSuccess) return e;
+            if ((e = launch_compress_generic(d, A.v, A.wcv, A.pev, A.hv, d.dv, s)) != hipSuccess) return e;
+        }
+        for (int isk = 1; isk >= 0; isk--) {
+            const int dim = isk ? d.dk : d.dv;
+            Dw2Problem<T> p2;
+            p2.M = p2.N = dim;
+            p2.K = BH * d.ncmp;
+            p2.G = A.kcv + (isk ? 0 : d.dk);
+            p2.gs = d.dk + d.dv;
+            p2.h = (const T *)(isk ? A.hk : A.hv);
+            p2.dim = dim;
+            p2.ncmp = d.ncmp;
+            p2.npad = d.npad;
+            p2.out = isk ? A.dw2k : A.dw2v;
+            hipLaunchKernelGGL(k_gemm<Dw2Problem<T>>, dim3((dim + 63) / 64, (dim + 63) / 64, 1), dim3(kThreads), 0, s,
+                               p2);
+            DaProblem<T> pa;
+            pa.M = d.npad;
+            pa.N = pa.K = dim;
+            pa.G = p2.G;
+            pa.gs = p2.gs;
+            pa.W2 = (const T *)(isk ? A.w2k : A.w2v);
+            pa.h = p2.h;
+            pa.da = A.da + (isk ? 0 : d.dk);
+            pa.dim = dim;
+            pa.ncmp = d.ncmp;
+            pa.npad = d.npad;
+            hipLaunchKernelGGL(k_gemm<DaProblem<T>>, dim3((d.npad + 63) / 64, (dim + 63) / 64, BH), dim3(kThreads), 0,
+                               s, pa);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        Am.kcv = A.da;
+    }
+    {
         hipLaunchKernelGGL(k_bwd_colsum_part, dim3((d.dk + d.dv + kWave - 1) / kWave, kColChunks), dim3(kThreads), 0, s,
-                           A);
-        hipLaunchKernelGGL(k_bwd_colsum, dim3((d.dk + d.dv + kThreads - 1) / kThreads), dim3(kThreads), 0, s, A);
+                           Am);
+        hipLaunchKernelGGL(k_bwd_colsum, dim3((d.dk + d.dv + kThreads - 1) / kThreads), dim3(kThreads), 0, s, Am);
         hipLaunchKernelGGL(k_bwd_dpe<T>, dim3((32 * (d.dk > d.dv ? d.dk : d.dv) + kThreads - 1) / kThreads, 2),
-                           dim3(kThreads), 0, s, A);
+                           dim3(kThreads), 0, s, Am);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // 4. compression map: weight gradients and token gradients
@@ -963,7 +1055,7 @@ hipError_t launch_all(const BwdArgs &A, hipStream_t s)
         pw.M = dim;
         pw.N = 32 * dim;
         pw.K = BH * d.ncmp;
-        pw.G = A.kcv + (isk ? 0 : d.dk);
+        pw.G = Am.kcv + (isk ? 0 : d.dk);
         pw.gs = d.dk + d.dv;
         pw.x = (const T *)(isk ? A.k : A.v);
         pw.pe = (const T *)(isk ? A.pek : A.pev);
@@ -973,7 +1065,7 @@ hipError_t launch_all(const BwdArgs &A, hipStream_t s)
         pw.npad = d.npad;
         pw.out = isk ? A.dwck : A.dwcv;
         if (bwd_keys_mfma_ok(d)) {
-            if ((e = launch_bwd_dw_mfma(A, isk == 1, s)) != hipSuccess) return e;
+            if ((e = launch_bwd_dw_mfma(Am, isk == 1, s)) != hipSuccess) return e;
         } else {
             hipLaunchKernelGGL(k_gemm<DwProblem<T>>, dim3((pw.M + 63) / 64, (pw.N + 63) / 64, 1), dim3(kThreads), 0,
                                s, pw);
@@ -1008,7 +1100,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
 
-size_t backward_layout(const Dims &d, void *ws, BwdArgs *A)
+size_t backward_layout(const Dims &d, void *ws, BwdArgs *A, bool mlp)
 {
     const int nchunk = (d.T + kRowChunk - 1) / kRowChunk;
     const int ngc = (int)(((long)d.B * d.T + kGateRows - 1) / kGateRows);
@@ -1032,6 +1124,13 @@ size_t backward_layout(const Dims &d, void *ws, BwdArgs *A)
     size_t kp_floats = 0;
     if (bwd_keys_mfma_ok(d)) bwd_key_chunks(d, &krc, &nkc, &kp_floats);
     const size_t o_kp = carve(kp_floats);
+    size_t o_hk = 0, o_hv = 0, o_da = 0;
+    if (mlp) {
+        const size_t es = d.dtype == NSA_FP32 ? 4 : 2;   // storage bytes per element
+        o_hk = carve((BH * d.npad * d.dk * es + 3) / 4);
+        o_hv = carve((BH * d.npad * d.dv * es + 3) / 4);
+        o_da = carve((size_t)BH * d.npad * (d.dk + d.dv));
+    }
     if (ws && A) {
         char *w = (char *)ws;
         A->rs = (float *)(w + o_rs);
@@ -1048,6 +1147,11 @@ size_t backward_layout(const Dims &d, void *ws, BwdArgs *A)
         A->nkc = nkc;
         A->nchunk = nchunk;
         A->ngc = ngc;
+        if (mlp) {
+            A->hk = w + o_hk;
+            A->hv = w + o_hv;
+            A->da = (float *)(w + o_da);
+        }
     }
     return off;
 }

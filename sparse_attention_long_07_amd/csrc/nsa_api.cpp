@@ -137,6 +137,8 @@ size_t nsa_workspace_bytes(const nsa_config *cfg, int op)
         return sparse_mfma_supported(d) ? align_up(sparse_mfma_ws_bytes(d)) : 0;
     case NSA_OP_BACKWARD:
         return backward_layout(d, nullptr, nullptr);
+    case NSA_OP_BACKWARD_MLP:
+        return backward_layout(d, nullptr, nullptr, true);
     case NSA_OP_DSA_DECODE:
         // the indexer scores, later reused for the split attention's partials
         return dsa_supported(d) ? align_up(std::max(sizeof(float) * (size_t)d.B * d.T, dsa_split_bytes(d, kDsaMaxSplit)))
@@ -563,6 +565,61 @@ nsa_status nsa_backward(const nsa_config *cfg, const void *q, const void *k, con
     A.dwg = d_wg;
     A.dbg = d_bg;
     backward_layout(d, ws, &A);
+    return hip_status(launch_backward(A, (hipStream_t)stream));
+}
+
+nsa_status nsa_backward_mlp(const nsa_config *cfg, const void *q, const void *k, const void *v, const void *cmp_k,
+                            const void *cmp_v, const void *w1_k, const void *pe_k, const void *w2_k,
+                            const void *w1_v, const void *pe_v, const void *w2_v, const void *w_g, const void *b_g,
+                            const int32_t *idx, const void *d_o, void *d_q, void *d_k, void *d_v, float *d_w1k,
+                            float *d_pek, float *d_w2k, float *d_w1v, float *d_pev, float *d_w2v, float *d_wg,
+                            float *d_bg, void *ws, size_t ws_bytes, void *stream)
+{
+    Dims d;
+    nsa_status st = check_config(cfg, &d);
+    if (st != NSA_OK) return st;
+    if ((long)d.B * d.Hkv > 65535) return NSA_ERR_SHAPE;
+    if (!q || !k || !v || !cmp_k || !cmp_v || !w1_k || !pe_k || !w2_k || !w1_v || !pe_v || !w2_v || !w_g || !b_g ||
+        !idx || !d_o || !d_q || !d_k || !d_v || !d_w1k || !d_pek || !d_w2k || !d_w1v || !d_pev || !d_w2v || !d_wg ||
+        !d_bg)
+        return NSA_ERR_NULL;
+    if (!all_aligned({q, k, v, cmp_k, cmp_v, w1_k, pe_k, w2_k, w1_v, pe_v, w2_v, w_g, b_g, idx, d_o, d_q, d_k, d_v,
+                      d_w1k, d_pek, d_w2k, d_w1v, d_pev, d_w2v, d_wg, d_bg}))
+        return NSA_ERR_ALIGN;
+    const size_t need = backward_layout(d, nullptr, nullptr, true);
+    if (!ws || ws_bytes < need) return NSA_ERR_WORKSPACE;
+    if ((uintptr_t)ws % kAlign) return NSA_ERR_ALIGN;
+    BwdArgs A;
+    memset(&A, 0, sizeof A);
+    A.d = d;
+    A.q = q;
+    A.k = k;
+    A.v = v;
+    A.kc = cmp_k;
+    A.vc = cmp_v;
+    A.wck = w1_k;   // the first layers take the linear map's place
+    A.pek = pe_k;
+    A.wcv = w1_v;
+    A.pev = pe_v;
+    A.wg = w_g;
+    A.bg = b_g;
+    A.idx = idx;
+    A.dO = d_o;
+    A.dq = d_q;
+    A.dk = d_k;
+    A.dv = d_v;
+    A.dwck = d_w1k;
+    A.dpek = d_pek;
+    A.dwcv = d_w1v;
+    A.dpev = d_pev;
+    A.dwg = d_wg;
+    A.dbg = d_bg;
+    A.mlp = true;
+    A.w2k = w2_k;
+    A.w2v = w2_v;
+    A.dw2k = d_w2k;
+    A.dw2v = d_w2v;
+    backward_layout(d, ws, &A, true);
     return hip_status(launch_backward(A, (hipStream_t)stream));
 }
 

@@ -121,13 +121,22 @@ struct BwdArgs {
     float *kpart;     // matrix-core key pass: per row chunk c, [B*Hkv][min(T, (c+1) krc)][dk+dv] partial raw dK, dV
     int nchunk, ngc;
     int krc, nkc;     // rows per chunk and chunks of the matrix-core key pass
+    // two-layer compression map (wck/pek/wcv/pev then hold the first layers):
+    // the second layers and their gradients, the recomputed hidden layers
+    // (storage dtype, [B*Hkv][npad][dk|dv], before the ReLU) and the gradient
+    // of the hidden layers (fp32, kcv's layout)
+    bool mlp;
+    const void *w2k, *w2v;
+    float *dw2k, *dw2v;
+    void *hk, *hv;
+    float *da;
 };
 // per (row, head) row statistics of the backward: {lse, D, gate, dz} for each
 // of the 3 branches (compressed, selected, window)
 constexpr int kBwdStat = 12;
 // rows per partial of the compressed-key gradient
 constexpr int kBwdRowChunk = 1024;
-size_t backward_layout(const Dims &d, void *ws, BwdArgs *A);   // bytes; carves A's buffers if ws
+size_t backward_layout(const Dims &d, void *ws, BwdArgs *A, bool mlp = false);   // bytes; carves A's buffers if ws
 hipError_t launch_backward(const BwdArgs &A, hipStream_t s);
 // raw-key gradients on the matrix cores (bf16, 16 heads per KV head, the
 // forward's (d_k, d_v) pairs); needs selbm built and rs filled

@@ -17,14 +17,14 @@ from .config import BF16, FP32, NSAShape
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libnsa.so")
 
-OP_FORWARD, OP_SELECT, OP_DECODE, OP_SPARSE, OP_BACKWARD, OP_DSA_DECODE, OP_DSA_PREFILL = 0, 1, 2, 3, 4, 5, 6
+OP_FORWARD, OP_SELECT, OP_DECODE, OP_SPARSE, OP_BACKWARD, OP_DSA_DECODE, OP_DSA_PREFILL, OP_BACKWARD_MLP = range(8)
 STATUS = {0: "NSA_OK", -1: "NSA_ERR_NULL", -2: "NSA_ERR_SHAPE", -3: "NSA_ERR_DTYPE", -4: "NSA_ERR_PARAM",
           -5: "NSA_ERR_WORKSPACE", -6: "NSA_ERR_HIP", -7: "NSA_ERR_ALIGN"}
 
 EXPORTS = ("nsa_workspace_bytes", "nsa_compress_kv", "nsa_compress_kv_mlp", "nsa_compress_append", "nsa_compressed_attention",
            "nsa_select_topn",
            "nsa_sparse_attention", "nsa_pack_kv_blocks", "nsa_window_attention", "nsa_selected_attention", "nsa_select_blocks",
-           "nsa_forward", "nsa_decode_step", "nsa_decode_step_noalloc", "nsa_backward", "nsa_dsa_decode", "nsa_dsa_prefill", "nsa_status_string")
+           "nsa_forward", "nsa_decode_step", "nsa_decode_step_noalloc", "nsa_backward", "nsa_backward_mlp", "nsa_dsa_decode", "nsa_dsa_prefill", "nsa_status_string")
 
 
 class NSAError(RuntimeError):
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.nsa_decode_step_noalloc.argtypes = [ctypes.POINTER(Config)] + [_vp] * 12
         L.nsa_backward.restype = ctypes.c_int
         L.nsa_backward.argtypes = [ctypes.POINTER(Config)] + [_vp] * 23 + [ctypes.c_size_t, _vp]
+        L.nsa_backward_mlp.restype = ctypes.c_int
+        L.nsa_backward_mlp.argtypes = [ctypes.POINTER(Config)] + [_vp] * 27 + [ctypes.c_size_t, _vp]
         _lib = L
     return _lib
 
@@ -507,4 +509,42 @@ def backward(s: NSAShape, q, k, v, cmp_k, cmp_v, w_ck, pe_k, w_cv, pe_v, w_g, b_
                                                  "d_bg")],
                             _p(ws), ws.numel(), _stream())
     _check("nsa_backward", st)
+    return g
+
+
+def backward_mlp(s: NSAShape, q, k, v, cmp_k, cmp_v, w1_k, pe_k, w2_k, w1_v, pe_v, w2_v, w_g, b_g, idx, d_o,
+                 ws=None):
+    """backward() with the two-layer compression map (compress_kv_mlp).
+    Returns a dict d_q, d_k, d_v (config dtype) and d_w1k, d_pek, d_w2k,
+    d_w1v, d_pev, d_w2v, d_wg, d_bg (fp32), in the layouts of the inputs."""
+    dt = _dt(s)
+    dev = q.device
+    _req(q, "q", (s.B, s.T, s.Hq, s.dk), dt)
+    _req(k, "k", (s.B, s.Hkv, s.T, s.dk), dt)
+    _req(v, "v", (s.B, s.Hkv, s.T, s.dv), dt)
+    _req(cmp_k, "cmp_k", (s.B, s.Hkv, s.n_pad, s.dk), dt)
+    _req(cmp_v, "cmp_v", (s.B, s.Hkv, s.n_pad, s.dv), dt)
+    _req(w1_k, "w1_k", (s.dk, s.l * s.dk), dt)
+    _req(pe_k, "pe_k", (s.l, s.dk), dt)
+    _req(w2_k, "w2_k", (s.dk, s.dk), dt)
+    _req(w1_v, "w1_v", (s.dv, s.l * s.dv), dt)
+    _req(pe_v, "pe_v", (s.l, s.dv), dt)
+    _req(w2_v, "w2_v", (s.dv, s.dv), dt)
+    _req(w_g, "w_g", (s.Hq, 3, s.dk), dt)
+    _req(b_g, "b_g", (s.Hq, 3), dt)
+    _req(idx, "idx", (s.B, s.Hkv, s.T, s.n), torch.int32)
+    _req(d_o, "d_o", (s.B, s.T, s.Hq, s.dv), dt)
+    f32 = lambda t: torch.empty(t.shape, dtype=torch.float32, device=dev)
+    g = {"d_q": torch.empty_like(q), "d_k": torch.empty_like(k), "d_v": torch.empty_like(v),
+         "d_w1k": f32(w1_k), "d_pek": f32(pe_k), "d_w2k": f32(w2_k), "d_w1v": f32(w1_v), "d_pev": f32(pe_v),
+         "d_w2v": f32(w2_v), "d_wg": f32(w_g), "d_bg": f32(b_g)}
+    if ws is None:
+        ws = workspace(s, OP_BACKWARD_MLP, dev)
+    c = config(s)
+    st = lib().nsa_backward_mlp(ctypes.byref(c), _p(q), _p(k), _p(v), _p(cmp_k), _p(cmp_v), _p(w1_k), _p(pe_k),
+                                _p(w2_k), _p(w1_v), _p(pe_v), _p(w2_v), _p(w_g), _p(b_g), _p(idx), _p(d_o),
+                                *[_p(g[n]) for n in ("d_q", "d_k", "d_v", "d_w1k", "d_pek", "d_w2k", "d_w1v", "d_pev",
+                                                     "d_w2v", "d_wg", "d_bg")],
+                                _p(ws), ws.numel(), _stream())
+    _check("nsa_backward_mlp", st)
     return g

@@ -83,6 +83,7 @@ def test_bad_config_rejected_everywhere(kw, code):
     assert L.nsa_forward(c, *f[:7], None, f[0], None, None, f[1], 1 << 40, None) == code
     assert L.nsa_decode_step(c, *f[:8], None, f[0], None, f[1], 1 << 40, None) == code
     assert L.nsa_backward(c, *([FAKE] * 22), FAKE, 1 << 40, None) == code
+    assert L.nsa_backward_mlp(c, *([FAKE] * 26), FAKE, 1 << 40, None) == code
     assert L.nsa_dsa_decode(c, 4, 64, 16, *([FAKE] * 10), FAKE, 1 << 40, None) == code
     assert L.nsa_dsa_prefill(c, 4, 64, 16, *([FAKE] * 9), FAKE, 1 << 40, None) == code
     assert L.nsa_sparse_attention(c, *f[:8], f[0], 1 << 40, None) == code
@@ -268,6 +269,34 @@ def test_backward_required_pointers(pos):
     assert L.nsa_backward(c, *args, FAKE, need, None) == NULL
     args[pos] = MIS
     assert L.nsa_backward(c, *args, FAKE, need, None) == ALIGN
+
+
+@pytest.mark.parametrize("pos", range(26))
+def test_backward_mlp_required_pointers(pos):
+    L = nsa.lib()
+    c = ctypes.byref(cfg())
+    need = L.nsa_workspace_bytes(c, nsa.OP_BACKWARD_MLP)
+    args = [FAKE] * 26
+    args[pos] = None
+    assert L.nsa_backward_mlp(c, *args, FAKE, need, None) == NULL
+    args[pos] = MIS
+    assert L.nsa_backward_mlp(c, *args, FAKE, need, None) == ALIGN
+
+
+def test_backward_mlp_workspace_checks():
+    L = nsa.lib()
+    c = cfg()
+    need = L.nsa_workspace_bytes(ctypes.byref(c), nsa.OP_BACKWARD_MLP)
+    base = L.nsa_workspace_bytes(ctypes.byref(c), nsa.OP_BACKWARD)
+    s = NSAShape(1, 256, 2, 4, 64, 32, "bf16")
+    # the linear map's workspace plus the hidden layers (bf16) and their gradient (fp32)
+    assert need >= base + s.B * s.Hkv * s.n_pad * (2 * (s.dk + s.dv) + 4 * (s.dk + s.dv))
+    assert need % 256 == 0
+    f = [FAKE] * 26
+    assert L.nsa_backward_mlp(ctypes.byref(c), *f, None, need, None) == WS
+    assert L.nsa_backward_mlp(ctypes.byref(c), *f, FAKE, need - 1, None) == WS
+    assert L.nsa_backward_mlp(ctypes.byref(c), *f, ctypes.c_void_p(0x10010), need, None) == ALIGN
+    assert L.nsa_backward_mlp(ctypes.byref(cfg(B=70000, H_kv=1, group=1)), *f, FAKE, 1 << 40, None) == SHAPE
 
 
 def test_backward_workspace_checks():

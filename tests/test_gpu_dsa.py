@@ -93,11 +93,11 @@ def test_dsa_decode_parity(name, s, lens, topk, hi, di):
     for b in range(s.B):
         L = _clamp_len(lens[b], s.T)
         sc = dsa.index_scores(qi[b], wi[b], ki[b], L)
-        same = _check_selection(sc, qi[b], wi[b], ki[b], L, sel[b], topk, (name, b))
-        if same:   # end to end where the two selections agree
-            n_same += 1
-            ref = dsa.attend(q[b], k[b], v[b], sel[b], G, scale)
-            assert np.abs(np64(o[b]) - ref).max() <= out_tol(s, ref), (name, b)
+        # the GPU's list is a valid top-k (and the oracle's own where no near-tie
+        # decides); the output is the oracle's attention over that list on every row
+        n_same += _check_selection(sc, qi[b], wi[b], ki[b], L, sel[b], topk, (name, b))
+        ref = dsa.attend(q[b], k[b], v[b], sel[b], G, scale)
+        assert np.abs(np64(o[b]) - ref).max() <= out_tol(s, ref), (name, b)
     assert n_same >= 1, name
 
 
@@ -211,7 +211,8 @@ PREFILL = [
 @pytest.mark.parametrize("name,s,topk,hi,di", PREFILL, ids=[c[0] for c in PREFILL])
 def test_dsa_prefill_parity(name, s, topk, hi, di):
     """Every position a query: sampled positions' selections against the
-    oracle (as in the decode test), end to end where they agree, and the
+    oracle (as in the decode test), each sampled position's output against the
+    oracle's attention over the GPU's own list, and the
     attention of every sampled position with the oracle's selection
     injected for all positions."""
     say("dsa prefill", name, s, topk)
@@ -235,10 +236,9 @@ def test_dsa_prefill_parity(name, s, topk, hi, di):
     n_same = 0
     for b, t in rows:
         sc = dsa.index_scores(QI[b, t], WI[b, t], KI[b], t + 1)
-        if _check_selection(sc, QI[b, t], WI[b, t], KI[b], t + 1, sel[b, t], topk, (name, b, t)):
-            n_same += 1
-            ref = dsa.attend(Q[b, t], K[b], V[b], sel[b, t], s.G, scale)
-            assert np.abs(np64(o[b, t]) - ref).max() <= out_tol(s, ref), (name, b, t)
+        n_same += _check_selection(sc, QI[b, t], WI[b, t], KI[b], t + 1, sel[b, t], topk, (name, b, t))
+        ref = dsa.attend(Q[b, t], K[b], V[b], sel[b, t], s.G, scale)   # over the GPU's own (valid) list
+        assert np.abs(np64(o[b, t]) - ref).max() <= out_tol(s, ref), (name, b, t)
     assert n_same >= 1
     # injected oracle selection for every position
     ref_all = dsa.dsa_prefill(QI, WI, KI, Q, K, V, topk, s.G, scale)
