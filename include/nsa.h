@@ -121,7 +121,7 @@ nsa_status nsa_compress_kv(const nsa_config *cfg, const void *k, const void *v, 
  * w2_k [dk][dk], w2_v [dv][dv] row-major, storage dtype, 16-byte aligned.
  * The compressed outputs feed nsa_compressed_attention, nsa_forward and
  * nsa_decode_step unchanged; nsa_backward_mlp is the backward pass with this
- * map (nsa_compress_append takes the linear map only). */
+ * map, and nsa_compress_append_mlp its incremental form for decoding. */
 nsa_status nsa_compress_kv_mlp(const nsa_config *cfg, const void *k, const void *v, const void *w1_k,
                                const void *pe_k, const void *w2_k, const void *w1_v, const void *pe_v,
                                const void *w2_v, void *cmp_k, void *cmp_v, void *stream);
@@ -144,6 +144,17 @@ nsa_status nsa_compress_append(const nsa_config *cfg, const int32_t *len_old, co
                                int32_t max_append, const void *k_cache, const void *v_cache, const void *w_ck,
                                const void *pe_k, const void *w_cv, const void *pe_v, void *cmp_k, void *cmp_v,
                                void *stream);
+
+/* nsa_compress_append with the two-layer map of nsa_compress_kv_mlp (the
+ * deepdaiv newsletter's small network; shapes of w1_k, pe_k, w2_k, w1_v,
+ * pe_v, w2_v as there): the blocks that growing the caches from len_old[b] to
+ * len_new[b] tokens completes are computed as nsa_compress_kv_mlp defines
+ * them, each bit for bit as nsa_compress_kv_mlp makes it; no other entry is
+ * touched.  Arguments and errors as nsa_compress_append. */
+nsa_status nsa_compress_append_mlp(const nsa_config *cfg, const int32_t *len_old, const int32_t *len_new,
+                                   int32_t max_append, const void *k_cache, const void *v_cache, const void *w1_k,
+                                   const void *pe_k, const void *w2_k, const void *w1_v, const void *pe_v,
+                                   const void *w2_v, void *cmp_k, void *cmp_v, void *stream);
 
 /* Stage S2 -- compressed attention and block importance (deepdaiv
  * newsletter, token compression and token selection paragraphs: the block

@@ -284,6 +284,36 @@ nsa_status nsa_compress_append(const nsa_config *cfg, const int32_t *len_old, co
     return NSA_OK;
 }
 
+nsa_status nsa_compress_append_mlp(const nsa_config *cfg, const int32_t *len_old, const int32_t *len_new,
+                                   int32_t max_append, const void *k_cache, const void *v_cache, const void *w1_k,
+                                   const void *pe_k, const void *w2_k, const void *w1_v, const void *pe_v,
+                                   const void *w2_v, void *cmp_k, void *cmp_v, void *stream)
+{
+    Dims d;
+    nsa_status st = check_config(cfg, &d);
+    if (st != NSA_OK) return st;
+    if (!len_new || !k_cache || !v_cache || !w1_k || !pe_k || !w2_k || !w1_v || !pe_v || !w2_v || !cmp_k || !cmp_v)
+        return NSA_ERR_NULL;
+    if (max_append < 1 || max_append > d.T) return NSA_ERR_PARAM;
+    const void *ptrs[] = {k_cache, v_cache, w1_k, pe_k, w2_k, w1_v, pe_v, w2_v, cmp_k, cmp_v};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return NSA_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    const int max_blocks = std::min(max_append / 16 + 1, d.npad);
+    // first layer: the linear append with W1 (pre-activations of the new blocks)
+    if (compress_bf16_supported(d)) {
+        NSA_TRY(launch_compress_bf16(d, k_cache, v_cache, w1_k, pe_k, w1_v, pe_v, cmp_k, cmp_v, s, len_old, len_new,
+                                     max_blocks));
+    } else {
+        const int tiles = (max_blocks + 63) / 64;
+        NSA_TRY(launch_compress_generic(d, k_cache, w1_k, pe_k, cmp_k, d.dk, s, len_old, len_new, tiles));
+        NSA_TRY(launch_compress_generic(d, v_cache, w1_v, pe_v, cmp_v, d.dv, s, len_old, len_new, tiles));
+    }
+    // second layer on the same rows only
+    NSA_TRY(launch_compress_mlp2(d, w2_k, w2_v, cmp_k, cmp_v, s, len_old, len_new, max_blocks));
+    return NSA_OK;
+}
+
 nsa_status nsa_compressed_attention(const nsa_config *cfg, const void *q, const void *cmp_k, const void *cmp_v,
                                     void *o_cmp, float *scores, void *stream)
 {

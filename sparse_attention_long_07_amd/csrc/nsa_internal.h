@@ -180,7 +180,8 @@ size_t dsa_split_bytes(const Dims &d, int nsplit);
 constexpr int kDsaMaxSplit = 4;
 // second layer of the two-layer compression, in place: rows <- W2 relu(rows)
 hipError_t launch_compress_mlp2(const Dims &d, const void *W2k, const void *W2v, void *cmp_k, void *cmp_v,
-                                hipStream_t s);
+                                hipStream_t s, const int32_t *len_old = nullptr, const int32_t *len_new = nullptr,
+                                int max_blocks = 0);
 hipError_t launch_select_generic(const RowArgs &a, hipStream_t s);
 hipError_t launch_sparse_generic(const RowArgs &a, hipStream_t s);
 

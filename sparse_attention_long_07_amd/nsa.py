@@ -21,7 +21,7 @@ OP_FORWARD, OP_SELECT, OP_DECODE, OP_SPARSE, OP_BACKWARD, OP_DSA_DECODE, OP_DSA_
 STATUS = {0: "NSA_OK", -1: "NSA_ERR_NULL", -2: "NSA_ERR_SHAPE", -3: "NSA_ERR_DTYPE", -4: "NSA_ERR_PARAM",
           -5: "NSA_ERR_WORKSPACE", -6: "NSA_ERR_HIP", -7: "NSA_ERR_ALIGN"}
 
-EXPORTS = ("nsa_workspace_bytes", "nsa_compress_kv", "nsa_compress_kv_mlp", "nsa_compress_append", "nsa_compressed_attention",
+EXPORTS = ("nsa_workspace_bytes", "nsa_compress_kv", "nsa_compress_kv_mlp", "nsa_compress_append", "nsa_compress_append_mlp", "nsa_compressed_attention",
            "nsa_select_topn",
            "nsa_sparse_attention", "nsa_pack_kv_blocks", "nsa_window_attention", "nsa_selected_attention", "nsa_select_blocks",
            "nsa_forward", "nsa_decode_step", "nsa_decode_step_noalloc", "nsa_backward", "nsa_backward_mlp", "nsa_dsa_decode", "nsa_dsa_prefill", "nsa_status_string")
@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.nsa_compress_kv_mlp.argtypes = [ctypes.POINTER(Config)] + [_vp] * 11
         L.nsa_compress_append.restype = ctypes.c_int
         L.nsa_compress_append.argtypes = [ctypes.POINTER(Config), _vp, _vp, ctypes.c_int32] + [_vp] * 9
+        L.nsa_compress_append_mlp.restype = ctypes.c_int
+        L.nsa_compress_append_mlp.argtypes = [ctypes.POINTER(Config), _vp, _vp, ctypes.c_int32] + [_vp] * 11
         L.nsa_compressed_attention.restype = ctypes.c_int
         L.nsa_compressed_attention.argtypes = [ctypes.POINTER(Config)] + [_vp] * 6
         L.nsa_select_topn.restype = ctypes.c_int
@@ -202,6 +204,32 @@ def compress_append(s: NSAShape, len_old, len_new, max_append, k_cache, v_cache,
            lib().nsa_compress_append(ctypes.byref(c), _p(len_old), _p(len_new), int(max_append), _p(k_cache),
                                      _p(v_cache), _p(w_ck), _p(pe_k), _p(w_cv), _p(pe_v), _p(cmp_k), _p(cmp_v),
                                      _stream()))
+    return cmp_k, cmp_v
+
+
+def compress_append_mlp(s: NSAShape, len_old, len_new, max_append, k_cache, v_cache, w1_k, pe_k, w2_k, w1_v, pe_v,
+                        w2_v, cmp_k, cmp_v):
+    """compress_append with the two-layer map of compress_kv_mlp.  cmp_k /
+    cmp_v are updated in place and returned."""
+    dt = _dt(s)
+    if len_old is not None:
+        _req(len_old, "len_old", (s.B,), torch.int32)
+    _req(len_new, "len_new", (s.B,), torch.int32)
+    _req(k_cache, "k_cache", (s.B, s.Hkv, s.T, s.dk), dt)
+    _req(v_cache, "v_cache", (s.B, s.Hkv, s.T, s.dv), dt)
+    _req(w1_k, "w1_k", (s.dk, s.l * s.dk), dt)
+    _req(pe_k, "pe_k", (s.l, s.dk), dt)
+    _req(w2_k, "w2_k", (s.dk, s.dk), dt)
+    _req(w1_v, "w1_v", (s.dv, s.l * s.dv), dt)
+    _req(pe_v, "pe_v", (s.l, s.dv), dt)
+    _req(w2_v, "w2_v", (s.dv, s.dv), dt)
+    _req(cmp_k, "cmp_k", (s.B, s.Hkv, s.n_pad, s.dk), dt)
+    _req(cmp_v, "cmp_v", (s.B, s.Hkv, s.n_pad, s.dv), dt)
+    c = config(s)
+    _check("nsa_compress_append_mlp",
+           lib().nsa_compress_append_mlp(ctypes.byref(c), _p(len_old), _p(len_new), int(max_append), _p(k_cache),
+                                         _p(v_cache), _p(w1_k), _p(pe_k), _p(w2_k), _p(w1_v), _p(pe_v), _p(w2_v),
+                                         _p(cmp_k), _p(cmp_v), _stream()))
     return cmp_k, cmp_v
 
 

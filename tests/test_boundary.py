@@ -79,6 +79,7 @@ def test_bad_config_rejected_everywhere(kw, code):
     assert L.nsa_compress_kv(c, *f[:8], None) == code
     assert L.nsa_compress_kv_mlp(c, *f[:10], None) == code
     assert L.nsa_compress_append(c, f[0], f[1], 1, *f[:8], None) == code
+    assert L.nsa_compress_append_mlp(c, f[0], f[1], 1, *f[:10], None) == code
     assert L.nsa_select_blocks(c, f[0], f[1], None, f[2], f[3], 1 << 40, None) == code
     assert L.nsa_forward(c, *f[:7], None, f[0], None, None, f[1], 1 << 40, None) == code
     assert L.nsa_decode_step(c, *f[:8], None, f[0], None, f[1], 1 << 40, None) == code
@@ -139,6 +140,22 @@ def test_compress_append_checks(pos):
     f = [FAKE] * 8
     for bad in (0, -1, 257):
         assert L.nsa_compress_append(c, FAKE, FAKE, bad, *f, None) == PARAM
+
+
+@pytest.mark.parametrize("pos", range(11))
+def test_compress_append_mlp_checks(pos):
+    """As test_compress_append_checks, with both layers' weights."""
+    L = nsa.lib()
+    c = ctypes.byref(cfg())
+    args = [FAKE] * 11          # len_new | k_cache v_cache w1_k pe_k w2_k w1_v pe_v w2_v cmp_k cmp_v
+    args[pos] = None
+    assert L.nsa_compress_append_mlp(c, None, args[0], 16, *args[1:], None) == NULL
+    if pos > 0:
+        args[pos] = MIS
+        assert L.nsa_compress_append_mlp(c, FAKE, args[0], 16, *args[1:], None) == ALIGN
+    f = [FAKE] * 10
+    for bad in (0, -1, 257):
+        assert L.nsa_compress_append_mlp(c, FAKE, FAKE, bad, *f, None) == PARAM
 
 
 @pytest.mark.parametrize("pos", range(8))

@@ -16,7 +16,7 @@ import torch
 
 from sparse_attention_long_07_amd import nsa
 from sparse_attention_long_07_amd.config import FP32, NSAShape
-from sparse_attention_long_07_amd.inputs import make_decode
+from sparse_attention_long_07_amd.inputs import make_decode, make_mlp_weights
 from tests.parity_util import compressed_close, np64, oracle_compress
 
 pytestmark = pytest.mark.gpu
@@ -87,6 +87,44 @@ def test_append_matches_full_compression(name, s, lens, lens0):
         assert compressed_close(s, np64(ck[b, :, :n]), ok_k[b, :, :n])
         assert compressed_close(s, np64(cv[b, :, :n]), ok_v[b, :, :n])
         # nothing past them is written
+        assert bool(torch.isnan(ck[b, :, n:].float()).all()) and bool(torch.isnan(cv[b, :, n:].float()).all())
+
+
+def _grow_mlp(s, x, w, lens0, lens, ck, cv):
+    """_grow with the two-layer map."""
+    dev = x["k"].device
+    a = (x["k"], x["v"], x["w_ck"], x["pe_k"], w["w2_k"], x["w_cv"], x["pe_v"], w["w2_v"], ck, cv)
+    cur = torch.tensor(lens0, dtype=torch.int32, device=dev)
+    nsa.compress_append_mlp(s, None, cur, max(max(lens0), 1), *a)
+    target = torch.tensor(lens, dtype=torch.int32, device=dev)
+    nxt = torch.minimum(cur + 37, target)
+    nsa.compress_append_mlp(s, cur, nxt, 37, *a)
+    cur = nxt
+    while bool((cur < target).any()):
+        nxt = torch.minimum(cur + 1, target)
+        nsa.compress_append_mlp(s, cur, nxt, 1, *a)
+        cur = nxt
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name,s,lens,lens0", CASES, ids=[c[0] for c in CASES])
+def test_append_mlp_matches_full_compression(name, s, lens, lens0):
+    """Appends with the two-layer map: the completed blocks bit for bit as
+    nsa_compress_kv_mlp writes them, and nothing past them written."""
+    say("append mlp", name, s, lens, lens0)
+    x = make_decode(s, 45, "cuda", seq_lens=lens)
+    w = make_mlp_weights(s, 46, "cuda")
+    dt = x["k"].dtype
+    ref_k, ref_v = nsa.compress_kv_mlp(s, x["k"], x["v"], x["w_ck"], x["pe_k"], w["w2_k"], x["w_cv"], x["pe_v"],
+                                       w["w2_v"])
+    ck = torch.full((s.B, s.Hkv, s.n_pad, s.dk), float("nan"), dtype=dt, device="cuda")
+    cv = torch.full((s.B, s.Hkv, s.n_pad, s.dv), float("nan"), dtype=dt, device="cuda")
+    _grow_mlp(s, x, w, lens0, lens, ck, cv)
+    for b, L in enumerate(lens):
+        n = nblk(L)
+        # (nsa_compress_kv_mlp itself is checked against the oracle in test_gpu_mlp.py)
+        assert torch.equal(ck[b, :, :n], ref_k[b, :, :n]), (name, b)
+        assert torch.equal(cv[b, :, :n], ref_v[b, :, :n]), (name, b)
         assert bool(torch.isnan(ck[b, :, n:].float()).all()) and bool(torch.isnan(cv[b, :, n:].float()).all())
 
 
