@@ -251,7 +251,9 @@ static int select_blocks(const orc_cfg *c, int t, const double *S, int *idx)
  *   o      [G][dv]
  *   idx_out[n], scores[nb] (nb >= j_cur+1; entries past j_cur = -inf) or NULL,
  *   branches [3][G][dv] (o_cmp, o_slc, o_win) or NULL, gates [G][3] or NULL,
- *   lse [G] (compressed-branch log-sum-exp, -inf if empty) or NULL */
+ *   lse [3][G] or NULL: each branch's log-sum-exp of its logits scale q.K
+ *   over its own key set (-inf if the set is empty), branches in the order
+ *   of `branches` */
 void orc_row(const orc_cfg *c, int t, const double *q, const double *kc, const double *vc,
              const double *k, const double *v, const double *wg, const double *bg,
              const int *idx_in, double *o, int *idx_out, double *scores, int nb,
@@ -317,15 +319,19 @@ void orc_row(const orc_cfg *c, int t, const double *q, const double *kc, const d
         }
         free(sorted);
     }
-    for (int h = 0; h < G; h++)
-        attend_list(q + (size_t)h * dk, k, v, dk, dv, c->scale, rows, nr, oslc + (size_t)h * dv, NULL);
+    for (int h = 0; h < G; h++) {
+        double L = attend_list(q + (size_t)h * dk, k, v, dk, dv, c->scale, rows, nr, oslc + (size_t)h * dv, NULL);
+        if (lse) lse[G + h] = L;
+    }
 
     /* Sliding window: [max(0, t-w+1), t]. */
     int lo = t - c->w + 1 > 0 ? t - c->w + 1 : 0;
     nr = 0;
     for (int tau = lo; tau <= t; tau++) rows[nr++] = tau;
-    for (int h = 0; h < G; h++)
-        attend_list(q + (size_t)h * dk, k, v, dk, dv, c->scale, rows, nr, owin + (size_t)h * dv, NULL);
+    for (int h = 0; h < G; h++) {
+        double L = attend_list(q + (size_t)h * dk, k, v, dk, dv, c->scale, rows, nr, owin + (size_t)h * dv, NULL);
+        if (lse) lse[2 * G + h] = L;
+    }
 
     /* Gated combination. */
     for (int h = 0; h < G; h++) {
@@ -358,7 +364,7 @@ void orc_row(const orc_cfg *c, int t, const double *q, const double *kc, const d
  *   wg [Hq][3][dk], bg [Hq][3]
  *   idx_in   [R][Hkv][n] or NULL
  *   o        [R][Hq][dv];  idx_out [R][Hkv][n];  scores [R][Hkv][nb] or NULL;
- *   branches [R][3][Hq][dv] or NULL; lse [R][Hq] or NULL */
+ *   branches [R][3][Hq][dv] or NULL; lse [R][3][Hq] (per branch, as orc_row) or NULL */
 void orc_forward_rows(const orc_cfg *c, int R, const int *b_list, const int *t_list,
                       const double *q, const double *kc, const double *vc, int npad,
                       const double *k, const double *v, const double *wg, const double *bg,
@@ -378,13 +384,19 @@ void orc_forward_rows(const orc_cfg *c, int R, const int *b_list, const int *t_l
         const double *vg = v + ((size_t)b * Hkv + g) * (size_t)T * dv;
         double *br = NULL;
         double *tmp = NULL;
+        double *lse3 = lse ? (double *)malloc(sizeof(double) * 3 * (size_t)G) : NULL;
         if (branches) tmp = (double *)malloc(sizeof(double) * 3 * (size_t)G * dv);
         orc_row(c, t, qr, kcg, vcg, kg, vg, wg + (size_t)g * G * 3 * dk, bg + (size_t)g * G * 3,
                 idx_in ? idx_in + ((size_t)r * Hkv + g) * n : NULL,
                 o + ((size_t)r * Hq + (size_t)g * G) * dv,
                 idx_out + ((size_t)r * Hkv + g) * n,
-                scores ? scores + ((size_t)r * Hkv + g) * nb : NULL, nb, tmp, NULL,
-                lse ? lse + (size_t)r * Hq + (size_t)g * G : NULL);
+                scores ? scores + ((size_t)r * Hkv + g) * nb : NULL, nb, tmp, NULL, lse ? lse3 : NULL);
+        if (lse) {
+            for (int br_i = 0; br_i < 3; br_i++)
+                memcpy(lse + ((size_t)r * 3 + br_i) * Hq + (size_t)g * G, lse3 + (size_t)br_i * G,
+                       sizeof(double) * (size_t)G);
+            free(lse3);
+        }
         if (branches) {
             for (int br_i = 0; br_i < 3; br_i++) {
                 br = branches + (((size_t)r * 3 + br_i) * Hq + (size_t)g * G) * dv;

@@ -157,7 +157,8 @@ def forward_rows(cfg: Cfg, b_list, t_list, q_rows, kc, vc, k, v, wg, bg, idx_in=
     kc [B,Hkv,npad,dk], vc [B,Hkv,npad,dv]; k [B,Hkv,T,dk], v [B,Hkv,T,dv];
     wg [Hq,3,dk], bg [Hq,3]; idx_in [R,Hkv,n] or None.
     Returns dict with o [R,Hq,dv], idx [R,Hkv,n] and optionally
-    scores [R,Hkv,nb], branches [R,3,Hq,dv] (o_cmp, o_slc, o_win), lse [R,Hq].
+    scores [R,Hkv,nb], branches [R,3,Hq,dv] (o_cmp, o_slc, o_win) and lse
+    [R,3,Hq] (each branch's log-sum-exp of its logits, -inf when empty).
     """
     assert cfg.n <= 64
     b_arr, bp = _i(b_list)
@@ -187,7 +188,7 @@ def forward_rows(cfg: Cfg, b_list, t_list, q_rows, kc, vc, k, v, wg, bg, idx_in=
     nb = cfg.nb
     scores = np.zeros((R, cfg.Hkv, nb)) if want_scores else None
     branches = np.zeros((R, 3, cfg.Hq, cfg.dv)) if want_branches else None
-    lse = np.zeros((R, cfg.Hq)) if want_lse else None
+    lse = np.zeros((R, 3, cfg.Hq)) if want_lse else None
     c = cfg.c()
     _load().orc_forward_rows(ctypes.byref(c), R, bp, tp, qp, kcp, vcp, npad, kp, vp, wgp, bgp, iip,
                              o.ctypes.data_as(_dp), idx.ctypes.data_as(_ip),
@@ -224,7 +225,7 @@ def forward(cfg: Cfg, q, kc, vc, k, v, wg, bg, idx_in=None, **kw):
     if "branches" in r:
         out["branches"] = r["branches"].reshape(B, T, 3, cfg.Hq, cfg.dv)
     if "lse" in r:
-        out["lse"] = r["lse"].reshape(B, T, cfg.Hq)
+        out["lse"] = r["lse"].reshape(B, T, 3, cfg.Hq)
     return out
 
 

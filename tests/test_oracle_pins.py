@@ -157,10 +157,10 @@ def test_compressed_branch_is_masked_attention(T):
             # log-sum-exp of the masked logits
             s = np.einsum("the,ne->htn", x["q"][0, :, heads], x["kc"][0, g, :N]) / 4.0
             lse = torch.logsumexp(torch.from_numpy(np.where(m[None], s, -np.inf)), dim=-1).numpy()
-            np.testing.assert_allclose(out["lse"][0, rows, heads].T, lse[:, rows], rtol=1e-12)
+            np.testing.assert_allclose(out["lse"][0, rows, 0, heads].T, lse[:, rows], rtol=1e-12)
         empty = ~m.any(axis=1) if N > 0 else np.ones(T, bool)
         assert np.all(ocmp[empty, heads] == 0)
-        assert np.all(np.isneginf(out["lse"][0, empty, heads]))
+        assert np.all(np.isneginf(out["lse"][0, empty, 0, heads]))
 
 
 def test_importance_sums_to_2G():
@@ -268,18 +268,27 @@ def test_dense_reduction(T):
         np.testing.assert_allclose(out["branches"][0, :, 2, heads], want, rtol=1e-11, atol=1e-12)
 
 
+def masked_lse(q, k, mask, scale):
+    """Library log-sum-exp of scale q.k over the keys of mask: q [T,H,E],
+    k [S,E], mask [T,S] bool; returns [T,H]."""
+    s = torch.from_numpy(np.einsum("the,se->ths", q, k) * scale)
+    return torch.logsumexp(s.masked_fill(~torch.from_numpy(mask)[:, None, :], -math.inf), dim=-1).numpy()
+
+
 def test_window_is_banded_attention():
     T, w = 300, 64
     cfg, x = make_case(T, Hkv=1, G=3, dk=16, dv=8, w=w, seed=7)
-    out = run(cfg, x, want_branches=True)
+    out = run(cfg, x, want_branches=True, want_lse=True)
     t = np.arange(T)[:, None]
     s = np.arange(T)[None, :]
     band = (s <= t) & (s >= t - w + 1)
     want = sdpa(x["q"][0].transpose(1, 0, 2), x["k"][0, 0], x["v"][0, 0], band, 0.25).transpose(1, 0, 2)
     np.testing.assert_allclose(out["branches"][0, :, 2], want, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(out["lse"][0, :, 2], masked_lse(x["q"][0], x["k"][0, 0], band, 0.25), rtol=1e-12)
     # selection is total for T <= n*l', so the selected branch is dense causal
     want = sdpa(x["q"][0].transpose(1, 0, 2), x["k"][0, 0], x["v"][0, 0], s <= t, 0.25).transpose(1, 0, 2)
     np.testing.assert_allclose(out["branches"][0, :, 1], want, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(out["lse"][0, :, 1], masked_lse(x["q"][0], x["k"][0, 0], s <= t, 0.25), rtol=1e-12)
 
 
 def test_selected_branch_is_attention_over_selected_blocks():
@@ -296,6 +305,24 @@ def test_selected_branch_is_attention_over_selected_blocks():
     want = sdpa(x["q"][0].transpose(1, 0, 2), x["k"][0, 0], x["v"][0, 0], mask, 0.25).transpose(1, 0, 2)
     np.testing.assert_allclose(out["branches"][0, :, 1], want, rtol=1e-11, atol=1e-12)
     assert (mask.sum(1) < (t[:, 0] + 1)).any(), "some rows must really be sparse"
+    # the branch's log-sum-exp is over the selected set only
+    lse = run(cfg, x, idx_in=out["idx"], want_lse=True)["lse"][0, :, 1]
+    np.testing.assert_allclose(lse, masked_lse(x["q"][0], x["k"][0, 0], mask, 0.25), rtol=1e-12)
+
+
+def test_empty_selection_has_no_mass():
+    """An index list with no valid block leaves the selected branch empty:
+    output 0 and log-sum-exp -inf, while the other branches are unaffected."""
+    T = 200
+    cfg, x = make_case(T, Hkv=1, G=2, n=4, seed=13)
+    inj = np.full((1, 1, T, 4), -1, np.int32)
+    inj[0, 0, 100:, 0] = 5          # a block past every row's causal limit is not valid either
+    out = run(cfg, x, idx_in=inj, want_branches=True, want_lse=True)
+    assert np.all(out["branches"][0, :, 1] == 0)
+    assert np.all(np.isneginf(out["lse"][0, :, 1]))
+    ref = run(cfg, x, want_branches=True, want_lse=True)
+    np.testing.assert_array_equal(out["lse"][0, :, 2], ref["lse"][0, :, 2])
+    np.testing.assert_array_equal(out["branches"][0, :, 0], ref["branches"][0, :, 0])
 
 
 def test_idx_injection_is_used():
