@@ -175,24 +175,43 @@ def mlp_compress(s, x, steps):
             "mlp_tflops": round((fl + fl2) / (mlp_ms * 1e-3) / 1e12, 2)}
 
 
+def _timed(fn, steps):
+    """Mean milliseconds of fn() over `steps` calls, each bracketed by events
+    on the current stream (one untimed call first)."""
+    fn()
+    torch.cuda.synchronize()
+    t = []
+    for _ in range(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        fn()
+        e[1].record()
+        torch.cuda.synchronize()
+        t.append(e[0].elapsed_time(e[1]))
+    return float(np.mean(t))
+
+
 def fwd_bwd(steps):
-    """Forward (compression, the three branches, selection) and backward with
-    the forward's selection at T=16384, timed apart from the headline step."""
+    """Training forward (compression, the three branches, selection, each
+    branch's softmax statistics saved) and backward with the forward's
+    selection and statistics at T=16384, timed apart from the headline step."""
     w = WORKLOADS["bf16_fwdbwd_T16384"]
     s = w.shape
     dev = torch.device("cuda:0")
     log("setup: fwd+bwd inputs", s)
     x = make_prefill(s, 1005, dev, unit_scaled=w.unit_scaled, with_grad=True)
     ws = nsa.workspace(s, nsa.OP_BACKWARD, dev)
+    wsf = nsa.workspace(s, nsa.OP_FORWARD, dev)
 
     def fwd():
         ck, cv = nsa.compress_kv(s, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"])
-        o, idx = nsa.forward(s, x["q"], x["k"], x["v"], ck, cv, x["w_g"], x["b_g"], want_idx=True)
-        return ck, cv, idx
+        _, saved, idx = nsa.forward_train(s, x["q"], x["k"], x["v"], ck, cv, x["w_g"], x["b_g"], want_idx=True,
+                                          ws=wsf)
+        return ck, cv, idx, saved
 
-    def bwd(ck, cv, idx):
+    def bwd(ck, cv, idx, saved):
         return nsa.backward(s, x["q"], x["k"], x["v"], ck, cv, x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"],
-                            x["w_g"], x["b_g"], idx, x["do"], ws=ws)
+                            x["w_g"], x["b_g"], idx, x["do"], ws=ws, saved=saved)
 
     bwd(*fwd())
     torch.cuda.synchronize()
@@ -201,39 +220,32 @@ def fwd_bwd(steps):
     for _ in range(steps):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         e[0].record()
-        ck, cv, idx = fwd()
+        ck, cv, idx, saved = fwd()
         e[1].record()
-        bwd(ck, cv, idx)
+        bwd(ck, cv, idx, saved)
         e[2].record()
         torch.cuda.synchronize()
         tf.append(e[0].elapsed_time(e[1]))
         tb.append(e[1].elapsed_time(e[2]))
     fms, bms = float(np.mean(tf)), float(np.mean(tb))
     ff, bf = prefill_flops(s)["total"], backward_flops(s)["total"]
+    # the backward that recomputes every branch's statistics, and the plain
+    # (inference) forward
+    rms = _timed(lambda: bwd(ck, cv, idx, None), steps)
+    pms = _timed(lambda: nsa.forward(s, x["q"], x["k"], x["v"], ck, cv, x["w_g"], x["b_g"], ws=wsf), steps)
     # the same backward with the two-layer compression map (its second layers,
     # the recomputed hidden layers and the ReLU added to the linear map's work)
     wm = make_mlp_weights(s, 1007, dev)
     wsm = nsa.workspace(s, nsa.OP_BACKWARD_MLP, dev)
     ckm, cvm = nsa.compress_kv_mlp(s, x["k"], x["v"], x["w_ck"], x["pe_k"], wm["w2_k"], x["w_cv"], x["pe_v"],
                                    wm["w2_v"])
-
-    def bwd_mlp():
-        return nsa.backward_mlp(s, x["q"], x["k"], x["v"], ckm, cvm, x["w_ck"], x["pe_k"], wm["w2_k"], x["w_cv"],
-                                x["pe_v"], wm["w2_v"], x["w_g"], x["b_g"], idx, x["do"], ws=wsm)
-
-    bwd_mlp()
-    torch.cuda.synchronize()
-    tm = []
-    for _ in range(steps):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        e[0].record()
-        bwd_mlp()
-        e[1].record()
-        torch.cuda.synchronize()
-        tm.append(e[0].elapsed_time(e[1]))
-    mms = float(np.mean(tm))
+    _, saved_m = nsa.forward_train(s, x["q"], x["k"], x["v"], ckm, cvm, x["w_g"], x["b_g"], idx_in=idx, ws=wsf)
+    mms = _timed(lambda: nsa.backward_mlp(s, x["q"], x["k"], x["v"], ckm, cvm, x["w_ck"], x["pe_k"], wm["w2_k"],
+                                          x["w_cv"], x["pe_v"], wm["w2_v"], x["w_g"], x["b_g"], idx, x["do"], ws=wsm,
+                                          saved=saved_m), steps)
     return {"workload": "NSA fwd+bwd bf16 T=16384 (B=1, 4 KV x 16 q heads, d_k=192, d_v=128), dO ~ N(0,1)",
             "fwd_ms": round(fms, 3), "bwd_ms": round(bms, 3), "bwd_mlp_map_ms": round(mms, 3),
+            "bwd_recompute_ms": round(rms, 3), "fwd_inference_ms": round(pms, 3),
             "bwd_over_fwd": round(bms / fms, 2),
             "fwd_tflops": round(ff / (fms * 1e-3) / 1e12, 2), "bwd_algorithmic_tflop": round(bf / 1e12, 4),
             "bwd_tflops": round(bf / (bms * 1e-3) / 1e12, 2),

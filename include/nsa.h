@@ -246,6 +246,26 @@ nsa_status nsa_forward(const nsa_config *cfg, const void *q, const void *k, cons
                        const void *cmp_v, const void *w_g, const void *b_g, const int32_t *idx_in, void *o,
                        int32_t *idx_out, float *scores_out, void *ws, size_t ws_bytes, void *stream);
 
+/* nsa_forward for training: the same results, and each branch's softmax
+ * statistics saved for the backward calls below.  The branches and their
+ * softmaxes are nsa_forward's; keeping a softmax's row statistics so that its
+ * backward need not recompute them is the FlashAttention practice.  For
+ * branch c (0 compressed, 1 selected, 2 window), row t of
+ * sequence b and query head h:
+ *   lse      [3][B][T][Hq] fp32: the natural log of sum_i exp(scale q.K_i)
+ *            over the branch's keys, -inf when the branch has none (the
+ *            compressed branch for t < 31, or an index list with no valid
+ *            block)
+ *   o_branch [3][B][T][Hq][dv] config dtype: the branch's normalised output
+ *            before gating (0 where lse is -inf)
+ * so o = sum_c g_c o_branch[c] up to rounding.  Both are required (NULL:
+ * NSA_ERR_NULL) and 16-byte aligned; every element is written.  Workspace
+ * as nsa_forward (NSA_OP_FORWARD). */
+nsa_status nsa_forward_train(const nsa_config *cfg, const void *q, const void *k, const void *v, const void *cmp_k,
+                             const void *cmp_v, const void *w_g, const void *b_g, const int32_t *idx_in, void *o,
+                             int32_t *idx_out, float *scores_out, float *lse, void *o_branch, void *ws,
+                             size_t ws_bytes, void *stream);
+
 /* One decode step for B sequences (valuable12.com section III.3: at 64k
  * context a step reads 5,632 tokens' keys and values instead of 65,536).
  * cfg->T is the cache capacity.  Sequence b holds seq_lens[b] tokens
@@ -290,12 +310,19 @@ nsa_status nsa_decode_step_noalloc(const nsa_config *cfg, const int32_t *seq_len
  * treats their bf16 rounding as the identity.  idx is what nsa_forward used
  * (its idx_out, or the idx_in given to it); d_o [B][T][Hq][dv] config dtype.
  * The result is deterministic (no floating-point atomics).
+ * lse_saved, o_saved: both NULL, or both the lse and o_branch that
+ * nsa_forward_train wrote for these inputs and this idx (one without the
+ * other: NSA_ERR_NULL).  With them the backward reads each branch's
+ * log-sum-exp and d_o . o_branch instead of recomputing them (the 16-head,
+ * bf16 configurations at d_k/d_v = 192/128, 128/128, 64/64; others ignore
+ * them); the gradients agree with the recomputing call to rounding.
  * ws: nsa_workspace_bytes(cfg, NSA_OP_BACKWARD) bytes.  B*H_kv <= 65535. */
 nsa_status nsa_backward(const nsa_config *cfg, const void *q, const void *k, const void *v, const void *cmp_k,
                         const void *cmp_v, const void *w_ck, const void *pe_k, const void *w_cv, const void *pe_v,
                         const void *w_g, const void *b_g, const int32_t *idx, const void *d_o, void *d_q,
                         void *d_k, void *d_v, float *d_wck, float *d_pek, float *d_wcv, float *d_pev,
-                        float *d_wg, float *d_bg, void *ws, size_t ws_bytes, void *stream);
+                        float *d_wg, float *d_bg, const float *lse_saved, const void *o_saved, void *ws,
+                        size_t ws_bytes, void *stream);
 
 /* Backward pass with the two-layer compression map of nsa_compress_kv_mlp
  * (deepdaiv newsletter: a small network summarises each block, and the
@@ -306,15 +333,17 @@ nsa_status nsa_backward(const nsa_config *cfg, const void *q, const void *k, con
  *   d_w1v [dv][32*dv], d_pev [32][dv], d_w2v [dv][dv]              fp32
  * in place of the linear map's gradients.  The hidden layer is recomputed;
  * its bf16 rounding and the output's are treated as the identity, and the
- * ReLU's derivative is taken as 0 at 0.  Deterministic.  ws:
- * nsa_workspace_bytes(cfg, NSA_OP_BACKWARD_MLP) bytes (nsa_backward's plus
- * the hidden layers and their gradient), 256-byte aligned.  B*H_kv <= 65535. */
+ * ReLU's derivative is taken as 0 at 0.  Deterministic.  lse_saved,
+ * o_saved as in nsa_backward.  ws: nsa_workspace_bytes(cfg,
+ * NSA_OP_BACKWARD_MLP) bytes (nsa_backward's plus the hidden layers and their
+ * gradient), 256-byte aligned.  B*H_kv <= 65535. */
 nsa_status nsa_backward_mlp(const nsa_config *cfg, const void *q, const void *k, const void *v, const void *cmp_k,
                             const void *cmp_v, const void *w1_k, const void *pe_k, const void *w2_k,
                             const void *w1_v, const void *pe_v, const void *w2_v, const void *w_g, const void *b_g,
                             const int32_t *idx, const void *d_o, void *d_q, void *d_k, void *d_v, float *d_w1k,
                             float *d_pek, float *d_w2k, float *d_w1v, float *d_pev, float *d_w2v, float *d_wg,
-                            float *d_bg, void *ws, size_t ws_bytes, void *stream);
+                            float *d_bg, const float *lse_saved, const void *o_saved, void *ws, size_t ws_bytes,
+                            void *stream);
 
 /* DSA-style decode step (DSA explainer, allinfo.ai.kr, section "쉽게
  * 이해하기": a lightning indexer with several small heads and one key per

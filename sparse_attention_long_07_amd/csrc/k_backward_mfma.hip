@@ -337,6 +337,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
 //   2. S^T, dP^T again; dS^T = scale p (gate dP - D) feeds dQ^T += K^T dS^T
 //      directly from the score layout; K reaches the A operand through LDS,
 //      read with transposing reads.
+// SAVED: the forward kept each branch's log-sum-exp and output, so sweep 1
+// becomes one read of them (dO . o_branch as a dot product), as FlashAttention
+// does with its saved softmax statistics, and every key is visited once.
 // Chunks (as in the forward): compressed blocks [0, nvis), 16 i + 31 <= t;
 // the distinct valid selected blocks in ascending order, tokens <= t; the
 // window [t - w + 1, t].  The compressed and window chunks of the 4 positions
@@ -347,7 +350,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
 // and passes K through a private 32-key LDS buffer.  Loads of keys outside a
 // range read the nearest valid key instead, so no unwritten or stale value
 // enters a product.
-template <int DK, int DV>
+template <int DK, int DV, bool SAVED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_rows_mfma(BwdArgs a)
 {
     constexpr int KS = DK + 16, VS = DV + 16;
@@ -462,24 +465,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         acc = __builtin_fmaf(acc, al, as);
         m = mn;
     };
-    // the branch's statistics from its sweep-1 sums
+    // the branch's statistics from lse (log2 units) and dO . o_branch
+    auto put_stats = [&](int br, float lse2, float dOo, float &D) {
+        const float gv = gate[br];
+        D = gv * dOo;
+        dzs[br] = dOo * gv * (1.f - gv);
+        if (act && lg == 0) {
+            float *st = a.rs + (row0 + h) * kBwdStat + br * 4;
+            st[0] = lse2 * kLn2;
+            st[1] = D;
+            st[2] = gv;
+            st[3] = dzs[br];
+        }
+    };
+    // ... from the sweep-1 sums
     auto finish = [&](int br, float m, float l, float acc, float &lse2, float &D) {
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
         acc += __shfl_xor(acc, 16);
         acc += __shfl_xor(acc, 32);
         lse2 = l > 0.f ? m + fast_log2(l) : -INFINITY;
-        const float dOo = l > 0.f ? acc / l : 0.f;
-        const float gv = gate[br];
-        D = gv * dOo;
-        dzs[br] = dOo * gv * (1.f - gv);
-        if (act && lg == 0) {
-            float *st = a.rs + (row0 + h) * kBwdStat + br * 4;
-            st[0] = lse2 * 0.6931471805599453f;
-            st[1] = D;
-            st[2] = gv;
-            st[3] = dzs[br];
-        }
+        put_stats(br, lse2, l > 0.f ? acc / l : 0.f, D);
+    };
+    // ... from the forward's saved log-sum-exp and branch output (o_branch
+    // row of head h, columns 32 c + 8 lg .. +7 as in of[c])
+    auto from_saved = [&](int br, float &lse2, float &D) {
+        const long slot = (long)d.B * d.T * d.Hq;
+        lse2 = a.lse_sv[br * slot + row0 + h] * kLog2e;
+        const uint16_t *orow = (const uint16_t *)a.o_sv + (br * slot + row0 + h) * DV + 8 * lg;
+        float dOo = 0.f;
+#pragma unroll
+        for (int c = 0; c < NO; c++) dOo = dot8_bf16(of[c], ld16(orow + 32 * c), dOo);
+        dOo += __shfl_xor(dOo, 16);
+        dOo += __shfl_xor(dOo, 32);
+        put_stats(br, lse2, dOo, D);
     };
     // ds of a tile's 4 keys per lane, scaled
     auto tile_ds = [&](const f32x4 &S, const f32x4 &P, int k16, int klo, int khi, float lse2, float gv, float D,
@@ -522,27 +541,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             lds_barrier();   // the shared chunk of the compressed branch is no longer read
             const uint16_t *K = (const uint16_t *)a.k + bgi * d.T * DK;
             const uint16_t *V = (const uint16_t *)a.v + bgi * d.T * DV;
-            float m = -INFINITY, l = 0.f, acc = 0.f;
-            for (int ch = 0; ch < nsel; ch++) {
-                const int key0 = 64 * blk[ch], khi = min(t, key0 + 63);
-                float sc[4][4], dp[4][4];
-#pragma unroll
-                for (int kt = 0; kt < 4; kt++) {
-                    f32x4 S, P;
-                    u32x4 kfr[NQ];
-                    const int row = min(key0 + 16 * kt + li, khi);   // rows past the range read its last key
-                    tile_scores(K + (long)(row - li) * DK, DK, V + (long)(row - li) * DV, DV, S, P, kfr);
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        const int key = key0 + 16 * kt + 4 * lg + e;
-                        sc[kt][e] = key <= khi ? S[e] * sl2 : -INFINITY;
-                        dp[kt][e] = P[e];
-                    }
-                }
-                online(sc, dp, m, l, acc);
-            }
             float lse2, D;
-            finish(1, m, l, acc, lse2, D);
+            if constexpr (SAVED) from_saved(1, lse2, D);
+            else {
+                float m = -INFINITY, l = 0.f, acc = 0.f;
+                for (int ch = 0; ch < nsel; ch++) {
+                    const int key0 = 64 * blk[ch], khi = min(t, key0 + 63);
+                    float sc[4][4], dp[4][4];
+#pragma unroll
+                    for (int kt = 0; kt < 4; kt++) {
+                        f32x4 S, P;
+                        u32x4 kfr[NQ];
+                        const int row = min(key0 + 16 * kt + li, khi);   // rows past the range read its last key
+                        tile_scores(K + (long)(row - li) * DK, DK, V + (long)(row - li) * DV, DV, S, P, kfr);
+#pragma unroll
+                        for (int e = 0; e < 4; e++) {
+                            const int key = key0 + 16 * kt + 4 * lg + e;
+                            sc[kt][e] = key <= khi ? S[e] * sl2 : -INFINITY;
+                            dp[kt][e] = P[e];
+                        }
+                    }
+                    online(sc, dp, m, l, acc);
+                }
+                finish(1, m, l, acc, lse2, D);
+            }
             for (int ch = 0; ch < nsel; ch++) {
                 const int key0 = 64 * blk[ch], khi = min(t, key0 + 63);
 #pragma unroll
@@ -589,30 +611,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 }
             }
         };
-        float m = -INFINITY, l = 0.f, acc = 0.f;
-        for (int ch = 0; ch < nch; ch++) {
-            const int key0 = glo + 64 * ch;
-            lds_barrier();
-            stage(key0);
-            lds_barrier();
-            if (max(key0, klo) > min(key0 + 63, khi)) continue;   // nothing this row sees
-            float sc[4][4], dp[4][4];
-#pragma unroll
-            for (int kt = 0; kt < 4; kt++) {
-                f32x4 S, P;
-                u32x4 kfr[NQ];
-                tile_scores(ksh + 16 * kt * KS, KS, vsh + 16 * kt * VS, VS, S, P, kfr);
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int key = key0 + 16 * kt + 4 * lg + e;
-                    sc[kt][e] = key >= klo && key <= khi ? S[e] * sl2 : -INFINITY;
-                    dp[kt][e] = P[e];
-                }
-            }
-            online(sc, dp, m, l, acc);
-        }
         float lse2, D;
-        finish(br, m, l, acc, lse2, D);
+        if constexpr (SAVED) from_saved(br, lse2, D);
+        else {
+            float m = -INFINITY, l = 0.f, acc = 0.f;
+            for (int ch = 0; ch < nch; ch++) {
+                const int key0 = glo + 64 * ch;
+                lds_barrier();
+                stage(key0);
+                lds_barrier();
+                if (max(key0, klo) > min(key0 + 63, khi)) continue;   // nothing this row sees
+                float sc[4][4], dp[4][4];
+#pragma unroll
+                for (int kt = 0; kt < 4; kt++) {
+                    f32x4 S, P;
+                    u32x4 kfr[NQ];
+                    tile_scores(ksh + 16 * kt * KS, KS, vsh + 16 * kt * VS, VS, S, P, kfr);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const int key = key0 + 16 * kt + 4 * lg + e;
+                        sc[kt][e] = key >= klo && key <= khi ? S[e] * sl2 : -INFINITY;
+                        dp[kt][e] = P[e];
+                    }
+                }
+                online(sc, dp, m, l, acc);
+            }
+            finish(br, m, l, acc, lse2, D);
+        }
         for (int ch = 0; ch < nch; ch++) {
             const int key0 = glo + 64 * ch;
             lds_barrier();
@@ -803,9 +828,15 @@ hipError_t launch_bwd_rows_mfma(const BwdArgs &A, hipStream_t s)
 {
     const Dims &d = A.d;
     const dim3 grid((d.T + kThreads / 64 - 1) / (kThreads / 64), d.Hkv, d.B);
-    if (d.dk == 192) hipLaunchKernelGGL((k_bwd_rows_mfma<192, 128>), grid, dim3(kThreads), 0, s, A);
-    else if (d.dk == 128) hipLaunchKernelGGL((k_bwd_rows_mfma<128, 128>), grid, dim3(kThreads), 0, s, A);
-    else hipLaunchKernelGGL((k_bwd_rows_mfma<64, 64>), grid, dim3(kThreads), 0, s, A);
+    if (A.lse_sv) {
+        if (d.dk == 192) hipLaunchKernelGGL((k_bwd_rows_mfma<192, 128, true>), grid, dim3(kThreads), 0, s, A);
+        else if (d.dk == 128) hipLaunchKernelGGL((k_bwd_rows_mfma<128, 128, true>), grid, dim3(kThreads), 0, s, A);
+        else hipLaunchKernelGGL((k_bwd_rows_mfma<64, 64, true>), grid, dim3(kThreads), 0, s, A);
+    } else {
+        if (d.dk == 192) hipLaunchKernelGGL((k_bwd_rows_mfma<192, 128, false>), grid, dim3(kThreads), 0, s, A);
+        else if (d.dk == 128) hipLaunchKernelGGL((k_bwd_rows_mfma<128, 128, false>), grid, dim3(kThreads), 0, s, A);
+        else hipLaunchKernelGGL((k_bwd_rows_mfma<64, 64, false>), grid, dim3(kThreads), 0, s, A);
+    }
     return hipGetLastError();
 }
 

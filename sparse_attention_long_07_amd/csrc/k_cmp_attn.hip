@@ -439,6 +439,8 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
     if (h == 0 && (lane & 15) == 0 && live && 16 * ntw <= tb) srow[16 * ntw] = carry;
 
     if (WITH_V && live) {
+        // the branch's log-sum-exp for the backward, when asked for
+        if (a.lse && h == 0) a.lse[((long)b * a.R + t) * d.Hq + g * 16 + head] = lse2 * kLn2;
         uint16_t *orow = (uint16_t *)a.ocmp + (((long)b * a.R + t) * d.Hq + g * 16 + head) * DV;
 #pragma unroll
         for (int dt = 0; dt < DT; dt++)

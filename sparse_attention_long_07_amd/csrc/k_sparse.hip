@@ -328,26 +328,33 @@ __global__ __launch_bounds__(kWThreads) void k_window_mfma(RowArgs a, int ntp)
     const float ltot = l + __shfl_xor(l, 32, 64);
     if (!live) return;
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    const long ooff = (((long)b * a.R + t) * d.Hq + g * 16 + head) * DV;
+    const long rh = ((long)b * a.R + t) * d.Hq + g * 16 + head;
+    const long ooff = rh * DV;
     const uint16_t *oc = (const uint16_t *)a.ocmp + ooff;
     uint16_t *orow = (uint16_t *)a.o + ooff;
+    // saved statistics for the backward (slot 2: the window branch)
+    const long slot = (long)d.B * a.R * d.Hq;
+    uint16_t *osv = a.osave ? (uint16_t *)a.osave + 2 * slot * DV + ooff : nullptr;
+    if (a.lse && h == 0) a.lse[2 * slot + rh] = ltot > 0.f ? (m + fast_log2(ltot)) * kLn2 : -INFINITY;
 #pragma unroll
     for (int dt = 0; dt < DT; dt++)
 #pragma unroll
         for (int q4 = 0; q4 < 4; q4++) {
             const int dv = 32 * dt + 8 * q4 + 4 * h;
             const uint2 cv = *(const uint2 *)(oc + dv);
-            float y[4];
+            float y[4], ow[4];
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const uint32_t word = e < 2 ? cv.x : cv.y;
                 const float ocv = __uint_as_float(e & 1 ? word & 0xffff0000u : word << 16);
-                y[e] = gate[0] * ocv + gate[2] * oacc[dt][4 * q4 + e] * inv;
+                ow[e] = oacc[dt][4 * q4 + e] * inv;
+                y[e] = gate[0] * ocv + gate[2] * ow[e];
             }
             uint2 w;
             w.x = pack_bf16x2(y[0], y[1]);
             w.y = pack_bf16x2(y[2], y[3]);
             *(uint2 *)(orow + dv) = w;
+            if (osv) *(uint2 *)(osv + dv) = uint2{pack_bf16x2(ow[0], ow[1]), pack_bf16x2(ow[2], ow[3])};
         }
 }
 
@@ -490,7 +497,8 @@ __global__ __launch_bounds__(kThreads) void k_selected_mfma(RowArgs a, const uin
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
     const float w = l > 0.f ? gsl / l : 0.f;
-    uint16_t *orow = (uint16_t *)a.o + (((long)b * a.R + t) * d.Hq + g * 16 + hd) * DV + 4 * q;
+    const long rh = ((long)b * a.R + t) * d.Hq + g * 16 + hd;
+    uint16_t *orow = (uint16_t *)a.o + rh * DV + 4 * q;
 #pragma unroll
     for (int dt = 0; dt < DT; dt++) {
         uint2 cur = *(uint2 *)(orow + 16 * dt);
@@ -503,6 +511,17 @@ __global__ __launch_bounds__(kThreads) void k_selected_mfma(RowArgs a, const uin
         cur.x = pack_bf16x2(y[0], y[1]);
         cur.y = pack_bf16x2(y[2], y[3]);
         *(uint2 *)(orow + 16 * dt) = cur;
+    }
+    // saved statistics for the backward (slot 1: the selected branch)
+    if (a.lse) {
+        const long slot = (long)d.B * a.R * d.Hq;
+        if (q == 0) a.lse[slot + rh] = l > 0.f ? (m + fast_log2(l)) * kLn2 : -INFINITY;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        uint16_t *osv = (uint16_t *)a.osave + (slot + rh) * DV + 4 * q;
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++)
+            *(uint2 *)(osv + 16 * dt) = uint2{pack_bf16x2(oacc[dt][0] * inv, oacc[dt][1] * inv),
+                                              pack_bf16x2(oacc[dt][2] * inv, oacc[dt][3] * inv)};
     }
 }
 

@@ -232,6 +232,8 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_generic(RowArgs a)
 
     float *srow = a.scores + (((long)b * d.Hkv + g) * a.R + r) * d.nb;
     for (int j = tid; j < d.nb; j += kThreads) srow[j] = j <= jcur ? S[j] : -INFINITY;
+    // the branch's log-sum-exp for the backward, when asked for
+    if (WITH_V && a.lse && tid < G) a.lse[((long)b * a.R + r) * d.Hq + (long)g * G + tid] = lse_s[tid];
     if (WITH_V) {
         T *orow = (T *)a.ocmp + (((long)b * a.R + r) * d.Hq + (long)g * G) * dv;
 #pragma unroll
@@ -384,6 +386,18 @@ __global__ __launch_bounds__(kThreads) void k_sparse_generic(RowArgs a)
             int e = tid + u * kThreads;
             int h = e / dv;
             res[br][u] = (u < nout && e < G * dv && l_s[h < 16 ? h : 0] > 0.f) ? acc[u] / l_s[h] : 0.f;
+        }
+        // saved statistics for the backward: slot 1 selected, slot 2 window
+        if (a.lse) {
+            const long slot = (long)d.B * a.R * d.Hq, rh = ((long)b * a.R + r) * d.Hq + (long)g * G;
+            if (tid < G) a.lse[(1 + br) * slot + rh + tid] = l_s[tid] > 0.f ? m_s[tid] + __logf(l_s[tid]) : -INFINITY;
+            T *osv = (T *)a.osave + ((1 + br) * slot + rh) * dv;
+#pragma unroll
+            for (int u = 0; u < 16; u++) {
+                if (u >= nout) break;
+                const int e = tid + u * kThreads;
+                if (e < G * dv) osv[e] = from_f<T>(res[br][u]);
+            }
         }
         __syncthreads();
     }

@@ -450,22 +450,36 @@ nsa_status nsa_select_blocks(const nsa_config *cfg, const void *q, const void *c
     return nsa_select_topn(cfg, scores, idx_out, stream);
 }
 
-nsa_status nsa_forward(const nsa_config *cfg, const void *q, const void *k, const void *v, const void *cmp_k,
-                       const void *cmp_v, const void *w_g, const void *b_g, const int32_t *idx_in, void *o,
-                       int32_t *idx_out, float *scores_out, void *ws, size_t ws_bytes, void *stream)
+// The prefill forward; with lse and o_branch (both or neither) it also saves
+// each branch's log-sum-exp and output for the backward.
+static nsa_status forward_impl(const nsa_config *cfg, const void *q, const void *k, const void *v, const void *cmp_k,
+                               const void *cmp_v, const void *w_g, const void *b_g, const int32_t *idx_in, void *o,
+                               int32_t *idx_out, float *scores_out, float *lse, void *o_branch, void *ws,
+                               size_t ws_bytes, void *stream)
 {
     Dims d;
     nsa_status st = check_config(cfg, &d);
     if (st != NSA_OK) return st;
     if (!q || !k || !v || !cmp_k || !cmp_v || !w_g || !b_g || !o) return NSA_ERR_NULL;
-    if (!all_aligned({q, k, v, cmp_k, cmp_v, w_g, b_g, idx_in, o, idx_out, scores_out})) return NSA_ERR_ALIGN;
+    if (!all_aligned({q, k, v, cmp_k, cmp_v, w_g, b_g, idx_in, o, idx_out, scores_out, lse, o_branch}))
+        return NSA_ERR_ALIGN;
     Layout L;
     if ((st = check_ws(d, d.T, ws, ws_bytes, &L)) != NSA_OK) return st;
     char *w = (char *)ws;
     hipStream_t s = (hipStream_t)stream;
-    void *ocmp = w + L.ocmp;
+    // with saved statistics the compressed-branch output goes to its slot
+    void *ocmp = o_branch ? o_branch : (void *)(w + L.ocmp);
     float *scores = scores_out ? scores_out : (float *)(w + L.scores);
-    if ((st = nsa_compressed_attention(cfg, q, cmp_k, cmp_v, ocmp, scores, stream)) != NSA_OK) return st;
+    {
+        RowArgs a = prefill_args(d, q);
+        a.kc = cmp_k;
+        a.vc = cmp_v;
+        a.ocmp = ocmp;
+        a.scores = scores;
+        a.lse = lse;
+        if (cmp_attn_mfma_supported(d)) NSA_TRY(launch_cmp_attn_mfma(a, true, s));
+        else NSA_TRY(launch_cmp_attn_generic(a, true, s));
+    }
     const int32_t *idx = idx_in;
     if (idx_in) {
         if (idx_out)
@@ -476,7 +490,40 @@ nsa_status nsa_forward(const nsa_config *cfg, const void *q, const void *k, cons
         if ((st = nsa_select_topn(cfg, scores, sel, stream)) != NSA_OK) return st;
         idx = sel;
     }
-    return nsa_sparse_attention(cfg, q, k, v, ocmp, idx, w_g, b_g, o, w + L.vt, L.total - L.vt, stream);
+    RowArgs a = prefill_args(d, q);
+    a.k = k;
+    a.v = v;
+    a.ocmp = ocmp;
+    a.idx = idx;
+    a.wg = w_g;
+    a.bg = b_g;
+    a.o = o;
+    a.lse = lse;
+    a.osave = o_branch;
+    if (sparse_mfma_supported(d)) return hip_status(launch_sparse_mfma(a, w + L.vt, s));
+    return hip_status(launch_sparse_generic(a, s));
+}
+
+nsa_status nsa_forward(const nsa_config *cfg, const void *q, const void *k, const void *v, const void *cmp_k,
+                       const void *cmp_v, const void *w_g, const void *b_g, const int32_t *idx_in, void *o,
+                       int32_t *idx_out, float *scores_out, void *ws, size_t ws_bytes, void *stream)
+{
+    return forward_impl(cfg, q, k, v, cmp_k, cmp_v, w_g, b_g, idx_in, o, idx_out, scores_out, nullptr, nullptr, ws,
+                        ws_bytes, stream);
+}
+
+nsa_status nsa_forward_train(const nsa_config *cfg, const void *q, const void *k, const void *v, const void *cmp_k,
+                             const void *cmp_v, const void *w_g, const void *b_g, const int32_t *idx_in, void *o,
+                             int32_t *idx_out, float *scores_out, float *lse, void *o_branch, void *ws,
+                             size_t ws_bytes, void *stream)
+{
+    if (!lse || !o_branch) {
+        Dims d;
+        const nsa_status st = check_config(cfg, &d);
+        return st != NSA_OK ? st : NSA_ERR_NULL;
+    }
+    return forward_impl(cfg, q, k, v, cmp_k, cmp_v, w_g, b_g, idx_in, o, idx_out, scores_out, lse, o_branch, ws,
+                        ws_bytes, stream);
 }
 
 nsa_status nsa_decode_step(const nsa_config *cfg, const int32_t *seq_lens, const void *q, const void *k_cache,
@@ -554,17 +601,18 @@ nsa_status nsa_backward(const nsa_config *cfg, const void *q, const void *k, con
                         const void *cmp_v, const void *w_ck, const void *pe_k, const void *w_cv, const void *pe_v,
                         const void *w_g, const void *b_g, const int32_t *idx, const void *d_o, void *d_q,
                         void *d_k, void *d_v, float *d_wck, float *d_pek, float *d_wcv, float *d_pev,
-                        float *d_wg, float *d_bg, void *ws, size_t ws_bytes, void *stream)
+                        float *d_wg, float *d_bg, const float *lse_saved, const void *o_saved, void *ws,
+                        size_t ws_bytes, void *stream)
 {
     Dims d;
     nsa_status st = check_config(cfg, &d);
     if (st != NSA_OK) return st;
     if ((long)d.B * d.Hkv > 65535) return NSA_ERR_SHAPE;
     if (!q || !k || !v || !cmp_k || !cmp_v || !w_ck || !pe_k || !w_cv || !pe_v || !w_g || !b_g || !idx || !d_o ||
-        !d_q || !d_k || !d_v || !d_wck || !d_pek || !d_wcv || !d_pev || !d_wg || !d_bg)
+        !d_q || !d_k || !d_v || !d_wck || !d_pek || !d_wcv || !d_pev || !d_wg || !d_bg || (!lse_saved) != (!o_saved))
         return NSA_ERR_NULL;
     if (!all_aligned({q, k, v, cmp_k, cmp_v, w_ck, pe_k, w_cv, pe_v, w_g, b_g, idx, d_o, d_q, d_k, d_v, d_wck,
-                      d_pek, d_wcv, d_pev, d_wg, d_bg}))
+                      d_pek, d_wcv, d_pev, d_wg, d_bg, lse_saved, o_saved}))
         return NSA_ERR_ALIGN;
     const size_t need = backward_layout(d, nullptr, nullptr);
     if (!ws || ws_bytes < need) return NSA_ERR_WORKSPACE;
@@ -594,6 +642,8 @@ nsa_status nsa_backward(const nsa_config *cfg, const void *q, const void *k, con
     A.dpev = d_pev;
     A.dwg = d_wg;
     A.dbg = d_bg;
+    A.lse_sv = lse_saved;
+    A.o_sv = o_saved;
     backward_layout(d, ws, &A);
     return hip_status(launch_backward(A, (hipStream_t)stream));
 }
@@ -603,7 +653,8 @@ nsa_status nsa_backward_mlp(const nsa_config *cfg, const void *q, const void *k,
                             const void *w1_v, const void *pe_v, const void *w2_v, const void *w_g, const void *b_g,
                             const int32_t *idx, const void *d_o, void *d_q, void *d_k, void *d_v, float *d_w1k,
                             float *d_pek, float *d_w2k, float *d_w1v, float *d_pev, float *d_w2v, float *d_wg,
-                            float *d_bg, void *ws, size_t ws_bytes, void *stream)
+                            float *d_bg, const float *lse_saved, const void *o_saved, void *ws, size_t ws_bytes,
+                            void *stream)
 {
     Dims d;
     nsa_status st = check_config(cfg, &d);
@@ -611,10 +662,10 @@ nsa_status nsa_backward_mlp(const nsa_config *cfg, const void *q, const void *k,
     if ((long)d.B * d.Hkv > 65535) return NSA_ERR_SHAPE;
     if (!q || !k || !v || !cmp_k || !cmp_v || !w1_k || !pe_k || !w2_k || !w1_v || !pe_v || !w2_v || !w_g || !b_g ||
         !idx || !d_o || !d_q || !d_k || !d_v || !d_w1k || !d_pek || !d_w2k || !d_w1v || !d_pev || !d_w2v || !d_wg ||
-        !d_bg)
+        !d_bg || (!lse_saved) != (!o_saved))
         return NSA_ERR_NULL;
     if (!all_aligned({q, k, v, cmp_k, cmp_v, w1_k, pe_k, w2_k, w1_v, pe_v, w2_v, w_g, b_g, idx, d_o, d_q, d_k, d_v,
-                      d_w1k, d_pek, d_w2k, d_w1v, d_pev, d_w2v, d_wg, d_bg}))
+                      d_w1k, d_pek, d_w2k, d_w1v, d_pev, d_w2v, d_wg, d_bg, lse_saved, o_saved}))
         return NSA_ERR_ALIGN;
     const size_t need = backward_layout(d, nullptr, nullptr, true);
     if (!ws || ws_bytes < need) return NSA_ERR_WORKSPACE;
@@ -649,6 +700,8 @@ nsa_status nsa_backward_mlp(const nsa_config *cfg, const void *q, const void *k,
     A.w2v = w2_v;
     A.dw2k = d_w2k;
     A.dw2v = d_w2v;
+    A.lse_sv = lse_saved;
+    A.o_sv = o_saved;
     backward_layout(d, ws, &A, true);
     return hip_status(launch_backward(A, (hipStream_t)stream));
 }

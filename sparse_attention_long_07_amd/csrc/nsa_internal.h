@@ -73,6 +73,13 @@ struct RowArgs {
     long o_sb, o_sr;
     int part;                   // sparse stage: 0 everything, 1 window (o written), 2 selected from packed blocks
                                 // (added to o), 3 pack K/V blocks only
+    // Saved statistics for the backward (prefill only), or nullptr: per branch
+    // c (0 compressed, 1 selected, 2 window) the natural-log log-sum-exp of
+    // its softmax, lse[c][B][R][Hq] (-inf for an empty branch), and its
+    // normalised output, osave[c][B][R][Hq][dv] in the storage dtype.  The
+    // compressed branch's output is ocmp, which then points at slot 0.
+    float *lse;
+    void *osave;
 };
 
 // Arguments of the matrix-core decode step (one row per sequence).  Each
@@ -130,6 +137,11 @@ struct BwdArgs {
     float *dw2k, *dw2v;
     void *hk, *hv;
     float *da;
+    // the forward's saved statistics (RowArgs::lse, RowArgs::osave layouts,
+    // R = T) or nullptr: the row pass then takes lse and dO . o per branch
+    // from them instead of sweeping each branch's keys twice
+    const float *lse_sv;
+    const void *o_sv;
 };
 // per (row, head) row statistics of the backward: {lse, D, gate, dz} for each
 // of the 3 branches (compressed, selected, window)

@@ -24,7 +24,7 @@ STATUS = {0: "NSA_OK", -1: "NSA_ERR_NULL", -2: "NSA_ERR_SHAPE", -3: "NSA_ERR_DTY
 EXPORTS = ("nsa_workspace_bytes", "nsa_compress_kv", "nsa_compress_kv_mlp", "nsa_compress_append", "nsa_compress_append_mlp", "nsa_compressed_attention",
            "nsa_select_topn",
            "nsa_sparse_attention", "nsa_pack_kv_blocks", "nsa_window_attention", "nsa_selected_attention", "nsa_select_blocks",
-           "nsa_forward", "nsa_decode_step", "nsa_decode_step_noalloc", "nsa_backward", "nsa_backward_mlp", "nsa_dsa_decode", "nsa_dsa_prefill", "nsa_status_string")
+           "nsa_forward", "nsa_forward_train", "nsa_decode_step", "nsa_decode_step_noalloc", "nsa_backward", "nsa_backward_mlp", "nsa_dsa_decode", "nsa_dsa_prefill", "nsa_status_string")
 
 
 class NSAError(RuntimeError):
@@ -84,14 +84,16 @@ def lib() -> ctypes.CDLL:
         L.nsa_select_blocks.argtypes = [ctypes.POINTER(Config), _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.nsa_forward.restype = ctypes.c_int
         L.nsa_forward.argtypes = [ctypes.POINTER(Config)] + [_vp] * 12 + [ctypes.c_size_t, _vp]
+        L.nsa_forward_train.restype = ctypes.c_int
+        L.nsa_forward_train.argtypes = [ctypes.POINTER(Config)] + [_vp] * 14 + [ctypes.c_size_t, _vp]
         L.nsa_decode_step.restype = ctypes.c_int
         L.nsa_decode_step.argtypes = [ctypes.POINTER(Config)] + [_vp] * 12 + [ctypes.c_size_t, _vp]
         L.nsa_decode_step_noalloc.restype = ctypes.c_int
         L.nsa_decode_step_noalloc.argtypes = [ctypes.POINTER(Config)] + [_vp] * 12
         L.nsa_backward.restype = ctypes.c_int
-        L.nsa_backward.argtypes = [ctypes.POINTER(Config)] + [_vp] * 23 + [ctypes.c_size_t, _vp]
+        L.nsa_backward.argtypes = [ctypes.POINTER(Config)] + [_vp] * 25 + [ctypes.c_size_t, _vp]
         L.nsa_backward_mlp.restype = ctypes.c_int
-        L.nsa_backward_mlp.argtypes = [ctypes.POINTER(Config)] + [_vp] * 27 + [ctypes.c_size_t, _vp]
+        L.nsa_backward_mlp.argtypes = [ctypes.POINTER(Config)] + [_vp] * 29 + [ctypes.c_size_t, _vp]
         _lib = L
     return _lib
 
@@ -385,6 +387,46 @@ def forward(s: NSAShape, q, k, v, cmp_k, cmp_v, w_g, b_g, idx_in=None, o=None, w
     return out[0] if len(out) == 1 else tuple(out)
 
 
+def forward_train(s: NSAShape, q, k, v, cmp_k, cmp_v, w_g, b_g, idx_in=None, o=None, want_idx=False, ws=None):
+    """forward() that also saves each branch's softmax statistics for the
+    backward.  Returns o and saved = (lse [3,B,T,Hq] fp32, o_branch
+    [3,B,T,Hq,dv] config dtype), then idx if asked: (o, saved[, idx])."""
+    dt = _dt(s)
+    _req(q, "q", (s.B, s.T, s.Hq, s.dk), dt)
+    _req(k, "k", (s.B, s.Hkv, s.T, s.dk), dt)
+    _req(v, "v", (s.B, s.Hkv, s.T, s.dv), dt)
+    _req(cmp_k, "cmp_k", (s.B, s.Hkv, s.n_pad, s.dk), dt)
+    _req(cmp_v, "cmp_v", (s.B, s.Hkv, s.n_pad, s.dv), dt)
+    _req(w_g, "w_g", (s.Hq, 3, s.dk), dt)
+    _req(b_g, "b_g", (s.Hq, 3), dt)
+    if idx_in is not None:
+        _req(idx_in, "idx_in", (s.B, s.Hkv, s.T, s.n), torch.int32)
+    if o is None:
+        o = torch.empty((s.B, s.T, s.Hq, s.dv), dtype=dt, device=q.device)
+    _req(o, "o", (s.B, s.T, s.Hq, s.dv), dt)
+    idx = torch.empty((s.B, s.Hkv, s.T, s.n), dtype=torch.int32, device=q.device) if want_idx else None
+    lse = torch.empty((3, s.B, s.T, s.Hq), dtype=torch.float32, device=q.device)
+    obr = torch.empty((3, s.B, s.T, s.Hq, s.dv), dtype=dt, device=q.device)
+    if ws is None:
+        ws = workspace(s, OP_FORWARD, q.device)
+    c = config(s)
+    _check("nsa_forward_train",
+           lib().nsa_forward_train(ctypes.byref(c), _p(q), _p(k), _p(v), _p(cmp_k), _p(cmp_v), _p(w_g), _p(b_g),
+                                   _p(idx_in), _p(o), _p(idx), None, _p(lse), _p(obr), _p(ws), ws.numel(),
+                                   _stream()))
+    return (o, (lse, obr), idx) if want_idx else (o, (lse, obr))
+
+
+def _saved_ptrs(s: NSAShape, saved, dt):
+    """Pointers of a forward_train `saved` pair, or two NULLs."""
+    if saved is None:
+        return None, None
+    lse, obr = saved
+    _req(lse, "lse_saved", (3, s.B, s.T, s.Hq), torch.float32)
+    _req(obr, "o_saved", (3, s.B, s.T, s.Hq, s.dv), dt)
+    return _p(lse), _p(obr)
+
+
 def decode_step(s: NSAShape, seq_lens, q, k_cache, v_cache, cmp_k, cmp_v, w_g, b_g, idx_in=None, o=None,
                 want_idx=False, ws=None):
     """One decode step (s.T = cache capacity); returns o [B,Hq,dv] (and idx [B,Hkv,n])."""
@@ -502,10 +544,12 @@ def dsa_prefill(s: NSAShape, idx_heads, idx_dim, topk, q_idx, w_idx, k_idx, q, k
     return (sel_in if sel_in is not None else sel), o
 
 
-def backward(s: NSAShape, q, k, v, cmp_k, cmp_v, w_ck, pe_k, w_cv, pe_v, w_g, b_g, idx, d_o, ws=None):
+def backward(s: NSAShape, q, k, v, cmp_k, cmp_v, w_ck, pe_k, w_cv, pe_v, w_g, b_g, idx, d_o, ws=None,
+             saved=None):
     """Gradients of sum(d_o * o) with the selection idx held fixed.  Returns a
     dict d_q, d_k, d_v (config dtype) and d_wck, d_pek, d_wcv, d_pev, d_wg,
-    d_bg (fp32), in the layouts of the corresponding inputs."""
+    d_bg (fp32), in the layouts of the corresponding inputs.  saved: the
+    (lse, o_branch) pair forward_train returned for these inputs, or None."""
     dt = _dt(s)
     dev = q.device
     _req(q, "q", (s.B, s.T, s.Hq, s.dk), dt)
@@ -535,13 +579,13 @@ def backward(s: NSAShape, q, k, v, cmp_k, cmp_v, w_ck, pe_k, w_cv, pe_v, w_g, b_
                             _p(w_cv), _p(pe_v), _p(w_g), _p(b_g), _p(idx), _p(d_o),
                             *[_p(g[n]) for n in ("d_q", "d_k", "d_v", "d_wck", "d_pek", "d_wcv", "d_pev", "d_wg",
                                                  "d_bg")],
-                            _p(ws), ws.numel(), _stream())
+                            *_saved_ptrs(s, saved, dt), _p(ws), ws.numel(), _stream())
     _check("nsa_backward", st)
     return g
 
 
 def backward_mlp(s: NSAShape, q, k, v, cmp_k, cmp_v, w1_k, pe_k, w2_k, w1_v, pe_v, w2_v, w_g, b_g, idx, d_o,
-                 ws=None):
+                 ws=None, saved=None):
     """backward() with the two-layer compression map (compress_kv_mlp).
     Returns a dict d_q, d_k, d_v (config dtype) and d_w1k, d_pek, d_w2k,
     d_w1v, d_pev, d_w2v, d_wg, d_bg (fp32), in the layouts of the inputs."""
@@ -573,6 +617,6 @@ def backward_mlp(s: NSAShape, q, k, v, cmp_k, cmp_v, w1_k, pe_k, w2_k, w1_v, pe_
                                 _p(w2_k), _p(w1_v), _p(pe_v), _p(w2_v), _p(w_g), _p(b_g), _p(idx), _p(d_o),
                                 *[_p(g[n]) for n in ("d_q", "d_k", "d_v", "d_w1k", "d_pek", "d_w2k", "d_w1v", "d_pev",
                                                      "d_w2v", "d_wg", "d_bg")],
-                                _p(ws), ws.numel(), _stream())
+                                *_saved_ptrs(s, saved, dt), _p(ws), ws.numel(), _stream())
     _check("nsa_backward_mlp", st)
     return g

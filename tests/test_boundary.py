@@ -82,9 +82,10 @@ def test_bad_config_rejected_everywhere(kw, code):
     assert L.nsa_compress_append_mlp(c, f[0], f[1], 1, *f[:10], None) == code
     assert L.nsa_select_blocks(c, f[0], f[1], None, f[2], f[3], 1 << 40, None) == code
     assert L.nsa_forward(c, *f[:7], None, f[0], None, None, f[1], 1 << 40, None) == code
+    assert L.nsa_forward_train(c, *f[:7], None, f[0], None, None, f[1], f[2], f[3], 1 << 40, None) == code
     assert L.nsa_decode_step(c, *f[:8], None, f[0], None, f[1], 1 << 40, None) == code
-    assert L.nsa_backward(c, *([FAKE] * 22), FAKE, 1 << 40, None) == code
-    assert L.nsa_backward_mlp(c, *([FAKE] * 26), FAKE, 1 << 40, None) == code
+    assert L.nsa_backward(c, *([FAKE] * 22), None, None, FAKE, 1 << 40, None) == code
+    assert L.nsa_backward_mlp(c, *([FAKE] * 26), None, None, FAKE, 1 << 40, None) == code
     assert L.nsa_dsa_decode(c, 4, 64, 16, *([FAKE] * 10), FAKE, 1 << 40, None) == code
     assert L.nsa_dsa_prefill(c, 4, 64, 16, *([FAKE] * 9), FAKE, 1 << 40, None) == code
     assert L.nsa_sparse_attention(c, *f[:8], f[0], 1 << 40, None) == code
@@ -179,6 +180,41 @@ def test_forward_workspace_checks():
                          None) == ALIGN
     # optional outputs are checked for alignment too
     assert L.nsa_forward(ctypes.byref(c), *f, MIS, FAKE, None, None, FAKE, 0, None) == ALIGN
+
+
+@pytest.mark.parametrize("pos", range(10))
+def test_forward_train_checks(pos):
+    """nsa_forward_train: the forward's operands plus lse and o_branch, all
+    required and 16-byte aligned; workspace as nsa_forward's."""
+    L = nsa.lib()
+    c = cfg()
+    need = L.nsa_workspace_bytes(ctypes.byref(c), nsa.OP_FORWARD)
+    args = [FAKE] * 10          # q k v cmp_k cmp_v w_g b_g | o | lse o_branch
+    args[pos] = None
+    q, k, v, ck, cv, wg, bg, o, lse, obr = args
+    assert L.nsa_forward_train(ctypes.byref(c), q, k, v, ck, cv, wg, bg, None, o, None, None, lse, obr, FAKE, need,
+                               None) == NULL
+    args[pos] = MIS
+    q, k, v, ck, cv, wg, bg, o, lse, obr = args
+    assert L.nsa_forward_train(ctypes.byref(c), q, k, v, ck, cv, wg, bg, None, o, None, None, lse, obr, FAKE, need,
+                               None) == ALIGN
+    f = [FAKE] * 7
+    assert L.nsa_forward_train(ctypes.byref(c), *f, None, FAKE, None, None, FAKE, FAKE, FAKE, need - 1, None) == WS
+
+
+@pytest.mark.parametrize("mlp", [False, True])
+def test_backward_saved_pair_checks(mlp):
+    """The saved statistics go in pairs (lse with o_branch) and are aligned."""
+    L = nsa.lib()
+    c = ctypes.byref(cfg())
+    fn, nreq, op = (L.nsa_backward_mlp, 26, nsa.OP_BACKWARD_MLP) if mlp else (L.nsa_backward, 22, nsa.OP_BACKWARD)
+    need = L.nsa_workspace_bytes(c, op)
+    args = [FAKE] * nreq
+    assert fn(c, *args, FAKE, None, FAKE, need, None) == NULL
+    assert fn(c, *args, None, FAKE, FAKE, need, None) == NULL
+    assert fn(c, *args, MIS, FAKE, FAKE, need, None) == ALIGN
+    assert fn(c, *args, FAKE, MIS, FAKE, need, None) == ALIGN
+    assert fn(c, *args, FAKE, FAKE, FAKE, need - 1, None) == WS
 
 
 def test_select_and_decode_checks():
@@ -283,9 +319,9 @@ def test_backward_required_pointers(pos):
     need = L.nsa_workspace_bytes(c, nsa.OP_BACKWARD)
     args = [FAKE] * 22
     args[pos] = None
-    assert L.nsa_backward(c, *args, FAKE, need, None) == NULL
+    assert L.nsa_backward(c, *args, None, None, FAKE, need, None) == NULL
     args[pos] = MIS
-    assert L.nsa_backward(c, *args, FAKE, need, None) == ALIGN
+    assert L.nsa_backward(c, *args, None, None, FAKE, need, None) == ALIGN
 
 
 @pytest.mark.parametrize("pos", range(26))
@@ -295,9 +331,9 @@ def test_backward_mlp_required_pointers(pos):
     need = L.nsa_workspace_bytes(c, nsa.OP_BACKWARD_MLP)
     args = [FAKE] * 26
     args[pos] = None
-    assert L.nsa_backward_mlp(c, *args, FAKE, need, None) == NULL
+    assert L.nsa_backward_mlp(c, *args, None, None, FAKE, need, None) == NULL
     args[pos] = MIS
-    assert L.nsa_backward_mlp(c, *args, FAKE, need, None) == ALIGN
+    assert L.nsa_backward_mlp(c, *args, None, None, FAKE, need, None) == ALIGN
 
 
 def test_backward_mlp_workspace_checks():
@@ -310,10 +346,10 @@ def test_backward_mlp_workspace_checks():
     assert need >= base + s.B * s.Hkv * s.n_pad * (2 * (s.dk + s.dv) + 4 * (s.dk + s.dv))
     assert need % 256 == 0
     f = [FAKE] * 26
-    assert L.nsa_backward_mlp(ctypes.byref(c), *f, None, need, None) == WS
-    assert L.nsa_backward_mlp(ctypes.byref(c), *f, FAKE, need - 1, None) == WS
-    assert L.nsa_backward_mlp(ctypes.byref(c), *f, ctypes.c_void_p(0x10010), need, None) == ALIGN
-    assert L.nsa_backward_mlp(ctypes.byref(cfg(B=70000, H_kv=1, group=1)), *f, FAKE, 1 << 40, None) == SHAPE
+    assert L.nsa_backward_mlp(ctypes.byref(c), *f, None, None, None, need, None) == WS
+    assert L.nsa_backward_mlp(ctypes.byref(c), *f, None, None, FAKE, need - 1, None) == WS
+    assert L.nsa_backward_mlp(ctypes.byref(c), *f, None, None, ctypes.c_void_p(0x10010), need, None) == ALIGN
+    assert L.nsa_backward_mlp(ctypes.byref(cfg(B=70000, H_kv=1, group=1)), *f, None, None, FAKE, 1 << 40, None) == SHAPE
 
 
 def test_backward_workspace_checks():
@@ -325,11 +361,11 @@ def test_backward_workspace_checks():
     assert need >= 4 * (s.B * s.T * s.Hq * 12 + s.B * s.Hkv * s.T * (s.dk + s.dv))
     assert need % 256 == 0
     f = [FAKE] * 22
-    assert L.nsa_backward(ctypes.byref(c), *f, None, need, None) == WS
-    assert L.nsa_backward(ctypes.byref(c), *f, FAKE, need - 1, None) == WS
-    assert L.nsa_backward(ctypes.byref(c), *f, ctypes.c_void_p(0x10010), need, None) == ALIGN
+    assert L.nsa_backward(ctypes.byref(c), *f, None, None, None, need, None) == WS
+    assert L.nsa_backward(ctypes.byref(c), *f, None, None, FAKE, need - 1, None) == WS
+    assert L.nsa_backward(ctypes.byref(c), *f, None, None, ctypes.c_void_p(0x10010), need, None) == ALIGN
     # B * H_kv above the grid limit of the key passes
-    assert L.nsa_backward(ctypes.byref(cfg(B=70000, H_kv=1, group=1)), *f, FAKE, 1 << 40, None) == SHAPE
+    assert L.nsa_backward(ctypes.byref(cfg(B=70000, H_kv=1, group=1)), *f, None, None, FAKE, 1 << 40, None) == SHAPE
 
 
 @pytest.mark.parametrize("pos", range(8))

@@ -56,11 +56,19 @@ def _setup(s, seed, scaled, idx=None):
     return x
 
 
-def _gpu_bwd(s, x, d_o):
+def _gpu_bwd(s, x, d_o, saved=None):
     g = nsa.backward(s, x["q"], x["k"], x["v"], x["cmp_k"], x["cmp_v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"],
-                     x["w_g"], x["b_g"], x["idx"], d_o)
+                     x["w_g"], x["b_g"], x["idx"], d_o, saved=saved)
     torch.cuda.synchronize()
     return g
+
+
+def _gpu_saved(s, x):
+    """The training forward's saved statistics for x's inputs and selection."""
+    _, saved = nsa.forward_train(s, x["q"], x["k"], x["v"], x["cmp_k"], x["cmp_v"], x["w_g"], x["b_g"],
+                                 idx_in=x["idx"])
+    torch.cuda.synchronize()
+    return saved
 
 
 # Gradients that cancel to (near) zero in exact arithmetic take the scale of a
@@ -100,15 +108,18 @@ SMALL = [
 
 @pytest.mark.parametrize("name,s,scaled,randsel", SMALL, ids=[c[0] for c in SMALL])
 def test_backward_parity(name, s, scaled, randsel):
+    """Both forms of the call: recomputing every branch's statistics, and
+    with the training forward's saved statistics."""
     say("backward", name, s)
     x = _setup(s, 5, scaled, random_selection(s, 6) if randsel else None)
-    g = _gpu_bwd(s, x, x["do"])
     ref = _oracle_bwd(s, x, np64(x["do"]))
-    for rn, gn in PAIRS:
-        got = np64(g[gn])
-        assert got.shape == ref[rn].shape, gn
-        err = float(np.abs(got - ref[rn]).max())
-        assert err <= _tol(s, ref, rn), (gn, err, _tol(s, ref, rn))
+    for saved in (None, _gpu_saved(s, x)):
+        g = _gpu_bwd(s, x, x["do"], saved)
+        for rn, gn in PAIRS:
+            got = np64(g[gn])
+            assert got.shape == ref[rn].shape, gn
+            err = float(np.abs(got - ref[rn]).max())
+            assert err <= _tol(s, ref, rn), (gn, saved is not None, err, _tol(s, ref, rn))
 
 
 def test_backward_deterministic():
@@ -117,6 +128,11 @@ def test_backward_deterministic():
     x = _setup(s, 7, False, random_selection(s, 8))
     g1 = _gpu_bwd(s, x, x["do"])
     g2 = _gpu_bwd(s, x, x["do"])
+    for _, gn in PAIRS:
+        assert torch.equal(g1[gn], g2[gn]), gn
+    saved = _gpu_saved(s, x)
+    g1 = _gpu_bwd(s, x, x["do"], saved)
+    g2 = _gpu_bwd(s, x, x["do"], saved)
     for _, gn in PAIRS:
         assert torch.equal(g1[gn], g2[gn]), gn
 
@@ -149,6 +165,14 @@ def test_backward_full_size():
     ref = _oracle_bwd(s, x, np64(do_mask))
     say("gpu backward, masked dO")
     g = _gpu_bwd(s, x, do_mask.to(dt))
+    for rn, gn in PAIRS:
+        got = np64(g[gn])
+        err = float(np.abs(got - ref[rn]).max())
+        say(gn, "max err", err, "tol", _tol(s, ref, rn))
+        assert err <= _tol(s, ref, rn), (gn, err)
+    assert not np.any(np64(g["d_q"])[:, ~keep])
+    say("gpu backward, masked dO, saved statistics")
+    g = _gpu_bwd(s, x, do_mask.to(dt), _gpu_saved(s, x))
     for rn, gn in PAIRS:
         got = np64(g[gn])
         err = float(np.abs(got - ref[rn]).max())

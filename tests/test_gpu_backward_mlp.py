@@ -72,19 +72,22 @@ def test_backward_mlp_parity(name, s, scaled, randsel):
         idx = orc.forward(ocfg(s), np64(x["q"]), kc, vc, np64(x["k"]), np64(x["v"]), np64(x["w_g"]),
                           np64(x["b_g"]))["idx"]
     idx = np.ascontiguousarray(idx, dtype=np.int32)
-    g = nsa.backward_mlp(s, x["q"], x["k"], x["v"], torch.from_numpy(kc).to(dt).cuda(),
-                         torch.from_numpy(vc).to(dt).cuda(), x["w_ck"], x["pe_k"], w["w2_k"], x["w_cv"], x["pe_v"],
-                         w["w2_v"], x["w_g"], x["b_g"], torch.from_numpy(idx).cuda(), x["do"])
-    torch.cuda.synchronize()
+    kc_d, vc_d, idx_d = torch.from_numpy(kc).to(dt).cuda(), torch.from_numpy(vc).to(dt).cuda(), torch.from_numpy(idx).cuda()
     ref = orc.backward_mlp(ocfg(s), np64(x["q"]), np64(x["k"]), np64(x["v"]), np64(x["w_ck"]), np64(x["pe_k"]),
                            np64(w["w2_k"]), np64(x["w_cv"]), np64(x["pe_v"]), np64(w["w2_v"]), np64(x["w_g"]),
                            np64(x["b_g"]), idx, np64(x["do"]), round_bf16=rb)
-    for rn, gn in PAIRS:
-        got = np64(g[gn])
-        assert got.shape == ref[rn].shape, gn
-        err = float(np.abs(got - ref[rn]).max())
-        assert np.all(np.isfinite(got)), gn
-        assert err <= _tol(s, ref, rn), (gn, err, _tol(s, ref, rn))
+    # recomputed statistics, then the training forward's saved ones
+    _, saved = nsa.forward_train(s, x["q"], x["k"], x["v"], kc_d, vc_d, x["w_g"], x["b_g"], idx_in=idx_d)
+    for sv in (None, saved):
+        g = nsa.backward_mlp(s, x["q"], x["k"], x["v"], kc_d, vc_d, x["w_ck"], x["pe_k"], w["w2_k"], x["w_cv"],
+                             x["pe_v"], w["w2_v"], x["w_g"], x["b_g"], idx_d, x["do"], saved=sv)
+        torch.cuda.synchronize()
+        for rn, gn in PAIRS:
+            got = np64(g[gn])
+            assert got.shape == ref[rn].shape, gn
+            err = float(np.abs(got - ref[rn]).max())
+            assert np.all(np.isfinite(got)), gn
+            assert err <= _tol(s, ref, rn), (gn, sv is not None, err, _tol(s, ref, rn))
 
 
 def test_backward_mlp_deterministic():

@@ -70,7 +70,7 @@ def test_select_and_forward_parity(name, s, scaled):
     kc = oracle_compress(s, x["k"], x["w_ck"], x["pe_k"])
     vc = oracle_compress(s, x["v"], x["w_cv"], x["pe_v"])
     ref = orc.forward(ocfg(s), np64(x["q"]), kc, vc, np64(x["k"]), np64(x["v"]), np64(x["w_g"]), np64(x["b_g"]),
-                      want_scores=True)
+                      want_scores=True, want_branches=True, want_lse=True)
     kc_d = torch.from_numpy(kc).to(dt).cuda()
     vc_d = torch.from_numpy(vc).to(dt).cuda()
 
@@ -94,6 +94,12 @@ def test_select_and_forward_parity(name, s, scaled):
     say("  max|o-o_ref| = %.3g (tol %.3g)" % (err, tol))
     assert err <= tol
 
+    # the training forward: the same output, and each branch's statistics
+    o_t, (lse, obr) = nsa.forward_train(s, x["q"], x["k"], x["v"], kc_d, vc_d, x["w_g"], x["b_g"], idx_in=idx_ref)
+    torch.cuda.synchronize()
+    assert torch.equal(o_t, o)
+    check_saved(s, lse, obr, ref)
+
     # the whole path on the GPU's own compression and selection
     ck, cv = nsa.compress_kv(s, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"])
     o2, idx2 = nsa.forward(s, x["q"], x["k"], x["v"], ck, cv, x["w_g"], x["b_g"], want_idx=True)
@@ -103,6 +109,27 @@ def test_select_and_forward_parity(name, s, scaled):
     ref2 = orc.forward(ocfg(s), np64(x["q"]), kc, vc, np64(x["k"]), np64(x["v"]), np64(x["w_g"]), np64(x["b_g"]),
                        idx_in=idx2.cpu().numpy())
     assert np.abs(np64(o2) - ref2["o"]).max() <= out_tol(s, ref2["o"])
+
+
+def check_saved(s, lse, obr, ref):
+    """forward_train's saved statistics against the oracle's per-branch
+    log-sum-exp and outputs (same inputs, same selection): -inf exactly where
+    a branch is empty; elsewhere the log-sum-exp to fp32 rounding of the
+    logits (1e-5, bf16 operands with fp32 sums 1e-4, relative to max(1, |lse|))
+    and each branch output to the forward's output rule."""
+    got = lse.permute(1, 2, 0, 3).cpu().numpy().astype(np.float64)      # [B,T,3,Hq]
+    want = ref["lse"]
+    inf = np.isneginf(want)
+    assert np.array_equal(np.isneginf(got), inf)
+    rel = 1e-4 if s.dtype == BF16 else 1e-5
+    err = np.abs(got[~inf] - want[~inf]) / np.maximum(1.0, np.abs(want[~inf]))
+    say("  saved lse: max rel err %.3g, %d empty" % (err.max() if err.size else 0.0, int(inf.sum())))
+    assert err.size == 0 or err.max() <= rel
+    ob = obr.permute(1, 2, 0, 3, 4)                                         # [B,T,3,Hq,dv]
+    for c in range(3):
+        g, r = np64(ob[:, :, c]), ref["branches"][:, :, c]
+        assert np.all(g[inf[:, :, c]] == 0)
+        assert np.abs(g - r).max() <= out_tol(s, r), (c, float(np.abs(g - r).max()))
 
 
 def test_forward_is_deterministic():
