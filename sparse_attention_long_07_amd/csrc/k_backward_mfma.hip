@@ -14,16 +14,20 @@
 // Raw keys: it visits the chunk's window rows of the block, then the chunk's
 // rows whose selection holds j (read from the (block, row) bitmap in ascending
 // order); compressed keys: the chunk's rows from 16 (64 j) + 31 on.  Rows come
-// in tiles of 4 rows x 16 heads = 64 query vectors.  Wave w keeps the fragments
-// of keys 16w .. 16w+15 in registers and per tile forms
+// in tiles of 4 rows x 16 heads = 64 query vectors.  Eight waves: wave w keeps
+// the fragments of keys 16 (w % 4) .. +15 in registers and takes the tile's
+// rows 2 (w / 4) and 2 (w / 4) + 1, forming per tile
 //   S = Q K^T, dP = dO V^T              (16x16x32 MFMA, A from LDS)
 //   P, dS                               (fp32, packed to bf16 in place)
 //   dV^T += dO^T P,  dK^T += Q^T dS     (A: transposing LDS reads)
-// The C layout of S holds, per lane, 4 heads of one key; two row tiles give
-// the 8 contraction slots of a B operand, with the slot order mirrored in the
-// A operand's transposing reads.  Each workgroup writes its block's partial
-// dK, dV; the chunks are then summed in order, so the result does not depend
-// on scheduling.
+// The C layout of S holds, per lane, 4 heads of one key; the wave's two row
+// tiles give the 8 contraction slots of a B operand, with the slot order
+// mirrored in the A operand's transposing reads.  Halving each wave's rows
+// keeps it under 256 registers, so two waves share each SIMD and hide each
+// other's waits.  The two row halves' partial sums of a key are added through
+// LDS (half 0 + half 1), each workgroup writes its block's partial dK, dV, and
+// the chunks are then summed in order, so the result does not depend on
+// scheduling.
 #include "mfma_util.h"
 #include "nsa_internal.h"
 
@@ -32,9 +36,10 @@ namespace nsa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kKThreads = 512;  // key pass: 8 waves, 4 key groups x 2 row halves
 constexpr int kRows = 4;        // rows per tile
 constexpr int kM = 16 * kRows;  // query vectors per tile
-constexpr int kBatchWords = kThreads;   // bitmap words per batch of selected rows (one per thread)
+constexpr int kBatchWords = 256;   // bitmap words per batch of selected rows (one per thread of the first 256)
 
 struct Chunking {
     int rc, nkc;
@@ -57,20 +62,26 @@ __host__ __device__ __forceinline__ long part_base(int c, int rc, long BH, int D
 }
 
 template <int DK, int DV, bool CMP>
-__global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
+__global__ __launch_bounds__(kKThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_keys_mfma(BwdArgs a)
 {
     constexpr int QS = DK + 16, OS = DV + 16;   // LDS row strides (bf16): 16-byte rows, transposing reads conflict-free
-    constexpr int NQ = DK / 32, NO = DV / 32;   // 16-byte pieces per thread of a tile's Q and dO; K, V fragments
+    constexpr int NQ = DK / 32, NO = DV / 32;   // K, V fragments (16-byte pieces) per lane
+    constexpr int QP = kM * DK / 8 / kKThreads, OP = kM * DV / 8 / kKThreads;   // a tile's pieces per thread
+    static_assert(QP * kKThreads == kM * DK / 8 && OP * kKThreads == kM * DV / 8, "tile pieces split evenly");
     constexpr int DD = DK + DV;
-    __shared__ __align__(16) uint16_t qt[kM * QS];
-    __shared__ __align__(16) uint16_t ot[kM * OS];
+    constexpr int NA = DK / 16 + DV / 16;       // 16x16 accumulator tiles per lane
+    // one LDS region: a tile's Q and dO rows, and at the end the second row
+    // half's partial sums
+    __shared__ __align__(16) uint16_t qo[kM * QS + kM * OS];
     __shared__ __align__(16) float s_lse[kM], s_D[kM], s_g[kM];
     __shared__ uint16_t rows[kBatchWords * 32];   // selected rows of a batch, less its first row
-    __shared__ int wcnt[kThreads / 64];
+    __shared__ int wcnt[kKThreads / 64];
     __shared__ int nsel_s;
+    uint16_t *qt = qo, *ot = qo + kM * QS;
 
     const Dims &d = a.d;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int kg = wave & 3, hf = wave >> 2;    // key group, row half
     const int li = lane & 15, lg = lane >> 4;
     const int jb = blockIdx.x, c = blockIdx.y, bgi = blockIdx.z;
     const int b = bgi / d.Hkv, g = bgi % d.Hkv;
@@ -85,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
                       : a.kpart + part_base(c, rc, BH, DD) + ((long)bgi * rend) * DD;   // rend keys per head
 
     // this lane's key and its K, V fragments (B operands of S and dP)
-    const int kk = key0 + 16 * wave + li;
+    const int kk = key0 + 16 * kg + li;
     const int nkeys = CMP ? d.ncmp : d.T, kstride = CMP ? d.npad : d.T;
     u32x4 kf[NQ], vf[NO];
     {
@@ -105,21 +116,21 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
     const float sl2 = d.scale * kLog2e;
     // a tile's rows in registers: Q and dO pieces, and (threads 0..63, one
     // query vector each) log2-scaled lse, D and gate
-    u32x4 qr[NQ], orr[NO];
+    u32x4 qr[QP], orr[OP];
     float st0 = 0.f, st1 = 0.f, st2 = 0.f;
     // row of slot r (r depends on the thread: a select chain, not an indexed array)
     auto slot = [](const int *tr, int r) { return r == 0 ? tr[0] : r == 1 ? tr[1] : r == 2 ? tr[2] : tr[3]; };
     auto fetch = [&](const int *tr, int br) {
 #pragma unroll
-        for (int i = 0; i < NQ; i++) {
-            const int p = tid + kThreads * i;          // piece: row slot p / (2 DK), offset 8 (p % (2 DK))
+        for (int i = 0; i < QP; i++) {
+            const int p = tid + kKThreads * i;          // piece: row slot p / (2 DK), offset 8 (p % (2 DK))
             const int r = p / (2 * DK), e = 8 * (p % (2 * DK)), t = slot(tr, r);
             qr[i] = t >= 0 ? ld16((const uint16_t *)a.q + ((long)b * d.T + t) * d.Hq * DK + (long)g * 16 * DK + e)
                            : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int i = 0; i < NO; i++) {
-            const int p = tid + kThreads * i;
+        for (int i = 0; i < OP; i++) {
+            const int p = tid + kKThreads * i;
             const int r = p / (2 * DV), e = 8 * (p % (2 * DV)), t = slot(tr, r);
             orr[i] = t >= 0 ? ld16((const uint16_t *)a.dO + ((long)b * d.T + t) * d.Hq * DV + (long)g * 16 * DV + e)
                             : u32x4{0u, 0u, 0u, 0u};
@@ -136,14 +147,14 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
     };
     auto stash = [&]() {
 #pragma unroll
-        for (int i = 0; i < NQ; i++) {
-            const int p = tid + kThreads * i;
+        for (int i = 0; i < QP; i++) {
+            const int p = tid + kKThreads * i;
             const int r = p / (2 * DK), e = 8 * (p % (2 * DK));
             st16(qt + (16 * r + e / DK) * QS + e % DK, qr[i]);
         }
 #pragma unroll
-        for (int i = 0; i < NO; i++) {
-            const int p = tid + kThreads * i;
+        for (int i = 0; i < OP; i++) {
+            const int p = tid + kKThreads * i;
             const int r = p / (2 * DV), e = 8 * (p % (2 * DV));
             st16(ot + (16 * r + e / DV) * OS + e % DV, orr[i]);
         }
@@ -153,48 +164,51 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
             s_g[tid] = st2;
         }
     };
-    // one tile from LDS; tr = its rows (-1: empty slot), br = branch (0 compressed, 1 selected, 2 window)
-    auto tile = [&](const int *tr, int br) {
-        f32x4 S[kRows], P[kRows];
+    // this wave's half of one tile from LDS: row slots 2 hf and 2 hf + 1 (rows
+    // t0, t1, -1: empty), br = branch (0 compressed, 1 selected, 2 window)
+    auto tile = [&](int t0, int t1, int br) {
+        f32x4 S[2], P[2];
 #pragma unroll
-        for (int r = 0; r < kRows; r++) {
+        for (int r = 0; r < 2; r++) {
             S[r] = f32x4{0.f, 0.f, 0.f, 0.f};
             P[r] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        const int v0 = 32 * hf + li;   // query vector of this lane's A rows (row slot 2 hf, head li)
         // A fragments of step i + 1 are read while step i's products run
         {
-            u32x4 an[kRows], cur[kRows];
+            u32x4 an[2], cur[2];
 #pragma unroll
-            for (int r = 0; r < kRows; r++) an[r] = ld16(qt + (16 * r + li) * QS + 8 * lg);
+            for (int r = 0; r < 2; r++) an[r] = ld16(qt + (v0 + 16 * r) * QS + 8 * lg);
 #pragma unroll
             for (int i = 0; i < NQ + NO; i++) {
 #pragma unroll
-                for (int r = 0; r < kRows; r++) cur[r] = an[r];
+                for (int r = 0; r < 2; r++) cur[r] = an[r];
                 if (i + 1 < NQ + NO) {
                     const int j = i + 1;
 #pragma unroll
-                    for (int r = 0; r < kRows; r++)
-                        an[r] = j < NQ ? ld16(qt + (16 * r + li) * QS + 32 * j + 8 * lg)
-                                       : ld16(ot + (16 * r + li) * OS + 32 * (j - NQ) + 8 * lg);
+                    for (int r = 0; r < 2; r++)
+                        an[r] = j < NQ ? ld16(qt + (v0 + 16 * r) * QS + 32 * j + 8 * lg)
+                                       : ld16(ot + (v0 + 16 * r) * OS + 32 * (j - NQ) + 8 * lg);
                 }
 #pragma unroll
-                for (int r = 0; r < kRows; r++) {
+                for (int r = 0; r < 2; r++) {
                     if (i < NQ) S[r] = mfma16(as_bf16x8(cur[r]), as_bf16x8(kf[i]), S[r]);
                     else P[r] = mfma16(as_bf16x8(cur[r]), as_bf16x8(vf[i - NQ]), P[r]);
                 }
             }
         }
-        // p and ds of (head 4 lg + e of row r, key kk)
-        float pg[kRows][4], ds[kRows][4];
+        // p and ds of (head 4 lg + e of row slot 2 hf + r, key kk)
+        float pg[2][4], ds[2][4];
 #pragma unroll
-        for (int r = 0; r < kRows; r++) {
-            const int t = tr[r];
+        for (int r = 0; r < 2; r++) {
+            const int t = r ? t1 : t0;
             bool vis;
             if constexpr (CMP) vis = kk < d.ncmp && 16 * kk + 31 <= t;
             else vis = kk <= t && (br == 1 || kk > t - d.w);
-            const f32x4 l4 = *(const f32x4 *)(s_lse + 16 * r + 4 * lg);
-            const f32x4 D4 = *(const f32x4 *)(s_D + 16 * r + 4 * lg);
-            const f32x4 g4 = *(const f32x4 *)(s_g + 16 * r + 4 * lg);
+            const int q0 = 32 * hf + 16 * r + 4 * lg;
+            const f32x4 l4 = *(const f32x4 *)(s_lse + q0);
+            const f32x4 D4 = *(const f32x4 *)(s_D + q0);
+            const f32x4 g4 = *(const f32x4 *)(s_g + q0);
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const float p = vis ? fast_exp2(__builtin_fmaf(S[r][e], sl2, -l4[e])) : 0.f;
@@ -202,67 +216,63 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
                 ds[r][e] = p * __builtin_fmaf(g4[e], P[r][e], -D4[e]) * d.scale;
             }
         }
-        // B operands: contraction slot 8 lg + e <-> query vector 32 s + 4 lg + e
-        // (e < 4, row tile 2s) or 32 s + 16 + 4 lg + e - 4 (row tile 2s + 1)
-        bf16x8 bp[2], bs[2];
-#pragma unroll
-        for (int s2 = 0; s2 < 2; s2++) {
+        // B operands: contraction slot 8 lg + e <-> query vector 32 hf + 4 lg + e
+        // (e < 4, row slot 2 hf) or 32 hf + 16 + 4 lg + e - 4 (row slot 2 hf + 1)
+        bf16x8 bp, bs;
+        {
             u32x4 x, y;
-            x[0] = pack_bf16x2(pg[2 * s2][0], pg[2 * s2][1]);
-            x[1] = pack_bf16x2(pg[2 * s2][2], pg[2 * s2][3]);
-            x[2] = pack_bf16x2(pg[2 * s2 + 1][0], pg[2 * s2 + 1][1]);
-            x[3] = pack_bf16x2(pg[2 * s2 + 1][2], pg[2 * s2 + 1][3]);
-            y[0] = pack_bf16x2(ds[2 * s2][0], ds[2 * s2][1]);
-            y[1] = pack_bf16x2(ds[2 * s2][2], ds[2 * s2][3]);
-            y[2] = pack_bf16x2(ds[2 * s2 + 1][0], ds[2 * s2 + 1][1]);
-            y[3] = pack_bf16x2(ds[2 * s2 + 1][2], ds[2 * s2 + 1][3]);
-            bp[s2] = as_bf16x8(x);
-            bs[s2] = as_bf16x8(y);
+            x[0] = pack_bf16x2(pg[0][0], pg[0][1]);
+            x[1] = pack_bf16x2(pg[0][2], pg[0][3]);
+            x[2] = pack_bf16x2(pg[1][0], pg[1][1]);
+            x[3] = pack_bf16x2(pg[1][2], pg[1][3]);
+            y[0] = pack_bf16x2(ds[0][0], ds[0][1]);
+            y[1] = pack_bf16x2(ds[0][2], ds[0][3]);
+            y[2] = pack_bf16x2(ds[1][0], ds[1][1]);
+            y[3] = pack_bf16x2(ds[1][2], ds[1][3]);
+            bp = as_bf16x8(x);
+            bs = as_bf16x8(y);
         }
         // transposing reads: lane li of group lg points at row r0 + li / 4,
         // columns 4 (li % 4) .. +3 of the column tile, and receives column li
         // of rows r0 .. r0 + 3
         const int trow = li >> 2, tcol = 4 * (li & 3);
+        const int r0 = 32 * hf + 4 * lg + trow, r1 = r0 + 16;
         // transposing reads in groups of 4 column tiles, issued before their products
 #pragma unroll
-        for (int s2 = 0; s2 < 2; s2++) {
-            const int r0 = 32 * s2 + 4 * lg + trow, r1 = r0 + 16;
+        for (int d0 = 0; d0 < DV / 16; d0 += 4) {
+            uint2 lo[4], hi[4];
 #pragma unroll
-            for (int d0 = 0; d0 < DV / 16; d0 += 4) {
-                uint2 lo[4], hi[4];
-#pragma unroll
-                for (int u = 0; u < 4; u++) {
-                    lo[u] = ld_tr16(ot + r0 * OS + 16 * (d0 + u) + tcol);
-                    hi[u] = ld_tr16(ot + r1 * OS + 16 * (d0 + u) + tcol);
-                }
-#pragma unroll
-                for (int u = 0; u < 4; u++)
-                    accv[d0 + u] = mfma16(as_bf16x8(u32x4{lo[u].x, lo[u].y, hi[u].x, hi[u].y}), bp[s2], accv[d0 + u]);
+            for (int u = 0; u < 4; u++) {
+                lo[u] = ld_tr16(ot + r0 * OS + 16 * (d0 + u) + tcol);
+                hi[u] = ld_tr16(ot + r1 * OS + 16 * (d0 + u) + tcol);
             }
 #pragma unroll
-            for (int d0 = 0; d0 < DK / 16; d0 += 4) {
-                uint2 lo[4], hi[4];
+            for (int u = 0; u < 4; u++)
+                accv[d0 + u] = mfma16(as_bf16x8(u32x4{lo[u].x, lo[u].y, hi[u].x, hi[u].y}), bp, accv[d0 + u]);
+        }
 #pragma unroll
-                for (int u = 0; u < 4; u++) {
-                    lo[u] = ld_tr16(qt + r0 * QS + 16 * (d0 + u) + tcol);
-                    hi[u] = ld_tr16(qt + r1 * QS + 16 * (d0 + u) + tcol);
-                }
+        for (int d0 = 0; d0 < DK / 16; d0 += 4) {
+            uint2 lo[4], hi[4];
 #pragma unroll
-                for (int u = 0; u < 4; u++)
-                    acck[d0 + u] = mfma16(as_bf16x8(u32x4{lo[u].x, lo[u].y, hi[u].x, hi[u].y}), bs[s2], acck[d0 + u]);
+            for (int u = 0; u < 4; u++) {
+                lo[u] = ld_tr16(qt + r0 * QS + 16 * (d0 + u) + tcol);
+                hi[u] = ld_tr16(qt + r1 * QS + 16 * (d0 + u) + tcol);
             }
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                acck[d0 + u] = mfma16(as_bf16x8(u32x4{lo[u].x, lo[u].y, hi[u].x, hi[u].y}), bs, acck[d0 + u]);
         }
     };
     // tiles over a list of n rows (row(i) gives the i-th), one branch
     auto run = [&](int n, int br, auto row) {
         if (n <= 0) return;
-        int tr[kRows], tn[kRows];
+        int tn[kRows];
 #pragma unroll
         for (int r = 0; r < kRows; r++) tn[r] = r < n ? row(r) : -1;
         fetch(tn, br);
         for (int i0 = 0; i0 < n; i0 += kRows) {
-#pragma unroll
-            for (int r = 0; r < kRows; r++) tr[r] = tn[r];
+            // this wave's two rows of the tile
+            const int t0 = hf ? tn[2] : tn[0], t1 = hf ? tn[3] : tn[1];
             lds_barrier();   // the previous tile's LDS reads are done
             stash();
             lds_barrier();
@@ -271,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
                 for (int r = 0; r < kRows; r++) tn[r] = i0 + kRows + r < n ? row(i0 + kRows + r) : -1;
                 fetch(tn, br);
             }
-            tile(tr, br);
+            tile(t0, t1, br);
         }
     };
 
@@ -284,17 +294,18 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
         const int lo = max(key0, rbeg), hi = min(min(d.T - 1, key0 + 63 + d.w - 1), rend - 1);
         run(hi - lo + 1, 2, [&](int i) { return lo + i; });
     }
-    // selected rows in this chunk, one batch of bitmap words at a time
+    // selected rows in this chunk, one batch of bitmap words at a time (one
+    // word per thread of the first kBatchWords)
     {
         const int nw = (d.T + 31) / 32;
         const uint32_t *bm = a.selbm + ((long)bgi * d.nb + jb) * nw;
         const int wlo = max(rbeg, key0) / 32, whi = (rend + 31) / 32;   // rbeg, key0, rc: multiples of 64
         for (int w0 = wlo; w0 < whi; w0 += kBatchWords) {
             const int w = w0 + tid;
-            uint32_t word = w < whi ? bm[w] : 0u;
-            if (32 * w + 32 > rend) word &= (1u << (rend - 32 * w)) - 1u;   // a partial last word (rend = T)
+            uint32_t word = tid < kBatchWords && w < whi ? bm[w] : 0u;
+            if (word && 32 * w + 32 > rend) word &= (1u << (rend - 32 * w)) - 1u;   // a partial last word (rend = T)
             // exclusive prefix of the words' bit counts: within each wave by
-            // shuffles, then over the 4 waves' totals
+            // shuffles, then over the waves' totals
             const int cnt = __popc(word);
             int incl = cnt;
 #pragma unroll
@@ -311,15 +322,39 @@ __global__ __launch_bounds__(kThreads) void k_bwd_keys_mfma(BwdArgs a)
                 int o = before + incl - cnt;
                 for (uint32_t x = word; x; x &= x - 1) rows[o++] = (uint16_t)(32 * tid + __ffs(x) - 1);
             }
-            if (tid == 0) nsel_s = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+            if (tid == 0) {
+                int tot = 0;
+                for (int w2 = 0; w2 < kKThreads / 64; w2++) tot += wcnt[w2];
+                nsel_s = tot;
+            }
             lds_barrier();
             const int base = 32 * w0;
             run(nsel_s, 1, [&](int i) { return base + (int)rows[i]; });
         }
     }
     }
+    // the two row halves' partial dK, dV of each key, added in a fixed order
+    // (half 0 + half 1) through LDS, in rounds of kRed accumulator tiles
+    auto acc = [&](int i) -> f32x4 & { return i < DK / 16 ? acck[i] : accv[i - DK / 16]; };
+    constexpr int kRed = (kM * QS + kM * OS) * 2 / (4 * 64 * 4 * 4);   // f32x4 tiles per lane per round
+    float *red = (float *)qo;
+#pragma unroll
+    for (int i0 = 0; i0 < NA; i0 += kRed) {
+        lds_barrier();   // the tile buffers (or the previous round) are no longer read
+        if (hf == 1) {
+#pragma unroll
+            for (int i = i0; i < NA && i < i0 + kRed; i++)
+                *(f32x4 *)(red + (((i - i0) * 4 + kg) * 64 + lane) * 4) = acc(i);
+        }
+        lds_barrier();
+        if (hf == 0) {
+#pragma unroll
+            for (int i = i0; i < NA && i < i0 + kRed; i++)
+                acc(i) += *(const f32x4 *)(red + (((i - i0) * 4 + kg) * 64 + lane) * 4);
+        }
+    }
     // partial dK, dV of the block: C[i = column][j = key] sits in lane j + 16 (i / 4), element i % 4
-    if (kk < kstride) {
+    if (hf == 0 && kk < kstride) {
         float *o = outp + (long)kk * DD;
 #pragma unroll
         for (int dt = 0; dt < DK / 16; dt++) *(f32x4 *)(o + 16 * dt + 4 * lg) = acck[dt];
@@ -780,8 +815,8 @@ template <int DK, int DV>
 hipError_t launch_cmp_dims(const BwdArgs &A, hipStream_t s)
 {
     const Dims &d = A.d;
-    hipLaunchKernelGGL((k_bwd_keys_mfma<DK, DV, true>), dim3(d.npad / 64, A.nchunk, d.B * d.Hkv), dim3(kThreads), 0, s,
-                       A);
+    hipLaunchKernelGGL((k_bwd_keys_mfma<DK, DV, true>), dim3(d.npad / 64, A.nchunk, d.B * d.Hkv), dim3(kKThreads), 0,
+                       s, A);
     return hipGetLastError();
 }
 
@@ -790,7 +825,7 @@ hipError_t launch_dims(const BwdArgs &A, hipStream_t s)
 {
     const Dims &d = A.d;
     const int BH = d.B * d.Hkv;
-    hipLaunchKernelGGL((k_bwd_keys_mfma<DK, DV, false>), dim3(d.nb, A.nkc, BH), dim3(kThreads), 0, s, A);
+    hipLaunchKernelGGL((k_bwd_keys_mfma<DK, DV, false>), dim3(d.nb, A.nkc, BH), dim3(kKThreads), 0, s, A);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long n4 = (long)BH * d.T * ((DK + DV) / 4);
