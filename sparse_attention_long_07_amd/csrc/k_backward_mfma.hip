@@ -118,6 +118,7 @@ __global__ __launch_bounds__(kKThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     // query vector each) log2-scaled lse, D and gate
     u32x4 qr[QP], orr[OP];
     float st0 = 0.f, st1 = 0.f, st2 = 0.f;
+    bool stv = false;   // the statistics belong to a row (not an empty slot)
     // row of slot r (r depends on the thread: a select chain, not an indexed array)
     auto slot = [](const int *tr, int r) { return r == 0 ? tr[0] : r == 1 ? tr[1] : r == 2 ? tr[2] : tr[3]; };
     auto fetch = [&](const int *tr, int br) {
@@ -137,12 +138,14 @@ __global__ __launch_bounds__(kKThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         }
         if (tid < kM) {
             const int r = tid >> 4, h = tid & 15, t = slot(tr, r);
-            // an empty slot reads row 0 and keeps zeros (no branch around the loads)
+            // an empty slot reads row 0 and stores zeros; the loaded values
+            // are used only at the stash, so that nothing here waits for them
+            // (or for the Q and dO loads just issued)
             const float *st = a.rs + (((long)b * d.T + max(t, 0)) * d.Hq + g * 16 + h) * kBwdStat + br * 4;
-            const float x0 = st[0], x1 = st[1], x2 = st[2];
-            st0 = t >= 0 ? x0 * kLog2e : 0.f;
-            st1 = t >= 0 ? x1 : 0.f;
-            st2 = t >= 0 ? x2 : 0.f;
+            st0 = st[0];
+            st1 = st[1];
+            st2 = st[2];
+            stv = t >= 0;
         }
     };
     auto stash = [&]() {
@@ -159,9 +162,9 @@ __global__ __launch_bounds__(kKThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             st16(ot + (16 * r + e / DV) * OS + e % DV, orr[i]);
         }
         if (tid < kM) {
-            s_lse[tid] = st0;
-            s_D[tid] = st1;
-            s_g[tid] = st2;
+            s_lse[tid] = stv ? st0 * kLog2e : 0.f;
+            s_D[tid] = stv ? st1 : 0.f;
+            s_g[tid] = stv ? st2 : 0.f;
         }
     };
     // this wave's half of one tile from LDS: row slots 2 hf and 2 hf + 1 (rows
@@ -628,21 +631,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int klo = br == 0 ? 0 : wlo, khi = br == 0 ? nvis - 1 : t;          // keys this row sees
         const int nch = ghi >= glo ? (ghi - glo + 64) / 64 : 0;
         auto stage = [&](int key0) {
-            // 64 K rows and 64 V rows, rows past the range read its last key
+            // 64 K rows and 64 V rows, rows past the range read its last key;
+            // all of K's loads are issued before its first store, then V's, so
+            // the chunk costs two load latencies (not one per piece)
+            constexpr int NKP = 64 * DK / 8 / kThreads, NVP = 64 * DV / 8 / kThreads;
+            static_assert(NKP * kThreads == 64 * DK / 8 && NVP * kThreads == 64 * DV / 8, "chunk pieces split evenly");
+            {
+                u32x4 kp[NKP];
 #pragma unroll
-            for (int i = 0; i < (64 * DK / 8 + kThreads - 1) / kThreads; i++) {
-                const int pc = tid + kThreads * i;
-                if (pc < 64 * DK / 8) {
-                    const int r = pc / (DK / 8), cc = 8 * (pc % (DK / 8));
-                    st16(ksh + r * KS + cc, ld16(K + (long)min(key0 + r, ghi) * DK + cc));
+                for (int i = 0; i < NKP; i++) {
+                    const int pc = tid + kThreads * i, r = pc / (DK / 8), cc = 8 * (pc % (DK / 8));
+                    kp[i] = ld16(K + (long)min(key0 + r, ghi) * DK + cc);
+                }
+#pragma unroll
+                for (int i = 0; i < NKP; i++) {
+                    const int pc = tid + kThreads * i, r = pc / (DK / 8), cc = 8 * (pc % (DK / 8));
+                    st16(ksh + r * KS + cc, kp[i]);
                 }
             }
+            {
+                u32x4 vp[NVP];
 #pragma unroll
-            for (int i = 0; i < (64 * DV / 8 + kThreads - 1) / kThreads; i++) {
-                const int pc = tid + kThreads * i;
-                if (pc < 64 * DV / 8) {
-                    const int r = pc / (DV / 8), cc = 8 * (pc % (DV / 8));
-                    st16(vsh + r * VS + cc, ld16(V + (long)min(key0 + r, ghi) * DV + cc));
+                for (int i = 0; i < NVP; i++) {
+                    const int pc = tid + kThreads * i, r = pc / (DV / 8), cc = 8 * (pc % (DV / 8));
+                    vp[i] = ld16(V + (long)min(key0 + r, ghi) * DV + cc);
+                }
+#pragma unroll
+                for (int i = 0; i < NVP; i++) {
+                    const int pc = tid + kThreads * i, r = pc / (DV / 8), cc = 8 * (pc % (DV / 8));
+                    st16(vsh + r * VS + cc, vp[i]);
                 }
             }
         };
