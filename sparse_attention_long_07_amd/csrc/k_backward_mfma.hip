@@ -70,14 +70,17 @@ __global__ __launch_bounds__(kKThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     static_assert(QP * kKThreads == kM * DK / 8 && OP * kKThreads == kM * DV / 8, "tile pieces split evenly");
     constexpr int DD = DK + DV;
     constexpr int NA = DK / 16 + DV / 16;       // 16x16 accumulator tiles per lane
-    // one LDS region: a tile's Q and dO rows, and at the end the second row
-    // half's partial sums
-    __shared__ __align__(16) uint16_t qo[kM * QS + kM * OS];
-    __shared__ __align__(16) float s_lse[kM], s_D[kM], s_g[kM];
+    // one LDS region: two tile buffers (a tile's Q and dO rows each), and at
+    // the end the second row half's partial sums
+    constexpr int kBuf = kM * QS + kM * OS;
+    __shared__ __align__(16) uint16_t qo[2 * kBuf];
+    __shared__ __align__(16) float s_lse[2][kM], s_D[2][kM], s_g[2][kM];
+    // window tiles of raw keys: the selected branch's statistics of rows that
+    // also selected the block (+inf log-sum-exp, so p = 0, for the others)
+    __shared__ __align__(16) float s_lse2[2][kM], s_D2[2][kM], s_g2[2][kM];
     __shared__ uint16_t rows[kBatchWords * 32];   // selected rows of a batch, less its first row
     __shared__ int wcnt[kKThreads / 64];
     __shared__ int nsel_s;
-    uint16_t *qt = qo, *ot = qo + kM * QS;
 
     const Dims &d = a.d;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -117,8 +120,10 @@ __global__ __launch_bounds__(kKThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     // a tile's rows in registers: Q and dO pieces, and (threads 0..63, one
     // query vector each) log2-scaled lse, D and gate
     u32x4 qr[QP], orr[OP];
-    float st0 = 0.f, st1 = 0.f, st2 = 0.f;
+    float st0 = 0.f, st1 = 0.f, st2 = 0.f, st3 = 0.f, st4 = 0.f, st5 = 0.f;
     bool stv = false;   // the statistics belong to a row (not an empty slot)
+    uint32_t sw = 0u;   // window tiles: the bitmap word of the row's (block, row) bit,
+    int sb = 0;         // and the bit's position in it
     // row of slot r (r depends on the thread: a select chain, not an indexed array)
     auto slot = [](const int *tr, int r) { return r == 0 ? tr[0] : r == 1 ? tr[1] : r == 2 ? tr[2] : tr[3]; };
     auto fetch = [&](const int *tr, int br) {
@@ -141,14 +146,23 @@ __global__ __launch_bounds__(kKThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             // an empty slot reads row 0 and stores zeros; the loaded values
             // are used only at the stash, so that nothing here waits for them
             // (or for the Q and dO loads just issued)
-            const float *st = a.rs + (((long)b * d.T + max(t, 0)) * d.Hq + g * 16 + h) * kBwdStat + br * 4;
-            st0 = st[0];
-            st1 = st[1];
-            st2 = st[2];
+            const float *st = a.rs + (((long)b * d.T + max(t, 0)) * d.Hq + g * 16 + h) * kBwdStat;
+            st0 = st[br * 4];
+            st1 = st[br * 4 + 1];
+            st2 = st[br * 4 + 2];
             stv = t >= 0;
+            if (!CMP && br == 2) {
+                st3 = st[4];
+                st4 = st[5];
+                st5 = st[6];
+                sw = a.selbm[((long)bgi * d.nb + jb) * ((d.T + 31) / 32) + max(t, 0) / 32];
+                sb = max(t, 0) & 31;
+            }
         }
     };
-    auto stash = [&]() {
+    // the fetched tile into LDS buffer bf
+    auto stash = [&](int bf) {
+        uint16_t *qt = qo + bf * kBuf, *ot = qt + kM * QS;
 #pragma unroll
         for (int i = 0; i < QP; i++) {
             const int p = tid + kKThreads * i;
@@ -162,14 +176,23 @@ __global__ __launch_bounds__(kKThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             st16(ot + (16 * r + e / DV) * OS + e % DV, orr[i]);
         }
         if (tid < kM) {
-            s_lse[tid] = stv ? st0 * kLog2e : 0.f;
-            s_D[tid] = stv ? st1 : 0.f;
-            s_g[tid] = stv ? st2 : 0.f;
+            s_lse[bf][tid] = stv ? st0 * kLog2e : 0.f;
+            s_D[bf][tid] = stv ? st1 : 0.f;
+            s_g[bf][tid] = stv ? st2 : 0.f;
+            if (!CMP) {
+                // (sw, sb are set in window tiles only; elsewhere sel is unused)
+                const bool sel = stv && ((sw >> sb) & 1u);
+                s_lse2[bf][tid] = sel ? st3 * kLog2e : INFINITY;
+                s_D2[bf][tid] = sel ? st4 : 0.f;
+                s_g2[bf][tid] = sel ? st5 : 0.f;
+            }
         }
     };
-    // this wave's half of one tile from LDS: row slots 2 hf and 2 hf + 1 (rows
-    // t0, t1, -1: empty), br = branch (0 compressed, 1 selected, 2 window)
-    auto tile = [&](int t0, int t1, int br) {
+    // this wave's half of the tile in LDS buffer bf: row slots 2 hf and
+    // 2 hf + 1 (rows t0, t1, -1: empty), br = branch (0 compressed, 1 selected,
+    // 2 window)
+    auto tile = [&](int bf, int t0, int t1, int br) {
+        const uint16_t *qt = qo + bf * kBuf, *ot = qt + kM * QS;
         f32x4 S[2], P[2];
 #pragma unroll
         for (int r = 0; r < 2; r++) {
@@ -200,7 +223,9 @@ __global__ __launch_bounds__(kKThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 }
             }
         }
-        // p and ds of (head 4 lg + e of row slot 2 hf + r, key kk)
+        // p and ds of (head 4 lg + e of row slot 2 hf + r, key kk); a window
+        // tile also carries the selected branch of rows that selected the
+        // block (its keys <= t), so S and dP serve both branches
         float pg[2][4], ds[2][4];
 #pragma unroll
         for (int r = 0; r < 2; r++) {
@@ -209,15 +234,29 @@ __global__ __launch_bounds__(kKThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             if constexpr (CMP) vis = kk < d.ncmp && 16 * kk + 31 <= t;
             else vis = kk <= t && (br == 1 || kk > t - d.w);
             const int q0 = 32 * hf + 16 * r + 4 * lg;
-            const f32x4 l4 = *(const f32x4 *)(s_lse + q0);
-            const f32x4 D4 = *(const f32x4 *)(s_D + q0);
-            const f32x4 g4 = *(const f32x4 *)(s_g + q0);
+            const f32x4 l4 = *(const f32x4 *)(&s_lse[bf][q0]);
+            const f32x4 D4 = *(const f32x4 *)(&s_D[bf][q0]);
+            const f32x4 g4 = *(const f32x4 *)(&s_g[bf][q0]);
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const float p = vis ? fast_exp2(__builtin_fmaf(S[r][e], sl2, -l4[e])) : 0.f;
                 pg[r][e] = p * g4[e];
-                ds[r][e] = p * __builtin_fmaf(g4[e], P[r][e], -D4[e]) * d.scale;
+                ds[r][e] = p * __builtin_fmaf(g4[e], P[r][e], -D4[e]);
             }
+            if (!CMP && br == 2) {
+                const bool vis2 = kk <= t;
+                const f32x4 l4s = *(const f32x4 *)(&s_lse2[bf][q0]);
+                const f32x4 D4s = *(const f32x4 *)(&s_D2[bf][q0]);
+                const f32x4 g4s = *(const f32x4 *)(&s_g2[bf][q0]);
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const float p = vis2 ? fast_exp2(__builtin_fmaf(S[r][e], sl2, -l4s[e])) : 0.f;
+                    pg[r][e] = __builtin_fmaf(p, g4s[e], pg[r][e]);
+                    ds[r][e] = __builtin_fmaf(p, __builtin_fmaf(g4s[e], P[r][e], -D4s[e]), ds[r][e]);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; e++) ds[r][e] *= d.scale;
         }
         // B operands: contraction slot 8 lg + e <-> query vector 32 hf + 4 lg + e
         // (e < 4, row slot 2 hf) or 32 hf + 16 + 4 lg + e - 4 (row slot 2 hf + 1)
@@ -266,25 +305,43 @@ __global__ __launch_bounds__(kKThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 acck[d0 + u] = mfma16(as_bf16x8(u32x4{lo[u].x, lo[u].y, hi[u].x, hi[u].y}), bs, acck[d0 + u]);
         }
     };
-    // tiles over a list of n rows (row(i) gives the i-th), one branch
+    // tiles over a list of n rows (row(i) gives the i-th), one branch.  Tile
+    // k is computed from LDS buffer k % 2 while tile k + 1, fetched into
+    // registers during tile k - 1, is stored into the other buffer and tile
+    // k + 2 is fetched: one barrier per tile, and each fetch has a tile's
+    // work to land.
     auto run = [&](int n, int br, auto row) {
         if (n <= 0) return;
         int tn[kRows];
 #pragma unroll
         for (int r = 0; r < kRows; r++) tn[r] = r < n ? row(r) : -1;
         fetch(tn, br);
-        for (int i0 = 0; i0 < n; i0 += kRows) {
-            // this wave's two rows of the tile
-            const int t0 = hf ? tn[2] : tn[0], t1 = hf ? tn[3] : tn[1];
-            lds_barrier();   // the previous tile's LDS reads are done
-            stash();
-            lds_barrier();
-            if (i0 + kRows < n) {
+        // this wave's two rows of the tile in the registers
+        int t0 = hf ? tn[2] : tn[0], t1 = hf ? tn[3] : tn[1];
+        lds_barrier();   // the buffers' previous readers are done
+        stash(0);
+        if (kRows < n) {
 #pragma unroll
-                for (int r = 0; r < kRows; r++) tn[r] = i0 + kRows + r < n ? row(i0 + kRows + r) : -1;
-                fetch(tn, br);
+            for (int r = 0; r < kRows; r++) tn[r] = kRows + r < n ? row(kRows + r) : -1;
+            fetch(tn, br);
+        }
+        lds_barrier();
+        int bf = 0;
+        for (int i0 = 0; i0 < n; i0 += kRows) {
+            tile(bf, t0, t1, br);
+            if (i0 + kRows < n) {
+                t0 = hf ? tn[2] : tn[0];
+                t1 = hf ? tn[3] : tn[1];
+                stash(bf ^ 1);   // its last readers finished before the previous barrier
+                if (i0 + 2 * kRows < n) {
+#pragma unroll
+                    for (int r = 0; r < kRows; r++)
+                        tn[r] = i0 + 2 * kRows + r < n ? row(i0 + 2 * kRows + r) : -1;
+                    fetch(tn, br);
+                }
             }
-            tile(t0, t1, br);
+            lds_barrier();   // buffer bf ^ 1 is written, buffer bf is read
+            bf ^= 1;
         }
     };
 
@@ -303,10 +360,14 @@ __global__ __launch_bounds__(kKThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         const int nw = (d.T + 31) / 32;
         const uint32_t *bm = a.selbm + ((long)bgi * d.nb + jb) * nw;
         const int wlo = max(rbeg, key0) / 32, whi = (rend + 31) / 32;   // rbeg, key0, rc: multiples of 64
+        const int wend = key0 + 63 + d.w - 1;   // the last row whose window reaches the block
         for (int w0 = wlo; w0 < whi; w0 += kBatchWords) {
             const int w = w0 + tid;
             uint32_t word = tid < kBatchWords && w < whi ? bm[w] : 0u;
             if (word && 32 * w + 32 > rend) word &= (1u << (rend - 32 * w)) - 1u;   // a partial last word (rend = T)
+            // rows up to the window range's end were taken with the window tiles
+            if (32 * w + 31 <= wend) word = 0u;
+            else if (32 * w <= wend) word &= ~((1u << (wend - 32 * w + 1)) - 1u);
             // exclusive prefix of the words' bit counts: within each wave by
             // shuffles, then over the waves' totals
             const int cnt = __popc(word);
@@ -339,7 +400,7 @@ __global__ __launch_bounds__(kKThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     // the two row halves' partial dK, dV of each key, added in a fixed order
     // (half 0 + half 1) through LDS, in rounds of kRed accumulator tiles
     auto acc = [&](int i) -> f32x4 & { return i < DK / 16 ? acck[i] : accv[i - DK / 16]; };
-    constexpr int kRed = (kM * QS + kM * OS) * 2 / (4 * 64 * 4 * 4);   // f32x4 tiles per lane per round
+    constexpr int kRed = 2 * kBuf * 2 / (4 * 64 * 4 * 4);   // f32x4 tiles per lane per round
     float *red = (float *)qo;
 #pragma unroll
     for (int i0 = 0; i0 < NA; i0 += kRed) {
