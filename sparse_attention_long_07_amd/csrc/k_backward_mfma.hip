@@ -492,10 +492,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         z += bf2f(((const uint16_t *)a.bg)[((long)g * 16 + h) * 3 + br]);
         gate[br] = 1.f / (1.f + __expf(-z));
     }
-    // the distinct valid selected blocks, ascending
-    int nsel;
+    // The distinct valid selected blocks, ascending.  Blocks from jlo on start
+    // inside the window's staged key range [max(0, t_lo - w + 1), t_hi] (at
+    // most 64 of them): their dS terms are added in the window sweep, where
+    // S and dP of those keys are formed anyway; the selected sweep takes the
+    // nlow blocks below jlo.  sm_lo, sm_hi: bit j - jlo of those blocks.
+    const int jcur = t / 64;
+    const int jlo = max((max(0, t_lo - d.w + 1) + 63) / 64, jcur - 63);
+    int nsel, nlow;
+    uint32_t sm_lo, sm_hi;
     {
-        const int jcur = t / 64;
         const int j = lane < d.n ? a.idx[(bgi * d.T + t) * d.n + lane] : -1;
         bool keep = j >= 0 && j <= jcur;
         for (int u = 0; u < d.n; u++) {
@@ -505,13 +511,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int kx = keep ? j : 0x7fffffff;
         int rank = 0;
         nsel = 0;
+        nlow = 0;
         for (int u = 0; u < d.n; u++) {
             const int x = __shfl(kx, u);
             rank += x < kx;
             nsel += x != 0x7fffffff;
+            nlow += x < jlo;
         }
         if (keep) blk[rank] = j;
+        const int bit = keep && j >= jlo ? j - jlo : -1;
+        uint32_t lo = bit >= 0 && bit < 32 ? 1u << bit : 0u, hi = bit >= 32 ? 1u << (bit - 32) : 0u;
+        for (int off = 1; off < 64; off <<= 1) {
+            lo |= __shfl_xor(lo, off);
+            hi |= __shfl_xor(hi, off);
+        }
+        sm_lo = lo;
+        sm_hi = hi;
     }
+    // the first key of those blocks (the window sweep's lower limit for this row)
+    const int sel_k0 = sm_lo ? 64 * (jlo + __builtin_ctz(sm_lo)) : sm_hi ? 64 * (jlo + 32 + __builtin_ctz(sm_hi)) : d.T;
 
     const float sl2 = d.scale * kLog2e;
     const int nvis = t >= 31 ? (t - 31) / 16 + 1 : 0;
@@ -609,6 +627,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             ds[e] = p * __builtin_fmaf(gv, P[e], -D) * d.scale;
         }
     };
+    // ... and in the window sweep, with the selected branch's terms of keys
+    // in its blocks from jlo on (statistics lse2s, Ds, gate gs)
+    auto tile_ds_win = [&](const f32x4 &S, const f32x4 &P, int k16, int klo, int khi, float lse2, float gv, float D,
+                           float lse2s, float gs, float Ds, float *ds) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int key = k16 + 4 * lg + e;
+            const float pw = key >= klo && key <= khi ? fast_exp2(__builtin_fmaf(S[e], sl2, -lse2)) : 0.f;
+            const int rel = (key >> 6) - jlo;
+            const uint32_t word = rel < 32 ? sm_lo : sm_hi;
+            const bool sel = key <= t && rel >= 0 && ((word >> (rel & 31)) & 1u);
+            const float ps = sel ? fast_exp2(__builtin_fmaf(S[e], sl2, -lse2s)) : 0.f;
+            ds[e] = __builtin_fmaf(pw, __builtin_fmaf(gv, P[e], -D), ps * __builtin_fmaf(gs, P[e], -Ds)) * d.scale;
+        }
+    };
     // dQ^T += K^T dS^T over 32 keys whose K rows sit at kb (stride KS):
     // contraction slot 8 lg + e <-> key 4 lg + e (e < 4) or 16 + 4 lg + e - 4
     auto dq_step = [&](const uint16_t *kb, const float *ds0, const float *ds1) {
@@ -633,6 +666,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
     };
 
+    float lse2s = -INFINITY, Ds = 0.f;   // the selected branch's statistics, for the window sweep
     for (int br = 0; br < 3; br++) {
         const float gv = gate[br];
         if (br == 1) {
@@ -664,7 +698,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 }
                 finish(1, m, l, acc, lse2, D);
             }
-            for (int ch = 0; ch < nsel; ch++) {
+            lse2s = lse2;
+            Ds = D;
+            for (int ch = 0; ch < nlow; ch++) {
                 const int key0 = 64 * blk[ch], khi = min(t, key0 + 63);
 #pragma unroll
                 for (int half = 0; half < 2; half++) {
@@ -690,6 +726,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const uint16_t *V = br == 0 ? (const uint16_t *)a.vc + bgi * d.npad * DV : (const uint16_t *)a.v + bgi * d.T * DV;
         const int glo = br == 0 ? 0 : wlo0, ghi = br == 0 ? nvis_hi - 1 : t_hi;   // keys loaded
         const int klo = br == 0 ? 0 : wlo, khi = br == 0 ? nvis - 1 : t;          // keys this row sees
+        const int klo2 = br == 0 ? 0 : min(wlo, sel_k0);   // ... with the selected blocks from jlo on
         const int nch = ghi >= glo ? (ghi - glo + 64) / 64 : 0;
         auto stage = [&](int key0) {
             // 64 K rows and 64 V rows, rows past the range read its last key;
@@ -756,7 +793,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             lds_barrier();
             stage(key0);
             lds_barrier();
-            if (max(key0, klo) > min(key0 + 63, khi)) continue;
+            if (max(key0, klo2) > min(key0 + 63, khi)) continue;
 #pragma unroll
             for (int half = 0; half < 2; half++) {
                 float ds[2][4];
@@ -766,7 +803,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     u32x4 kfr[NQ];
                     const int r16 = 32 * half + 16 * kh;
                     tile_scores(ksh + r16 * KS, KS, vsh + r16 * VS, VS, S, P, kfr);
-                    tile_ds(S, P, key0 + r16, klo, khi, lse2, gv, D, ds[kh]);
+                    if (br == 2) tile_ds_win(S, P, key0 + r16, klo, khi, lse2, gv, D, lse2s, gate[1], Ds, ds[kh]);
+                    else tile_ds(S, P, key0 + r16, klo, khi, lse2, gv, D, ds[kh]);
                 }
                 dq_step(ksh + 32 * half * KS, ds[0], ds[1]);
             }
