@@ -868,40 +868,78 @@ struct DaProblem {
 };
 
 // Gate gradients per chunk of kGateRows rows of one head: element e of
-// [3][dk+1] (column dk is the bias) sums dz_c * q (or dz_c).  A thread owns
-// column x for all three branches (q read once) and keeps 8 rows' loads in
-// flight; rows are summed in order.
+// [3][dk+1] (column dk is the bias) sums dz_c * q (or dz_c).  A thread owns 8
+// consecutive columns (one 16-byte load of a bf16 row, two of an fp32 row) of
+// every nrl-th row of the chunk, for all three branches; the row lanes' sums
+// are then added in lane order through LDS, so the result does not depend on
+// scheduling.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_bwd_gate_part(BwdArgs a)
 {
+    __shared__ float red[kThreads * 24];   // per thread: 3 branches x 8 columns
+    __shared__ float bred[kThreads * 3];   // per row lane: 3 bias sums (threads of column group 0)
     const Dims &d = a.d;
     const int h = blockIdx.x, chunk = blockIdx.y;
     const int W1 = d.dk + 1;
+    const int ncg = d.dk / 8;             // column groups (d_k is a multiple of 8, at most 256)
+    const int nrl = kThreads / ncg;       // row lanes
+    const int tid = threadIdx.x, rl = tid / ncg, cg = tid % ncg;
     const long r0 = (long)chunk * kGateRows, r1 = min((long)d.B * d.T, r0 + kGateRows);
-    for (int x = threadIdx.x; x < W1; x += kThreads) {
-        float s0 = 0.f, s1 = 0.f, s2 = 0.f;
-        for (long rb = r0; rb < r1; rb += 8) {
-            float qv[8], z0[8], z1[8], z2[8];
+    float acc[3][8], bacc[3] = {0.f, 0.f, 0.f};
 #pragma unroll
-            for (int u = 0; u < 8; u++) {
-                const long r = rb + u < r1 ? rb + u : r1 - 1;
-                const float *st = a.rs + (r * d.Hq + h) * kStat;
-                z0[u] = rb + u < r1 ? st[3] : 0.f;
-                z1[u] = rb + u < r1 ? st[7] : 0.f;
-                z2[u] = rb + u < r1 ? st[11] : 0.f;
-                qv[u] = x < d.dk ? to_f(((const T *)a.q)[(r * d.Hq + h) * d.dk + x]) : 1.f;
+    for (int c = 0; c < 3; c++)
+#pragma unroll
+        for (int i = 0; i < 8; i++) acc[c][i] = 0.f;
+    if (rl < nrl) {
+        for (long r = r0 + rl; r < r1; r += nrl) {
+            const float *st = a.rs + (r * d.Hq + h) * kStat;
+            const float z0 = st[3], z1 = st[7], z2 = st[11];
+            const T *qr = (const T *)a.q + (r * d.Hq + h) * d.dk + 8 * cg;
+            float q[8];
+            if constexpr (sizeof(T) == 2) {
+                const uint4 w = *(const uint4 *)qr;
+                const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    q[2 * i] = __uint_as_float(ws[i] << 16);
+                    q[2 * i + 1] = __uint_as_float(ws[i] & 0xffff0000u);
+                }
+            } else {
+                const float4 w0 = *(const float4 *)qr, w1 = *(const float4 *)(qr + 4);
+                q[0] = w0.x; q[1] = w0.y; q[2] = w0.z; q[3] = w0.w;
+                q[4] = w1.x; q[5] = w1.y; q[6] = w1.z; q[7] = w1.w;
             }
 #pragma unroll
-            for (int u = 0; u < 8; u++) {
-                s0 += z0[u] * qv[u];
-                s1 += z1[u] * qv[u];
-                s2 += z2[u] * qv[u];
+            for (int i = 0; i < 8; i++) {
+                acc[0][i] = __builtin_fmaf(z0, q[i], acc[0][i]);
+                acc[1][i] = __builtin_fmaf(z1, q[i], acc[1][i]);
+                acc[2][i] = __builtin_fmaf(z2, q[i], acc[2][i]);
             }
+            bacc[0] += z0;
+            bacc[1] += z1;
+            bacc[2] += z2;
         }
-        float *gp = a.gpart + ((long)h * a.ngc + chunk) * 3 * W1;
-        gp[x] = s0;
-        gp[W1 + x] = s1;
-        gp[2 * W1 + x] = s2;
+    }
+#pragma unroll
+    for (int c = 0; c < 3; c++)
+#pragma unroll
+        for (int i = 0; i < 8; i++) red[tid * 24 + c * 8 + i] = acc[c][i];
+    if (cg == 0 && rl < nrl) {
+        bred[rl * 3] = bacc[0];
+        bred[rl * 3 + 1] = bacc[1];
+        bred[rl * 3 + 2] = bacc[2];
+    }
+    __syncthreads();
+    float *gp = a.gpart + ((long)h * a.ngc + chunk) * 3 * W1;
+    for (int e = tid; e < 3 * W1; e += kThreads) {
+        const int c = e / W1, x = e % W1;
+        float sum = 0.f;
+        if (x < d.dk) {
+            for (int l = 0; l < nrl; l++) sum += red[(l * ncg + x / 8) * 24 + c * 8 + x % 8];
+        } else {
+            for (int l = 0; l < nrl; l++) sum += bred[l * 3 + c];
+        }
+        gp[e] = sum;
     }
 }
 
