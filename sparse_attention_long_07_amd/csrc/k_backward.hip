@@ -1121,8 +1121,12 @@ hipError_t launch_all(const BwdArgs &A, hipStream_t s)
         px.dim = dim;
         px.ncmp = d.ncmp;
         px.npad = d.npad;
-        hipLaunchKernelGGL(k_gemm<DxProblem<T>>, dim3((px.M + 63) / 64, (px.N + 63) / 64, BH), dim3(kThreads), 0, s,
-                           px);
+        if (bwd_keys_mfma_ok(d)) {
+            if ((e = launch_bwd_dx_mfma(Am, isk == 1, s)) != hipSuccess) return e;
+        } else {
+            hipLaunchKernelGGL(k_gemm<DxProblem<T>>, dim3((px.M + 63) / 64, (px.N + 63) / 64, BH), dim3(kThreads), 0,
+                               s, px);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // 5. gates

@@ -927,6 +927,86 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dw_mfma(const float *__restric
     }
 }
 
+// Token gradient of one compression map on the matrix cores, added to the
+// raw-key gradient.  Block i covers tokens 16 i .. 16 i + 31, so token 16 m + u
+// (u < 16) is position u of block m and position 16 + u of block m - 1:
+//   dx[bh][16 m + u][e] = raw + sum_c G[bh][m][c] W[c][u DIM + e]
+//                             + sum_c G[bh][m-1][c] W[c][(16 + u) DIM + e]
+// (blocks outside 0 .. ncmp-1 contribute nothing).  A workgroup owns 64 token
+// groups m x 64 columns n = u DIM + e of one (b, KV head), wave w the groups
+// 16 w .. 16 w + 15.  Per 32-deep step over (block m or m - 1, channel) the W
+// tile (32 channels x 64 columns) is staged in LDS, double-buffered, and read
+// as the B operand by transposing reads; the A operand (G rows, fp32 to bf16)
+// comes straight from memory, one step ahead.
+template <int DIM>
+__global__ __launch_bounds__(kThreads) void k_bwd_dx_mfma(const float *__restrict__ G, int gs,
+                                                          const uint16_t *__restrict__ W, const float *__restrict__ raw,
+                                                          uint16_t *__restrict__ dx, int T, int ncmp, int npad)
+{
+    constexpr int RS = 72;                 // LDS row stride (bf16) of the staged W tile
+    constexpr int CS = DIM / 32;           // 32-channel steps per block
+    constexpr int NSTEP = 2 * CS;
+    __shared__ __align__(16) uint16_t wt[2][32 * RS];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64, bh = blockIdx.z;
+    const int trow = li >> 2, tcol = 4 * (li & 3);
+    const int sr = tid >> 3, sc = 8 * (tid & 7);   // staging: channel row, 8 columns
+    const int m = m0 + 16 * wave + li;            // this lane's A row (token group)
+    f32x4 acc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; nt++) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto wload = [&](int st) {
+        const int c = 32 * (st % CS) + sr;
+        return ld16(W + (long)c * 32 * DIM + 16 * DIM * (st / CS) + n0 + sc);
+    };
+    auto aload = [&](int st) {
+        const int i = m - st / CS, c = 32 * (st % CS) + 8 * lg;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (i >= 0 && i < ncmp) {
+            const float *gr = G + ((long)bh * npad + i) * gs + c;
+            const float4 f0 = *(const float4 *)gr, f1 = *(const float4 *)(gr + 4);
+            v = u32x4{pack_bf16x2(f0.x, f0.y), pack_bf16x2(f0.z, f0.w), pack_bf16x2(f1.x, f1.y),
+                      pack_bf16x2(f1.z, f1.w)};
+        }
+        return v;
+    };
+    u32x4 wv = wload(0), av = aload(0);
+    for (int st = 0; st < NSTEP; st++) {
+        const int buf = st & 1;
+        // buffer buf's last readers (step st - 2) passed the previous barrier
+        st16(wt[buf] + sr * RS + sc, wv);
+        const bf16x8 a = as_bf16x8(av);
+        if (st + 1 < NSTEP) {
+            wv = wload(st + 1);
+            av = aload(st + 1);
+        }
+        lds_barrier();
+        uint2 lo[4], hi[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; nt++) {
+            lo[nt] = ld_tr16(wt[buf] + (8 * lg + trow) * RS + 16 * nt + tcol);
+            hi[nt] = ld_tr16(wt[buf] + (8 * lg + 4 + trow) * RS + 16 * nt + tcol);
+        }
+#pragma unroll
+        for (int nt = 0; nt < 4; nt++)
+            acc[nt] = mfma16(a, as_bf16x8(u32x4{lo[nt].x, lo[nt].y, hi[nt].x, hi[nt].y}), acc[nt]);
+    }
+    // C[i = group][j = column]: lane j + 16 (i / 4), element i % 4
+#pragma unroll
+    for (int nt = 0; nt < 4; nt++) {
+        const int n = n0 + 16 * nt + li, u = n / DIM, e = n % DIM;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int tok = 16 * (m0 + 16 * wave + 4 * lg + r) + u;
+            if (tok < T) {
+                const long o = ((long)bh * T + tok) * DIM + e;
+                dx[o] = f2bf(raw[o] + acc[nt][r]);
+            }
+        }
+    }
+}
+
 template <int DK, int DV>
 hipError_t launch_cmp_dims(const BwdArgs &A, hipStream_t s)
 {
@@ -988,6 +1068,22 @@ hipError_t launch_bwd_rows_mfma(const BwdArgs &A, hipStream_t s)
         else if (d.dk == 128) hipLaunchKernelGGL((k_bwd_rows_mfma<128, 128, false>), grid, dim3(kThreads), 0, s, A);
         else hipLaunchKernelGGL((k_bwd_rows_mfma<64, 64, false>), grid, dim3(kThreads), 0, s, A);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dx_mfma(const BwdArgs &A, bool isk, hipStream_t s)
+{
+    const Dims &d = A.d;
+    const int dim = isk ? d.dk : d.dv;
+    const float *G = A.kcv + (isk ? 0 : d.dk);
+    const uint16_t *W = (const uint16_t *)(isk ? A.wck : A.wcv);
+    const float *raw = isk ? A.dk_raw : A.dv_raw;
+    uint16_t *dx = (uint16_t *)(isk ? A.dk : A.dv);
+    const int gs = d.dk + d.dv;
+    const dim3 grid(16 * dim / 64, ((d.T + 15) / 16 + 63) / 64, d.B * d.Hkv);
+    if (dim == 192) hipLaunchKernelGGL(k_bwd_dx_mfma<192>, grid, dim3(kThreads), 0, s, G, gs, W, raw, dx, d.T, d.ncmp, d.npad);
+    else if (dim == 128) hipLaunchKernelGGL(k_bwd_dx_mfma<128>, grid, dim3(kThreads), 0, s, G, gs, W, raw, dx, d.T, d.ncmp, d.npad);
+    else hipLaunchKernelGGL(k_bwd_dx_mfma<64>, grid, dim3(kThreads), 0, s, G, gs, W, raw, dx, d.T, d.ncmp, d.npad);
     return hipGetLastError();
 }
 

@@ -160,6 +160,9 @@ hipError_t launch_bwd_cmp_keys_mfma(const BwdArgs &A, hipStream_t s);
 // weight gradient of the K (isk) or V compression map on the matrix cores,
 // same shapes; needs kcv and colsum
 hipError_t launch_bwd_dw_mfma(const BwdArgs &A, bool isk, hipStream_t s);
+// token gradient of the K (isk) or V compression map on the matrix cores, added
+// to the raw-key gradient and stored in the storage dtype (same shapes)
+hipError_t launch_bwd_dx_mfma(const BwdArgs &A, bool isk, hipStream_t s);
 // the row pass (rs and dq) on the matrix cores, same shapes
 hipError_t launch_bwd_rows_mfma(const BwdArgs &A, hipStream_t s);
 
