@@ -454,6 +454,33 @@ __global__ __launch_bounds__(kThreads) void k_bwd_fill_u32(uint32_t *p, long n)
     for (long i = (long)blockIdx.x * kThreads + threadIdx.x; i < n; i += (long)gridDim.x * kThreads) p[i] = 0u;
 }
 
+// The same bitmap for kThreads consecutive rows of one (b, KV head) per
+// workgroup: the bits are gathered with LDS atomics, then every word of those
+// rows is stored (zeros included), so no fill is needed.  nb * 8 words of LDS.
+__global__ __launch_bounds__(kThreads) void k_bwd_selmap_lds(BwdArgs a)
+{
+    extern __shared__ uint32_t wbits[];   // [nb][kThreads / 32]
+    constexpr int WPB = kThreads / 32;    // words of one block's bits in this workgroup
+    const Dims &d = a.d;
+    const int tid = threadIdx.x, t0 = blockIdx.x * kThreads, bgi = blockIdx.y;
+    for (int i = tid; i < d.nb * WPB; i += kThreads) wbits[i] = 0u;
+    __syncthreads();
+    const int t = t0 + tid;
+    if (t < d.T) {
+        const int32_t *ir = a.idx + ((long)bgi * d.T + t) * d.n;
+        for (int u = 0; u < d.n; u++) {
+            const int j = ir[u];
+            if (j >= 0 && j <= t / 64) atomicOr(&wbits[j * WPB + tid / 32], 1u << (tid & 31));
+        }
+    }
+    __syncthreads();
+    const int nw = (d.T + 31) / 32, w0 = t0 / 32, nwl = min(WPB, nw - w0);
+    for (int i = tid; i < d.nb * WPB; i += kThreads) {
+        const int j = i / WPB, wl = i % WPB;
+        if (wl < nwl) a.selbm[((long)bgi * d.nb + j) * nw + w0 + wl] = wbits[i];
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void k_bwd_selmap(BwdArgs a)
 {
     const Dims &d = a.d;
@@ -708,19 +735,31 @@ __global__ __launch_bounds__(kThreads) void k_bwd_colsum(BwdArgs a)
 }
 
 // dPE[m] = sum_c W[c][m] colsum[c] for the K map (m < 32 dk) and the V map.
+// A workgroup takes 64 columns m; wave w sums the channels c = w mod 4, and
+// the four partial sums are added in wave order.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_bwd_dpe(BwdArgs a)
 {
+    __shared__ float part[kThreads / kWave][kWave];
     const Dims &d = a.d;
-    const int m = blockIdx.x * kThreads + threadIdx.x;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int m = blockIdx.x * kWave + lane;
     const bool isk = blockIdx.y == 0;
     const int dim = isk ? d.dk : d.dv;
-    if (m >= 32 * dim) return;
     const T *W = (const T *)(isk ? a.wck : a.wcv);
     const float *cs = a.colsum + (isk ? 0 : d.dk);
     float s = 0.f;
-    for (int c = 0; c < dim; c++) s += to_f(W[(long)c * 32 * dim + m]) * cs[c];
-    (isk ? a.dpek : a.dpev)[m] = s;
+    if (m < 32 * dim) {
+#pragma unroll 8
+        for (int c = wave; c < dim; c += kThreads / kWave) s += to_f(W[(long)c * 32 * dim + m]) * cs[c];
+    }
+    part[wave][lane] = s;
+    __syncthreads();
+    if (wave == 0 && m < 32 * dim) {
+        float t = part[0][lane];
+        for (int w = 1; w < kThreads / kWave; w++) t += part[w][lane];
+        (isk ? a.dpek : a.dpev)[m] = t;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -999,10 +1038,15 @@ hipError_t launch_all(const BwdArgs &A, hipStream_t s)
                                          2 * (size_t)d.G * kKeyTile);
     // 2. raw keys: the selection bitmap, then one workgroup per 64-key block
     {
-        const long nwords = (long)BH * d.nb * ((d.T + 31) / 32);
-        hipLaunchKernelGGL(k_bwd_fill_u32, dim3((unsigned)std::min<long>((nwords + kThreads - 1) / kThreads, 4096)),
-                           dim3(kThreads), 0, s, A.selbm, nwords);
-        hipLaunchKernelGGL(k_bwd_selmap, dim3((d.T + kThreads - 1) / kThreads, BH), dim3(kThreads), 0, s, A);
+        const size_t lds = sizeof(uint32_t) * (size_t)d.nb * (kThreads / 32);
+        if (lds <= 64 * 1024) {
+            hipLaunchKernelGGL(k_bwd_selmap_lds, dim3((d.T + kThreads - 1) / kThreads, BH), dim3(kThreads), lds, s, A);
+        } else {
+            const long nwords = (long)BH * d.nb * ((d.T + 31) / 32);
+            hipLaunchKernelGGL(k_bwd_fill_u32, dim3((unsigned)std::min<long>((nwords + kThreads - 1) / kThreads, 4096)),
+                               dim3(kThreads), 0, s, A.selbm, nwords);
+            hipLaunchKernelGGL(k_bwd_selmap, dim3((d.T + kThreads - 1) / kThreads, BH), dim3(kThreads), 0, s, A);
+        }
         if (bwd_keys_mfma_ok(d)) {
             if ((e = launch_bwd_keys_mfma(A, s)) != hipSuccess) return e;
         } else {
@@ -1082,7 +1126,7 @@ hipError_t launch_all(const BwdArgs &A, hipStream_t s)
         hipLaunchKernelGGL(k_bwd_colsum_part, dim3((d.dk + d.dv + kWave - 1) / kWave, kColChunks), dim3(kThreads), 0, s,
                            Am);
         hipLaunchKernelGGL(k_bwd_colsum, dim3((d.dk + d.dv + kThreads - 1) / kThreads), dim3(kThreads), 0, s, Am);
-        hipLaunchKernelGGL(k_bwd_dpe<T>, dim3((32 * (d.dk > d.dv ? d.dk : d.dv) + kThreads - 1) / kThreads, 2),
+        hipLaunchKernelGGL(k_bwd_dpe<T>, dim3((32 * (d.dk > d.dv ? d.dk : d.dv) + kWave - 1) / kWave, 2),
                            dim3(kThreads), 0, s, Am);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
