@@ -886,6 +886,38 @@ struct Dw2Problem {
     __device__ void store(int, int m, int n, float v) const { out[(long)m * N + n] = v; }
 };
 
+// Dw2Problem with its contraction split into ranges of K rows: split z (the
+// batch index of k_gemm) covers rows z K .. z K + K - 1 of the Ktot and writes
+// its partial product to part[z]; k_sum_splits then adds the splits in order.
+// (9 or 4 workgroups over 4,092 rows took 0.87 ms each at T=16384.)
+template <typename T>
+struct Dw2SplitProblem {
+    int M, N, K, Ktot;
+    Dw2Problem<T> base;
+    float *part;   // [nsplit][M][N]
+    __device__ float a(int z, int m, int k) const
+    {
+        const int kg = z * K + k;
+        return kg < Ktot ? base.a(0, m, kg) : 0.f;
+    }
+    __device__ float b(int z, int k, int n) const
+    {
+        const int kg = z * K + k;
+        return kg < Ktot ? base.b(0, kg, n) : 0.f;
+    }
+    __device__ void store(int z, int m, int n, float v) const { part[((long)z * M + m) * N + n] = v; }
+};
+
+__global__ __launch_bounds__(kThreads) void k_sum_splits(const float *__restrict__ part, int nsplit, long n,
+                                                         float *__restrict__ out)
+{
+    const long i = (long)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n) return;
+    float s = 0.f;
+    for (int z = 0; z < nsplit; z++) s += part[(long)z * n + i];
+    out[i] = s;
+}
+
 // dA[z][i][j] = (sum_c G[z][i][c] W2[c][j]) [h[z][i][j] > 0] for sequence and
 // head z (the ReLU's derivative taken as 0 at 0), rows i >= ncmp zero:
 // M = npad, N = K = dim.  Written in kcv's layout (column offset applied).
@@ -1103,8 +1135,25 @@ hipError_t launch_all(const BwdArgs &A, hipStream_t s)
             p2.ncmp = d.ncmp;
             p2.npad = d.npad;
             p2.out = isk ? A.dw2k : A.dw2v;
-            hipLaunchKernelGGL(k_gemm<Dw2Problem<T>>, dim3((dim + 63) / 64, (dim + 63) / 64, 1), dim3(kThreads), 0, s,
-                               p2);
+            {
+                // split over the compressed-key partials' buffer, which the
+                // chunk sum above has consumed: at most 32 splits of at least
+                // 64 rows, as many as the buffer holds
+                const long cap = (long)A.nchunk * BH * d.npad * (d.dk + d.dv);
+                int ns = (int)std::min<long>(32, std::max<long>(1, cap / ((long)dim * dim)));
+                ns = std::min(ns, std::max(1, (p2.K + 63) / 64));
+                Dw2SplitProblem<T> ps;
+                ps.M = ps.N = dim;
+                ps.K = (p2.K + ns - 1) / ns;
+                ps.Ktot = p2.K;
+                ps.base = p2;
+                ps.part = A.part;
+                hipLaunchKernelGGL(k_gemm<Dw2SplitProblem<T>>, dim3((dim + 63) / 64, (dim + 63) / 64, ns),
+                                   dim3(kThreads), 0, s, ps);
+                const long n = (long)dim * dim;
+                hipLaunchKernelGGL(k_sum_splits, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
+                                   (const float *)A.part, ns, n, p2.out);
+            }
             DaProblem<T> pa;
             pa.M = d.npad;
             pa.N = pa.K = dim;
