@@ -103,6 +103,11 @@ SMALL = [
     ("bf16_T2100_g16_d128_randsel", NSAShape(1, 2100, 1, 16, 128, 128, n=8, w=256), False, True),
     # K/V of a key chunk too wide to stage in LDS: read in place
     ("fp32_T260_g16_d256_unstaged", NSAShape(1, 260, 1, 16, 256, 256, FP32, n=4, w=100), False, True),
+    # matrix-core passes with a window shorter than a selection block (selected blocks shared with the
+    # window sweep and window rows carrying both branches start mid-block), and with the window
+    # covering the whole sequence
+    ("bf16_T700_g16_d64_w40_randsel", NSAShape(1, 700, 1, 16, 64, 64, n=5, w=40), False, True),
+    ("bf16_T600_g16_d128_wT_randsel", NSAShape(1, 600, 2, 16, 128, 128, n=4, w=1024), False, True),
 ]
 
 
