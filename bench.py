@@ -436,6 +436,25 @@ def main():
     st_ms = per.mean(axis=0)
     step_ms = float(np.array([e[0].elapsed_time(e[nst]) for e in evs]).mean())
 
+    # decode steps back to back as a serving loop runs them, alternating the
+    # two cache copies (2 x 461 MB, more than the 256 MB Infinity Cache, so a
+    # step does not find the previous step's bytes cached); median of the steps
+    def dec_step(i):
+        y = dec[i % 2]
+        nsa.decode_step(sd, y["seq_lens"], y["q"], y["k"], y["v"], y["ck"], y["cv"], y["w_g"], y["b_g"], None,
+                        od, None, wsd)
+
+    nb2b = max(2 * args.steps, 10)
+    dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nb2b)]
+    dec_step(0)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(dev_ev):
+        a.record()
+        dec_step(i + 1)
+        b.record()
+    torch.cuda.synchronize()
+    dec_b2b_us = sorted(a.elapsed_time(b) * 1e3 for a, b in dev_ev)[nb2b // 2]
+
     fl = prefill_flops(sp)
     prefill_ms = float(st_ms[:nst - 1].sum())
     tflops = fl["total"] / (prefill_ms * 1e-3) / 1e12
@@ -493,6 +512,7 @@ def main():
         "prefill_algorithmic_tflop": round(fl["total"] / 1e12, 4),
         "stage_ms": {k: round(float(v), 4) for k, v in zip(stages, st_ms)},
         "decode_us_per_step": round(dec_us, 2),
+        "decode_us_per_step_back_to_back": round(dec_b2b_us, 2),
         "decode_tokens_per_s": round(sd.B / (dec_us * 1e-6), 1),
         "decode_GBps": round(dec_gbps, 1),
         "decode_hbm_frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
