@@ -815,13 +815,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // plus the gate terms sum_c dz_c W_g[h][c]
     uint16_t *dq = (uint16_t *)a.dq + (row0 + h) * DK;
     const uint16_t *wg = (const uint16_t *)a.wg + ((long)g * 16 + h) * 3 * DK;
+    // all gate-weight loads are issued before the first store (the two
+    // pointers may alias as far as the compiler knows)
+    uint2 wv[DK / 16][3];
+#pragma unroll
+    for (int dt = 0; dt < DK / 16; dt++)
+#pragma unroll
+        for (int br = 0; br < 3; br++) wv[dt][br] = *(const uint2 *)(wg + br * DK + 16 * dt + 4 * lg);
 #pragma unroll
     for (int dt = 0; dt < DK / 16; dt++) {
         const int col = 16 * dt + 4 * lg;
         float z[4] = {dqa[dt][0], dqa[dt][1], dqa[dt][2], dqa[dt][3]};
 #pragma unroll
         for (int br = 0; br < 3; br++) {
-            const uint2 w = *(const uint2 *)(wg + br * DK + col);
+            const uint2 w = wv[dt][br];
             z[0] = __builtin_fmaf(dzs[br], bf2f((uint16_t)(w.x & 0xffffu)), z[0]);
             z[1] = __builtin_fmaf(dzs[br], bf2f((uint16_t)(w.x >> 16)), z[1]);
             z[2] = __builtin_fmaf(dzs[br], bf2f((uint16_t)(w.y & 0xffffu)), z[2]);
