@@ -73,8 +73,10 @@ def _gpu_saved(s, x):
 
 # Gradients that cancel to (near) zero in exact arithmetic take the scale of a
 # counterpart that does not: dPE_k always (a common shift of every compressed
-# key), dK when a row's softmax has a single key (then ds = p (dP - D) = 0).
-COMPANION = {"dpek": "dpev", "dk": "dv"}
+# key), dK when a row's softmax has a single key (then ds = p (dP - D) = 0), and
+# dW_k when every row sees at most one compressed key (T < 47: the compressed
+# keys' gradient is then zero, and so is its weight gradient).
+COMPANION = {"dpek": "dpev", "dk": "dv", "dwck": "dwcv"}
 
 
 def _tol(s, ref, rn):
@@ -108,6 +110,9 @@ SMALL = [
     # covering the whole sequence
     ("bf16_T700_g16_d64_w40_randsel", NSAShape(1, 700, 1, 16, 64, 64, n=5, w=40), False, True),
     ("bf16_T600_g16_d128_wT_randsel", NSAShape(1, 600, 2, 16, 128, 128, n=4, w=1024), False, True),
+    # matrix-core passes with no compressed block (T < 32) and with one (T = 47)
+    ("bf16_T20_g16", NSAShape(1, 20, 1, 16, 192, 128), False, False),
+    ("bf16_T47_g16_d64_B2_randsel", NSAShape(2, 47, 1, 16, 64, 64, n=4, w=40), False, True),
 ]
 
 

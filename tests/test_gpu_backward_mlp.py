@@ -51,6 +51,7 @@ CASES = [
     ("bf16_T2100_g16_d128_randsel", NSAShape(1, 2100, 1, 16, 128, 128, n=8, w=256), False, True),
     ("fp32_T300_g5_w64", NSAShape(1, 300, 2, 5, 32, 16, FP32, n=3, w=64), False, False),
     ("bf16_T31", NSAShape(1, 31, 1, 2, 16, 16), False, False),
+    ("bf16_T20_g16", NSAShape(1, 20, 1, 16, 192, 128), False, False),
 ]
 
 

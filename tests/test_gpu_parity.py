@@ -40,6 +40,9 @@ SMALL = [
     ("fp32_T1", NSAShape(1, 1, 1, 1, 8, 8, FP32), True),
     ("bf16_T31", NSAShape(1, 31, 1, 2, 16, 16), False),
     ("bf16_T64_g16", NSAShape(1, 64, 1, 16, 64, 64), False),
+    # matrix-core kernels with no compressed block (T < 32) and with one (T = 47), one selection block
+    ("bf16_T20_g16", NSAShape(1, 20, 1, 16, 192, 128), False),
+    ("bf16_T47_g16_d128_B2", NSAShape(2, 47, 2, 16, 128, 128), False),
     ("fp32_T300_g5_w64", NSAShape(1, 300, 2, 5, 32, 16, FP32, n=3, w=64), False),
 ]
 
