@@ -2,9 +2,10 @@
 
 One step = the whole hot path over one batch of synthetic input:
   * the 64k prefill forward (B=1, T=65536, 4 KV heads x 16 query heads,
-    d_k=192, d_v=128, bf16): compression (S1), compressed attention with
-    block importance (S2), top-n selection (S3), selected + window attention
-    with the gated sum (S4, timed as its three kernels: pack, window, selected);
+    d_k=192, d_v=128, bf16) as nsa_forward launches it after compression
+    (S1): compressed attention with block importance (S2) together with the
+    window half of S4 in one kernel, top-n selection (S3), then packing of
+    the K/V blocks and the selected half of S4 with the gated sum;
   * one decode step on 32 sequences with 65,536-token caches (same heads).
 Inputs are resident in HBM before timing starts.  Each stage is bracketed by
 HIP events on the stream the kernels run on; the printed JSON line carries
@@ -40,9 +41,9 @@ PEAK_FP32_VALU_TFLOPS = 157.3
 PEAK_HBM_GBPS = 8000.0
 
 # HBM bytes per launch of a kernel from the FETCH_SIZE and WRITE_SIZE counters
-# (scaled by a plain device copy's readings), with the source file they were
-# taken on and its SHA-256: the figure is reported only while that source is
-# unchanged.
+# (scaled by a plain device copy's readings), with the source file(s) they were
+# taken on and their SHA-256: the figure is reported only while those sources
+# are unchanged.
 MEASURED_TRAFFIC = {
     "k_selected_mfma": ("sparse_attention_long_07_amd/csrc/k_sparse.hip",
                         "57255b9998ed212525c4db292ff91264587c8f84267c043de1f8aef8da4d0bce", 61.56e9),
@@ -50,12 +51,19 @@ MEASURED_TRAFFIC = {
 
 
 def measured_traffic(kernel):
+    """HBM bytes per launch from the committed counter summary, while the
+    kernel's sources (one path or several, each with its SHA-256) are the
+    ones it was measured on; else None."""
     ent = MEASURED_TRAFFIC.get(kernel)
     if ent is None:
         return None
-    path, sha, nbytes = ent
-    with open(os.path.join(ROOT, path), "rb") as f:
-        return nbytes if hashlib.sha256(f.read()).hexdigest() == sha else None
+    *srcs, nbytes = ent
+    pairs = [srcs] if isinstance(srcs[0], str) else srcs[0]
+    for path, sha in pairs:
+        with open(os.path.join(ROOT, path), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != sha:
+                return None
+    return nbytes
 
 
 def dsa_decode(s, y, steps, topk=2048, hi=4, di=64):
@@ -391,7 +399,9 @@ def main():
     wsd = nsa.workspace(sd, nsa.OP_DECODE, dev)
     torch.cuda.synchronize()
 
-    stages = ["S1_compress", "S2_compressed_attention", "S3_select", "S4a_pack_kv_blocks", "S4b_window_gate",
+    # nsa_forward's launches, each on its own: S2 runs with the window half of
+    # S4 in one kernel (nsa_compressed_window_attention)
+    stages = ["S1_compress", "S2_compressed_attention_and_window", "S3_select", "S4a_pack_kv_blocks",
               "S4c_selected_gate", "decode_step"]
     nst = len(stages)
 
@@ -402,22 +412,19 @@ def main():
         mark(0)
         nsa.compress_kv(sp, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"], ck, cv)
         mark(1)
-        nsa.compressed_attention(sp, x["q"], ck, cv, ocmp, scores)
+        # the launches nsa_forward makes, each timed on its own
+        nsa.compressed_window_attention(sp, x["q"], x["k"], x["v"], ck, cv, x["w_g"], x["b_g"], scores, o)
         mark(2)
         nsa.select_topn(sp, scores, idx)
         mark(3)
-        # S4 in its three parts (the same kernels nsa_sparse_attention runs), so
-        # that each kernel is timed on its own
         nsa.pack_kv_blocks(sp, x["k"], x["v"], wss)
         mark(4)
-        nsa.window_attention(sp, x["q"], x["k"], x["v"], ocmp, x["w_g"], x["b_g"], o)
-        mark(5)
         nsa.selected_attention(sp, x["q"], x["k"], x["v"], idx, x["w_g"], x["b_g"], o, wss)
-        mark(6)
+        mark(5)
         y = dec[i % 2]
         nsa.decode_step(sd, y["seq_lens"], y["q"], y["k"], y["v"], y["ck"], y["cv"], y["w_g"], y["b_g"], None,
                         od, None, wsd)
-        mark(7)
+        mark(6)
 
     log("warmup", args.warmup)
     for i in range(args.warmup):
@@ -455,6 +462,24 @@ def main():
     torch.cuda.synchronize()
     dec_b2b_us = sorted(a.elapsed_time(b) * 1e3 for a, b in dev_ev)[nb2b // 2]
 
+    # S2 and the window kernel as the stage-by-stage calls run them on their
+    # own (nsa_compressed_attention, then nsa_window_attention on its o_cmp)
+    def standalone(fn):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        fn()
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    log("standalone S2 and window kernels", args.steps)
+    sa_ms = {"k_cmp_attn_mfma": standalone(lambda: nsa.compressed_attention(sp, x["q"], ck, cv, ocmp, scores)),
+             "k_window_mfma": standalone(lambda: nsa.window_attention(sp, x["q"], x["k"], x["v"], ocmp, x["w_g"],
+                                                                      x["b_g"], o))}
+
     fl = prefill_flops(sp)
     prefill_ms = float(st_ms[:nst - 1].sum())
     tflops = fl["total"] / (prefill_ms * 1e-3) / 1e12
@@ -466,13 +491,13 @@ def main():
     # on the stream the events are recorded on (S1 launches its kernel twice,
     # once for K and once for V; the decode step runs two kernels)
     kv_bytes = 2 * sp.B * sp.Hkv * sp.T * (sp.dk + sp.dv)
+    win_flop = fl["window"] + fl["gates"] * 2 // 3
     work = {
-        "S2_compressed_attention": ("k_cmp_attn_mfma", "mfma", fl["compressed"], PEAK_BF16_TFLOPS, "TFLOP/s"),
+        "S2_compressed_attention_and_window": ("k_cmp_attn_mfma+window", "mfma", fl["compressed"] + win_flop,
+                                               PEAK_BF16_TFLOPS, "TFLOP/s"),
         "S3_select": ("k_select_generic", "hbm", 4 * sp.B * sp.Hkv * sum(t // 64 + 1 for t in range(0, sp.T, 1)) +
                       4 * sp.B * sp.Hkv * sp.T * sp.n, PEAK_HBM_GBPS, "GB/s"),
         "S4a_pack_kv_blocks": ("k_pack_blocks", "hbm", 2 * kv_bytes, PEAK_HBM_GBPS, "GB/s"),
-        "S4b_window_gate": ("k_window_mfma", "mfma", fl["window"] + fl["gates"] * 2 // 3, PEAK_BF16_TFLOPS,
-                            "TFLOP/s"),
         "S4c_selected_gate": ("k_selected_mfma", "mfma", fl["selected"] + fl["gates"] // 3, PEAK_BF16_TFLOPS,
                               "TFLOP/s"),
     }
@@ -489,6 +514,11 @@ def main():
         ach = u / (st_ms[stages.index(k)] * 1e-3) / (1e12 if un == "TFLOP/s" else 1e9)
         kernels[kn] = {"ms": round(float(st_ms[stages.index(k)]), 4), "bound": bd, "achieved": round(ach, 2),
                        "unit": un, "frac": round(ach / pk, 4)}
+    kernels_standalone = {}
+    for kn, flop in (("k_cmp_attn_mfma", fl["compressed"]), ("k_window_mfma", win_flop)):
+        ach = flop / (sa_ms[kn] * 1e-3) / 1e12
+        kernels_standalone[kn] = {"ms": round(sa_ms[kn], 4), "bound": "mfma", "achieved": round(ach, 2),
+                                  "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
 
     res = {
         "metric": "NSA fwd TFLOP/s @64k prefill",
@@ -522,6 +552,7 @@ def main():
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
         "kernels": kernels,
+        "kernels_standalone": kernels_standalone,
     }
     res["prefill_fp32_T1024"] = small_prefill("fp32_T1024", args.steps)
     res["prefill_bf16_T8192"] = small_prefill("bf16_T8192", args.steps)

@@ -77,7 +77,8 @@ typedef enum {
     NSA_OP_BACKWARD = 4, /* nsa_backward */
     NSA_OP_DSA_DECODE = 5, /* nsa_dsa_decode: B*T fp32 indexer scores, then the split attention's partials */
     NSA_OP_DSA_PREFILL = 6, /* nsa_dsa_prefill: the indexer scores of one chunk of rows (<= 256 MiB) */
-    NSA_OP_BACKWARD_MLP = 7 /* nsa_backward_mlp */
+    NSA_OP_BACKWARD_MLP = 7, /* nsa_backward_mlp */
+    NSA_OP_CMP_WINDOW = 8 /* nsa_compressed_window_attention: o_cmp when not run as one kernel */
 } nsa_op;
 
 /* Problem description.  Supported ranges (checked on every call):
@@ -200,8 +201,11 @@ nsa_status nsa_sparse_attention(const nsa_config *cfg, const void *q, const void
 /* Stage S4 in parts, for callers that schedule them separately (for
  * example to overlap the window half with other work or to time each
  * kernel).  nsa_sparse_attention equals nsa_pack_kv_blocks, then
- * nsa_window_attention, then nsa_selected_attention on the same o, bit for
- * bit.
+ * nsa_window_attention, then nsa_selected_attention on the same o: bit for
+ * bit where the packed-block workspace is used (NSA_OP_SPARSE size > 0);
+ * elsewhere to the rounding of o (the one-call form rounds the gated sum of
+ * the three branches once, the parts round after the window and compressed
+ * terms and again after the selected one).
  *   nsa_pack_kv_blocks:     writes K and V, repacked per 64-token block,
  *                           into ws (nsa_workspace_bytes(cfg,
  *                           NSA_OP_SPARSE) bytes; nothing is written when
@@ -219,6 +223,23 @@ nsa_status nsa_window_attention(const nsa_config *cfg, const void *q, const void
 nsa_status nsa_selected_attention(const nsa_config *cfg, const void *q, const void *k, const void *v,
                                   const int32_t *idx, const void *w_g, const void *b_g, void *o, void *ws,
                                   size_t ws_bytes, void *stream);
+
+/* Stage S2 and the window half of S4 in one call: scores as written by
+ * nsa_compressed_attention, and o = g_cmp * o_cmp + g_win * o_win as written
+ * by nsa_window_attention (definitions as for those two; the 16-head bf16
+ * configurations at d_k/d_v = 192/128, 128/128, 64/64 run it as one kernel,
+ * which reuses each workgroup's query fragments and o_cmp for its window
+ * rows).  o_cmp: written if non-NULL, else only used internally.  Followed
+ * by nsa_select_topn, nsa_pack_kv_blocks and nsa_selected_attention on the
+ * same o, it is nsa_forward in parts (for callers that schedule or time
+ * them): bit for bit where NSA_OP_SPARSE's workspace size is non-zero,
+ * elsewhere to the rounding of o as for nsa_sparse_attention's parts.  ws: nsa_workspace_bytes(cfg, NSA_OP_CMP_WINDOW)
+ * bytes, 256-byte aligned, needed only when that size is non-zero and o_cmp
+ * is NULL (it then holds o_cmp). */
+nsa_status nsa_compressed_window_attention(const nsa_config *cfg, const void *q, const void *k, const void *v,
+                                           const void *cmp_k, const void *cmp_v, const void *w_g, const void *b_g,
+                                           float *scores, void *o, void *o_cmp, void *ws, size_t ws_bytes,
+                                           void *stream);
 
 /* Block selection alone: S2 (scores only) followed by S3, i.e. the
  * importance of each selection block derived from the compressed branch's

@@ -30,6 +30,7 @@
 // barrier per tile.  Causal masking is applied only on a wave's last tiles.
 #include "mfma_util.h"
 #include "nsa_internal.h"
+#include "window_phase.h"
 
 namespace nsa {
 
@@ -87,9 +88,28 @@ __device__ __forceinline__ bool cmp_map_wg(int id, int BG, int ntp, int &bg, int
     return true;
 }
 
-template <int DK, int DV, bool WITH_V>
+// LDS of the kernel: with WIN the window phase reuses it once the
+// compressed phase is done.
+template <int DK, int DV, bool WIN>
+struct CmpShared {
+    CmpLds<DK, DV> c;
+};
+template <int DK, int DV>
+struct CmpShared<DK, DV, true> {
+    union {
+        CmpLds<DK, DV> c;
+        win::WinLds<DK, DV> w;
+    };
+};
+
+// WIN (with WITH_V): the workgroup goes on to the window branch of its 16
+// positions and writes o = g_cmp o_cmp + g_win o_win (window_phase.h) from
+// the query fragments and o_cmp it holds; o_cmp is stored only where a.ocmp
+// asks for it (the saved statistics' slot).
+template <int DK, int DV, bool WITH_V, bool WIN = false>
 __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, int BG)
 {
+    static_assert(!WIN || WITH_V, "the window phase needs o_cmp");
     constexpr int KSTEPS = DK / 16;
     constexpr int DT = DV / 32;
     constexpr int CH = DK / 8;                                  // 16-byte chunks per K row
@@ -98,7 +118,8 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
     constexpr int VTASKS = kTile * (DV / 8);                    // 16-byte V chunks per tile
     constexpr int VTK = (VTASKS + kThreads - 1) / kThreads;
     using L = CmpLds<DK, DV>;
-    __shared__ L sm;
+    __shared__ CmpShared<DK, DV, WIN> sh;
+    L &sm = sh.c;
 
     const Dims &d = a.d;
     int bg, ptile;
@@ -438,7 +459,29 @@ __global__ __launch_bounds__(kThreads) void k_cmp_attn_mfma(RowArgs a, int ntp, 
     // visible to it).
     if (h == 0 && (lane & 15) == 0 && live && 16 * ntw <= tb) srow[16 * ntw] = carry;
 
-    if (WITH_V && live) {
+    if constexpr (WIN) {
+        uint2 ocw[DT][4];
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; q4++) {
+                ocw[dt][q4].x = pack_bf16x2(oacc[dt][4 * q4], oacc[dt][4 * q4 + 1]);
+                ocw[dt][q4].y = pack_bf16x2(oacc[dt][4 * q4 + 2], oacc[dt][4 * q4 + 3]);
+            }
+        if (live) {
+            if (a.lse && h == 0) a.lse[((long)b * a.R + t) * d.Hq + g * 16 + head] = lse2 * kLn2;
+            if (a.ocmp) {
+                uint16_t *orow = (uint16_t *)a.ocmp + (((long)b * a.R + t) * d.Hq + g * 16 + head) * DV;
+#pragma unroll
+                for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; q4++) *(uint2 *)(orow + 32 * dt + 8 * q4 + 4 * h) = ocw[dt][q4];
+            }
+        }
+        // every wave's last reads of the compressed tiles passed the loop's
+        // final barrier, so the window phase may overwrite the LDS
+        win::window_phase<DK, DV, true>(a, sh.w, bg, ptile, qf, ocw);
+    } else if (WITH_V && live) {
         // the branch's log-sum-exp for the backward, when asked for
         if (a.lse && h == 0) a.lse[((long)b * a.R + t) * d.Hq + g * 16 + head] = lse2 * kLn2;
         uint16_t *orow = (uint16_t *)a.ocmp + (((long)b * a.R + t) * d.Hq + g * 16 + head) * DV;
@@ -473,6 +516,31 @@ static hipError_t launch_dims(const RowArgs &a, bool with_v, hipStream_t s)
     if (with_v) hipLaunchKernelGGL((k_cmp_attn_mfma<DK, DV, true>), dim3((unsigned)nwg), dim3(kThreads), 0, s, a, ntp, BG);
     else hipLaunchKernelGGL((k_cmp_attn_mfma<DK, DV, false>), dim3((unsigned)nwg), dim3(kThreads), 0, s, a, ntp, BG);
     return hipGetLastError();
+}
+
+// S2 with the window branch fused (the k_window_mfma work of the same 16
+// positions, on the same workgroup)
+template <int DK, int DV>
+static hipError_t launch_win_dims(const RowArgs &a, hipStream_t s)
+{
+    static_assert(kPos == win::kPos && kThreads == win::kThreads, "one workgroup shape for both phases");
+    const Dims &d = a.d;
+    const int ntp = (a.R + kPos - 1) / kPos;
+    const int BG = d.B * d.Hkv;
+    long nwg;
+    if (BG <= 8 && 8 % BG == 0) nwg = 8L * ((ntp + 8 / BG - 1) / (8 / BG));
+    else nwg = (long)BG * ntp;
+    hipLaunchKernelGGL((k_cmp_attn_mfma<DK, DV, true, true>), dim3((unsigned)nwg), dim3(kThreads), 0, s, a, ntp, BG);
+    return hipGetLastError();
+}
+
+hipError_t launch_cmp_win_mfma(const RowArgs &a, hipStream_t s)
+{
+    const Dims &d = a.d;
+    if (d.dk == 192 && d.dv == 128) return launch_win_dims<192, 128>(a, s);
+    if (d.dk == 128 && d.dv == 128) return launch_win_dims<128, 128>(a, s);
+    if (d.dk == 64 && d.dv == 64) return launch_win_dims<64, 64>(a, s);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_cmp_attn_mfma(const RowArgs &a, bool with_v, hipStream_t s)

@@ -112,6 +112,9 @@ RowArgs prefill_args(const Dims &d, const void *q)
     return a;
 }
 
+// S2 and the window half of S4 as one kernel
+bool cmp_window_fused(const Dims &d) { return cmp_attn_mfma_supported(d) && sparse_mfma_supported(d); }
+
 bool all_aligned(std::initializer_list<const void *> ps)
 {
     for (const void *p : ps)
@@ -139,6 +142,8 @@ size_t nsa_workspace_bytes(const nsa_config *cfg, int op)
         return backward_layout(d, nullptr, nullptr);
     case NSA_OP_BACKWARD_MLP:
         return backward_layout(d, nullptr, nullptr, true);
+    case NSA_OP_CMP_WINDOW:
+        return cmp_window_fused(d) ? 0 : align_up((d.dtype == NSA_FP32 ? 4 : 2) * (size_t)d.B * d.T * d.Hq * d.dv);
     case NSA_OP_DSA_DECODE:
         // the indexer scores, later reused for the split attention's partials
         return dsa_supported(d) ? align_up(std::max(sizeof(float) * (size_t)d.B * d.T, dsa_split_bytes(d, kDsaMaxSplit)))
@@ -332,6 +337,40 @@ nsa_status nsa_compressed_attention(const nsa_config *cfg, const void *q, const 
     return hip_status(launch_cmp_attn_generic(a, o_cmp != nullptr, (hipStream_t)stream));
 }
 
+nsa_status nsa_compressed_window_attention(const nsa_config *cfg, const void *q, const void *k, const void *v,
+                                           const void *cmp_k, const void *cmp_v, const void *w_g, const void *b_g,
+                                           float *scores, void *o, void *o_cmp, void *ws, size_t ws_bytes,
+                                           void *stream)
+{
+    Dims d;
+    nsa_status st = check_config(cfg, &d);
+    if (st != NSA_OK) return st;
+    if (!q || !k || !v || !cmp_k || !cmp_v || !w_g || !b_g || !scores || !o) return NSA_ERR_NULL;
+    if (!all_aligned({q, k, v, cmp_k, cmp_v, w_g, b_g, scores, o, o_cmp})) return NSA_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    RowArgs a = prefill_args(d, q);
+    a.kc = cmp_k;
+    a.vc = cmp_v;
+    a.scores = scores;
+    a.k = k;
+    a.v = v;
+    a.wg = w_g;
+    a.bg = b_g;
+    a.o = o;
+    a.ocmp = o_cmp;
+    if (cmp_window_fused(d)) return hip_status(launch_cmp_win_mfma(a, s));
+    if (!o_cmp) {
+        if (!ws || ws_bytes < nsa_workspace_bytes(cfg, NSA_OP_CMP_WINDOW)) return NSA_ERR_WORKSPACE;
+        if ((uintptr_t)ws % kAlign) return NSA_ERR_ALIGN;
+        a.ocmp = ws;
+    }
+    if (cmp_attn_mfma_supported(d)) NSA_TRY(launch_cmp_attn_mfma(a, true, s));
+    else NSA_TRY(launch_cmp_attn_generic(a, true, s));
+    a.part = 1;
+    if (sparse_mfma_supported(d)) return hip_status(launch_sparse_mfma(a, nullptr, s));
+    return hip_status(launch_sparse_generic(a, s));
+}
+
 nsa_status nsa_select_topn(const nsa_config *cfg, const float *scores, int32_t *idx, void *stream)
 {
     Dims d;
@@ -470,6 +509,9 @@ static nsa_status forward_impl(const nsa_config *cfg, const void *q, const void 
     // with saved statistics the compressed-branch output goes to its slot
     void *ocmp = o_branch ? o_branch : (void *)(w + L.ocmp);
     float *scores = scores_out ? scores_out : (float *)(w + L.scores);
+    // matrix-core shapes: the window half of S4 runs inside the S2 launch,
+    // which then writes o_cmp only into the saved statistics
+    const bool fused = cmp_window_fused(d);
     {
         RowArgs a = prefill_args(d, q);
         a.kc = cmp_k;
@@ -477,8 +519,20 @@ static nsa_status forward_impl(const nsa_config *cfg, const void *q, const void 
         a.ocmp = ocmp;
         a.scores = scores;
         a.lse = lse;
-        if (cmp_attn_mfma_supported(d)) NSA_TRY(launch_cmp_attn_mfma(a, true, s));
-        else NSA_TRY(launch_cmp_attn_generic(a, true, s));
+        if (fused) {
+            a.ocmp = o_branch;
+            a.k = k;
+            a.v = v;
+            a.wg = w_g;
+            a.bg = b_g;
+            a.o = o;
+            a.osave = o_branch;
+            NSA_TRY(launch_cmp_win_mfma(a, s));
+        } else if (cmp_attn_mfma_supported(d)) {
+            NSA_TRY(launch_cmp_attn_mfma(a, true, s));
+        } else {
+            NSA_TRY(launch_cmp_attn_generic(a, true, s));
+        }
     }
     const int32_t *idx = idx_in;
     if (idx_in) {
@@ -500,6 +554,12 @@ static nsa_status forward_impl(const nsa_config *cfg, const void *q, const void 
     a.o = o;
     a.lse = lse;
     a.osave = o_branch;
+    if (fused) {   // the window half is done: pack the K/V blocks, then the selected half
+        a.part = 3;
+        NSA_TRY(launch_sparse_mfma(a, w + L.vt, s));
+        a.part = 2;
+        return hip_status(launch_sparse_mfma(a, w + L.vt, s));
+    }
     if (sparse_mfma_supported(d)) return hip_status(launch_sparse_mfma(a, w + L.vt, s));
     return hip_status(launch_sparse_generic(a, s));
 }

@@ -210,6 +210,11 @@ hipError_t launch_compress_bf16(const Dims &d, const void *k, const void *v, con
 // Matrix-core kernels (bf16 storage, G = 16; prefill rows only).
 bool cmp_attn_mfma_supported(const Dims &d);
 hipError_t launch_cmp_attn_mfma(const RowArgs &a, bool with_v, hipStream_t s);
+// S2 and the window half of S4 in one launch (cmp_attn_mfma_supported shapes):
+// needs q, kc, vc, scores, k, v, wg, bg, o; writes scores and o = g_cmp o_cmp
+// + g_win o_win, and o_cmp only where a.ocmp is set (with lse / osave: the
+// saved statistics of the compressed and window branches)
+hipError_t launch_cmp_win_mfma(const RowArgs &a, hipStream_t s);
 bool sparse_mfma_supported(const Dims &d);
 size_t sparse_mfma_ws_bytes(const Dims &d);   // K and V packed per 64-token block
 hipError_t launch_sparse_mfma(const RowArgs &a, void *vt_ws, hipStream_t s);   // honours a.part

@@ -17,12 +17,13 @@ from .config import BF16, FP32, NSAShape
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libnsa.so")
 
-OP_FORWARD, OP_SELECT, OP_DECODE, OP_SPARSE, OP_BACKWARD, OP_DSA_DECODE, OP_DSA_PREFILL, OP_BACKWARD_MLP = range(8)
+(OP_FORWARD, OP_SELECT, OP_DECODE, OP_SPARSE, OP_BACKWARD, OP_DSA_DECODE, OP_DSA_PREFILL, OP_BACKWARD_MLP,
+ OP_CMP_WINDOW) = range(9)
 STATUS = {0: "NSA_OK", -1: "NSA_ERR_NULL", -2: "NSA_ERR_SHAPE", -3: "NSA_ERR_DTYPE", -4: "NSA_ERR_PARAM",
           -5: "NSA_ERR_WORKSPACE", -6: "NSA_ERR_HIP", -7: "NSA_ERR_ALIGN"}
 
 EXPORTS = ("nsa_workspace_bytes", "nsa_compress_kv", "nsa_compress_kv_mlp", "nsa_compress_append", "nsa_compress_append_mlp", "nsa_compressed_attention",
-           "nsa_select_topn",
+           "nsa_compressed_window_attention", "nsa_select_topn",
            "nsa_sparse_attention", "nsa_pack_kv_blocks", "nsa_window_attention", "nsa_selected_attention", "nsa_select_blocks",
            "nsa_forward", "nsa_forward_train", "nsa_decode_step", "nsa_decode_step_noalloc", "nsa_backward", "nsa_backward_mlp", "nsa_dsa_decode", "nsa_dsa_prefill", "nsa_status_string")
 
@@ -70,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.nsa_compress_append_mlp.argtypes = [ctypes.POINTER(Config), _vp, _vp, ctypes.c_int32] + [_vp] * 11
         L.nsa_compressed_attention.restype = ctypes.c_int
         L.nsa_compressed_attention.argtypes = [ctypes.POINTER(Config)] + [_vp] * 6
+        L.nsa_compressed_window_attention.restype = ctypes.c_int
+        L.nsa_compressed_window_attention.argtypes = [ctypes.POINTER(Config)] + [_vp] * 11 + [ctypes.c_size_t, _vp]
         L.nsa_select_topn.restype = ctypes.c_int
         L.nsa_select_topn.argtypes = [ctypes.POINTER(Config)] + [_vp] * 3
         L.nsa_sparse_attention.restype = ctypes.c_int
@@ -254,6 +257,36 @@ def compressed_attention(s: NSAShape, q, cmp_k, cmp_v=None, o_cmp=None, scores=N
     _check("nsa_compressed_attention", lib().nsa_compressed_attention(ctypes.byref(c), _p(q), _p(cmp_k), _p(cmp_v),
                                                                       _p(o_cmp), _p(scores), _stream()))
     return o_cmp, scores
+
+
+def compressed_window_attention(s: NSAShape, q, k, v, cmp_k, cmp_v, w_g, b_g, scores=None, o=None, o_cmp=None,
+                                ws=None):
+    """Stage S2 and the window half of S4 in one call: returns (o, scores),
+    o = g_cmp o_cmp + g_win o_win; o_cmp is written only when given."""
+    dt = _dt(s)
+    _req(q, "q", (s.B, s.T, s.Hq, s.dk), dt)
+    _req(k, "k", (s.B, s.Hkv, s.T, s.dk), dt)
+    _req(v, "v", (s.B, s.Hkv, s.T, s.dv), dt)
+    _req(cmp_k, "cmp_k", (s.B, s.Hkv, s.n_pad, s.dk), dt)
+    _req(cmp_v, "cmp_v", (s.B, s.Hkv, s.n_pad, s.dv), dt)
+    _req(w_g, "w_g", (s.Hq, 3, s.dk), dt)
+    _req(b_g, "b_g", (s.Hq, 3), dt)
+    if scores is None:
+        scores = torch.empty((s.B, s.Hkv, s.T, s.nb), dtype=torch.float32, device=q.device)
+    _req(scores, "scores", (s.B, s.Hkv, s.T, s.nb), torch.float32)
+    if o is None:
+        o = torch.empty((s.B, s.T, s.Hq, s.dv), dtype=dt, device=q.device)
+    _req(o, "o", (s.B, s.T, s.Hq, s.dv), dt)
+    if o_cmp is not None:
+        _req(o_cmp, "o_cmp", (s.B, s.T, s.Hq, s.dv), dt)
+    if ws is None and o_cmp is None and workspace_bytes(s, OP_CMP_WINDOW) > 0:
+        ws = workspace(s, OP_CMP_WINDOW, q.device)
+    c = config(s)
+    _check("nsa_compressed_window_attention",
+           lib().nsa_compressed_window_attention(ctypes.byref(c), _p(q), _p(k), _p(v), _p(cmp_k), _p(cmp_v), _p(w_g),
+                                                 _p(b_g), _p(scores), _p(o), _p(o_cmp), _p(ws),
+                                                 0 if ws is None else ws.numel(), _stream()))
+    return o, scores
 
 
 def select_topn(s: NSAShape, scores, idx=None):

@@ -93,6 +93,7 @@ def test_bad_config_rejected_everywhere(kw, code):
     assert L.nsa_pack_kv_blocks(c, f[0], f[1], f[2], 1 << 40, None) == code
     assert L.nsa_selected_attention(c, *f[:7], f[0], 1 << 40, None) == code
     assert L.nsa_compressed_attention(c, *f[:5], None) == code
+    assert L.nsa_compressed_window_attention(c, *f[:10], f[0], 1 << 40, None) == code
     assert L.nsa_select_topn(c, f[0], f[1], None) == code
 
 
@@ -430,6 +431,30 @@ def test_compressed_attention_checks(pos):
     assert L.nsa_compressed_attention(c, FAKE, FAKE, None, FAKE, FAKE, None) == NULL
     assert L.nsa_compressed_attention(c, FAKE, FAKE, MIS, FAKE, FAKE, None) == ALIGN
     assert L.nsa_compressed_attention(c, FAKE, FAKE, FAKE, MIS, FAKE, None) == ALIGN
+
+
+@pytest.mark.parametrize("pos", range(9))
+def test_compressed_window_attention_checks(pos):
+    """q k v cmp_k cmp_v w_g b_g scores o are required, o_cmp is optional,
+    every pointer 16-byte aligned; without o_cmp, a configuration that is
+    not one kernel needs a 256-byte aligned workspace for it."""
+    L = nsa.lib()
+    c = ctypes.byref(cfg())
+    req = [FAKE] * 9
+    req[pos] = None
+    assert L.nsa_compressed_window_attention(c, *req, FAKE, None, 0, None) == NULL
+    req[pos] = MIS
+    assert L.nsa_compressed_window_attention(c, *req, FAKE, None, 0, None) == ALIGN
+    assert L.nsa_compressed_window_attention(c, *([FAKE] * 9), MIS, None, 0, None) == ALIGN
+    need = L.nsa_workspace_bytes(c, nsa.OP_CMP_WINDOW)
+    s = NSAShape(1, 256, 2, 4, 64, 32, "bf16")
+    assert need == (s.esize * s.B * s.T * s.Hq * s.dv + 255) // 256 * 256
+    assert L.nsa_compressed_window_attention(c, *([FAKE] * 9), None, None, 0, None) == WS
+    assert L.nsa_compressed_window_attention(c, *([FAKE] * 9), None, FAKE, need - 1, None) == WS
+    assert L.nsa_compressed_window_attention(c, *([FAKE] * 9), None, ctypes.c_void_p(0x10010), need, None) == ALIGN
+    # one kernel (16 heads per KV head, bf16, d_k/d_v = 192/128): no workspace
+    one = nsa.config(NSAShape(1, 256, 2, 16, 192, 128, "bf16"))
+    assert L.nsa_workspace_bytes(ctypes.byref(one), nsa.OP_CMP_WINDOW) == 0
 
 
 def test_select_topn_checks():

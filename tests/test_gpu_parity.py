@@ -260,17 +260,26 @@ def test_prefill_full_size(name, wname, scaled, stride, floor):
     x = make_prefill(s, 1000 if scaled == wl.unit_scaled else 1010, "cuda", unit_scaled=scaled)
     ck, cv = nsa.compress_kv(s, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"])
     o, idx = nsa.forward(s, x["q"], x["k"], x["v"], ck, cv, x["w_g"], x["b_g"], want_idx=True)
-    # the stage-by-stage calls that bench.py times give the same result, bit for bit
+    # the stage-by-stage calls that bench.py times (S2 with the window half,
+    # S3, packing, the selected half), and the calls of every stage on its
+    # own, give the same result, bit for bit
+    o3, sc3 = nsa.compressed_window_attention(s, x["q"], x["k"], x["v"], ck, cv, x["w_g"], x["b_g"])
+    idx3 = nsa.select_topn(s, sc3)
+    ws = nsa.pack_kv_blocks(s, x["k"], x["v"])
+    nsa.selected_attention(s, x["q"], x["k"], x["v"], idx3, x["w_g"], x["b_g"], o3, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(idx3, idx)
+    assert torch.equal(o3, o)
+    del o3, sc3, idx3
     ocmp, sc = nsa.compressed_attention(s, x["q"], ck, cv)
     idx2 = nsa.select_topn(s, sc)
-    ws = nsa.pack_kv_blocks(s, x["k"], x["v"])
     o2 = nsa.window_attention(s, x["q"], x["k"], x["v"], ocmp, x["w_g"], x["b_g"])
     nsa.selected_attention(s, x["q"], x["k"], x["v"], idx2, x["w_g"], x["b_g"], o2, ws)
     torch.cuda.synchronize()
     assert torch.equal(idx2, idx)
     assert torch.equal(o2, o)
     del ocmp, sc, idx2, ws, o2
-    say("  gpu done (staged path identical); oracle compression")
+    say("  gpu done (staged paths identical); oracle compression")
     kc = oracle_compress(s, x["k"], x["w_ck"], x["pe_k"])
     vc = oracle_compress(s, x["v"], x["w_cv"], x["pe_v"])
     for got, ref in ((ck, kc), (cv, vc)):
@@ -444,6 +453,32 @@ def test_stage_parity(name, s, scaled):
     if nsa.workspace_bytes(s, nsa.OP_SPARSE) > 0:
         # packed-block (matrix core) path: the combined call runs the same two kernels in the same order
         assert torch.equal(o2, o)
+    # S2 with the window half of S4 in one call (one kernel on the matrix-core
+    # shapes): its scores are S2's, its o_cmp (when asked for) is S2's and its o
+    # is nsa_window_attention's on that o_cmp, bit for bit; followed by S3,
+    # packing and the selected half it is nsa_forward (bit for bit on the
+    # packed-block path; elsewhere the one-call form rounds the gated sum once)
+    kc_d = torch.from_numpy(kc).to(dt).cuda()
+    vc_d = torch.from_numpy(vc).to(dt).cuda()
+    ocmp2 = torch.empty_like(ocmp)
+    o_w, sc_w = nsa.compressed_window_attention(s, x["q"], x["k"], x["v"], kc_d, vc_d, x["w_g"], x["b_g"],
+                                                o_cmp=ocmp2)
+    o_win = nsa.window_attention(s, x["q"], x["k"], x["v"], ocmp, x["w_g"], x["b_g"])
+    torch.cuda.synchronize()
+    assert torch.equal(ocmp2, ocmp)
+    assert torch.equal(sc_w[causal_t], sc[causal_t])
+    assert torch.equal(o_w, o_win)
+    o3, sc3 = nsa.compressed_window_attention(s, x["q"], x["k"], x["v"], kc_d, vc_d, x["w_g"], x["b_g"])
+    idx3 = nsa.select_topn(s, sc3)
+    ws3 = nsa.pack_kv_blocks(s, x["k"], x["v"])
+    nsa.selected_attention(s, x["q"], x["k"], x["v"], idx3, x["w_g"], x["b_g"], o3, ws3)
+    o_f, idx_f = nsa.forward(s, x["q"], x["k"], x["v"], kc_d, vc_d, x["w_g"], x["b_g"], want_idx=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx3, idx_f)
+    if nsa.workspace_bytes(s, nsa.OP_SPARSE) > 0:
+        assert torch.equal(o3, o_f)
+    else:
+        assert np.abs(np64(o3) - np64(o_f)).max() <= 1e-6 * max(1.0, float(np.abs(np64(o_f)).max()))
 
 
 @pytest.mark.parametrize("mode", ["random", "quantized_ties", "all_equal", "huge_T"])
