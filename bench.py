@@ -46,7 +46,11 @@ PEAK_HBM_GBPS = 8000.0
 # are unchanged.
 MEASURED_TRAFFIC = {
     "k_selected_mfma": ("sparse_attention_long_07_amd/csrc/k_sparse.hip",
-                        "57255b9998ed212525c4db292ff91264587c8f84267c043de1f8aef8da4d0bce", 61.56e9),
+                        "a6af748442c4ff8354ece7709a69d22c16f0311ad928bb3c5c3170b79f28c283", 63.45e9),
+    "k_cmp_attn_mfma+window": ([("sparse_attention_long_07_amd/csrc/k_cmp_attn.hip",
+                                 "96fc76f52e5346f84f25d99280ed1081f2bcfdd517e2fc26f46b1094e5519cc9"),
+                                ("sparse_attention_long_07_amd/csrc/window_phase.h",
+                                 "c6c0db9e68159d260edbf8d4d9ec3cbe63465c2724d7ddfa440db8ff653f1bb4")], 4.417e9),
 }
 
 
