@@ -112,6 +112,7 @@ SMALL = [
     ("bf16_T600_g16_d128_wT_randsel", NSAShape(1, 600, 2, 16, 128, 128, n=4, w=1024), False, True),
     # matrix-core passes with no compressed block (T < 32) and with one (T = 47)
     ("bf16_T20_g16", NSAShape(1, 20, 1, 16, 192, 128), False, False),
+    ("bf16_T300_g16_d64_Hkv3_randsel", NSAShape(1, 300, 3, 16, 64, 64, n=4, w=100), False, True),
     ("bf16_T47_g16_d64_B2_randsel", NSAShape(2, 47, 1, 16, 64, 64, n=4, w=40), False, True),
 ]
 

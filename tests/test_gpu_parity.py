@@ -43,6 +43,8 @@ SMALL = [
     # matrix-core kernels with no compressed block (T < 32) and with one (T = 47), one selection block
     ("bf16_T20_g16", NSAShape(1, 20, 1, 16, 192, 128), False),
     ("bf16_T47_g16_d128_B2", NSAShape(2, 47, 2, 16, 128, 128), False),
+    # (sequence, KV head) pairs that do not divide the 8 XCDs: the other workgroup order of S2
+    ("bf16_T600_g16_B3", NSAShape(3, 600, 1, 16, 192, 128), False),
     ("fp32_T300_g5_w64", NSAShape(1, 300, 2, 5, 32, 16, FP32, n=3, w=64), False),
 ]
 
@@ -398,6 +400,7 @@ STAGE = [
     ("bf16_T700_g16_d128_B2", NSAShape(2, 700, 1, 16, 128, 128, n=4, w=64), True),
     # long enough that S2 runs its unmasked main tiles (t >= 1039) before the masked tail
     ("bf16_T2100_g16_d128_B2", NSAShape(2, 2100, 1, 16, 128, 128, n=8, w=256), False),
+    ("bf16_T500_g16_d64_Hkv3", NSAShape(1, 500, 3, 16, 64, 64, n=5, w=100), False),
     ("fp32_T1024", NSAShape(1, 1024, 1, 4, 64, 64, FP32), True),
 ]
 
