@@ -1,7 +1,7 @@
-"""Sequences longer than the 64k workloads, on the matrix-core paths: a 128k
-prefill (131,072 tokens: 2,048 selection blocks, past the 1,024 blocks the
-selector's fast path handles) and a decode step on 80,000-token caches, each
-compared with the oracle on sampled rows."""
+"""Long sequences on the matrix-core paths: a 128k prefill (131,072 tokens:
+2,048 selection blocks, past the 1,024 blocks the selector's fast path
+handles), a decode step on 80,000-token caches and the backward at T=65536,
+each compared with the oracle on sampled rows."""
 from __future__ import annotations
 
 import sys
@@ -102,3 +102,37 @@ def test_decode_80k_caches():
                          idx_in=torch.from_numpy(np.ascontiguousarray(ref["idx"]).astype(np.int32)).cuda())
     torch.cuda.synchronize()
     assert np.abs(np64(o3) - ref["o"]).max() <= out_tol(s, ref["o"])
+
+
+def test_backward_64k_masked_do():
+    """The backward at T=65536 (one KV group of 16 heads, d_k=192, d_v=128),
+    both forms, against the oracle's exact gradients for a dO that is zero
+    outside 32 sampled rows and the last 192 (so the oracle visits only those
+    rows); d_q must be zero on every other row."""
+    from tests.parity_util import random_selection
+    from tests.test_gpu_backward import PAIRS, _gpu_bwd, _gpu_saved, _oracle_bwd, _tol
+
+    s = NSAShape(1, 65536, 1, 16, 192, 128)
+    say("64k backward", s)
+    x = make_prefill(s, 14, "cuda", unit_scaled=False, with_grad=True)
+    ck, cv = nsa.compress_kv(s, x["k"], x["v"], x["w_ck"], x["pe_k"], x["w_cv"], x["pe_v"])
+    x["cmp_k"], x["cmp_v"] = ck, cv
+    x["idx"] = torch.from_numpy(random_selection(s, 13)).cuda()
+    T = s.T
+    t0 = T - 192
+    rng = np.random.default_rng(15)
+    rows = np.unique(np.concatenate([rng.choice(t0, size=24, replace=False), [0, 31, 63, 64, 511, 512, 32767, 32768]]))
+    keep = np.zeros(T, dtype=bool)
+    keep[rows] = True
+    keep[t0:] = True
+    do_mask = x["do"].clone()
+    do_mask[:, torch.from_numpy(~keep).cuda()] = 0
+    say("  oracle backward on", int(keep.sum()), "rows")
+    ref = _oracle_bwd(s, x, np64(do_mask))
+    for saved in (None, _gpu_saved(s, x)):
+        g = _gpu_bwd(s, x, do_mask, saved)
+        for rn, gn in PAIRS:
+            err = float(np.abs(np64(g[gn]) - ref[rn]).max())
+            say("  ", gn, "saved" if saved is not None else "recomputed", "max err %.3g tol %.3g" % (err, _tol(s, ref, rn)))
+            assert err <= _tol(s, ref, rn), (gn, saved is not None, err)
+        assert not np.any(np64(g["d_q"])[:, ~keep])
