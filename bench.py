@@ -46,11 +46,11 @@ PEAK_HBM_GBPS = 8000.0
 # are unchanged.
 MEASURED_TRAFFIC = {
     "k_selected_mfma": ("sparse_attention_long_07_amd/csrc/k_sparse.hip",
-                        "a6af748442c4ff8354ece7709a69d22c16f0311ad928bb3c5c3170b79f28c283", 63.45e9),
+                        "44a66c0b754df24b5e81780b0588c8a12a37842d851c7b1c6c85a64f2de53085", 63.16e9),
     "k_cmp_attn_mfma+window": ([("sparse_attention_long_07_amd/csrc/k_cmp_attn.hip",
-                                 "96fc76f52e5346f84f25d99280ed1081f2bcfdd517e2fc26f46b1094e5519cc9"),
+                                 "87cd1dd624260d4ecdf2552ed97c4deab85161ecc3a576b3a349e344a069f7f8"),
                                 ("sparse_attention_long_07_amd/csrc/window_phase.h",
-                                 "c6c0db9e68159d260edbf8d4d9ec3cbe63465c2724d7ddfa440db8ff653f1bb4")], 4.417e9),
+                                 "c6c0db9e68159d260edbf8d4d9ec3cbe63465c2724d7ddfa440db8ff653f1bb4")], 4.416e9),
 }
 
 

@@ -41,11 +41,9 @@ constexpr int kTile = 64;    // compressed keys per LDS tile
 constexpr int kThreads = 512;
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int kSgValu = 0x402;      // VALU, transcendental included
-constexpr int kSgTrans = 0x400;
 constexpr int kSgMfma = 0x008;
 constexpr int kSgVmemRead = 0x020;
 constexpr int kSgDsRead = 0x100;
-constexpr int kSgDsWrite = 0x200;
 
 template <int DK, int DV>
 struct CmpLds {

@@ -34,12 +34,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTile = 64;
 
-__device__ __forceinline__ int krow(int k)
-{
-    int h = k >> 4, m = (k >> 2) & 3, u = k & 3;
-    return 8 * m + 4 * h + u;
-}
-
 __device__ __forceinline__ float sigmoid(float z) { return 1.f / (1.f + __expf(-z)); }
 
 // Fragment-major packing of K and V per 64-token block, so that every operand
